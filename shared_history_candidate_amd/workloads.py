@@ -1,0 +1,205 @@
+"""Seeded synthetic inputs for shared-history cross-attention.
+
+This module only draws random numbers and lays them out; it holds none of the
+method's arithmetic.  Both the GPU path's tests/bench and the CPU oracle read
+the arrays it returns, so the two sides always see identical inputs.
+
+Shapes and distributions follow the workloads the pages describe:
+  * ReST-like serving (ReST reading note, s.3.3 and s.5.3): d = 256, q = 3
+    token-specific query tokens ([CLS]/ad/user), memory = encoder output H used
+    as both K and V, ragged history lengths;
+  * long history (ReST reading note s.5.3, length axis up to 16k, width 512);
+  * TransX-like memory (TransX report s.2): 64 recent + 32 chunk-summary slots
+    with separate K and V, one query per candidate, ~1000 candidates per
+    request (EST article s.1: thousands of candidates per request);
+  * ragged shared-prefix training batch (ReST reading note s.3.5 ULT; TransX
+    report s.2 trajectory packing): lognormal history lengths, 1..64
+    candidates per user.
+
+Draw order (numpy PCG64, ``default_rng(seed)``): memory lengths, candidate
+counts, H (or K then V), Z, W_Q slots in order.  Values are standard normal
+(float32 draws); W_Q has variance 1/d.  In bf16 mode every array is rounded to
+the nearest bf16 value (round-to-nearest-even) and kept as float32 holding
+that exact value, so converting it to bf16 on the device is exact and the
+oracle reads the same numbers upcast to fp64.
+
+W_Q is returned output-major: ``wt[s][o][i]`` is W_Q[s] of Eq. (7) at (i, o).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional, Sequence
+
+import numpy as np
+
+__all__ = ["Workload", "CONFIGS", "make", "custom", "round_bf16"]
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bf16 (ties to even); returns float32
+    arrays whose low 16 mantissa bits are zero.  Inputs must be finite."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return (u.astype(np.uint32) << 16).view(np.float32)
+
+
+@dataclass
+class Workload:
+    name: str
+    q: int
+    d: int
+    heads: int
+    dtype: str                 # "bf16" or "fp32"
+    kv_mode: str               # "shared" (K = V = H) or "separate"
+    cu_kv: np.ndarray          # int32 [R+1]
+    cu_cand: np.ndarray        # int32 [R+1]
+    Z: np.ndarray              # float32 [total_cand, q, d]
+    wt: np.ndarray             # float32 [q, d, d]  output-major W_Q
+    K: np.ndarray              # float32 [total_kv, d]  (= H in shared mode)
+    V: Optional[np.ndarray]    # float32 [total_kv, d] or None in shared mode
+    seed: int = 0
+    info: dict = field(default_factory=dict)
+
+    @property
+    def R(self) -> int:
+        return len(self.cu_kv) - 1
+
+    @property
+    def total_cand(self) -> int:
+        return int(self.cu_cand[-1])
+
+    @property
+    def total_kv(self) -> int:
+        return int(self.cu_kv[-1])
+
+    @property
+    def rows(self) -> int:
+        return self.total_cand * self.q
+
+    @property
+    def d_h(self) -> int:
+        return self.d // self.heads
+
+    @property
+    def lengths(self) -> np.ndarray:
+        return np.diff(self.cu_kv)
+
+    @property
+    def cands(self) -> np.ndarray:
+        return np.diff(self.cu_cand)
+
+    def flops(self) -> float:
+        """Algorithmic FLOPs of one pass: projection 2*rows*d*d plus
+        QK^T and PV, 4 * sum_r M_r * L_r * d."""
+        m = self.cands.astype(np.float64) * self.q
+        return 2.0 * self.rows * self.d * self.d + 4.0 * float(np.sum(m * self.lengths)) * self.d
+
+    def bytes(self) -> float:
+        """Algorithmic HBM bytes of one pass: K (and V), Z, W_Q, O, each once."""
+        b = 2 if self.dtype == "bf16" else 4
+        kv = (1 if self.kv_mode == "shared" else 2) * self.total_kv * self.d
+        return float(b * (kv + 2 * self.rows * self.d + self.q * self.d * self.d))
+
+
+def _normal(rng, shape, std=1.0):
+    a = rng.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        a *= np.float32(std)
+    return a
+
+
+def custom(name: str, lengths: Sequence[int], cands: Sequence[int], q: int, d: int,
+           heads: int, dtype: str = "bf16", kv_mode: str = "shared", seed: int = 0,
+           wq_std: Optional[float] = None, rng=None, info=None) -> Workload:
+    """Build a workload with the given per-request memory lengths and candidate
+    counts.  Draws H (or K then V), Z, then W_Q slots from ``rng`` (or from
+    ``default_rng(seed)``)."""
+    if rng is None:
+        rng = np.random.default_rng(seed)
+    lengths = np.asarray(lengths, dtype=np.int64)
+    cands = np.asarray(cands, dtype=np.int64)
+    assert lengths.shape == cands.shape
+    cu_kv = np.zeros(len(lengths) + 1, dtype=np.int32)
+    cu_kv[1:] = np.cumsum(lengths)
+    cu_cand = np.zeros(len(cands) + 1, dtype=np.int32)
+    cu_cand[1:] = np.cumsum(cands)
+    total_kv, total_cand = int(cu_kv[-1]), int(cu_cand[-1])
+    K = _normal(rng, (total_kv, d))
+    V = _normal(rng, (total_kv, d)) if kv_mode == "separate" else None
+    Z = _normal(rng, (total_cand, q, d))
+    wt = _normal(rng, (q, d, d), std=(wq_std if wq_std is not None else 1.0 / np.sqrt(d)))
+    if dtype == "bf16":
+        K = round_bf16(K)
+        V = round_bf16(V) if V is not None else None
+        Z = round_bf16(Z)
+        wt = round_bf16(wt)
+    elif dtype != "fp32":
+        raise ValueError("dtype must be bf16 or fp32")
+    return Workload(name=name, q=q, d=d, heads=heads, dtype=dtype, kv_mode=kv_mode,
+                    cu_kv=cu_kv, cu_cand=cu_cand, Z=Z, wt=wt, K=K, V=V, seed=seed,
+                    info=dict(info or {}))
+
+
+def _tiny(seed):
+    # 1 request, L = 64, d = 64 (2 heads x 32), K = V = H, 4 candidates x 3
+    # query tokens, W_Q ~ N(0, 1/64) per slot, fp32.
+    return custom("tiny_fp32", [64], [4], q=3, d=64, heads=2, dtype="fp32",
+                  kv_mode="shared", seed=seed)
+
+
+def _rest(seed):
+    # 8 requests, L ~ U{512..1024}, d = 256 (4 x 64), K = V = H, 256
+    # candidates x 3 TSP query tokens per request.
+    rng = np.random.default_rng(seed)
+    R = 8
+    lengths = rng.integers(512, 1025, size=R)
+    cands = np.full(R, 256)
+    return custom("rest_bf16", lengths, cands, q=3, d=256, heads=4, dtype="bf16",
+                  kv_mode="shared", seed=seed, rng=rng)
+
+
+def _long(seed):
+    # 4 requests, L = 16384, d = 512 (8 x 64), K = V = H, 512 candidates x 3.
+    rng = np.random.default_rng(seed)
+    R = 4
+    return custom("long_bf16", np.full(R, 16384), np.full(R, 512), q=3, d=512, heads=8,
+                  dtype="bf16", kv_mode="shared", seed=seed, rng=rng)
+
+
+def _transx(seed):
+    # 256 requests, 96 memory slots (64 recent + 32 chunk summaries), separate
+    # K and V, d = 256 (4 x 64), 1024 candidates x 1 query token.
+    rng = np.random.default_rng(seed)
+    R = 256
+    return custom("transx_bf16", np.full(R, 96), np.full(R, 1024), q=1, d=256, heads=4,
+                  dtype="bf16", kv_mode="separate", seed=seed, rng=rng,
+                  info={"recent": 64, "summaries": 32})
+
+
+def _ragged(seed):
+    # 64 users, L = clip(rint(exp(N(7.5, 0.6^2))), 256, 4096), candidates per
+    # user ~ U{1..64}, d = 256 (8 x 32), K = V = H, 3 TSP query tokens.
+    rng = np.random.default_rng(seed)
+    R = 64
+    lengths = np.clip(np.rint(np.exp(rng.normal(7.5, 0.6, size=R))), 256, 4096).astype(np.int64)
+    cands = rng.integers(1, 65, size=R)
+    return custom("ragged_bf16", lengths, cands, q=3, d=256, heads=8, dtype="bf16",
+                  kv_mode="shared", seed=seed, rng=rng)
+
+
+CONFIGS = {
+    "tiny": _tiny,       # 1 request, L=64, d=64, fp32
+    "rest": _rest,       # ReST-like serving batch, bf16
+    "long": _long,       # long history L=16384, d=512, bf16
+    "transx": _transx,   # TransX-like 96-slot memory, separate K/V, bf16
+    "ragged": _ragged,   # ragged shared-prefix training batch, bf16
+}
+
+
+def make(config: str, seed: int = 0) -> Workload:
+    """Generate one of the named workloads (see CONFIGS) with the given seed."""
+    try:
+        return CONFIGS[config](seed)
+    except KeyError:
+        raise ValueError("unknown config %r (choose from %s)" % (config, sorted(CONFIGS)))

@@ -1,0 +1,478 @@
+"""Pins for the fp64 CPU oracle (oracle/xattn_oracle.c).
+
+The oracle is the reference every GPU result is compared with, so it is first
+pinned to things other than itself:
+  * hand-derived closed-form cases stored under tests/golden/ (each cites the
+    passage and shows its derivation);
+  * library routines that compute the same definition by another route:
+    numpy matmul for the TSP projection, torch's CPU float64
+    scaled_dot_product_attention for the per-head attention;
+  * mathematical identities: softmax-of-one-row, identical keys, zero query,
+    two keys (logistic weight), the log-sum-exp gradient identity for K = V,
+    translation equivariance, key-permutation invariance, shared-prefix
+    equivalence (the pages' reason for sharing the memory), request
+    independence, softmax rows summing to 1, and the Gaussian large-L limit;
+  * integer plan: cu_q, row_req against numpy, tile coverage and ordering.
+A mutation test at the end plants plausible mistakes in copies of the oracle
+source and checks that these pins catch every one of them.
+"""
+import glob
+import importlib.util
+import json
+import os
+import shutil
+import tempfile
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import expit, logsumexp
+
+import oracle
+from shared_history_candidate_amd import workloads as W
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+GOLDEN = sorted(glob.glob(os.path.join(HERE, "golden", "*.json")))
+
+
+def _rand_case(rng, R=3, q=2, d=8, heads=2, kv_mode="separate", Lmax=9, Nmax=4):
+    lengths = rng.integers(1, Lmax + 1, size=R)
+    cands = rng.integers(1, Nmax + 1, size=R)
+    return W.custom("rand", lengths, cands, q=q, d=d, heads=heads, dtype="fp32",
+                    kv_mode=kv_mode, rng=rng)
+
+
+def _oracle_out(orc, wl, **kw):
+    return orc.forward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, wl.K, wl.V, **kw)
+
+
+# ----------------------------------------------------------------------------
+# Golden closed forms (hand-derived)
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("path", GOLDEN, ids=[os.path.basename(p) for p in GOLDEN])
+def test_golden_closed_forms(oracle_mod, path):
+    g = json.load(open(path))
+    assert g["source"] and g["derivation"]
+    V = np.array(g["V"]) if g["V"] is not None else None
+    O = oracle_mod.forward(g["cu_kv"], g["cu_cand"], g["q"], g["heads"], np.array(g["Z"]),
+                           np.array(g["wt"]), np.array(g["K"]), V)
+    np.testing.assert_allclose(O, np.array(g["O"]), rtol=g["rtol"], atol=1e-15)
+
+
+# ----------------------------------------------------------------------------
+# Library cross-checks
+# ----------------------------------------------------------------------------
+def _check_projection(orc, seed):
+    rng = np.random.default_rng(seed)
+    q, d, n = 3, 16, 7
+    Z = rng.standard_normal((n, q, d))
+    wt = rng.standard_normal((q, d, d))
+    Q = orc.project(Z, wt, q)
+    ref = np.stack([Z[:, s, :] @ wt[s].T for s in range(q)], axis=1)
+    return np.max(np.abs(Q - ref))
+
+
+def test_projection_matches_numpy_matmul(oracle_mod):
+    """Eq. (8): slot s of every candidate uses its own W_Q[s]."""
+    assert _check_projection(oracle_mod, 0) < 1e-12
+
+
+def _sdpa_reference(wl):
+    """Per request and head: torch CPU float64 scaled_dot_product_attention on
+    Q = Z W_Q[slot] (numpy matmul) and the head's column slices of K, V."""
+    d, dh, q = wl.d, wl.d_h, wl.q
+    Z = wl.Z.astype(np.float64).reshape(-1, q, d)
+    Q = np.stack([Z[:, s, :] @ wl.wt[s].astype(np.float64).T for s in range(q)], axis=1)
+    Q = Q.reshape(-1, d)
+    K = wl.K.astype(np.float64)
+    V = wl.V.astype(np.float64) if wl.V is not None else K
+    out = np.zeros_like(Q)
+    for r in range(wl.R):
+        rows = slice(int(wl.cu_cand[r]) * q, int(wl.cu_cand[r + 1]) * q)
+        kv = slice(int(wl.cu_kv[r]), int(wl.cu_kv[r + 1]))
+        if rows.stop == rows.start or kv.stop == kv.start:
+            continue
+        qt = torch.from_numpy(Q[rows]).reshape(-1, wl.heads, dh).transpose(0, 1).unsqueeze(0)
+        kt = torch.from_numpy(K[kv]).reshape(-1, wl.heads, dh).transpose(0, 1).unsqueeze(0)
+        vt = torch.from_numpy(V[kv]).reshape(-1, wl.heads, dh).transpose(0, 1).unsqueeze(0)
+        o = torch.nn.functional.scaled_dot_product_attention(qt.contiguous(), kt.contiguous(),
+                                                             vt.contiguous())
+        out[rows] = o.squeeze(0).transpose(0, 1).reshape(-1, d).numpy()
+    return out
+
+
+def _check_sdpa(orc, seed, kv_mode):
+    rng = np.random.default_rng(seed)
+    wl = _rand_case(rng, R=3, q=int(rng.integers(1, 4)), d=8,
+                    heads=int(rng.choice([1, 2, 4])), kv_mode=kv_mode)
+    return np.max(np.abs(_oracle_out(orc, wl) - _sdpa_reference(wl)))
+
+
+@pytest.mark.parametrize("kv_mode", ["shared", "separate"])
+@pytest.mark.parametrize("seed", range(6))
+def test_matches_torch_sdpa_float64(oracle_mod, seed, kv_mode):
+    assert _check_sdpa(oracle_mod, seed, kv_mode) < 1e-12
+
+
+def test_config_tiny_matches_torch_sdpa(oracle_mod):
+    wl = W.make("tiny", 0)
+    assert np.max(np.abs(_oracle_out(oracle_mod, wl) - _sdpa_reference(wl))) < 1e-12
+
+
+# ----------------------------------------------------------------------------
+# Closed forms and identities
+# ----------------------------------------------------------------------------
+def _check_single_row(orc, seed):
+    """L = 1: one weight equal to 1, so each head outputs the memory row's slice."""
+    rng = np.random.default_rng(seed)
+    wl = W.custom("l1", [1, 1], [3, 2], q=2, d=8, heads=4, dtype="fp32",
+                  kv_mode="separate", rng=rng)
+    O = _oracle_out(orc, wl)
+    ref = np.concatenate([np.repeat(wl.V[r:r + 1], wl.cands[r] * wl.q, 0) for r in range(2)])
+    return np.max(np.abs(O - ref))
+
+
+def test_single_memory_row(oracle_mod):
+    assert _check_single_row(oracle_mod, 1) == 0.0
+
+
+def _check_identical_keys(orc, seed):
+    """All keys equal: uniform weights, output = column mean of V."""
+    rng = np.random.default_rng(seed)
+    wl = W.custom("ik", [5], [3], q=2, d=8, heads=2, dtype="fp32", kv_mode="separate", rng=rng)
+    wl.K[:] = wl.K[0:1]
+    O = _oracle_out(orc, wl)
+    return np.max(np.abs(O - wl.V.astype(np.float64).mean(0, keepdims=True)))
+
+
+def test_identical_keys_give_mean_value(oracle_mod):
+    assert _check_identical_keys(oracle_mod, 2) < 1e-14
+
+
+def test_identical_memory_rows_pfkv(oracle_mod):
+    """K = V = H with all rows equal: the output is that row."""
+    rng = np.random.default_rng(3)
+    wl = W.custom("ir", [7], [2], q=3, d=8, heads=2, dtype="fp32", kv_mode="shared", rng=rng)
+    wl.K[:] = wl.K[0:1]
+    O = _oracle_out(oracle_mod, wl)
+    assert np.max(np.abs(O - wl.K[0:1].astype(np.float64))) < 1e-14
+
+
+def _check_zero_query(orc, seed):
+    """Z = 0 gives Q = 0 and uniform weights: output = mean of V rows per request."""
+    rng = np.random.default_rng(seed)
+    wl = W.custom("zq", [4, 6], [2, 3], q=2, d=8, heads=2, dtype="fp32",
+                  kv_mode="separate", rng=rng)
+    wl.Z[:] = 0
+    O = _oracle_out(orc, wl)
+    ref = np.concatenate([np.repeat(wl.V[wl.cu_kv[r]:wl.cu_kv[r + 1]].astype(np.float64)
+                                    .mean(0, keepdims=True), wl.cands[r] * wl.q, 0)
+                          for r in range(2)])
+    return np.max(np.abs(O - ref))
+
+
+def test_zero_query_gives_mean_value(oracle_mod):
+    assert _check_zero_query(oracle_mod, 4) < 1e-14
+
+
+def _check_two_keys(orc, seed):
+    """Two keys: weight of key 1 is the logistic function of s1 - s2."""
+    rng = np.random.default_rng(seed)
+    wl = W.custom("tk", [2], [3], q=1, d=4, heads=1, dtype="fp32", kv_mode="separate", rng=rng)
+    O = _oracle_out(orc, wl)
+    Q = wl.Z.astype(np.float64).reshape(-1, 4) @ wl.wt[0].astype(np.float64).T
+    K = wl.K.astype(np.float64)
+    V = wl.V.astype(np.float64)
+    s = Q @ K.T / 2.0  # sqrt(d_h) = 2
+    p1 = expit(s[:, 0] - s[:, 1])[:, None]
+    return np.max(np.abs(O - (p1 * V[0] + (1 - p1) * V[1])))
+
+
+def test_two_keys_logistic_weight(oracle_mod):
+    assert _check_two_keys(oracle_mod, 5) < 1e-15
+
+
+def _check_lse_gradient(orc, seed):
+    """With K = V = H the head output is sqrt(d_h) times the gradient of
+    q -> logsumexp(H_h q / sqrt(d_h)); compared by central differences of
+    scipy's logsumexp (an independent route to the same number)."""
+    rng = np.random.default_rng(seed)
+    d, heads = 8, 2
+    dh = d // heads
+    wl = W.custom("lse", [11], [2], q=1, d=d, heads=heads, dtype="fp32", kv_mode="shared", rng=rng)
+    O = _oracle_out(orc, wl)
+    Q = wl.Z.astype(np.float64).reshape(-1, d) @ wl.wt[0].astype(np.float64).T
+    H = wl.K.astype(np.float64)
+    err = 0.0
+    eps = 1e-6
+    for row in range(Q.shape[0]):
+        for h in range(heads):
+            Hh = H[:, h * dh:(h + 1) * dh]
+            qv = Q[row, h * dh:(h + 1) * dh]
+            f = lambda x: logsumexp(Hh @ x / np.sqrt(dh))
+            g = np.array([(f(qv + eps * np.eye(dh)[e]) - f(qv - eps * np.eye(dh)[e])) / (2 * eps)
+                          for e in range(dh)])
+            err = max(err, np.max(np.abs(O[row, h * dh:(h + 1) * dh] - np.sqrt(dh) * g)))
+    return err
+
+
+def test_logsumexp_gradient_identity(oracle_mod):
+    assert _check_lse_gradient(oracle_mod, 6) < 1e-8
+
+
+def _check_translation(orc, seed):
+    """PF-KV: adding u to every memory row shifts each score row by a constant
+    (weights unchanged) and shifts the values by u, so O -> O + u."""
+    rng = np.random.default_rng(seed)
+    wl = _rand_case(rng, R=2, q=2, d=8, heads=2, kv_mode="shared")
+    O = _oracle_out(orc, wl)
+    u = rng.standard_normal(8)
+    O2 = orc.forward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, wl.K + u)
+    return np.max(np.abs(O2 - (O + u)))
+
+
+def test_translation_equivariance_pfkv(oracle_mod):
+    assert _check_translation(oracle_mod, 7) < 1e-12
+
+
+def test_separate_kv_shift_rules(oracle_mod):
+    """Separate K/V: shifting all keys leaves O unchanged; shifting all values by u adds u."""
+    rng = np.random.default_rng(8)
+    wl = _rand_case(rng, R=2, q=2, d=8, heads=2, kv_mode="separate")
+    O = _oracle_out(oracle_mod, wl)
+    u = rng.standard_normal(8)
+    Ok = oracle_mod.forward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, wl.K + u, wl.V)
+    Ov = oracle_mod.forward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, wl.K, wl.V + u)
+    assert np.max(np.abs(Ok - O)) < 1e-12
+    assert np.max(np.abs(Ov - (O + u))) < 1e-12
+
+
+def _check_permutation(orc, seed):
+    """Permuting memory rows within each request (K and V jointly) leaves O unchanged."""
+    rng = np.random.default_rng(seed)
+    wl = _rand_case(rng, R=3, q=2, d=8, heads=2, kv_mode="separate")
+    O = _oracle_out(orc, wl)
+    perm = np.concatenate([wl.cu_kv[r] + rng.permutation(wl.lengths[r]) for r in range(wl.R)])
+    O2 = orc.forward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, wl.K[perm], wl.V[perm])
+    return np.max(np.abs(O2 - O))
+
+
+def test_key_permutation_invariance(oracle_mod):
+    assert _check_permutation(oracle_mod, 9) < 1e-13
+
+
+def _check_shared_prefix(orc, seed):
+    """ReST s.3.5 shared-prefix serving: scoring a request's N candidates against
+    one H equals N single-candidate requests that each carry a copy of H."""
+    rng = np.random.default_rng(seed)
+    wl = _rand_case(rng, R=2, q=3, d=8, heads=2, kv_mode="shared", Nmax=5)
+    O = _oracle_out(orc, wl)
+    Ks, lens, cands = [], [], []
+    for r in range(wl.R):
+        for _ in range(wl.cands[r]):
+            Ks.append(wl.K[wl.cu_kv[r]:wl.cu_kv[r + 1]])
+            lens.append(wl.lengths[r])
+            cands.append(1)
+    cu_kv = np.concatenate([[0], np.cumsum(lens)])
+    cu_c = np.concatenate([[0], np.cumsum(cands)])
+    O2 = orc.forward(cu_kv, cu_c, wl.q, wl.heads, wl.Z, wl.wt, np.concatenate(Ks))
+    return np.max(np.abs(O2 - O))
+
+
+def test_shared_prefix_equivalence(oracle_mod):
+    assert _check_shared_prefix(oracle_mod, 10) == 0.0
+
+
+def test_request_independence_and_order(oracle_mod):
+    """Requests do not interact: reversing the request order reverses the row blocks."""
+    rng = np.random.default_rng(11)
+    wl = _rand_case(rng, R=4, q=2, d=8, heads=2, kv_mode="separate")
+    O = _oracle_out(oracle_mod, wl)
+    order = list(range(wl.R))[::-1]
+    kv_idx = np.concatenate([np.arange(wl.cu_kv[r], wl.cu_kv[r + 1]) for r in order])
+    c_idx = np.concatenate([np.arange(wl.cu_cand[r], wl.cu_cand[r + 1]) for r in order])
+    cu_kv = np.concatenate([[0], np.cumsum(wl.lengths[order])])
+    cu_c = np.concatenate([[0], np.cumsum(wl.cands[order])])
+    O2 = oracle_mod.forward(cu_kv, cu_c, wl.q, wl.heads, wl.Z[c_idx], wl.wt, wl.K[kv_idx],
+                            wl.V[kv_idx])
+    rows = (c_idx[:, None] * wl.q + np.arange(wl.q)[None]).reshape(-1)
+    assert np.array_equal(O2, O[rows])
+
+
+def test_softmax_rows_sum_to_one(oracle_mod):
+    rng = np.random.default_rng(12)
+    wl = _rand_case(rng, R=2, q=2, d=8, heads=2, kv_mode="shared")
+    for row in range(wl.rows):
+        for h in range(wl.heads):
+            p = oracle_mod.probs(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, wl.K, row, h)
+            assert np.all(p >= 0)
+            assert abs(p.sum() - 1.0) < 1e-12
+
+
+def test_gaussian_large_memory_limit(oracle_mod):
+    """K = V = H ~ N(0, I): as L grows the softmax-weighted mean tends to the
+    exponentially tilted Gaussian mean q_h / sqrt(d_h) (loose statistical check;
+    it catches a wrong score scale such as 1/sqrt(d) instead of 1/sqrt(d_h))."""
+    rng = np.random.default_rng(13)
+    wl = W.custom("big", [8192], [8], q=1, d=256, heads=4, dtype="fp32", kv_mode="shared", rng=rng)
+    O = _oracle_out(oracle_mod, wl)
+    Q = wl.Z.astype(np.float64).reshape(-1, 256) @ wl.wt[0].astype(np.float64).T
+    slope = float(np.sum(O * Q) / np.sum(Q * Q))
+    # 1/sqrt(d_h) = 0.125; the 1/sqrt(d) reading would give 0.0625.
+    assert abs(slope - 0.125) < 0.0125
+    assert np.mean(np.abs(O - Q / np.sqrt(64))) < 0.05
+
+
+def test_thread_count_independence(oracle_mod):
+    rng = np.random.default_rng(14)
+    wl = _rand_case(rng, R=5, q=3, d=16, heads=4, kv_mode="shared", Lmax=40, Nmax=9)
+    oracle_mod.set_threads(1)
+    O1 = _oracle_out(oracle_mod, wl)
+    oracle_mod.set_threads(4)
+    O4 = _oracle_out(oracle_mod, wl)
+    oracle_mod.set_threads(os.cpu_count() or 1)
+    assert np.array_equal(O1, O4)
+
+
+def test_row_subset_matches_full(oracle_mod):
+    rng = np.random.default_rng(15)
+    wl = _rand_case(rng, R=3, q=2, d=8, heads=2, kv_mode="separate")
+    O = _oracle_out(oracle_mod, wl)
+    rows = [0, wl.rows - 1, wl.rows // 2]
+    assert np.array_equal(_oracle_out(oracle_mod, wl, rows=rows), O[rows])
+
+
+# ----------------------------------------------------------------------------
+# Integer plan
+# ----------------------------------------------------------------------------
+def check_plan(cu_kv, cu_cand, q, tile_m, cu_q, row_req, tiles):
+    """Properties that define the plan: cu_q = q*cu_cand, row_req is the
+    range map, tiles cover every query row exactly once with nc <= tile_m,
+    ordered by request length descending (ties by index), then block, then slot."""
+    cu_kv = np.asarray(cu_kv)
+    cu_cand = np.asarray(cu_cand)
+    R = len(cu_kv) - 1
+    L = np.diff(cu_kv)
+    N = np.diff(cu_cand)
+    assert np.array_equal(cu_q, q * cu_cand)
+    if row_req is not None:
+        assert np.array_equal(row_req, np.repeat(np.arange(R), N * q))
+    cover = np.zeros(int(cu_cand[-1]) * q, dtype=np.int64)
+    for (r, s, c0, nc) in tiles:
+        assert 0 <= r < R and 0 <= s < q and 0 < nc <= tile_m
+        assert cu_cand[r] <= c0 and c0 + nc <= cu_cand[r + 1]
+        assert (c0 - cu_cand[r]) % tile_m == 0
+        cover[(np.arange(c0, c0 + nc)) * q + s] += 1
+    assert np.all(cover == 1)
+    keys = [(-L[r], r, c0, s) for (r, s, c0, nc) in tiles]
+    assert keys == sorted(keys)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_plan_properties(oracle_mod, seed):
+    rng = np.random.default_rng(seed)
+    R = int(rng.integers(1, 20))
+    L = rng.integers(0, 50, size=R)
+    L[rng.integers(0, R)] = L[0]  # force a tie
+    N = rng.integers(0, 200, size=R)
+    cu_kv = np.concatenate([[0], np.cumsum(L)])
+    cu_c = np.concatenate([[0], np.cumsum(N)])
+    for q in (1, 3):
+        for tm in (16, 64):
+            cu_q, row_req, tiles = oracle_mod.plan(cu_kv, cu_c, q, tm)
+            check_plan(cu_kv, cu_c, q, tm, cu_q, row_req, tiles)
+            assert len(tiles) == sum(q * ((n + tm - 1) // tm) for n in N)
+
+
+def test_plan_configs(oracle_mod):
+    for name in ("rest", "ragged"):
+        wl = W.make(name, 0)
+        cu_q, row_req, tiles = oracle_mod.plan(wl.cu_kv, wl.cu_cand, wl.q, 64)
+        check_plan(wl.cu_kv, wl.cu_cand, wl.q, 64, cu_q, row_req, tiles)
+
+
+# ----------------------------------------------------------------------------
+# Mutation test: plausible mistakes planted in copies of the oracle are caught
+# ----------------------------------------------------------------------------
+MUTANTS = {
+    "scale_uses_d": ("1.0 / sqrt((double)d_h)", "1.0 / sqrt((double)d)"),
+    "slot_ignored": ("wt + (size_t)(row % q) * d * d", "wt + (size_t)0 * d * d"),
+    "weight_transposed": ("Z[(size_t)row * d + i] * w[(size_t)o * d + i]",
+                          "Z[(size_t)row * d + i] * w[(size_t)i * d + o]"),
+    "key_head_offset_dropped": ("K[(size_t)(kv0 + j) * d + head * d_h + e]",
+                                "K[(size_t)(kv0 + j) * d + e]"),
+    "value_head_offset_dropped": ("Vm[(size_t)(kv0 + j) * d + h * d_h + e]",
+                                  "Vm[(size_t)(kv0 + j) * d + e]"),
+    "separate_value_ignored": ("const double *Vm = V ? V : K;", "const double *Vm = K;"),
+    "last_key_dropped": ("for (int j = 0; j < L; ++j) {\n        double s = 0.0;",
+                         "for (int j = 0; j < L - 1; ++j) {\n        double s = 0.0;"),
+    "no_normalisation": ("p[j] /= z;", "p[j] /= 1.0;"),
+    "sign_of_max": ("p[j] = exp(p[j] - m);", "p[j] = exp(m - p[j]);"),
+    "wrong_request_base": ("const int kv0 = cu_kv[r], L = cu_kv[r + 1] - cu_kv[r];\n                /* Q",
+                           "const int kv0 = 0, L = cu_kv[r + 1] - cu_kv[r];\n                /* Q"),
+}
+
+
+def _all_pins(orc):
+    """Run every pin above against an oracle module; return the failing ones."""
+    fails = []
+    checks = {
+        "projection": lambda: _check_projection(orc, 0) < 1e-12,
+        "sdpa_shared": lambda: all(_check_sdpa(orc, s, "shared") < 1e-12 for s in range(3)),
+        "sdpa_separate": lambda: all(_check_sdpa(orc, s, "separate") < 1e-12 for s in range(3)),
+        "single_row": lambda: _check_single_row(orc, 1) == 0.0,
+        "identical_keys": lambda: _check_identical_keys(orc, 2) < 1e-14,
+        "zero_query": lambda: _check_zero_query(orc, 4) < 1e-14,
+        "two_keys": lambda: _check_two_keys(orc, 5) < 1e-15,
+        "lse_gradient": lambda: _check_lse_gradient(orc, 6) < 1e-8,
+        "translation": lambda: _check_translation(orc, 7) < 1e-12,
+        "permutation": lambda: _check_permutation(orc, 9) < 1e-13,
+        "shared_prefix": lambda: _check_shared_prefix(orc, 10) == 0.0,
+    }
+    for path in GOLDEN:
+        g = json.load(open(path))
+        V = np.array(g["V"]) if g["V"] is not None else None
+
+        def gold(g=g, V=V):
+            O = orc.forward(g["cu_kv"], g["cu_cand"], g["q"], g["heads"], np.array(g["Z"]),
+                            np.array(g["wt"]), np.array(g["K"]), V)
+            return np.allclose(O, np.array(g["O"]), rtol=max(g["rtol"], 1e-15), atol=1e-15)
+        checks["golden:" + os.path.basename(path)] = gold
+    for name, fn in checks.items():
+        try:
+            ok = bool(fn())
+        except Exception:
+            ok = False
+        if not ok:
+            fails.append(name)
+    return fails
+
+
+def _load_mutant(tmpdir, name, old, new):
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "xattn_oracle.c")).read()
+    assert src.count(old) >= 1, "mutation anchor for %s not found" % name
+    msrc = os.path.join(tmpdir, "mut_%s.c" % name)
+    open(msrc, "w").write(src.replace(old, new))
+    spec = importlib.util.spec_from_file_location("oracle_mut_" + name,
+                                                  os.path.join(os.path.dirname(oracle.__file__),
+                                                               "__init__.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    mod._SRC = msrc
+    mod._LIB = os.path.join(tmpdir, "libmut_%s.so" % name)
+    mod.build(force=True)
+    return mod
+
+
+def test_unmutated_oracle_passes_all_pins(oracle_mod):
+    assert _all_pins(oracle_mod) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name):
+    tmpdir = tempfile.mkdtemp(prefix="oracle_mut_")
+    try:
+        mod = _load_mutant(tmpdir, name, *MUTANTS[name])
+        assert _all_pins(mod), "mutant %s passed every pin" % name
+    finally:
+        shutil.rmtree(tmpdir, ignore_errors=True)
