@@ -1,0 +1,202 @@
+#!/usr/bin/env python3
+"""Benchmark of shared-history cross-attention on one MI355X.
+
+One step = one xattn_forward call over one batch of synthetic inputs resident
+in HBM: the varlen planner plus the fused TSP-projection + attention kernel.
+Default workload: the ReST-like serving batch (8 requests, history length
+U{512..1024}, d = 256 as 4 heads x 64, 256 candidates x 3 query tokens, bf16).
+
+Prints one JSON line with the whole-step throughput (candidate-queries/s),
+the dominant kernel's roofline fraction (its average launch duration measured
+with HIP events on the launch stream), and the fp64 CPU oracle timed on a
+bounded sample of the same workload on this host's cores.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+# workload name -> roofline bound of the fused kernel on that workload
+BOUND = {"rest": "mfma", "long": "mfma", "transx": "hbm", "ragged": "hbm", "tiny": "alu"}
+KERNEL_SOURCES = ["shared_history_candidate_amd/csrc/attn_bf16.hip",
+                  "shared_history_candidate_amd/csrc/common.h"]
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", default="rest", choices=sorted(BOUND))
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="target CPU time of the oracle baseline sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="run only a plain device copy of this many MiB (counter calibration)")
+    return p.parse_args()
+
+
+def kernel_sha():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(config, dispatches_per_step=1):
+    """HBM bytes per launch of the fused kernel from committed rocprofv3 counter
+    runs (FETCH_SIZE, WRITE_SIZE scaled by a copy-kernel calibration), or None
+    when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "counters_attn_%s.json" % config)
+    if not os.path.exists(path):
+        return None
+    c = json.load(open(path))
+    if c.get("kernel_source_sha") != kernel_sha():
+        return None
+    return (c["fetch_kib"] + c["write_kib"]) * 1024.0 * c["copy_calibration"]
+
+
+def cpu_baseline(wl, target_s):
+    """The fp64 oracle as it stands, timed on this host on a bounded sample of
+    the workload's query rows (grown until it takes about target_s)."""
+    import numpy as np
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    oracle.set_threads(threads)
+    rng = np.random.default_rng(1)
+    n = min(wl.rows, 64)
+    done, elapsed, runs = 0, 0.0, 0
+    while True:
+        rows = np.sort(rng.choice(wl.rows, size=n, replace=False)) if n < wl.rows else None
+        t0 = time.perf_counter()
+        oracle.forward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, wl.K, wl.V, rows=rows)
+        dt = time.perf_counter() - t0
+        done += n
+        elapsed += dt
+        runs += 1
+        if elapsed >= target_s:
+            break
+        if n < wl.rows:
+            per_row = dt / n
+            n = int(min(wl.rows, max(n * 2, (target_s - elapsed) / max(per_row, 1e-9))))
+    if runs == 1 and n == wl.rows:
+        sample = "all %d query rows once" % wl.rows
+    else:
+        sample = "%d query rows in %d oracle calls (random rows of the same batch, full rows " \
+                 "of the batch when it fits)" % (done, runs)
+    return {"value": done / elapsed, "unit": "candidate-queries/s", "cores": threads,
+            "kind": "oracle", "sample": sample, "seconds": round(elapsed, 2)}
+
+
+def calib_copy(mib):
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes_read": n * 4, "calib_copy_bytes_written": n * 4,
+                      "launches": 5}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
+              "(requests shard across GPUs with no exchange; see DESIGN.md). Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.calib_copy_mib:
+        calib_copy(args.calib_copy_mib)
+        return
+
+    import numpy as np
+    import torch
+    from shared_history_candidate_amd import workloads as W
+    from shared_history_candidate_amd import xattn as X
+
+    wl = W.make(args.config, args.seed)
+    print("bench: workload %s R=%d rows=%d total_kv=%d d=%d heads=%d" %
+          (wl.name, wl.R, wl.rows, wl.total_kv, wl.d, wl.heads), file=sys.stderr, flush=True)
+    ctx = X.XAttn(wl.d, wl.q, wl.dtype, wl.kv_mode)
+    t = X.to_device(wl)
+    ws = ctx.alloc_workspace(wl.R, wl.total_cand, wl.heads)
+    O = torch.empty((wl.total_cand, wl.q, wl.d), dtype=ctx.torch_dtype, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ctx.forward(t["Z"], t["W_Q"], t["K"], t["V"], t["cu_kv"], t["cu_cand"], wl.heads,
+                    O=O, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    print("bench: %d steps, %.4f ms/step" % (args.steps, ms_per_step), file=sys.stderr, flush=True)
+
+    # Dominant kernel alone: the fused attention kernel over the plan the last
+    # step left in the workspace, one event pair per launch on its stream.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        ctx.attend(t["Z"], t["W_Q"], t["K"], t["V"], t["cu_kv"], t["cu_cand"], wl.heads, ws,
+                   O=O, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    print("bench: attention kernel %.4f ms/launch" % kern_ms, file=sys.stderr, flush=True)
+
+    flops, nbytes = wl.flops(), wl.bytes()
+    bound = BOUND[args.config]
+    if bound == "mfma":
+        achieved, peak, unit = flops / (kern_ms * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    elif bound == "hbm":
+        achieved, peak, unit = nbytes / (kern_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
+    else:
+        achieved, peak, unit = flops / (kern_ms * 1e-3) / 1e12, PEAK_FP32_TFLOPS, "TFLOP/s"
+    roof = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 5), "traffic": traffic_for(args.config),
+            "kernel": "attn_bf16_kernel" if wl.dtype == "bf16" else "attn_f32_kernel",
+            "kernel_ms": round(kern_ms, 5),
+            "algorithmic_flops": flops, "algorithmic_bytes": nbytes}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: timing the fp64 oracle on the host", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+
+    value = wl.rows / (ms_per_step * 1e-3)
+    line = {
+        "metric": "candidate-queries scored/sec", "value": round(value, 1),
+        "unit": "candidate-queries/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "requests": wl.R, "candidates": wl.total_cand,
+                   "query_tokens": wl.q, "memory_rows": wl.total_kv, "d": wl.d,
+                   "heads": wl.heads, "kv_mode": wl.kv_mode, "seed": args.seed},
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

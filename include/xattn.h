@@ -1,0 +1,206 @@
+/*
+ * xattn - one-history-to-many-candidates cross-attention on AMD Instinct
+ * MI355X (gfx950).  C ABI.
+ *
+ * What it computes.  A batch holds R requests.  Request r owns L_r memory rows
+ * (its shared history) and N_r candidates; every candidate carries q query
+ * tokens.  For query row `row = c*q + s` of candidate c in request r (slot s):
+ *
+ *     Q[row]          = Z[row] . W_Q[s]                              (TSP)
+ *     O[row, head h]  = softmax( Q_h K_r,h^T / sqrt(d_h) ) V_r,h       (Eq. 7)
+ *
+ * with heads splitting the d feature columns contiguously, d_h = d / heads.
+ * Sources (the pages on the subject):
+ *   - ReST reading note (paper-archivist), s.3.3.1 Eq. (7): projection-free
+ *     K/V - the encoder output H is used as both K and V, so per-candidate
+ *     work has no W_K / W_V.  The output gate and W_o of Eq. (7) are left to
+ *     the caller: O is the concatenated multi-head attention output.
+ *   - ReST reading note, s.3.3.2 Eq. (8): token-specific parameterisation -
+ *     each query-token type (slot) s has its own W_Q[s].
+ *   - ReST reading note, s.3.5: shared-prefix serving - H is computed once per
+ *     request and all N candidates' query tokens are decoded against it.
+ *   - TransX technical report (paper-daily), s.2: a compact behaviour memory
+ *     turned into separate keys and values that every candidate's query
+ *     cross-attends (XATTN_KV_SEPARATE).
+ *   - HELIX card (ai-papers-daily, "Sequence Modeling"): candidate-independent
+ *     KV cache, candidate side does cross-attention only, padding-free
+ *     variable-length execution (the ragged cu_* offsets below).
+ *
+ * Conventions.
+ *   - Every tensor is row-major, device-resident and owned by the caller.
+ *     Element type is bf16 (XATTN_BF16) or fp32 (XATTN_FP32) for Z, W_Q, K, V
+ *     and O alike; offsets are int32.
+ *   - Z     [total_cand][q][d]   query tokens; row c*q+s is slot s of cand c.
+ *   - W_Q   [q][d][d]            output-major: W_Q[s][o][i] multiplies Z[.][i]
+ *                                into Q[.][o] (W_Q[s] of Eq. (7) transposed,
+ *                                the layout of a PyTorch Linear weight).
+ *   - K     [total_kv][d]        memory rows; this is H in XATTN_KV_SHARED.
+ *   - V     [total_kv][d]        values (XATTN_KV_SEPARATE); must be NULL in
+ *                                XATTN_KV_SHARED, where V = K = H.
+ *   - cu_seqlens_kv [R+1]        cu[0] = 0, non-decreasing, cu[R] = total_kv;
+ *                                request r's memory rows are
+ *                                [cu_seqlens_kv[r], cu_seqlens_kv[r+1]).
+ *   - cu_cand       [R+1]        cu[0] = 0, non-decreasing,
+ *                                cu[R] = total_cand; request r's candidates.
+ *   - O     [total_cand][q][d]   output, heads concatenated by column.
+ *   - A request with L_r = 0 gets all-zero output rows (the pages route users
+ *     without memory to a fallback model; zero is this library's convention).
+ *     A request with N_r = 0 produces no rows.  No mask: every query row
+ *     attends to all L_r rows of its request.
+ *   - Precision: XATTN_BF16 multiplies bf16 operands into fp32 accumulators
+ *     on the matrix cores; Q and the softmax weights are rounded to bf16 for
+ *     the second and third products; O is rounded to bf16 (nearest-even).
+ *     XATTN_FP32 computes in fp32 throughout.
+ *
+ * Supported: d_h = d / heads in {32, 64, 128} for bf16 (1..128 for fp32),
+ * q in [1, 64], d a multiple of 32 for bf16, R >= 0.
+ *
+ * Errors.  Every entry point returns an xattn_status.  Problems visible on
+ * the host (NULL pointers, bad sizes, unsupported shapes, a workspace that is
+ * too small) return before anything is enqueued.  Launch failures return
+ * XATTN_EHIP.  xattn_last_error() describes the last failure on the calling
+ * thread.  The device re-checks the offset arrays (cu[0] = 0, non-decreasing,
+ * cu[R] equal to the totals passed on the host) before any kernel reads
+ * through them; on a mismatch it computes nothing and raises a flag in the
+ * workspace that xattn_device_error() reads back.
+ *
+ * Streams and threads.  Work is enqueued on `stream` (a hipStream_t; NULL is
+ * the default stream) and returns without synchronising.  A context may be
+ * used from one thread at a time; separate contexts are independent.  The
+ * workspace must not be shared by calls that may run concurrently.  No entry
+ * point except xattn_create / xattn_destroy allocates or frees memory.
+ */
+#ifndef XATTN_H
+#define XATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct xattn_ctx xattn_ctx;
+
+typedef enum {
+    XATTN_OK = 0,
+    XATTN_EINVAL = -1,        /* invalid argument; nothing enqueued            */
+    XATTN_EUNSUPPORTED = -2,  /* valid but not supported (e.g. d_h = 48, bf16) */
+    XATTN_EHIP = -3,          /* HIP runtime error                             */
+    XATTN_EWORKSPACE = -4     /* workspace NULL or smaller than required       */
+} xattn_status;
+
+typedef enum { XATTN_BF16 = 0, XATTN_FP32 = 1 } xattn_dtype;
+
+typedef enum {
+    XATTN_KV_SHARED = 0,   /* K = V = H, projection-free (ReST Eq. (7))       */
+    XATTN_KV_SEPARATE = 1  /* separate K and V memory (TransX behaviour memory) */
+} xattn_kv_mode;
+
+typedef struct {
+    int32_t d_model;        /* d: model width (query, key and value width)   */
+    int32_t n_slots;        /* q: query tokens per candidate (TSP slots)      */
+    xattn_dtype dtype;
+    xattn_kv_mode kv_mode;
+    int32_t device;         /* HIP device ordinal the context launches on     */
+} xattn_config;
+
+/* Create a context.  Validates cfg (d_model >= 1, 1 <= n_slots <= 64, known
+ * dtype and kv_mode, device >= 0) and copies it; allocates only the handle.
+ * Returns XATTN_EINVAL (and *out = NULL) on a bad config. */
+xattn_status xattn_create(const xattn_config* cfg, xattn_ctx** out);
+
+/* Destroy a context created by xattn_create.  NULL is allowed. */
+void xattn_destroy(xattn_ctx* ctx);
+
+/* Bytes of device workspace xattn_forward needs for a batch of
+ * `num_requests` requests, `total_cand` candidates and `heads` heads
+ * (a plan header plus one 16-byte work item per query tile).  Returns 0 on
+ * invalid arguments. */
+size_t xattn_workspace_size(const xattn_ctx* ctx, int32_t num_requests,
+                            int32_t total_cand, int32_t heads);
+
+/* Shared-history cross-attention forward (Eq. (7) attention with Eq. (8)
+ * per-slot W_Q; layouts and precision in the header comment).  Enqueues the
+ * varlen planner and the fused projection + attention kernel on `stream`.
+ * `workspace` is device memory of at least xattn_workspace_size() bytes,
+ * owned by the caller; its contents on entry are ignored.
+ * Errors: XATTN_EINVAL for NULL pointers / negative counts / heads not
+ * dividing d / V given in shared mode or missing in separate mode;
+ * XATTN_EUNSUPPORTED for an unsupported d_h; XATTN_EWORKSPACE for a small
+ * workspace; XATTN_EHIP for a launch failure. */
+xattn_status xattn_forward(xattn_ctx* ctx,
+                           const void* Z, const void* W_Q,
+                           const void* K, const void* V,
+                           const int32_t* cu_seqlens_kv, const int32_t* cu_cand,
+                           int32_t num_requests, int32_t total_cand,
+                           int32_t total_kv, int32_t heads,
+                           void* O, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* Attention alone: the fused projection + attention kernel of xattn_forward,
+ * reading the plan that a previous xattn_plan or xattn_forward call left in
+ * `workspace` for the SAME offsets and shape arguments (a decoder with several
+ * cross-attention layers over one batch plans once and attends per layer).
+ * Arguments and errors as for xattn_forward.  If the workspace holds the plan
+ * of a different batch shape (another candidates-per-tile size), the kernel
+ * computes nothing; a plan of a different batch with the same tile size gives
+ * undefined output. */
+xattn_status xattn_attend(xattn_ctx* ctx,
+                          const void* Z, const void* W_Q,
+                          const void* K, const void* V,
+                          const int32_t* cu_seqlens_kv, const int32_t* cu_cand,
+                          int32_t num_requests, int32_t total_cand,
+                          int32_t total_kv, int32_t heads,
+                          void* O, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Varlen plan alone (integer outputs, for callers that want the row map and
+ * for tests).  Writes, on the device:
+ *   cu_q[r]      = q * cu_cand[r]                (R+1 entries)
+ *   row_req[row] = r for cu_q[r] <= row < cu_q[r+1]   (total_cand*q entries;
+ *                  may be NULL)
+ *   tiles        = work items {r, s, c0, nc} (4 int32 each): candidates
+ *                  [c0, c0+nc) of request r, slot s, nc <= *tile_m, covering
+ *                  every query row once, ordered by L_r descending (ties by
+ *                  r), then candidate block, then slot.  Capacity
+ *                  xattn_max_tiles() entries.
+ *   n_tiles[0]   = number of tiles (device int32).
+ * *tile_m (host) receives the candidates-per-tile used by xattn_forward for
+ * this batch shape.  `workspace` as for xattn_forward. */
+xattn_status xattn_plan(xattn_ctx* ctx,
+                        const int32_t* cu_seqlens_kv, const int32_t* cu_cand,
+                        int32_t num_requests, int32_t total_cand,
+                        int32_t total_kv, int32_t heads,
+                        int32_t* cu_q, int32_t* row_req, int32_t* tiles,
+                        int32_t* n_tiles, int32_t* tile_m,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Upper bound on the number of tiles xattn_plan can emit for this shape. */
+int64_t xattn_max_tiles(const xattn_ctx* ctx, int32_t num_requests,
+                        int32_t total_cand, int32_t heads);
+
+/* TSP query projection alone (Eq. (8) applied to W_Q of Eq. (7)):
+ * Q[row] = Z[row] . W_Q[row % q], Q [total_cand][q][d] in the context's
+ * dtype (bf16: fp32 accumulation, rounded to nearest-even).  xattn_forward
+ * computes the same projection inside its attention kernel; this entry point
+ * exposes it on its own. */
+xattn_status xattn_project(xattn_ctx* ctx, const void* Z, const void* W_Q,
+                           int32_t total_cand, void* Q, void* stream);
+
+/* Synchronise `stream` and read the device-side validation flag a previous
+ * xattn_forward / xattn_plan left in `workspace`: *flag = 0 when the offset
+ * arrays were consistent, otherwise a bitmask (1: cu_seqlens_kv, 2: cu_cand).
+ * Clears nothing. */
+xattn_status xattn_device_error(xattn_ctx* ctx, const void* workspace,
+                                int32_t* flag, void* stream);
+
+/* Text describing the last failure on the calling thread ("" if none).
+ * Valid until the next xattn call on this thread. */
+const char* xattn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* XATTN_H */

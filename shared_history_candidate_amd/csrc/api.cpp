@@ -1,0 +1,272 @@
+// C-ABI surface of libxattn: argument validation, workspace sizing, tile-size
+// choice and kernel dispatch.  The operation and the conventions are stated in
+// include/xattn.h.
+#include "xattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <new>
+#include <string>
+
+#include "internal.h"
+#include "plan_layout.h"
+
+struct xattn_ctx {
+    xattn_config cfg;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+xattn_status fail(xattn_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+xattn_status hip_fail(hipError_t e, const char* what) {
+    return fail(XATTN_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool bf16_dh_supported(int dh) { return dh == 32 || dh == 64 || dh == 128; }
+
+// Waves per work-group for the bf16 kernel (each wave owns 32 candidates of
+// one slot).  Four waves share each staged memory tile among more queries;
+// two waves give twice the work-groups.  Use four when the batch still
+// yields at least two work-groups per compute unit.
+int choose_waves(const xattn_config& c, int R, int total_cand, int heads) {
+    if (c.dtype != XATTN_BF16) return 1;
+    const int64_t wg4 = (int64_t)c.n_slots * heads * ((int64_t)total_cand / 128 + R);
+    return wg4 >= 512 ? 4 : 2;
+}
+
+int tile_m_for(const xattn_config& c, int R, int total_cand, int heads) {
+    if (c.dtype != XATTN_BF16) return 64;
+    return 32 * choose_waves(c, R, total_cand, heads);
+}
+
+int64_t max_tiles_for(const xattn_config& c, int R, int total_cand, int tile_m) {
+    // sum_r ceil(N_r / tile_m) <= (total_cand + R * (tile_m - 1)) / tile_m
+    return (int64_t)c.n_slots * (((int64_t)total_cand + (int64_t)R * (tile_m - 1)) / tile_m);
+}
+
+struct DeviceGuard {
+    int prev = -1;
+    hipError_t err = hipSuccess;
+    explicit DeviceGuard(int dev) {
+        err = hipGetDevice(&prev);
+        if (err == hipSuccess && prev != dev) err = hipSetDevice(dev);
+        else if (err == hipSuccess) prev = -1;
+    }
+    ~DeviceGuard() {
+        if (prev >= 0) (void)hipSetDevice(prev);
+    }
+};
+
+xattn_status check_shape(const xattn_ctx* ctx, int R, int total_cand, int total_kv, int heads) {
+    if (!ctx) return fail(XATTN_EINVAL, "ctx is NULL");
+    if (R < 0 || total_cand < 0 || total_kv < 0)
+        return fail(XATTN_EINVAL, "negative count (num_requests=%d total_cand=%d total_kv=%d)", R,
+                    total_cand, total_kv);
+    if (heads < 1 || ctx->cfg.d_model % heads != 0)
+        return fail(XATTN_EINVAL, "heads=%d must be >= 1 and divide d_model=%d", heads,
+                    ctx->cfg.d_model);
+    const int dh = ctx->cfg.d_model / heads;
+    if (ctx->cfg.dtype == XATTN_BF16 && !bf16_dh_supported(dh))
+        return fail(XATTN_EUNSUPPORTED, "bf16 path supports d_h in {32, 64, 128}, got %d", dh);
+    if (ctx->cfg.dtype == XATTN_FP32 && dh > 128)
+        return fail(XATTN_EUNSUPPORTED, "fp32 path supports d_h <= 128, got %d", dh);
+    if (R > xattn::kPlanMaxRequests)
+        return fail(XATTN_EUNSUPPORTED, "num_requests=%d exceeds the planner limit %d", R,
+                    xattn::kPlanMaxRequests);
+    if ((int64_t)total_cand * ctx->cfg.n_slots > INT32_MAX)
+        return fail(XATTN_EUNSUPPORTED, "total_cand * q exceeds int32");
+    return XATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* xattn_last_error(void) { return g_last_error.c_str(); }
+
+xattn_status xattn_create(const xattn_config* cfg, xattn_ctx** out) {
+    g_last_error.clear();
+    if (!out) return fail(XATTN_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (!cfg) return fail(XATTN_EINVAL, "cfg is NULL");
+    if (cfg->d_model < 1) return fail(XATTN_EINVAL, "d_model=%d must be >= 1", cfg->d_model);
+    if (cfg->n_slots < 1 || cfg->n_slots > 64)
+        return fail(XATTN_EINVAL, "n_slots=%d must be in [1, 64]", cfg->n_slots);
+    if (cfg->dtype != XATTN_BF16 && cfg->dtype != XATTN_FP32)
+        return fail(XATTN_EINVAL, "unknown dtype %d", (int)cfg->dtype);
+    if (cfg->kv_mode != XATTN_KV_SHARED && cfg->kv_mode != XATTN_KV_SEPARATE)
+        return fail(XATTN_EINVAL, "unknown kv_mode %d", (int)cfg->kv_mode);
+    if (cfg->device < 0) return fail(XATTN_EINVAL, "device=%d must be >= 0", cfg->device);
+    if (cfg->dtype == XATTN_BF16 && cfg->d_model % 32 != 0)
+        return fail(XATTN_EUNSUPPORTED, "bf16 path needs d_model %% 32 == 0, got %d",
+                    cfg->d_model);
+    xattn_ctx* ctx = new (std::nothrow) xattn_ctx;
+    if (!ctx) return fail(XATTN_EINVAL, "out of host memory");
+    ctx->cfg = *cfg;
+    *out = ctx;
+    return XATTN_OK;
+}
+
+void xattn_destroy(xattn_ctx* ctx) { delete ctx; }
+
+int64_t xattn_max_tiles(const xattn_ctx* ctx, int32_t R, int32_t total_cand, int32_t heads) {
+    if (!ctx || R < 0 || total_cand < 0 || heads < 1) return 0;
+    return max_tiles_for(ctx->cfg, R, total_cand, tile_m_for(ctx->cfg, R, total_cand, heads));
+}
+
+size_t xattn_workspace_size(const xattn_ctx* ctx, int32_t R, int32_t total_cand, int32_t heads) {
+    if (!ctx || R < 0 || total_cand < 0 || heads < 1) return 0;
+    return (size_t)xattn::kPlanHeaderBytes + 16 * (size_t)xattn_max_tiles(ctx, R, total_cand, heads);
+}
+
+xattn_status xattn_plan(xattn_ctx* ctx, const int32_t* cu_kv, const int32_t* cu_cand, int32_t R,
+                        int32_t total_cand, int32_t total_kv, int32_t heads, int32_t* cu_q,
+                        int32_t* row_req, int32_t* tiles, int32_t* n_tiles, int32_t* tile_m,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    g_last_error.clear();
+    xattn_status st = check_shape(ctx, R, total_cand, total_kv, heads);
+    if (st != XATTN_OK) return st;
+    if (!cu_kv || !cu_cand || !cu_q || !tiles || !n_tiles)
+        return fail(XATTN_EINVAL, "NULL offset or output pointer");
+    if (!workspace || workspace_bytes < xattn_workspace_size(ctx, R, total_cand, heads))
+        return fail(XATTN_EWORKSPACE, "workspace needs %zu bytes, got %zu",
+                    xattn_workspace_size(ctx, R, total_cand, heads), workspace_bytes);
+    const int tm = tile_m_for(ctx->cfg, R, total_cand, heads);
+    if (tile_m) *tile_m = tm;
+    DeviceGuard dg(ctx->cfg.device);
+    if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
+    hipError_t e = xattn::launch_plan(cu_kv, cu_cand, R, ctx->cfg.n_slots, tm, total_cand,
+                                      total_kv, workspace, max_tiles_for(ctx->cfg, R, total_cand, tm),
+                                      cu_q, row_req, tiles, n_tiles,
+                                      static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
+    return XATTN_OK;
+}
+
+namespace {
+
+// Shared body of xattn_forward (plan = true) and xattn_attend (plan = false).
+xattn_status run_forward(bool plan, xattn_ctx* ctx, const void* Z, const void* W_Q,
+                         const void* K, const void* V, const int32_t* cu_kv,
+                         const int32_t* cu_cand, int32_t R, int32_t total_cand, int32_t total_kv,
+                         int32_t heads, void* O, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    g_last_error.clear();
+    xattn_status st = check_shape(ctx, R, total_cand, total_kv, heads);
+    if (st != XATTN_OK) return st;
+    const xattn_config& c = ctx->cfg;
+    if (c.kv_mode == XATTN_KV_SHARED && V)
+        return fail(XATTN_EINVAL, "V must be NULL in XATTN_KV_SHARED mode (V = K = H)");
+    if (!cu_kv || !cu_cand) return fail(XATTN_EINVAL, "NULL offset array");
+    if (total_cand > 0 && (!Z || !W_Q || !O))
+        return fail(XATTN_EINVAL, "NULL Z, W_Q or O");
+    if (total_kv > 0 && !K) return fail(XATTN_EINVAL, "NULL K");
+    if (total_kv > 0 && c.kv_mode == XATTN_KV_SEPARATE && !V)
+        return fail(XATTN_EINVAL, "V is NULL in XATTN_KV_SEPARATE mode");
+    const size_t need = xattn_workspace_size(ctx, R, total_cand, heads);
+    if (!workspace || workspace_bytes < need)
+        return fail(XATTN_EWORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+    if (R == 0 && (total_cand != 0 || total_kv != 0))
+        return fail(XATTN_EINVAL, "num_requests=0 with total_cand=%d total_kv=%d", total_cand,
+                    total_kv);
+    if (R == 0 || total_cand == 0) return XATTN_OK;  // no query rows: nothing to compute
+
+    const int tm = tile_m_for(c, R, total_cand, heads);
+    const int64_t max_tiles = max_tiles_for(c, R, total_cand, tm);
+    if (max_tiles * heads > INT32_MAX)
+        return fail(XATTN_EUNSUPPORTED, "grid of %lld work-groups is too large",
+                    (long long)(max_tiles * heads));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    DeviceGuard dg(c.device);
+    if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
+    hipError_t e;
+    if (plan) {
+        e = xattn::launch_plan(cu_kv, cu_cand, R, c.n_slots, tm, total_cand, total_kv, workspace,
+                               max_tiles, nullptr, nullptr, nullptr, nullptr, s);
+        if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
+    }
+    if (c.dtype == XATTN_BF16) {
+        e = xattn::launch_attn_bf16(Z, W_Q, K, c.kv_mode == XATTN_KV_SEPARATE ? V : nullptr, cu_kv,
+                                    workspace, max_tiles, c.n_slots, c.d_model, heads, tm / 32, O,
+                                    s);
+    } else {
+        e = xattn::launch_attn_f32(static_cast<const float*>(Z), static_cast<const float*>(W_Q),
+                                   static_cast<const float*>(K),
+                                   c.kv_mode == XATTN_KV_SEPARATE ? static_cast<const float*>(V)
+                                                                  : nullptr,
+                                   cu_kv, workspace, max_tiles, c.n_slots, c.d_model, heads,
+                                   static_cast<float*>(O), s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+    return XATTN_OK;
+}
+
+}  // namespace
+
+xattn_status xattn_forward(xattn_ctx* ctx, const void* Z, const void* W_Q, const void* K,
+                           const void* V, const int32_t* cu_kv, const int32_t* cu_cand,
+                           int32_t R, int32_t total_cand, int32_t total_kv, int32_t heads,
+                           void* O, void* workspace, size_t workspace_bytes, void* stream) {
+    return run_forward(true, ctx, Z, W_Q, K, V, cu_kv, cu_cand, R, total_cand, total_kv, heads, O,
+                       workspace, workspace_bytes, stream);
+}
+
+xattn_status xattn_attend(xattn_ctx* ctx, const void* Z, const void* W_Q, const void* K,
+                          const void* V, const int32_t* cu_kv, const int32_t* cu_cand,
+                          int32_t R, int32_t total_cand, int32_t total_kv, int32_t heads,
+                          void* O, void* workspace, size_t workspace_bytes, void* stream) {
+    return run_forward(false, ctx, Z, W_Q, K, V, cu_kv, cu_cand, R, total_cand, total_kv, heads, O,
+                       workspace, workspace_bytes, stream);
+}
+
+xattn_status xattn_project(xattn_ctx* ctx, const void* Z, const void* W_Q, int32_t total_cand,
+                           void* Q, void* stream) {
+    g_last_error.clear();
+    if (!ctx) return fail(XATTN_EINVAL, "ctx is NULL");
+    if (total_cand < 0) return fail(XATTN_EINVAL, "negative total_cand");
+    if (total_cand == 0) return XATTN_OK;
+    if (!Z || !W_Q || !Q) return fail(XATTN_EINVAL, "NULL Z, W_Q or Q");
+    const xattn_config& c = ctx->cfg;
+    DeviceGuard dg(c.device);
+    if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = c.dtype == XATTN_BF16
+                       ? xattn::launch_project_bf16(Z, W_Q, total_cand, c.n_slots, c.d_model, Q, s)
+                       : xattn::launch_project_f32(static_cast<const float*>(Z),
+                                                   static_cast<const float*>(W_Q), total_cand,
+                                                   c.n_slots, c.d_model, static_cast<float*>(Q), s);
+    if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
+    return XATTN_OK;
+}
+
+xattn_status xattn_device_error(xattn_ctx* ctx, const void* workspace, int32_t* flag,
+                                void* stream) {
+    g_last_error.clear();
+    if (!ctx || !workspace || !flag) return fail(XATTN_EINVAL, "NULL argument");
+    DeviceGuard dg(ctx->cfg.device);
+    if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    int32_t v = 0;
+    e = hipMemcpy(&v, static_cast<const char*>(workspace) + sizeof(int32_t) * xattn::kPlanError,
+                  sizeof v, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpy");
+    *flag = v;
+    return XATTN_OK;
+}
+
+}  // extern "C"

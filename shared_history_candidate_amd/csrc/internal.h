@@ -1,0 +1,29 @@
+// Host-side launchers shared between the C-ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace xattn {
+
+hipError_t launch_plan(const int* cu_kv, const int* cu_cand, int R, int q, int tile_m,
+                       int total_cand, int total_kv, void* ws, int64_t max_tiles, int* cu_q,
+                       int* row_req, int* tiles, int* n_tiles, hipStream_t stream);
+
+// bf16 fused projection + attention.  `waves` = 2 or 4 (tile_m = 32 * waves).
+hipError_t launch_attn_bf16(const void* Z, const void* Wq, const void* K, const void* V,
+                            const int* cu_kv, const void* ws, int64_t max_tiles, int q, int d,
+                            int heads, int waves, void* O, hipStream_t stream);
+
+hipError_t launch_project_bf16(const void* Z, const void* Wq, int total_cand, int q, int d,
+                               void* Q, hipStream_t stream);
+
+// fp32 path (tile_m = 64).
+hipError_t launch_attn_f32(const float* Z, const float* Wq, const float* K, const float* V,
+                           const int* cu_kv, const void* ws, int64_t max_tiles, int q, int d,
+                           int heads, float* O, hipStream_t stream);
+
+hipError_t launch_project_f32(const float* Z, const float* Wq, int total_cand, int q, int d,
+                              float* Q, hipStream_t stream);
+
+}  // namespace xattn

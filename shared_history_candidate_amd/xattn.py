@@ -1,0 +1,233 @@
+"""Thin ctypes binding of libxattn (include/xattn.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  PyTorch supplies device memory and the stream;
+host scalars (request, candidate and memory-row counts) come from tensor
+shapes, so no call synchronises with the device.  The library is loaded on
+first use and a missing build raises ``RuntimeError`` - there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libxattn.so")
+_lib = None
+
+XATTN_OK, XATTN_EINVAL, XATTN_EUNSUPPORTED, XATTN_EHIP, XATTN_EWORKSPACE = 0, -1, -2, -3, -4
+XATTN_BF16, XATTN_FP32 = 0, 1
+XATTN_KV_SHARED, XATTN_KV_SEPARATE = 0, 1
+
+EXPORTED = ("xattn_create", "xattn_destroy", "xattn_workspace_size", "xattn_forward",
+            "xattn_attend", "xattn_plan", "xattn_max_tiles", "xattn_project", "xattn_device_error",
+            "xattn_last_error")
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("n_slots", ctypes.c_int32),
+                ("dtype", ctypes.c_int), ("kv_mode", ctypes.c_int), ("device", ctypes.c_int32)]
+
+
+class XAttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("xattn status %d: %s" % (status, msg))
+        self.status = status
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Load libxattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError("libxattn.so is not built (%s); run "
+                               "`python -m shared_history_candidate_amd.build`" % _LIB_PATH)
+        L = ctypes.CDLL(_LIB_PATH)
+        P, I32, SZ, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_int64
+        L.xattn_create.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(P)]
+        L.xattn_create.restype = ctypes.c_int
+        L.xattn_destroy.argtypes = [P]
+        L.xattn_destroy.restype = None
+        L.xattn_workspace_size.argtypes = [P, I32, I32, I32]
+        L.xattn_workspace_size.restype = SZ
+        L.xattn_max_tiles.argtypes = [P, I32, I32, I32]
+        L.xattn_max_tiles.restype = I64
+        L.xattn_forward.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, P, P, SZ, P]
+        L.xattn_forward.restype = ctypes.c_int
+        L.xattn_attend.argtypes = L.xattn_forward.argtypes
+        L.xattn_attend.restype = ctypes.c_int
+        L.xattn_plan.argtypes = [P, P, P, I32, I32, I32, I32, P, P, P, P,
+                                 ctypes.POINTER(I32), P, SZ, P]
+        L.xattn_plan.restype = ctypes.c_int
+        L.xattn_project.argtypes = [P, P, P, I32, P, P]
+        L.xattn_project.restype = ctypes.c_int
+        L.xattn_device_error.argtypes = [P, P, ctypes.POINTER(I32), P]
+        L.xattn_device_error.restype = ctypes.c_int
+        L.xattn_last_error.argtypes = []
+        L.xattn_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != XATTN_OK:
+        raise XAttnError(status, lib().xattn_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(device, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+_DTYPES = {"bf16": (XATTN_BF16, torch.bfloat16), "fp32": (XATTN_FP32, torch.float32)}
+_MODES = {"shared": XATTN_KV_SHARED, "separate": XATTN_KV_SEPARATE}
+
+
+class XAttn:
+    """One library context: fixed d_model, q (slots), dtype and K/V mode."""
+
+    def __init__(self, d_model: int, n_slots: int, dtype: str = "bf16", kv_mode: str = "shared",
+                 device: int = 0):
+        if dtype not in _DTYPES or kv_mode not in _MODES:
+            raise ValueError("dtype must be bf16|fp32 and kv_mode shared|separate")
+        self.d_model, self.q, self.dtype_name, self.kv_mode = d_model, n_slots, dtype, kv_mode
+        self.torch_dtype = _DTYPES[dtype][1]
+        self.device = device
+        cfg = Config(d_model, n_slots, _DTYPES[dtype][0], _MODES[kv_mode], device)
+        h = ctypes.c_void_p()
+        _check(lib().xattn_create(ctypes.byref(cfg), ctypes.byref(h)))
+        self._h = h
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            lib().xattn_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- sizes ---------------------------------------------------------------
+    def workspace_size(self, num_requests: int, total_cand: int, heads: int) -> int:
+        return int(lib().xattn_workspace_size(self._h, num_requests, total_cand, heads))
+
+    def max_tiles(self, num_requests: int, total_cand: int, heads: int) -> int:
+        return int(lib().xattn_max_tiles(self._h, num_requests, total_cand, heads))
+
+    def alloc_workspace(self, num_requests: int, total_cand: int, heads: int) -> torch.Tensor:
+        n = self.workspace_size(num_requests, total_cand, heads)
+        return torch.empty(max(n, 256), dtype=torch.uint8, device="cuda:%d" % self.device)
+
+    def _check_tensor(self, name, t, dtype, shape=None):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError("%s must be a CUDA tensor" % name)
+        if t.dtype != dtype:
+            raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError("%s must have shape %s, got %s" % (name, shape, tuple(t.shape)))
+
+    # -- entry points ----------------------------------------------------------
+    def forward(self, Z, W_Q, K, V, cu_seqlens_kv, cu_cand, heads: int, O=None,
+                workspace=None, stream=None, plan: bool = True) -> torch.Tensor:
+        """O = cross-attention of Z's query tokens against their requests' memory
+        (see include/xattn.h).  Z [total_cand, q, d], W_Q [q, d, d] output-major,
+        K [total_kv, d] (= H), V [total_kv, d] or None, cu_* int32 [R+1]."""
+        d, q, dt = self.d_model, self.q, self.torch_dtype
+        total_cand, total_kv = Z.shape[0], K.shape[0]
+        R = cu_seqlens_kv.numel() - 1
+        self._check_tensor("Z", Z, dt, (total_cand, q, d))
+        self._check_tensor("W_Q", W_Q, dt, (q, d, d))
+        self._check_tensor("K", K, dt, (total_kv, d))
+        if V is not None:
+            self._check_tensor("V", V, dt, (total_kv, d))
+        self._check_tensor("cu_seqlens_kv", cu_seqlens_kv, torch.int32, (R + 1,))
+        self._check_tensor("cu_cand", cu_cand, torch.int32, (R + 1,))
+        if O is None:
+            O = torch.empty((total_cand, q, d), dtype=dt, device=Z.device)
+        self._check_tensor("O", O, dt, (total_cand, q, d))
+        if workspace is None:
+            if not plan:
+                raise ValueError("attend() needs the workspace that holds the batch's plan")
+            workspace = self.alloc_workspace(R, total_cand, heads)
+        fn = lib().xattn_forward if plan else lib().xattn_attend
+        _check(fn(self._h, _ptr(Z), _ptr(W_Q), _ptr(K), _ptr(V), _ptr(cu_seqlens_kv),
+                  _ptr(cu_cand), R, total_cand, total_kv, heads, _ptr(O), _ptr(workspace),
+                  workspace.numel(), _stream(Z.device, stream)))
+        return O
+
+    def attend(self, Z, W_Q, K, V, cu_seqlens_kv, cu_cand, heads: int, workspace, O=None,
+               stream=None) -> torch.Tensor:
+        """The attention kernel alone, reusing the plan a previous forward()/plan()
+        of the same batch left in `workspace`."""
+        return self.forward(Z, W_Q, K, V, cu_seqlens_kv, cu_cand, heads, O=O,
+                            workspace=workspace, stream=stream, plan=False)
+
+    def plan(self, cu_seqlens_kv, cu_cand, heads: int, total_cand: int, total_kv: int,
+             with_row_req: bool = True, workspace=None, stream=None):
+        """Integer varlen plan: returns (cu_q, row_req, tiles[n,4], tile_m) as device
+        tensors (tiles sliced to the device-reported count; this reads one int)."""
+        R = cu_seqlens_kv.numel() - 1
+        dev = cu_cand.device
+        cu_q = torch.empty(R + 1, dtype=torch.int32, device=dev)
+        row_req = (torch.empty(max(total_cand * self.q, 1), dtype=torch.int32, device=dev)
+                   if with_row_req else None)
+        mt = max(self.max_tiles(R, total_cand, heads), 1)
+        tiles = torch.empty((mt, 4), dtype=torch.int32, device=dev)
+        n_tiles = torch.zeros(1, dtype=torch.int32, device=dev)
+        if workspace is None:
+            workspace = self.alloc_workspace(R, total_cand, heads)
+        tm = ctypes.c_int32(0)
+        _check(lib().xattn_plan(self._h, _ptr(cu_seqlens_kv), _ptr(cu_cand), R, total_cand,
+                                total_kv, heads, _ptr(cu_q), _ptr(row_req), _ptr(tiles),
+                                _ptr(n_tiles), ctypes.byref(tm), _ptr(workspace),
+                                workspace.numel(), _stream(dev, stream)))
+        n = int(n_tiles.item())
+        rr = row_req[: total_cand * self.q] if row_req is not None else None
+        return cu_q, rr, tiles[:n], tm.value
+
+    def project(self, Z, W_Q, Q=None, stream=None) -> torch.Tensor:
+        """TSP projection alone: Q[row] = Z[row] . W_Q[row % q] (output-major W_Q)."""
+        d, q, dt = self.d_model, self.q, self.torch_dtype
+        total_cand = Z.shape[0]
+        self._check_tensor("Z", Z, dt, (total_cand, q, d))
+        self._check_tensor("W_Q", W_Q, dt, (q, d, d))
+        if Q is None:
+            Q = torch.empty((total_cand, q, d), dtype=dt, device=Z.device)
+        self._check_tensor("Q", Q, dt, (total_cand, q, d))
+        _check(lib().xattn_project(self._h, _ptr(Z), _ptr(W_Q), total_cand, _ptr(Q),
+                                   _stream(Z.device, stream)))
+        return Q
+
+    def device_error(self, workspace, stream=None) -> int:
+        """Synchronise and read the device-side offset-validation flag."""
+        flag = ctypes.c_int32(0)
+        _check(lib().xattn_device_error(self._h, _ptr(workspace), ctypes.byref(flag),
+                                        _stream(workspace.device, stream)))
+        return flag.value
+
+
+def to_device(wl, device="cuda"):
+    """Upload a workloads.Workload's arrays (already exactly representable in the
+    workload's dtype) as device tensors: dict of Z, W_Q, K, V, cu_kv, cu_cand."""
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+
+    def up(a):
+        return None if a is None else torch.from_numpy(a).to(device).to(dt).contiguous()
+    return {
+        "Z": up(wl.Z), "W_Q": up(wl.wt), "K": up(wl.K), "V": up(wl.V),
+        "cu_kv": torch.from_numpy(wl.cu_kv).to(device), "cu_cand": torch.from_numpy(wl.cu_cand).to(device),
+    }

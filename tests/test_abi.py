@@ -1,0 +1,152 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol that
+include/xattn.h declares, and rejects bad arguments on the host before it
+enqueues anything (fake, never-dereferenced device pointers are passed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from shared_history_candidate_amd import xattn as X
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "xattn.h")
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every case fails validation first
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(X.lib_path()):
+        from shared_history_candidate_amd import build
+        build.build()
+    return X.lib()
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(xattn_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert set(names) == set(X.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _create(L, d=256, q=3, dtype=X.XATTN_BF16, mode=X.XATTN_KV_SHARED, dev=0):
+    cfg = X.Config(d, q, dtype, mode, dev)
+    h = ctypes.c_void_p()
+    st = L.xattn_create(ctypes.byref(cfg), ctypes.byref(h))
+    return st, h
+
+
+@pytest.mark.parametrize("d,q,dtype,mode,dev,want", [
+    (0, 3, X.XATTN_BF16, 0, 0, X.XATTN_EINVAL),
+    (256, 0, X.XATTN_BF16, 0, 0, X.XATTN_EINVAL),
+    (256, 65, X.XATTN_BF16, 0, 0, X.XATTN_EINVAL),
+    (256, 3, 7, 0, 0, X.XATTN_EINVAL),
+    (256, 3, X.XATTN_BF16, 5, 0, X.XATTN_EINVAL),
+    (256, 3, X.XATTN_BF16, 0, -1, X.XATTN_EINVAL),
+    (48, 3, X.XATTN_BF16, 0, 0, X.XATTN_EUNSUPPORTED),
+    (48, 3, X.XATTN_FP32, 0, 0, X.XATTN_OK),
+    (256, 3, X.XATTN_BF16, 1, 0, X.XATTN_OK),
+])
+def test_create_validation(L, d, q, dtype, mode, dev, want):
+    st, h = _create(L, d, q, dtype, mode, dev)
+    assert st == want
+    if want == X.XATTN_OK:
+        assert h.value
+        L.xattn_destroy(h)
+    else:
+        assert not h.value
+        assert L.xattn_last_error().decode()
+
+
+def test_create_null_args(L):
+    h = ctypes.c_void_p()
+    assert L.xattn_create(None, ctypes.byref(h)) == X.XATTN_EINVAL
+    cfg = X.Config(64, 1, 0, 0, 0)
+    assert L.xattn_create(ctypes.byref(cfg), None) == X.XATTN_EINVAL
+    L.xattn_destroy(None)
+
+
+def test_workspace_size(L):
+    st, h = _create(L)
+    assert st == 0
+    a = L.xattn_workspace_size(h, 8, 2048, 4)
+    b = L.xattn_workspace_size(h, 8, 4096, 4)
+    assert 256 < a < b
+    assert L.xattn_workspace_size(h, -1, 10, 4) == 0
+    assert L.xattn_workspace_size(h, 1, 10, 0) == 0
+    assert L.xattn_workspace_size(None, 1, 10, 4) == 0
+    assert L.xattn_max_tiles(h, 8, 2048, 4) * 16 + 256 == a
+    L.xattn_destroy(h)
+
+
+def _fwd(L, h, Z=FAKE, W=FAKE, K=FAKE, V=None, cu_kv=FAKE, cu_c=FAKE, R=2, tc=10, tkv=20,
+         heads=4, O=FAKE, ws=FAKE, wsb=1 << 20):
+    return L.xattn_forward(h, Z, W, K, V, cu_kv, cu_c, R, tc, tkv, heads, O, ws, wsb, None)
+
+
+def test_forward_host_validation(L):
+    st, h = _create(L, 256, 3, X.XATTN_BF16, X.XATTN_KV_SHARED)
+    assert st == 0
+    assert _fwd(L, None) == X.XATTN_EINVAL
+    assert _fwd(L, h, heads=3) == X.XATTN_EINVAL           # 3 does not divide 256
+    assert _fwd(L, h, heads=0) == X.XATTN_EINVAL
+    assert _fwd(L, h, heads=16) == X.XATTN_EUNSUPPORTED    # d_h = 16 on bf16
+    assert _fwd(L, h, heads=1) == X.XATTN_EUNSUPPORTED     # d_h = 256
+    assert _fwd(L, h, V=FAKE) == X.XATTN_EINVAL            # V given in shared mode
+    assert _fwd(L, h, Z=None) == X.XATTN_EINVAL
+    assert _fwd(L, h, O=None) == X.XATTN_EINVAL
+    assert _fwd(L, h, K=None) == X.XATTN_EINVAL
+    assert _fwd(L, h, cu_kv=None) == X.XATTN_EINVAL
+    assert _fwd(L, h, R=-1) == X.XATTN_EINVAL
+    assert _fwd(L, h, tc=-5) == X.XATTN_EINVAL
+    assert _fwd(L, h, R=5000) == X.XATTN_EUNSUPPORTED      # planner request limit
+    assert _fwd(L, h, ws=None) == X.XATTN_EWORKSPACE
+    assert _fwd(L, h, wsb=16) == X.XATTN_EWORKSPACE
+    assert _fwd(L, h, R=0, tc=10) == X.XATTN_EINVAL        # rows without requests
+    assert "R" in L.xattn_last_error().decode() or L.xattn_last_error().decode()
+    # empty batch: valid, nothing to launch
+    assert _fwd(L, h, R=0, tc=0, tkv=0) == X.XATTN_OK
+    assert L.xattn_last_error().decode() == ""
+    L.xattn_destroy(h)
+
+
+def test_forward_separate_mode_needs_v(L):
+    st, h = _create(L, 256, 1, X.XATTN_BF16, X.XATTN_KV_SEPARATE)
+    assert st == 0
+    assert _fwd(L, h, V=None) == X.XATTN_EINVAL
+    L.xattn_destroy(h)
+
+
+def test_fp32_dh_limit(L):
+    st, h = _create(L, 512, 1, X.XATTN_FP32, X.XATTN_KV_SHARED)
+    assert st == 0
+    assert _fwd(L, h, heads=2) == X.XATTN_EUNSUPPORTED     # d_h = 256 > 128
+    L.xattn_destroy(h)
+
+
+def test_plan_host_validation(L):
+    st, h = _create(L)
+    tm = ctypes.c_int32(0)
+    assert L.xattn_plan(h, FAKE, FAKE, 2, 10, 20, 4, None, None, FAKE, FAKE, ctypes.byref(tm),
+                        FAKE, 1 << 20, None) == X.XATTN_EINVAL
+    assert L.xattn_plan(h, FAKE, FAKE, 2, 10, 20, 4, FAKE, None, FAKE, FAKE, ctypes.byref(tm),
+                        FAKE, 8, None) == X.XATTN_EWORKSPACE
+    assert L.xattn_project(h, None, FAKE, 4, FAKE, None) == X.XATTN_EINVAL
+    assert L.xattn_project(h, FAKE, FAKE, -1, FAKE, None) == X.XATTN_EINVAL
+    assert L.xattn_project(h, FAKE, FAKE, 0, FAKE, None) == X.XATTN_OK
+    flag = ctypes.c_int32(0)
+    assert L.xattn_device_error(h, None, ctypes.byref(flag), None) == X.XATTN_EINVAL
+    L.xattn_destroy(h)
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(X, "_LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(X, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        X.lib()
