@@ -43,7 +43,47 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="run only a plain device copy of this many MiB (counter calibration)")
+    p.add_argument("--micro", action="store_true",
+                   help="run only the unit micro-benchmarks (achievable MFMA/exp/VALU/LDS/HBM)")
     return p.parse_args()
+
+
+def micro():
+    """Achievable rates of the units that bound the fused kernel (one JSON line)."""
+    import ctypes
+    import torch
+    from shared_history_candidate_amd import xattn as X
+    L = X.lib()
+    L.xattn_micro_run.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p, ctypes.c_void_p]
+    L.xattn_micro_run.restype = ctypes.c_float
+    L.xattn_micro_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                   ctypes.c_int, ctypes.c_void_p]
+    L.xattn_micro_copy.restype = ctypes.c_float
+    props = torch.cuda.get_device_properties(0)
+    cus = props.multi_processor_count
+    clk = 2.4e9
+    blocks = cus * 8
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {"cus": cus, "assumed_clock_ghz": clk / 1e9}
+    iters = 2000
+    ms = L.xattn_micro_run(0, blocks, iters, 5, ctypes.c_void_p(out.data_ptr()), st)
+    fl = blocks * 4 * iters * 8 * 32768.0
+    res["mfma_bf16_tflops"] = fl / (ms * 1e-3) / 1e12
+    for kind, name, per in ((1, "exp", 16), (2, "fma", 16)):
+        ms = L.xattn_micro_run(kind, blocks, iters, 5, ctypes.c_void_p(out.data_ptr()), st)
+        ops = blocks * 256 * iters * per
+        res[name + "_per_cu_per_clk"] = ops / (ms * 1e-3) / (cus * clk)
+    for kind, name, nbytes in ((3, "lds_b64", 16), (4, "lds_b128", 16), (5, "lds_tr16_b64", 16)):
+        ms = L.xattn_micro_run(kind, blocks, iters, 5, ctypes.c_void_p(out.data_ptr()), st)
+        b = blocks * 256 * iters * float(nbytes)
+        res[name + "_bytes_per_cu_per_clk"] = b / (ms * 1e-3) / (cus * clk)
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b2 = torch.empty_like(a)
+    ms = L.xattn_micro_copy(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(b2.data_ptr()), n, 10, st)
+    res["hbm_copy_gbs"] = 2.0 * n / (ms * 1e-3) / 1e9
+    print(json.dumps({k: (round(v, 3) if isinstance(v, float) else v) for k, v in res.items()}))
 
 
 def kernel_sha():
@@ -114,11 +154,14 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
-              "(requests shard across GPUs with no exchange; see DESIGN.md). Use --gpus 1.",
+              "(requests shard across GPUs with no exchange). Use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
     if args.calib_copy_mib:
         calib_copy(args.calib_copy_mib)
+        return
+    if args.micro:
+        micro()
         return
 
     import numpy as np

@@ -7,6 +7,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <new>
 #include <string>
 
@@ -37,24 +38,49 @@ xattn_status hip_fail(hipError_t e, const char* what) {
 
 bool bf16_dh_supported(int dh) { return dh == 32 || dh == 64 || dh == 128; }
 
-// Waves per work-group for the bf16 kernel (each wave owns 32 candidates of
-// one slot).  Four waves share each staged memory tile among more queries;
-// two waves give twice the work-groups.  Use four when the batch still
-// yields at least two work-groups per compute unit.
-int choose_waves(const xattn_config& c, int R, int total_cand, int heads) {
-    if (c.dtype != XATTN_BF16) return 1;
-    const int64_t wg4 = (int64_t)c.n_slots * heads * ((int64_t)total_cand / 128 + R);
-    return wg4 >= 512 ? 4 : 2;
+// Work-group shape of the bf16 kernel: rb query blocks of 32 candidates and
+// ksplit memory splits (rb * ksplit waves).  Long memories favour splitting
+// the memory so that every SIMD holds several waves; batches with many query
+// tiles favour wide query blocks that share each staged memory tile.
+// XATTN_VARIANT="rb,ksplit" overrides the choice (tuning and tests).
+struct Variant {
+    int rb, ksplit;
+};
+
+Variant choose_variant(const xattn_config& c, int R, int total_cand, int total_kv, int heads) {
+    const int dh = c.d_model / heads;
+    const bool sep = c.kv_mode == XATTN_KV_SEPARATE;
+    if (const char* env = getenv("XATTN_VARIANT")) {
+        int rb = 0, ks = 0;
+        if (sscanf(env, "%d,%d", &rb, &ks) == 2 && xattn::attn_bf16_variant_ok(dh, rb, ks, sep))
+            return {rb, ks};
+    }
+    const double rows = (double)total_cand * c.n_slots * heads;   // query rows x heads
+    const double mean_L = R > 0 ? (double)total_kv / R : 0.0;
+    Variant v{2, 2};
+    if (rows / 128.0 >= 4096.0) v = {4, 1};   // many query tiles already fill the chip
+    else if (rows / 64.0 < 1024.0 && mean_L >= 1024.0) v = {1, 4};   // few tiles, long memory
+    // fall back to a variant that is built for this head width and mode
+    const Variant order[] = {v, {2, 2}, {4, 1}, {2, 1}};
+    for (const Variant& o : order)
+        if (xattn::attn_bf16_variant_ok(dh, o.rb, o.ksplit, sep)) return o;
+    return {2, 1};
 }
 
-int tile_m_for(const xattn_config& c, int R, int total_cand, int heads) {
+int tile_m_for(const xattn_config& c, int R, int total_cand, int total_kv, int heads) {
     if (c.dtype != XATTN_BF16) return 64;
-    return 32 * choose_waves(c, R, total_cand, heads);
+    return 32 * choose_variant(c, R, total_cand, total_kv, heads).rb;
 }
 
 int64_t max_tiles_for(const xattn_config& c, int R, int total_cand, int tile_m) {
     // sum_r ceil(N_r / tile_m) <= (total_cand + R * (tile_m - 1)) / tile_m
     return (int64_t)c.n_slots * (((int64_t)total_cand + (int64_t)R * (tile_m - 1)) / tile_m);
+}
+
+// The workspace is sized for the smallest tile (32 candidates), which bounds
+// the tile count of every variant.
+int64_t max_tiles_any(const xattn_config& c, int R, int total_cand) {
+    return max_tiles_for(c, R, total_cand, 32);
 }
 
 struct DeviceGuard {
@@ -124,7 +150,7 @@ void xattn_destroy(xattn_ctx* ctx) { delete ctx; }
 
 int64_t xattn_max_tiles(const xattn_ctx* ctx, int32_t R, int32_t total_cand, int32_t heads) {
     if (!ctx || R < 0 || total_cand < 0 || heads < 1) return 0;
-    return max_tiles_for(ctx->cfg, R, total_cand, tile_m_for(ctx->cfg, R, total_cand, heads));
+    return max_tiles_any(ctx->cfg, R, total_cand);
 }
 
 size_t xattn_workspace_size(const xattn_ctx* ctx, int32_t R, int32_t total_cand, int32_t heads) {
@@ -144,7 +170,7 @@ xattn_status xattn_plan(xattn_ctx* ctx, const int32_t* cu_kv, const int32_t* cu_
     if (!workspace || workspace_bytes < xattn_workspace_size(ctx, R, total_cand, heads))
         return fail(XATTN_EWORKSPACE, "workspace needs %zu bytes, got %zu",
                     xattn_workspace_size(ctx, R, total_cand, heads), workspace_bytes);
-    const int tm = tile_m_for(ctx->cfg, R, total_cand, heads);
+    const int tm = tile_m_for(ctx->cfg, R, total_cand, total_kv, heads);
     if (tile_m) *tile_m = tm;
     DeviceGuard dg(ctx->cfg.device);
     if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
@@ -184,7 +210,8 @@ xattn_status run_forward(bool plan, xattn_ctx* ctx, const void* Z, const void* W
                     total_kv);
     if (R == 0 || total_cand == 0) return XATTN_OK;  // no query rows: nothing to compute
 
-    const int tm = tile_m_for(c, R, total_cand, heads);
+    const Variant var = choose_variant(c, R, total_cand, total_kv, heads);
+    const int tm = tile_m_for(c, R, total_cand, total_kv, heads);
     const int64_t max_tiles = max_tiles_for(c, R, total_cand, tm);
     if (max_tiles * heads > INT32_MAX)
         return fail(XATTN_EUNSUPPORTED, "grid of %lld work-groups is too large",
@@ -200,8 +227,8 @@ xattn_status run_forward(bool plan, xattn_ctx* ctx, const void* Z, const void* W
     }
     if (c.dtype == XATTN_BF16) {
         e = xattn::launch_attn_bf16(Z, W_Q, K, c.kv_mode == XATTN_KV_SEPARATE ? V : nullptr, cu_kv,
-                                    workspace, max_tiles, c.n_slots, c.d_model, heads, tm / 32, O,
-                                    s);
+                                    workspace, max_tiles, c.n_slots, c.d_model, heads, var.rb,
+                                    var.ksplit, O, s);
     } else {
         e = xattn::launch_attn_f32(static_cast<const float*>(Z), static_cast<const float*>(W_Q),
                                    static_cast<const float*>(K),

@@ -11,20 +11,31 @@
 // request stream the same memory rows (shared-prefix serving, ReST reading
 // note s.3.5).
 //
-// Work decomposition.  One work-group handles one work item and one head with
-// `WAVES` waves; wave w owns query columns c0 + 32w .. c0 + 32w + 31.  The
-// product is computed transposed, S^T = K Q^T, so that each lane holds one
-// query row's scores and the softmax reductions along the key axis stay
-// inside a lane (plus one exchange between the two 32-lane halves):
-//   projection  Q_h^T (d_h x 32)  = W_h (d_h x d)   . Z^T (d x 32)
-//   scores      S^T   (32 x 32)   = K_tile (32 x d_h) . Q_h^T
-//   output      O^T   (d_h x 32) += V_tile^T (d_h x 32) . P^T (32 x 32)
-// The memory is streamed in tiles of 32 rows through double-buffered LDS
-// (one buffer serves as both K and V in projection-free mode).  V^T operands
-// are read from the row-major tile with LDS transpose reads.  The scores'
-// k-index (feature e) and the PV k-index (memory row j) follow the
-// accumulator layout of the previous product, so Q and P go from
-// accumulators to operands without any data movement.
+// Work decomposition.  A work-group handles one work item and one head with
+// RB x KSPLIT waves: wave w owns query block rb = w % RB (32 query columns)
+// and memory split ks = w / RB (memory tiles t with t % KSPLIT == ks).  The
+// waves of one split share the staged memory tiles; the KSPLIT partial
+// softmax states of a query block are merged through LDS at the end.
+//
+// Products are computed transposed so that each lane holds one query row and
+// the softmax reductions along the key axis stay inside the lane (plus one
+// exchange between the two 32-lane halves, needed only when the running
+// maximum moves):
+//   projection  Q_h^T (d_h x 32) = W_h (d_h x d) . Z^T (d x 32)
+//   scores      S^T   (64 x 32)  = K_tile (64 x d_h) . Q_h^T
+//   output      O^T   (d_h x 32) += V_tile^T (d_h x 64) . P^T (64 x 32)
+// The accumulator layout of each product is the operand layout of the next,
+// so Q and P never move between lanes.  W_h and the query tokens are staged
+// into LDS with direct global->LDS loads (XOR-swizzled 16-byte chunks); the
+// memory is streamed in tiles of 64 rows through double-buffered LDS (one
+// buffer is both K and V in projection-free mode) and V^T operands come from
+// LDS transpose reads.
+//
+// Softmax: exp2 of log2(e)/sqrt(d_h)-scaled scores.  The running maximum is
+// only moved when a tile exceeds it by more than 2^8 (then the accumulators
+// are rescaled); between moves the weights are bounded by 2^8, which fp32
+// sums and bf16 operands hold exactly as well as weights <= 1.  Row sums
+// accumulate the bf16-rounded weights that enter the PV product (v_dot2).
 #include "common.h"
 #include "internal.h"
 
@@ -32,192 +43,335 @@ namespace xattn {
 
 namespace {
 
-constexpr int BN = 32;  // memory rows per tile
+constexpr int BN = 64;               // memory rows per tile
+constexpr float kLazy = 8.0f;        // exp2-domain headroom of the running maximum
 
-// One 32(e) x 32(query) block of Q^T for the lane's query row:
-//   acc[reg r] = sum_i W[s][erow0 + (r/4)*8 + 4*g + r%4][i] * Z[cand][s][i].
-// wrow points at W[s][erow0 + lane%32][0]; zrow at Z[cand][s][0] (or nullptr
-// for an out-of-range query column, which then contributes zeros).
-__device__ __forceinline__ void project_acc(const bf16* __restrict__ wrow,
-                                            const bf16* __restrict__ zrow, int d, int g,
-                                            f32x16& acc) {
-    const bf16x8 zero = {};
-    for (int k0 = 0; k0 < d; k0 += 16) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(wrow + k0 + 8 * g);
-        const bf16x8 b = zrow ? *reinterpret_cast<const bf16x8*>(zrow + k0 + 8 * g) : zero;
-        acc = mfma32(a, b, acc);
+constexpr int pow2floor(int x) {
+    int p = 1;
+    while (p * 2 <= x) p *= 2;
+    return p;
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+template <int DH, int RB, int KSPLIT, bool SEP>
+struct Cfg {
+    static constexpr int NW = RB * KSPLIT;
+    static constexpr int NT = 64 * NW;
+    static constexpr int EB = DH / 32;        // 32-wide feature blocks
+    static constexpr int KST = DH / 16;       // k-steps of the score product
+    static constexpr int LDK = DH + 8;        // memory tile pitch (elements)
+    static constexpr int PLANES = SEP ? 2 : 1;
+    static constexpr int TILE = BN * LDK;     // elements per plane per buffer
+    static constexpr int KV_BYTES = KSPLIT * 2 * PLANES * TILE * 2;
+    // projection stage width (input features): a power of two <= 256 that
+    // keeps the W_h and query-token stages within 72 KB of LDS
+    static constexpr int SC = pow2floor((36864 / (DH + 32 * RB)) < 256 ? 36864 / (DH + 32 * RB) : 256);
+    static constexpr int W_BYTES = DH * SC * 2;
+    static constexpr int ZT_BYTES = 32 * RB * SC * 2;
+    static constexpr int QS_BYTES = KSPLIT > 1 ? RB * EB * 2 * 64 * 16 : 0;  // shared Q^T
+    static constexpr int P1_BYTES = W_BYTES + ZT_BYTES + QS_BYTES;
+    static constexpr int CMB_BYTES = KSPLIT > 1 ? RB * (KSPLIT - 1) * 64 * (EB * 16 + 2) * 4 : 0;
+    static constexpr int SMEM = P1_BYTES > KV_BYTES ? (P1_BYTES > CMB_BYTES ? P1_BYTES : CMB_BYTES)
+                                                    : (KV_BYTES > CMB_BYTES ? KV_BYTES : CMB_BYTES);
+    static constexpr int KV_CHUNKS = BN * DH / 8;                 // 16-byte chunks per plane
+    static constexpr int KV_CPT = (KV_CHUNKS + 64 * RB - 1) / (64 * RB);
+    static constexpr int MYEB = (EB + KSPLIT - 1) / KSPLIT;       // e-blocks projected per wave
+};
+
+__device__ __forceinline__ void lds_dma16(const void* gptr, void* lds_base) {
+    __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_base, 16,
+                                     0, 0);
+}
+
+// Stage rows [0, nrows) x columns [k0, k0+w) of a bf16 matrix (row i at
+// src_row(i)) into LDS as rows of w elements whose 16-byte chunks are
+// XOR-swizzled by (row mod chunks-per-row).  Each wave instruction fills 1 KB
+// of LDS (64 lanes x 16 bytes, lane order); instructions are dealt
+// round-robin to the work-group's waves.  w is a multiple of 32.
+template <int NT, typename RowPtr>
+__device__ __forceinline__ void stage_rows(char* lds, int nrows, int w, RowPtr src_row, int k0) {
+    const int cpr = w / 8;                    // chunks per row
+    const int total = nrows * cpr;            // chunks (a multiple of 64)
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int base = wave * 64; base < total; base += NT) {
+        const int c = base + lane;            // LDS chunk written by this lane
+        const int row = c / cpr, pc = c - row * cpr;
+        const int lc = pc ^ (row & (cpr - 1));    // logical chunk stored there
+        const bf16* src = src_row(row) + k0 + lc * 8;
+        lds_dma16(src, lds + base * 16);
     }
 }
 
-template <int DH, int WAVES, bool SEPARATE>
-__global__ __launch_bounds__(64 * WAVES) void attn_bf16_kernel(
+__device__ __forceinline__ bf16x8 lds_chunk(const char* lds, int row, int chunk, int cpr) {
+    const int pc = chunk ^ (row & (cpr - 1));
+    return *reinterpret_cast<const bf16x8*>(lds + (row * cpr + pc) * 16);
+}
+
+template <int DH, int RB, int KSPLIT, bool SEP>
+__global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(
     const bf16* __restrict__ Z, const bf16* __restrict__ Wq, const bf16* __restrict__ K,
     const bf16* __restrict__ V, const int* __restrict__ cu_kv, const int* __restrict__ ws,
     int q, int d, int heads, float scale_log2, bf16* __restrict__ O) {
-    constexpr int NT = 64 * WAVES;
-    constexpr int LDK = DH + 8;             // LDS row pitch (elements)
-    constexpr int EB = DH / 32;             // 32-wide feature blocks
-    constexpr int KS = DH / 16;             // k-steps of the score product
-    constexpr int CHUNKS = BN * DH / 8;     // 16-byte chunks per memory tile
-    constexpr int CPT = (CHUNKS + NT - 1) / NT;
-    constexpr int NBUF = SEPARATE ? 2 : 1;  // K (and V) planes per stage
-    __shared__ __attribute__((aligned(16))) bf16 lds[2][NBUF][BN * LDK];
+    using C = Cfg<DH, RB, KSPLIT, SEP>;
+    __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
 
     const int n_tiles = ws[kPlanNTiles];
     const int tile = blockIdx.x / heads;
     const int h = blockIdx.x - tile * heads;
     // A plan built for another tile size (another batch shape) is not ours.
-    if (tile >= n_tiles || ws[kPlanTileM] != 32 * WAVES) return;
+    if (tile >= n_tiles || ws[kPlanTileM] != 32 * RB) return;
     const int4 item = reinterpret_cast<const int4*>(
         reinterpret_cast<const char*>(ws) + kPlanHeaderBytes)[tile];
     const int r = item.x, s = item.y, c0 = item.z, nc = item.w;
     const int kv0 = cu_kv[r];
     const int L = cu_kv[r + 1] - kv0;
 
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int g = lane >> 5;         // 32-lane half
-    const int l32 = lane & 31;
-    const int qcol = wave * 32 + l32;  // query column inside the tile
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int rb = w % RB, ksg = w / RB;     // query block, memory split
+    const int g = lane >> 5, l32 = lane & 31;
+    const int qcol = rb * 32 + l32;
     const bool qvalid = qcol < nc;
     const int cand = c0 + qcol;
+    const int gt = tid - ksg * 64 * RB;       // thread index inside the split group
 
-    // ---- 1. projection: Q_h^T for this wave's 32 query columns ----
-    bf16x8 qb[KS];
+    // ---------------- 1. projection: Q_h^T of this wave's 32 queries ----------------
+    bf16x8 qb[C::KST];
     {
-        const bf16* zrow = qvalid ? Z + ((size_t)cand * q + s) * d : nullptr;
+        char* w_lds = smem;
+        char* z_lds = smem + C::W_BYTES;
+        const bf16* wsrc = Wq + ((size_t)s * d + h * DH) * d;
+        const int zlast = c0 + nc - 1;        // rows past the tile re-read the last valid one
+        f32x16 pacc[C::MYEB];
 #pragma unroll
-        for (int eb = 0; eb < EB; ++eb) {
-            f32x16 acc = {};
-            const bf16* wrow = Wq + ((size_t)s * d + h * DH + eb * 32 + l32) * d;
-            project_acc(wrow, zrow, d, g, acc);
-            // accumulator reg 8u+t holds feature e = eb*32 + 16u + (t/4)*8 + 4g + t%4,
-            // which is exactly k-slot t of score k-step 2*eb+u.
+        for (int i = 0; i < C::MYEB; ++i) pacc[i] = f32x16{};
+        for (int k0 = 0; k0 < d;) {
+            // a power-of-two stage width keeps the chunk swizzle a permutation
+            // (d is a multiple of 32, so every stage is at least 32 wide)
+            int wdt = C::SC;
+            while (wdt > d - k0) wdt >>= 1;
+            const int cpr = wdt / 8;
+            if (k0 > 0) __syncthreads();   // previous stage fully consumed
+            stage_rows<C::NT>(w_lds, DH, wdt, [&](int e) { return wsrc + (size_t)e * d; }, k0);
+            stage_rows<C::NT>(z_lds, 32 * RB, wdt,
+                              [&](int i) { return Z + ((size_t)min(c0 + i, zlast) * q + s) * d; },
+                              k0);
+            __builtin_amdgcn_s_waitcnt(0);   // this thread's LDS-DMA loads have landed
+            __syncthreads();                 // ... and every other thread's
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
+            for (int i = 0; i < C::MYEB; ++i) {
+                const int eb = ksg + i * KSPLIT;
+                if (eb < C::EB) {
+                    for (int kk = 0; kk < wdt / 16; ++kk) {
+                        const bf16x8 a = lds_chunk(w_lds, eb * 32 + l32, 2 * kk + g, cpr);
+                        const bf16x8 b = lds_chunk(z_lds, rb * 32 + l32, 2 * kk + g, cpr);
+                        pacc[i] = mfma32(a, b, pacc[i]);
+                    }
+                }
+            }
+            k0 += wdt;
+        }
+        // accumulator reg 8u+t of e-block eb holds feature eb*32 + 16u + (t/4)*8 + 4g + t%4,
+        // which is k-slot t of score k-step 2*eb+u.
+        if constexpr (KSPLIT == 1) {
 #pragma unroll
-                for (int t = 0; t < 8; ++t) qb[2 * eb + u][t] = (bf16)acc[8 * u + t];
+            for (int eb = 0; eb < C::EB; ++eb)
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) qb[2 * eb + u][t] = (bf16)pacc[eb][8 * u + t];
+        } else {
+            // the KSPLIT waves of a query block each projected some e-blocks: share them
+            bf16x8* qs = reinterpret_cast<bf16x8*>(smem + C::W_BYTES + C::ZT_BYTES);
+#pragma unroll
+            for (int i = 0; i < C::MYEB; ++i) {
+                const int eb = ksg + i * KSPLIT;
+                if (eb < C::EB) {
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        bf16x8 v;
+#pragma unroll
+                        for (int t = 0; t < 8; ++t) v[t] = (bf16)pacc[i][8 * u + t];
+                        qs[((rb * C::EB + eb) * 2 + u) * 64 + lane] = v;
+                    }
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < C::KST; ++k) qb[k] = qs[(rb * C::EB * 2 + k) * 64 + lane];
         }
     }
+    __syncthreads();   // projection LDS is reused for the memory tiles below
 
-    // ---- 2. stream the memory rows ----
-    f32x16 oacc[EB];
+    // ---------------- 2. stream this split's memory tiles ----------------
+    f32x16 oacc[C::EB];
 #pragma unroll
-    for (int eb = 0; eb < EB; ++eb) oacc[eb] = f32x16{};
-    float m_run = -INFINITY;  // running max of raw scores (same in both halves)
-    float l_run = 0.f;        // running sum of weights over this half's keys
+    for (int eb = 0; eb < C::EB; ++eb) oacc[eb] = f32x16{};
+    float m_run = -INFINITY;   // running max, exp2 domain (identical in both halves)
+    float l_run = 0.f;         // this half's share of the row sum
 
+    bf16* kvl = reinterpret_cast<bf16*>(smem) + (size_t)ksg * 2 * C::PLANES * C::TILE;
     const int ntiles_kv = (L + BN - 1) / BN;
-    uint4 kreg[CPT];
-    uint4 vreg[SEPARATE ? CPT : 1];
+    const int n_iter = (ntiles_kv + KSPLIT - 1) / KSPLIT;
     const bf16* Kh = K + (size_t)kv0 * d + h * DH;
-    const bf16* Vh = SEPARATE ? V + (size_t)kv0 * d + h * DH : nullptr;
+    const bf16* Vh = SEP ? V + (size_t)kv0 * d + h * DH : nullptr;
+    uint4 kreg[C::KV_CPT];
+    uint4 vreg[SEP ? C::KV_CPT : 1];
 
-    auto gload = [&](int kt) {
+    auto gload = [&](int t) {
 #pragma unroll
-        for (int u = 0; u < CPT; ++u) {
-            const int c = threadIdx.x + u * NT;
+        for (int u = 0; u < C::KV_CPT; ++u) {
+            const int c = gt + u * 64 * RB;
             const int j = c / (DH / 8), c8 = c % (DH / 8);
-            const int jj = kt * BN + j;
-            const bool ok = (c < CHUNKS) && (jj < L);
+            const int jj = t * BN + j;
+            const bool ok = (c < C::KV_CHUNKS) && (jj < L);
             const size_t off = (size_t)jj * d + c8 * 8;
             kreg[u] = ok ? *reinterpret_cast<const uint4*>(Kh + off) : make_uint4(0, 0, 0, 0);
-            if constexpr (SEPARATE)
+            if constexpr (SEP)
                 vreg[u] = ok ? *reinterpret_cast<const uint4*>(Vh + off) : make_uint4(0, 0, 0, 0);
         }
     };
     auto lstore = [&](int buf) {
+        bf16* base = kvl + buf * C::PLANES * C::TILE;
 #pragma unroll
-        for (int u = 0; u < CPT; ++u) {
-            const int c = threadIdx.x + u * NT;
-            if (c < CHUNKS) {
+        for (int u = 0; u < C::KV_CPT; ++u) {
+            const int c = gt + u * 64 * RB;
+            if (c < C::KV_CHUNKS) {
                 const int j = c / (DH / 8), c8 = c % (DH / 8);
-                *reinterpret_cast<uint4*>(&lds[buf][0][j * LDK + c8 * 8]) = kreg[u];
-                if constexpr (SEPARATE)
-                    *reinterpret_cast<uint4*>(&lds[buf][NBUF - 1][j * LDK + c8 * 8]) = vreg[u];
+                *reinterpret_cast<uint4*>(base + j * C::LDK + c8 * 8) = kreg[u];
+                if constexpr (SEP)
+                    *reinterpret_cast<uint4*>(base + C::TILE + j * C::LDK + c8 * 8) = vreg[u];
             }
         }
     };
 
-    if (ntiles_kv > 0) {
-        gload(0);
+    if (ksg < ntiles_kv) {
+        gload(ksg);
         lstore(0);
     }
     __syncthreads();
 
-    // Per-lane constants of the transposed V read (see lds_read_tr16): in each
-    // 16-lane group G, source lane k addresses row 4*(G/2) + k/4 and column
-    // 16*(G%2) + 4*(k%4) of the 16-row slab, so lane l receives
-    // V[16u + 4g + t][eb*32 + l%32] for t = 0..3.
+    // transposed V read: lane l receives V[16u + 4g + t][eb*32 + l%32], t = 0..3
     const int G = lane >> 4, k16 = lane & 15;
     const int tr_row = 4 * (G >> 1) + (k16 >> 2);
     const int tr_col = 16 * (G & 1) + 4 * (k16 & 3);
+    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 
-    for (int kt = 0; kt < ntiles_kv; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < ntiles_kv) gload(kt + 1);
-        const bf16* kb = lds[buf][0];
-        const bf16* vb = lds[buf][NBUF - 1];
-
-        // scores S^T: lane holds query l32, keys j = (r/4)*8 + 4g + r%4
-        f32x16 sacc = {};
+    for (int it = 0; it < n_iter; ++it) {
+        const int t = ksg + it * KSPLIT;          // this split's tile
+        const int buf = it & 1;
+        const bool have = t < ntiles_kv;
+        const bool next = t + KSPLIT < ntiles_kv;
+        if (next) gload(t + KSPLIT);
+        if (have) {
+            const bf16* kb = kvl + buf * C::PLANES * C::TILE;
+            const bf16* vb = kb + (C::PLANES - 1) * C::TILE;
+            // scores: sacc[0] keys 0..31, sacc[1] keys 32..63 of the tile
+            f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int e0 = 32 * (ks >> 1) + 16 * (ks & 1);
-            const bf16x4 lo = *reinterpret_cast<const bf16x4*>(kb + l32 * LDK + e0 + 4 * g);
-            const bf16x4 hi = *reinterpret_cast<const bf16x4*>(kb + l32 * LDK + e0 + 8 + 4 * g);
-            sacc = mfma32(cat(lo, hi), qb[ks], sacc);
-        }
-        const int jleft = L - kt * BN;  // valid keys in this tile
-        if (jleft < BN) {
+            for (int k = 0; k < C::KST; ++k) {
+                const int e0 = 32 * (k >> 1) + 16 * (k & 1) + 4 * g;
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                const int j = (rr >> 2) * 8 + 4 * g + (rr & 3);
-                if (j >= jleft) sacc[rr] = -INFINITY;
+                for (int hh = 0; hh < 2; ++hh) {
+                    const bf16* row = kb + (hh * 32 + l32) * C::LDK + e0;
+                    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row);
+                    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 8);
+                    sacc[hh] = mfma32(cat(lo, hi), qb[k], sacc[hh]);
+                }
+            }
+            const int jleft = L - t * BN;
+            if (jleft < BN) {
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int rr = 0; rr < 16; ++rr) {
+                        const int j = hh * 32 + (rr >> 2) * 8 + 4 * g + (rr & 3);
+                        if (j >= jleft) sacc[hh][rr] = -INFINITY;
+                    }
+            }
+            float mt = fmaxf(sacc[0][0], sacc[0][1]);
+#pragma unroll
+            for (int rr = 2; rr < 16; rr += 2) mt = fmaxf(mt, fmaxf(sacc[0][rr], sacc[0][rr + 1]));
+#pragma unroll
+            for (int rr = 0; rr < 16; rr += 2) mt = fmaxf(mt, fmaxf(sacc[1][rr], sacc[1][rr + 1]));
+            mt *= scale_log2;
+            if (__any(mt > m_run + kLazy)) {
+                const float m_new = fmaxf(m_run, fmaxf(mt, xor32(mt)));
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                m_run = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int eb = 0; eb < C::EB; ++eb) oacc[eb] *= alpha;
+            }
+            bf16x8 pb[4];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int rr = 0; rr < 16; rr += 2) {
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[hh][rr], scale_log2, -m_run));
+                    const float p1 =
+                        __builtin_amdgcn_exp2f(fmaf(sacc[hh][rr + 1], scale_log2, -m_run));
+                    const bf16x2 pp = {(bf16)p0, (bf16)p1};
+                    l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run, false);
+                    pb[hh * 2 + (rr >> 3)][rr & 7] = pp[0];
+                    pb[hh * 2 + (rr >> 3)][(rr & 7) + 1] = pp[1];
+                }
+            // O^T += V^T P^T over the four 16-key slabs of the tile
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+#pragma unroll
+                for (int eb = 0; eb < C::EB; ++eb) {
+                    const bf16* base = vb + (16 * u + tr_row) * C::LDK + eb * 32 + tr_col;
+                    const bf16x4 lo = lds_read_tr16(base);
+                    const bf16x4 hi = lds_read_tr16(base + 8 * C::LDK);
+                    oacc[eb] = mfma32(cat(lo, hi), pb[u], oacc[eb]);
+                }
             }
         }
-        float mt = sacc[0];
-#pragma unroll
-        for (int rr = 1; rr < 16; ++rr) mt = fmaxf(mt, sacc[rr]);
-        mt = fmaxf(mt, xor32(mt));
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = exp2f((m_run - m_new) * scale_log2);
-        const float mb = m_new * scale_log2;
-        bf16x8 pb[2];
-        float psum = 0.f;
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-            const float p = exp2f(fmaf(sacc[rr], scale_log2, -mb));
-            psum += p;
-            pb[rr >> 3][rr & 7] = (bf16)p;
-        }
-        l_run = fmaf(l_run, alpha, psum);
-        m_run = m_new;
-#pragma unroll
-        for (int eb = 0; eb < EB; ++eb) oacc[eb] *= alpha;
-
-        // O^T += V^T P^T over the two 16-key halves of the tile
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-#pragma unroll
-            for (int eb = 0; eb < EB; ++eb) {
-                const bf16* base = vb + (16 * u + tr_row) * LDK + eb * 32 + tr_col;
-                const bf16x4 lo = lds_read_tr16(base);
-                const bf16x4 hi = lds_read_tr16(base + 8 * LDK);
-                oacc[eb] = mfma32(cat(lo, hi), pb[u], oacc[eb]);
-            }
-        }
-        if (kt + 1 < ntiles_kv) lstore(buf ^ 1);
+        if (next) lstore(buf ^ 1);
         __syncthreads();
     }
 
-    // ---- 3. normalise and store ----
-    const float l_tot = l_run + xor32(l_run);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    // ---------------- 3. merge the memory splits, normalise, store ----------------
+    l_run += xor32(l_run);   // both halves' keys
+    if constexpr (KSPLIT > 1) {
+        float* cmb = reinterpret_cast<float*>(smem);
+        constexpr int PER = C::EB * 16 + 2;
+        if (ksg > 0) {
+            float* dst = cmb + ((size_t)(rb * (KSPLIT - 1) + ksg - 1) * PER) * 64;
+#pragma unroll
+            for (int eb = 0; eb < C::EB; ++eb)
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) dst[(eb * 16 + rr) * 64 + lane] = oacc[eb][rr];
+            dst[(PER - 2) * 64 + lane] = m_run;
+            dst[(PER - 1) * 64 + lane] = l_run;
+        }
+        __syncthreads();
+        if (ksg > 0) return;
+#pragma unroll
+        for (int k = 1; k < KSPLIT; ++k) {
+            const float* src = cmb + ((size_t)(rb * (KSPLIT - 1) + k - 1) * PER) * 64;
+            const float mk = src[(PER - 2) * 64 + lane];
+            const float lk = src[(PER - 1) * 64 + lane];
+            const float m_new = fmaxf(m_run, mk);
+            // a split that saw no memory rows (m = -inf) contributes nothing
+            const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+            const float a1 = mk == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mk - m_new);
+            l_run = l_run * a0 + lk * a1;
+#pragma unroll
+            for (int eb = 0; eb < C::EB; ++eb)
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr)
+                    oacc[eb][rr] = oacc[eb][rr] * a0 + src[(eb * 16 + rr) * 64 + lane] * a1;
+            m_run = m_new;
+        }
+    }
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     if (qvalid) {
         bf16* orow = O + ((size_t)cand * q + s) * d + h * DH;
 #pragma unroll
-        for (int eb = 0; eb < EB; ++eb) {
+        for (int eb = 0; eb < C::EB; ++eb) {
 #pragma unroll
             for (int b4 = 0; b4 < 4; ++b4) {
                 bf16x4 v;
@@ -229,7 +383,8 @@ __global__ __launch_bounds__(64 * WAVES) void attn_bf16_kernel(
     }
 }
 
-// Standalone projection: Q[c][s][e] for a 32(e) x 32(cand) block per wave.
+// Standalone projection: Q[c][s][e] for a 32(e) x 32(cand) block per wave,
+// operands read straight from global memory.
 template <int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void project_bf16_kernel(
     const bf16* __restrict__ Z, const bf16* __restrict__ Wq, int total_cand, int q, int d,
@@ -241,8 +396,14 @@ __global__ __launch_bounds__(64 * WAVES) void project_bf16_kernel(
     const int s = blockIdx.z;
     const bool valid = cand < total_cand;
     const bf16* zrow = valid ? Z + ((size_t)cand * q + s) * d : nullptr;
+    const bf16* wrow = Wq + ((size_t)s * d + e0 + l32) * d;
+    const bf16x8 zero = {};
     f32x16 acc = {};
-    project_acc(Wq + ((size_t)s * d + e0 + l32) * d, zrow, d, g, acc);
+    for (int k0 = 0; k0 < d; k0 += 16) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(wrow + k0 + 8 * g);
+        const bf16x8 b = zrow ? *reinterpret_cast<const bf16x8*>(zrow + k0 + 8 * g) : zero;
+        acc = mfma32(a, b, acc);
+    }
     if (valid) {
         bf16* qrow = Q + ((size_t)cand * q + s) * d + e0;
 #pragma unroll
@@ -255,47 +416,98 @@ __global__ __launch_bounds__(64 * WAVES) void project_bf16_kernel(
     }
 }
 
-template <int DH, int WAVES, bool SEP>
+// Variants whose LDS footprint exceeds this are not built (they would leave
+// one work-group per compute unit at best); the host picks another.
+constexpr int kMaxSmem = 81920;
+
+template <int DH, int RB, int KSPLIT, bool SEP>
+constexpr bool fits() {
+    return Cfg<DH, RB, KSPLIT, SEP>::SMEM <= kMaxSmem;
+}
+
+template <int DH, int RB, int KSPLIT, bool SEP>
 hipError_t launch_one(const void* Z, const void* Wq, const void* K, const void* V,
                       const int* cu_kv, const void* ws, int64_t max_tiles, int q, int d,
                       int heads, void* O, hipStream_t stream) {
+    if constexpr (!fits<DH, RB, KSPLIT, SEP>()) {
+        return hipErrorInvalidValue;
+    } else {
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)DH);
     const int64_t blocks = max_tiles * heads;
     if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL((attn_bf16_kernel<DH, WAVES, SEP>), dim3((unsigned)blocks),
-                       dim3(64 * WAVES), 0, stream, static_cast<const bf16*>(Z),
+    hipLaunchKernelGGL((attn_bf16_kernel<DH, RB, KSPLIT, SEP>), dim3((unsigned)blocks),
+                       dim3(64 * RB * KSPLIT), 0, stream, static_cast<const bf16*>(Z),
                        static_cast<const bf16*>(Wq), static_cast<const bf16*>(K),
                        static_cast<const bf16*>(V), cu_kv, static_cast<const int*>(ws), q, d,
                        heads, scale_log2, static_cast<bf16*>(O));
     return hipGetLastError();
+    }
 }
 
-template <int DH, int WAVES>
-hipError_t launch_dh_w(const void* Z, const void* Wq, const void* K, const void* V,
-                       const int* cu_kv, const void* ws, int64_t max_tiles, int q, int d,
-                       int heads, void* O, hipStream_t stream) {
-    if (V) return launch_one<DH, WAVES, true>(Z, Wq, K, V, cu_kv, ws, max_tiles, q, d, heads, O, stream);
-    return launch_one<DH, WAVES, false>(Z, Wq, K, V, cu_kv, ws, max_tiles, q, d, heads, O, stream);
+template <int DH, int RB, int KSPLIT>
+hipError_t launch_sep(const void* Z, const void* Wq, const void* K, const void* V,
+                      const int* cu_kv, const void* ws, int64_t max_tiles, int q, int d,
+                      int heads, void* O, hipStream_t stream) {
+    if (V)
+        return launch_one<DH, RB, KSPLIT, true>(Z, Wq, K, V, cu_kv, ws, max_tiles, q, d, heads, O,
+                                                stream);
+    return launch_one<DH, RB, KSPLIT, false>(Z, Wq, K, V, cu_kv, ws, max_tiles, q, d, heads, O,
+                                             stream);
 }
 
 template <int DH>
 hipError_t launch_dh(const void* Z, const void* Wq, const void* K, const void* V,
                      const int* cu_kv, const void* ws, int64_t max_tiles, int q, int d,
-                     int heads, int waves, void* O, hipStream_t stream) {
-    if (waves == 4) return launch_dh_w<DH, 4>(Z, Wq, K, V, cu_kv, ws, max_tiles, q, d, heads, O, stream);
-    return launch_dh_w<DH, 2>(Z, Wq, K, V, cu_kv, ws, max_tiles, q, d, heads, O, stream);
+                     int heads, int rb, int ksplit, void* O, hipStream_t stream) {
+#define XATTN_CASE(R_, S_)                                                                     \
+    if (rb == R_ && ksplit == S_)                                                              \
+        return launch_sep<DH, R_, S_>(Z, Wq, K, V, cu_kv, ws, max_tiles, q, d, heads, O, stream);
+    XATTN_CASE(1, 4)
+    XATTN_CASE(2, 2)
+    XATTN_CASE(4, 1)
+    XATTN_CASE(2, 1)
+#undef XATTN_CASE
+    return hipErrorInvalidValue;
+}
+
+template <int DH>
+bool variant_fits(int rb, int ksplit, bool sep) {
+#define XATTN_FIT(R_, S_)                                                                      \
+    if (rb == R_ && ksplit == S_) return sep ? fits<DH, R_, S_, true>() : fits<DH, R_, S_, false>();
+    XATTN_FIT(1, 4)
+    XATTN_FIT(2, 2)
+    XATTN_FIT(4, 1)
+    XATTN_FIT(2, 1)
+#undef XATTN_FIT
+    return false;
 }
 
 }  // namespace
 
+bool attn_bf16_variant_ok(int dh, int rb, int ksplit, bool sep) {
+    switch (dh) {
+        case 32: return variant_fits<32>(rb, ksplit, sep);
+        case 64: return variant_fits<64>(rb, ksplit, sep);
+        case 128: return variant_fits<128>(rb, ksplit, sep);
+        default: return false;
+    }
+}
+
 hipError_t launch_attn_bf16(const void* Z, const void* Wq, const void* K, const void* V,
                             const int* cu_kv, const void* ws, int64_t max_tiles, int q, int d,
-                            int heads, int waves, void* O, hipStream_t stream) {
+                            int heads, int rb, int ksplit, void* O, hipStream_t stream) {
     switch (d / heads) {
-        case 32: return launch_dh<32>(Z, Wq, K, V, cu_kv, ws, max_tiles, q, d, heads, waves, O, stream);
-        case 64: return launch_dh<64>(Z, Wq, K, V, cu_kv, ws, max_tiles, q, d, heads, waves, O, stream);
-        case 128: return launch_dh<128>(Z, Wq, K, V, cu_kv, ws, max_tiles, q, d, heads, waves, O, stream);
-        default: return hipErrorInvalidValue;
+        case 32:
+            return launch_dh<32>(Z, Wq, K, V, cu_kv, ws, max_tiles, q, d, heads, rb, ksplit, O,
+                                 stream);
+        case 64:
+            return launch_dh<64>(Z, Wq, K, V, cu_kv, ws, max_tiles, q, d, heads, rb, ksplit, O,
+                                 stream);
+        case 128:
+            return launch_dh<128>(Z, Wq, K, V, cu_kv, ws, max_tiles, q, d, heads, rb, ksplit, O,
+                                  stream);
+        default:
+            return hipErrorInvalidValue;
     }
 }
 

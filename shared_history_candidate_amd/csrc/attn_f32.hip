@@ -16,6 +16,7 @@ namespace {
 
 constexpr int kRows = 64;  // candidates per work item (tile_m of the fp32 path)
 constexpr int kBN = 32;    // memory rows per tile
+constexpr int kKC = 32;    // projection chunk (input features)
 
 template <int DHMAX>
 __global__ __launch_bounds__(kRows) void attn_f32_kernel(
@@ -24,6 +25,7 @@ __global__ __launch_bounds__(kRows) void attn_f32_kernel(
     int q, int d, int heads, float scale_log2, float* __restrict__ O) {
     __shared__ float ks[kBN][DHMAX];
     __shared__ float vs[kBN][DHMAX];
+    __shared__ float wsm[DHMAX][kKC + 1];
     const int dh = d / heads;
     const int n_tiles = ws[kPlanNTiles];
     const int tile = blockIdx.x / heads;
@@ -38,18 +40,28 @@ __global__ __launch_bounds__(kRows) void attn_f32_kernel(
     const bool valid = i < nc;
     const int cand = c0 + i;
 
-    // projection: qv[e] = sum_k Z[cand][s][k] * W[s][h*dh + e][k]
+    // projection: qv[e] = sum_k Z[cand][s][k] * W[s][h*dh + e][k], with W_h
+    // staged through LDS in chunks of kKC input features
     float qv[DHMAX];
 #pragma unroll
     for (int e = 0; e < DHMAX; ++e) qv[e] = 0.f;
-    if (valid) {
-        const float* zrow = Z + ((size_t)cand * q + s) * d;
+    {
+        const float* zrow = Z + ((size_t)(valid ? cand : c0) * q + s) * d;
         const float* w = Wq + ((size_t)s * d + h * dh) * d;
-        for (int k = 0; k < d; ++k) {
-            const float z = zrow[k];
+        for (int k0 = 0; k0 < d; k0 += kKC) {
+            float zc[kKC];
 #pragma unroll
-            for (int e = 0; e < DHMAX; ++e)
-                if (e < dh) qv[e] = fmaf(z, w[(size_t)e * d + k], qv[e]);
+            for (int kk = 0; kk < kKC; ++kk) zc[kk] = (k0 + kk < d) ? zrow[k0 + kk] : 0.f;
+            for (int idx = i; idx < DHMAX * kKC; idx += kRows) {
+                const int e = idx / kKC, kk = idx % kKC;
+                wsm[e][kk] = (e < dh && k0 + kk < d) ? w[(size_t)e * d + k0 + kk] : 0.f;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int kk = 0; kk < kKC; ++kk)
+#pragma unroll
+                for (int e = 0; e < DHMAX; ++e) qv[e] = fmaf(zc[kk], wsm[e][kk], qv[e]);
+            __syncthreads();
         }
     }
 
