@@ -25,6 +25,12 @@ HIPCC_FLAGS = [
     "-Wall", "-Wno-unused-function",
     # keep the compiler from emitting packed-fp32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs: no accvgpr moves before the
+    # softmax arithmetic reads the scores
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # NaN operands are not supported inputs; without this every fmaxf operand
+    # is canonicalised first (infinities are still honoured)
+    "-fno-honor-nans",
     "-I" + INCLUDE, "-I" + CSRC,
 ]
 
@@ -37,7 +43,8 @@ def _hipcc() -> str:
 
 
 def _compile(src: str, obj: str, verbose: bool) -> None:
-    cmd = [_hipcc()] + HIPCC_FLAGS + ["-c", src, "-o", obj]
+    extra = os.environ.get("XATTN_EXTRA_HIPCC_FLAGS", "").split()   # tuning experiments
+    cmd = [_hipcc()] + HIPCC_FLAGS + extra + ["-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd = [_hipcc(), "-O3", "-std=c++17", "-fPIC", "-Wall", "-I" + INCLUDE, "-I" + CSRC,
                "-c", src, "-o", obj]
@@ -51,22 +58,22 @@ def _compile(src: str, obj: str, verbose: bool) -> None:
         print(errs)
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    """Compile every HIP/C++ source under csrc/ and link libxattn.so."""
+def build(verbose: bool = False, jobs: int = 8, out: str = LIB) -> str:
+    """Compile every HIP/C++ source under csrc/ and link libxattn.so (or `out`)."""
     os.makedirs(OBJDIR, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     objs = [os.path.join(OBJDIR, os.path.basename(s) + ".o") for s in srcs]
     with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
         list(ex.map(lambda so: _compile(so[0], so[1], verbose), zip(srcs, objs)))
-    tmp = LIB + ".tmp%d" % os.getpid()
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [_hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed:\n" + res.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

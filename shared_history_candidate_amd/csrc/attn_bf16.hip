@@ -43,6 +43,10 @@ namespace xattn {
 
 namespace {
 
+#ifndef XATTN_LDS_PAD
+#define XATTN_LDS_PAD 4
+#endif
+
 constexpr int BN = 64;               // memory rows per tile
 constexpr float kLazy = 8.0f;        // exp2-domain headroom of the running maximum
 
@@ -60,7 +64,12 @@ struct Cfg {
     static constexpr int NT = 64 * NW;
     static constexpr int EB = DH / 32;        // 32-wide feature blocks
     static constexpr int KST = DH / 16;       // k-steps of the score product
-    static constexpr int LDK = DH + 8;        // memory tile pitch (elements)
+    static constexpr int PAD = XATTN_LDS_PAD; // row padding of the memory tile (elements)
+    static constexpr int LDK = DH + PAD;      // memory tile pitch (elements)
+    // one wave per split: a wave reads only the tiles it stored itself, so the
+    // memory loop needs no work-group barrier (a wave's LDS operations retire
+    // in program order)
+    static constexpr bool PRIVATE = RB == 1;
     static constexpr int PLANES = SEP ? 2 : 1;
     static constexpr int TILE = BN * LDK;     // elements per plane per buffer
     static constexpr int KV_BYTES = KSPLIT * 2 * PLANES * TILE * 2;
@@ -75,7 +84,8 @@ struct Cfg {
     static constexpr int SMEM = P1_BYTES > KV_BYTES ? (P1_BYTES > CMB_BYTES ? P1_BYTES : CMB_BYTES)
                                                     : (KV_BYTES > CMB_BYTES ? KV_BYTES : CMB_BYTES);
     static constexpr int KV_CHUNKS = BN * DH / 8;                 // 16-byte chunks per plane
-    static constexpr int KV_CPT = (KV_CHUNKS + 64 * RB - 1) / (64 * RB);
+    static constexpr int KV_CPT = KV_CHUNKS / (64 * RB);
+    static_assert(KV_CHUNKS % (64 * RB) == 0, "memory tile must split evenly over a split group");
     static constexpr int MYEB = (EB + KSPLIT - 1) / KSPLIT;       // e-blocks projected per wave
 };
 
@@ -128,7 +138,10 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(
     const int L = cu_kv[r + 1] - kv0;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
+    const int lane = tid & 63;
+    // the wave index is uniform across the wave: keep it (and every tile
+    // address derived from it) in scalar registers
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int rb = w % RB, ksg = w / RB;     // query block, memory split
     const int g = lane >> 5, l32 = lane & 31;
     const int qcol = rb * 32 + l32;
@@ -218,30 +231,52 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(
     const bf16* Vh = SEP ? V + (size_t)kv0 * d + h * DH : nullptr;
     uint4 kreg[C::KV_CPT];
     uint4 vreg[SEP ? C::KV_CPT : 1];
-
-    auto gload = [&](int t) {
+    // Chunk u of this thread: tile row j_u, 16-byte column chunk c8_u.  Its
+    // global byte offset inside a tile and its LDS element offset are fixed;
+    // tiles differ only by the buffer base.  Buffer loads return zeros past
+    // the request's last memory row, so partial tiles need no special case.
+    int goff[C::KV_CPT], loff[C::KV_CPT];
 #pragma unroll
-        for (int u = 0; u < C::KV_CPT; ++u) {
-            const int c = gt + u * 64 * RB;
-            const int j = c / (DH / 8), c8 = c % (DH / 8);
-            const int jj = t * BN + j;
-            const bool ok = (c < C::KV_CHUNKS) && (jj < L);
-            const size_t off = (size_t)jj * d + c8 * 8;
-            kreg[u] = ok ? *reinterpret_cast<const uint4*>(Kh + off) : make_uint4(0, 0, 0, 0);
-            if constexpr (SEP)
-                vreg[u] = ok ? *reinterpret_cast<const uint4*>(Vh + off) : make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < C::KV_CPT; ++u) {
+        const int c = gt + u * 64 * RB;
+        const int j = c / (DH / 8), c8 = c % (DH / 8);
+        goff[u] = (j * d + c8 * 8) * 2;
+        loff[u] = j * C::LDK + c8 * 8;
+    }
+    auto gload = [&](int t) {
+        const size_t row0 = (size_t)t * BN;
+        const size_t rest = (size_t)(L - (int)row0) * d * 2;   // bytes left in the request
+        const uint32_t bytes = rest > 0xFFFFFFF0u ? 0xFFFFFFF0u : (uint32_t)rest;
+        const __amdgpu_buffer_rsrc_t rk =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(Kh + row0 * d), (short)0, bytes, 0x00020000);
+#pragma unroll
+        for (int u = 0; u < C::KV_CPT; ++u)
+            kreg[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, goff[u], 0, 0));
+        if constexpr (SEP) {
+            const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(Vh + row0 * d), (short)0, bytes, 0x00020000);
+#pragma unroll
+            for (int u = 0; u < C::KV_CPT; ++u)
+                vreg[u] =
+                    __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, goff[u], 0, 0));
         }
     };
     auto lstore = [&](int buf) {
         bf16* base = kvl + buf * C::PLANES * C::TILE;
 #pragma unroll
         for (int u = 0; u < C::KV_CPT; ++u) {
-            const int c = gt + u * 64 * RB;
-            if (c < C::KV_CHUNKS) {
-                const int j = c / (DH / 8), c8 = c % (DH / 8);
-                *reinterpret_cast<uint4*>(base + j * C::LDK + c8 * 8) = kreg[u];
-                if constexpr (SEP)
-                    *reinterpret_cast<uint4*>(base + C::TILE + j * C::LDK + c8 * 8) = vreg[u];
+            if constexpr (C::PAD % 8 == 0) {
+                *reinterpret_cast<uint4*>(base + loff[u]) = kreg[u];
+                if constexpr (SEP) *reinterpret_cast<uint4*>(base + C::TILE + loff[u]) = vreg[u];
+            } else {   // rows are only 8-byte aligned
+                uint2* p = reinterpret_cast<uint2*>(base + loff[u]);
+                p[0] = make_uint2(kreg[u].x, kreg[u].y);
+                p[1] = make_uint2(kreg[u].z, kreg[u].w);
+                if constexpr (SEP) {
+                    uint2* pv = reinterpret_cast<uint2*>(base + C::TILE + loff[u]);
+                    pv[0] = make_uint2(vreg[u].x, vreg[u].y);
+                    pv[1] = make_uint2(vreg[u].z, vreg[u].w);
+                }
             }
         }
     };
@@ -267,19 +302,38 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(
         if (have) {
             const bf16* kb = kvl + buf * C::PLANES * C::TILE;
             const bf16* vb = kb + (C::PLANES - 1) * C::TILE;
-            // scores: sacc[0] keys 0..31, sacc[1] keys 32..63 of the tile
-            f32x16 sacc[2] = {f32x16{}, f32x16{}};
+            // scores: sacc[0] keys 0..31, sacc[1] keys 32..63 of the tile.
+            // All K fragments are read before the first product so that the
+            // LDS latency is paid once per tile.
+            bf16x8 kf[2][C::KST];
 #pragma unroll
             for (int k = 0; k < C::KST; ++k) {
                 const int e0 = 32 * (k >> 1) + 16 * (k & 1) + 4 * g;
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     const bf16* row = kb + (hh * 32 + l32) * C::LDK + e0;
-                    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row);
-                    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 8);
-                    sacc[hh] = mfma32(cat(lo, hi), qb[k], sacc[hh]);
+                    kf[hh][k] = cat(*reinterpret_cast<const bf16x4*>(row),
+                                    *reinterpret_cast<const bf16x4*>(row + 8));
                 }
             }
+            f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+            for (int k = 0; k < C::KST; ++k)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) sacc[hh] = mfma32(kf[hh][k], qb[k], sacc[hh]);
+            // scheduling: every K-fragment read ahead of the score products
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::KST, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::KST, 0);
+            // V^T fragments for the output product, issued now so that they
+            // arrive while the weights are being computed
+            bf16x8 vf[4][C::EB];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int eb = 0; eb < C::EB; ++eb) {
+                    const bf16* base = vb + (16 * u + tr_row) * C::LDK + eb * 32 + tr_col;
+                    vf[u][eb] = cat(lds_read_tr16(base), lds_read_tr16(base + 8 * C::LDK));
+                }
             const int jleft = L - t * BN;
             if (jleft < BN) {
 #pragma unroll
@@ -319,19 +373,14 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(
                 }
             // O^T += V^T P^T over the four 16-key slabs of the tile
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < 4; ++u)
 #pragma unroll
-                for (int eb = 0; eb < C::EB; ++eb) {
-                    const bf16* base = vb + (16 * u + tr_row) * C::LDK + eb * 32 + tr_col;
-                    const bf16x4 lo = lds_read_tr16(base);
-                    const bf16x4 hi = lds_read_tr16(base + 8 * C::LDK);
-                    oacc[eb] = mfma32(cat(lo, hi), pb[u], oacc[eb]);
-                }
-            }
+                for (int eb = 0; eb < C::EB; ++eb) oacc[eb] = mfma32(vf[u][eb], pb[u], oacc[eb]);
         }
         if (next) lstore(buf ^ 1);
-        __syncthreads();
+        if constexpr (!C::PRIVATE) __syncthreads();
     }
+    if constexpr (C::PRIVATE) __syncthreads();   // the merge below reuses the tile buffers
 
     // ---------------- 3. merge the memory splits, normalise, store ----------------
     l_run += xor32(l_run);   // both halves' keys

@@ -14,7 +14,8 @@ from typing import Optional
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libxattn.so")
+_LIB_PATH = os.environ.get("XATTN_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libxattn.so")
 _lib = None
 
 XATTN_OK, XATTN_EINVAL, XATTN_EUNSUPPORTED, XATTN_EHIP, XATTN_EWORKSPACE = 0, -1, -2, -3, -4
