@@ -52,7 +52,7 @@ Variant choose_variant(const xattn_config& c, int R, int total_cand, int total_k
     const bool sep = c.kv_mode == XATTN_KV_SEPARATE;
     if (const char* env = getenv("XATTN_VARIANT")) {
         int rb = 0, ks = 0;
-        if (sscanf(env, "%d,%d", &rb, &ks) == 2 && xattn::attn_bf16_variant_ok(dh, rb, ks, sep))
+        if (sscanf(env, "%d,%d", &rb, &ks) == 2 && xattn::attn_bf16_variant_smem(dh, rb, ks, sep))
             return {rb, ks};
     }
     const double rows = (double)total_cand * c.n_slots * heads;   // query rows x heads
@@ -60,11 +60,20 @@ Variant choose_variant(const xattn_config& c, int R, int total_cand, int total_k
     Variant v{2, 2};
     if (rows / 128.0 >= 4096.0) v = {4, 1};   // many query tiles already fill the chip
     else if (rows / 64.0 < 1024.0 && mean_L >= 1024.0) v = {1, 4};   // few tiles, long memory
-    // fall back to a variant that is built for this head width and mode
-    const Variant order[] = {v, {2, 2}, {4, 1}, {2, 1}};
-    for (const Variant& o : order)
-        if (xattn::attn_bf16_variant_ok(dh, o.rb, o.ksplit, sep)) return o;
-    return {2, 1};
+    // Take the preferred variant if it leaves room for two work-groups per
+    // compute unit, else the first such fallback, else the smallest built one.
+    const Variant order[] = {v, {2, 2}, {4, 1}, {1, 4}, {2, 1}};
+    for (const Variant& o : order) {
+        const int sm = xattn::attn_bf16_variant_smem(dh, o.rb, o.ksplit, sep);
+        if (sm > 0 && sm <= 81920) return o;
+    }
+    Variant best{2, 1};
+    int best_sm = 1 << 30;
+    for (const Variant& o : order) {
+        const int sm = xattn::attn_bf16_variant_smem(dh, o.rb, o.ksplit, sep);
+        if (sm > 0 && sm < best_sm) best = o, best_sm = sm;
+    }
+    return best;
 }
 
 int tile_m_for(const xattn_config& c, int R, int total_cand, int total_kv, int heads) {

@@ -465,9 +465,10 @@ __global__ __launch_bounds__(64 * WAVES) void project_bf16_kernel(
     }
 }
 
-// Variants whose LDS footprint exceeds this are not built (they would leave
-// one work-group per compute unit at best); the host picks another.
-constexpr int kMaxSmem = 81920;
+// Variants whose LDS footprint exceeds what one work-group may hold are not
+// built; the host prefers variants that leave room for two work-groups per
+// compute unit (attn_bf16_variant_smem).
+constexpr int kMaxSmem = 163840;
 
 template <int DH, int RB, int KSPLIT, bool SEP>
 constexpr bool fits() {
@@ -519,26 +520,32 @@ hipError_t launch_dh(const void* Z, const void* Wq, const void* K, const void* V
     return hipErrorInvalidValue;
 }
 
+template <int DH, int RB, int KSPLIT, bool SEP>
+constexpr int smem_if_built() {
+    return fits<DH, RB, KSPLIT, SEP>() ? Cfg<DH, RB, KSPLIT, SEP>::SMEM : 0;
+}
+
 template <int DH>
-bool variant_fits(int rb, int ksplit, bool sep) {
+int variant_smem(int rb, int ksplit, bool sep) {
 #define XATTN_FIT(R_, S_)                                                                      \
-    if (rb == R_ && ksplit == S_) return sep ? fits<DH, R_, S_, true>() : fits<DH, R_, S_, false>();
+    if (rb == R_ && ksplit == S_)                                                              \
+        return sep ? smem_if_built<DH, R_, S_, true>() : smem_if_built<DH, R_, S_, false>();
     XATTN_FIT(1, 4)
     XATTN_FIT(2, 2)
     XATTN_FIT(4, 1)
     XATTN_FIT(2, 1)
 #undef XATTN_FIT
-    return false;
+    return 0;
 }
 
 }  // namespace
 
-bool attn_bf16_variant_ok(int dh, int rb, int ksplit, bool sep) {
+int attn_bf16_variant_smem(int dh, int rb, int ksplit, bool sep) {
     switch (dh) {
-        case 32: return variant_fits<32>(rb, ksplit, sep);
-        case 64: return variant_fits<64>(rb, ksplit, sep);
-        case 128: return variant_fits<128>(rb, ksplit, sep);
-        default: return false;
+        case 32: return variant_smem<32>(rb, ksplit, sep);
+        case 64: return variant_smem<64>(rb, ksplit, sep);
+        case 128: return variant_smem<128>(rb, ksplit, sep);
+        default: return 0;
     }
 }
 

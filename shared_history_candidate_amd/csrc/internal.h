@@ -12,9 +12,9 @@ hipError_t launch_plan(const int* cu_kv, const int* cu_cand, int R, int q, int t
 
 // bf16 fused projection + attention.  A work-group has rb x ksplit waves:
 // rb query blocks of 32 candidates (tile_m = 32 * rb) and ksplit memory
-// splits merged on chip.  attn_bf16_variant_ok tells whether (rb, ksplit) is
-// built for head width dh and the K/V mode.
-bool attn_bf16_variant_ok(int dh, int rb, int ksplit, bool sep);
+// splits merged on chip.  attn_bf16_variant_smem returns the LDS bytes of
+// variant (rb, ksplit) for head width dh and the K/V mode, 0 if not built.
+int attn_bf16_variant_smem(int dh, int rb, int ksplit, bool sep);
 hipError_t launch_attn_bf16(const void* Z, const void* Wq, const void* K, const void* V,
                             const int* cu_kv, const void* ws, int64_t max_tiles, int q, int d,
                             int heads, int rb, int ksplit, void* O, hipStream_t stream);
