@@ -25,10 +25,12 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
-# workload name -> roofline bound of the fused kernel on that workload
-BOUND = {"rest": "mfma", "long": "mfma", "transx": "hbm", "ragged": "hbm", "tiny": "alu"}
-KERNEL_SOURCES = ["shared_history_candidate_amd/csrc/attn_bf16.hip",
-                  "shared_history_candidate_amd/csrc/common.h"]
+CONFIGS = ("rest", "long", "transx", "ragged", "tiny")
+KERNEL_SOURCES = {"attention": ["shared_history_candidate_amd/csrc/attn_bf16.hip",
+                                "shared_history_candidate_amd/csrc/common.h"],
+                  "projection": ["shared_history_candidate_amd/csrc/gemm_bf16.hip",
+                                 "shared_history_candidate_amd/csrc/plan_device.h",
+                                 "shared_history_candidate_amd/csrc/common.h"]}
 
 
 def parse():
@@ -36,7 +38,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", default="rest", choices=sorted(BOUND))
+    p.add_argument("--config", default="rest", choices=CONFIGS)
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle baseline sample")
@@ -86,24 +88,41 @@ def micro():
     print(json.dumps({k: (round(v, 3) if isinstance(v, float) else v) for k, v in res.items()}))
 
 
-def kernel_sha():
+def kernel_sha(kernel):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kernel]:
         h.update(open(os.path.join(ROOT, f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def traffic_for(config, dispatches_per_step=1):
-    """HBM bytes per launch of the fused kernel from committed rocprofv3 counter
-    runs (FETCH_SIZE, WRITE_SIZE scaled by a copy-kernel calibration), or None
+def traffic_for(kernel, config):
+    """HBM bytes per launch of a kernel from committed rocprofv3 counter runs
+    (FETCH_SIZE and WRITE_SIZE, scaled by a copy-kernel calibration), or None
     when absent or taken on a different kernel source."""
-    path = os.path.join(ROOT, "profiles", "counters_attn_%s.json" % config)
+    path = os.path.join(ROOT, "profiles", "counters_%s_%s.json" % (kernel, config))
     if not os.path.exists(path):
         return None
     c = json.load(open(path))
-    if c.get("kernel_source_sha") != kernel_sha():
+    if c.get("kernel_source_sha") != kernel_sha(kernel):
         return None
     return (c["fetch_kib"] + c["write_kib"]) * 1024.0 * c["copy_calibration"]
+
+
+def roofline(flops, nbytes, ms, dtype):
+    """Bound of a kernel by its arithmetic intensity against the ridge point,
+    and the achieved rate against that bound's MI355X peak."""
+    peak_flops = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_FP32_TFLOPS
+    ridge = peak_flops * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if dtype != "bf16":
+        bound = "alu"
+    else:
+        bound = "mfma" if flops / nbytes >= ridge else "hbm"
+    if bound == "hbm":
+        achieved, peak, unit = nbytes / (ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
+    else:
+        achieved, peak, unit = flops / (ms * 1e-3) / 1e12, peak_flops, "TFLOP/s"
+    return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 5)}
 
 
 def cpu_baseline(wl, target_s):
@@ -195,32 +214,41 @@ def main():
     ms_per_step = t0.elapsed_time(t1) / args.steps
     print("bench: %d steps, %.4f ms/step" % (args.steps, ms_per_step), file=sys.stderr, flush=True)
 
-    # Dominant kernel alone: the fused attention kernel over the plan the last
-    # step left in the workspace, one event pair per launch on its stream.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for a, b in evs:
-        a.record(stream)
-        ctx.attend(t["Z"], t["W_Q"], t["K"], t["V"], t["cu_kv"], t["cu_cand"], wl.heads, ws,
-                   O=O, stream=stream)
-        b.record(stream)
-    torch.cuda.synchronize()
-    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    print("bench: attention kernel %.4f ms/launch" % kern_ms, file=sys.stderr, flush=True)
+    # Each kernel alone, one HIP event pair per launch on its stream: the
+    # projection (into a query buffer) and the attention kernel over those
+    # queries and the plan the last step left in the workspace.
+    Qbuf = torch.empty_like(O)
 
-    flops, nbytes = wl.flops(), wl.bytes()
-    bound = BOUND[args.config]
-    if bound == "mfma":
-        achieved, peak, unit = flops / (kern_ms * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
-    elif bound == "hbm":
-        achieved, peak, unit = nbytes / (kern_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
-    else:
-        achieved, peak, unit = flops / (kern_ms * 1e-3) / 1e12, PEAK_FP32_TFLOPS, "TFLOP/s"
-    roof = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 5), "traffic": traffic_for(args.config),
-            "kernel": "attn_bf16_kernel" if wl.dtype == "bf16" else "attn_f32_kernel",
-            "kernel_ms": round(kern_ms, 5),
-            "algorithmic_flops": flops, "algorithmic_bytes": nbytes}
+    def per_launch_ms(fn):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    proj_ms = per_launch_ms(lambda: ctx.project(t["Z"], t["W_Q"], Q=Qbuf, stream=stream))
+    attn_ms = per_launch_ms(lambda: ctx.attend_q(Qbuf, t["K"], t["V"], t["cu_kv"], t["cu_cand"],
+                                                 wl.heads, ws, O=O, stream=stream))
+    print("bench: projection %.4f ms, attention %.4f ms per launch" % (proj_ms, attn_ms),
+          file=sys.stderr, flush=True)
+    kernels = {
+        "attention": dict(roofline(wl.flops_attention(), wl.bytes_attention(), attn_ms, wl.dtype),
+                          kernel_ms=round(attn_ms, 5), algorithmic_flops=wl.flops_attention(),
+                          algorithmic_bytes=wl.bytes_attention(),
+                          traffic=traffic_for("attention", args.config)),
+        "projection": dict(roofline(wl.flops_projection(), wl.bytes_projection(), proj_ms,
+                                    wl.dtype),
+                           kernel_ms=round(proj_ms, 5), algorithmic_flops=wl.flops_projection(),
+                           algorithmic_bytes=wl.bytes_projection(),
+                           traffic=traffic_for("projection", args.config)),
+    }
+    dominant = max(kernels, key=lambda k: kernels[k]["kernel_ms"])
+    roof = dict(kernels[dominant], kernel=dominant)
+    other = [k for k in kernels if k != dominant][0]
+    roof["other_kernel"] = dict(kernels[other], kernel=other)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -114,15 +114,18 @@ xattn_status xattn_create(const xattn_config* cfg, xattn_ctx** out);
 void xattn_destroy(xattn_ctx* ctx);
 
 /* Bytes of device workspace xattn_forward needs for a batch of
- * `num_requests` requests, `total_cand` candidates and `heads` heads
- * (a plan header plus one 16-byte work item per query tile).  Returns 0 on
- * invalid arguments. */
+ * `num_requests` requests, `total_cand` candidates and `heads` heads: a plan
+ * header, one 16-byte work item per query tile, and the projected queries
+ * (total_cand * q * d elements of the context's type).  Returns 0 on invalid
+ * arguments. */
 size_t xattn_workspace_size(const xattn_ctx* ctx, int32_t num_requests,
                             int32_t total_cand, int32_t heads);
 
 /* Shared-history cross-attention forward (Eq. (7) attention with Eq. (8)
- * per-slot W_Q; layouts and precision in the header comment).  Enqueues the
- * varlen planner and the fused projection + attention kernel on `stream`.
+ * per-slot W_Q; layouts and precision in the header comment).  Enqueues on
+ * `stream` the TSP projection (whose launch also runs the varlen planner in
+ * one extra work-group) and then the attention kernel, which reads the
+ * projected queries and the plan from the workspace.
  * `workspace` is device memory of at least xattn_workspace_size() bytes,
  * owned by the caller; its contents on entry are ignored.
  * Errors: XATTN_EINVAL for NULL pointers / negative counts / heads not
@@ -138,14 +141,15 @@ xattn_status xattn_forward(xattn_ctx* ctx,
                            void* O, void* workspace, size_t workspace_bytes,
                            void* stream);
 
-/* Attention alone: the fused projection + attention kernel of xattn_forward,
- * reading the plan that a previous xattn_plan or xattn_forward call left in
- * `workspace` for the SAME offsets and shape arguments (a decoder with several
- * cross-attention layers over one batch plans once and attends per layer).
- * Arguments and errors as for xattn_forward.  If the workspace holds the plan
- * of a different batch shape (another candidates-per-tile size), the kernel
- * computes nothing; a plan of a different batch with the same tile size gives
- * undefined output. */
+/* Projection and attention without re-planning: like xattn_forward, but the
+ * plan is read from `workspace`, where a previous xattn_plan or xattn_forward
+ * call left it for the SAME offsets and shape arguments (a decoder with
+ * several cross-attention layers over one batch plans once and runs the
+ * projection and attention per layer).  Arguments and errors as for
+ * xattn_forward.  If the workspace holds the plan of a different batch shape
+ * (another candidates-per-tile size), the attention kernel computes nothing;
+ * a plan of a different batch with the same tile size gives undefined
+ * output. */
 xattn_status xattn_attend(xattn_ctx* ctx,
                           const void* Z, const void* W_Q,
                           const void* K, const void* V,
@@ -154,6 +158,19 @@ xattn_status xattn_attend(xattn_ctx* ctx,
                           int32_t total_kv, int32_t heads,
                           void* O, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/* Attention kernel alone, over queries the caller already projected:
+ * Q [total_cand][q][d] in the context's type holds Z . W_Q[slot] (as
+ * xattn_project writes it); the plan is read from `workspace` as for
+ * xattn_attend.  For callers that fuse the query projection into their own
+ * producer.  Errors as for xattn_forward (NULL Q is XATTN_EINVAL). */
+xattn_status xattn_attend_q(xattn_ctx* ctx, const void* Q,
+                            const void* K, const void* V,
+                            const int32_t* cu_seqlens_kv, const int32_t* cu_cand,
+                            int32_t num_requests, int32_t total_cand,
+                            int32_t total_kv, int32_t heads,
+                            void* O, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /* Varlen plan alone (integer outputs, for callers that want the row map and
  * for tests).  Writes, on the device:
@@ -182,9 +199,8 @@ int64_t xattn_max_tiles(const xattn_ctx* ctx, int32_t num_requests,
 
 /* TSP query projection alone (Eq. (8) applied to W_Q of Eq. (7)):
  * Q[row] = Z[row] . W_Q[row % q], Q [total_cand][q][d] in the context's
- * dtype (bf16: fp32 accumulation, rounded to nearest-even).  xattn_forward
- * computes the same projection inside its attention kernel; this entry point
- * exposes it on its own. */
+ * dtype (bf16: fp32 accumulation, rounded to nearest-even) - the same kernel
+ * xattn_forward runs into its workspace. */
 xattn_status xattn_project(xattn_ctx* ctx, const void* Z, const void* W_Q,
                            int32_t total_cand, void* Q, void* stream);
 

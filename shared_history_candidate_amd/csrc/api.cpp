@@ -92,6 +92,19 @@ int64_t max_tiles_any(const xattn_config& c, int R, int total_cand) {
     return max_tiles_for(c, R, total_cand, 32);
 }
 
+// Workspace layout: plan header and tiles, then (256-byte aligned) the
+// projected queries [total_cand][q][d] in the context's element type.
+size_t q_offset(const xattn_config& c, int R, int total_cand) {
+    const size_t plan = (size_t)xattn::kPlanHeaderBytes + 16 * (size_t)max_tiles_any(c, R, total_cand);
+    return (plan + 255) & ~(size_t)255;
+}
+
+size_t elem_bytes(const xattn_config& c) { return c.dtype == XATTN_BF16 ? 2 : 4; }
+
+size_t workspace_bytes(const xattn_config& c, int R, int total_cand) {
+    return q_offset(c, R, total_cand) + (size_t)total_cand * c.n_slots * c.d_model * elem_bytes(c);
+}
+
 struct DeviceGuard {
     int prev = -1;
     hipError_t err = hipSuccess;
@@ -164,7 +177,7 @@ int64_t xattn_max_tiles(const xattn_ctx* ctx, int32_t R, int32_t total_cand, int
 
 size_t xattn_workspace_size(const xattn_ctx* ctx, int32_t R, int32_t total_cand, int32_t heads) {
     if (!ctx || R < 0 || total_cand < 0 || heads < 1) return 0;
-    return (size_t)xattn::kPlanHeaderBytes + 16 * (size_t)xattn_max_tiles(ctx, R, total_cand, heads);
+    return workspace_bytes(ctx->cfg, R, total_cand);
 }
 
 xattn_status xattn_plan(xattn_ctx* ctx, const int32_t* cu_kv, const int32_t* cu_cand, int32_t R,
@@ -193,11 +206,15 @@ xattn_status xattn_plan(xattn_ctx* ctx, const int32_t* cu_kv, const int32_t* cu_
 
 namespace {
 
-// Shared body of xattn_forward (plan = true) and xattn_attend (plan = false).
-xattn_status run_forward(bool plan, xattn_ctx* ctx, const void* Z, const void* W_Q,
+enum class Mode { kForward, kAttend, kAttendQ };
+
+// Shared body of xattn_forward (plan + projection + attention), xattn_attend
+// (projection + attention over the plan in the workspace) and xattn_attend_q
+// (attention over caller-projected queries and the plan in the workspace).
+xattn_status run_forward(Mode mode, xattn_ctx* ctx, const void* Z, const void* W_Q, const void* Qin,
                          const void* K, const void* V, const int32_t* cu_kv,
                          const int32_t* cu_cand, int32_t R, int32_t total_cand, int32_t total_kv,
-                         int32_t heads, void* O, void* workspace, size_t workspace_bytes,
+                         int32_t heads, void* O, void* workspace, size_t workspace_bytes_,
                          void* stream) {
     g_last_error.clear();
     xattn_status st = check_shape(ctx, R, total_cand, total_kv, heads);
@@ -206,41 +223,58 @@ xattn_status run_forward(bool plan, xattn_ctx* ctx, const void* Z, const void* W
     if (c.kv_mode == XATTN_KV_SHARED && V)
         return fail(XATTN_EINVAL, "V must be NULL in XATTN_KV_SHARED mode (V = K = H)");
     if (!cu_kv || !cu_cand) return fail(XATTN_EINVAL, "NULL offset array");
-    if (total_cand > 0 && (!Z || !W_Q || !O))
-        return fail(XATTN_EINVAL, "NULL Z, W_Q or O");
+    if (total_cand > 0 && !O) return fail(XATTN_EINVAL, "NULL O");
+    if (total_cand > 0 && mode != Mode::kAttendQ && (!Z || !W_Q))
+        return fail(XATTN_EINVAL, "NULL Z or W_Q");
+    if (total_cand > 0 && mode == Mode::kAttendQ && !Qin) return fail(XATTN_EINVAL, "NULL Q");
     if (total_kv > 0 && !K) return fail(XATTN_EINVAL, "NULL K");
     if (total_kv > 0 && c.kv_mode == XATTN_KV_SEPARATE && !V)
         return fail(XATTN_EINVAL, "V is NULL in XATTN_KV_SEPARATE mode");
-    const size_t need = xattn_workspace_size(ctx, R, total_cand, heads);
-    if (!workspace || workspace_bytes < need)
-        return fail(XATTN_EWORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+    const size_t need = workspace_bytes(c, R, total_cand);
+    if (!workspace || workspace_bytes_ < need)
+        return fail(XATTN_EWORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes_);
     if (R == 0 && (total_cand != 0 || total_kv != 0))
         return fail(XATTN_EINVAL, "num_requests=0 with total_cand=%d total_kv=%d", total_cand,
                     total_kv);
     if (R == 0 || total_cand == 0) return XATTN_OK;  // no query rows: nothing to compute
 
-    const Variant var = choose_variant(c, R, total_cand, total_kv, heads);
+    const Variant var = c.dtype == XATTN_BF16 ? choose_variant(c, R, total_cand, total_kv, heads)
+                                              : Variant{2, 1};
     const int tm = tile_m_for(c, R, total_cand, total_kv, heads);
     const int64_t max_tiles = max_tiles_for(c, R, total_cand, tm);
     if (max_tiles * heads > INT32_MAX)
         return fail(XATTN_EUNSUPPORTED, "grid of %lld work-groups is too large",
                     (long long)(max_tiles * heads));
+    void* qws = static_cast<char*>(workspace) + q_offset(c, R, total_cand);
+    const void* Qp = mode == Mode::kAttendQ ? Qin : qws;
     hipStream_t s = static_cast<hipStream_t>(stream);
     DeviceGuard dg(c.device);
     if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
-    hipError_t e;
-    if (plan) {
-        e = xattn::launch_plan(cu_kv, cu_cand, R, c.n_slots, tm, total_cand, total_kv, workspace,
-                               max_tiles, nullptr, nullptr, nullptr, nullptr, s);
-        if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
-    }
+    hipError_t e = hipSuccess;
     if (c.dtype == XATTN_BF16) {
-        e = xattn::launch_attn_bf16(Z, W_Q, K, c.kv_mode == XATTN_KV_SEPARATE ? V : nullptr, cu_kv,
+        if (mode != Mode::kAttendQ) {
+            e = xattn::launch_project_plan_bf16(Z, W_Q, total_cand, c.n_slots, c.d_model, qws, cu_kv,
+                                                cu_cand, R, tm, total_kv,
+                                                mode == Mode::kForward ? workspace : nullptr,
+                                                max_tiles, s);
+            if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
+        }
+        e = xattn::launch_attn_bf16(Qp, K, c.kv_mode == XATTN_KV_SEPARATE ? V : nullptr, cu_kv,
                                     workspace, max_tiles, c.n_slots, c.d_model, heads, var.rb,
                                     var.ksplit, O, s);
     } else {
-        e = xattn::launch_attn_f32(static_cast<const float*>(Z), static_cast<const float*>(W_Q),
-                                   static_cast<const float*>(K),
+        if (mode == Mode::kForward) {
+            e = xattn::launch_plan(cu_kv, cu_cand, R, c.n_slots, tm, total_cand, total_kv, workspace,
+                                   max_tiles, nullptr, nullptr, nullptr, nullptr, s);
+            if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
+        }
+        if (mode != Mode::kAttendQ) {
+            e = xattn::launch_project_f32(static_cast<const float*>(Z),
+                                          static_cast<const float*>(W_Q), total_cand, c.n_slots,
+                                          c.d_model, static_cast<float*>(qws), s);
+            if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
+        }
+        e = xattn::launch_attn_f32(static_cast<const float*>(Qp), static_cast<const float*>(K),
                                    c.kv_mode == XATTN_KV_SEPARATE ? static_cast<const float*>(V)
                                                                   : nullptr,
                                    cu_kv, workspace, max_tiles, c.n_slots, c.d_model, heads,
@@ -255,17 +289,25 @@ xattn_status run_forward(bool plan, xattn_ctx* ctx, const void* Z, const void* W
 xattn_status xattn_forward(xattn_ctx* ctx, const void* Z, const void* W_Q, const void* K,
                            const void* V, const int32_t* cu_kv, const int32_t* cu_cand,
                            int32_t R, int32_t total_cand, int32_t total_kv, int32_t heads,
-                           void* O, void* workspace, size_t workspace_bytes, void* stream) {
-    return run_forward(true, ctx, Z, W_Q, K, V, cu_kv, cu_cand, R, total_cand, total_kv, heads, O,
-                       workspace, workspace_bytes, stream);
+                           void* O, void* workspace, size_t workspace_bytes_, void* stream) {
+    return run_forward(Mode::kForward, ctx, Z, W_Q, nullptr, K, V, cu_kv, cu_cand, R, total_cand,
+                       total_kv, heads, O, workspace, workspace_bytes_, stream);
 }
 
 xattn_status xattn_attend(xattn_ctx* ctx, const void* Z, const void* W_Q, const void* K,
                           const void* V, const int32_t* cu_kv, const int32_t* cu_cand,
                           int32_t R, int32_t total_cand, int32_t total_kv, int32_t heads,
-                          void* O, void* workspace, size_t workspace_bytes, void* stream) {
-    return run_forward(false, ctx, Z, W_Q, K, V, cu_kv, cu_cand, R, total_cand, total_kv, heads, O,
-                       workspace, workspace_bytes, stream);
+                          void* O, void* workspace, size_t workspace_bytes_, void* stream) {
+    return run_forward(Mode::kAttend, ctx, Z, W_Q, nullptr, K, V, cu_kv, cu_cand, R, total_cand,
+                       total_kv, heads, O, workspace, workspace_bytes_, stream);
+}
+
+xattn_status xattn_attend_q(xattn_ctx* ctx, const void* Q, const void* K, const void* V,
+                            const int32_t* cu_kv, const int32_t* cu_cand, int32_t R,
+                            int32_t total_cand, int32_t total_kv, int32_t heads, void* O,
+                            void* workspace, size_t workspace_bytes_, void* stream) {
+    return run_forward(Mode::kAttendQ, ctx, nullptr, nullptr, Q, K, V, cu_kv, cu_cand, R,
+                       total_cand, total_kv, heads, O, workspace, workspace_bytes_, stream);
 }
 
 xattn_status xattn_project(xattn_ctx* ctx, const void* Z, const void* W_Q, int32_t total_cand,
@@ -280,7 +322,9 @@ xattn_status xattn_project(xattn_ctx* ctx, const void* Z, const void* W_Q, int32
     if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = c.dtype == XATTN_BF16
-                       ? xattn::launch_project_bf16(Z, W_Q, total_cand, c.n_slots, c.d_model, Q, s)
+                       ? xattn::launch_project_plan_bf16(Z, W_Q, total_cand, c.n_slots, c.d_model,
+                                                         Q, nullptr, nullptr, 0, 0, 0, nullptr, 0,
+                                                         s)
                        : xattn::launch_project_f32(static_cast<const float*>(Z),
                                                    static_cast<const float*>(W_Q), total_cand,
                                                    c.n_slots, c.d_model, static_cast<float*>(Q), s);

@@ -1,15 +1,14 @@
-// Fused TSP query projection + shared-memory cross-attention, bf16 in, fp32
+// Shared-memory cross-attention over projected queries, bf16 in, fp32
 // accumulate, bf16 out, for gfx950 matrix cores.
 //
-// Computes, for every work item {r, s, c0, nc} of the plan and every head h,
-//   Q_h   = Z[c, s, :] . W_Q[s][h*d_h:(h+1)*d_h, :]^T   (ReST reading note,
-//           s.3.3.2 Eq. (8): slot s has its own W_Q[s])
-//   O_h   = softmax(Q_h K_h^T / sqrt(d_h)) V_h          (s.3.3.1 Eq. (7);
-//           K = V = H in projection-free mode, separate K, V for the TransX
-//           behaviour memory, TransX report s.2)
-// for the nc candidates c in [c0, c0+nc) of request r.  All candidates of a
-// request stream the same memory rows (shared-prefix serving, ReST reading
-// note s.3.5).
+// For every work item {r, s, c0, nc} of the plan and every head h:
+//   O_h = softmax(Q_h K_h^T / sqrt(d_h)) V_h            (ReST reading note,
+//         s.3.3.1 Eq. (7); K = V = H in projection-free mode, separate K, V
+//         for the TransX behaviour memory, TransX report s.2)
+// for the nc candidates c in [c0, c0+nc) of request r, query slot s, where
+// Q = Z W_Q[s] comes from the projection kernel (gemm_bf16.hip).  All
+// candidates of a request stream the same memory rows (shared-prefix
+// serving, ReST reading note s.3.5).
 //
 // Work decomposition.  A work-group handles one work item and one head with
 // RB x KSPLIT waves: wave w owns query block rb = w % RB (32 query columns)
@@ -21,15 +20,12 @@
 // the softmax reductions along the key axis stay inside the lane (plus one
 // exchange between the two 32-lane halves, needed only when the running
 // maximum moves):
-//   projection  Q_h^T (d_h x 32) = W_h (d_h x d) . Z^T (d x 32)
 //   scores      S^T   (64 x 32)  = K_tile (64 x d_h) . Q_h^T
 //   output      O^T   (d_h x 32) += V_tile^T (d_h x 64) . P^T (64 x 32)
-// The accumulator layout of each product is the operand layout of the next,
-// so Q and P never move between lanes.  W_h and the query tokens are staged
-// into LDS with direct global->LDS loads (XOR-swizzled 16-byte chunks); the
-// memory is streamed in tiles of 64 rows through double-buffered LDS (one
-// buffer is both K and V in projection-free mode) and V^T operands come from
-// LDS transpose reads.
+// The score accumulator layout is the operand layout of P^T, so the weights
+// never move between lanes.  The memory is streamed in tiles of 64 rows
+// through double-buffered LDS (one buffer is both K and V in projection-free
+// mode) and V^T operands come from LDS transpose reads.
 //
 // Softmax: exp2 of log2(e)/sqrt(d_h)-scaled scores.  The running maximum is
 // only moved when a tile exceeds it by more than 2^8 (then the accumulators
@@ -73,56 +69,18 @@ struct Cfg {
     static constexpr int PLANES = SEP ? 2 : 1;
     static constexpr int TILE = BN * LDK;     // elements per plane per buffer
     static constexpr int KV_BYTES = KSPLIT * 2 * PLANES * TILE * 2;
-    // projection stage width (input features): a power of two <= 256 that
-    // keeps the W_h and query-token stages within 72 KB of LDS
-    static constexpr int SC = pow2floor((36864 / (DH + 32 * RB)) < 256 ? 36864 / (DH + 32 * RB) : 256);
-    static constexpr int W_BYTES = DH * SC * 2;
-    static constexpr int ZT_BYTES = 32 * RB * SC * 2;
-    static constexpr int QS_BYTES = KSPLIT > 1 ? RB * EB * 2 * 64 * 16 : 0;  // shared Q^T
-    static constexpr int P1_BYTES = W_BYTES + ZT_BYTES + QS_BYTES;
     static constexpr int CMB_BYTES = KSPLIT > 1 ? RB * (KSPLIT - 1) * 64 * (EB * 16 + 2) * 4 : 0;
-    static constexpr int SMEM = P1_BYTES > KV_BYTES ? (P1_BYTES > CMB_BYTES ? P1_BYTES : CMB_BYTES)
-                                                    : (KV_BYTES > CMB_BYTES ? KV_BYTES : CMB_BYTES);
+    static constexpr int SMEM = KV_BYTES > CMB_BYTES ? KV_BYTES : CMB_BYTES;
     static constexpr int KV_CHUNKS = BN * DH / 8;                 // 16-byte chunks per plane
     static constexpr int KV_CPT = KV_CHUNKS / (64 * RB);
     static_assert(KV_CHUNKS % (64 * RB) == 0, "memory tile must split evenly over a split group");
-    static constexpr int MYEB = (EB + KSPLIT - 1) / KSPLIT;       // e-blocks projected per wave
 };
-
-__device__ __forceinline__ void lds_dma16(const void* gptr, void* lds_base) {
-    __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_base, 16,
-                                     0, 0);
-}
-
-// Stage rows [0, nrows) x columns [k0, k0+w) of a bf16 matrix (row i at
-// src_row(i)) into LDS as rows of w elements whose 16-byte chunks are
-// XOR-swizzled by (row mod chunks-per-row).  Each wave instruction fills 1 KB
-// of LDS (64 lanes x 16 bytes, lane order); instructions are dealt
-// round-robin to the work-group's waves.  w is a multiple of 32.
-template <int NT, typename RowPtr>
-__device__ __forceinline__ void stage_rows(char* lds, int nrows, int w, RowPtr src_row, int k0) {
-    const int cpr = w / 8;                    // chunks per row
-    const int total = nrows * cpr;            // chunks (a multiple of 64)
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    for (int base = wave * 64; base < total; base += NT) {
-        const int c = base + lane;            // LDS chunk written by this lane
-        const int row = c / cpr, pc = c - row * cpr;
-        const int lc = pc ^ (row & (cpr - 1));    // logical chunk stored there
-        const bf16* src = src_row(row) + k0 + lc * 8;
-        lds_dma16(src, lds + base * 16);
-    }
-}
-
-__device__ __forceinline__ bf16x8 lds_chunk(const char* lds, int row, int chunk, int cpr) {
-    const int pc = chunk ^ (row & (cpr - 1));
-    return *reinterpret_cast<const bf16x8*>(lds + (row * cpr + pc) * 16);
-}
 
 template <int DH, int RB, int KSPLIT, bool SEP>
 __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(
-    const bf16* __restrict__ Z, const bf16* __restrict__ Wq, const bf16* __restrict__ K,
-    const bf16* __restrict__ V, const int* __restrict__ cu_kv, const int* __restrict__ ws,
-    int q, int d, int heads, float scale_log2, bf16* __restrict__ O) {
+    const bf16* __restrict__ Qp, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const int* __restrict__ cu_kv, const int* __restrict__ ws, int q, int d, int heads,
+    float scale_log2, bf16* __restrict__ O) {
     using C = Cfg<DH, RB, KSPLIT, SEP>;
     __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
 
@@ -149,73 +107,16 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(
     const int cand = c0 + qcol;
     const int gt = tid - ksg * 64 * RB;       // thread index inside the split group
 
-    // ---------------- 1. projection: Q_h^T of this wave's 32 queries ----------------
+    // ---------------- 1. this wave's Q_h^T operands ----------------
+    // k-step k, half g: features 16k + 8g .. 16k + 8g + 7 of the lane's query
+    // row (columns past the tile re-read its last row; their output is dropped)
     bf16x8 qb[C::KST];
     {
-        char* w_lds = smem;
-        char* z_lds = smem + C::W_BYTES;
-        const bf16* wsrc = Wq + ((size_t)s * d + h * DH) * d;
-        const int zlast = c0 + nc - 1;        // rows past the tile re-read the last valid one
-        f32x16 pacc[C::MYEB];
+        const bf16* qrow = Qp + ((size_t)(qvalid ? cand : c0 + nc - 1) * q + s) * d + h * DH;
 #pragma unroll
-        for (int i = 0; i < C::MYEB; ++i) pacc[i] = f32x16{};
-        for (int k0 = 0; k0 < d;) {
-            // a power-of-two stage width keeps the chunk swizzle a permutation
-            // (d is a multiple of 32, so every stage is at least 32 wide)
-            int wdt = C::SC;
-            while (wdt > d - k0) wdt >>= 1;
-            const int cpr = wdt / 8;
-            if (k0 > 0) __syncthreads();   // previous stage fully consumed
-            stage_rows<C::NT>(w_lds, DH, wdt, [&](int e) { return wsrc + (size_t)e * d; }, k0);
-            stage_rows<C::NT>(z_lds, 32 * RB, wdt,
-                              [&](int i) { return Z + ((size_t)min(c0 + i, zlast) * q + s) * d; },
-                              k0);
-            __builtin_amdgcn_s_waitcnt(0);   // this thread's LDS-DMA loads have landed
-            __syncthreads();                 // ... and every other thread's
-#pragma unroll
-            for (int i = 0; i < C::MYEB; ++i) {
-                const int eb = ksg + i * KSPLIT;
-                if (eb < C::EB) {
-                    for (int kk = 0; kk < wdt / 16; ++kk) {
-                        const bf16x8 a = lds_chunk(w_lds, eb * 32 + l32, 2 * kk + g, cpr);
-                        const bf16x8 b = lds_chunk(z_lds, rb * 32 + l32, 2 * kk + g, cpr);
-                        pacc[i] = mfma32(a, b, pacc[i]);
-                    }
-                }
-            }
-            k0 += wdt;
-        }
-        // accumulator reg 8u+t of e-block eb holds feature eb*32 + 16u + (t/4)*8 + 4g + t%4,
-        // which is k-slot t of score k-step 2*eb+u.
-        if constexpr (KSPLIT == 1) {
-#pragma unroll
-            for (int eb = 0; eb < C::EB; ++eb)
-#pragma unroll
-                for (int u = 0; u < 2; ++u)
-#pragma unroll
-                    for (int t = 0; t < 8; ++t) qb[2 * eb + u][t] = (bf16)pacc[eb][8 * u + t];
-        } else {
-            // the KSPLIT waves of a query block each projected some e-blocks: share them
-            bf16x8* qs = reinterpret_cast<bf16x8*>(smem + C::W_BYTES + C::ZT_BYTES);
-#pragma unroll
-            for (int i = 0; i < C::MYEB; ++i) {
-                const int eb = ksg + i * KSPLIT;
-                if (eb < C::EB) {
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        bf16x8 v;
-#pragma unroll
-                        for (int t = 0; t < 8; ++t) v[t] = (bf16)pacc[i][8 * u + t];
-                        qs[((rb * C::EB + eb) * 2 + u) * 64 + lane] = v;
-                    }
-                }
-            }
-            __syncthreads();
-#pragma unroll
-            for (int k = 0; k < C::KST; ++k) qb[k] = qs[(rb * C::EB * 2 + k) * 64 + lane];
-        }
+        for (int k = 0; k < C::KST; ++k)
+            qb[k] = *reinterpret_cast<const bf16x8*>(qrow + 16 * k + 8 * g);
     }
-    __syncthreads();   // projection LDS is reused for the memory tiles below
 
     // ---------------- 2. stream this split's memory tiles ----------------
     f32x16 oacc[C::EB];
@@ -308,12 +209,12 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(
             bf16x8 kf[2][C::KST];
 #pragma unroll
             for (int k = 0; k < C::KST; ++k) {
-                const int e0 = 32 * (k >> 1) + 16 * (k & 1) + 4 * g;
+                const int e0 = 16 * k + 8 * g;
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     const bf16* row = kb + (hh * 32 + l32) * C::LDK + e0;
                     kf[hh][k] = cat(*reinterpret_cast<const bf16x4*>(row),
-                                    *reinterpret_cast<const bf16x4*>(row + 8));
+                                    *reinterpret_cast<const bf16x4*>(row + 4));
                 }
             }
             f32x16 sacc[2] = {f32x16{}, f32x16{}};
@@ -432,39 +333,6 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(
     }
 }
 
-// Standalone projection: Q[c][s][e] for a 32(e) x 32(cand) block per wave,
-// operands read straight from global memory.
-template <int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void project_bf16_kernel(
-    const bf16* __restrict__ Z, const bf16* __restrict__ Wq, int total_cand, int q, int d,
-    bf16* __restrict__ Q) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int g = lane >> 5, l32 = lane & 31;
-    const int cand = (blockIdx.x * WAVES + wave) * 32 + l32;
-    const int e0 = blockIdx.y * 32;
-    const int s = blockIdx.z;
-    const bool valid = cand < total_cand;
-    const bf16* zrow = valid ? Z + ((size_t)cand * q + s) * d : nullptr;
-    const bf16* wrow = Wq + ((size_t)s * d + e0 + l32) * d;
-    const bf16x8 zero = {};
-    f32x16 acc = {};
-    for (int k0 = 0; k0 < d; k0 += 16) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(wrow + k0 + 8 * g);
-        const bf16x8 b = zrow ? *reinterpret_cast<const bf16x8*>(zrow + k0 + 8 * g) : zero;
-        acc = mfma32(a, b, acc);
-    }
-    if (valid) {
-        bf16* qrow = Q + ((size_t)cand * q + s) * d + e0;
-#pragma unroll
-        for (int b4 = 0; b4 < 4; ++b4) {
-            bf16x4 v;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) v[t] = (bf16)acc[4 * b4 + t];
-            *reinterpret_cast<bf16x4*>(qrow + b4 * 8 + 4 * g) = v;
-        }
-    }
-}
-
 // Variants whose LDS footprint exceeds what one work-group may hold are not
 // built; the host prefers variants that leave room for two work-groups per
 // compute unit (attn_bf16_variant_smem).
@@ -476,7 +344,7 @@ constexpr bool fits() {
 }
 
 template <int DH, int RB, int KSPLIT, bool SEP>
-hipError_t launch_one(const void* Z, const void* Wq, const void* K, const void* V,
+hipError_t launch_one(const void* Qp, const void* K, const void* V,
                       const int* cu_kv, const void* ws, int64_t max_tiles, int q, int d,
                       int heads, void* O, hipStream_t stream) {
     if constexpr (!fits<DH, RB, KSPLIT, SEP>()) {
@@ -486,8 +354,8 @@ hipError_t launch_one(const void* Z, const void* Wq, const void* K, const void* 
     const int64_t blocks = max_tiles * heads;
     if (blocks <= 0) return hipSuccess;
     hipLaunchKernelGGL((attn_bf16_kernel<DH, RB, KSPLIT, SEP>), dim3((unsigned)blocks),
-                       dim3(64 * RB * KSPLIT), 0, stream, static_cast<const bf16*>(Z),
-                       static_cast<const bf16*>(Wq), static_cast<const bf16*>(K),
+                       dim3(64 * RB * KSPLIT), 0, stream, static_cast<const bf16*>(Qp),
+                       static_cast<const bf16*>(K),
                        static_cast<const bf16*>(V), cu_kv, static_cast<const int*>(ws), q, d,
                        heads, scale_log2, static_cast<bf16*>(O));
     return hipGetLastError();
@@ -495,23 +363,23 @@ hipError_t launch_one(const void* Z, const void* Wq, const void* K, const void* 
 }
 
 template <int DH, int RB, int KSPLIT>
-hipError_t launch_sep(const void* Z, const void* Wq, const void* K, const void* V,
+hipError_t launch_sep(const void* Qp, const void* K, const void* V,
                       const int* cu_kv, const void* ws, int64_t max_tiles, int q, int d,
                       int heads, void* O, hipStream_t stream) {
     if (V)
-        return launch_one<DH, RB, KSPLIT, true>(Z, Wq, K, V, cu_kv, ws, max_tiles, q, d, heads, O,
+        return launch_one<DH, RB, KSPLIT, true>(Qp, K, V, cu_kv, ws, max_tiles, q, d, heads, O,
                                                 stream);
-    return launch_one<DH, RB, KSPLIT, false>(Z, Wq, K, V, cu_kv, ws, max_tiles, q, d, heads, O,
+    return launch_one<DH, RB, KSPLIT, false>(Qp, K, V, cu_kv, ws, max_tiles, q, d, heads, O,
                                              stream);
 }
 
 template <int DH>
-hipError_t launch_dh(const void* Z, const void* Wq, const void* K, const void* V,
+hipError_t launch_dh(const void* Qp, const void* K, const void* V,
                      const int* cu_kv, const void* ws, int64_t max_tiles, int q, int d,
                      int heads, int rb, int ksplit, void* O, hipStream_t stream) {
 #define XATTN_CASE(R_, S_)                                                                     \
     if (rb == R_ && ksplit == S_)                                                              \
-        return launch_sep<DH, R_, S_>(Z, Wq, K, V, cu_kv, ws, max_tiles, q, d, heads, O, stream);
+        return launch_sep<DH, R_, S_>(Qp, K, V, cu_kv, ws, max_tiles, q, d, heads, O, stream);
     XATTN_CASE(1, 4)
     XATTN_CASE(2, 2)
     XATTN_CASE(4, 1)
@@ -549,33 +417,22 @@ int attn_bf16_variant_smem(int dh, int rb, int ksplit, bool sep) {
     }
 }
 
-hipError_t launch_attn_bf16(const void* Z, const void* Wq, const void* K, const void* V,
+hipError_t launch_attn_bf16(const void* Qp, const void* K, const void* V,
                             const int* cu_kv, const void* ws, int64_t max_tiles, int q, int d,
                             int heads, int rb, int ksplit, void* O, hipStream_t stream) {
     switch (d / heads) {
         case 32:
-            return launch_dh<32>(Z, Wq, K, V, cu_kv, ws, max_tiles, q, d, heads, rb, ksplit, O,
+            return launch_dh<32>(Qp, K, V, cu_kv, ws, max_tiles, q, d, heads, rb, ksplit, O,
                                  stream);
         case 64:
-            return launch_dh<64>(Z, Wq, K, V, cu_kv, ws, max_tiles, q, d, heads, rb, ksplit, O,
+            return launch_dh<64>(Qp, K, V, cu_kv, ws, max_tiles, q, d, heads, rb, ksplit, O,
                                  stream);
         case 128:
-            return launch_dh<128>(Z, Wq, K, V, cu_kv, ws, max_tiles, q, d, heads, rb, ksplit, O,
+            return launch_dh<128>(Qp, K, V, cu_kv, ws, max_tiles, q, d, heads, rb, ksplit, O,
                                   stream);
         default:
             return hipErrorInvalidValue;
     }
-}
-
-hipError_t launch_project_bf16(const void* Z, const void* Wq, int total_cand, int q, int d,
-                               void* Q, hipStream_t stream) {
-    constexpr int W = 2;
-    if (total_cand <= 0) return hipSuccess;
-    dim3 grid((total_cand + 32 * W - 1) / (32 * W), d / 32, q);
-    hipLaunchKernelGGL((project_bf16_kernel<W>), grid, dim3(64 * W), 0, stream,
-                       static_cast<const bf16*>(Z), static_cast<const bf16*>(Wq), total_cand, q,
-                       d, static_cast<bf16*>(Q));
-    return hipGetLastError();
 }
 
 }  // namespace xattn

@@ -1,12 +1,12 @@
-// fp32 path of the fused projection + shared-memory cross-attention (the
-// full-precision mode: nothing is rounded below fp32).
+// fp32 path (the full-precision mode: nothing is rounded below fp32): the
+// TSP projection and the shared-memory cross-attention over its output.
 //
-// Same definition as the bf16 kernel (ReST reading note, s.3.3.1 Eq. (7) with
+// Same definition as the bf16 path (ReST reading note, s.3.3.1 Eq. (7) with
 // the per-slot W_Q of s.3.3.2 Eq. (8); separate K/V as in the TransX report
-// s.2).  One work-group of 64 threads handles one plan work item and one head;
-// thread i owns query column c0 + i.  Memory rows stream through LDS in tiles
-// of 32; each thread keeps its projected query and its output accumulator in
-// registers and applies the online-softmax update once per tile.
+// s.2).  Projection: one thread per output element.  Attention: one
+// work-group of 64 threads per plan work item and head, thread i owning query
+// column c0 + i; memory rows stream through LDS in tiles of 32 and each
+// thread applies the online-softmax update once per tile.
 #include "common.h"
 #include "internal.h"
 
@@ -16,16 +16,14 @@ namespace {
 
 constexpr int kRows = 64;  // candidates per work item (tile_m of the fp32 path)
 constexpr int kBN = 32;    // memory rows per tile
-constexpr int kKC = 32;    // projection chunk (input features)
 
 template <int DHMAX>
 __global__ __launch_bounds__(kRows) void attn_f32_kernel(
-    const float* __restrict__ Z, const float* __restrict__ Wq, const float* __restrict__ K,
-    const float* __restrict__ V, const int* __restrict__ cu_kv, const int* __restrict__ ws,
-    int q, int d, int heads, float scale_log2, float* __restrict__ O) {
+    const float* __restrict__ Qp, const float* __restrict__ K, const float* __restrict__ V,
+    const int* __restrict__ cu_kv, const int* __restrict__ ws, int q, int d, int heads,
+    float scale_log2, float* __restrict__ O) {
     __shared__ float ks[kBN][DHMAX];
     __shared__ float vs[kBN][DHMAX];
-    __shared__ float wsm[DHMAX][kKC + 1];
     const int dh = d / heads;
     const int n_tiles = ws[kPlanNTiles];
     const int tile = blockIdx.x / heads;
@@ -40,29 +38,12 @@ __global__ __launch_bounds__(kRows) void attn_f32_kernel(
     const bool valid = i < nc;
     const int cand = c0 + i;
 
-    // projection: qv[e] = sum_k Z[cand][s][k] * W[s][h*dh + e][k], with W_h
-    // staged through LDS in chunks of kKC input features
+    // this thread's projected query (head slice)
     float qv[DHMAX];
-#pragma unroll
-    for (int e = 0; e < DHMAX; ++e) qv[e] = 0.f;
     {
-        const float* zrow = Z + ((size_t)(valid ? cand : c0) * q + s) * d;
-        const float* w = Wq + ((size_t)s * d + h * dh) * d;
-        for (int k0 = 0; k0 < d; k0 += kKC) {
-            float zc[kKC];
+        const float* qrow = Qp + ((size_t)(valid ? cand : c0) * q + s) * d + h * dh;
 #pragma unroll
-            for (int kk = 0; kk < kKC; ++kk) zc[kk] = (k0 + kk < d) ? zrow[k0 + kk] : 0.f;
-            for (int idx = i; idx < DHMAX * kKC; idx += kRows) {
-                const int e = idx / kKC, kk = idx % kKC;
-                wsm[e][kk] = (e < dh && k0 + kk < d) ? w[(size_t)e * d + k0 + kk] : 0.f;
-            }
-            __syncthreads();
-#pragma unroll
-            for (int kk = 0; kk < kKC; ++kk)
-#pragma unroll
-                for (int e = 0; e < DHMAX; ++e) qv[e] = fmaf(zc[kk], wsm[e][kk], qv[e]);
-            __syncthreads();
-        }
+        for (int e = 0; e < DHMAX; ++e) qv[e] = e < dh ? qrow[e] : 0.f;
     }
 
     float acc[DHMAX];
@@ -132,7 +113,7 @@ __global__ void project_f32_kernel(const float* __restrict__ Z, const float* __r
 }
 
 template <int DHMAX>
-hipError_t launch_f32(const float* Z, const float* Wq, const float* K, const float* V,
+hipError_t launch_f32(const float* Qp, const float* K, const float* V,
                       const int* cu_kv, const void* ws, int64_t max_tiles, int q, int d,
                       int heads, float* O, hipStream_t stream) {
     const int dh = d / heads;
@@ -140,22 +121,22 @@ hipError_t launch_f32(const float* Z, const float* Wq, const float* K, const flo
     const int64_t blocks = max_tiles * heads;
     if (blocks <= 0) return hipSuccess;
     hipLaunchKernelGGL((attn_f32_kernel<DHMAX>), dim3((unsigned)blocks), dim3(kRows), 0, stream,
-                       Z, Wq, K, V, cu_kv, static_cast<const int*>(ws), q, d, heads,
+                       Qp, K, V, cu_kv, static_cast<const int*>(ws), q, d, heads,
                        scale_log2, O);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attn_f32(const float* Z, const float* Wq, const float* K, const float* V,
+hipError_t launch_attn_f32(const float* Qp, const float* K, const float* V,
                            const int* cu_kv, const void* ws, int64_t max_tiles, int q, int d,
                            int heads, float* O, hipStream_t stream) {
     const int dh = d / heads;
-    if (dh <= 8) return launch_f32<8>(Z, Wq, K, V, cu_kv, ws, max_tiles, q, d, heads, O, stream);
-    if (dh <= 16) return launch_f32<16>(Z, Wq, K, V, cu_kv, ws, max_tiles, q, d, heads, O, stream);
-    if (dh <= 32) return launch_f32<32>(Z, Wq, K, V, cu_kv, ws, max_tiles, q, d, heads, O, stream);
-    if (dh <= 64) return launch_f32<64>(Z, Wq, K, V, cu_kv, ws, max_tiles, q, d, heads, O, stream);
-    if (dh <= 128) return launch_f32<128>(Z, Wq, K, V, cu_kv, ws, max_tiles, q, d, heads, O, stream);
+    if (dh <= 8) return launch_f32<8>(Qp, K, V, cu_kv, ws, max_tiles, q, d, heads, O, stream);
+    if (dh <= 16) return launch_f32<16>(Qp, K, V, cu_kv, ws, max_tiles, q, d, heads, O, stream);
+    if (dh <= 32) return launch_f32<32>(Qp, K, V, cu_kv, ws, max_tiles, q, d, heads, O, stream);
+    if (dh <= 64) return launch_f32<64>(Qp, K, V, cu_kv, ws, max_tiles, q, d, heads, O, stream);
+    if (dh <= 128) return launch_f32<128>(Qp, K, V, cu_kv, ws, max_tiles, q, d, heads, O, stream);
     return hipErrorInvalidValue;
 }
 

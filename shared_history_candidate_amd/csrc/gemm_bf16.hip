@@ -1,0 +1,219 @@
+// TSP query projection on the gfx950 matrix cores, bf16 in, fp32 accumulate,
+// bf16 out (ReST reading note, s.3.3.2 Eq. (8) applied to W_Q of s.3.3.1
+// Eq. (7): query slot s of every candidate has its own W_Q[s]):
+//
+//     Q[c][s][o] = sum_i Z[c][s][i] * W_Q[s][o][i]
+//
+// Each slot is an independent GEMM over all candidates.  A work-group of four
+// waves computes a TE (output features) x TC (candidates) tile of Q^T =
+// W_Q[s] . Z_s^T, the waves arranged 2 x 2, each holding (TE/64) x (TC/64)
+// 32x32 accumulators.  Input features stream through LDS in stages (256 wide
+// for small tiles, so that d <= 256 is one memory round trip; 64 wide and
+// double-buffered for wide tiles), the next stage's loads in flight during
+// the current stage's products.  Operands arrive through bounds-checked
+// buffer loads, so rows past the last candidate (or output feature) read as
+// zeros and are never stored.
+//
+// The same launch can carry the varlen planner in one extra work-group
+// (blockIdx.x == 0): the plan and the projection are independent, and the
+// attention kernel that follows on the stream needs both.
+#include "internal.h"
+#include "plan_device.h"
+
+namespace xattn {
+
+namespace {
+
+// Tile shapes: TE output features x TC candidates, KC input features per LDS
+// stage.  Small tiles stage up to 256 input features at once, so a d = 256
+// projection costs a single memory round trip per work-group; wide tiles
+// (large batches, where many work-groups hide the latency) stage 64.
+template <int TE, int TC, int KC>
+struct GCfg {
+    static constexpr int LDP = KC + 8;   // LDS row pitch (elements, 16-byte aligned rows)
+    static constexpr int NBUF = KC >= 256 ? 1 : 2;   // LDS stages (register prefetch either way)
+    static constexpr int BE = TE / 64;   // 32-row accumulator blocks per wave along o
+    static constexpr int BC = TC / 64;   // ... along candidates
+    static constexpr int A_ELEMS = TE * LDP;
+    static constexpr int B_ELEMS = TC * LDP;
+    static constexpr int STAGE = A_ELEMS + B_ELEMS;
+    static constexpr int BYTES = NBUF * STAGE * 2;
+    static constexpr int A_CPT = TE * (KC / 8) / 256;   // 16-byte chunks per thread per stage
+    static constexpr int B_CPT = TC * (KC / 8) / 256;
+    static constexpr int SMEM = BYTES > (int)sizeof(PlanSmem) ? BYTES : (int)sizeof(PlanSmem);
+};
+
+struct PlanArgs {
+    const int* cu_kv;
+    const int* cu_cand;
+    int* ws;
+    int64_t max_tiles;
+    int R, tile_m, total_kv;
+    int enabled;
+};
+
+__device__ __forceinline__ uint32_t clamp_bytes(size_t b) {
+    return b > 0xFFFFFFF0u ? 0xFFFFFFF0u : (uint32_t)b;
+}
+
+template <int TE, int TC, int KC>
+__global__ __launch_bounds__(256) void prep_kernel(const bf16* __restrict__ Z,
+                                                   const bf16* __restrict__ Wq, int total_cand,
+                                                   int q, int d, bf16* __restrict__ Q,
+                                                   int tiles_e, int tiles_c, PlanArgs pa) {
+    using C = GCfg<TE, TC, KC>;
+    constexpr int LDP = C::LDP;
+    __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
+    int bid = blockIdx.x;
+    if (pa.enabled) {
+        if (bid == 0) {
+            run_plan<256>(pa.cu_kv, pa.cu_cand, pa.R, q, pa.tile_m, total_cand, pa.total_kv, pa.ws,
+                          pa.max_tiles, nullptr, nullptr, nullptr, nullptr,
+                          *reinterpret_cast<PlanSmem*>(smem));
+            return;
+        }
+        --bid;
+    }
+    // output-feature tiles fastest: consecutive work-groups share the same
+    // query tokens (L2) while W_Q[s] stays cache-resident
+    const int per_slot = tiles_e * tiles_c;
+    const int s = bid / per_slot;
+    const int rem = bid - s * per_slot;
+    const int tc = rem / tiles_e, te = rem - tc * tiles_e;
+    const int e0 = te * TE, c0 = tc * TC;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wr = w >> 1, wc = w & 1;
+    const int g = lane >> 5, l32 = lane & 31;
+
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(Wq + ((size_t)s * d + e0) * d), (short)0,
+        clamp_bytes((size_t)(d - e0) * d * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(Z + ((size_t)c0 * q + s) * d), (short)0,
+        clamp_bytes(((size_t)(total_cand - c0) * q - s) * d * 2), 0x00020000);
+
+    bf16* lds = reinterpret_cast<bf16*>(smem);
+    uint4 areg[C::A_CPT], breg[C::B_CPT];
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int u = 0; u < C::A_CPT; ++u) {
+            const int i = tid + u * 256, row = i / (KC / 8), col = i % (KC / 8);
+            areg[u] = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, (row * d + k0 + col * 8) * 2, 0, 0));
+        }
+#pragma unroll
+        for (int u = 0; u < C::B_CPT; ++u) {
+            const int i = tid + u * 256, row = i / (KC / 8), col = i % (KC / 8);
+            breg[u] = __builtin_bit_cast(
+                uint4,
+                __builtin_amdgcn_raw_buffer_load_b128(rz, (row * q * d + k0 + col * 8) * 2, 0, 0));
+        }
+    };
+    auto lstore = [&](int buf) {
+        bf16* a = lds + buf * C::STAGE;
+        bf16* b = a + C::A_ELEMS;
+#pragma unroll
+        for (int u = 0; u < C::A_CPT; ++u) {
+            const int i = tid + u * 256, row = i / (KC / 8), col = i % (KC / 8);
+            *reinterpret_cast<uint4*>(a + row * LDP + col * 8) = areg[u];
+        }
+#pragma unroll
+        for (int u = 0; u < C::B_CPT; ++u) {
+            const int i = tid + u * 256, row = i / (KC / 8), col = i % (KC / 8);
+            *reinterpret_cast<uint4*>(b + row * LDP + col * 8) = breg[u];
+        }
+    };
+
+    f32x16 acc[C::BE][C::BC];
+#pragma unroll
+    for (int i = 0; i < C::BE; ++i)
+#pragma unroll
+        for (int j = 0; j < C::BC; ++j) acc[i][j] = f32x16{};
+
+    // d is a multiple of 32: the last stage may be partly empty (its columns
+    // past d are loaded but never multiplied)
+    const int nk = (d + KC - 1) / KC;
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int kc = 0; kc < nk; ++kc) {
+        const int buf = C::NBUF == 2 ? (kc & 1) : 0;
+        if (kc + 1 < nk) gload((kc + 1) * KC);
+        const bf16* a = lds + buf * C::STAGE;
+        const bf16* b = a + C::A_ELEMS;
+        const int ksteps = min(KC, d - kc * KC) / 16;
+        for (int kk = 0; kk < ksteps; ++kk) {
+            bf16x8 af[C::BE], bfr[C::BC];
+#pragma unroll
+            for (int i = 0; i < C::BE; ++i)
+                af[i] = *reinterpret_cast<const bf16x8*>(
+                    a + (wr * (TE / 2) + i * 32 + l32) * LDP + kk * 16 + 8 * g);
+#pragma unroll
+            for (int j = 0; j < C::BC; ++j)
+                bfr[j] = *reinterpret_cast<const bf16x8*>(
+                    b + (wc * (TC / 2) + j * 32 + l32) * LDP + kk * 16 + 8 * g);
+#pragma unroll
+            for (int i = 0; i < C::BE; ++i)
+#pragma unroll
+                for (int j = 0; j < C::BC; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+        }
+        if (kc + 1 < nk) {
+            if constexpr (C::NBUF == 1) __syncthreads();   // stage fully consumed
+            lstore(C::NBUF == 2 ? buf ^ 1 : 0);
+        }
+        __syncthreads();
+    }
+
+    // accumulator (i, j) reg 4*b4 + t holds o = e0 + wr*TE/2 + 32i + 8*b4 + 4g + t
+    // for candidate c0 + wc*TC/2 + 32j + l32
+#pragma unroll
+    for (int j = 0; j < C::BC; ++j) {
+        const int c = c0 + wc * (TC / 2) + j * 32 + l32;
+        if (c >= total_cand) continue;
+        bf16* qrow = Q + ((size_t)c * q + s) * d;
+#pragma unroll
+        for (int i = 0; i < C::BE; ++i)
+#pragma unroll
+            for (int b4 = 0; b4 < 4; ++b4) {
+                const int o = e0 + wr * (TE / 2) + i * 32 + b4 * 8 + 4 * g;
+                if (o < d) {
+                    bf16x4 v;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) v[t] = (bf16)acc[i][j][4 * b4 + t];
+                    *reinterpret_cast<bf16x4*>(qrow + o) = v;
+                }
+            }
+    }
+}
+
+template <int TE, int TC, int KC>
+hipError_t launch_prep(const void* Z, const void* Wq, int total_cand, int q, int d, void* Q,
+                       const PlanArgs& pa, hipStream_t stream) {
+    const int tiles_e = (d + TE - 1) / TE;
+    const int tiles_c = (total_cand + TC - 1) / TC;
+    const int64_t blocks = (int64_t)q * tiles_e * tiles_c + (pa.enabled ? 1 : 0);
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL((prep_kernel<TE, TC, KC>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const bf16*>(Z), static_cast<const bf16*>(Wq), total_cand, q, d,
+                       static_cast<bf16*>(Q), tiles_e, tiles_c, pa);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_project_plan_bf16(const void* Z, const void* Wq, int total_cand, int q, int d,
+                                    void* Q, const int* cu_kv, const int* cu_cand, int R,
+                                    int tile_m, int total_kv, void* ws, int64_t max_tiles,
+                                    hipStream_t stream) {
+    PlanArgs pa{cu_kv, cu_cand, static_cast<int*>(ws), max_tiles, R, tile_m, total_kv,
+                ws != nullptr ? 1 : 0};
+    if (total_cand <= 0 && !pa.enabled) return hipSuccess;
+    // wide tiles when they still give at least two work-groups per compute unit
+    const int64_t big = (int64_t)q * ((d + 127) / 128) * ((total_cand + 127) / 128);
+    if (big >= 512) return launch_prep<128, 128, 64>(Z, Wq, total_cand, q, d, Q, pa, stream);
+    return launch_prep<64, 64, 256>(Z, Wq, total_cand, q, d, Q, pa, stream);
+}
+
+}  // namespace xattn

@@ -101,6 +101,26 @@ class Workload:
         kv = (1 if self.kv_mode == "shared" else 2) * self.total_kv * self.d
         return float(b * (kv + 2 * self.rows * self.d + self.q * self.d * self.d))
 
+    def flops_projection(self) -> float:
+        """FLOPs of the TSP projection alone: 2 * rows * d * d."""
+        return 2.0 * self.rows * self.d * self.d
+
+    def bytes_projection(self) -> float:
+        """Bytes the projection must move: Z and W_Q in, Q out."""
+        b = 2 if self.dtype == "bf16" else 4
+        return float(b * (2 * self.rows * self.d + self.q * self.d * self.d))
+
+    def flops_attention(self) -> float:
+        """FLOPs of QK^T and PV: 4 * sum_r M_r * L_r * d."""
+        m = self.cands.astype(np.float64) * self.q
+        return 4.0 * float(np.sum(m * self.lengths)) * self.d
+
+    def bytes_attention(self) -> float:
+        """Bytes the attention over projected queries must move: K (and V), Q, O."""
+        b = 2 if self.dtype == "bf16" else 4
+        kv = (1 if self.kv_mode == "shared" else 2) * self.total_kv * self.d
+        return float(b * (kv + 2 * self.rows * self.d))
+
 
 def _normal(rng, shape, std=1.0):
     a = rng.standard_normal(size=shape, dtype=np.float32)

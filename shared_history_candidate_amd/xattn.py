@@ -23,7 +23,7 @@ XATTN_BF16, XATTN_FP32 = 0, 1
 XATTN_KV_SHARED, XATTN_KV_SEPARATE = 0, 1
 
 EXPORTED = ("xattn_create", "xattn_destroy", "xattn_workspace_size", "xattn_forward",
-            "xattn_attend", "xattn_plan", "xattn_max_tiles", "xattn_project", "xattn_device_error",
+            "xattn_attend", "xattn_attend_q", "xattn_plan", "xattn_max_tiles", "xattn_project", "xattn_device_error",
             "xattn_last_error")
 
 
@@ -63,6 +63,8 @@ def lib():
         L.xattn_forward.restype = ctypes.c_int
         L.xattn_attend.argtypes = L.xattn_forward.argtypes
         L.xattn_attend.restype = ctypes.c_int
+        L.xattn_attend_q.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, P, P, SZ, P]
+        L.xattn_attend_q.restype = ctypes.c_int
         L.xattn_plan.argtypes = [P, P, P, I32, I32, I32, I32, P, P, P, P,
                                  ctypes.POINTER(I32), P, SZ, P]
         L.xattn_plan.restype = ctypes.c_int
@@ -172,10 +174,32 @@ class XAttn:
 
     def attend(self, Z, W_Q, K, V, cu_seqlens_kv, cu_cand, heads: int, workspace, O=None,
                stream=None) -> torch.Tensor:
-        """The attention kernel alone, reusing the plan a previous forward()/plan()
-        of the same batch left in `workspace`."""
+        """Projection + attention, reusing the plan a previous forward()/plan() of
+        the same batch left in `workspace`."""
         return self.forward(Z, W_Q, K, V, cu_seqlens_kv, cu_cand, heads, O=O,
                             workspace=workspace, stream=stream, plan=False)
+
+    def attend_q(self, Q, K, V, cu_seqlens_kv, cu_cand, heads: int, workspace, O=None,
+                 stream=None) -> torch.Tensor:
+        """Attention kernel alone over already-projected queries Q [total_cand, q, d],
+        reusing the plan in `workspace`."""
+        d, q, dt = self.d_model, self.q, self.torch_dtype
+        total_cand, total_kv = Q.shape[0], K.shape[0]
+        R = cu_seqlens_kv.numel() - 1
+        self._check_tensor("Q", Q, dt, (total_cand, q, d))
+        self._check_tensor("K", K, dt, (total_kv, d))
+        if V is not None:
+            self._check_tensor("V", V, dt, (total_kv, d))
+        self._check_tensor("cu_seqlens_kv", cu_seqlens_kv, torch.int32, (R + 1,))
+        self._check_tensor("cu_cand", cu_cand, torch.int32, (R + 1,))
+        if O is None:
+            O = torch.empty((total_cand, q, d), dtype=dt, device=Q.device)
+        self._check_tensor("O", O, dt, (total_cand, q, d))
+        _check(lib().xattn_attend_q(self._h, _ptr(Q), _ptr(K), _ptr(V), _ptr(cu_seqlens_kv),
+                                    _ptr(cu_cand), R, total_cand, total_kv, heads, _ptr(O),
+                                    _ptr(workspace), workspace.numel(),
+                                    _stream(Q.device, stream)))
+        return O
 
     def plan(self, cu_seqlens_kv, cu_cand, heads: int, total_cand: int, total_kv: int,
              with_row_req: bool = True, workspace=None, stream=None):

@@ -85,7 +85,9 @@ def test_workspace_size(L):
     assert L.xattn_workspace_size(h, -1, 10, 4) == 0
     assert L.xattn_workspace_size(h, 1, 10, 0) == 0
     assert L.xattn_workspace_size(None, 1, 10, 4) == 0
-    assert L.xattn_max_tiles(h, 8, 2048, 4) * 16 + 256 == a
+    # plan header + 16 bytes per tile (256-aligned), then the projected bf16 queries
+    plan = (L.xattn_max_tiles(h, 8, 2048, 4) * 16 + 256 + 255) // 256 * 256
+    assert a == plan + 2048 * 3 * 256 * 2
     L.xattn_destroy(h)
 
 
@@ -144,6 +146,8 @@ def test_plan_host_validation(L):
     assert L.xattn_project(h, None, FAKE, 4, FAKE, None) == X.XATTN_EINVAL
     assert L.xattn_project(h, FAKE, FAKE, -1, FAKE, None) == X.XATTN_EINVAL
     assert L.xattn_project(h, FAKE, FAKE, 0, FAKE, None) == X.XATTN_OK
+    assert L.xattn_attend_q(h, None, FAKE, None, FAKE, FAKE, 2, 10, 20, 4, FAKE, FAKE, 1 << 24,
+                            None) == X.XATTN_EINVAL
     flag = ctypes.c_int32(0)
     assert L.xattn_device_error(h, None, ctypes.byref(flag), None) == X.XATTN_EINVAL
     L.xattn_destroy(h)

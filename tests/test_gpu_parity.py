@@ -216,3 +216,22 @@ def test_device_validation_flags_bad_offsets():
     ctx.forward(t["Z"], t["W_Q"], t["K"], None, t["cu_kv"], t["cu_cand"], wl.heads, O=O,
                 workspace=ws)
     assert ctx.device_error(ws) == 0
+
+
+@pytest.mark.parametrize("name", ["rest", "tiny"])
+def test_attend_and_attend_q_match_forward(name):
+    """attend (projection + attention over the stored plan) and attend_q
+    (attention over caller-projected queries) run the same kernels as forward."""
+    require_gpu()
+    wl = W.make(name, 0)
+    ctx = ctx_for(wl)
+    t = X.to_device(wl)
+    ws = ctx.alloc_workspace(wl.R, wl.total_cand, wl.heads)
+    a = ctx.forward(t["Z"], t["W_Q"], t["K"], t["V"], t["cu_kv"], t["cu_cand"], wl.heads,
+                    workspace=ws).clone()
+    b = ctx.attend(t["Z"], t["W_Q"], t["K"], t["V"], t["cu_kv"], t["cu_cand"], wl.heads, ws)
+    Q = ctx.project(t["Z"], t["W_Q"])
+    c = ctx.attend_q(Q, t["K"], t["V"], t["cu_kv"], t["cu_cand"], wl.heads, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert torch.equal(a, c)
