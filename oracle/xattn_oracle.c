@@ -25,7 +25,7 @@
  *       is turned into separate keys and values that each candidate's query
  *       cross-attends; here K and V are inputs (separate-K/V mode).
  *
- * Readings where the pages leave a step open (each is listed in the design doc):
+ * Readings where the pages leave a step open:
  *   - multi-head split: head h uses feature columns [h*d_h, (h+1)*d_h) of
  *     Z W_Q, of K and of V; d_h = d / heads; the score scale is 1/sqrt(d_h);
  *   - query row numbering: candidate c's slot s is row c*q + s, slot s uses

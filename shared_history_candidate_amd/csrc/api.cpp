@@ -259,7 +259,7 @@ xattn_status run_forward(Mode mode, xattn_ctx* ctx, const void* Z, const void* W
                                                 max_tiles, s);
             if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
         }
-        e = xattn::launch_attn_bf16(Qp, K, c.kv_mode == XATTN_KV_SEPARATE ? V : nullptr, cu_kv,
+        e = xattn::launch_attn_bf16(Qp, K, c.kv_mode == XATTN_KV_SEPARATE ? V : nullptr,
                                     workspace, max_tiles, c.n_slots, c.d_model, heads, var.rb,
                                     var.ksplit, O, s);
     } else {
@@ -277,7 +277,7 @@ xattn_status run_forward(Mode mode, xattn_ctx* ctx, const void* Z, const void* W
         e = xattn::launch_attn_f32(static_cast<const float*>(Qp), static_cast<const float*>(K),
                                    c.kv_mode == XATTN_KV_SEPARATE ? static_cast<const float*>(V)
                                                                   : nullptr,
-                                   cu_kv, workspace, max_tiles, c.n_slots, c.d_model, heads,
+                                   workspace, max_tiles, c.n_slots, c.d_model, heads,
                                    static_cast<float*>(O), s);
     }
     if (e != hipSuccess) return hip_fail(e, "attention kernel launch");

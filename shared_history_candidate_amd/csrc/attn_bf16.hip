@@ -27,10 +27,11 @@
 // through double-buffered LDS (one buffer is both K and V in projection-free
 // mode) and V^T operands come from LDS transpose reads.
 //
-// Softmax: exp2 of log2(e)/sqrt(d_h)-scaled scores.  The running maximum is
-// only moved when a tile exceeds it by more than 2^8 (then the accumulators
-// are rescaled); between moves the weights are bounded by 2^8, which fp32
-// sums and bf16 operands hold exactly as well as weights <= 1.  Row sums
+// Softmax: exp2 of log2(e)/sqrt(d_h)-scaled scores against a running maximum
+// that is set by the first tile and afterwards moved (with a rescale of the
+// accumulators) only when a lane's weights of a tile sum to more than 2^12.
+// Weights up to that bound are held by fp32 sums and bf16 operands exactly as
+// well as weights <= 1, and no per-tile maximum has to be computed.  Row sums
 // accumulate the bf16-rounded weights that enter the PV product (v_dot2).
 #include "common.h"
 #include "internal.h"
@@ -44,7 +45,7 @@ namespace {
 #endif
 
 constexpr int BN = 64;               // memory rows per tile
-constexpr float kLazy = 8.0f;        // exp2-domain headroom of the running maximum
+constexpr float kSumCap = 4096.0f;   // largest accepted per-lane weight sum of one tile
 
 constexpr int pow2floor(int x) {
     int p = 1;
@@ -74,26 +75,30 @@ struct Cfg {
     static constexpr int KV_CHUNKS = BN * DH / 8;                 // 16-byte chunks per plane
     static constexpr int KV_CPT = KV_CHUNKS / (64 * RB);
     static_assert(KV_CHUNKS % (64 * RB) == 0, "memory tile must split evenly over a split group");
+    // Register stages of the memory prefetch: up to 8 x 16 bytes per thread
+    // in flight (32 VGPRs), at most 4 tiles ahead of the LDS stage.
+    static constexpr int STAGE_REGS = KV_CPT * PLANES;
+    static constexpr int P = STAGE_REGS >= 8 ? 1 : (8 / STAGE_REGS >= 4 ? 4 : 8 / STAGE_REGS);
 };
 
 template <int DH, int RB, int KSPLIT, bool SEP>
 __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(
     const bf16* __restrict__ Qp, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const int* __restrict__ cu_kv, const int* __restrict__ ws, int q, int d, int heads,
-    float scale_log2, bf16* __restrict__ O) {
+    const int* __restrict__ ws, int q, int d, int heads, float scale_log2,
+    bf16* __restrict__ O) {
     using C = Cfg<DH, RB, KSPLIT, SEP>;
+    constexpr int P = C::P;
     __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
 
     const int n_tiles = ws[kPlanNTiles];
     const int tile = blockIdx.x / heads;
     const int h = blockIdx.x - tile * heads;
-    // A plan built for another tile size (another batch shape) is not ours.
-    if (tile >= n_tiles || ws[kPlanTileM] != 32 * RB) return;
     const int4 item = reinterpret_cast<const int4*>(
         reinterpret_cast<const char*>(ws) + kPlanHeaderBytes)[tile];
-    const int r = item.x, s = item.y, c0 = item.z, nc = item.w;
-    const int kv0 = cu_kv[r];
-    const int L = cu_kv[r + 1] - kv0;
+    // A plan built for another tile size (another batch shape) is not ours.
+    if (tile >= n_tiles || ws[kPlanTileM] != 32 * RB) return;
+    const int kv0 = item.x, L = item.y, c0 = item.z;
+    const int nc = item.w & kItemNcMask, s = item.w >> 16;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -107,7 +112,65 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(
     const int cand = c0 + qcol;
     const int gt = tid - ksg * 64 * RB;       // thread index inside the split group
 
-    // ---------------- 1. this wave's Q_h^T operands ----------------
+    // ---------------- 1. memory prefetch and this wave's Q_h^T operands ----------------
+    const int ntiles_kv = (L + BN - 1) / BN;
+    const int n_iter = (ntiles_kv + KSPLIT - 1) / KSPLIT;
+    const bf16* Kh = K + (size_t)kv0 * d + h * DH;
+    const bf16* Vh = SEP ? V + (size_t)kv0 * d + h * DH : nullptr;
+    // Chunk u of this thread: tile row j_u, 16-byte column chunk c8_u.  Its
+    // global byte offset inside a tile and its LDS element offset are fixed;
+    // tiles differ only by the buffer base.  Buffer loads return zeros past
+    // the request's last memory row (and for whole tiles past it, whose
+    // descriptor covers no bytes), so partial tiles need no special case.
+    int goff[C::KV_CPT], loff[C::KV_CPT];
+#pragma unroll
+    for (int u = 0; u < C::KV_CPT; ++u) {
+        const int c = gt + u * 64 * RB;
+        const int j = c / (DH / 8), c8 = c % (DH / 8);
+        goff[u] = (j * d + c8 * 8) * 2;
+        loff[u] = j * C::LDK + c8 * 8;
+    }
+    uint4 kreg[P][C::KV_CPT];
+    uint4 vreg[P][SEP ? C::KV_CPT : 1];
+    auto gload = [&](int t, uint4 (&kr)[C::KV_CPT], uint4 (&vr)[SEP ? C::KV_CPT : 1]) {
+        const int row0 = t * BN;
+        const int left = L - row0;   // memory rows of the request from this tile on
+        const size_t nb = left > 0 ? (size_t)left * d * 2 : 0;
+        const uint32_t bytes = nb > 0xFFFFFFF0u ? 0xFFFFFFF0u : (uint32_t)nb;
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(Kh + (size_t)row0 * d), (short)0, bytes, 0x00020000);
+#pragma unroll
+        for (int u = 0; u < C::KV_CPT; ++u)
+            kr[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, goff[u], 0, 0));
+        if constexpr (SEP) {
+            const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(Vh + (size_t)row0 * d), (short)0, bytes, 0x00020000);
+#pragma unroll
+            for (int u = 0; u < C::KV_CPT; ++u)
+                vr[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, goff[u], 0, 0));
+        }
+    };
+    bf16* kvl = reinterpret_cast<bf16*>(smem) + (size_t)ksg * 2 * C::PLANES * C::TILE;
+    auto lstore = [&](int buf, const uint4 (&kr)[C::KV_CPT], const uint4 (&vr)[SEP ? C::KV_CPT : 1]) {
+        bf16* base = kvl + buf * C::PLANES * C::TILE;
+#pragma unroll
+        for (int u = 0; u < C::KV_CPT; ++u) {
+            if constexpr (C::PAD % 8 == 0) {
+                *reinterpret_cast<uint4*>(base + loff[u]) = kr[u];
+                if constexpr (SEP) *reinterpret_cast<uint4*>(base + C::TILE + loff[u]) = vr[u];
+            } else {   // rows are only 8-byte aligned
+                uint2* p = reinterpret_cast<uint2*>(base + loff[u]);
+                p[0] = make_uint2(kr[u].x, kr[u].y);
+                p[1] = make_uint2(kr[u].z, kr[u].w);
+                if constexpr (SEP) {
+                    uint2* pv = reinterpret_cast<uint2*>(base + C::TILE + loff[u]);
+                    pv[0] = make_uint2(vr[u].x, vr[u].y);
+                    pv[1] = make_uint2(vr[u].z, vr[u].w);
+                }
+            }
+        }
+    };
+
     // k-step k, half g: features 16k + 8g .. 16k + 8g + 7 of the lane's query
     // row (columns past the tile re-read its last row; their output is dropped)
     bf16x8 qb[C::KST];
@@ -117,6 +180,19 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(
         for (int k = 0; k < C::KST; ++k)
             qb[k] = *reinterpret_cast<const bf16x8*>(qrow + 16 * k + 8 * g);
     }
+    // The first P tiles of this split are requested right behind the queries.
+#pragma unroll
+    for (int j = 0; j < P; ++j) gload(ksg + j * KSPLIT, kreg[j], vreg[j]);
+    // Consume the query registers here, before the loop: the queries are then
+    // known to have arrived on entry to the memory loop, and the only loads in
+    // flight across its iterations are the memory stages, which keeps the
+    // compiler's wait counts inside the loop exact (no wait on a later stage).
+#pragma unroll
+    for (int k = 0; k < C::KST; ++k) asm volatile("" ::"v"(qb[k]));
+
+    lstore(0, kreg[0], vreg[0]);
+    gload(ksg + P * KSPLIT, kreg[0], vreg[0]);
+    __syncthreads();
 
     // ---------------- 2. stream this split's memory tiles ----------------
     f32x16 oacc[C::EB];
@@ -124,69 +200,7 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(
     for (int eb = 0; eb < C::EB; ++eb) oacc[eb] = f32x16{};
     float m_run = -INFINITY;   // running max, exp2 domain (identical in both halves)
     float l_run = 0.f;         // this half's share of the row sum
-
-    bf16* kvl = reinterpret_cast<bf16*>(smem) + (size_t)ksg * 2 * C::PLANES * C::TILE;
-    const int ntiles_kv = (L + BN - 1) / BN;
-    const int n_iter = (ntiles_kv + KSPLIT - 1) / KSPLIT;
-    const bf16* Kh = K + (size_t)kv0 * d + h * DH;
-    const bf16* Vh = SEP ? V + (size_t)kv0 * d + h * DH : nullptr;
-    uint4 kreg[C::KV_CPT];
-    uint4 vreg[SEP ? C::KV_CPT : 1];
-    // Chunk u of this thread: tile row j_u, 16-byte column chunk c8_u.  Its
-    // global byte offset inside a tile and its LDS element offset are fixed;
-    // tiles differ only by the buffer base.  Buffer loads return zeros past
-    // the request's last memory row, so partial tiles need no special case.
-    int goff[C::KV_CPT], loff[C::KV_CPT];
-#pragma unroll
-    for (int u = 0; u < C::KV_CPT; ++u) {
-        const int c = gt + u * 64 * RB;
-        const int j = c / (DH / 8), c8 = c % (DH / 8);
-        goff[u] = (j * d + c8 * 8) * 2;
-        loff[u] = j * C::LDK + c8 * 8;
-    }
-    auto gload = [&](int t) {
-        const size_t row0 = (size_t)t * BN;
-        const size_t rest = (size_t)(L - (int)row0) * d * 2;   // bytes left in the request
-        const uint32_t bytes = rest > 0xFFFFFFF0u ? 0xFFFFFFF0u : (uint32_t)rest;
-        const __amdgpu_buffer_rsrc_t rk =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(Kh + row0 * d), (short)0, bytes, 0x00020000);
-#pragma unroll
-        for (int u = 0; u < C::KV_CPT; ++u)
-            kreg[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, goff[u], 0, 0));
-        if constexpr (SEP) {
-            const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-                (void*)(Vh + row0 * d), (short)0, bytes, 0x00020000);
-#pragma unroll
-            for (int u = 0; u < C::KV_CPT; ++u)
-                vreg[u] =
-                    __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, goff[u], 0, 0));
-        }
-    };
-    auto lstore = [&](int buf) {
-        bf16* base = kvl + buf * C::PLANES * C::TILE;
-#pragma unroll
-        for (int u = 0; u < C::KV_CPT; ++u) {
-            if constexpr (C::PAD % 8 == 0) {
-                *reinterpret_cast<uint4*>(base + loff[u]) = kreg[u];
-                if constexpr (SEP) *reinterpret_cast<uint4*>(base + C::TILE + loff[u]) = vreg[u];
-            } else {   // rows are only 8-byte aligned
-                uint2* p = reinterpret_cast<uint2*>(base + loff[u]);
-                p[0] = make_uint2(kreg[u].x, kreg[u].y);
-                p[1] = make_uint2(kreg[u].z, kreg[u].w);
-                if constexpr (SEP) {
-                    uint2* pv = reinterpret_cast<uint2*>(base + C::TILE + loff[u]);
-                    pv[0] = make_uint2(vreg[u].x, vreg[u].y);
-                    pv[1] = make_uint2(vreg[u].z, vreg[u].w);
-                }
-            }
-        }
-    };
-
-    if (ksg < ntiles_kv) {
-        gload(ksg);
-        lstore(0);
-    }
-    __syncthreads();
+    bool started = false;      // m_run holds a tile maximum (wave-uniform)
 
     // transposed V read: lane l receives V[16u + 4g + t][eb*32 + l%32], t = 0..3
     const int G = lane >> 4, k16 = lane & 15;
@@ -194,93 +208,131 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(
     const int tr_col = 16 * (G & 1) + 4 * (k16 & 3);
     const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 
-    for (int it = 0; it < n_iter; ++it) {
-        const int t = ksg + it * KSPLIT;          // this split's tile
-        const int buf = it & 1;
-        const bool have = t < ntiles_kv;
-        const bool next = t + KSPLIT < ntiles_kv;
-        if (next) gload(t + KSPLIT);
-        if (have) {
-            const bf16* kb = kvl + buf * C::PLANES * C::TILE;
-            const bf16* vb = kb + (C::PLANES - 1) * C::TILE;
-            // scores: sacc[0] keys 0..31, sacc[1] keys 32..63 of the tile.
-            // All K fragments are read before the first product so that the
-            // LDS latency is paid once per tile.
-            bf16x8 kf[2][C::KST];
+    // One memory tile (t, staged in LDS buffer buf) against this wave's queries.
+    auto tile_step = [&](int t, int buf) {
+        const bf16* kb = kvl + buf * C::PLANES * C::TILE;
+        const bf16* vb = kb + (C::PLANES - 1) * C::TILE;
+        // scores: sacc[0] keys 0..31, sacc[1] keys 32..63 of the tile.
+        // All K fragments are read before the first product so that the
+        // LDS latency is paid once per tile.
+        bf16x8 kf[2][C::KST];
 #pragma unroll
-            for (int k = 0; k < C::KST; ++k) {
-                const int e0 = 16 * k + 8 * g;
+        for (int k = 0; k < C::KST; ++k) {
+            const int e0 = 16 * k + 8 * g;
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const bf16* row = kb + (hh * 32 + l32) * C::LDK + e0;
-                    kf[hh][k] = cat(*reinterpret_cast<const bf16x4*>(row),
-                                    *reinterpret_cast<const bf16x4*>(row + 4));
-                }
+            for (int hh = 0; hh < 2; ++hh) {
+                const bf16* row = kb + (hh * 32 + l32) * C::LDK + e0;
+                kf[hh][k] = cat(*reinterpret_cast<const bf16x4*>(row),
+                                *reinterpret_cast<const bf16x4*>(row + 4));
             }
-            f32x16 sacc[2] = {f32x16{}, f32x16{}};
+        }
+        f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-            for (int k = 0; k < C::KST; ++k)
+        for (int k = 0; k < C::KST; ++k)
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) sacc[hh] = mfma32(kf[hh][k], qb[k], sacc[hh]);
-            // scheduling: every K-fragment read ahead of the score products
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::KST, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::KST, 0);
-            // V^T fragments for the output product, issued now so that they
-            // arrive while the weights are being computed
-            bf16x8 vf[4][C::EB];
+            for (int hh = 0; hh < 2; ++hh) sacc[hh] = mfma32(kf[hh][k], qb[k], sacc[hh]);
+        // scheduling: every K-fragment read ahead of the score products
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::KST, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::KST, 0);
+        // V^T fragments for the output product, issued now so that they
+        // arrive while the weights are being computed
+        bf16x8 vf[4][C::EB];
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
-                for (int eb = 0; eb < C::EB; ++eb) {
-                    const bf16* base = vb + (16 * u + tr_row) * C::LDK + eb * 32 + tr_col;
-                    vf[u][eb] = cat(lds_read_tr16(base), lds_read_tr16(base + 8 * C::LDK));
-                }
-            const int jleft = L - t * BN;
-            if (jleft < BN) {
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-                    for (int rr = 0; rr < 16; ++rr) {
-                        const int j = hh * 32 + (rr >> 2) * 8 + 4 * g + (rr & 3);
-                        if (j >= jleft) sacc[hh][rr] = -INFINITY;
-                    }
+            for (int eb = 0; eb < C::EB; ++eb) {
+                const bf16* base = vb + (16 * u + tr_row) * C::LDK + eb * 32 + tr_col;
+                vf[u][eb] = cat(lds_read_tr16(base), lds_read_tr16(base + 8 * C::LDK));
             }
+        const int jleft = L - t * BN;
+        // Only the request's last tile is partial.  The opaque copy keeps the
+        // compiler from folding the tile-level test into the per-score tests
+        // (which would then run on every tile).
+        int jl = jleft;
+        asm volatile("" : "+s"(jl));
+        if (jl < BN) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    const int j = hh * 32 + (rr >> 2) * 8 + 4 * g + (rr & 3);
+                    if (j >= jleft) sacc[hh][rr] = -INFINITY;
+                }
+        }
+        // Weights against the running maximum m_run, summed per lane over the
+        // bf16 values that enter the PV product.
+        bf16x8 pb[4];
+        auto weights = [&]() {
+            float lt = 0.f;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int rr = 0; rr < 16; rr += 2) {
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[hh][rr], scale_log2, -m_run));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[hh][rr + 1], scale_log2, -m_run));
+                    const bf16x2 pp = {(bf16)p0, (bf16)p1};
+                    lt = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lt, false);
+                    pb[hh * 2 + (rr >> 3)][rr & 7] = pp[0];
+                    pb[hh * 2 + (rr >> 3)][(rr & 7) + 1] = pp[1];
+                }
+            return lt;
+        };
+        float lt = weights();
+        // The running maximum is moved only when it has to be: before the
+        // first tile, or when some weight of this tile could exceed
+        // kSumCap (a lane's sum of its 32 non-negative weights bounds each of
+        // them).  Weights up to kSumCap are as exact in the fp32 sums and as
+        // well represented as bf16 operands as weights <= 1, and the final
+        // normalisation divides the common factor out.
+        if (!started || __any(lt > kSumCap)) {
             float mt = fmaxf(sacc[0][0], sacc[0][1]);
 #pragma unroll
             for (int rr = 2; rr < 16; rr += 2) mt = fmaxf(mt, fmaxf(sacc[0][rr], sacc[0][rr + 1]));
 #pragma unroll
             for (int rr = 0; rr < 16; rr += 2) mt = fmaxf(mt, fmaxf(sacc[1][rr], sacc[1][rr + 1]));
             mt *= scale_log2;
-            if (__any(mt > m_run + kLazy)) {
-                const float m_new = fmaxf(m_run, fmaxf(mt, xor32(mt)));
-                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-                m_run = m_new;
-                l_run *= alpha;
+            const float m_new = fmaxf(m_run, fmaxf(mt, xor32(mt)));
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
 #pragma unroll
-                for (int eb = 0; eb < C::EB; ++eb) oacc[eb] *= alpha;
-            }
-            bf16x8 pb[4];
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-                for (int rr = 0; rr < 16; rr += 2) {
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[hh][rr], scale_log2, -m_run));
-                    const float p1 =
-                        __builtin_amdgcn_exp2f(fmaf(sacc[hh][rr + 1], scale_log2, -m_run));
-                    const bf16x2 pp = {(bf16)p0, (bf16)p1};
-                    l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run, false);
-                    pb[hh * 2 + (rr >> 3)][rr & 7] = pp[0];
-                    pb[hh * 2 + (rr >> 3)][(rr & 7) + 1] = pp[1];
-                }
-            // O^T += V^T P^T over the four 16-key slabs of the tile
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int eb = 0; eb < C::EB; ++eb) oacc[eb] = mfma32(vf[u][eb], pb[u], oacc[eb]);
+            for (int eb = 0; eb < C::EB; ++eb) oacc[eb] *= alpha;
+            lt = weights();
+            started = true;
         }
-        if (next) lstore(buf ^ 1);
+        l_run += lt;
+        // O^T += V^T P^T over the four 16-key slabs of the tile
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int eb = 0; eb < C::EB; ++eb) oacc[eb] = mfma32(vf[u][eb], pb[u], oacc[eb]);
+    };
+
+    // Iteration it computes this split's tile ksg + it*KSPLIT from LDS buffer
+    // it&1, then moves the next tile from register stage (it+1)%P into the
+    // other buffer and refills that stage with the tile P iterations ahead.
+    // The refill is issued on every path (past the end it moves no bytes), so
+    // the loads in flight are always the same stages in the same order and
+    // the compiler's wait before each LDS store covers only the stage stored.
+    auto step = [&](int it, int j) {
+        const int t = ksg + it * KSPLIT;
+        if (t < ntiles_kv) tile_step(t, it & 1);
+        const int jn = (j + 1) % P;
+        if (it + 1 < n_iter) lstore((it + 1) & 1, kreg[jn], vreg[jn]);
+        gload(ksg + (it + 1 + P) * KSPLIT, kreg[jn], vreg[jn]);
         if constexpr (!C::PRIVATE) __syncthreads();
+    };
+    // Whole groups of P iterations in a loop whose body has no early exit (the
+    // register stage of every step is static), then the remaining < P
+    // iterations once each.
+    int it0 = 0;
+    for (; it0 + P <= n_iter; it0 += P) {
+#pragma unroll
+        for (int j = 0; j < P; ++j) step(it0 + j, j);
     }
+#pragma unroll
+    for (int j = 0; j < P - 1; ++j)
+        if (it0 + j < n_iter) step(it0 + j, j);
     if constexpr (C::PRIVATE) __syncthreads();   // the merge below reuses the tile buffers
 
     // ---------------- 3. merge the memory splits, normalise, store ----------------
@@ -345,7 +397,7 @@ constexpr bool fits() {
 
 template <int DH, int RB, int KSPLIT, bool SEP>
 hipError_t launch_one(const void* Qp, const void* K, const void* V,
-                      const int* cu_kv, const void* ws, int64_t max_tiles, int q, int d,
+                      const void* ws, int64_t max_tiles, int q, int d,
                       int heads, void* O, hipStream_t stream) {
     if constexpr (!fits<DH, RB, KSPLIT, SEP>()) {
         return hipErrorInvalidValue;
@@ -356,7 +408,7 @@ hipError_t launch_one(const void* Qp, const void* K, const void* V,
     hipLaunchKernelGGL((attn_bf16_kernel<DH, RB, KSPLIT, SEP>), dim3((unsigned)blocks),
                        dim3(64 * RB * KSPLIT), 0, stream, static_cast<const bf16*>(Qp),
                        static_cast<const bf16*>(K),
-                       static_cast<const bf16*>(V), cu_kv, static_cast<const int*>(ws), q, d,
+                       static_cast<const bf16*>(V), static_cast<const int*>(ws), q, d,
                        heads, scale_log2, static_cast<bf16*>(O));
     return hipGetLastError();
     }
@@ -364,22 +416,22 @@ hipError_t launch_one(const void* Qp, const void* K, const void* V,
 
 template <int DH, int RB, int KSPLIT>
 hipError_t launch_sep(const void* Qp, const void* K, const void* V,
-                      const int* cu_kv, const void* ws, int64_t max_tiles, int q, int d,
+                      const void* ws, int64_t max_tiles, int q, int d,
                       int heads, void* O, hipStream_t stream) {
     if (V)
-        return launch_one<DH, RB, KSPLIT, true>(Qp, K, V, cu_kv, ws, max_tiles, q, d, heads, O,
+        return launch_one<DH, RB, KSPLIT, true>(Qp, K, V, ws, max_tiles, q, d, heads, O,
                                                 stream);
-    return launch_one<DH, RB, KSPLIT, false>(Qp, K, V, cu_kv, ws, max_tiles, q, d, heads, O,
+    return launch_one<DH, RB, KSPLIT, false>(Qp, K, V, ws, max_tiles, q, d, heads, O,
                                              stream);
 }
 
 template <int DH>
 hipError_t launch_dh(const void* Qp, const void* K, const void* V,
-                     const int* cu_kv, const void* ws, int64_t max_tiles, int q, int d,
+                     const void* ws, int64_t max_tiles, int q, int d,
                      int heads, int rb, int ksplit, void* O, hipStream_t stream) {
 #define XATTN_CASE(R_, S_)                                                                     \
     if (rb == R_ && ksplit == S_)                                                              \
-        return launch_sep<DH, R_, S_>(Qp, K, V, cu_kv, ws, max_tiles, q, d, heads, O, stream);
+        return launch_sep<DH, R_, S_>(Qp, K, V, ws, max_tiles, q, d, heads, O, stream);
     XATTN_CASE(1, 4)
     XATTN_CASE(2, 2)
     XATTN_CASE(4, 1)
@@ -418,17 +470,17 @@ int attn_bf16_variant_smem(int dh, int rb, int ksplit, bool sep) {
 }
 
 hipError_t launch_attn_bf16(const void* Qp, const void* K, const void* V,
-                            const int* cu_kv, const void* ws, int64_t max_tiles, int q, int d,
+                            const void* ws, int64_t max_tiles, int q, int d,
                             int heads, int rb, int ksplit, void* O, hipStream_t stream) {
     switch (d / heads) {
         case 32:
-            return launch_dh<32>(Qp, K, V, cu_kv, ws, max_tiles, q, d, heads, rb, ksplit, O,
+            return launch_dh<32>(Qp, K, V, ws, max_tiles, q, d, heads, rb, ksplit, O,
                                  stream);
         case 64:
-            return launch_dh<64>(Qp, K, V, cu_kv, ws, max_tiles, q, d, heads, rb, ksplit, O,
+            return launch_dh<64>(Qp, K, V, ws, max_tiles, q, d, heads, rb, ksplit, O,
                                  stream);
         case 128:
-            return launch_dh<128>(Qp, K, V, cu_kv, ws, max_tiles, q, d, heads, rb, ksplit, O,
+            return launch_dh<128>(Qp, K, V, ws, max_tiles, q, d, heads, rb, ksplit, O,
                                   stream);
         default:
             return hipErrorInvalidValue;

@@ -20,8 +20,8 @@ constexpr int kBN = 32;    // memory rows per tile
 template <int DHMAX>
 __global__ __launch_bounds__(kRows) void attn_f32_kernel(
     const float* __restrict__ Qp, const float* __restrict__ K, const float* __restrict__ V,
-    const int* __restrict__ cu_kv, const int* __restrict__ ws, int q, int d, int heads,
-    float scale_log2, float* __restrict__ O) {
+    const int* __restrict__ ws, int q, int d, int heads, float scale_log2,
+    float* __restrict__ O) {
     __shared__ float ks[kBN][DHMAX];
     __shared__ float vs[kBN][DHMAX];
     const int dh = d / heads;
@@ -31,9 +31,8 @@ __global__ __launch_bounds__(kRows) void attn_f32_kernel(
     if (tile >= n_tiles || ws[kPlanTileM] != kRows) return;
     const int4 item = reinterpret_cast<const int4*>(
         reinterpret_cast<const char*>(ws) + kPlanHeaderBytes)[tile];
-    const int r = item.x, s = item.y, c0 = item.z, nc = item.w;
-    const int kv0 = cu_kv[r];
-    const int L = cu_kv[r + 1] - kv0;
+    const int kv0 = item.x, L = item.y, c0 = item.z;
+    const int nc = item.w & kItemNcMask, s = item.w >> 16;
     const int i = threadIdx.x;
     const bool valid = i < nc;
     const int cand = c0 + i;
@@ -114,29 +113,28 @@ __global__ void project_f32_kernel(const float* __restrict__ Z, const float* __r
 
 template <int DHMAX>
 hipError_t launch_f32(const float* Qp, const float* K, const float* V,
-                      const int* cu_kv, const void* ws, int64_t max_tiles, int q, int d,
+                      const void* ws, int64_t max_tiles, int q, int d,
                       int heads, float* O, hipStream_t stream) {
     const int dh = d / heads;
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)dh);
     const int64_t blocks = max_tiles * heads;
     if (blocks <= 0) return hipSuccess;
     hipLaunchKernelGGL((attn_f32_kernel<DHMAX>), dim3((unsigned)blocks), dim3(kRows), 0, stream,
-                       Qp, K, V, cu_kv, static_cast<const int*>(ws), q, d, heads,
-                       scale_log2, O);
+                       Qp, K, V, static_cast<const int*>(ws), q, d, heads, scale_log2, O);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_f32(const float* Qp, const float* K, const float* V,
-                           const int* cu_kv, const void* ws, int64_t max_tiles, int q, int d,
+                           const void* ws, int64_t max_tiles, int q, int d,
                            int heads, float* O, hipStream_t stream) {
     const int dh = d / heads;
-    if (dh <= 8) return launch_f32<8>(Qp, K, V, cu_kv, ws, max_tiles, q, d, heads, O, stream);
-    if (dh <= 16) return launch_f32<16>(Qp, K, V, cu_kv, ws, max_tiles, q, d, heads, O, stream);
-    if (dh <= 32) return launch_f32<32>(Qp, K, V, cu_kv, ws, max_tiles, q, d, heads, O, stream);
-    if (dh <= 64) return launch_f32<64>(Qp, K, V, cu_kv, ws, max_tiles, q, d, heads, O, stream);
-    if (dh <= 128) return launch_f32<128>(Qp, K, V, cu_kv, ws, max_tiles, q, d, heads, O, stream);
+    if (dh <= 8) return launch_f32<8>(Qp, K, V, ws, max_tiles, q, d, heads, O, stream);
+    if (dh <= 16) return launch_f32<16>(Qp, K, V, ws, max_tiles, q, d, heads, O, stream);
+    if (dh <= 32) return launch_f32<32>(Qp, K, V, ws, max_tiles, q, d, heads, O, stream);
+    if (dh <= 64) return launch_f32<64>(Qp, K, V, ws, max_tiles, q, d, heads, O, stream);
+    if (dh <= 128) return launch_f32<128>(Qp, K, V, ws, max_tiles, q, d, heads, O, stream);
     return hipErrorInvalidValue;
 }
 

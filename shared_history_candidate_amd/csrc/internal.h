@@ -16,8 +16,7 @@ hipError_t launch_plan(const int* cu_kv, const int* cu_cand, int R, int q, int t
 // returns the LDS bytes of variant (rb, ksplit) for head width dh and the
 // K/V mode, 0 if not built.
 int attn_bf16_variant_smem(int dh, int rb, int ksplit, bool sep);
-hipError_t launch_attn_bf16(const void* Qp, const void* K, const void* V, const int* cu_kv,
-                            const void* ws, int64_t max_tiles, int q, int d, int heads, int rb,
+hipError_t launch_attn_bf16(const void* Qp, const void* K, const void* V, const void* ws, int64_t max_tiles, int q, int d, int heads, int rb,
                             int ksplit, void* O, hipStream_t stream);
 
 // bf16 TSP projection Q = Z W_Q[slot] into Qp; when ws is not NULL the same
@@ -28,8 +27,7 @@ hipError_t launch_project_plan_bf16(const void* Z, const void* Wq, int total_can
                                     hipStream_t stream);
 
 // fp32 path (tile_m = 64): attention over projected queries, projection.
-hipError_t launch_attn_f32(const float* Qp, const float* K, const float* V, const int* cu_kv,
-                           const void* ws, int64_t max_tiles, int q, int d, int heads, float* O,
+hipError_t launch_attn_f32(const float* Qp, const float* K, const float* V, const void* ws, int64_t max_tiles, int q, int d, int heads, float* O,
                            hipStream_t stream);
 
 hipError_t launch_project_f32(const float* Z, const float* Wq, int total_cand, int q, int d,

@@ -140,9 +140,9 @@ __device__ void run_plan(const int* __restrict__ cu_kv, const int* __restrict__ 
         const int n = cu_cand[r + 1] - cu_cand[r];
         const int c0 = cu_cand[r] + b * tile_m;
         const int nc = min(tile_m, n - b * tile_m);
-        const int4 rec = make_int4(r, s, c0, nc);
-        tiles[i] = rec;
-        if (tiles_out) reinterpret_cast<int4*>(tiles_out)[i] = rec;
+        const int kv0 = cu_kv[r];
+        tiles[i] = make_int4(kv0, cu_kv[r + 1] - kv0, c0, nc | (s << 16));
+        if (tiles_out) reinterpret_cast<int4*>(tiles_out)[i] = make_int4(r, s, c0, nc);
     }
     if (t == 0) {
         ws[kPlanNTiles] = total;
