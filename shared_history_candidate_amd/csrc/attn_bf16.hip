@@ -33,6 +33,8 @@
 // Weights up to that bound are held by fp32 sums and bf16 operands exactly as
 // well as weights <= 1, and no per-tile maximum has to be computed.  Row sums
 // accumulate the bf16-rounded weights that enter the PV product (v_dot2).
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -183,12 +185,16 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(
     // The first P tiles of this split are requested right behind the queries.
 #pragma unroll
     for (int j = 0; j < P; ++j) gload(ksg + j * KSPLIT, kreg[j], vreg[j]);
-    // Consume the query registers here, before the loop: the queries are then
+    // Fold log2(e)/sqrt(d_h) into the query operands (one more bf16 rounding
+    // of Q; the scores then come out of the products in exp2 units).  This
+    // also consumes the query registers before the loop: the queries are then
     // known to have arrived on entry to the memory loop, and the only loads in
     // flight across its iterations are the memory stages, which keeps the
     // compiler's wait counts inside the loop exact (no wait on a later stage).
 #pragma unroll
-    for (int k = 0; k < C::KST; ++k) asm volatile("" ::"v"(qb[k]));
+    for (int k = 0; k < C::KST; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qb[k][e] = (bf16)((float)qb[k][e] * scale_log2);
 
     lstore(0, kreg[0], vreg[0]);
     gload(ksg + P * KSPLIT, kreg[0], vreg[0]);
@@ -201,6 +207,10 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(
     float m_run = -INFINITY;   // running max, exp2 domain (identical in both halves)
     float l_run = 0.f;         // this half's share of the row sum
     bool started = false;      // m_run holds a tile maximum (wave-uniform)
+    // Seed of every score accumulator: -m_run once started (0 before), so the
+    // products deliver s*log2(e)/sqrt(d_h) - m_run and the weights are a bare
+    // exp2.  All 16 registers of a lane belong to its query row.
+    f32x16 negm = f32x16{};
 
     // transposed V read: lane l receives V[16u + 4g + t][eb*32 + l%32], t = 0..3
     const int G = lane >> 4, k16 = lane & 15;
@@ -226,9 +236,11 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(
                                 *reinterpret_cast<const bf16x4*>(row + 4));
             }
         }
-        f32x16 sacc[2] = {f32x16{}, f32x16{}};
+        f32x16 sacc[2];
 #pragma unroll
-        for (int k = 0; k < C::KST; ++k)
+        for (int hh = 0; hh < 2; ++hh) sacc[hh] = mfma32(kf[hh][0], qb[0], negm);
+#pragma unroll
+        for (int k = 1; k < C::KST; ++k)
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) sacc[hh] = mfma32(kf[hh][k], qb[k], sacc[hh]);
         // scheduling: every K-fragment read ahead of the score products
@@ -259,17 +271,19 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(
                     if (j >= jleft) sacc[hh][rr] = -INFINITY;
                 }
         }
-        // Weights against the running maximum m_run, summed per lane over the
-        // bf16 values that enter the PV product.
+        // Weights 2^(score - m_run + shift), summed per lane over the bf16
+        // values that enter the PV product.
         bf16x8 pb[4];
-        auto weights = [&]() {
+        auto weights = [&](auto shifted, float shift) {
             float lt = 0.f;
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
                 for (int rr = 0; rr < 16; rr += 2) {
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[hh][rr], scale_log2, -m_run));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[hh][rr + 1], scale_log2, -m_run));
+                    float x0 = sacc[hh][rr], x1 = sacc[hh][rr + 1];
+                    if constexpr (decltype(shifted)::value) x0 += shift, x1 += shift;
+                    const float p0 = __builtin_amdgcn_exp2f(x0);
+                    const float p1 = __builtin_amdgcn_exp2f(x1);
                     const bf16x2 pp = {(bf16)p0, (bf16)p1};
                     lt = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lt, false);
                     pb[hh * 2 + (rr >> 3)][rr & 7] = pp[0];
@@ -277,7 +291,7 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(
                 }
             return lt;
         };
-        float lt = weights();
+        float lt = weights(std::false_type{}, 0.f);
         // The running maximum is moved only when it has to be: before the
         // first tile, or when some weight of this tile could exceed
         // kSumCap (a lane's sum of its 32 non-negative weights bounds each of
@@ -285,20 +299,22 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(
         // well represented as bf16 operands as weights <= 1, and the final
         // normalisation divides the common factor out.
         if (!started || __any(lt > kSumCap)) {
+            const float m_seed = started ? m_run : 0.f;   // what the scores are relative to
             float mt = fmaxf(sacc[0][0], sacc[0][1]);
 #pragma unroll
             for (int rr = 2; rr < 16; rr += 2) mt = fmaxf(mt, fmaxf(sacc[0][rr], sacc[0][rr + 1]));
 #pragma unroll
             for (int rr = 0; rr < 16; rr += 2) mt = fmaxf(mt, fmaxf(sacc[1][rr], sacc[1][rr + 1]));
-            mt *= scale_log2;
-            const float m_new = fmaxf(m_run, fmaxf(mt, xor32(mt)));
+            const float m_new = fmaxf(m_run, m_seed + fmaxf(mt, xor32(mt)));
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
             m_run = m_new;
             l_run *= alpha;
 #pragma unroll
             for (int eb = 0; eb < C::EB; ++eb) oacc[eb] *= alpha;
-            lt = weights();
+            lt = weights(std::true_type{}, m_seed - m_new);
             started = true;
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) negm[rr] = -m_new;
         }
         l_run += lt;
         // O^T += V^T P^T over the four 16-key slabs of the tile
