@@ -74,9 +74,17 @@ __global__ __launch_bounds__(256) void prep_kernel(const bf16* __restrict__ Z,
         }
         --bid;
     }
-    // output-feature tiles fastest: consecutive work-groups share the same
-    // query tokens (L2) while W_Q[s] stays cache-resident
+    // Work-groups are dealt to the 8 XCDs (each with its own L2) in turn, so
+    // tile number n runs on XCD n % 8.  Remap so that tiles adjacent in
+    // (slot, candidate tile, output-feature tile) order - which read the same
+    // query tokens - run on the same XCD: logical tile = x * per + y for
+    // physical n = y * 8 + x (the last partial round keeps its order).
     const int per_slot = tiles_e * tiles_c;
+    {
+        const int nb = q * per_slot;
+        const int per = nb / 8;
+        if (bid < 8 * per) bid = (bid % 8) * per + bid / 8;
+    }
     const int s = bid / per_slot;
     const int rem = bid - s * per_slot;
     const int tc = rem / tiles_e, te = rem - tc * tiles_e;
