@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="run only a plain device copy of this many MiB (counter calibration)")
+    p.add_argument("--ingest-counters", metavar="DIR",
+                   help="write profiles/counters_*_<config>.json from rocprofv3 --pmc runs in DIR "
+                        "(fetch/, write/, calib_fetch/, calib_write/)")
     p.add_argument("--micro", action="store_true",
                    help="run only the unit micro-benchmarks (achievable MFMA/exp/VALU/LDS/HBM)")
     return p.parse_args()
@@ -95,17 +98,57 @@ def kernel_sha(kernel):
     return h.hexdigest()[:16]
 
 
+KERNEL_NAMES = {"attention": "attn_bf16_kernel", "projection": "prep_kernel"}
+
+
 def traffic_for(kernel, config):
     """HBM bytes per launch of a kernel from committed rocprofv3 counter runs
-    (FETCH_SIZE and WRITE_SIZE, scaled by a copy-kernel calibration), or None
-    when absent or taken on a different kernel source."""
+    (FETCH_SIZE and WRITE_SIZE, each scaled by what the same counter reads for
+    a plain copy of known size), or None when absent or taken on a different
+    kernel source."""
     path = os.path.join(ROOT, "profiles", "counters_%s_%s.json" % (kernel, config))
     if not os.path.exists(path):
         return None
     c = json.load(open(path))
     if c.get("kernel_source_sha") != kernel_sha(kernel):
         return None
-    return (c["fetch_kib"] + c["write_kib"]) * 1024.0 * c["copy_calibration"]
+    return round(c["fetch_kib"] * 1024.0 * c["fetch_calibration"] +
+                 c["write_kib"] * 1024.0 * c["write_calibration"], 1)
+
+
+def _counter_means(csv_path, name_part, counter):
+    """Average per dispatch of one counter over the dispatches of kernels
+    whose name contains name_part (rocprofv3 --pmc CSV)."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(csv_path)):
+        if name_part in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit("no %s dispatches of %s in %s" % (counter, name_part, csv_path))
+    return sum(per.values()) / len(per), len(per)
+
+
+def ingest_counters(d, config, calib_mib):
+    """Turn four rocprofv3 --pmc runs under directory d (fetch/, write/:
+    this benchmark; calib_fetch/, calib_write/: --calib-copy-mib) into
+    profiles/counters_<kernel>_<config>.json for both kernels."""
+    csvf = lambda sub: os.path.join(d, sub, "run_counter_collection.csv")
+    known = calib_mib * (1 << 20)
+    cf, _ = _counter_means(csvf("calib_fetch"), "copy_kernel", "FETCH_SIZE")
+    cw, _ = _counter_means(csvf("calib_write"), "copy_kernel", "WRITE_SIZE")
+    for kernel, part in KERNEL_NAMES.items():
+        f, nf = _counter_means(csvf("fetch"), part, "FETCH_SIZE")
+        w, nw = _counter_means(csvf("write"), part, "WRITE_SIZE")
+        out = {"kernel": part, "workload": config, "fetch_kib": round(f, 1),
+               "write_kib": round(w, 1), "dispatches": [nf, nw],
+               "fetch_calibration": round(known / (cf * 1024.0), 4),
+               "write_calibration": round(known / (cw * 1024.0), 4),
+               "calibration_copy_bytes": known,
+               "kernel_source_sha": kernel_sha(kernel)}
+        path = os.path.join(ROOT, "profiles", "counters_%s_%s.json" % (kernel, config))
+        json.dump(out, open(path, "w"), indent=1)
+        print(path, json.dumps(out))
 
 
 def roofline(flops, nbytes, ms, dtype):
@@ -158,15 +201,24 @@ def cpu_baseline(wl, target_s):
 
 
 def calib_copy(mib):
+    """A plain device copy of mib MiB (the library's copy_kernel, 16-byte
+    loads and stores): the known-size reference for the HBM byte counters."""
+    import ctypes
     import torch
-    n = mib * (1 << 20) // 4
-    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    from shared_history_candidate_amd import xattn as X
+    L = X.lib()
+    L.xattn_micro_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                   ctypes.c_int, ctypes.c_void_p]
+    L.xattn_micro_copy.restype = ctypes.c_float
+    n = mib * (1 << 20)
+    a = torch.ones(n // 4, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
-    for _ in range(5):
-        b.copy_(a)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ms = L.xattn_micro_copy(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(b.data_ptr()), n, 5, st)
     torch.cuda.synchronize()
-    print(json.dumps({"calib_copy_bytes_read": n * 4, "calib_copy_bytes_written": n * 4,
-                      "launches": 5}))
+    print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n,
+                      "launches": 6, "ms_per_copy": round(ms, 4),
+                      "copy_gbs": round(2.0 * n / (ms * 1e-3) / 1e9, 1)}))
 
 
 def main():
@@ -176,6 +228,9 @@ def main():
               "(requests shard across GPUs with no exchange). Use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
+    if args.ingest_counters:
+        ingest_counters(args.ingest_counters, args.config, args.calib_copy_mib or 256)
+        return
     if args.calib_copy_mib:
         calib_copy(args.calib_copy_mib)
         return
@@ -214,20 +269,23 @@ def main():
     ms_per_step = t0.elapsed_time(t1) / args.steps
     print("bench: %d steps, %.4f ms/step" % (args.steps, ms_per_step), file=sys.stderr, flush=True)
 
-    # Each kernel alone, one HIP event pair per launch on its stream: the
-    # projection (into a query buffer) and the attention kernel over those
-    # queries and the plan the last step left in the workspace.
+    # Each kernel alone: K back-to-back launches between one HIP event pair on
+    # the launch stream, averaged (an event pair per launch would add its own
+    # ~1-2 us to every launch).  The projection writes a query buffer and the
+    # attention kernel reads it with the plan the last step left in the
+    # workspace.
     Qbuf = torch.empty_like(O)
 
     def per_launch_ms(fn):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-        for a, b in evs:
-            a.record(stream)
+        fn()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.steps):
             fn()
-            b.record(stream)
+        b.record(stream)
         torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        return a.elapsed_time(b) / args.steps
 
     proj_ms = per_launch_ms(lambda: ctx.project(t["Z"], t["W_Q"], Q=Qbuf, stream=stream))
     attn_ms = per_launch_ms(lambda: ctx.attend_q(Qbuf, t["K"], t["V"], t["cu_kv"], t["cu_cand"],
