@@ -2,9 +2,12 @@
 """Benchmark of shared-history cross-attention on one MI355X.
 
 One step = one xattn_forward call over one batch of synthetic inputs resident
-in HBM: the varlen planner plus the fused TSP-projection + attention kernel.
-Default workload: the ReST-like serving batch (8 requests, history length
-U{512..1024}, d = 256 as 4 heads x 64, 256 candidates x 3 query tokens, bf16).
+in HBM.  For small batches (at most 16 requests, model width at most 256)
+that is a single kernel that plans the batch, projects its queries and runs
+the attention; otherwise it is the projection GEMM (which also runs the
+planner) followed by the attention kernel.  Default workload: the ReST-like
+serving batch (8 requests, history length U{512..1024}, d = 256 as 4 heads x
+64, 256 candidates x 3 query tokens, bf16).
 
 Prints one JSON line with the whole-step throughput (candidate-queries/s),
 the dominant kernel's roofline fraction (its average launch duration measured
@@ -26,8 +29,10 @@ PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 CONFIGS = ("rest", "long", "transx", "ragged", "tiny")
-KERNEL_SOURCES = {"attention": ["shared_history_candidate_amd/csrc/attn_bf16.hip",
-                                "shared_history_candidate_amd/csrc/common.h"],
+_ATTN_SRC = ["shared_history_candidate_amd/csrc/attn_bf16.hip",
+             "shared_history_candidate_amd/csrc/plan_wave.h",
+             "shared_history_candidate_amd/csrc/common.h"]
+KERNEL_SOURCES = {"fused": _ATTN_SRC, "attention": _ATTN_SRC,
                   "projection": ["shared_history_candidate_amd/csrc/gemm_bf16.hip",
                                  "shared_history_candidate_amd/csrc/plan_device.h",
                                  "shared_history_candidate_amd/csrc/common.h"]}
@@ -98,7 +103,14 @@ def kernel_sha(kernel):
     return h.hexdigest()[:16]
 
 
-KERNEL_NAMES = {"attention": "attn_bf16_kernel", "projection": "prep_kernel"}
+# Kernel names (regular expressions over the mangled names) of the three
+# kernels a step can run: the single launch of a small batch (attention kernel
+# that projects its own queries: last template flag 1), or the projection
+# GEMM and the attention kernel over its output (flag 0).
+KERNEL_NAMES = {
+    "fused": r"attn_bf16_kernel(<\d+, \d+, \d+, \w+, true>|ILi\d+ELi\d+ELi\d+ELb[01]ELb1E)",
+    "attention": r"attn_bf16_kernel(<\d+, \d+, \d+, \w+, false>|ILi\d+ELi\d+ELi\d+ELb[01]ELb0E)",
+    "projection": r"prep_kernel"}
 
 
 def traffic_for(kernel, config):
@@ -116,16 +128,17 @@ def traffic_for(kernel, config):
                  c["write_kib"] * 1024.0 * c["write_calibration"], 1)
 
 
-def _counter_means(csv_path, name_part, counter):
+def _counter_means(csv_path, name_re, counter):
     """Average per dispatch of one counter over the dispatches of kernels
-    whose name contains name_part (rocprofv3 --pmc CSV)."""
+    whose name matches name_re (rocprofv3 --pmc CSV), or None if none ran."""
     import csv
+    import re
     per = {}
     for r in csv.DictReader(open(csv_path)):
-        if name_part in r["Kernel_Name"] and r["Counter_Name"] == counter:
+        if re.search(name_re, r["Kernel_Name"]) and r["Counter_Name"] == counter:
             per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
     if not per:
-        raise SystemExit("no %s dispatches of %s in %s" % (counter, name_part, csv_path))
+        return None, 0
     return sum(per.values()) / len(per), len(per)
 
 
@@ -140,6 +153,8 @@ def ingest_counters(d, config, calib_mib):
     for kernel, part in KERNEL_NAMES.items():
         f, nf = _counter_means(csvf("fetch"), part, "FETCH_SIZE")
         w, nw = _counter_means(csvf("write"), part, "WRITE_SIZE")
+        if f is None or w is None:
+            continue   # this workload does not run that kernel
         out = {"kernel": part, "workload": config, "fetch_kib": round(f, 1),
                "write_kib": round(w, 1), "dispatches": [nf, nw],
                "fetch_calibration": round(known / (cf * 1024.0), 4),
@@ -287,26 +302,35 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / args.steps
 
-    proj_ms = per_launch_ms(lambda: ctx.project(t["Z"], t["W_Q"], Q=Qbuf, stream=stream))
-    attn_ms = per_launch_ms(lambda: ctx.attend_q(Qbuf, t["K"], t["V"], t["cu_kv"], t["cu_cand"],
-                                                 wl.heads, ws, O=O, stream=stream))
-    print("bench: projection %.4f ms, attention %.4f ms per launch" % (proj_ms, attn_ms),
-          file=sys.stderr, flush=True)
-    kernels = {
-        "attention": dict(roofline(wl.flops_attention(), wl.bytes_attention(), attn_ms, wl.dtype),
-                          kernel_ms=round(attn_ms, 5), algorithmic_flops=wl.flops_attention(),
-                          algorithmic_bytes=wl.bytes_attention(),
-                          traffic=traffic_for("attention", args.config)),
-        "projection": dict(roofline(wl.flops_projection(), wl.bytes_projection(), proj_ms,
-                                    wl.dtype),
-                           kernel_ms=round(proj_ms, 5), algorithmic_flops=wl.flops_projection(),
-                           algorithmic_bytes=wl.bytes_projection(),
-                           traffic=traffic_for("projection", args.config)),
-    }
-    dominant = max(kernels, key=lambda k: kernels[k]["kernel_ms"])
-    roof = dict(kernels[dominant], kernel=dominant)
-    other = [k for k in kernels if k != dominant][0]
-    roof["other_kernel"] = dict(kernels[other], kernel=other)
+    launches = ctx.forward_launches(wl.R, wl.total_cand, wl.total_kv, wl.heads)
+
+    def entry(kernel, flops, nbytes, ms):
+        return dict(roofline(flops, nbytes, ms, wl.dtype), kernel_ms=round(ms, 5),
+                    algorithmic_flops=flops, algorithmic_bytes=nbytes,
+                    traffic=traffic_for(kernel, args.config), kernel=kernel)
+
+    if launches == 1:
+        # The step is one kernel: the attention kernel plans the batch and
+        # projects its own queries.  Its work is the whole path's.
+        fused_ms = per_launch_ms(step)
+        print("bench: single launch %.4f ms" % fused_ms, file=sys.stderr, flush=True)
+        roof = entry("fused", wl.flops(), wl.bytes(), fused_ms)
+        roof["other_kernel"] = None
+    else:
+        proj_ms = per_launch_ms(lambda: ctx.project(t["Z"], t["W_Q"], Q=Qbuf, stream=stream))
+        attn_ms = per_launch_ms(lambda: ctx.attend_q(Qbuf, t["K"], t["V"], t["cu_kv"],
+                                                     t["cu_cand"], wl.heads, ws, O=O,
+                                                     stream=stream))
+        print("bench: projection %.4f ms, attention %.4f ms per launch" % (proj_ms, attn_ms),
+              file=sys.stderr, flush=True)
+        kernels = {
+            "attention": entry("attention", wl.flops_attention(), wl.bytes_attention(), attn_ms),
+            "projection": entry("projection", wl.flops_projection(), wl.bytes_projection(),
+                                proj_ms),
+        }
+        dominant = max(kernels, key=lambda k: kernels[k]["kernel_ms"])
+        roof = dict(kernels[dominant])
+        roof["other_kernel"] = kernels["projection" if dominant == "attention" else "attention"]
 
     cpu = None
     if not args.no_cpu_baseline:

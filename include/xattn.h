@@ -48,9 +48,11 @@
  *     A request with N_r = 0 produces no rows.  No mask: every query row
  *     attends to all L_r rows of its request.
  *   - Precision: XATTN_BF16 multiplies bf16 operands into fp32 accumulators
- *     on the matrix cores; Q and the softmax weights are rounded to bf16 for
- *     the second and third products; O is rounded to bf16 (nearest-even).
- *     XATTN_FP32 computes in fp32 throughout.
+ *     on the matrix cores; Q is rounded to bf16 after the projection and once
+ *     more after scaling by log2(e)/sqrt(d_h) (the softmax scale folded into
+ *     the query operands); the softmax weights are rounded to bf16 for the PV
+ *     product; O is rounded to bf16 (nearest-even).  XATTN_FP32 computes in
+ *     fp32 throughout.
  *
  * Supported: d_h = d / heads in {32, 64, 128} for bf16 (1..128 for fp32),
  * q in [1, 64], d a multiple of 32 for bf16, R >= 0.
@@ -123,9 +125,12 @@ size_t xattn_workspace_size(const xattn_ctx* ctx, int32_t num_requests,
 
 /* Shared-history cross-attention forward (Eq. (7) attention with Eq. (8)
  * per-slot W_Q; layouts and precision in the header comment).  Enqueues on
- * `stream` the TSP projection (whose launch also runs the varlen planner in
- * one extra work-group) and then the attention kernel, which reads the
- * projected queries and the plan from the workspace.
+ * `stream` either one kernel - bf16 batches of at most 16 requests on a model
+ * of at most 256 features: the attention kernel plans the batch, projects its
+ * own queries and writes the plan into the workspace - or the TSP projection
+ * (whose launch also runs the varlen planner in one extra work-group) and
+ * then the attention kernel, which reads the projected queries and the plan
+ * from the workspace (xattn_forward_launches() tells which).
  * `workspace` is device memory of at least xattn_workspace_size() bytes,
  * owned by the caller; its contents on entry are ignored.
  * Errors: XATTN_EINVAL for NULL pointers / negative counts / heads not
@@ -141,9 +146,10 @@ xattn_status xattn_forward(xattn_ctx* ctx,
                            void* O, void* workspace, size_t workspace_bytes,
                            void* stream);
 
-/* Projection and attention without re-planning: like xattn_forward, but the
- * plan is read from `workspace`, where a previous xattn_plan or xattn_forward
- * call left it for the SAME offsets and shape arguments (a decoder with
+/* Projection and attention without re-planning (one kernel where
+ * xattn_forward would run one): like xattn_forward, but the plan is read
+ * from `workspace`, where a previous xattn_plan or xattn_forward call left it
+ * for the SAME offsets and shape arguments (a decoder with
  * several cross-attention layers over one batch plans once and runs the
  * projection and attention per layer).  Arguments and errors as for
  * xattn_forward.  If the workspace holds the plan of a different batch shape
@@ -196,6 +202,15 @@ xattn_status xattn_plan(xattn_ctx* ctx,
 /* Upper bound on the number of tiles xattn_plan can emit for this shape. */
 int64_t xattn_max_tiles(const xattn_ctx* ctx, int32_t num_requests,
                         int32_t total_cand, int32_t heads);
+
+/* Number of kernel launches xattn_forward enqueues for this batch shape (for
+ * callers that capture or time it): 1 for bf16 batches of at most 16
+ * requests on a model of at most 256 features (the attention kernel plans
+ * the batch and projects its own queries), 2 for other bf16 batches
+ * (projection GEMM with the planner, then attention), 3 in fp32 mode.
+ * Returns 0 for invalid arguments or a batch without query rows. */
+int32_t xattn_forward_launches(const xattn_ctx* ctx, int32_t num_requests,
+                               int32_t total_cand, int32_t total_kv, int32_t heads);
 
 /* TSP query projection alone (Eq. (8) applied to W_Q of Eq. (7)):
  * Q[row] = Z[row] . W_Q[row % q], Q [total_cand][q][d] in the context's

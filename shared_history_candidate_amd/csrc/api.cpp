@@ -47,12 +47,28 @@ struct Variant {
     int rb, ksplit;
 };
 
+// Batches of at most kInPlanMaxRequests requests on a model of at most
+// kAttnProjMaxD features run as one launch: the attention kernel plans the
+// batch and projects its own queries.  Larger ones run the projection GEMM
+// (with the planner) and then the attention kernel over its output.
+bool fused_shape(const xattn_config& c, int R) {
+    return c.d_model <= xattn::kAttnProjMaxD && R <= xattn::kInPlanMaxRequests;
+}
+
+// LDS bytes of a variant as this batch shape launches it.  The choice depends
+// only on the batch shape, never on the entry point: a plan built by one call
+// is read by the next, and its tile size is the variant's.
+int variant_smem(const xattn_config& c, int R, int dh, int rb, int ks) {
+    const bool sep = c.kv_mode == XATTN_KV_SEPARATE;
+    const int proj = fused_shape(c, R) ? xattn::attn_bf16_variant_smem(dh, rb, ks, sep, true) : 0;
+    return proj > 0 ? proj : xattn::attn_bf16_variant_smem(dh, rb, ks, sep, false);
+}
+
 Variant choose_variant(const xattn_config& c, int R, int total_cand, int total_kv, int heads) {
     const int dh = c.d_model / heads;
-    const bool sep = c.kv_mode == XATTN_KV_SEPARATE;
     if (const char* env = getenv("XATTN_VARIANT")) {
         int rb = 0, ks = 0;
-        if (sscanf(env, "%d,%d", &rb, &ks) == 2 && xattn::attn_bf16_variant_smem(dh, rb, ks, sep))
+        if (sscanf(env, "%d,%d", &rb, &ks) == 2 && variant_smem(c, R, dh, rb, ks) > 0)
             return {rb, ks};
     }
     const double rows = (double)total_cand * c.n_slots * heads;   // query rows x heads
@@ -64,13 +80,13 @@ Variant choose_variant(const xattn_config& c, int R, int total_cand, int total_k
     // compute unit, else the first such fallback, else the smallest built one.
     const Variant order[] = {v, {2, 2}, {4, 1}, {1, 4}, {2, 1}};
     for (const Variant& o : order) {
-        const int sm = xattn::attn_bf16_variant_smem(dh, o.rb, o.ksplit, sep);
+        const int sm = variant_smem(c, R, dh, o.rb, o.ksplit);
         if (sm > 0 && sm <= 81920) return o;
     }
     Variant best{2, 1};
     int best_sm = 1 << 30;
     for (const Variant& o : order) {
-        const int sm = xattn::attn_bf16_variant_smem(dh, o.rb, o.ksplit, sep);
+        const int sm = variant_smem(c, R, dh, o.rb, o.ksplit);
         if (sm > 0 && sm < best_sm) best = o, best_sm = sm;
     }
     return best;
@@ -175,6 +191,19 @@ int64_t xattn_max_tiles(const xattn_ctx* ctx, int32_t R, int32_t total_cand, int
     return max_tiles_any(ctx->cfg, R, total_cand);
 }
 
+int32_t xattn_forward_launches(const xattn_ctx* ctx, int32_t R, int32_t total_cand,
+                               int32_t total_kv, int32_t heads) {
+    if (!ctx || R <= 0 || total_cand <= 0 || total_kv < 0 || heads < 1 ||
+        ctx->cfg.d_model % heads != 0)
+        return 0;
+    const xattn_config& c = ctx->cfg;
+    if (c.dtype != XATTN_BF16) return 3;
+    const Variant var = choose_variant(c, R, total_cand, total_kv, heads);
+    return fused_shape(c, R) && xattn::attn_bf16_variant_smem(c.d_model / heads, var.rb, var.ksplit,
+                                                              c.kv_mode == XATTN_KV_SEPARATE, true) > 0
+               ? 1 : 2;
+}
+
 size_t xattn_workspace_size(const xattn_ctx* ctx, int32_t R, int32_t total_cand, int32_t heads) {
     if (!ctx || R < 0 || total_cand < 0 || heads < 1) return 0;
     return workspace_bytes(ctx->cfg, R, total_cand);
@@ -252,16 +281,43 @@ xattn_status run_forward(Mode mode, xattn_ctx* ctx, const void* Z, const void* W
     if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
     hipError_t e = hipSuccess;
     if (c.dtype == XATTN_BF16) {
-        if (mode != Mode::kAttendQ) {
+        xattn::AttnArgs a{};
+        a.K = K;
+        a.V = c.kv_mode == XATTN_KV_SEPARATE ? V : nullptr;
+        a.ws = workspace;
+        a.cu_kv = cu_kv;
+        a.cu_cand = cu_cand;
+        a.max_tiles = max_tiles;
+        a.R = R;
+        a.total_cand = total_cand;
+        a.total_kv = total_kv;
+        a.q = c.n_slots;
+        a.d = c.d_model;
+        a.heads = heads;
+        a.O = O;
+        const bool fused_proj =
+            fused_shape(c, R) &&
+            xattn::attn_bf16_variant_smem(c.d_model / heads, var.rb, var.ksplit,
+                                          c.kv_mode == XATTN_KV_SEPARATE, true) > 0;
+        if (mode == Mode::kAttendQ) {
+            a.Qp = Qin;   // caller-projected queries, stored plan
+        } else if (fused_proj) {
+            // one launch: the attention kernel projects its own queries, and
+            // plans a small batch itself (forward) or reads the stored plan
+            a.Z = Z;
+            a.Wq = W_Q;
+            a.inplan = mode == Mode::kForward;
+        } else {
+            // projection GEMM into the workspace (its launch also runs the
+            // planner for a forward pass), then attention over those queries
             e = xattn::launch_project_plan_bf16(Z, W_Q, total_cand, c.n_slots, c.d_model, qws, cu_kv,
                                                 cu_cand, R, tm, total_kv,
                                                 mode == Mode::kForward ? workspace : nullptr,
                                                 max_tiles, s);
             if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
+            a.Qp = qws;
         }
-        e = xattn::launch_attn_bf16(Qp, K, c.kv_mode == XATTN_KV_SEPARATE ? V : nullptr,
-                                    workspace, max_tiles, c.n_slots, c.d_model, heads, var.rb,
-                                    var.ksplit, O, s);
+        e = xattn::launch_attn_bf16(a, var.rb, var.ksplit, s);
     } else {
         if (mode == Mode::kForward) {
             e = xattn::launch_plan(cu_kv, cu_cand, R, c.n_slots, tm, total_cand, total_kv, workspace,

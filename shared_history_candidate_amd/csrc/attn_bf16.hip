@@ -37,6 +37,7 @@
 
 #include "common.h"
 #include "internal.h"
+#include "plan_wave.h"
 
 namespace xattn {
 
@@ -49,15 +50,12 @@ namespace {
 constexpr int BN = 64;               // memory rows per tile
 constexpr float kSumCap = 4096.0f;   // largest accepted per-lane weight sum of one tile
 
-constexpr int pow2floor(int x) {
-    int p = 1;
-    while (p * 2 <= x) p *= 2;
-    return p;
-}
-
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-template <int DH, int RB, int KSPLIT, bool SEP>
+// Widest model the fused projection stages in LDS.
+constexpr int kProjMaxD = kAttnProjMaxD;
+
+template <int DH, int RB, int KSPLIT, bool SEP, bool PROJ>
 struct Cfg {
     static constexpr int NW = RB * KSPLIT;
     static constexpr int NT = 64 * NW;
@@ -73,7 +71,23 @@ struct Cfg {
     static constexpr int TILE = BN * LDK;     // elements per plane per buffer
     static constexpr int KV_BYTES = KSPLIT * 2 * PLANES * TILE * 2;
     static constexpr int CMB_BYTES = KSPLIT > 1 ? RB * (KSPLIT - 1) * 64 * (EB * 16 + 2) * 4 : 0;
-    static constexpr int SMEM = KV_BYTES > CMB_BYTES ? KV_BYTES : CMB_BYTES;
+    // Fused projection (PROJ): the tile's query tokens (32*RB rows) and head
+    // h's rows of W_Q[s] (DH rows) are staged in LDS (up to kProjMaxD wide,
+    // aliasing the memory buffers, which are filled only afterwards); the
+    // projected Q_h tile goes to its own LDS region behind both.
+    static constexpr int LDS_K = kProjMaxD + 8;       // staging pitch (16-byte rows)
+    static constexpr int STG_BYTES = PROJ ? (32 * RB + DH) * LDS_K * 2 : 0;
+    static constexpr int ZCPT = (32 * RB * (kProjMaxD / 8) + NT - 1) / NT;   // staging chunks per thread
+    static constexpr int WCPT = (DH * (kProjMaxD / 8) + NT - 1) / NT;
+    static constexpr int LDQ = DH + 8;
+    static constexpr int QT_OFF = KV_BYTES > STG_BYTES ? KV_BYTES : STG_BYTES;
+    static constexpr int QT_BYTES = PROJ ? 32 * RB * LDQ * 2 : 0;
+    static constexpr int PB = EB * RB;                 // 32x32 blocks of Q_h^T
+    static constexpr int PB_PER_WAVE = (PB + NW - 1) / NW;
+    static constexpr int SMEM_MAIN = PROJ ? QT_OFF + QT_BYTES : KV_BYTES;
+    static constexpr int SMEM = SMEM_MAIN > CMB_BYTES ? SMEM_MAIN : CMB_BYTES;
+    // the staging registers must leave room for the rest of the prologue
+    static constexpr bool BUILT = !PROJ || ZCPT + WCPT <= 24;
     static constexpr int KV_CHUNKS = BN * DH / 8;                 // 16-byte chunks per plane
     static constexpr int KV_CPT = KV_CHUNKS / (64 * RB);
     static_assert(KV_CHUNKS % (64 * RB) == 0, "memory tile must split evenly over a split group");
@@ -83,24 +97,44 @@ struct Cfg {
     static constexpr int P = STAGE_REGS >= 8 ? 1 : (8 / STAGE_REGS >= 4 ? 4 : 8 / STAGE_REGS);
 };
 
-template <int DH, int RB, int KSPLIT, bool SEP>
-__global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(
-    const bf16* __restrict__ Qp, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const int* __restrict__ ws, int q, int d, int heads, float scale_log2,
-    bf16* __restrict__ O) {
-    using C = Cfg<DH, RB, KSPLIT, SEP>;
+template <int DH, int RB, int KSPLIT, bool SEP, bool PROJ>
+__global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(AttnArgs a) {
+    using C = Cfg<DH, RB, KSPLIT, SEP, PROJ>;
     constexpr int P = C::P;
     __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
+    const int q = a.q, d = a.d, heads = a.heads;
+    const float scale_log2 = a.scale_log2;
+    const bf16* __restrict__ K = static_cast<const bf16*>(a.K);
+    const bf16* __restrict__ V = static_cast<const bf16*>(a.V);
+    bf16* __restrict__ O = static_cast<bf16*>(a.O);
+    int* __restrict__ ws = static_cast<int*>(a.ws);
 
-    const int n_tiles = ws[kPlanNTiles];
     const int tile = blockIdx.x / heads;
     const int h = blockIdx.x - tile * heads;
-    const int4 item = reinterpret_cast<const int4*>(
-        reinterpret_cast<const char*>(ws) + kPlanHeaderBytes)[tile];
-    // A plan built for another tile size (another batch shape) is not ours.
-    if (tile >= n_tiles || ws[kPlanTileM] != 32 * RB) return;
-    const int kv0 = item.x, L = item.y, c0 = item.z;
-    const int nc = item.w & kItemNcMask, s = item.w >> 16;
+    int4 item;
+    if (a.inplan) {
+        // Small batch: every wave plans it (one lane per request) and takes
+        // its work-group's item; the first wave also publishes the plan in
+        // the workspace (for later calls that reuse it) or the validation
+        // failure, in which case no work-group computes anything.
+        const WavePlan wp = wave_plan(a.cu_kv, a.cu_cand, a.R, q, 32 * RB, a.total_cand,
+                                      a.total_kv);
+        if (blockIdx.x == 0 && threadIdx.x < 64) wave_plan_publish(wp, a.R, q, 32 * RB, ws, a.max_tiles);
+        if (wp.err || tile >= wp.total) return;
+        item = wave_plan_item(wp, tile, q, 32 * RB);
+    } else {
+        const int n_tiles = ws[kPlanNTiles];
+        item = reinterpret_cast<const int4*>(reinterpret_cast<const char*>(ws) +
+                                             kPlanHeaderBytes)[tile];
+        // A plan built for another tile size (another batch shape) is not ours.
+        if (tile >= n_tiles || ws[kPlanTileM] != 32 * RB) return;
+    }
+    // the item is the same in every lane: keep it in scalar registers
+    const int kv0 = __builtin_amdgcn_readfirstlane(item.x);
+    const int L = __builtin_amdgcn_readfirstlane(item.y);
+    const int c0 = __builtin_amdgcn_readfirstlane(item.z);
+    const int iw = __builtin_amdgcn_readfirstlane(item.w);
+    const int nc = iw & kItemNcMask, s = iw >> 16;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -176,15 +210,92 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(
     // k-step k, half g: features 16k + 8g .. 16k + 8g + 7 of the lane's query
     // row (columns past the tile re-read its last row; their output is dropped)
     bf16x8 qb[C::KST];
-    {
-        const bf16* qrow = Qp + ((size_t)(qvalid ? cand : c0 + nc - 1) * q + s) * d + h * DH;
+    uint4 zst[PROJ ? C::ZCPT : 1], wst[PROJ ? C::WCPT : 1];
+    const int cpr = d >> 3;   // 16-byte chunks per model row
+    if constexpr (PROJ) {
+        // Operands of the TSP projection (ReST reading note, s.3.3.2 Eq. (8)):
+        // this tile's query tokens (candidates c0.., slot s; rows past nc are
+        // outside the descriptor and read as zeros) and head h's rows of
+        // W_Q[s], in coalesced 16-byte chunks.
+        const size_t zbytes = ((size_t)(nc - 1) * q + 1) * d * 2;
+        const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(static_cast<const bf16*>(a.Z) + ((size_t)c0 * q + s) * d), (short)0,
+            zbytes > 0xFFFFFFF0u ? 0xFFFFFFF0u : (uint32_t)zbytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(static_cast<const bf16*>(a.Wq) + ((size_t)s * d + h * DH) * d), (short)0,
+            (uint32_t)(DH * d * 2), 0x00020000);
+#pragma unroll
+        for (int u = 0; u < C::ZCPT; ++u) {
+            const int idx = tid + u * C::NT, row = idx / cpr, col = idx - row * cpr;
+            zst[u] = idx < 32 * RB * cpr
+                         ? __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                         rz, (row * q * d + col * 8) * 2, 0, 0))
+                         : uint4{};
+        }
+#pragma unroll
+        for (int u = 0; u < C::WCPT; ++u) {
+            const int idx = tid + u * C::NT, row = idx / cpr, col = idx - row * cpr;
+            wst[u] = idx < DH * cpr
+                         ? __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                         rw, (row * d + col * 8) * 2, 0, 0))
+                         : uint4{};
+        }
+    } else {
+        const bf16* qrow = static_cast<const bf16*>(a.Qp) +
+                           ((size_t)(qvalid ? cand : c0 + nc - 1) * q + s) * d + h * DH;
 #pragma unroll
         for (int k = 0; k < C::KST; ++k)
             qb[k] = *reinterpret_cast<const bf16x8*>(qrow + 16 * k + 8 * g);
     }
-    // The first P tiles of this split are requested right behind the queries.
+    // The first P tiles of this split are requested right behind.
 #pragma unroll
     for (int j = 0; j < P; ++j) gload(ksg + j * KSPLIT, kreg[j], vreg[j]);
+    if constexpr (PROJ) {
+        bf16* zs = reinterpret_cast<bf16*>(smem);
+        bf16* wsh = zs + 32 * RB * C::LDS_K;
+#pragma unroll
+        for (int u = 0; u < C::ZCPT; ++u) {
+            const int idx = tid + u * C::NT, row = idx / cpr, col = idx - row * cpr;
+            if (idx < 32 * RB * cpr) *reinterpret_cast<uint4*>(zs + row * C::LDS_K + col * 8) = zst[u];
+        }
+#pragma unroll
+        for (int u = 0; u < C::WCPT; ++u) {
+            const int idx = tid + u * C::NT, row = idx / cpr, col = idx - row * cpr;
+            if (idx < DH * cpr) *reinterpret_cast<uint4*>(wsh + row * C::LDS_K + col * 8) = wst[u];
+        }
+        __syncthreads();
+        // Q_h^T block (e, r) = W rows 32e.. x Z rows 32r..: fp32 over the
+        // whole model width, rounded once to bf16 into the Q tile.
+        bf16* qt = reinterpret_cast<bf16*>(smem + C::QT_OFF);
+        const int kst = d >> 4;
+#pragma unroll
+        for (int u = 0; u < C::PB_PER_WAVE; ++u) {
+            const int b = w + u * C::NW;
+            if (b < C::PB) {
+                const int e = b % C::EB, r = b / C::EB;
+                const bf16* ap = wsh + (32 * e + l32) * C::LDS_K + 8 * g;
+                const bf16* bp = zs + (32 * r + l32) * C::LDS_K + 8 * g;
+                f32x16 acc = f32x16{};
+                for (int k = 0; k < kst; ++k)
+                    acc = mfma32(*reinterpret_cast<const bf16x8*>(ap + 16 * k),
+                                 *reinterpret_cast<const bf16x8*>(bp + 16 * k), acc);
+                // acc reg 4*j4 + t: feature 32e + 8*j4 + 4g + t of candidate row 32r + l32
+                bf16* qrow = qt + (32 * r + l32) * C::LDQ + 32 * e + 4 * g;
+#pragma unroll
+                for (int j4 = 0; j4 < 4; ++j4) {
+                    bf16x4 v;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) v[t] = (bf16)acc[4 * j4 + t];
+                    *reinterpret_cast<bf16x4*>(qrow + 8 * j4) = v;
+                }
+            }
+        }
+        __syncthreads();
+        const bf16* qrow = qt + (rb * 32 + l32) * C::LDQ;
+#pragma unroll
+        for (int k = 0; k < C::KST; ++k)
+            qb[k] = *reinterpret_cast<const bf16x8*>(qrow + 16 * k + 8 * g);
+    }
     // Fold log2(e)/sqrt(d_h) into the query operands (one more bf16 rounding
     // of Q; the scores then come out of the products in exp2 units).  This
     // also consumes the query registers before the loop: the queries are then
@@ -401,53 +512,48 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(
     }
 }
 
-// Variants whose LDS footprint exceeds what one work-group may hold are not
-// built; the host prefers variants that leave room for two work-groups per
-// compute unit (attn_bf16_variant_smem).
+// Variants whose LDS footprint exceeds what one work-group may hold (or whose
+// projection staging would need too many registers) are not built; the host
+// prefers variants that leave room for two work-groups per compute unit
+// (attn_bf16_variant_smem).
 constexpr int kMaxSmem = 163840;
 
-template <int DH, int RB, int KSPLIT, bool SEP>
-constexpr bool fits() {
-    return Cfg<DH, RB, KSPLIT, SEP>::SMEM <= kMaxSmem;
+template <int DH, int RB, int KSPLIT, bool SEP, bool PROJ>
+constexpr bool built() {
+    using C = Cfg<DH, RB, KSPLIT, SEP, PROJ>;
+    return C::SMEM <= kMaxSmem && C::BUILT;
 }
 
-template <int DH, int RB, int KSPLIT, bool SEP>
-hipError_t launch_one(const void* Qp, const void* K, const void* V,
-                      const void* ws, int64_t max_tiles, int q, int d,
-                      int heads, void* O, hipStream_t stream) {
-    if constexpr (!fits<DH, RB, KSPLIT, SEP>()) {
+template <int DH, int RB, int KSPLIT, bool SEP, bool PROJ>
+hipError_t launch_one(const AttnArgs& a, hipStream_t stream) {
+    if constexpr (!built<DH, RB, KSPLIT, SEP, PROJ>()) {
         return hipErrorInvalidValue;
     } else {
-    const float scale_log2 = 1.4426950408889634f / sqrtf((float)DH);
-    const int64_t blocks = max_tiles * heads;
-    if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL((attn_bf16_kernel<DH, RB, KSPLIT, SEP>), dim3((unsigned)blocks),
-                       dim3(64 * RB * KSPLIT), 0, stream, static_cast<const bf16*>(Qp),
-                       static_cast<const bf16*>(K),
-                       static_cast<const bf16*>(V), static_cast<const int*>(ws), q, d,
-                       heads, scale_log2, static_cast<bf16*>(O));
-    return hipGetLastError();
+        if (PROJ && a.d > kProjMaxD) return hipErrorInvalidValue;
+        AttnArgs k = a;
+        k.scale_log2 = 1.4426950408889634f / sqrtf((float)DH);
+        const int64_t blocks = a.max_tiles * a.heads;
+        if (blocks <= 0) return hipSuccess;
+        hipLaunchKernelGGL((attn_bf16_kernel<DH, RB, KSPLIT, SEP, PROJ>), dim3((unsigned)blocks),
+                           dim3(64 * RB * KSPLIT), 0, stream, k);
+        return hipGetLastError();
     }
 }
 
 template <int DH, int RB, int KSPLIT>
-hipError_t launch_sep(const void* Qp, const void* K, const void* V,
-                      const void* ws, int64_t max_tiles, int q, int d,
-                      int heads, void* O, hipStream_t stream) {
-    if (V)
-        return launch_one<DH, RB, KSPLIT, true>(Qp, K, V, ws, max_tiles, q, d, heads, O,
-                                                stream);
-    return launch_one<DH, RB, KSPLIT, false>(Qp, K, V, ws, max_tiles, q, d, heads, O,
-                                             stream);
+hipError_t launch_mode(const AttnArgs& a, hipStream_t stream) {
+    const bool sep = a.V != nullptr, proj = a.Z != nullptr;
+    if (sep)
+        return proj ? launch_one<DH, RB, KSPLIT, true, true>(a, stream)
+                    : launch_one<DH, RB, KSPLIT, true, false>(a, stream);
+    return proj ? launch_one<DH, RB, KSPLIT, false, true>(a, stream)
+                : launch_one<DH, RB, KSPLIT, false, false>(a, stream);
 }
 
 template <int DH>
-hipError_t launch_dh(const void* Qp, const void* K, const void* V,
-                     const void* ws, int64_t max_tiles, int q, int d,
-                     int heads, int rb, int ksplit, void* O, hipStream_t stream) {
-#define XATTN_CASE(R_, S_)                                                                     \
-    if (rb == R_ && ksplit == S_)                                                              \
-        return launch_sep<DH, R_, S_>(Qp, K, V, ws, max_tiles, q, d, heads, O, stream);
+hipError_t launch_dh(const AttnArgs& a, int rb, int ksplit, hipStream_t stream) {
+#define XATTN_CASE(R_, S_) \
+    if (rb == R_ && ksplit == S_) return launch_mode<DH, R_, S_>(a, stream);
     XATTN_CASE(1, 4)
     XATTN_CASE(2, 2)
     XATTN_CASE(4, 1)
@@ -456,16 +562,23 @@ hipError_t launch_dh(const void* Qp, const void* K, const void* V,
     return hipErrorInvalidValue;
 }
 
-template <int DH, int RB, int KSPLIT, bool SEP>
+template <int DH, int RB, int KSPLIT, bool SEP, bool PROJ>
 constexpr int smem_if_built() {
-    return fits<DH, RB, KSPLIT, SEP>() ? Cfg<DH, RB, KSPLIT, SEP>::SMEM : 0;
+    return built<DH, RB, KSPLIT, SEP, PROJ>() ? Cfg<DH, RB, KSPLIT, SEP, PROJ>::SMEM : 0;
+}
+
+template <int DH, int RB, int KSPLIT>
+int smem_of(bool sep, bool proj) {
+    if (sep) return proj ? smem_if_built<DH, RB, KSPLIT, true, true>()
+                         : smem_if_built<DH, RB, KSPLIT, true, false>();
+    return proj ? smem_if_built<DH, RB, KSPLIT, false, true>()
+                : smem_if_built<DH, RB, KSPLIT, false, false>();
 }
 
 template <int DH>
-int variant_smem(int rb, int ksplit, bool sep) {
-#define XATTN_FIT(R_, S_)                                                                      \
-    if (rb == R_ && ksplit == S_)                                                              \
-        return sep ? smem_if_built<DH, R_, S_, true>() : smem_if_built<DH, R_, S_, false>();
+int variant_smem(int rb, int ksplit, bool sep, bool proj) {
+#define XATTN_FIT(R_, S_) \
+    if (rb == R_ && ksplit == S_) return smem_of<DH, R_, S_>(sep, proj);
     XATTN_FIT(1, 4)
     XATTN_FIT(2, 2)
     XATTN_FIT(4, 1)
@@ -476,30 +589,21 @@ int variant_smem(int rb, int ksplit, bool sep) {
 
 }  // namespace
 
-int attn_bf16_variant_smem(int dh, int rb, int ksplit, bool sep) {
+int attn_bf16_variant_smem(int dh, int rb, int ksplit, bool sep, bool proj) {
     switch (dh) {
-        case 32: return variant_smem<32>(rb, ksplit, sep);
-        case 64: return variant_smem<64>(rb, ksplit, sep);
-        case 128: return variant_smem<128>(rb, ksplit, sep);
+        case 32: return variant_smem<32>(rb, ksplit, sep, proj);
+        case 64: return variant_smem<64>(rb, ksplit, sep, proj);
+        case 128: return variant_smem<128>(rb, ksplit, sep, proj);
         default: return 0;
     }
 }
 
-hipError_t launch_attn_bf16(const void* Qp, const void* K, const void* V,
-                            const void* ws, int64_t max_tiles, int q, int d,
-                            int heads, int rb, int ksplit, void* O, hipStream_t stream) {
-    switch (d / heads) {
-        case 32:
-            return launch_dh<32>(Qp, K, V, ws, max_tiles, q, d, heads, rb, ksplit, O,
-                                 stream);
-        case 64:
-            return launch_dh<64>(Qp, K, V, ws, max_tiles, q, d, heads, rb, ksplit, O,
-                                 stream);
-        case 128:
-            return launch_dh<128>(Qp, K, V, ws, max_tiles, q, d, heads, rb, ksplit, O,
-                                  stream);
-        default:
-            return hipErrorInvalidValue;
+hipError_t launch_attn_bf16(const AttnArgs& a, int rb, int ksplit, hipStream_t stream) {
+    switch (a.d / a.heads) {
+        case 32: return launch_dh<32>(a, rb, ksplit, stream);
+        case 64: return launch_dh<64>(a, rb, ksplit, stream);
+        case 128: return launch_dh<128>(a, rb, ksplit, stream);
+        default: return hipErrorInvalidValue;
     }
 }
 

@@ -10,14 +10,33 @@ hipError_t launch_plan(const int* cu_kv, const int* cu_cand, int R, int q, int t
                        int total_cand, int total_kv, void* ws, int64_t max_tiles, int* cu_q,
                        int* row_req, int* tiles, int* n_tiles, hipStream_t stream);
 
-// bf16 attention over projected queries Qp [total_cand][q][d].  A
-// work-group has rb x ksplit waves: rb query blocks of 32 candidates (tile_m
-// = 32 * rb) and ksplit memory splits merged on chip.  attn_bf16_variant_smem
-// returns the LDS bytes of variant (rb, ksplit) for head width dh and the
-// K/V mode, 0 if not built.
-int attn_bf16_variant_smem(int dh, int rb, int ksplit, bool sep);
-hipError_t launch_attn_bf16(const void* Qp, const void* K, const void* V, const void* ws, int64_t max_tiles, int q, int d, int heads, int rb,
-                            int ksplit, void* O, hipStream_t stream);
+// bf16 attention (attn_bf16.hip).  A work-group has rb x ksplit waves: rb
+// query blocks of 32 candidates (tile_m = 32 * rb) and ksplit memory splits
+// merged on chip.  With Z and Wq set the kernel projects its own queries
+// (d <= 256; otherwise it reads Qp); with inplan set every wave plans the
+// batch itself (R <= kInPlanMaxRequests) instead of reading the plan from
+// ws, and the first one writes the plan there.  V is NULL in
+// projection-free mode.
+struct AttnArgs {
+    const void* Qp;
+    const void* Z;
+    const void* Wq;
+    const void* K;
+    const void* V;
+    void* ws;
+    const int* cu_kv;
+    const int* cu_cand;
+    int64_t max_tiles;
+    int R, total_cand, total_kv, inplan, q, d, heads;
+    float scale_log2;   // set by the launcher
+    void* O;
+};
+// Widest model (d) whose queries the attention kernel projects itself.
+constexpr int kAttnProjMaxD = 256;
+// LDS bytes of variant (rb, ksplit) for head width dh, K/V mode and query
+// source, 0 if not built.
+int attn_bf16_variant_smem(int dh, int rb, int ksplit, bool sep, bool proj);
+hipError_t launch_attn_bf16(const AttnArgs& a, int rb, int ksplit, hipStream_t stream);
 
 // bf16 TSP projection Q = Z W_Q[slot] into Qp; when ws is not NULL the same
 // launch also runs the planner into ws (one extra work-group).

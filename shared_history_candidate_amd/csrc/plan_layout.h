@@ -14,6 +14,7 @@ constexpr int kPlanNTiles = 0;          // header[0]: number of tiles
 constexpr int kPlanError = 1;           // header[1]: validation bitmask (0 = ok)
 constexpr int kPlanTileM = 2;           // header[2]: candidates per tile
 constexpr int kPlanMaxRequests = 4096;  // requests the single-work-group planner holds in LDS
+constexpr int kInPlanMaxRequests = 16;  // batches whose attention waves plan for themselves
 
 constexpr int kItemNcMask = 0xFFFF;     // low half of item.w: nc; high half: slot s
 

@@ -23,7 +23,8 @@ XATTN_BF16, XATTN_FP32 = 0, 1
 XATTN_KV_SHARED, XATTN_KV_SEPARATE = 0, 1
 
 EXPORTED = ("xattn_create", "xattn_destroy", "xattn_workspace_size", "xattn_forward",
-            "xattn_attend", "xattn_attend_q", "xattn_plan", "xattn_max_tiles", "xattn_project", "xattn_device_error",
+            "xattn_attend", "xattn_attend_q", "xattn_plan", "xattn_max_tiles",
+            "xattn_forward_launches", "xattn_project", "xattn_device_error",
             "xattn_last_error")
 
 
@@ -59,6 +60,8 @@ def lib():
         L.xattn_workspace_size.restype = SZ
         L.xattn_max_tiles.argtypes = [P, I32, I32, I32]
         L.xattn_max_tiles.restype = I64
+        L.xattn_forward_launches.argtypes = [P, I32, I32, I32, I32]
+        L.xattn_forward_launches.restype = I32
         L.xattn_forward.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, P, P, SZ, P]
         L.xattn_forward.restype = ctypes.c_int
         L.xattn_attend.argtypes = L.xattn_forward.argtypes
@@ -128,6 +131,12 @@ class XAttn:
 
     def max_tiles(self, num_requests: int, total_cand: int, heads: int) -> int:
         return int(lib().xattn_max_tiles(self._h, num_requests, total_cand, heads))
+
+    def forward_launches(self, num_requests: int, total_cand: int, total_kv: int,
+                         heads: int) -> int:
+        """Kernel launches xattn_forward enqueues for this batch shape."""
+        return int(lib().xattn_forward_launches(self._h, num_requests, total_cand, total_kv,
+                                                heads))
 
     def alloc_workspace(self, num_requests: int, total_cand: int, heads: int) -> torch.Tensor:
         n = self.workspace_size(num_requests, total_cand, heads)

@@ -91,6 +91,26 @@ def test_workspace_size(L):
     L.xattn_destroy(h)
 
 
+def test_forward_launch_count(L):
+    """One launch for small bf16 batches on narrow models, two otherwise,
+    three in fp32 mode; 0 for invalid shapes or no query rows."""
+    st, h = _create(L, 256, 3, X.XATTN_BF16, X.XATTN_KV_SHARED)
+    assert st == 0
+    L.xattn_forward_launches.restype = ctypes.c_int32
+    assert L.xattn_forward_launches(h, 8, 2048, 5482, 4) == 1
+    assert L.xattn_forward_launches(h, 16, 64, 100, 4) == 1
+    assert L.xattn_forward_launches(h, 17, 64, 100, 4) == 2
+    assert L.xattn_forward_launches(h, 8, 0, 100, 4) == 0
+    assert L.xattn_forward_launches(h, 8, 10, 100, 3) == 0
+    L.xattn_destroy(h)
+    st, h = _create(L, 512, 3, X.XATTN_BF16, X.XATTN_KV_SHARED)
+    assert L.xattn_forward_launches(h, 4, 2048, 65536, 8) == 2
+    L.xattn_destroy(h)
+    st, h = _create(L, 64, 3, X.XATTN_FP32, X.XATTN_KV_SHARED)
+    assert L.xattn_forward_launches(h, 1, 4, 64, 2) == 3
+    L.xattn_destroy(h)
+
+
 def _fwd(L, h, Z=FAKE, W=FAKE, K=FAKE, V=None, cu_kv=FAKE, cu_c=FAKE, R=2, tc=10, tkv=20,
          heads=4, O=FAKE, ws=FAKE, wsb=1 << 20):
     return L.xattn_forward(h, Z, W, K, V, cu_kv, cu_c, R, tc, tkv, heads, O, ws, wsb, None)

@@ -235,3 +235,34 @@ def test_attend_and_attend_q_match_forward(name):
     torch.cuda.synchronize()
     assert torch.equal(a, b)
     assert torch.equal(a, c)
+
+
+@pytest.mark.parametrize("R,dh,heads,q,mode", [
+    (1, 64, 4, 3, "shared"), (5, 32, 8, 2, "separate"), (16, 64, 2, 1, "shared"),
+    (16, 128, 2, 3, "separate"), (17, 64, 4, 3, "shared"), (3, 64, 8, 2, "shared"),
+])
+def test_single_launch_and_split_paths_agree(R, dh, heads, q, mode):
+    """Small batches on models up to 256 wide run as one launch (the attention
+    kernel plans the batch and projects its own queries); attend_q runs the
+    attention kernel over queries from the projection GEMM, and attend reads
+    the plan the single launch published.  All three give the same bits, and
+    match the oracle."""
+    require_gpu()
+    rng = np.random.default_rng(R * 100 + dh)
+    wl = W.custom("paths", rng.integers(1, 300, R), rng.integers(0, 90, R), q=q, d=dh * heads,
+                  heads=heads, dtype="bf16", kv_mode=mode, seed=R + dh)
+    if wl.total_cand == 0:
+        pytest.skip("no candidates drawn")
+    ctx = ctx_for(wl)
+    t = X.to_device(wl)
+    ws = ctx.alloc_workspace(wl.R, wl.total_cand, wl.heads)
+    a = ctx.forward(t["Z"], t["W_Q"], t["K"], t["V"], t["cu_kv"], t["cu_cand"], wl.heads,
+                    workspace=ws).clone()
+    b = ctx.attend(t["Z"], t["W_Q"], t["K"], t["V"], t["cu_kv"], t["cu_cand"], wl.heads, ws)
+    Q = ctx.project(t["Z"], t["W_Q"])
+    c = ctx.attend_q(Q, t["K"], t["V"], t["cu_kv"], t["cu_cand"], wl.heads, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert torch.equal(a, c)
+    got = a.float().cpu().numpy().astype(np.float64).reshape(wl.rows, wl.d)
+    assert_close(got, _oracle(wl), "bf16", "paths R=%d dh=%d" % (R, dh))
