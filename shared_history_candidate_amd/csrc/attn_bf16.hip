@@ -43,10 +43,6 @@ namespace xattn {
 
 namespace {
 
-#ifndef XATTN_LDS_PAD
-#define XATTN_LDS_PAD 4
-#endif
-
 constexpr int BN = 64;               // memory rows per tile
 constexpr float kSumCap = 4096.0f;   // largest accepted per-lane weight sum of one tile
 
@@ -61,7 +57,10 @@ struct Cfg {
     static constexpr int NT = 64 * NW;
     static constexpr int EB = DH / 32;        // 32-wide feature blocks
     static constexpr int KST = DH / 16;       // k-steps of the score product
-    static constexpr int PAD = XATTN_LDS_PAD; // row padding of the memory tile (elements)
+    // Row padding of the memory tile (elements).  16-byte rows (8) let the
+    // score operands come in single 16-byte LDS reads; the separate-K/V tiles
+    // measured faster with 8-byte rows (4).
+    static constexpr int PAD = SEP ? 4 : 8;
     static constexpr int LDK = DH + PAD;      // memory tile pitch (elements)
     // one wave per split: a wave reads only the tiles it stored itself, so the
     // memory loop needs no work-group barrier (a wave's LDS operations retire

@@ -17,6 +17,9 @@
 // The same launch can carry the varlen planner in one extra work-group
 // (blockIdx.x == 0): the plan and the projection are independent, and the
 // attention kernel that follows on the stream needs both.
+#include <cstdio>
+#include <cstdlib>
+
 #include "internal.h"
 #include "plan_device.h"
 
@@ -218,6 +221,22 @@ hipError_t launch_project_plan_bf16(const void* Z, const void* Wq, int total_can
     PlanArgs pa{cu_kv, cu_cand, static_cast<int*>(ws), max_tiles, R, tile_m, total_kv,
                 ws != nullptr ? 1 : 0};
     if (total_cand <= 0 && !pa.enabled) return hipSuccess;
+    // XATTN_GEMM="TE,TC,KC" picks a tile shape (tuning).
+    if (const char* env = getenv("XATTN_GEMM")) {
+        int te = 0, tc = 0, kc = 0;
+        if (sscanf(env, "%d,%d,%d", &te, &tc, &kc) == 3) {
+#define XATTN_GEMM_CASE(A_, B_, C_) \
+    if (te == A_ && tc == B_ && kc == C_) return launch_prep<A_, B_, C_>(Z, Wq, total_cand, q, d, Q, pa, stream);
+            XATTN_GEMM_CASE(128, 128, 64)
+            XATTN_GEMM_CASE(64, 64, 256)
+            XATTN_GEMM_CASE(128, 128, 32)
+            XATTN_GEMM_CASE(128, 64, 64)
+            XATTN_GEMM_CASE(64, 128, 64)
+            XATTN_GEMM_CASE(256, 64, 32)
+            XATTN_GEMM_CASE(64, 64, 64)
+#undef XATTN_GEMM_CASE
+        }
+    }
     // wide tiles when they still give at least two work-groups per compute unit
     const int64_t big = (int64_t)q * ((d + 127) / 128) * ((total_cand + 127) / 128);
     if (big >= 512) return launch_prep<128, 128, 64>(Z, Wq, total_cand, q, d, Q, pa, stream);
