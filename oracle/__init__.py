@@ -46,7 +46,9 @@ def _load():
         lib.oracle_forward.argtypes = [I, P, P, I, I, I, P, P, P, P, P, Lg, P]
         lib.oracle_probs.argtypes = [I, P, P, I, I, I, P, P, P, Lg, I, P]
         lib.oracle_plan.argtypes = [I, P, P, I, I, P, P, P, Lg, P]
-        for f in (lib.oracle_project, lib.oracle_forward, lib.oracle_probs, lib.oracle_plan):
+        lib.oracle_output.argtypes = [Lg, I, I, P, P, P, P, P]
+        for f in (lib.oracle_project, lib.oracle_forward, lib.oracle_probs, lib.oracle_plan,
+                  lib.oracle_output):
             f.restype = I
         _lib = lib
     return _lib
@@ -85,6 +87,24 @@ def project(Z, wt, q: int) -> np.ndarray:
     if rc != 0:
         raise ValueError("oracle_project: invalid arguments")
     return Q.reshape(Z.shape)
+
+
+def output(Z, wgo, O, wo, q: int) -> np.ndarray:
+    """Output gate and projection of Eq. (7) (ReST reading note, s.3.3.1) with
+    the per-slot gate weights of Eq. (8) (s.3.3.2):
+    Y[row] = (O[row] * sigmoid(Z[row] @ wgo[row % q].T)) @ wo.T, weights stored
+    output-major.  Z, O: [rows, d] (or [cand, q, d]); returns [rows, d]."""
+    wgo = _f64(wgo)
+    d = wgo.shape[-1]
+    Z2 = _f64(Z).reshape(-1, d)
+    O2 = _f64(O).reshape(-1, d)
+    assert Z2.shape == O2.shape
+    Y = np.empty_like(Z2)
+    rc = _load().oracle_output(Z2.shape[0], q, d, _ptr(Z2), _ptr(wgo), _ptr(O2),
+                               _ptr(_f64(wo)), _ptr(Y))
+    if rc != 0:
+        raise ValueError("oracle_output: invalid arguments")
+    return Y
 
 
 def forward(cu_kv, cu_cand, q: int, heads: int, Z, wt, K, V=None, rows=None) -> np.ndarray:

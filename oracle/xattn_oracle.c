@@ -88,6 +88,46 @@ int oracle_project(long n_rows, int q, int d, const double *Z,
 }
 
 /*
+ * Output gate and output projection of Eq. (7) (ReST reading note, section
+ * 3.3.1), with the gate projection token-specific (section 3.3.2, Eq. (8):
+ * W_go is one of the candidate-side transforms that get per-slot weights;
+ * W_o is not listed among them and is shared by all slots):
+ *   G[row][o] = sigmoid( sum_{i<d} Z[row][i] * wgo[row % q][o][i] )
+ *   Y[row][p] = sum_{o<d} ( O[row][o] * G[row][o] ) * wo[p][o]
+ * O is the concatenated multi-head attention output of the same rows.
+ * Weights are stored output-major like W_Q.  Z, O, Y: [n_rows][d];
+ * wgo: [q][d][d]; wo: [d][d].
+ */
+int oracle_output(long n_rows, int q, int d, const double *Z, const double *wgo,
+                  const double *O, const double *wo, double *Y)
+{
+    if (n_rows < 0 || q < 1 || d < 1 || !Z || !wgo || !O || !wo || !Y)
+        return ORACLE_EINVAL;
+#pragma omp parallel
+    {
+        double *x = malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(static)
+        for (long row = 0; row < n_rows; ++row) {
+            const double *w = wgo + (size_t)(row % q) * d * d;
+            for (int o = 0; o < d; ++o) {
+                double acc = 0.0;
+                for (int i = 0; i < d; ++i)
+                    acc += Z[(size_t)row * d + i] * w[(size_t)o * d + i];
+                x[o] = O[(size_t)row * d + o] / (1.0 + exp(-acc));
+            }
+            for (int p = 0; p < d; ++p) {
+                double acc = 0.0;
+                for (int o = 0; o < d; ++o)
+                    acc += x[o] * wo[(size_t)p * d + o];
+                Y[(size_t)row * d + p] = acc;
+            }
+        }
+        free(x);
+    }
+    return ORACLE_OK;
+}
+
+/*
  * Softmax weights of one (query row, head) over its request's memory rows:
  *   p[j] = exp(s_j - max_k s_k) / sum_k exp(s_k - max_k s_k),
  *   s_j  = <Q[row, head cols], K[kv0 + j, head cols]> / sqrt(d_h).
