@@ -33,6 +33,8 @@ _ATTN_SRC = ["shared_history_candidate_amd/csrc/attn_bf16.hip",
              "shared_history_candidate_amd/csrc/plan_wave.h",
              "shared_history_candidate_amd/csrc/common.h"]
 KERNEL_SOURCES = {"fused": _ATTN_SRC, "attention": _ATTN_SRC,
+                  "output": ["shared_history_candidate_amd/csrc/gemm_bf16.hip",
+                             "shared_history_candidate_amd/csrc/common.h"],
                   "projection": ["shared_history_candidate_amd/csrc/gemm_bf16.hip",
                                  "shared_history_candidate_amd/csrc/plan_device.h",
                                  "shared_history_candidate_amd/csrc/common.h"]}
@@ -48,6 +50,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--stage", default="attention", choices=("attention", "output"),
+                   help="attention: the hot path (xattn_forward, the default); output: the "
+                        "gate and output projection of Eq. (7) alone (xattn_output)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="run only a plain device copy of this many MiB (counter calibration)")
     p.add_argument("--ingest-counters", metavar="DIR",
@@ -183,20 +188,31 @@ def roofline(flops, nbytes, ms, dtype):
             "frac": round(achieved / peak, 5)}
 
 
-def cpu_baseline(wl, target_s):
+def cpu_baseline(wl, target_s, stage="attention", seed=0):
     """The fp64 oracle as it stands, timed on this host on a bounded sample of
-    the workload's query rows (grown until it takes about target_s)."""
+    the workload's query rows (grown until it takes about target_s).  For the
+    output stage the sample is whole candidates (all their query slots)."""
     import numpy as np
     import oracle
+    from shared_history_candidate_amd import workloads as W
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     oracle.set_threads(threads)
     rng = np.random.default_rng(1)
+    if stage == "output":
+        wgo, wo = W.output_weights(wl, seed + 1)
+        O_in = W.attention_like(wl, seed + 2)
     n = min(wl.rows, 64)
     done, elapsed, runs = 0, 0.0, 0
     while True:
         rows = np.sort(rng.choice(wl.rows, size=n, replace=False)) if n < wl.rows else None
         t0 = time.perf_counter()
-        oracle.forward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, wl.K, wl.V, rows=rows)
+        if stage == "output":
+            c = np.unique(rows // wl.q) if rows is not None else np.arange(wl.total_cand)
+            oracle.output(wl.Z[c], wgo, O_in[c], wo, wl.q)
+            n = len(c) * wl.q
+        else:
+            oracle.forward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, wl.K, wl.V,
+                           rows=rows)
         dt = time.perf_counter() - t0
         done += n
         elapsed += dt
@@ -267,9 +283,18 @@ def main():
     O = torch.empty((wl.total_cand, wl.q, wl.d), dtype=ctx.torch_dtype, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step():
-        ctx.forward(t["Z"], t["W_Q"], t["K"], t["V"], t["cu_kv"], t["cu_cand"], wl.heads,
-                    O=O, workspace=ws, stream=stream)
+    if args.stage == "output":
+        wgo, wo = W.output_weights(wl, args.seed + 1)
+        dt = ctx.torch_dtype
+        up = lambda a: torch.from_numpy(a).to("cuda").to(dt).contiguous()
+        Wgo_d, Wo_d, O_in = up(wgo), up(wo), up(W.attention_like(wl, args.seed + 2))
+
+        def step():
+            ctx.output(t["Z"], Wgo_d, O_in, Wo_d, ws, Y=O, stream=stream)
+    else:
+        def step():
+            ctx.forward(t["Z"], t["W_Q"], t["K"], t["V"], t["cu_kv"], t["cu_cand"], wl.heads,
+                        O=O, workspace=ws, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -303,13 +328,21 @@ def main():
         return a.elapsed_time(b) / args.steps
 
     launches = ctx.forward_launches(wl.R, wl.total_cand, wl.total_kv, wl.heads)
+    if args.stage == "output":
+        launches = 0
 
     def entry(kernel, flops, nbytes, ms):
         return dict(roofline(flops, nbytes, ms, wl.dtype), kernel_ms=round(ms, 5),
                     algorithmic_flops=flops, algorithmic_bytes=nbytes,
                     traffic=traffic_for(kernel, args.config), kernel=kernel)
 
-    if launches == 1:
+    if args.stage == "output":
+        # gate GEMM (sigmoid and product with O in its epilogue) + W_o GEMM
+        out_ms = per_launch_ms(step)
+        print("bench: output stage %.4f ms" % out_ms, file=sys.stderr, flush=True)
+        roof = entry("output", wl.flops_output(), wl.bytes_output(), out_ms)
+        roof["other_kernel"] = None
+    elif launches == 1:
         # The step is one kernel: the attention kernel plans the batch and
         # projects its own queries.  Its work is the whole path's.
         fused_ms = per_launch_ms(step)
@@ -335,7 +368,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("bench: timing the fp64 oracle on the host", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(wl, args.cpu_seconds)
+        cpu = cpu_baseline(wl, args.cpu_seconds, args.stage, args.seed)
 
     value = wl.rows / (ms_per_step * 1e-3)
     line = {
@@ -345,7 +378,9 @@ def main():
         "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
         "config": {"workload": wl.name, "requests": wl.R, "candidates": wl.total_cand,
                    "query_tokens": wl.q, "memory_rows": wl.total_kv, "d": wl.d,
-                   "heads": wl.heads, "kv_mode": wl.kv_mode, "seed": args.seed},
+                   "heads": wl.heads, "kv_mode": wl.kv_mode, "seed": args.seed,
+                   "stage": "forward (attention path)" if args.stage == "attention"
+                   else "output gate and projection"},
         "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -219,6 +219,27 @@ int32_t xattn_forward_launches(const xattn_ctx* ctx, int32_t num_requests,
 xattn_status xattn_project(xattn_ctx* ctx, const void* Z, const void* W_Q,
                            int32_t total_cand, void* Q, void* stream);
 
+/* Output gate and output projection of Eq. (7) (ReST reading note, s.3.3.1),
+ * the gate projection token-specific as in Eq. (8) (s.3.3.2), W_o shared by
+ * all slots:
+ *     Y[row] = ( O[row] * sigmoid( Z[row] . W_go[s] ) ) . W_o     (row = c*q + s)
+ * with O the attention output of xattn_forward for the same batch.
+ *   - Z, O, Y  [total_cand][q][d] in the context's type;
+ *   - W_go     [q][d][d] output-major: W_go[s][o][i] multiplies Z[.][i] into
+ *              gate feature o (like W_Q);
+ *   - W_o      [d][d] output-major: W_o[p][o] multiplies gated feature o into
+ *              Y[.][p].
+ * Two launches on `stream`: the gate GEMM (sigmoid and product with O in its
+ * epilogue; bf16: the gated values are rounded to bf16) writing the last
+ * total_cand*q*d elements of `workspace` - the projected-query region of a
+ * workspace sized by xattn_workspace_size, so a plan stored there is kept -
+ * then the W_o GEMM.  `workspace_bytes` must cover that region.  Errors:
+ * XATTN_EINVAL for NULL pointers or a negative count; XATTN_EWORKSPACE for a
+ * small workspace; XATTN_EHIP for a launch failure. */
+xattn_status xattn_output(xattn_ctx* ctx, const void* Z, const void* W_go, const void* O,
+                          const void* W_o, int32_t total_cand, void* Y, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
 /* Synchronise `stream` and read the device-side validation flag a previous
  * xattn_forward / xattn_plan left in `workspace`: *flag = 0 when the offset
  * arrays were consistent, otherwise a bitmask (1: cu_seqlens_kv, 2: cu_cand).

@@ -388,6 +388,39 @@ xattn_status xattn_project(xattn_ctx* ctx, const void* Z, const void* W_Q, int32
     return XATTN_OK;
 }
 
+xattn_status xattn_output(xattn_ctx* ctx, const void* Z, const void* W_go, const void* O,
+                          const void* W_o, int32_t total_cand, void* Y, void* workspace,
+                          size_t workspace_bytes_, void* stream) {
+    g_last_error.clear();
+    if (!ctx) return fail(XATTN_EINVAL, "ctx is NULL");
+    if (total_cand < 0) return fail(XATTN_EINVAL, "negative total_cand");
+    if (total_cand == 0) return XATTN_OK;
+    if (!Z || !W_go || !O || !W_o || !Y) return fail(XATTN_EINVAL, "NULL Z, W_go, O, W_o or Y");
+    const xattn_config& c = ctx->cfg;
+    if ((int64_t)total_cand * c.n_slots > INT32_MAX)
+        return fail(XATTN_EUNSUPPORTED, "total_cand * q exceeds int32");
+    const size_t xbytes = (size_t)total_cand * c.n_slots * c.d_model * elem_bytes(c);
+    if (!workspace || workspace_bytes_ < xbytes)
+        return fail(XATTN_EWORKSPACE, "workspace needs %zu bytes, got %zu", xbytes,
+                    workspace_bytes_);
+    // the gated values go to the end of the workspace, 256-byte aligned
+    const size_t xoff = (workspace_bytes_ - xbytes) & ~(size_t)255;
+    void* X = static_cast<char*>(workspace) + xoff;
+    DeviceGuard dg(c.device);
+    if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = c.dtype == XATTN_BF16
+                       ? xattn::launch_gate_output_bf16(Z, W_go, O, W_o, total_cand, c.n_slots,
+                                                        c.d_model, X, Y, s)
+                       : xattn::launch_gate_output_f32(
+                             static_cast<const float*>(Z), static_cast<const float*>(W_go),
+                             static_cast<const float*>(O), static_cast<const float*>(W_o),
+                             total_cand, c.n_slots, c.d_model, static_cast<float*>(X),
+                             static_cast<float*>(Y), s);
+    if (e != hipSuccess) return hip_fail(e, "output kernel launch");
+    return XATTN_OK;
+}
+
 xattn_status xattn_device_error(xattn_ctx* ctx, const void* workspace, int32_t* flag,
                                 void* stream) {
     g_last_error.clear();

@@ -111,6 +111,21 @@ __global__ void project_f32_kernel(const float* __restrict__ Z, const float* __r
     Q[idx] = a;
 }
 
+// Output gate of Eq. (7) in fp32: X[row][o] = O[row][o] * sigmoid(Z[row] . W_go[row % q][o]).
+__global__ void gate_f32_kernel(const float* __restrict__ Z, const float* __restrict__ Wgo,
+                                const float* __restrict__ O, int64_t n, int q, int d,
+                                float* __restrict__ X) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= n) return;
+    const int64_t row = idx / d;
+    const int o = (int)(idx - row * d);
+    const float* zrow = Z + (size_t)row * d;
+    const float* w = Wgo + ((size_t)(row % q) * d + o) * d;
+    float a = 0.f;
+    for (int k = 0; k < d; ++k) a = fmaf(zrow[k], w[k], a);
+    X[idx] = O[idx] / (1.0f + expf(-a));
+}
+
 template <int DHMAX>
 hipError_t launch_f32(const float* Qp, const float* K, const float* V,
                       const void* ws, int64_t max_tiles, int q, int d,
@@ -146,6 +161,19 @@ hipError_t launch_project_f32(const float* Z, const float* Wq, int total_cand, i
     hipLaunchKernelGGL(project_f32_kernel, dim3((unsigned)((n + threads - 1) / threads)),
                        dim3(threads), 0, stream, Z, Wq, n, q, d, Q);
     return hipGetLastError();
+}
+
+hipError_t launch_gate_output_f32(const float* Z, const float* Wgo, const float* O,
+                                  const float* Wo, int total_cand, int q, int d, float* X,
+                                  float* Y, hipStream_t stream) {
+    const int64_t n = (int64_t)total_cand * q * d;
+    if (n <= 0) return hipSuccess;
+    const int threads = 256;
+    hipLaunchKernelGGL(gate_f32_kernel, dim3((unsigned)((n + threads - 1) / threads)),
+                       dim3(threads), 0, stream, Z, Wgo, O, n, q, d, X);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_project_f32(X, Wo, total_cand * q, 1, d, Y, stream);
 }
 
 }  // namespace xattn

@@ -17,6 +17,12 @@
 // The same launch can carry the varlen planner in one extra work-group
 // (blockIdx.x == 0): the plan and the projection are independent, and the
 // attention kernel that follows on the stream needs both.
+//
+// With a gate operand Og the kernel is the output gate of Eq. (7) instead
+// (ReST reading note, s.3.3.1; per-slot W_go as in s.3.3.2 Eq. (8)): it
+// stores O[c][s][o] * sigmoid(Z[c][s] . W_go[s][o]) rounded to bf16, the
+// operand of the output projection, which is this kernel again with one
+// slot (W_o shared by all slots).
 #include <cstdio>
 #include <cstdlib>
 
@@ -63,7 +69,8 @@ template <int TE, int TC, int KC>
 __global__ __launch_bounds__(256) void prep_kernel(const bf16* __restrict__ Z,
                                                    const bf16* __restrict__ Wq, int total_cand,
                                                    int q, int d, bf16* __restrict__ Q,
-                                                   int tiles_e, int tiles_c, PlanArgs pa) {
+                                                   int tiles_e, int tiles_c, PlanArgs pa,
+                                                   const bf16* __restrict__ Og) {
     using C = GCfg<TE, TC, KC>;
     constexpr int LDP = C::LDP;
     __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
@@ -191,8 +198,19 @@ __global__ __launch_bounds__(256) void prep_kernel(const bf16* __restrict__ Z,
                 const int o = e0 + wr * (TE / 2) + i * 32 + b4 * 8 + 4 * g;
                 if (o < d) {
                     bf16x4 v;
+                    if (Og) {
+                        const bf16x4 ov =
+                            *reinterpret_cast<const bf16x4*>(Og + ((size_t)c * q + s) * d + o);
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) v[t] = (bf16)acc[i][j][4 * b4 + t];
+                        for (int t = 0; t < 4; ++t) {
+                            const float e = __builtin_amdgcn_exp2f(-acc[i][j][4 * b4 + t] *
+                                                                   1.4426950408889634f);
+                            v[t] = (bf16)((float)ov[t] / (1.0f + e));
+                        }
+                    } else {
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) v[t] = (bf16)acc[i][j][4 * b4 + t];
+                    }
                     *reinterpret_cast<bf16x4*>(qrow + o) = v;
                 }
             }
@@ -201,14 +219,15 @@ __global__ __launch_bounds__(256) void prep_kernel(const bf16* __restrict__ Z,
 
 template <int TE, int TC, int KC>
 hipError_t launch_prep(const void* Z, const void* Wq, int total_cand, int q, int d, void* Q,
-                       const PlanArgs& pa, hipStream_t stream) {
+                       const PlanArgs& pa, hipStream_t stream, const void* Og) {
     const int tiles_e = (d + TE - 1) / TE;
     const int tiles_c = (total_cand + TC - 1) / TC;
     const int64_t blocks = (int64_t)q * tiles_e * tiles_c + (pa.enabled ? 1 : 0);
     if (blocks <= 0) return hipSuccess;
     hipLaunchKernelGGL((prep_kernel<TE, TC, KC>), dim3((unsigned)blocks), dim3(256), 0, stream,
                        static_cast<const bf16*>(Z), static_cast<const bf16*>(Wq), total_cand, q, d,
-                       static_cast<bf16*>(Q), tiles_e, tiles_c, pa);
+                       static_cast<bf16*>(Q), tiles_e, tiles_c, pa,
+                       static_cast<const bf16*>(Og));
     return hipGetLastError();
 }
 
@@ -217,7 +236,7 @@ hipError_t launch_prep(const void* Z, const void* Wq, int total_cand, int q, int
 hipError_t launch_project_plan_bf16(const void* Z, const void* Wq, int total_cand, int q, int d,
                                     void* Q, const int* cu_kv, const int* cu_cand, int R,
                                     int tile_m, int total_kv, void* ws, int64_t max_tiles,
-                                    hipStream_t stream) {
+                                    hipStream_t stream, const void* Og) {
     PlanArgs pa{cu_kv, cu_cand, static_cast<int*>(ws), max_tiles, R, tile_m, total_kv,
                 ws != nullptr ? 1 : 0};
     if (total_cand <= 0 && !pa.enabled) return hipSuccess;
@@ -226,7 +245,7 @@ hipError_t launch_project_plan_bf16(const void* Z, const void* Wq, int total_can
         int te = 0, tc = 0, kc = 0;
         if (sscanf(env, "%d,%d,%d", &te, &tc, &kc) == 3) {
 #define XATTN_GEMM_CASE(A_, B_, C_) \
-    if (te == A_ && tc == B_ && kc == C_) return launch_prep<A_, B_, C_>(Z, Wq, total_cand, q, d, Q, pa, stream);
+    if (te == A_ && tc == B_ && kc == C_) return launch_prep<A_, B_, C_>(Z, Wq, total_cand, q, d, Q, pa, stream, Og);
             XATTN_GEMM_CASE(128, 128, 64)
             XATTN_GEMM_CASE(64, 64, 256)
             XATTN_GEMM_CASE(128, 128, 32)
@@ -239,8 +258,18 @@ hipError_t launch_project_plan_bf16(const void* Z, const void* Wq, int total_can
     }
     // wide tiles when they still give at least two work-groups per compute unit
     const int64_t big = (int64_t)q * ((d + 127) / 128) * ((total_cand + 127) / 128);
-    if (big >= 512) return launch_prep<128, 128, 64>(Z, Wq, total_cand, q, d, Q, pa, stream);
-    return launch_prep<64, 64, 256>(Z, Wq, total_cand, q, d, Q, pa, stream);
+    if (big >= 512) return launch_prep<128, 128, 64>(Z, Wq, total_cand, q, d, Q, pa, stream, Og);
+    return launch_prep<64, 64, 256>(Z, Wq, total_cand, q, d, Q, pa, stream, Og);
+}
+
+hipError_t launch_gate_output_bf16(const void* Z, const void* Wgo, const void* O, const void* Wo,
+                                   int total_cand, int q, int d, void* X, void* Y,
+                                   hipStream_t stream) {
+    hipError_t e = launch_project_plan_bf16(Z, Wgo, total_cand, q, d, X, nullptr, nullptr, 0, 0, 0,
+                                            nullptr, 0, stream, O);
+    if (e != hipSuccess) return e;
+    return launch_project_plan_bf16(X, Wo, total_cand * q, 1, d, Y, nullptr, nullptr, 0, 0, 0,
+                                    nullptr, 0, stream, nullptr);
 }
 
 }  // namespace xattn

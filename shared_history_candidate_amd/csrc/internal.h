@@ -43,7 +43,13 @@ hipError_t launch_attn_bf16(const AttnArgs& a, int rb, int ksplit, hipStream_t s
 hipError_t launch_project_plan_bf16(const void* Z, const void* Wq, int total_cand, int q, int d,
                                     void* Qp, const int* cu_kv, const int* cu_cand, int R,
                                     int tile_m, int total_kv, void* ws, int64_t max_tiles,
-                                    hipStream_t stream);
+                                    hipStream_t stream, const void* Og = nullptr);
+
+// Output gate and projection of Eq. (7): X = O * sigmoid(Z W_go[slot]) (bf16,
+// [total_cand][q][d]), then Y = X W_o; two launches of the projection kernel.
+hipError_t launch_gate_output_bf16(const void* Z, const void* Wgo, const void* O, const void* Wo,
+                                   int total_cand, int q, int d, void* X, void* Y,
+                                   hipStream_t stream);
 
 // fp32 path (tile_m = 64): attention over projected queries, projection.
 hipError_t launch_attn_f32(const float* Qp, const float* K, const float* V, const void* ws, int64_t max_tiles, int q, int d, int heads, float* O,
@@ -51,5 +57,10 @@ hipError_t launch_attn_f32(const float* Qp, const float* K, const float* V, cons
 
 hipError_t launch_project_f32(const float* Z, const float* Wq, int total_cand, int q, int d,
                               float* Q, hipStream_t stream);
+
+// fp32 output gate and projection (same definition, one thread per output).
+hipError_t launch_gate_output_f32(const float* Z, const float* Wgo, const float* O,
+                                  const float* Wo, int total_cand, int q, int d, float* X,
+                                  float* Y, hipStream_t stream);
 
 }  // namespace xattn

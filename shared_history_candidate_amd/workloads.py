@@ -32,7 +32,8 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-__all__ = ["Workload", "CONFIGS", "make", "custom", "round_bf16"]
+__all__ = ["Workload", "CONFIGS", "make", "custom", "round_bf16", "output_weights",
+           "attention_like"]
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
@@ -114,6 +115,15 @@ class Workload:
         """FLOPs of QK^T and PV: 4 * sum_r M_r * L_r * d."""
         m = self.cands.astype(np.float64) * self.q
         return 4.0 * float(np.sum(m * self.lengths)) * self.d
+
+    def flops_output(self) -> float:
+        """FLOPs of the gate and output projections of Eq. (7): 4 * rows * d * d."""
+        return 4.0 * self.rows * self.d * self.d
+
+    def bytes_output(self) -> float:
+        """Bytes the output stage must move: Z, O in, Y out, W_go and W_o."""
+        b = 2 if self.dtype == "bf16" else 4
+        return float(b * (3 * self.rows * self.d + (self.q + 1) * self.d * self.d))
 
     def bytes_attention(self) -> float:
         """Bytes the attention over projected queries must move: K (and V), Q, O."""
@@ -206,6 +216,29 @@ def _ragged(seed):
     cands = rng.integers(1, 65, size=R)
     return custom("ragged_bf16", lengths, cands, q=3, d=256, heads=8, dtype="bf16",
                   kv_mode="shared", seed=seed, rng=rng)
+
+
+def output_weights(wl: Workload, seed: int = 0):
+    """Gate and output weights of Eq. (7) for a workload: W_go [q][d][d] (one
+    set per query slot, output-major) and W_o [d][d] (output-major), each
+    N(0, 1/d) like W_Q, drawn from default_rng(seed) in that order and rounded
+    to bf16 in bf16 mode (float32 arrays holding the exact values)."""
+    rng = np.random.default_rng(seed)
+    std = 1.0 / np.sqrt(wl.d)
+    wgo = _normal(rng, (wl.q, wl.d, wl.d), std=std)
+    wo = _normal(rng, (wl.d, wl.d), std=std)
+    if wl.dtype == "bf16":
+        wgo, wo = round_bf16(wgo), round_bf16(wo)
+    return wgo, wo
+
+
+def attention_like(wl: Workload, seed: int = 0, std: float = 0.5) -> np.ndarray:
+    """A stand-in attention output [total_cand][q][d] for testing the output
+    stage alone: N(0, std^2) draws from default_rng(seed), bf16-rounded in bf16
+    mode."""
+    rng = np.random.default_rng(seed)
+    O = _normal(rng, (wl.total_cand, wl.q, wl.d), std=std)
+    return round_bf16(O) if wl.dtype == "bf16" else O
 
 
 CONFIGS = {

@@ -24,7 +24,7 @@ XATTN_KV_SHARED, XATTN_KV_SEPARATE = 0, 1
 
 EXPORTED = ("xattn_create", "xattn_destroy", "xattn_workspace_size", "xattn_forward",
             "xattn_attend", "xattn_attend_q", "xattn_plan", "xattn_max_tiles",
-            "xattn_forward_launches", "xattn_project", "xattn_device_error",
+            "xattn_forward_launches", "xattn_project", "xattn_output", "xattn_device_error",
             "xattn_last_error")
 
 
@@ -72,6 +72,8 @@ def lib():
                                  ctypes.POINTER(I32), P, SZ, P]
         L.xattn_plan.restype = ctypes.c_int
         L.xattn_project.argtypes = [P, P, P, I32, P, P]
+        L.xattn_output.argtypes = [P, P, P, P, P, I32, P, P, ctypes.c_size_t, P]
+        L.xattn_output.restype = ctypes.c_int
         L.xattn_project.restype = ctypes.c_int
         L.xattn_device_error.argtypes = [P, P, ctypes.POINTER(I32), P]
         L.xattn_device_error.restype = ctypes.c_int
@@ -245,6 +247,24 @@ class XAttn:
         _check(lib().xattn_project(self._h, _ptr(Z), _ptr(W_Q), total_cand, _ptr(Q),
                                    _stream(Z.device, stream)))
         return Q
+
+    def output(self, Z, W_go, O, W_o, workspace, Y=None, stream=None) -> torch.Tensor:
+        """Output gate and projection of Eq. (7):
+        Y[row] = (O[row] * sigmoid(Z[row] . W_go[row % q])) . W_o (output-major
+        weights); uses the end of `workspace` as scratch (see include/xattn.h)."""
+        d, q, dt = self.d_model, self.q, self.torch_dtype
+        total_cand = Z.shape[0]
+        self._check_tensor("Z", Z, dt, (total_cand, q, d))
+        self._check_tensor("W_go", W_go, dt, (q, d, d))
+        self._check_tensor("O", O, dt, (total_cand, q, d))
+        self._check_tensor("W_o", W_o, dt, (d, d))
+        if Y is None:
+            Y = torch.empty((total_cand, q, d), dtype=dt, device=Z.device)
+        self._check_tensor("Y", Y, dt, (total_cand, q, d))
+        _check(lib().xattn_output(self._h, _ptr(Z), _ptr(W_go), _ptr(O), _ptr(W_o), total_cand,
+                                  _ptr(Y), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _stream(Z.device, stream)))
+        return Y
 
     def device_error(self, workspace, stream=None) -> int:
         """Synchronise and read the device-side offset-validation flag."""

@@ -178,3 +178,21 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(X, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         X.lib()
+
+
+def test_output_host_validation(L):
+    st, h = _create(L, 256, 3, X.XATTN_BF16, X.XATTN_KV_SHARED)
+    assert st == 0
+    need = 10 * 3 * 256 * 2
+
+    def out(Z=FAKE, Wgo=FAKE, O=FAKE, Wo=FAKE, tc=10, Y=FAKE, ws=FAKE, wsb=need):
+        return L.xattn_output(h, Z, Wgo, O, Wo, tc, Y, ws, wsb, None)
+
+    assert out(tc=-1) == X.XATTN_EINVAL
+    assert out(tc=0) == X.XATTN_OK            # nothing to do, nothing enqueued
+    for kw in ({"Z": None}, {"Wgo": None}, {"O": None}, {"Wo": None}, {"Y": None}):
+        assert out(**kw) == X.XATTN_EINVAL
+    assert out(ws=None) == X.XATTN_EWORKSPACE
+    assert out(wsb=need - 1) == X.XATTN_EWORKSPACE
+    assert L.xattn_output(None, FAKE, FAKE, FAKE, FAKE, 10, FAKE, FAKE, need, None) == X.XATTN_EINVAL
+    L.xattn_destroy(h)

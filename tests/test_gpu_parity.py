@@ -266,3 +266,57 @@ def test_single_launch_and_split_paths_agree(R, dh, heads, q, mode):
     assert torch.equal(a, c)
     got = a.float().cpu().numpy().astype(np.float64).reshape(wl.rows, wl.d)
     assert_close(got, _oracle(wl), "bf16", "paths R=%d dh=%d" % (R, dh))
+
+
+# ---------------------------------------------------------------------------
+# Output gate and output projection of Eq. (7)
+# ---------------------------------------------------------------------------
+def _up(a, dt):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(dt).contiguous()
+
+
+@pytest.mark.parametrize("name,dtype", [("rest", "bf16"), ("transx", "bf16"), ("tiny", "fp32")])
+def test_output_stage_alone(name, dtype):
+    """xattn_output on a stand-in attention output against the oracle's gate
+    and projection of the same inputs."""
+    require_gpu()
+    wl = W.make(name, 0)
+    if name == "transx":   # a slice of the batch keeps the oracle fast
+        wl = W.custom("transx_part", wl.lengths[:8], wl.cands[:8], q=wl.q, d=wl.d,
+                      heads=wl.heads, dtype="bf16", kv_mode="separate", seed=3)
+    wgo, wo = W.output_weights(wl, 5)
+    O = W.attention_like(wl, 6)
+    ctx = ctx_for(wl)
+    dt = ctx.torch_dtype
+    t = X.to_device(wl)
+    ws = ctx.alloc_workspace(wl.R, wl.total_cand, wl.heads)
+    Y = ctx.output(t["Z"], _up(wgo, dt), _up(O, dt), _up(wo, dt), ws)
+    torch.cuda.synchronize()
+    got = Y.float().cpu().numpy().astype(np.float64).reshape(-1, wl.d)
+    ref = oracle.output(wl.Z, wgo, O, wo, wl.q)
+    err, rel = assert_close(got, ref, wl.dtype, "output " + name)
+    print("output %s: max-abs %.3e normwise %.3e" % (name, err, rel))
+
+
+@pytest.mark.parametrize("name", ["rest", "ragged"])
+def test_full_eq7(name):
+    """Attention (xattn_forward) then the gate and output projection
+    (xattn_output) against the oracle's full Eq. (7) on every row; the stored
+    plan survives xattn_output (xattn_attend afterwards gives the same bits)."""
+    require_gpu()
+    wl = W.make(name, 0)
+    wgo, wo = W.output_weights(wl, 7)
+    ctx = ctx_for(wl)
+    dt = ctx.torch_dtype
+    t = X.to_device(wl)
+    ws = ctx.alloc_workspace(wl.R, wl.total_cand, wl.heads)
+    O = ctx.forward(t["Z"], t["W_Q"], t["K"], t["V"], t["cu_kv"], t["cu_cand"], wl.heads,
+                    workspace=ws).clone()
+    Y = ctx.output(t["Z"], _up(wgo, dt), O, _up(wo, dt), ws)
+    O2 = ctx.attend(t["Z"], t["W_Q"], t["K"], t["V"], t["cu_kv"], t["cu_cand"], wl.heads, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(O, O2)
+    got = Y.float().cpu().numpy().astype(np.float64).reshape(-1, wl.d)
+    ref = oracle.output(wl.Z, wgo, _oracle(wl), wo, wl.q)
+    err, rel = assert_close(got, ref, wl.dtype, "eq7 " + name)
+    print("full Eq. (7) %s: max-abs %.3e normwise %.3e" % (name, err, rel))
