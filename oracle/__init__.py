@@ -47,8 +47,9 @@ def _load():
         lib.oracle_probs.argtypes = [I, P, P, I, I, I, P, P, P, Lg, I, P]
         lib.oracle_plan.argtypes = [I, P, P, I, I, P, P, P, Lg, P]
         lib.oracle_output.argtypes = [Lg, I, I, P, P, P, P, P]
+        lib.oracle_forward_prefix.argtypes = [I, P, P, I, I, I, P, P, P, P, P, P, Lg, P]
         for f in (lib.oracle_project, lib.oracle_forward, lib.oracle_probs, lib.oracle_plan,
-                  lib.oracle_output):
+                  lib.oracle_output, lib.oracle_forward_prefix):
             f.restype = I
         _lib = lib
     return _lib
@@ -107,10 +108,13 @@ def output(Z, wgo, O, wo, q: int) -> np.ndarray:
     return Y
 
 
-def forward(cu_kv, cu_cand, q: int, heads: int, Z, wt, K, V=None, rows=None) -> np.ndarray:
+def forward(cu_kv, cu_cand, q: int, heads: int, Z, wt, K, V=None, rows=None,
+            kv_len=None) -> np.ndarray:
     """Cross-attention of Eq. (7) (ReST reading note s.3.3.1) without gate/W_o,
     per-slot W_Q of Eq. (8), K = V = H when V is None, separate K/V otherwise
-    (TransX report s.2).  Returns O [n_rows, d] (all rows c*q+s when rows is None)."""
+    (TransX report s.2).  kv_len (one int per candidate, optional) limits each
+    candidate to a prefix of its request's memory (ReST reading note s.3.5,
+    ULT).  Returns O [n_rows, d] (all rows c*q+s when rows is None)."""
     cu_kv = _i32(cu_kv)
     cu_cand = _i32(cu_cand)
     R = len(cu_kv) - 1
@@ -127,9 +131,17 @@ def forward(cu_kv, cu_cand, q: int, heads: int, Z, wt, K, V=None, rows=None) -> 
         rows_a = None
         n_out = Z2.shape[0]
     O = np.empty((n_out, d), dtype=np.float64)
-    rc = _load().oracle_forward(R, _ptr(cu_kv), _ptr(cu_cand), q, d, heads, _ptr(Z2),
-                                _ptr(wt), _ptr(K), _ptr(Vd), _ptr(rows_a),
-                                n_out if rows_a is not None else 0, _ptr(O))
+    if kv_len is not None:
+        kl = _i32(kv_len)
+        assert kl.shape == (int(cu_cand[-1]),)
+        rc = _load().oracle_forward_prefix(R, _ptr(cu_kv), _ptr(cu_cand), q, d, heads,
+                                           _ptr(Z2), _ptr(wt), _ptr(K), _ptr(Vd), _ptr(kl),
+                                           _ptr(rows_a), n_out if rows_a is not None else 0,
+                                           _ptr(O))
+    else:
+        rc = _load().oracle_forward(R, _ptr(cu_kv), _ptr(cu_cand), q, d, heads, _ptr(Z2),
+                                    _ptr(wt), _ptr(K), _ptr(Vd), _ptr(rows_a),
+                                    n_out if rows_a is not None else 0, _ptr(O))
     if rc != 0:
         raise ValueError("oracle_forward: invalid arguments")
     return O

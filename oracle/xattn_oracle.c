@@ -163,10 +163,18 @@ static void softmax_weights(const double *qrow, const double *K, int d,
  * Z: [total_cand*q][d]; K, V: [cu_kv[R]][d]; O: [n_out][d] where
  * n_out = n_rows if rows != NULL else total_cand*q.
  */
-int oracle_forward(int R, const int *cu_kv, const int *cu_cand, int q, int d,
-                   int heads, const double *Z, const double *wt,
-                   const double *K, const double *V, const long *rows,
-                   long n_rows, double *O)
+/*
+ * Shared body of oracle_forward and oracle_forward_prefix.  kv_len (one int
+ * per candidate, or NULL) restricts candidate c to the first
+ * min(max(kv_len[c], 0), L_r) memory rows of its request: the prefix-valid
+ * reading of the per-candidate cutoff (ReST reading note, section 3.5, ULT:
+ * each sample sees only the part of its user's sequence that precedes it).
+ * A candidate with no visible row gets zeros, like a request with L_r = 0.
+ */
+static int forward_impl(int R, const int *cu_kv, const int *cu_cand, int q, int d,
+                        int heads, const double *Z, const double *wt,
+                        const double *K, const double *V, const int *kv_len,
+                        const long *rows, long n_rows, double *O)
 {
     if (R < 0 || q < 1 || d < 1 || heads < 1 || d % heads != 0 || !cu_kv ||
         !cu_cand || !Z || !wt || !K || !O)
@@ -200,6 +208,12 @@ int oracle_forward(int R, const int *cu_kv, const int *cu_cand, int q, int d,
                 const long row = rows ? rows[k] : k;
                 const int r = request_of_row(R, cu_cand, q, row);
                 const int kv0 = cu_kv[r], L = cu_kv[r + 1] - cu_kv[r];
+                /* visible memory rows of this row's candidate */
+                int Lc = L;
+                if (kv_len) {
+                    const int want = kv_len[row / q];
+                    Lc = want < 0 ? 0 : (want < L ? want : L);
+                }
                 /* Q = Z W_Q[slot] for this row (Eq. (7) with Eq. (8)). */
                 const double *w = wt + (size_t)(row % q) * d * d;
                 for (int o = 0; o < d; ++o) {
@@ -210,15 +224,15 @@ int oracle_forward(int R, const int *cu_kv, const int *cu_cand, int q, int d,
                 }
                 for (int h = 0; h < heads; ++h) {
                     double *out = O + (size_t)k * d + h * d_h;
-                    if (L == 0) {
+                    if (Lc == 0) {
                         for (int e = 0; e < d_h; ++e)
                             out[e] = 0.0;
                         continue;
                     }
-                    softmax_weights(qrow, K, d, d_h, h, kv0, L, p);
+                    softmax_weights(qrow, K, d, d_h, h, kv0, Lc, p);
                     for (int e = 0; e < d_h; ++e) {
                         double acc = 0.0;
-                        for (int j = 0; j < L; ++j)
+                        for (int j = 0; j < Lc; ++j)
                             acc += p[j] * Vm[(size_t)(kv0 + j) * d + h * d_h + e];
                         out[e] = acc;
                     }
@@ -229,6 +243,28 @@ int oracle_forward(int R, const int *cu_kv, const int *cu_cand, int q, int d,
         free(p);
     }
     return bad ? ORACLE_EINVAL : ORACLE_OK;
+}
+
+int oracle_forward(int R, const int *cu_kv, const int *cu_cand, int q, int d,
+                   int heads, const double *Z, const double *wt,
+                   const double *K, const double *V, const long *rows,
+                   long n_rows, double *O)
+{
+    return forward_impl(R, cu_kv, cu_cand, q, d, heads, Z, wt, K, V, NULL, rows,
+                        n_rows, O);
+}
+
+/* Forward with a per-candidate prefix cutoff kv_len[total_cand] (see
+ * forward_impl). */
+int oracle_forward_prefix(int R, const int *cu_kv, const int *cu_cand, int q, int d,
+                          int heads, const double *Z, const double *wt,
+                          const double *K, const double *V, const int *kv_len,
+                          const long *rows, long n_rows, double *O)
+{
+    if (!kv_len)
+        return ORACLE_EINVAL;
+    return forward_impl(R, cu_kv, cu_cand, q, d, heads, Z, wt, K, V, kv_len, rows,
+                        n_rows, O);
 }
 
 /*

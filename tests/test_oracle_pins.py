@@ -394,6 +394,86 @@ def test_plan_configs(oracle_mod):
 
 
 # ----------------------------------------------------------------------------
+# Per-candidate prefix cutoff (ReST reading note s.3.5, ULT)
+# ----------------------------------------------------------------------------
+def _check_prefix_sdpa(orc, seed):
+    """Against torch float64 SDPA with a boolean mask that hides every key at
+    or past the candidate's cutoff; cutoffs include 0 (zeros), 1, L and more
+    than L, and negative values (read as 0)."""
+    rng = np.random.default_rng(seed)
+    wl = _rand_case(rng, R=3, q=2, d=8, heads=2, kv_mode="separate", Lmax=9, Nmax=4)
+    kv_len = rng.integers(-2, 12, size=wl.total_cand)
+    kv_len[: min(3, wl.total_cand)] = [0, 1, 100][: min(3, wl.total_cand)]
+    O = orc.forward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, wl.K, wl.V,
+                    kv_len=kv_len)
+    Zt = torch.tensor(wl.Z.astype(np.float64)).reshape(-1, wl.d)
+    Kt = torch.tensor(wl.K.astype(np.float64))
+    Vt = torch.tensor(wl.V.astype(np.float64))
+    dh = wl.d // wl.heads
+    err = 0.0
+    for r in range(wl.R):
+        k, v = Kt[wl.cu_kv[r]:wl.cu_kv[r + 1]], Vt[wl.cu_kv[r]:wl.cu_kv[r + 1]]
+        L = k.shape[0]
+        for c in range(wl.cu_cand[r], wl.cu_cand[r + 1]):
+            cut = int(min(max(kv_len[c], 0), L))
+            for s_ in range(wl.q):
+                row = c * wl.q + s_
+                qv = Zt[row] @ torch.tensor(wl.wt[s_].astype(np.float64)).T
+                if cut == 0:
+                    err = max(err, float(np.max(np.abs(O[row]))))
+                    continue
+                mask = (torch.arange(L) < cut).view(1, 1, L)
+                o = torch.cat([torch.nn.functional.scaled_dot_product_attention(
+                    qv[h * dh:(h + 1) * dh].view(1, 1, dh), k[:, h * dh:(h + 1) * dh].view(1, L, dh),
+                    v[:, h * dh:(h + 1) * dh].view(1, L, dh), attn_mask=mask).view(dh)
+                    for h in range(wl.heads)])
+                err = max(err, float(np.max(np.abs(O[row] - o.numpy()))))
+    return err
+
+
+def _check_prefix_full_is_plain(orc, seed):
+    """Cutoffs at or past every request's length change nothing (bitwise)."""
+    rng = np.random.default_rng(seed)
+    wl = _rand_case(rng, R=3, q=2, d=8, heads=2, kv_mode="shared", Lmax=9, Nmax=4)
+    O1 = orc.forward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, wl.K, wl.V)
+    O2 = orc.forward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, wl.K, wl.V,
+                     kv_len=np.full(wl.total_cand, 1 << 20))
+    return float(np.max(np.abs(O1 - O2)))
+
+
+def _check_prefix_truncation(orc, seed):
+    """A candidate with cutoff L' equals the same candidate alone in a request
+    whose memory is the first L' rows (bitwise: rows are independent)."""
+    rng = np.random.default_rng(seed)
+    wl = _rand_case(rng, R=2, q=2, d=8, heads=2, kv_mode="shared", Lmax=9, Nmax=4)
+    kv_len = rng.integers(1, 10, size=wl.total_cand)
+    O = orc.forward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, wl.K, wl.V,
+                    kv_len=kv_len)
+    err = 0.0
+    for r in range(wl.R):
+        L = int(wl.cu_kv[r + 1] - wl.cu_kv[r])
+        for c in range(wl.cu_cand[r], wl.cu_cand[r + 1]):
+            cut = min(int(kv_len[c]), L)
+            Kc = wl.K[wl.cu_kv[r]:wl.cu_kv[r] + cut]
+            Oc = orc.forward([0, cut], [0, 1], wl.q, wl.heads, wl.Z[c:c + 1], wl.wt, Kc)
+            err = max(err, float(np.max(np.abs(Oc - O[c * wl.q:(c + 1) * wl.q]))))
+    return err
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_prefix_cutoff_matches_masked_sdpa(oracle_mod, seed):
+    assert _check_prefix_sdpa(oracle_mod, seed) < 1e-12
+
+
+def test_prefix_cutoff_past_length_is_plain(oracle_mod):
+    assert _check_prefix_full_is_plain(oracle_mod, 3) == 0.0
+
+
+def test_prefix_cutoff_equals_truncated_memory(oracle_mod):
+    assert _check_prefix_truncation(oracle_mod, 4) == 0.0
+
+
+# ----------------------------------------------------------------------------
 # Output gate and output projection (Eq. (7) after the attention)
 # ----------------------------------------------------------------------------
 def _perm_wo(d, rng):
@@ -498,9 +578,12 @@ MUTANTS = {
                          "for (int j = 0; j < L - 1; ++j) {\n        double s = 0.0;"),
     "no_normalisation": ("p[j] /= z;", "p[j] /= 1.0;"),
     "sign_of_max": ("p[j] = exp(p[j] - m);", "p[j] = exp(m - p[j]);"),
-    "wrong_request_base": ("const int kv0 = cu_kv[r], L = cu_kv[r + 1] - cu_kv[r];\n                /* Q",
-                           "const int kv0 = 0, L = cu_kv[r + 1] - cu_kv[r];\n                /* Q"),
+    "wrong_request_base": ("const int kv0 = cu_kv[r], L = cu_kv[r + 1] - cu_kv[r];\n                /* visible",
+                           "const int kv0 = 0, L = cu_kv[r + 1] - cu_kv[r];\n                /* visible"),
     "gate_sign": ("/ (1.0 + exp(-acc));", "/ (1.0 + exp(acc));"),
+    "cutoff_ignored": ("Lc = want < 0 ? 0 : (want < L ? want : L);", "Lc = L;"),
+    "cutoff_off_by_one": ("Lc = want < 0 ? 0 : (want < L ? want : L);",
+                          "Lc = want < 0 ? 0 : (want + 1 < L ? want + 1 : L);"),
     "gate_missing": ("x[o] = O[(size_t)row * d + o] / (1.0 + exp(-acc));",
                      "x[o] = O[(size_t)row * d + o];"),
     "gate_slot_ignored": ("const double *w = wgo + (size_t)(row % q) * d * d;",
@@ -527,6 +610,8 @@ def _all_pins(orc):
         "shared_prefix": lambda: _check_shared_prefix(orc, 10) == 0.0,
         "gate_half_saturated": lambda: _check_gate_half_and_saturated(orc, 0) == 0.0,
         "gate_symmetry": lambda: _check_gate_symmetry(orc, 1) < 1e-12,
+        "prefix_sdpa": lambda: all(_check_prefix_sdpa(orc, s_) < 1e-12 for s_ in range(2)),
+        "prefix_truncation": lambda: _check_prefix_truncation(orc, 4) == 0.0,
     }
     for path in GOLDEN_OUTPUT:
         checks["golden:" + os.path.basename(path)] = lambda path=path: _check_gate_golden(orc, path)
