@@ -32,7 +32,7 @@ CONFIGS = ("rest", "long", "transx", "ragged", "tiny")
 _ATTN_SRC = ["shared_history_candidate_amd/csrc/attn_bf16.hip",
              "shared_history_candidate_amd/csrc/plan_wave.h",
              "shared_history_candidate_amd/csrc/common.h"]
-KERNEL_SOURCES = {"fused": _ATTN_SRC, "attention": _ATTN_SRC,
+KERNEL_SOURCES = {"fused": _ATTN_SRC, "attention": _ATTN_SRC, "prefix": _ATTN_SRC,
                   "output": ["shared_history_candidate_amd/csrc/gemm_bf16.hip",
                              "shared_history_candidate_amd/csrc/common.h"],
                   "projection": ["shared_history_candidate_amd/csrc/gemm_bf16.hip",
@@ -50,9 +50,10 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--stage", default="attention", choices=("attention", "output"),
+    p.add_argument("--stage", default="attention", choices=("attention", "output", "prefix"),
                    help="attention: the hot path (xattn_forward, the default); output: the "
-                        "gate and output projection of Eq. (7) alone (xattn_output)")
+                        "gate and output projection of Eq. (7) alone (xattn_output); prefix: "
+                        "the forward with per-candidate prefix lengths (xattn_forward_prefix)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="run only a plain device copy of this many MiB (counter calibration)")
     p.add_argument("--ingest-counters", metavar="DIR",
@@ -108,13 +109,18 @@ def kernel_sha(kernel):
     return h.hexdigest()[:16]
 
 
-# Kernel names (regular expressions over the mangled names) of the three
-# kernels a step can run: the single launch of a small batch (attention kernel
-# that projects its own queries: last template flag 1), or the projection
-# GEMM and the attention kernel over its output (flag 0).
+# Kernel names (regular expressions over the demangled or mangled names) of
+# the kernels a step can run: the single launch of a small batch (attention
+# kernel that projects its own queries: flags PROJ=1, CUT=0), or the
+# projection GEMM and the attention kernel over its output (PROJ=0; CUT=1
+# with per-candidate prefix lengths).
 KERNEL_NAMES = {
-    "fused": r"attn_bf16_kernel(<\d+, \d+, \d+, \w+, true>|ILi\d+ELi\d+ELi\d+ELb[01]ELb1E)",
-    "attention": r"attn_bf16_kernel(<\d+, \d+, \d+, \w+, false>|ILi\d+ELi\d+ELi\d+ELb[01]ELb0E)",
+    "fused": r"attn_bf16_kernel(<\d+, \d+, \d+, \w+, true, false>|"
+             r"ILi\d+ELi\d+ELi\d+ELb[01]ELb1ELb0E)",
+    "attention": r"attn_bf16_kernel(<\d+, \d+, \d+, \w+, false, false>|"
+                 r"ILi\d+ELi\d+ELi\d+ELb[01]ELb0ELb0E)",
+    "prefix": r"attn_bf16_kernel(<\d+, \d+, \d+, \w+, false, true>|"
+              r"ILi\d+ELi\d+ELi\d+ELb[01]ELb0ELb1E)",
     "projection": r"prep_kernel"}
 
 
@@ -191,13 +197,15 @@ def roofline(flops, nbytes, ms, dtype):
 def cpu_baseline(wl, target_s, stage="attention", seed=0):
     """The fp64 oracle as it stands, timed on this host on a bounded sample of
     the workload's query rows (grown until it takes about target_s).  For the
-    output stage the sample is whole candidates (all their query slots)."""
+    output stage the sample is whole candidates (all their query slots); the
+    prefix stage runs the oracle with the same prefix lengths as the GPU."""
     import numpy as np
     import oracle
     from shared_history_candidate_amd import workloads as W
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     oracle.set_threads(threads)
     rng = np.random.default_rng(1)
+    kv_len = W.prefix_lengths(wl, seed + 3, out_of_range=False) if stage == "prefix" else None
     if stage == "output":
         wgo, wo = W.output_weights(wl, seed + 1)
         O_in = W.attention_like(wl, seed + 2)
@@ -212,7 +220,7 @@ def cpu_baseline(wl, target_s, stage="attention", seed=0):
             n = len(c) * wl.q
         else:
             oracle.forward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, wl.K, wl.V,
-                           rows=rows)
+                           rows=rows, kv_len=kv_len)
         dt = time.perf_counter() - t0
         done += n
         elapsed += dt
@@ -291,6 +299,14 @@ def main():
 
         def step():
             ctx.output(t["Z"], Wgo_d, O_in, Wo_d, ws, Y=O, stream=stream)
+    elif args.stage == "prefix":
+        # per-candidate prefix lengths: sorted draws from U{0..L_r} per request
+        kv_len = W.prefix_lengths(wl, args.seed + 3, out_of_range=False)
+        cl = torch.from_numpy(kv_len).to("cuda")
+
+        def step():
+            ctx.forward(t["Z"], t["W_Q"], t["K"], t["V"], t["cu_kv"], t["cu_cand"], wl.heads,
+                        O=O, workspace=ws, stream=stream, cand_kv_len=cl)
     else:
         def step():
             ctx.forward(t["Z"], t["W_Q"], t["K"], t["V"], t["cu_kv"], t["cu_cand"], wl.heads,
@@ -328,7 +344,7 @@ def main():
         return a.elapsed_time(b) / args.steps
 
     launches = ctx.forward_launches(wl.R, wl.total_cand, wl.total_kv, wl.heads)
-    if args.stage == "output":
+    if args.stage != "attention":
         launches = 0
 
     def entry(kernel, flops, nbytes, ms):
@@ -350,14 +366,18 @@ def main():
         roof = entry("fused", wl.flops(), wl.bytes(), fused_ms)
         roof["other_kernel"] = None
     else:
+        cut = cl if args.stage == "prefix" else None
+        kv_arg = kv_len if args.stage == "prefix" else None
+        attn_name = "prefix" if args.stage == "prefix" else "attention"
         proj_ms = per_launch_ms(lambda: ctx.project(t["Z"], t["W_Q"], Q=Qbuf, stream=stream))
         attn_ms = per_launch_ms(lambda: ctx.attend_q(Qbuf, t["K"], t["V"], t["cu_kv"],
                                                      t["cu_cand"], wl.heads, ws, O=O,
-                                                     stream=stream))
+                                                     stream=stream, cand_kv_len=cut))
         print("bench: projection %.4f ms, attention %.4f ms per launch" % (proj_ms, attn_ms),
               file=sys.stderr, flush=True)
         kernels = {
-            "attention": entry("attention", wl.flops_attention(), wl.bytes_attention(), attn_ms),
+            "attention": entry(attn_name, wl.flops_attention(kv_arg), wl.bytes_attention(kv_arg),
+                               attn_ms),
             "projection": entry("projection", wl.flops_projection(), wl.bytes_projection(),
                                 proj_ms),
         }
@@ -379,8 +399,10 @@ def main():
         "config": {"workload": wl.name, "requests": wl.R, "candidates": wl.total_cand,
                    "query_tokens": wl.q, "memory_rows": wl.total_kv, "d": wl.d,
                    "heads": wl.heads, "kv_mode": wl.kv_mode, "seed": args.seed,
-                   "stage": "forward (attention path)" if args.stage == "attention"
-                   else "output gate and projection"},
+                   "stage": {"attention": "forward (attention path)",
+                             "output": "output gate and projection",
+                             "prefix": "forward with per-candidate prefix lengths "
+                                       "(sorted U{0..L_r} per request)"}[args.stage]},
         "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -46,7 +46,8 @@
  *   - A request with L_r = 0 gets all-zero output rows (the pages route users
  *     without memory to a fallback model; zero is this library's convention).
  *     A request with N_r = 0 produces no rows.  No mask: every query row
- *     attends to all L_r rows of its request.
+ *     attends to all L_r rows of its request (xattn_forward_prefix limits
+ *     each candidate to a prefix of them).
  *   - Precision: XATTN_BF16 multiplies bf16 operands into fp32 accumulators
  *     on the matrix cores; Q is rounded to bf16 after the projection and once
  *     more after scaling by log2(e)/sqrt(d_h) (the softmax scale folded into
@@ -146,6 +147,29 @@ xattn_status xattn_forward(xattn_ctx* ctx,
                            void* O, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* xattn_forward with a per-candidate memory prefix (ReST reading note, s.3.5:
+ * under the unified-long-term reading every training sample of a user sees
+ * only the part of that user's sequence that precedes it, so the candidates
+ * of one request may see different prefixes of the shared memory).
+ *   - cand_kv_len [total_cand] int32, device: candidate c of request r
+ *     attends to memory rows [cu_seqlens_kv[r], cu_seqlens_kv[r] + n) with
+ *     n = cand_kv_len[c] clamped to [0, L_r]; every slot of the candidate
+ *     uses the same n.  A candidate with n = 0 gets all-zero output rows.
+ * Always two launches in bf16 (projection GEMM with the planner, then the
+ * attention kernel with the per-row mask), three in fp32.  Other arguments,
+ * workspace and errors as for xattn_forward; a NULL cand_kv_len with
+ * total_cand > 0 is XATTN_EINVAL.  With every cand_kv_len[c] >= L_r the
+ * result equals xattn_forward's. */
+xattn_status xattn_forward_prefix(xattn_ctx* ctx,
+                                  const void* Z, const void* W_Q,
+                                  const void* K, const void* V,
+                                  const int32_t* cu_seqlens_kv, const int32_t* cu_cand,
+                                  const int32_t* cand_kv_len,
+                                  int32_t num_requests, int32_t total_cand,
+                                  int32_t total_kv, int32_t heads,
+                                  void* O, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
 /* Projection and attention without re-planning (one kernel where
  * xattn_forward would run one): like xattn_forward, but the plan is read
  * from `workspace`, where a previous xattn_plan or xattn_forward call left it
@@ -177,6 +201,22 @@ xattn_status xattn_attend_q(xattn_ctx* ctx, const void* Q,
                             int32_t total_kv, int32_t heads,
                             void* O, void* workspace, size_t workspace_bytes,
                             void* stream);
+
+/* xattn_attend_q with the per-candidate memory prefix of
+ * xattn_forward_prefix: attention over caller-projected queries Q, the plan
+ * read from `workspace` (left there by xattn_forward_prefix, xattn_forward or
+ * xattn_plan for the same batch), candidate c limited to the first
+ * cand_kv_len[c] memory rows of its request (clamped to [0, L_r]).  Errors as
+ * for xattn_attend_q; a NULL cand_kv_len with total_cand > 0 is
+ * XATTN_EINVAL. */
+xattn_status xattn_attend_q_prefix(xattn_ctx* ctx, const void* Q,
+                                   const void* K, const void* V,
+                                   const int32_t* cu_seqlens_kv, const int32_t* cu_cand,
+                                   const int32_t* cand_kv_len,
+                                   int32_t num_requests, int32_t total_cand,
+                                   int32_t total_kv, int32_t heads,
+                                   void* O, void* workspace, size_t workspace_bytes,
+                                   void* stream);
 
 /* Varlen plan alone (integer outputs, for callers that want the row map and
  * for tests).  Writes, on the device:

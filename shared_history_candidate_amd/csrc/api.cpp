@@ -238,13 +238,15 @@ namespace {
 enum class Mode { kForward, kAttend, kAttendQ };
 
 // Shared body of xattn_forward (plan + projection + attention), xattn_attend
-// (projection + attention over the plan in the workspace) and xattn_attend_q
-// (attention over caller-projected queries and the plan in the workspace).
+// (projection + attention over the plan in the workspace), xattn_attend_q
+// (attention over caller-projected queries and the plan in the workspace) and
+// xattn_forward_prefix (xattn_forward with a per-candidate memory prefix,
+// cand_len not NULL).
 xattn_status run_forward(Mode mode, xattn_ctx* ctx, const void* Z, const void* W_Q, const void* Qin,
                          const void* K, const void* V, const int32_t* cu_kv,
                          const int32_t* cu_cand, int32_t R, int32_t total_cand, int32_t total_kv,
                          int32_t heads, void* O, void* workspace, size_t workspace_bytes_,
-                         void* stream) {
+                         void* stream, const int32_t* cand_len = nullptr) {
     g_last_error.clear();
     xattn_status st = check_shape(ctx, R, total_cand, total_kv, heads);
     if (st != XATTN_OK) return st;
@@ -295,8 +297,10 @@ xattn_status run_forward(Mode mode, xattn_ctx* ctx, const void* Z, const void* W
         a.d = c.d_model;
         a.heads = heads;
         a.O = O;
+        a.cand_len = cand_len;
+        // the prefix cutoff runs over projected queries in the workspace
         const bool fused_proj =
-            fused_shape(c, R) &&
+            !cand_len && fused_shape(c, R) &&
             xattn::attn_bf16_variant_smem(c.d_model / heads, var.rb, var.ksplit,
                                           c.kv_mode == XATTN_KV_SEPARATE, true) > 0;
         if (mode == Mode::kAttendQ) {
@@ -333,7 +337,7 @@ xattn_status run_forward(Mode mode, xattn_ctx* ctx, const void* Z, const void* W
         e = xattn::launch_attn_f32(static_cast<const float*>(Qp), static_cast<const float*>(K),
                                    c.kv_mode == XATTN_KV_SEPARATE ? static_cast<const float*>(V)
                                                                   : nullptr,
-                                   workspace, max_tiles, c.n_slots, c.d_model, heads,
+                                   workspace, cand_len, max_tiles, c.n_slots, c.d_model, heads,
                                    static_cast<float*>(O), s);
     }
     if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
@@ -350,6 +354,19 @@ xattn_status xattn_forward(xattn_ctx* ctx, const void* Z, const void* W_Q, const
                        total_kv, heads, O, workspace, workspace_bytes_, stream);
 }
 
+xattn_status xattn_forward_prefix(xattn_ctx* ctx, const void* Z, const void* W_Q, const void* K,
+                                  const void* V, const int32_t* cu_kv, const int32_t* cu_cand,
+                                  const int32_t* cand_kv_len, int32_t R, int32_t total_cand,
+                                  int32_t total_kv, int32_t heads, void* O, void* workspace,
+                                  size_t workspace_bytes_, void* stream) {
+    if (ctx && total_cand > 0 && !cand_kv_len) {
+        g_last_error.clear();
+        return fail(XATTN_EINVAL, "NULL cand_kv_len");
+    }
+    return run_forward(Mode::kForward, ctx, Z, W_Q, nullptr, K, V, cu_kv, cu_cand, R, total_cand,
+                       total_kv, heads, O, workspace, workspace_bytes_, stream, cand_kv_len);
+}
+
 xattn_status xattn_attend(xattn_ctx* ctx, const void* Z, const void* W_Q, const void* K,
                           const void* V, const int32_t* cu_kv, const int32_t* cu_cand,
                           int32_t R, int32_t total_cand, int32_t total_kv, int32_t heads,
@@ -364,6 +381,20 @@ xattn_status xattn_attend_q(xattn_ctx* ctx, const void* Q, const void* K, const 
                             void* workspace, size_t workspace_bytes_, void* stream) {
     return run_forward(Mode::kAttendQ, ctx, nullptr, nullptr, Q, K, V, cu_kv, cu_cand, R,
                        total_cand, total_kv, heads, O, workspace, workspace_bytes_, stream);
+}
+
+xattn_status xattn_attend_q_prefix(xattn_ctx* ctx, const void* Q, const void* K, const void* V,
+                                   const int32_t* cu_kv, const int32_t* cu_cand,
+                                   const int32_t* cand_kv_len, int32_t R, int32_t total_cand,
+                                   int32_t total_kv, int32_t heads, void* O, void* workspace,
+                                   size_t workspace_bytes_, void* stream) {
+    if (ctx && total_cand > 0 && !cand_kv_len) {
+        g_last_error.clear();
+        return fail(XATTN_EINVAL, "NULL cand_kv_len");
+    }
+    return run_forward(Mode::kAttendQ, ctx, nullptr, nullptr, Q, K, V, cu_kv, cu_cand, R,
+                       total_cand, total_kv, heads, O, workspace, workspace_bytes_, stream,
+                       cand_kv_len);
 }
 
 xattn_status xattn_project(xattn_ctx* ctx, const void* Z, const void* W_Q, int32_t total_cand,

@@ -51,7 +51,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // Widest model the fused projection stages in LDS.
 constexpr int kProjMaxD = kAttnProjMaxD;
 
-template <int DH, int RB, int KSPLIT, bool SEP, bool PROJ>
+template <int DH, int RB, int KSPLIT, bool SEP, bool PROJ, bool CUT = false>
 struct Cfg {
     static constexpr int NW = RB * KSPLIT;
     static constexpr int NT = 64 * NW;
@@ -96,9 +96,9 @@ struct Cfg {
     static constexpr int P = STAGE_REGS >= 8 ? 1 : (8 / STAGE_REGS >= 4 ? 4 : 8 / STAGE_REGS);
 };
 
-template <int DH, int RB, int KSPLIT, bool SEP, bool PROJ>
+template <int DH, int RB, int KSPLIT, bool SEP, bool PROJ, bool CUT>
 __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(AttnArgs a) {
-    using C = Cfg<DH, RB, KSPLIT, SEP, PROJ>;
+    using C = Cfg<DH, RB, KSPLIT, SEP, PROJ, CUT>;
     constexpr int P = C::P;
     __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
     const int q = a.q, d = a.d, heads = a.heads;
@@ -147,8 +147,31 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(AttnArgs a)
     const int cand = c0 + qcol;
     const int gt = tid - ksg * 64 * RB;       // thread index inside the split group
 
+    // Per-candidate prefix cutoff (CUT; ReST reading note s.3.5, ULT): the
+    // lane's query row sees memory rows [0, cut) of its request.  The tile
+    // loop runs to the work-group's largest cutoff (every wave computes it
+    // from all nc candidates, so all waves agree); rows past a lane's own
+    // cutoff are masked.  wmin is this wave's smallest cutoff: tiles below it
+    // need no mask.
+    int cut = L, L_loop = L, wmin = L;
+    if constexpr (CUT) {
+        const int* __restrict__ cl = a.cand_len;
+        auto clampL = [&](int v) { return v < 0 ? 0 : (v < L ? v : L); };
+        cut = qvalid ? clampL(cl[cand]) : L;
+        int mx = 0;
+        for (int i = lane; i < nc; i += 64) mx = max(mx, clampL(cl[c0 + i]));
+        int mn = cut;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            mx = max(mx, __shfl_xor(mx, off, 64));
+            mn = min(mn, __shfl_xor(mn, off, 64));
+        }
+        L_loop = __builtin_amdgcn_readfirstlane(mx);
+        wmin = __builtin_amdgcn_readfirstlane(mn);
+    }
+
     // ---------------- 1. memory prefetch and this wave's Q_h^T operands ----------------
-    const int ntiles_kv = (L + BN - 1) / BN;
+    const int ntiles_kv = (L_loop + BN - 1) / BN;
     const int n_iter = (ntiles_kv + KSPLIT - 1) / KSPLIT;
     const bf16* Kh = K + (size_t)kv0 * d + h * DH;
     const bf16* Vh = SEP ? V + (size_t)kv0 * d + h * DH : nullptr;
@@ -169,7 +192,7 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(AttnArgs a)
     uint4 vreg[P][SEP ? C::KV_CPT : 1];
     auto gload = [&](int t, uint4 (&kr)[C::KV_CPT], uint4 (&vr)[SEP ? C::KV_CPT : 1]) {
         const int row0 = t * BN;
-        const int left = L - row0;   // memory rows of the request from this tile on
+        const int left = L_loop - row0;   // memory rows still read from this tile on
         const size_t nb = left > 0 ? (size_t)left * d * 2 : 0;
         const uint32_t bytes = nb > 0xFFFFFFF0u ? 0xFFFFFFF0u : (uint32_t)nb;
         const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
@@ -366,11 +389,12 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(AttnArgs a)
                 const bf16* base = vb + (16 * u + tr_row) * C::LDK + eb * 32 + tr_col;
                 vf[u][eb] = cat(lds_read_tr16(base), lds_read_tr16(base + 8 * C::LDK));
             }
-        const int jleft = L - t * BN;
-        // Only the request's last tile is partial.  The opaque copy keeps the
-        // compiler from folding the tile-level test into the per-score tests
-        // (which would then run on every tile).
-        int jl = jleft;
+        // Only the request's last tile is partial (with cutoffs: tiles past
+        // the wave's smallest cutoff).  The opaque copy keeps the compiler
+        // from folding the tile-level test into the per-score tests (which
+        // would then run on every tile).
+        const int jleft = (CUT ? cut : L) - t * BN;   // this lane's visible rows in the tile
+        int jl = (CUT ? wmin : L) - t * BN;
         asm volatile("" : "+s"(jl));
         if (jl < BN) {
 #pragma unroll
@@ -408,23 +432,31 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(AttnArgs a)
         // them).  Weights up to kSumCap are as exact in the fp32 sums and as
         // well represented as bf16 operands as weights <= 1, and the final
         // normalisation divides the common factor out.
+        // With cutoffs a lane may leave the first tile with maximum -inf
+        // (no visible row); its weights then stay zero: its visible rows
+        // are a prefix of the memory, so a split whose first tile shows it
+        // nothing shows it nothing later either.
         if (!started || __any(lt > kSumCap)) {
-            const float m_seed = started ? m_run : 0.f;   // what the scores are relative to
+            // what the scores are relative to (with cutoffs a lane may have
+            // seen no visible row yet: its maximum is still -inf, its seed 0)
+            const float m_seed = CUT ? (m_run == -INFINITY ? 0.f : m_run) : (started ? m_run : 0.f);
             float mt = fmaxf(sacc[0][0], sacc[0][1]);
 #pragma unroll
             for (int rr = 2; rr < 16; rr += 2) mt = fmaxf(mt, fmaxf(sacc[0][rr], sacc[0][rr + 1]));
 #pragma unroll
             for (int rr = 0; rr < 16; rr += 2) mt = fmaxf(mt, fmaxf(sacc[1][rr], sacc[1][rr + 1]));
             const float m_new = fmaxf(m_run, m_seed + fmaxf(mt, xor32(mt)));
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            // a lane without a visible row so far keeps m = -inf and zero weights
+            const bool none = CUT && m_new == -INFINITY;
+            const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
             m_run = m_new;
             l_run *= alpha;
 #pragma unroll
             for (int eb = 0; eb < C::EB; ++eb) oacc[eb] *= alpha;
-            lt = weights(std::true_type{}, m_seed - m_new);
+            lt = weights(std::true_type{}, none ? -INFINITY : m_seed - m_new);
             started = true;
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) negm[rr] = -m_new;
+            for (int rr = 0; rr < 16; ++rr) negm[rr] = none ? 0.f : -m_new;
         }
         l_run += lt;
         // O^T += V^T P^T over the four 16-key slabs of the tile
@@ -533,8 +565,18 @@ hipError_t launch_one(const AttnArgs& a, hipStream_t stream) {
         k.scale_log2 = 1.4426950408889634f / sqrtf((float)DH);
         const int64_t blocks = a.max_tiles * a.heads;
         if (blocks <= 0) return hipSuccess;
-        hipLaunchKernelGGL((attn_bf16_kernel<DH, RB, KSPLIT, SEP, PROJ>), dim3((unsigned)blocks),
-                           dim3(64 * RB * KSPLIT), 0, stream, k);
+        if (a.cand_len) {
+            // cutoffs run over caller-projected queries only
+            if constexpr (PROJ) {
+                return hipErrorInvalidValue;
+            } else {
+                hipLaunchKernelGGL((attn_bf16_kernel<DH, RB, KSPLIT, SEP, false, true>),
+                                   dim3((unsigned)blocks), dim3(64 * RB * KSPLIT), 0, stream, k);
+            }
+        } else {
+            hipLaunchKernelGGL((attn_bf16_kernel<DH, RB, KSPLIT, SEP, PROJ, false>),
+                               dim3((unsigned)blocks), dim3(64 * RB * KSPLIT), 0, stream, k);
+        }
         return hipGetLastError();
     }
 }

@@ -20,8 +20,8 @@ constexpr int kBN = 32;    // memory rows per tile
 template <int DHMAX>
 __global__ __launch_bounds__(kRows) void attn_f32_kernel(
     const float* __restrict__ Qp, const float* __restrict__ K, const float* __restrict__ V,
-    const int* __restrict__ ws, int q, int d, int heads, float scale_log2,
-    float* __restrict__ O) {
+    const int* __restrict__ ws, const int* __restrict__ cand_len, int q, int d, int heads,
+    float scale_log2, float* __restrict__ O) {
     __shared__ float ks[kBN][DHMAX];
     __shared__ float vs[kBN][DHMAX];
     const int dh = d / heads;
@@ -36,6 +36,12 @@ __global__ __launch_bounds__(kRows) void attn_f32_kernel(
     const int i = threadIdx.x;
     const bool valid = i < nc;
     const int cand = c0 + i;
+    // per-candidate prefix cutoff: this row sees memory rows [0, Lc)
+    int Lc = L;
+    if (cand_len && valid) {
+        const int want = cand_len[cand];
+        Lc = want < 0 ? 0 : (want < L ? want : L);
+    }
 
     // this thread's projected query (head slice)
     float qv[DHMAX];
@@ -69,10 +75,11 @@ __global__ __launch_bounds__(kRows) void attn_f32_kernel(
             float a = 0.f;
 #pragma unroll
             for (int e = 0; e < DHMAX; ++e) a = fmaf(qv[e], ks[j][e], a);
-            sc[j] = j < nj ? a : -INFINITY;
+            sc[j] = (j < nj && j0 + j < Lc) ? a : -INFINITY;
             mt = fmaxf(mt, sc[j]);
         }
         const float m_new = fmaxf(m_run, mt);
+        if (m_new == -INFINITY) continue;   // no visible row yet
         const float alpha = exp2f((m_run - m_new) * scale_log2);
         const float mb = m_new * scale_log2;
         l_run *= alpha;
@@ -128,28 +135,29 @@ __global__ void gate_f32_kernel(const float* __restrict__ Z, const float* __rest
 
 template <int DHMAX>
 hipError_t launch_f32(const float* Qp, const float* K, const float* V,
-                      const void* ws, int64_t max_tiles, int q, int d,
-                      int heads, float* O, hipStream_t stream) {
+                      const void* ws, const int* cand_len, int64_t max_tiles, int q,
+                      int d, int heads, float* O, hipStream_t stream) {
     const int dh = d / heads;
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)dh);
     const int64_t blocks = max_tiles * heads;
     if (blocks <= 0) return hipSuccess;
     hipLaunchKernelGGL((attn_f32_kernel<DHMAX>), dim3((unsigned)blocks), dim3(kRows), 0, stream,
-                       Qp, K, V, static_cast<const int*>(ws), q, d, heads, scale_log2, O);
+                       Qp, K, V, static_cast<const int*>(ws), cand_len, q, d, heads, scale_log2,
+                       O);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_f32(const float* Qp, const float* K, const float* V,
-                           const void* ws, int64_t max_tiles, int q, int d,
-                           int heads, float* O, hipStream_t stream) {
+                           const void* ws, const int* cand_len, int64_t max_tiles, int q,
+                           int d, int heads, float* O, hipStream_t stream) {
     const int dh = d / heads;
-    if (dh <= 8) return launch_f32<8>(Qp, K, V, ws, max_tiles, q, d, heads, O, stream);
-    if (dh <= 16) return launch_f32<16>(Qp, K, V, ws, max_tiles, q, d, heads, O, stream);
-    if (dh <= 32) return launch_f32<32>(Qp, K, V, ws, max_tiles, q, d, heads, O, stream);
-    if (dh <= 64) return launch_f32<64>(Qp, K, V, ws, max_tiles, q, d, heads, O, stream);
-    if (dh <= 128) return launch_f32<128>(Qp, K, V, ws, max_tiles, q, d, heads, O, stream);
+    if (dh <= 8) return launch_f32<8>(Qp, K, V, ws, cand_len, max_tiles, q, d, heads, O, stream);
+    if (dh <= 16) return launch_f32<16>(Qp, K, V, ws, cand_len, max_tiles, q, d, heads, O, stream);
+    if (dh <= 32) return launch_f32<32>(Qp, K, V, ws, cand_len, max_tiles, q, d, heads, O, stream);
+    if (dh <= 64) return launch_f32<64>(Qp, K, V, ws, cand_len, max_tiles, q, d, heads, O, stream);
+    if (dh <= 128) return launch_f32<128>(Qp, K, V, ws, cand_len, max_tiles, q, d, heads, O, stream);
     return hipErrorInvalidValue;
 }
 

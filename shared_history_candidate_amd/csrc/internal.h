@@ -26,6 +26,7 @@ struct AttnArgs {
     void* ws;
     const int* cu_kv;
     const int* cu_cand;
+    const int* cand_len;   // per-candidate prefix cutoff, or NULL (Qp path only)
     int64_t max_tiles;
     int R, total_cand, total_kv, inplan, q, d, heads;
     float scale_log2;   // set by the launcher
@@ -51,9 +52,11 @@ hipError_t launch_gate_output_bf16(const void* Z, const void* Wgo, const void* O
                                    int total_cand, int q, int d, void* X, void* Y,
                                    hipStream_t stream);
 
-// fp32 path (tile_m = 64): attention over projected queries, projection.
-hipError_t launch_attn_f32(const float* Qp, const float* K, const float* V, const void* ws, int64_t max_tiles, int q, int d, int heads, float* O,
-                           hipStream_t stream);
+// fp32 path (tile_m = 64): attention over projected queries (cand_len: the
+// per-candidate prefix cutoff, or NULL), projection.
+hipError_t launch_attn_f32(const float* Qp, const float* K, const float* V, const void* ws,
+                           const int* cand_len, int64_t max_tiles, int q, int d, int heads,
+                           float* O, hipStream_t stream);
 
 hipError_t launch_project_f32(const float* Z, const float* Wq, int total_cand, int q, int d,
                               float* Q, hipStream_t stream);

@@ -33,7 +33,7 @@ from typing import Optional, Sequence
 import numpy as np
 
 __all__ = ["Workload", "CONFIGS", "make", "custom", "round_bf16", "output_weights",
-           "attention_like"]
+           "attention_like", "prefix_lengths"]
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
@@ -111,10 +111,18 @@ class Workload:
         b = 2 if self.dtype == "bf16" else 4
         return float(b * (2 * self.rows * self.d + self.q * self.d * self.d))
 
-    def flops_attention(self) -> float:
-        """FLOPs of QK^T and PV: 4 * sum_r M_r * L_r * d."""
+    def flops_attention(self, kv_len: Optional[np.ndarray] = None) -> float:
+        """FLOPs of QK^T and PV: 4 * sum_r M_r * L_r * d; with per-candidate
+        prefix lengths, 4 * q * d * sum_c clamp(kv_len[c], 0, L_r)."""
+        if kv_len is not None:
+            return 4.0 * self.q * self.d * float(np.sum(self._visible(kv_len)))
         m = self.cands.astype(np.float64) * self.q
         return 4.0 * float(np.sum(m * self.lengths)) * self.d
+
+    def _visible(self, kv_len: np.ndarray) -> np.ndarray:
+        """Memory rows each candidate sees under a prefix length."""
+        L = np.repeat(self.lengths, self.cands)
+        return np.clip(np.asarray(kv_len, dtype=np.int64), 0, L)
 
     def flops_output(self) -> float:
         """FLOPs of the gate and output projections of Eq. (7): 4 * rows * d * d."""
@@ -125,11 +133,20 @@ class Workload:
         b = 2 if self.dtype == "bf16" else 4
         return float(b * (3 * self.rows * self.d + (self.q + 1) * self.d * self.d))
 
-    def bytes_attention(self) -> float:
-        """Bytes the attention over projected queries must move: K (and V), Q, O."""
+    def bytes_attention(self, kv_len: Optional[np.ndarray] = None) -> float:
+        """Bytes the attention over projected queries must move: K (and V), Q, O.
+        With per-candidate prefix lengths only the rows some candidate of the
+        request sees (the longest prefix) count, plus the lengths themselves."""
         b = 2 if self.dtype == "bf16" else 4
-        kv = (1 if self.kv_mode == "shared" else 2) * self.total_kv * self.d
-        return float(b * (kv + 2 * self.rows * self.d))
+        rows_kv = self.total_kv
+        extra = 0
+        if kv_len is not None:
+            vis = self._visible(kv_len)
+            rows_kv = sum(int(vis[a:c].max()) if c > a else 0
+                          for a, c in zip(self.cu_cand[:-1], self.cu_cand[1:]))
+            extra = 4 * self.total_cand
+        kv = (1 if self.kv_mode == "shared" else 2) * rows_kv * self.d
+        return float(b * (kv + 2 * self.rows * self.d) + extra)
 
 
 def _normal(rng, shape, std=1.0):
@@ -239,6 +256,28 @@ def attention_like(wl: Workload, seed: int = 0, std: float = 0.5) -> np.ndarray:
     rng = np.random.default_rng(seed)
     O = _normal(rng, (wl.total_cand, wl.q, wl.d), std=std)
     return round_bf16(O) if wl.dtype == "bf16" else O
+
+
+def prefix_lengths(wl: Workload, seed: int = 0, out_of_range: bool = True) -> np.ndarray:
+    """Per-candidate memory prefix lengths [total_cand] int32 for the prefix
+    cutoff (ReST reading note s.3.5, ULT: the samples of one user are ordered
+    in time and each sees the part of the history before it).  Request r's
+    candidates get sorted draws from U{0..L_r}; with out_of_range, about one
+    in eight is replaced by a value below 0 or above L_r, which the method
+    clamps.  Drawn from default_rng(seed), request by request."""
+    rng = np.random.default_rng(seed)
+    out = np.zeros(wl.total_cand, dtype=np.int32)
+    for r in range(wl.R):
+        a, b = int(wl.cu_cand[r]), int(wl.cu_cand[r + 1])
+        L = int(wl.lengths[r])
+        v = np.sort(rng.integers(0, L + 1, size=b - a))
+        if out_of_range and b > a:
+            hit = rng.random(b - a) < 0.125
+            wild = np.where(rng.random(b - a) < 0.5, -rng.integers(1, 5, size=b - a),
+                            L + rng.integers(1, 100, size=b - a))
+            v = np.where(hit, wild, v)
+        out[a:b] = v
+    return out
 
 
 CONFIGS = {

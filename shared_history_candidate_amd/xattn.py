@@ -25,7 +25,7 @@ XATTN_KV_SHARED, XATTN_KV_SEPARATE = 0, 1
 EXPORTED = ("xattn_create", "xattn_destroy", "xattn_workspace_size", "xattn_forward",
             "xattn_attend", "xattn_attend_q", "xattn_plan", "xattn_max_tiles",
             "xattn_forward_launches", "xattn_project", "xattn_output", "xattn_device_error",
-            "xattn_last_error")
+            "xattn_last_error", "xattn_forward_prefix", "xattn_attend_q_prefix")
 
 
 class Config(ctypes.Structure):
@@ -64,10 +64,15 @@ def lib():
         L.xattn_forward_launches.restype = I32
         L.xattn_forward.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, P, P, SZ, P]
         L.xattn_forward.restype = ctypes.c_int
+        L.xattn_forward_prefix.argtypes = [P, P, P, P, P, P, P, P, I32, I32, I32, I32, P, P, SZ,
+                                           P]
+        L.xattn_forward_prefix.restype = ctypes.c_int
         L.xattn_attend.argtypes = L.xattn_forward.argtypes
         L.xattn_attend.restype = ctypes.c_int
         L.xattn_attend_q.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, P, P, SZ, P]
         L.xattn_attend_q.restype = ctypes.c_int
+        L.xattn_attend_q_prefix.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, P, P, SZ, P]
+        L.xattn_attend_q_prefix.restype = ctypes.c_int
         L.xattn_plan.argtypes = [P, P, P, I32, I32, I32, I32, P, P, P, P,
                                  ctypes.POINTER(I32), P, SZ, P]
         L.xattn_plan.restype = ctypes.c_int
@@ -156,10 +161,13 @@ class XAttn:
 
     # -- entry points ----------------------------------------------------------
     def forward(self, Z, W_Q, K, V, cu_seqlens_kv, cu_cand, heads: int, O=None,
-                workspace=None, stream=None, plan: bool = True) -> torch.Tensor:
+                workspace=None, stream=None, plan: bool = True,
+                cand_kv_len=None) -> torch.Tensor:
         """O = cross-attention of Z's query tokens against their requests' memory
         (see include/xattn.h).  Z [total_cand, q, d], W_Q [q, d, d] output-major,
-        K [total_kv, d] (= H), V [total_kv, d] or None, cu_* int32 [R+1]."""
+        K [total_kv, d] (= H), V [total_kv, d] or None, cu_* int32 [R+1].
+        cand_kv_len (int32 [total_cand], optional): candidate c sees only the
+        first cand_kv_len[c] memory rows of its request (xattn_forward_prefix)."""
         d, q, dt = self.d_model, self.q, self.torch_dtype
         total_cand, total_kv = Z.shape[0], K.shape[0]
         R = cu_seqlens_kv.numel() - 1
@@ -177,6 +185,15 @@ class XAttn:
             if not plan:
                 raise ValueError("attend() needs the workspace that holds the batch's plan")
             workspace = self.alloc_workspace(R, total_cand, heads)
+        if cand_kv_len is not None:
+            if not plan:
+                raise ValueError("a per-candidate prefix is only available with planning")
+            self._check_tensor("cand_kv_len", cand_kv_len, torch.int32, (total_cand,))
+            _check(lib().xattn_forward_prefix(
+                self._h, _ptr(Z), _ptr(W_Q), _ptr(K), _ptr(V), _ptr(cu_seqlens_kv),
+                _ptr(cu_cand), _ptr(cand_kv_len), R, total_cand, total_kv, heads, _ptr(O),
+                _ptr(workspace), workspace.numel(), _stream(Z.device, stream)))
+            return O
         fn = lib().xattn_forward if plan else lib().xattn_attend
         _check(fn(self._h, _ptr(Z), _ptr(W_Q), _ptr(K), _ptr(V), _ptr(cu_seqlens_kv),
                   _ptr(cu_cand), R, total_cand, total_kv, heads, _ptr(O), _ptr(workspace),
@@ -191,9 +208,10 @@ class XAttn:
                             workspace=workspace, stream=stream, plan=False)
 
     def attend_q(self, Q, K, V, cu_seqlens_kv, cu_cand, heads: int, workspace, O=None,
-                 stream=None) -> torch.Tensor:
+                 stream=None, cand_kv_len=None) -> torch.Tensor:
         """Attention kernel alone over already-projected queries Q [total_cand, q, d],
-        reusing the plan in `workspace`."""
+        reusing the plan in `workspace`; cand_kv_len as for forward()
+        (xattn_attend_q_prefix)."""
         d, q, dt = self.d_model, self.q, self.torch_dtype
         total_cand, total_kv = Q.shape[0], K.shape[0]
         R = cu_seqlens_kv.numel() - 1
@@ -206,6 +224,13 @@ class XAttn:
         if O is None:
             O = torch.empty((total_cand, q, d), dtype=dt, device=Q.device)
         self._check_tensor("O", O, dt, (total_cand, q, d))
+        if cand_kv_len is not None:
+            self._check_tensor("cand_kv_len", cand_kv_len, torch.int32, (total_cand,))
+            _check(lib().xattn_attend_q_prefix(
+                self._h, _ptr(Q), _ptr(K), _ptr(V), _ptr(cu_seqlens_kv), _ptr(cu_cand),
+                _ptr(cand_kv_len), R, total_cand, total_kv, heads, _ptr(O), _ptr(workspace),
+                workspace.numel(), _stream(Q.device, stream)))
+            return O
         _check(lib().xattn_attend_q(self._h, _ptr(Q), _ptr(K), _ptr(V), _ptr(cu_seqlens_kv),
                                     _ptr(cu_cand), R, total_cand, total_kv, heads, _ptr(O),
                                     _ptr(workspace), workspace.numel(),

@@ -196,3 +196,38 @@ def test_output_host_validation(L):
     assert out(wsb=need - 1) == X.XATTN_EWORKSPACE
     assert L.xattn_output(None, FAKE, FAKE, FAKE, FAKE, 10, FAKE, FAKE, need, None) == X.XATTN_EINVAL
     L.xattn_destroy(h)
+
+
+def test_forward_prefix_host_validation(L):
+    st, h = _create(L, 256, 3, X.XATTN_BF16, X.XATTN_KV_SHARED)
+    assert st == 0
+
+    def pre(cl=FAKE, h_=h, Z=FAKE, R=2, tc=10, tkv=20, heads=4, ws=FAKE, wsb=1 << 20):
+        return L.xattn_forward_prefix(h_, Z, FAKE, FAKE, None, FAKE, FAKE, cl, R, tc, tkv,
+                                      heads, FAKE, ws, wsb, None)
+
+    assert pre(cl=None) == X.XATTN_EINVAL                  # cutoffs are required
+    assert "cand_kv_len" in L.xattn_last_error().decode()
+    assert pre(h_=None) == X.XATTN_EINVAL
+    assert pre(Z=None) == X.XATTN_EINVAL
+    assert pre(heads=3) == X.XATTN_EINVAL
+    assert pre(heads=16) == X.XATTN_EUNSUPPORTED
+    assert pre(ws=None) == X.XATTN_EWORKSPACE
+    assert pre(wsb=16) == X.XATTN_EWORKSPACE
+    # empty batch: valid without cutoffs, nothing to launch
+    assert pre(cl=None, R=0, tc=0, tkv=0) == X.XATTN_OK
+    L.xattn_destroy(h)
+
+
+def test_attend_q_prefix_host_validation(L):
+    st, h = _create(L, 256, 3, X.XATTN_BF16, X.XATTN_KV_SHARED)
+    assert st == 0
+
+    def aq(cl=FAKE, Q=FAKE, tc=10):
+        return L.xattn_attend_q_prefix(h, Q, FAKE, None, FAKE, FAKE, cl, 2, tc, 20, 4, FAKE,
+                                       FAKE, 1 << 20, None)
+
+    assert aq(cl=None) == X.XATTN_EINVAL
+    assert aq(Q=None) == X.XATTN_EINVAL
+    assert aq(cl=None, tc=-1) == X.XATTN_EINVAL
+    L.xattn_destroy(h)
