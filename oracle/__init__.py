@@ -48,8 +48,9 @@ def _load():
         lib.oracle_plan.argtypes = [I, P, P, I, I, P, P, P, Lg, P]
         lib.oracle_output.argtypes = [Lg, I, I, P, P, P, P, P]
         lib.oracle_forward_prefix.argtypes = [I, P, P, I, I, I, P, P, P, P, P, P, Lg, P]
+        lib.oracle_backward.argtypes = [I, P, P, I, I, I, P, P, P, P, P, P, P, P, P, P, P]
         for f in (lib.oracle_project, lib.oracle_forward, lib.oracle_probs, lib.oracle_plan,
-                  lib.oracle_output, lib.oracle_forward_prefix):
+                  lib.oracle_output, lib.oracle_forward_prefix, lib.oracle_backward):
             f.restype = I
         _lib = lib
     return _lib
@@ -186,3 +187,35 @@ def plan(cu_kv, cu_cand, q: int, tile_m: int, with_row_req: bool = True):
     if rc != 0:
         raise ValueError("oracle_plan: invalid arguments")
     return cu_q, (row_req[:total_rows] if with_row_req else None), tiles[: n.value]
+
+
+def backward(cu_kv, cu_cand, q: int, heads: int, Z, wt, K, V, dO, kv_len=None) -> dict:
+    """Gradients of <dO, forward(...)> (the backward pass of the cross-attention;
+    ReST reading note s.3.3.1 Eq. (7) with Eq. (8)'s per-slot W_Q, TransX
+    report s.2: candidate gradients summed back into the one memory).
+    Returns dQ, dZ [rows, d], dwt [q, d, d] (output-major like wt), dK
+    [total_kv, d] (the gradient of H, both roles, when V is None) and dV
+    (None when V is None).  kv_len: optional per-candidate prefix cutoff as
+    in forward()."""
+    cu_kv = _i32(cu_kv)
+    cu_cand = _i32(cu_cand)
+    R = len(cu_kv) - 1
+    wt = _f64(wt)
+    d = wt.shape[-1]
+    Z2 = _f64(Z).reshape(-1, d)
+    dO2 = _f64(dO).reshape(-1, d)
+    assert Z2.shape == dO2.shape
+    K2 = _f64(K).reshape(-1, d)
+    V2 = _f64(V).reshape(-1, d) if V is not None else None
+    kl = _i32(kv_len) if kv_len is not None else None
+    if kl is not None:
+        assert kl.shape == (int(cu_cand[-1]),)
+    out = {"dQ": np.empty_like(Z2), "dZ": np.empty_like(Z2), "dwt": np.empty_like(wt),
+           "dK": np.empty_like(K2), "dV": np.empty_like(V2) if V2 is not None else None}
+    rc = _load().oracle_backward(R, _ptr(cu_kv), _ptr(cu_cand), q, d, heads, _ptr(Z2), _ptr(wt),
+                                 _ptr(K2), _ptr(V2), _ptr(kl), _ptr(dO2), _ptr(out["dQ"]),
+                                 _ptr(out["dZ"]), _ptr(out["dwt"]), _ptr(out["dK"]),
+                                 _ptr(out["dV"]))
+    if rc != 0:
+        raise ValueError("oracle_backward: invalid arguments")
+    return out

@@ -380,3 +380,173 @@ int oracle_plan(int R, const int *cu_kv, const int *cu_cand, int q, int tile_m,
     free(taken);
     return ORACLE_OK;
 }
+
+/*
+ * Backward pass of the cross-attention (NEXT-2): the gradients of the scalar
+ * <dO, O(Z, W_Q, K, V)> with respect to Z, W_Q, K and V, where O is
+ * forward_impl's output (same readings, same optional prefix cutoff kv_len).
+ * Under projection-free K/V (V == NULL) the memory H is both key and value,
+ * so its gradient is the sum of both roles; summed over every query row of
+ * the request, this is the TransX report's "candidate gradients sum back into
+ * the one encoding" (section 2, trajectory packing; ReST reading note
+ * section 3.5, ULT).
+ *
+ * Chain rule for one query row i of request r and head h (q_i, k_j, v_j, o_i
+ * the head slices, c = 1/sqrt(d_h), j over the row's visible memory rows):
+ *   s_ij = c <q_i, k_j>,  p_ij = exp(s_ij) / sum_k exp(s_ik),  o_i = sum_j p_ij v_j
+ *   dv_j  += p_ij do_i
+ *   dp_ij  = <do_i, v_j>
+ *   ds_ij  = sum_k dp_ik * (d p_ik / d s_ij) = p_ij (dp_ij - sum_k p_ik dp_ik)
+ *            (softmax Jacobian: d p_ik / d s_ij = p_ik (delta_kj - p_ij))
+ *   dq_i   = c sum_j ds_ij k_j
+ *   dk_j  += c ds_ij q_i
+ * then, through the projection Q[row][o] = sum_i Z[row][i] wt[s][o][i]:
+ *   dZ[row][i]   = sum_o dQ[row][o] wt[row % q][o][i]
+ *   dwt[s][o][i] = sum over rows of slot s of dQ[row][o] Z[row][i]
+ *
+ * Z, dZ, dO, dQ: [total_cand*q][d]; wt, dwt: [q][d][d] (output-major, like
+ * wt); K, dK: [total_kv][d] (dK is dH when V == NULL); V, dV: [total_kv][d]
+ * (dV must be NULL when V is).  dQ may be NULL.  Memory rows no query row
+ * sees get zero gradients.  Accumulation order is fixed (rows ascending), so
+ * the result does not depend on the thread count.
+ */
+int oracle_backward(int R, const int *cu_kv, const int *cu_cand, int q, int d,
+                    int heads, const double *Z, const double *wt, const double *K,
+                    const double *V, const int *kv_len, const double *dO, double *dQ,
+                    double *dZ, double *dwt, double *dK, double *dV)
+{
+    if (R < 0 || q < 1 || d < 1 || heads < 1 || d % heads != 0 || !cu_kv ||
+        !cu_cand || !Z || !wt || !K || !dO || !dZ || !dwt || !dK)
+        return ORACLE_EINVAL;
+    if ((V == NULL) != (dV == NULL))
+        return ORACLE_EINVAL;
+    if (!check_offsets(R, cu_kv) || !check_offsets(R, cu_cand))
+        return ORACLE_EINVAL;
+    const int d_h = d / heads;
+    const double c = 1.0 / sqrt((double)d_h);
+    const double *Vm = V ? V : K;
+    const long total_rows = (long)cu_cand[R] * q;
+    const long total_kv = cu_kv[R];
+    int max_L = 0;
+    for (int r = 0; r < R; ++r)
+        if (cu_kv[r + 1] - cu_kv[r] > max_L)
+            max_L = cu_kv[r + 1] - cu_kv[r];
+
+    double *Q = (double *)malloc(sizeof(double) * (size_t)(total_rows > 0 ? total_rows : 1) * d);
+    double *gQ = dQ ? dQ : (double *)malloc(sizeof(double) * (size_t)(total_rows > 0 ? total_rows : 1) * d);
+    /* key-role and value-role gradients kept apart until the end */
+    double *gK = (double *)calloc((size_t)(total_kv > 0 ? total_kv : 1) * d, sizeof(double));
+    double *gV = (double *)calloc((size_t)(total_kv > 0 ? total_kv : 1) * d, sizeof(double));
+    if (!Q || !gQ || !gK || !gV) {
+        free(Q);
+        if (!dQ)
+            free(gQ);
+        free(gK);
+        free(gV);
+        return ORACLE_EINVAL;
+    }
+    if (oracle_project(total_rows, q, d, Z, wt, Q) != ORACLE_OK) {
+        free(Q);
+        if (!dQ)
+            free(gQ);
+        free(gK);
+        free(gV);
+        return ORACLE_EINVAL;
+    }
+
+    int bad = 0;
+    /* one task per (request, head): it owns that head's columns of the
+     * request's query rows and memory rows, so tasks never share an output */
+#pragma omp parallel
+    {
+        double *p = (double *)malloc(sizeof(double) * (size_t)(max_L > 0 ? max_L : 1));
+        double *dp = (double *)malloc(sizeof(double) * (size_t)(max_L > 0 ? max_L : 1));
+        if (!p || !dp) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic)
+            for (long task = 0; task < (long)R * heads; ++task) {
+                const int r = (int)(task / heads), h = (int)(task % heads);
+                const int kv0 = cu_kv[r], L = cu_kv[r + 1] - cu_kv[r];
+                for (long row = (long)cu_cand[r] * q; row < (long)cu_cand[r + 1] * q; ++row) {
+                    const double *qi = Q + (size_t)row * d + h * d_h;
+                    const double *doi = dO + (size_t)row * d + h * d_h;
+                    double *dqi = gQ + (size_t)row * d + h * d_h;
+                    for (int e = 0; e < d_h; ++e)
+                        dqi[e] = 0.0;
+                    int Lc = L;
+                    if (kv_len) {
+                        const int want = kv_len[row / q];
+                        Lc = want < 0 ? 0 : (want < L ? want : L);
+                    }
+                    if (Lc == 0)
+                        continue;   /* the output row is the constant 0 */
+                    softmax_weights(Q + (size_t)row * d, K, d, d_h, h, kv0, Lc, p);
+                    double pdp = 0.0;
+                    for (int j = 0; j < Lc; ++j) {
+                        const double *vj = Vm + (size_t)(kv0 + j) * d + h * d_h;
+                        double a = 0.0;
+                        for (int e = 0; e < d_h; ++e)
+                            a += doi[e] * vj[e];
+                        dp[j] = a;
+                        pdp += p[j] * a;
+                    }
+                    for (int j = 0; j < Lc; ++j) {
+                        const double ds = p[j] * (dp[j] - pdp);
+                        const double *kj = K + (size_t)(kv0 + j) * d + h * d_h;
+                        double *gkj = gK + (size_t)(kv0 + j) * d + h * d_h;
+                        double *gvj = gV + (size_t)(kv0 + j) * d + h * d_h;
+                        for (int e = 0; e < d_h; ++e) {
+                            dqi[e] += c * ds * kj[e];
+                            gkj[e] += c * ds * qi[e];
+                            gvj[e] += p[j] * doi[e];
+                        }
+                    }
+                }
+            }
+        }
+        free(p);
+        free(dp);
+    }
+
+    /* through the projection */
+#pragma omp parallel for schedule(static)
+    for (long row = 0; row < total_rows; ++row) {
+        const double *w = wt + (size_t)(row % q) * d * d;
+        for (int i = 0; i < d; ++i) {
+            double acc = 0.0;
+            for (int o = 0; o < d; ++o)
+                acc += gQ[(size_t)row * d + o] * w[(size_t)o * d + i];
+            dZ[(size_t)row * d + i] = acc;
+        }
+    }
+#pragma omp parallel for schedule(static)
+    for (long so = 0; so < (long)q * d; ++so) {
+        const int s = (int)(so / d), o = (int)(so % d);
+        double *out = dwt + (size_t)s * d * d + (size_t)o * d;
+        for (int i = 0; i < d; ++i)
+            out[i] = 0.0;
+        for (long row = s; row < total_rows; row += q) {
+            const double g = gQ[(size_t)row * d + o];
+            for (int i = 0; i < d; ++i)
+                out[i] += g * Z[(size_t)row * d + i];
+        }
+    }
+
+    /* memory gradients: separate roles, or both roles of H summed */
+    for (long k = 0; k < total_kv * d; ++k) {
+        if (V) {
+            dK[k] = gK[k];
+            dV[k] = gV[k];
+        } else {
+            dK[k] = gK[k] + gV[k];
+        }
+    }
+    free(Q);
+    if (!dQ)
+        free(gQ);
+    free(gK);
+    free(gV);
+    return bad ? ORACLE_EINVAL : ORACLE_OK;
+}

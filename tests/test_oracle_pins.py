@@ -562,6 +562,226 @@ def test_full_eq7_composes(oracle_mod):
 
 
 # ----------------------------------------------------------------------------
+# Backward pass (gradients of <dO, O>)
+# ----------------------------------------------------------------------------
+def _torch_grads(wl, dO, kv_len=None):
+    """Gradients of <dO, O> by torch CPU float64 autograd through an
+    independent statement of the forward: Q = Z W_Q[slot]; per request, head
+    and query row, softmax over the visible memory rows, then the weighted sum
+    of values.  In projection-free mode H is one leaf used as both key and
+    value, so autograd adds both roles itself."""
+    d, dh, q = wl.d, wl.d_h, wl.q
+    Z = torch.tensor(wl.Z.astype(np.float64).reshape(-1, d), requires_grad=True)
+    wt = torch.tensor(wl.wt.astype(np.float64), requires_grad=True)
+    K = torch.tensor(wl.K.astype(np.float64), requires_grad=True)
+    V = torch.tensor(wl.V.astype(np.float64), requires_grad=True) if wl.V is not None else None
+    Vm = V if V is not None else K
+    rows = Z.shape[0]
+    Q = torch.stack([Z[r] @ wt[r % q].T for r in range(rows)]) if rows else Z
+    outs = []
+    for r in range(wl.R):
+        kv0, L = int(wl.cu_kv[r]), int(wl.cu_kv[r + 1] - wl.cu_kv[r])
+        for row in range(int(wl.cu_cand[r]) * q, int(wl.cu_cand[r + 1]) * q):
+            cut = L if kv_len is None else min(max(int(kv_len[row // q]), 0), L)
+            heads_out = []
+            for h in range(wl.heads):
+                cols = slice(h * dh, (h + 1) * dh)
+                if cut == 0:
+                    heads_out.append(torch.zeros(dh, dtype=torch.float64))
+                    continue
+                sc = K[kv0:kv0 + cut, cols] @ Q[row, cols] / np.sqrt(dh)
+                heads_out.append(torch.softmax(sc, dim=0) @ Vm[kv0:kv0 + cut, cols])
+            outs.append(torch.cat(heads_out))
+    O = torch.stack(outs)
+    (O * torch.from_numpy(np.asarray(dO, dtype=np.float64).reshape(-1, d))).sum().backward()
+    return {"dZ": Z.grad.numpy(), "dwt": wt.grad.numpy(), "dK": K.grad.numpy(),
+            "dV": V.grad.numpy() if V is not None else None}
+
+
+def _dO_for(wl, rng):
+    return rng.normal(size=(wl.rows, wl.d))
+
+
+def _check_bwd_autograd(orc, seed, kv_mode, prefix=False):
+    rng = np.random.default_rng(seed)
+    wl = _rand_case(rng, R=3, q=int(rng.integers(1, 4)), d=8,
+                    heads=int(rng.choice([1, 2, 4])), kv_mode=kv_mode)
+    dO = _dO_for(wl, rng)
+    kv_len = rng.integers(-1, 11, size=wl.total_cand) if prefix else None
+    g = orc.backward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, wl.K, wl.V, dO,
+                     kv_len=kv_len)
+    t = _torch_grads(wl, dO, kv_len)
+    err = 0.0
+    for k in ("dZ", "dwt", "dK", "dV"):
+        if t[k] is None:
+            assert g[k] is None
+            continue
+        err = max(err, float(np.max(np.abs(g[k].reshape(t[k].shape) - t[k]))))
+    return err
+
+
+@pytest.mark.parametrize("kv_mode", ["shared", "separate"])
+@pytest.mark.parametrize("seed", range(4))
+def test_backward_matches_torch_autograd(oracle_mod, seed, kv_mode):
+    assert _check_bwd_autograd(oracle_mod, seed, kv_mode) < 1e-12
+
+
+@pytest.mark.parametrize("kv_mode", ["shared", "separate"])
+def test_backward_prefix_matches_torch_autograd(oracle_mod, kv_mode):
+    assert _check_bwd_autograd(oracle_mod, 21, kv_mode, prefix=True) < 1e-12
+
+
+def _check_bwd_finite_diff(orc, seed, kv_mode):
+    """Central differences of f = <dO, forward(x)> (the separately pinned
+    forward) along random directions in Z, W_Q, K and V, against <grad, dir>.
+    Returns the largest relative mismatch."""
+    rng = np.random.default_rng(seed)
+    wl = _rand_case(rng, R=2, q=2, d=8, heads=2, kv_mode=kv_mode, Lmax=6, Nmax=3)
+    dO = _dO_for(wl, rng)
+    g = orc.backward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, wl.K, wl.V, dO)
+    base = {"Z": wl.Z.astype(np.float64), "wt": wl.wt.astype(np.float64),
+            "K": wl.K.astype(np.float64),
+            "V": wl.V.astype(np.float64) if wl.V is not None else None}
+
+    def f(x):
+        O = orc.forward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, x["Z"], x["wt"], x["K"], x["V"])
+        return float(np.sum(O * dO))
+
+    worst = 0.0
+    eps = 1e-6
+    for name, gname in (("Z", "dZ"), ("wt", "dwt"), ("K", "dK"), ("V", "dV")):
+        if base[name] is None:
+            continue
+        v = rng.normal(size=base[name].shape)
+        xp = dict(base)
+        xm = dict(base)
+        xp[name] = base[name] + eps * v
+        xm[name] = base[name] - eps * v
+        fd = (f(xp) - f(xm)) / (2 * eps)
+        an = float(np.sum(g[gname].reshape(v.shape) * v))
+        worst = max(worst, abs(fd - an) / max(1.0, abs(an)))
+    return worst
+
+
+@pytest.mark.parametrize("kv_mode", ["shared", "separate"])
+def test_backward_finite_differences(oracle_mod, kv_mode):
+    assert _check_bwd_finite_diff(oracle_mod, 30, kv_mode) < 1e-7
+
+
+def _check_bwd_single_row(orc, seed):
+    """L = 1: the one weight is exactly 1 whatever the query, so no gradient
+    reaches Z, W_Q or the key role, and the memory row's value gradient is the
+    sum of the request's dO rows (head by head).  Returns the largest error."""
+    rng = np.random.default_rng(seed)
+    wl = W.custom("l1", [1, 1], [3, 2], q=2, d=8, heads=4, dtype="fp32",
+                  kv_mode="separate", rng=rng)
+    dO = _dO_for(wl, rng)
+    g = orc.backward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, wl.K, wl.V, dO)
+    err = max(np.max(np.abs(g["dZ"])), np.max(np.abs(g["dwt"])), np.max(np.abs(g["dK"])))
+    for r in range(wl.R):
+        a, b = int(wl.cu_cand[r]) * wl.q, int(wl.cu_cand[r + 1]) * wl.q
+        err = max(err, float(np.max(np.abs(g["dV"][r] - dO[a:b].sum(axis=0)))))
+    return err
+
+
+def test_backward_single_memory_row(oracle_mod):
+    assert _check_bwd_single_row(oracle_mod, 31) < 1e-14
+
+
+def _check_bwd_identical_keys(orc, seed):
+    """All keys of a request equal: the weights are uniform for every query,
+    so nothing flows back into the queries (dZ = dW_Q = 0)."""
+    rng = np.random.default_rng(seed)
+    wl = _rand_case(rng, R=2, q=2, d=8, heads=2, kv_mode="separate")
+    K = wl.K.copy()
+    for r in range(wl.R):
+        K[wl.cu_kv[r]:wl.cu_kv[r + 1]] = K[wl.cu_kv[r]]
+    dO = _dO_for(wl, rng)
+    g = orc.backward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, K, wl.V, dO)
+    return max(np.max(np.abs(g["dZ"])), np.max(np.abs(g["dwt"])))
+
+
+def test_backward_identical_keys(oracle_mod):
+    assert _check_bwd_identical_keys(oracle_mod, 32) < 1e-13
+
+
+def _check_bwd_shared_prefix_sum(orc, seed):
+    """TransX report s.2 (trajectory packing): the memory gradient of a
+    request's N candidates scored against one H equals the sum, over N
+    single-candidate requests that each carry a copy of H, of their memory
+    gradients; the query-side gradients are unchanged."""
+    rng = np.random.default_rng(seed)
+    wl = _rand_case(rng, R=2, q=2, d=8, heads=2, kv_mode="shared", Nmax=5)
+    dO = _dO_for(wl, rng)
+    g = orc.backward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, wl.K, None, dO)
+    Ks, lens, owner = [], [], []
+    for r in range(wl.R):
+        for _ in range(wl.cands[r]):
+            Ks.append(wl.K[wl.cu_kv[r]:wl.cu_kv[r + 1]])
+            lens.append(wl.lengths[r])
+            owner.append(r)
+    cu_kv = np.concatenate([[0], np.cumsum(lens)])
+    cu_c = np.arange(len(lens) + 1)
+    g2 = orc.backward(cu_kv, cu_c, wl.q, wl.heads, wl.Z, wl.wt, np.concatenate(Ks), None, dO)
+    err = max(np.max(np.abs(g2["dZ"] - g["dZ"])), np.max(np.abs(g2["dwt"] - g["dwt"])))
+    summed = np.zeros_like(g["dK"])
+    for n, r in enumerate(owner):
+        summed[wl.cu_kv[r]:wl.cu_kv[r + 1]] += g2["dK"][cu_kv[n]:cu_kv[n + 1]]
+    return max(err, float(np.max(np.abs(summed - g["dK"]))))
+
+
+def test_backward_candidate_gradients_sum_into_one_memory(oracle_mod):
+    assert _check_bwd_shared_prefix_sum(oracle_mod, 33) < 1e-13
+
+
+def _check_bwd_prefix_truncation(orc, seed):
+    """With every candidate of a request cut at L', the gradients equal those
+    of the request with its memory truncated to L' rows; rows past L' get
+    zero memory gradient."""
+    rng = np.random.default_rng(seed)
+    wl = W.custom("trunc", [9], [4], q=2, d=8, heads=2, dtype="fp32", kv_mode="separate",
+                  rng=rng)
+    cut = 5
+    dO = _dO_for(wl, rng)
+    g = orc.backward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, wl.K, wl.V, dO,
+                     kv_len=np.full(wl.total_cand, cut))
+    t = orc.backward([0, cut], wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, wl.K[:cut], wl.V[:cut],
+                     dO)
+    err = max(np.max(np.abs(g["dZ"] - t["dZ"])), np.max(np.abs(g["dwt"] - t["dwt"])),
+              np.max(np.abs(g["dK"][:cut] - t["dK"])), np.max(np.abs(g["dV"][:cut] - t["dV"])),
+              np.max(np.abs(g["dK"][cut:])), np.max(np.abs(g["dV"][cut:])))
+    return err
+
+
+def test_backward_prefix_truncation(oracle_mod):
+    assert _check_bwd_prefix_truncation(oracle_mod, 34) == 0.0
+
+
+def test_backward_is_linear_in_dO(oracle_mod):
+    rng = np.random.default_rng(35)
+    wl = _rand_case(rng, R=2, q=2, d=8, heads=2, kv_mode="shared")
+    a, b = _dO_for(wl, rng), _dO_for(wl, rng)
+    ga = oracle_mod.backward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, wl.K, None, a)
+    gb = oracle_mod.backward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, wl.K, None, b)
+    gc = oracle_mod.backward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, wl.K, None,
+                             2.0 * a - 3.0 * b)
+    for k in ("dZ", "dwt", "dK"):
+        assert np.max(np.abs(gc[k] - (2.0 * ga[k] - 3.0 * gb[k]))) < 1e-12
+
+
+def test_backward_thread_count_independent(oracle_mod):
+    rng = np.random.default_rng(36)
+    wl = _rand_case(rng, R=5, q=3, d=16, heads=4, kv_mode="shared", Lmax=40, Nmax=6)
+    dO = _dO_for(wl, rng)
+    oracle_mod.set_threads(1)
+    g1 = oracle_mod.backward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, wl.K, None, dO)
+    oracle_mod.set_threads(4)
+    g4 = oracle_mod.backward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, wl.K, None, dO)
+    for k in ("dQ", "dZ", "dwt", "dK"):
+        assert np.array_equal(g1[k], g4[k])
+
+
+# ----------------------------------------------------------------------------
 # Mutation test: plausible mistakes planted in copies of the oracle are caught
 # ----------------------------------------------------------------------------
 MUTANTS = {
@@ -590,6 +810,18 @@ MUTANTS = {
                           "const double *w = wgo;"),
     "output_weight_transposed": ("acc += x[o] * wo[(size_t)p * d + o];",
                                  "acc += x[o] * wo[(size_t)o * d + p];"),
+    "bwd_softmax_mean_dropped": ("const double ds = p[j] * (dp[j] - pdp);",
+                                 "const double ds = p[j] * dp[j];"),
+    "bwd_key_scale_dropped": ("gkj[e] += c * ds * qi[e];", "gkj[e] += ds * qi[e];"),
+    "bwd_value_role_dropped": ("dK[k] = gK[k] + gV[k];", "dK[k] = gK[k];"),
+    "bwd_dz_weight_transposed": ("acc += gQ[(size_t)row * d + o] * w[(size_t)o * d + i];",
+                                 "acc += gQ[(size_t)row * d + o] * w[(size_t)i * d + o];"),
+    "bwd_dw_all_slots": ("for (long row = s; row < total_rows; row += q) {",
+                         "for (long row = 0; row < total_rows; row += 1) {"),
+    "bwd_dq_reads_values": ("dqi[e] += c * ds * kj[e];",
+                            "dqi[e] += c * ds * Vm[(size_t)(kv0 + j) * d + h * d_h + e];"),
+    "bwd_cutoff_ignored": ("Lc = want < 0 ? 0 : (want < L ? want : L);\n                    }\n                    if (Lc == 0)\n                        continue;",
+                           "Lc = L;\n                    }\n                    if (Lc == 0)\n                        continue;"),
 }
 
 
@@ -612,6 +844,15 @@ def _all_pins(orc):
         "gate_symmetry": lambda: _check_gate_symmetry(orc, 1) < 1e-12,
         "prefix_sdpa": lambda: all(_check_prefix_sdpa(orc, s_) < 1e-12 for s_ in range(2)),
         "prefix_truncation": lambda: _check_prefix_truncation(orc, 4) == 0.0,
+        "bwd_autograd_shared": lambda: _check_bwd_autograd(orc, 0, "shared") < 1e-12,
+        "bwd_autograd_separate": lambda: _check_bwd_autograd(orc, 1, "separate") < 1e-12,
+        "bwd_autograd_prefix": lambda: _check_bwd_autograd(orc, 21, "shared", True) < 1e-12,
+        "bwd_finite_diff": lambda: all(_check_bwd_finite_diff(orc, 30, m) < 1e-7
+                                       for m in ("shared", "separate")),
+        "bwd_single_row": lambda: _check_bwd_single_row(orc, 31) < 1e-14,
+        "bwd_identical_keys": lambda: _check_bwd_identical_keys(orc, 32) < 1e-13,
+        "bwd_shared_prefix_sum": lambda: _check_bwd_shared_prefix_sum(orc, 33) < 1e-13,
+        "bwd_prefix_truncation": lambda: _check_bwd_prefix_truncation(orc, 34) == 0.0,
     }
     for path in GOLDEN_OUTPUT:
         checks["golden:" + os.path.basename(path)] = lambda path=path: _check_gate_golden(orc, path)
