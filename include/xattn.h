@@ -218,6 +218,47 @@ xattn_status xattn_attend_q_prefix(xattn_ctx* ctx, const void* Q,
                                    void* O, void* workspace, size_t workspace_bytes,
                                    void* stream);
 
+/* Bytes of device workspace xattn_backward needs for this batch shape (0 on
+ * invalid arguments). */
+size_t xattn_backward_workspace_size(const xattn_ctx* ctx, int32_t num_requests,
+                                     int32_t total_cand, int32_t total_kv, int32_t heads);
+
+/* Backward pass of xattn_forward: the gradients of <dO, O> with respect to
+ * the query tokens, the per-slot W_Q and the memory, for the loss gradient
+ * dO of the attention output O (ReST reading note s.3.3.1 Eq. (7) with
+ * Eq. (8)'s per-slot W_Q).  The memory gradient of a request sums the
+ * contributions of all its candidates' query rows: the candidates of one
+ * user send their gradients back into the one encoded memory (TransX
+ * report s.2, trajectory packing; ReST reading note s.3.5, ULT).
+ *   - Z, W_Q, K, V, offsets, shapes: as for xattn_forward (the same batch).
+ *   - dO  [total_cand][q][d] context type: gradient of the loss w.r.t. O.
+ *   - dZ  [total_cand][q][d] context type.
+ *   - dW_Q [q][d][d] fp32 in both modes, output-major like W_Q, summed over
+ *     every candidate of every request (overwritten, not accumulated).
+ *   - dK  [total_kv][d] context type.  In XATTN_KV_SHARED mode this is the
+ *     gradient of H, which is both key and value (dV must be NULL).
+ *   - dV  [total_kv][d] context type in XATTN_KV_SEPARATE mode.
+ * Memory rows that no query row sees get zero gradient; requests without
+ * memory rows give zero dZ.  The forward statistics (softmax normaliser and
+ * <dO, O> per row and head) are recomputed inside; every reduction runs in a
+ * fixed order, so the result is deterministic bit for bit.  Enqueues, on
+ * `stream`: the projection (with the query-tile planner), the memory-tile
+ * planner, the statistics pass, the dQ kernel, the dK/dV kernel, a weight
+ * transpose, the dZ GEMM and the dW_Q kernels.  bf16: products on the matrix
+ * cores with fp32 accumulation; P and dS are rounded to bf16 as operands,
+ * dQ to bf16 before the dZ and dW_Q products.  `workspace` holds at least
+ * xattn_backward_workspace_size() bytes.  Errors as for xattn_forward; NULL
+ * dO, dZ, dW_Q or dK (where rows exist) is XATTN_EINVAL.  On offsets that
+ * fail the device check nothing is written. */
+xattn_status xattn_backward(xattn_ctx* ctx,
+                            const void* Z, const void* W_Q,
+                            const void* K, const void* V, const void* dO,
+                            const int32_t* cu_seqlens_kv, const int32_t* cu_cand,
+                            int32_t num_requests, int32_t total_cand,
+                            int32_t total_kv, int32_t heads,
+                            void* dZ, float* dW_Q, void* dK, void* dV,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* Varlen plan alone (integer outputs, for callers that want the row map and
  * for tests).  Writes, on the device:
  *   cu_q[r]      = q * cu_cand[r]                (R+1 entries)

@@ -397,6 +397,203 @@ xattn_status xattn_attend_q_prefix(xattn_ctx* ctx, const void* Q, const void* K,
                        cand_kv_len);
 }
 
+namespace {
+
+// Backward workspace: the query-tile plan (tiles of 64 candidates), the
+// memory-tile plan (64 rows), the projected (bf16: pre-scaled) queries, the
+// forward statistics lse and D, dQ, the transposed W_Q and, in bf16, the
+// split-K partials of dW_Q.  Every region starts 256-byte aligned.
+struct BwdLayout {
+    size_t plan, kplan, qs, lse, dsum, dq, wt, part, total;
+    int nch;
+    int64_t max_q, max_k;
+};
+
+BwdLayout bwd_layout(const xattn_config& c, int R, int total_cand, int total_kv, int heads) {
+    BwdLayout L{};
+    const size_t eb = elem_bytes(c);
+    const size_t rows = (size_t)total_cand * c.n_slots, d = (size_t)c.d_model;
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    L.max_q = max_tiles_for(c, R, total_cand, 64);
+    L.max_k = ((int64_t)total_kv + (int64_t)R * 63) / 64;
+    L.nch = c.dtype == XATTN_BF16 ? xattn::bwd_dw_chunks(total_cand, c.n_slots, c.d_model) : 0;
+    size_t off = 0;
+    L.plan = off;
+    off = al(off + xattn::kPlanHeaderBytes + 16 * (size_t)(L.max_q > 0 ? L.max_q : 1));
+    L.kplan = off;
+    off = al(off + xattn::kPlanHeaderBytes + 16 * (size_t)(L.max_k > 0 ? L.max_k : 1));
+    L.qs = off;
+    off = al(off + rows * d * eb);
+    L.lse = off;
+    off = al(off + rows * heads * 4);
+    L.dsum = off;
+    off = al(off + rows * heads * 4);
+    L.dq = off;
+    off = al(off + rows * d * eb);
+    L.wt = off;
+    off = al(off + (size_t)c.n_slots * d * d * eb);
+    L.part = off;
+    off = al(off + (size_t)L.nch * c.n_slots * d * d * 4);
+    L.total = off;
+    return L;
+}
+
+}  // namespace
+
+size_t xattn_backward_workspace_size(const xattn_ctx* ctx, int32_t R, int32_t total_cand,
+                                     int32_t total_kv, int32_t heads) {
+    if (!ctx || R < 0 || total_cand < 0 || total_kv < 0 || heads < 1 ||
+        ctx->cfg.d_model % heads != 0)
+        return 0;
+    return bwd_layout(ctx->cfg, R, total_cand, total_kv, heads).total;
+}
+
+xattn_status xattn_backward(xattn_ctx* ctx, const void* Z, const void* W_Q, const void* K,
+                            const void* V, const void* dO, const int32_t* cu_kv,
+                            const int32_t* cu_cand, int32_t R, int32_t total_cand,
+                            int32_t total_kv, int32_t heads, void* dZ, float* dW_Q, void* dK,
+                            void* dV, void* workspace, size_t workspace_bytes_, void* stream) {
+    g_last_error.clear();
+    xattn_status st = check_shape(ctx, R, total_cand, total_kv, heads);
+    if (st != XATTN_OK) return st;
+    const xattn_config& c = ctx->cfg;
+    const bool sep = c.kv_mode == XATTN_KV_SEPARATE;
+    if (!sep && (V || dV))
+        return fail(XATTN_EINVAL, "V and dV must be NULL in XATTN_KV_SHARED mode (dK is dH)");
+    if (!cu_kv || !cu_cand) return fail(XATTN_EINVAL, "NULL offset array");
+    if (!dW_Q) return fail(XATTN_EINVAL, "NULL dW_Q");
+    if (total_cand > 0 && (!Z || !dO || !dZ)) return fail(XATTN_EINVAL, "NULL Z, dO or dZ");
+    if (!W_Q) return fail(XATTN_EINVAL, "NULL W_Q");
+    if (total_kv > 0 && (!K || !dK)) return fail(XATTN_EINVAL, "NULL K or dK");
+    if (total_kv > 0 && sep && (!V || !dV))
+        return fail(XATTN_EINVAL, "V or dV is NULL in XATTN_KV_SEPARATE mode");
+    if (R == 0 && (total_cand != 0 || total_kv != 0))
+        return fail(XATTN_EINVAL, "num_requests=0 with total_cand=%d total_kv=%d", total_cand,
+                    total_kv);
+    const BwdLayout Lw = bwd_layout(c, R, total_cand, total_kv, heads);
+    if (!workspace || workspace_bytes_ < Lw.total)
+        return fail(XATTN_EWORKSPACE, "workspace needs %zu bytes, got %zu", Lw.total,
+                    workspace_bytes_);
+    if ((Lw.max_q + Lw.max_k) * heads > INT32_MAX)
+        return fail(XATTN_EUNSUPPORTED, "grid too large");
+    DeviceGuard dg(c.device);
+    if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    const int q = c.n_slots, d = c.d_model, dh = d / heads;
+    const bool bf = c.dtype == XATTN_BF16;
+    hipError_t e = hipSuccess;
+#define XATTN_TRY(call, what)                     \
+    do {                                          \
+        e = (call);                               \
+        if (e != hipSuccess) return hip_fail(e, what); \
+    } while (0)
+    if (R == 0) {   // no parameters were used: a zero weight gradient
+        XATTN_TRY(bf ? xattn::launch_bwd_dw_bf16(nullptr, nullptr, 0, q, d, nullptr, 0, dW_Q, s)
+                     : xattn::launch_bwd_dw_f32(nullptr, nullptr, 0, q, d, dW_Q, s),
+                  "weight-gradient launch");
+        return XATTN_OK;
+    }
+    // 1. plans: query tiles of 64 candidates, memory tiles of 64 rows (the
+    //    planner with memory and candidates exchanged)
+    // 2. queries (bf16: scaled by log2(e)/sqrt(d_h) exactly as the forward
+    //    kernel scales them)
+    if (bf) {
+        XATTN_TRY(xattn::launch_project_plan_bf16(Z, W_Q, total_cand, q, d, ws + Lw.qs, cu_kv,
+                                                  cu_cand, R, 64, total_kv, ws + Lw.plan, Lw.max_q,
+                                                  s, nullptr,
+                                                  1.4426950408889634f / sqrtf((float)dh)),
+                  "projection kernel launch");
+    } else {
+        XATTN_TRY(xattn::launch_plan(cu_kv, cu_cand, R, q, 64, total_cand, total_kv, ws + Lw.plan,
+                                     Lw.max_q, nullptr, nullptr, nullptr, nullptr, s),
+                  "plan kernel launch");
+        XATTN_TRY(xattn::launch_project_f32(static_cast<const float*>(Z),
+                                            static_cast<const float*>(W_Q), total_cand, q, d,
+                                            reinterpret_cast<float*>(ws + Lw.qs), s),
+                  "projection kernel launch");
+    }
+    XATTN_TRY(xattn::launch_plan(cu_cand, cu_kv, R, 1, 64, total_kv, total_cand, ws + Lw.kplan,
+                                 Lw.max_k, nullptr, nullptr, nullptr, nullptr, s),
+              "memory plan kernel launch");
+    // 3. forward statistics lse and D = <dO, O> per row and head
+    float* lse = reinterpret_cast<float*>(ws + Lw.lse);
+    float* dsum = reinterpret_cast<float*>(ws + Lw.dsum);
+    if (bf) {
+        xattn::AttnArgs a{};
+        a.Qp = ws + Lw.qs;
+        a.K = K;
+        a.V = sep ? V : nullptr;
+        a.ws = ws + Lw.plan;
+        a.cu_kv = cu_kv;
+        a.cu_cand = cu_cand;
+        a.max_tiles = Lw.max_q;
+        a.R = R;
+        a.total_cand = total_cand;
+        a.total_kv = total_kv;
+        a.q = q;
+        a.d = d;
+        a.heads = heads;
+        a.prescaled = 1;
+        a.lse = lse;
+        a.Dsum = dsum;
+        a.dO = dO;
+        const int ks = xattn::attn_bf16_variant_smem(dh, 2, 2, sep, false) > 0 ? 2 : 1;
+        XATTN_TRY(xattn::launch_attn_bf16(a, 2, ks, s), "statistics kernel launch");
+    } else {
+        XATTN_TRY(xattn::launch_attn_f32_stats(reinterpret_cast<const float*>(ws + Lw.qs),
+                                               static_cast<const float*>(K),
+                                               sep ? static_cast<const float*>(V) : nullptr,
+                                               ws + Lw.plan, Lw.max_q, q, d, heads,
+                                               static_cast<const float*>(dO), lse, dsum, s),
+                  "statistics kernel launch");
+    }
+    // 4. dQ (per query tile) and dK, dV (per memory tile, summed over the
+    //    request's query rows)
+    xattn::BwdArgs b{};
+    b.Qs = ws + Lw.qs;
+    b.K = K;
+    b.V = sep ? V : nullptr;
+    b.dO = dO;
+    b.lse = lse;
+    b.Dsum = dsum;
+    b.plan = reinterpret_cast<const int*>(ws + Lw.plan);
+    b.kplan = reinterpret_cast<const int*>(ws + Lw.kplan);
+    b.dQ = ws + Lw.dq;
+    b.dK = dK;
+    b.dV = sep ? dV : nullptr;
+    b.q = q;
+    b.d = d;
+    b.heads = heads;
+    b.scale = 1.0f / sqrtf((float)dh);
+    XATTN_TRY(bf ? xattn::launch_bwd_attn_bf16(b, sep, Lw.max_q, Lw.max_k, s)
+                 : xattn::launch_bwd_attn_f32(b, sep, Lw.max_q, Lw.max_k, s),
+              "attention backward launch");
+    // 5. dZ = dQ W_Q[slot] through the transposed weights; 6. dW_Q
+    XATTN_TRY(xattn::launch_transpose_weights(W_Q, q, d, !bf, ws + Lw.wt, s),
+              "transpose kernel launch");
+    if (bf) {
+        XATTN_TRY(xattn::launch_project_plan_bf16(ws + Lw.dq, ws + Lw.wt, total_cand, q, d, dZ,
+                                                  nullptr, nullptr, 0, 0, 0, nullptr, 0, s),
+                  "input-gradient launch");
+        XATTN_TRY(xattn::launch_bwd_dw_bf16(ws + Lw.dq, Z, total_cand, q, d,
+                                            reinterpret_cast<float*>(ws + Lw.part), Lw.nch, dW_Q,
+                                            s),
+                  "weight-gradient launch");
+    } else {
+        XATTN_TRY(xattn::launch_project_f32(reinterpret_cast<const float*>(ws + Lw.dq),
+                                            reinterpret_cast<const float*>(ws + Lw.wt),
+                                            total_cand, q, d, static_cast<float*>(dZ), s),
+                  "input-gradient launch");
+        XATTN_TRY(xattn::launch_bwd_dw_f32(reinterpret_cast<const float*>(ws + Lw.dq),
+                                           static_cast<const float*>(Z), total_cand, q, d, dW_Q,
+                                           s),
+                  "weight-gradient launch");
+    }
+#undef XATTN_TRY
+    return XATTN_OK;
+}
+
 xattn_status xattn_project(xattn_ctx* ctx, const void* Z, const void* W_Q, int32_t total_cand,
                            void* Q, void* stream) {
     g_last_error.clear();

@@ -528,7 +528,29 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(AttnArgs a)
         }
     }
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    if (qvalid) {
+    if (a.lse) {
+        // statistics for the backward pass: the row's log2 normaliser and
+        // D = <dO_row, O_row> over this head's features (fp32 O)
+        float dpart = 0.f;
+        if (a.dO && qvalid) {
+            const bf16* drow = static_cast<const bf16*>(a.dO) + ((size_t)cand * q + s) * d + h * DH;
+#pragma unroll
+            for (int eb = 0; eb < C::EB; ++eb)
+#pragma unroll
+                for (int b4 = 0; b4 < 4; ++b4) {
+                    const bf16x4 dv = *reinterpret_cast<const bf16x4*>(drow + eb * 32 + b4 * 8 + 4 * g);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) dpart += oacc[eb][4 * b4 + t] * inv * (float)dv[t];
+                }
+        }
+        dpart += xor32(dpart);
+        if (qvalid && g == 0) {
+            const size_t idx = ((size_t)cand * q + s) * heads + h;
+            a.lse[idx] = l_run > 0.f ? m_run + __builtin_amdgcn_logf(l_run) : -INFINITY;   // v_log_f32 is log2
+            if (a.Dsum) a.Dsum[idx] = dpart;
+        }
+    }
+    if (qvalid && O) {
         bf16* orow = O + ((size_t)cand * q + s) * d + h * DH;
 #pragma unroll
         for (int eb = 0; eb < C::EB; ++eb) {
@@ -562,7 +584,7 @@ hipError_t launch_one(const AttnArgs& a, hipStream_t stream) {
     } else {
         if (PROJ && a.d > kProjMaxD) return hipErrorInvalidValue;
         AttnArgs k = a;
-        k.scale_log2 = 1.4426950408889634f / sqrtf((float)DH);
+        k.scale_log2 = a.prescaled ? 1.0f : 1.4426950408889634f / sqrtf((float)DH);
         const int64_t blocks = a.max_tiles * a.heads;
         if (blocks <= 0) return hipSuccess;
         if (a.cand_len) {

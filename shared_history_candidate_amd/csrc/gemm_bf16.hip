@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const bf16* __restrict__ Z,
                                                    const bf16* __restrict__ Wq, int total_cand,
                                                    int q, int d, bf16* __restrict__ Q,
                                                    int tiles_e, int tiles_c, PlanArgs pa,
-                                                   const bf16* __restrict__ Og) {
+                                                   const bf16* __restrict__ Og, float oscale) {
     using C = GCfg<TE, TC, KC>;
     constexpr int LDP = C::LDP;
     __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
@@ -207,9 +207,13 @@ __global__ __launch_bounds__(256) void prep_kernel(const bf16* __restrict__ Z,
                                                                    1.4426950408889634f);
                             v[t] = (bf16)((float)ov[t] / (1.0f + e));
                         }
-                    } else {
+                    } else if (oscale == 1.0f) {
 #pragma unroll
                         for (int t = 0; t < 4; ++t) v[t] = (bf16)acc[i][j][4 * b4 + t];
+                    } else {
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+                            v[t] = (bf16)((float)(bf16)acc[i][j][4 * b4 + t] * oscale);
                     }
                     *reinterpret_cast<bf16x4*>(qrow + o) = v;
                 }
@@ -219,7 +223,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const bf16* __restrict__ Z,
 
 template <int TE, int TC, int KC>
 hipError_t launch_prep(const void* Z, const void* Wq, int total_cand, int q, int d, void* Q,
-                       const PlanArgs& pa, hipStream_t stream, const void* Og) {
+                       const PlanArgs& pa, hipStream_t stream, const void* Og, float oscale) {
     const int tiles_e = (d + TE - 1) / TE;
     const int tiles_c = (total_cand + TC - 1) / TC;
     const int64_t blocks = (int64_t)q * tiles_e * tiles_c + (pa.enabled ? 1 : 0);
@@ -227,7 +231,7 @@ hipError_t launch_prep(const void* Z, const void* Wq, int total_cand, int q, int
     hipLaunchKernelGGL((prep_kernel<TE, TC, KC>), dim3((unsigned)blocks), dim3(256), 0, stream,
                        static_cast<const bf16*>(Z), static_cast<const bf16*>(Wq), total_cand, q, d,
                        static_cast<bf16*>(Q), tiles_e, tiles_c, pa,
-                       static_cast<const bf16*>(Og));
+                       static_cast<const bf16*>(Og), oscale);
     return hipGetLastError();
 }
 
@@ -236,7 +240,7 @@ hipError_t launch_prep(const void* Z, const void* Wq, int total_cand, int q, int
 hipError_t launch_project_plan_bf16(const void* Z, const void* Wq, int total_cand, int q, int d,
                                     void* Q, const int* cu_kv, const int* cu_cand, int R,
                                     int tile_m, int total_kv, void* ws, int64_t max_tiles,
-                                    hipStream_t stream, const void* Og) {
+                                    hipStream_t stream, const void* Og, float oscale) {
     PlanArgs pa{cu_kv, cu_cand, static_cast<int*>(ws), max_tiles, R, tile_m, total_kv,
                 ws != nullptr ? 1 : 0};
     if (total_cand <= 0 && !pa.enabled) return hipSuccess;
@@ -245,7 +249,7 @@ hipError_t launch_project_plan_bf16(const void* Z, const void* Wq, int total_can
         int te = 0, tc = 0, kc = 0;
         if (sscanf(env, "%d,%d,%d", &te, &tc, &kc) == 3) {
 #define XATTN_GEMM_CASE(A_, B_, C_) \
-    if (te == A_ && tc == B_ && kc == C_) return launch_prep<A_, B_, C_>(Z, Wq, total_cand, q, d, Q, pa, stream, Og);
+    if (te == A_ && tc == B_ && kc == C_) return launch_prep<A_, B_, C_>(Z, Wq, total_cand, q, d, Q, pa, stream, Og, oscale);
             XATTN_GEMM_CASE(128, 128, 64)
             XATTN_GEMM_CASE(64, 64, 256)
             XATTN_GEMM_CASE(128, 128, 32)
@@ -258,8 +262,8 @@ hipError_t launch_project_plan_bf16(const void* Z, const void* Wq, int total_can
     }
     // wide tiles when they still give at least two work-groups per compute unit
     const int64_t big = (int64_t)q * ((d + 127) / 128) * ((total_cand + 127) / 128);
-    if (big >= 512) return launch_prep<128, 128, 64>(Z, Wq, total_cand, q, d, Q, pa, stream, Og);
-    return launch_prep<64, 64, 256>(Z, Wq, total_cand, q, d, Q, pa, stream, Og);
+    if (big >= 512) return launch_prep<128, 128, 64>(Z, Wq, total_cand, q, d, Q, pa, stream, Og, oscale);
+    return launch_prep<64, 64, 256>(Z, Wq, total_cand, q, d, Q, pa, stream, Og, oscale);
 }
 
 hipError_t launch_gate_output_bf16(const void* Z, const void* Wgo, const void* O, const void* Wo,

@@ -29,8 +29,16 @@ struct AttnArgs {
     const int* cand_len;   // per-candidate prefix cutoff, or NULL (Qp path only)
     int64_t max_tiles;
     int R, total_cand, total_kv, inplan, q, d, heads;
+    // Qp already holds bf16(Q * log2(e)/sqrt(d_h)) (backward pass)
+    int prescaled;
     float scale_log2;   // set by the launcher
-    void* O;
+    void* O;            // may be NULL when lse is set
+    // Statistics for the backward pass, [rows][heads] fp32 (row = c*q + s):
+    // lse = log2 of the row's softmax normaliser in the scaled exp2 units of
+    // the scores; Dsum = <dO_row, O_row> of the head (fp32 O), if dO is set.
+    float* lse;
+    float* Dsum;
+    const void* dO;
 };
 // Widest model (d) whose queries the attention kernel projects itself.
 constexpr int kAttnProjMaxD = 256;
@@ -41,16 +49,58 @@ hipError_t launch_attn_bf16(const AttnArgs& a, int rb, int ksplit, hipStream_t s
 
 // bf16 TSP projection Q = Z W_Q[slot] into Qp; when ws is not NULL the same
 // launch also runs the planner into ws (one extra work-group).
+// With oscale != 1 the stored value is bf16(float(bf16(acc)) * oscale): the
+// queries pre-scaled exactly as the attention kernel scales them.
 hipError_t launch_project_plan_bf16(const void* Z, const void* Wq, int total_cand, int q, int d,
                                     void* Qp, const int* cu_kv, const int* cu_cand, int R,
                                     int tile_m, int total_kv, void* ws, int64_t max_tiles,
-                                    hipStream_t stream, const void* Og = nullptr);
+                                    hipStream_t stream, const void* Og = nullptr,
+                                    float oscale = 1.0f);
 
 // Output gate and projection of Eq. (7): X = O * sigmoid(Z W_go[slot]) (bf16,
 // [total_cand][q][d]), then Y = X W_o; two launches of the projection kernel.
 hipError_t launch_gate_output_bf16(const void* Z, const void* Wgo, const void* O, const void* Wo,
                                    int total_cand, int q, int d, void* X, void* Y,
                                    hipStream_t stream);
+
+// Backward pass (bwd_bf16.hip, bwd in attn_f32.hip).  plan: query tiles of
+// 64 candidates (the forward's plan layout); kplan: memory tiles of 64 rows,
+// the same planner with memory and candidates exchanged.  Qs holds the
+// queries scaled by log2(e)/sqrt(d_h) in bf16 mode (unscaled in fp32 mode),
+// lse and Dsum the forward statistics ([rows][heads]).  dK is dH (both
+// roles) when V is NULL.
+struct BwdArgs {
+    const void* Qs;
+    const void* K;
+    const void* V;
+    const void* dO;
+    const float* lse;
+    const float* Dsum;
+    const int* plan;
+    const int* kplan;
+    void* dQ;
+    void* dK;
+    void* dV;
+    int q, d, heads;
+    float scale;   // 1/sqrt(d_h)
+};
+hipError_t launch_bwd_attn_bf16(const BwdArgs& a, bool sep, int64_t q_items, int64_t k_items,
+                                hipStream_t stream);
+// dW_Q = sum over rows of slot s of dQ^T Z (fp32 [q][d][d], output-major),
+// nch split-K chunks through part ([nch][q][d][d] fp32) reduced in order.
+int bwd_dw_chunks(int total_cand, int q, int d);
+hipError_t launch_bwd_dw_bf16(const void* dQ, const void* Z, int total_cand, int q, int d,
+                              float* part, int nch, float* dW, hipStream_t stream);
+hipError_t launch_transpose_weights(const void* wt, int q, int d, bool fp32, void* wT,
+                                    hipStream_t stream);
+hipError_t launch_bwd_attn_f32(const BwdArgs& a, bool sep, int64_t q_items, int64_t k_items,
+                               hipStream_t stream);
+hipError_t launch_bwd_dw_f32(const float* dQ, const float* Z, int total_cand, int q, int d,
+                             float* dW, hipStream_t stream);
+// fp32 forward statistics (lse, Dsum for the backward pass), O may be NULL.
+hipError_t launch_attn_f32_stats(const float* Qp, const float* K, const float* V, const void* ws,
+                                 int64_t max_tiles, int q, int d, int heads, const float* dO,
+                                 float* lse, float* Dsum, hipStream_t stream);
 
 // fp32 path (tile_m = 64): attention over projected queries (cand_len: the
 // per-candidate prefix cutoff, or NULL), projection.

@@ -33,7 +33,7 @@ from typing import Optional, Sequence
 import numpy as np
 
 __all__ = ["Workload", "CONFIGS", "make", "custom", "round_bf16", "output_weights",
-           "attention_like", "prefix_lengths"]
+           "attention_like", "prefix_lengths", "output_grad"]
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
@@ -256,6 +256,14 @@ def attention_like(wl: Workload, seed: int = 0, std: float = 0.5) -> np.ndarray:
     rng = np.random.default_rng(seed)
     O = _normal(rng, (wl.total_cand, wl.q, wl.d), std=std)
     return round_bf16(O) if wl.dtype == "bf16" else O
+
+
+def output_grad(wl: Workload, seed: int = 0) -> np.ndarray:
+    """A loss gradient dO [total_cand][q][d] for the backward pass: N(0, 1)
+    draws from default_rng(seed), bf16-rounded in bf16 mode."""
+    rng = np.random.default_rng(seed)
+    g = _normal(rng, (wl.total_cand, wl.q, wl.d))
+    return round_bf16(g) if wl.dtype == "bf16" else g
 
 
 def prefix_lengths(wl: Workload, seed: int = 0, out_of_range: bool = True) -> np.ndarray:

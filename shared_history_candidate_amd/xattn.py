@@ -25,7 +25,8 @@ XATTN_KV_SHARED, XATTN_KV_SEPARATE = 0, 1
 EXPORTED = ("xattn_create", "xattn_destroy", "xattn_workspace_size", "xattn_forward",
             "xattn_attend", "xattn_attend_q", "xattn_plan", "xattn_max_tiles",
             "xattn_forward_launches", "xattn_project", "xattn_output", "xattn_device_error",
-            "xattn_last_error", "xattn_forward_prefix", "xattn_attend_q_prefix")
+            "xattn_last_error", "xattn_forward_prefix", "xattn_attend_q_prefix",
+            "xattn_backward_workspace_size", "xattn_backward")
 
 
 class Config(ctypes.Structure):
@@ -73,6 +74,11 @@ def lib():
         L.xattn_attend_q.restype = ctypes.c_int
         L.xattn_attend_q_prefix.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, P, P, SZ, P]
         L.xattn_attend_q_prefix.restype = ctypes.c_int
+        L.xattn_backward_workspace_size.argtypes = [P, I32, I32, I32, I32]
+        L.xattn_backward_workspace_size.restype = SZ
+        L.xattn_backward.argtypes = [P, P, P, P, P, P, P, P, I32, I32, I32, I32, P, P, P, P, P,
+                                     SZ, P]
+        L.xattn_backward.restype = ctypes.c_int
         L.xattn_plan.argtypes = [P, P, P, I32, I32, I32, I32, P, P, P, P,
                                  ctypes.POINTER(I32), P, SZ, P]
         L.xattn_plan.restype = ctypes.c_int
@@ -236,6 +242,55 @@ class XAttn:
                                     _ptr(workspace), workspace.numel(),
                                     _stream(Q.device, stream)))
         return O
+
+    def backward_workspace_size(self, num_requests: int, total_cand: int, total_kv: int,
+                                heads: int) -> int:
+        return int(lib().xattn_backward_workspace_size(self._h, num_requests, total_cand,
+                                                       total_kv, heads))
+
+    def backward(self, Z, W_Q, K, V, dO, cu_seqlens_kv, cu_cand, heads: int, workspace=None,
+                 out=None, stream=None) -> dict:
+        """Gradients of <dO, O> for O = forward(Z, W_Q, K, V, ...) (see
+        include/xattn.h, xattn_backward): returns {"dZ", "dW_Q" (fp32), "dK"
+        (dH in shared mode), "dV" (None in shared mode)}; `out` may supply
+        those tensors."""
+        d, q, dt = self.d_model, self.q, self.torch_dtype
+        total_cand, total_kv = Z.shape[0], K.shape[0]
+        R = cu_seqlens_kv.numel() - 1
+        self._check_tensor("Z", Z, dt, (total_cand, q, d))
+        self._check_tensor("W_Q", W_Q, dt, (q, d, d))
+        self._check_tensor("K", K, dt, (total_kv, d))
+        if V is not None:
+            self._check_tensor("V", V, dt, (total_kv, d))
+        self._check_tensor("dO", dO, dt, (total_cand, q, d))
+        self._check_tensor("cu_seqlens_kv", cu_seqlens_kv, torch.int32, (R + 1,))
+        self._check_tensor("cu_cand", cu_cand, torch.int32, (R + 1,))
+        out = dict(out or {})
+        dev = Z.device
+        if out.get("dZ") is None:
+            out["dZ"] = torch.empty((total_cand, q, d), dtype=dt, device=dev)
+        if out.get("dW_Q") is None:
+            out["dW_Q"] = torch.empty((q, d, d), dtype=torch.float32, device=dev)
+        if out.get("dK") is None:
+            out["dK"] = torch.empty((total_kv, d), dtype=dt, device=dev)
+        if V is not None and out.get("dV") is None:
+            out["dV"] = torch.empty((total_kv, d), dtype=dt, device=dev)
+        if V is None:
+            out["dV"] = None
+        self._check_tensor("dZ", out["dZ"], dt, (total_cand, q, d))
+        self._check_tensor("dW_Q", out["dW_Q"], torch.float32, (q, d, d))
+        self._check_tensor("dK", out["dK"], dt, (total_kv, d))
+        if V is not None:
+            self._check_tensor("dV", out["dV"], dt, (total_kv, d))
+        if workspace is None:
+            n = self.backward_workspace_size(R, total_cand, total_kv, heads)
+            workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+        _check(lib().xattn_backward(self._h, _ptr(Z), _ptr(W_Q), _ptr(K), _ptr(V), _ptr(dO),
+                                    _ptr(cu_seqlens_kv), _ptr(cu_cand), R, total_cand, total_kv,
+                                    heads, _ptr(out["dZ"]), _ptr(out["dW_Q"]), _ptr(out["dK"]),
+                                    _ptr(out["dV"]), _ptr(workspace), workspace.numel(),
+                                    _stream(dev, stream)))
+        return out
 
     def plan(self, cu_seqlens_kv, cu_cand, heads: int, total_cand: int, total_kv: int,
              with_row_req: bool = True, workspace=None, stream=None):

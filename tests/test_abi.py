@@ -231,3 +231,36 @@ def test_attend_q_prefix_host_validation(L):
     assert aq(Q=None) == X.XATTN_EINVAL
     assert aq(cl=None, tc=-1) == X.XATTN_EINVAL
     L.xattn_destroy(h)
+
+
+def test_backward_host_validation(L):
+    st, h = _create(L, 256, 3, X.XATTN_BF16, X.XATTN_KV_SHARED)
+    assert st == 0
+    need = L.xattn_backward_workspace_size(h, 2, 10, 20, 4)
+    assert need > 0
+    assert L.xattn_backward_workspace_size(h, 2, 10, 20, 3) == 0     # 3 does not divide 256
+    assert L.xattn_backward_workspace_size(None, 2, 10, 20, 4) == 0
+
+    def bwd(h_=h, Z=FAKE, W=FAKE, K=FAKE, V=None, dO=FAKE, R=2, tc=10, tkv=20, heads=4,
+            dZ=FAKE, dW=FAKE, dK=FAKE, dV=None, ws=FAKE, wsb=need):
+        return L.xattn_backward(h_, Z, W, K, V, dO, FAKE, FAKE, R, tc, tkv, heads, dZ, dW, dK,
+                                dV, ws, wsb, None)
+
+    assert bwd(h_=None) == X.XATTN_EINVAL
+    assert bwd(V=FAKE) == X.XATTN_EINVAL           # shared mode: no V
+    assert bwd(dV=FAKE) == X.XATTN_EINVAL          # shared mode: dK is dH
+    for kw in ({"Z": None}, {"W": None}, {"K": None}, {"dO": None}, {"dZ": None},
+               {"dW": None}, {"dK": None}):
+        assert bwd(**kw) == X.XATTN_EINVAL, kw
+    assert bwd(heads=16) == X.XATTN_EUNSUPPORTED
+    assert bwd(ws=None) == X.XATTN_EWORKSPACE
+    assert bwd(wsb=need - 1) == X.XATTN_EWORKSPACE
+    assert bwd(R=0, tc=5, tkv=0) == X.XATTN_EINVAL
+    L.xattn_destroy(h)
+    st, h = _create(L, 256, 1, X.XATTN_BF16, X.XATTN_KV_SEPARATE)
+    need = L.xattn_backward_workspace_size(h, 2, 10, 20, 4)
+    assert L.xattn_backward(h, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 2, 10, 20, 4, FAKE, FAKE,
+                            FAKE, FAKE, FAKE, need, None) == X.XATTN_EINVAL
+    assert L.xattn_backward(h, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 10, 20, 4, FAKE, FAKE,
+                            FAKE, None, FAKE, need, None) == X.XATTN_EINVAL
+    L.xattn_destroy(h)
