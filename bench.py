@@ -33,6 +33,7 @@ _ATTN_SRC = ["shared_history_candidate_amd/csrc/attn_bf16.hip",
              "shared_history_candidate_amd/csrc/plan_wave.h",
              "shared_history_candidate_amd/csrc/common.h"]
 KERNEL_SOURCES = {"fused": _ATTN_SRC, "attention": _ATTN_SRC, "prefix": _ATTN_SRC,
+                  "backward": ["shared_history_candidate_amd/csrc/bwd_bf16.hip"] + _ATTN_SRC,
                   "output": ["shared_history_candidate_amd/csrc/gemm_bf16.hip",
                              "shared_history_candidate_amd/csrc/common.h"],
                   "projection": ["shared_history_candidate_amd/csrc/gemm_bf16.hip",
@@ -50,10 +51,12 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--stage", default="attention", choices=("attention", "output", "prefix"),
+    p.add_argument("--stage", default="attention",
+                   choices=("attention", "output", "prefix", "backward"),
                    help="attention: the hot path (xattn_forward, the default); output: the "
                         "gate and output projection of Eq. (7) alone (xattn_output); prefix: "
-                        "the forward with per-candidate prefix lengths (xattn_forward_prefix)")
+                        "the forward with per-candidate prefix lengths (xattn_forward_prefix); "
+                        "backward: the gradients of the attention (xattn_backward)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="run only a plain device copy of this many MiB (counter calibration)")
     p.add_argument("--ingest-counters", metavar="DIR",
@@ -206,6 +209,8 @@ def cpu_baseline(wl, target_s, stage="attention", seed=0):
     oracle.set_threads(threads)
     rng = np.random.default_rng(1)
     kv_len = W.prefix_lengths(wl, seed + 3, out_of_range=False) if stage == "prefix" else None
+    if stage == "backward":
+        return _cpu_baseline_backward(wl, target_s, seed, threads)
     if stage == "output":
         wgo, wo = W.output_weights(wl, seed + 1)
         O_in = W.attention_like(wl, seed + 2)
@@ -237,6 +242,36 @@ def cpu_baseline(wl, target_s, stage="attention", seed=0):
                  "of the batch when it fits)" % (done, runs)
     return {"value": done / elapsed, "unit": "candidate-queries/s", "cores": threads,
             "kind": "oracle", "sample": sample, "seconds": round(elapsed, 2)}
+
+
+def _cpu_baseline_backward(wl, target_s, seed, threads):
+    """The oracle's backward on the batch's first k requests (a gradient of a
+    memory needs every query row of its request), k doubled until the run
+    takes about target_s; rows of those requests per second."""
+    import numpy as np
+    import oracle
+    from shared_history_candidate_amd import workloads as W
+    dO = W.output_grad(wl, seed + 4).reshape(-1, wl.d)
+    k, done, elapsed, runs = 1, 0, 0.0, 0
+    while True:
+        cu_kv = wl.cu_kv[:k + 1]
+        cu_c = wl.cu_cand[:k + 1]
+        rows = int(cu_c[-1]) * wl.q
+        kv = int(cu_kv[-1])
+        t0 = time.perf_counter()
+        oracle.backward(cu_kv, cu_c, wl.q, wl.heads, wl.Z.reshape(-1, wl.d)[:rows], wl.wt,
+                        wl.K[:kv], wl.V[:kv] if wl.V is not None else None, dO[:rows])
+        dt = time.perf_counter() - t0
+        done += rows
+        elapsed += dt
+        runs += 1
+        if elapsed >= target_s or k >= wl.R:
+            break
+        k = min(wl.R, k * 2)
+    return {"value": done / elapsed, "unit": "candidate-queries/s", "cores": threads,
+            "kind": "oracle", "seconds": round(elapsed, 2),
+            "sample": "backward of the first requests of the batch (%d query rows in %d oracle "
+                      "calls, up to %d of %d requests)" % (done, runs, k, wl.R)}
 
 
 def calib_copy(mib):
@@ -299,6 +334,18 @@ def main():
 
         def step():
             ctx.output(t["Z"], Wgo_d, O_in, Wo_d, ws, Y=O, stream=stream)
+    elif args.stage == "backward":
+        dO_d = torch.from_numpy(W.output_grad(wl, args.seed + 4)).to("cuda").to(
+            ctx.torch_dtype).contiguous()
+        grads = ctx.backward(t["Z"], t["W_Q"], t["K"], t["V"], dO_d, t["cu_kv"], t["cu_cand"],
+                             wl.heads)
+        bws = torch.empty(max(ctx.backward_workspace_size(wl.R, wl.total_cand, wl.total_kv,
+                                                          wl.heads), 256),
+                          dtype=torch.uint8, device="cuda")
+
+        def step():
+            ctx.backward(t["Z"], t["W_Q"], t["K"], t["V"], dO_d, t["cu_kv"], t["cu_cand"],
+                         wl.heads, workspace=bws, out=grads, stream=stream)
     elif args.stage == "prefix":
         # per-candidate prefix lengths: sorted draws from U{0..L_r} per request
         kv_len = W.prefix_lengths(wl, args.seed + 3, out_of_range=False)
@@ -352,7 +399,14 @@ def main():
                     algorithmic_flops=flops, algorithmic_bytes=nbytes,
                     traffic=traffic_for(kernel, args.config), kernel=kernel)
 
-    if args.stage == "output":
+    if args.stage == "backward":
+        # eight launches (plans, projection, statistics, dQ, dK/dV, transpose,
+        # dZ, dW_Q) timed as one unit; the per-kernel split is in the trace
+        bwd_ms = per_launch_ms(step)
+        print("bench: backward %.4f ms" % bwd_ms, file=sys.stderr, flush=True)
+        roof = entry("backward", wl.flops_backward(), wl.bytes_backward(), bwd_ms)
+        roof["other_kernel"] = None
+    elif args.stage == "output":
         # gate GEMM (sigmoid and product with O in its epilogue) + W_o GEMM
         out_ms = per_launch_ms(step)
         print("bench: output stage %.4f ms" % out_ms, file=sys.stderr, flush=True)
@@ -402,7 +456,9 @@ def main():
                    "stage": {"attention": "forward (attention path)",
                              "output": "output gate and projection",
                              "prefix": "forward with per-candidate prefix lengths "
-                                       "(sorted U{0..L_r} per request)"}[args.stage]},
+                                       "(sorted U{0..L_r} per request)",
+                             "backward": "backward pass (gradients of Z, W_Q, K/V for a "
+                                         "N(0,1) dO)"}[args.stage]},
         "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

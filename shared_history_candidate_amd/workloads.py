@@ -124,6 +124,20 @@ class Workload:
         L = np.repeat(self.lengths, self.cands)
         return np.clip(np.asarray(kv_len, dtype=np.int64), 0, L)
 
+    def flops_backward(self) -> float:
+        """Algorithmic FLOPs of the backward pass: scores recomputed, dP, dQ,
+        dK and dV (10 * sum_r M_r * L_r * d), dZ and dW_Q (4 * rows * d * d)."""
+        m = self.cands.astype(np.float64) * self.q
+        return 10.0 * float(np.sum(m * self.lengths)) * self.d + 4.0 * self.rows * self.d * self.d
+
+    def bytes_backward(self) -> float:
+        """Algorithmic bytes of the backward pass: Z, W_Q, K (and V), dO in;
+        dZ, dK (and dV) out, dW_Q out in fp32."""
+        b = 2 if self.dtype == "bf16" else 4
+        kv = (1 if self.kv_mode == "shared" else 2) * self.total_kv * self.d
+        return float(b * (3 * self.rows * self.d + self.q * self.d * self.d + 2 * kv)
+                     + 4 * self.q * self.d * self.d)
+
     def flops_output(self) -> float:
         """FLOPs of the gate and output projections of Eq. (7): 4 * rows * d * d."""
         return 4.0 * self.rows * self.d * self.d
