@@ -52,11 +52,12 @@ def parse():
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--stage", default="attention",
-                   choices=("attention", "output", "prefix", "backward"),
+                   choices=("attention", "output", "prefix", "backward", "backward_prefix"),
                    help="attention: the hot path (xattn_forward, the default); output: the "
                         "gate and output projection of Eq. (7) alone (xattn_output); prefix: "
                         "the forward with per-candidate prefix lengths (xattn_forward_prefix); "
-                        "backward: the gradients of the attention (xattn_backward)")
+                        "backward: the gradients of the attention (xattn_backward); "
+                        "backward_prefix: the same with per-candidate prefix lengths")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="run only a plain device copy of this many MiB (counter calibration)")
     p.add_argument("--ingest-counters", metavar="DIR",
@@ -208,9 +209,11 @@ def cpu_baseline(wl, target_s, stage="attention", seed=0):
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     oracle.set_threads(threads)
     rng = np.random.default_rng(1)
-    kv_len = W.prefix_lengths(wl, seed + 3, out_of_range=False) if stage == "prefix" else None
-    if stage == "backward":
-        return _cpu_baseline_backward(wl, target_s, seed, threads)
+    kv_len = (W.prefix_lengths(wl, seed + 3, out_of_range=False)
+              if stage in ("prefix", "backward_prefix") else None)
+    if stage in ("backward", "backward_prefix"):
+        return _cpu_baseline_backward(wl, target_s, seed, threads,
+                                      kv_len if stage == "backward_prefix" else None)
     if stage == "output":
         wgo, wo = W.output_weights(wl, seed + 1)
         O_in = W.attention_like(wl, seed + 2)
@@ -244,7 +247,7 @@ def cpu_baseline(wl, target_s, stage="attention", seed=0):
             "kind": "oracle", "sample": sample, "seconds": round(elapsed, 2)}
 
 
-def _cpu_baseline_backward(wl, target_s, seed, threads):
+def _cpu_baseline_backward(wl, target_s, seed, threads, kv_len=None):
     """The oracle's backward on the batch's first k requests (a gradient of a
     memory needs every query row of its request), k doubled until the run
     takes about target_s; rows of those requests per second."""
@@ -260,7 +263,8 @@ def _cpu_baseline_backward(wl, target_s, seed, threads):
         kv = int(cu_kv[-1])
         t0 = time.perf_counter()
         oracle.backward(cu_kv, cu_c, wl.q, wl.heads, wl.Z.reshape(-1, wl.d)[:rows], wl.wt,
-                        wl.K[:kv], wl.V[:kv] if wl.V is not None else None, dO[:rows])
+                        wl.K[:kv], wl.V[:kv] if wl.V is not None else None, dO[:rows],
+                        kv_len=kv_len[:int(cu_c[-1])] if kv_len is not None else None)
         dt = time.perf_counter() - t0
         done += rows
         elapsed += dt
@@ -334,18 +338,21 @@ def main():
 
         def step():
             ctx.output(t["Z"], Wgo_d, O_in, Wo_d, ws, Y=O, stream=stream)
-    elif args.stage == "backward":
+    elif args.stage in ("backward", "backward_prefix"):
         dO_d = torch.from_numpy(W.output_grad(wl, args.seed + 4)).to("cuda").to(
             ctx.torch_dtype).contiguous()
+        kv_len = (W.prefix_lengths(wl, args.seed + 3, out_of_range=False)
+                  if args.stage == "backward_prefix" else None)
+        cl = torch.from_numpy(kv_len).to("cuda") if kv_len is not None else None
         grads = ctx.backward(t["Z"], t["W_Q"], t["K"], t["V"], dO_d, t["cu_kv"], t["cu_cand"],
-                             wl.heads)
+                             wl.heads, cand_kv_len=cl)
         bws = torch.empty(max(ctx.backward_workspace_size(wl.R, wl.total_cand, wl.total_kv,
                                                           wl.heads), 256),
                           dtype=torch.uint8, device="cuda")
 
         def step():
             ctx.backward(t["Z"], t["W_Q"], t["K"], t["V"], dO_d, t["cu_kv"], t["cu_cand"],
-                         wl.heads, workspace=bws, out=grads, stream=stream)
+                         wl.heads, workspace=bws, out=grads, stream=stream, cand_kv_len=cl)
     elif args.stage == "prefix":
         # per-candidate prefix lengths: sorted draws from U{0..L_r} per request
         kv_len = W.prefix_lengths(wl, args.seed + 3, out_of_range=False)
@@ -399,12 +406,12 @@ def main():
                     algorithmic_flops=flops, algorithmic_bytes=nbytes,
                     traffic=traffic_for(kernel, args.config), kernel=kernel)
 
-    if args.stage == "backward":
+    if args.stage in ("backward", "backward_prefix"):
         # eight launches (plans, projection, statistics, dQ, dK/dV, transpose,
         # dZ, dW_Q) timed as one unit; the per-kernel split is in the trace
         bwd_ms = per_launch_ms(step)
         print("bench: backward %.4f ms" % bwd_ms, file=sys.stderr, flush=True)
-        roof = entry("backward", wl.flops_backward(), wl.bytes_backward(), bwd_ms)
+        roof = entry("backward", wl.flops_backward(kv_len), wl.bytes_backward(), bwd_ms)
         roof["other_kernel"] = None
     elif args.stage == "output":
         # gate GEMM (sigmoid and product with O in its epilogue) + W_o GEMM
@@ -458,7 +465,9 @@ def main():
                              "prefix": "forward with per-candidate prefix lengths "
                                        "(sorted U{0..L_r} per request)",
                              "backward": "backward pass (gradients of Z, W_Q, K/V for a "
-                                         "N(0,1) dO)"}[args.stage]},
+                                         "N(0,1) dO)",
+                             "backward_prefix": "backward pass with per-candidate prefix "
+                                                "lengths (sorted U{0..L_r} per request)"}[args.stage]},
         "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -238,6 +238,9 @@ size_t xattn_backward_workspace_size(const xattn_ctx* ctx, int32_t num_requests,
  *   - dK  [total_kv][d] context type.  In XATTN_KV_SHARED mode this is the
  *     gradient of H, which is both key and value (dV must be NULL).
  *   - dV  [total_kv][d] context type in XATTN_KV_SEPARATE mode.
+ *   - cand_kv_len [total_cand] int32 or NULL: the per-candidate prefix of
+ *     xattn_forward_prefix (the backward of that forward); NULL for the
+ *     backward of xattn_forward.
  * Memory rows that no query row sees get zero gradient; requests without
  * memory rows give zero dZ.  The forward statistics (softmax normaliser and
  * <dO, O> per row and head) are recomputed inside; every reduction runs in a
@@ -254,6 +257,7 @@ xattn_status xattn_backward(xattn_ctx* ctx,
                             const void* Z, const void* W_Q,
                             const void* K, const void* V, const void* dO,
                             const int32_t* cu_seqlens_kv, const int32_t* cu_cand,
+                            const int32_t* cand_kv_len,
                             int32_t num_requests, int32_t total_cand,
                             int32_t total_kv, int32_t heads,
                             void* dZ, float* dW_Q, void* dK, void* dV,

@@ -404,7 +404,7 @@ namespace {
 // forward statistics lse and D, dQ, the transposed W_Q and, in bf16, the
 // split-K partials of dW_Q.  Every region starts 256-byte aligned.
 struct BwdLayout {
-    size_t plan, kplan, qs, lse, dsum, dq, wt, part, total;
+    size_t plan, kplan, qs, lse, dsum, dq, wt, part, vis, total;
     int nch;
     int64_t max_q, max_k;
 };
@@ -434,6 +434,8 @@ BwdLayout bwd_layout(const xattn_config& c, int R, int total_cand, int total_kv,
     off = al(off + (size_t)c.n_slots * d * d * eb);
     L.part = off;
     off = al(off + (size_t)L.nch * c.n_slots * d * d * 4);
+    L.vis = off;
+    off = al(off + (size_t)total_cand * 4);
     L.total = off;
     return L;
 }
@@ -450,7 +452,8 @@ size_t xattn_backward_workspace_size(const xattn_ctx* ctx, int32_t R, int32_t to
 
 xattn_status xattn_backward(xattn_ctx* ctx, const void* Z, const void* W_Q, const void* K,
                             const void* V, const void* dO, const int32_t* cu_kv,
-                            const int32_t* cu_cand, int32_t R, int32_t total_cand,
+                            const int32_t* cu_cand, const int32_t* cand_kv_len, int32_t R,
+                            int32_t total_cand,
                             int32_t total_kv, int32_t heads, void* dZ, float* dW_Q, void* dK,
                             void* dV, void* workspace, size_t workspace_bytes_, void* stream) {
     g_last_error.clear();
@@ -516,6 +519,11 @@ xattn_status xattn_backward(xattn_ctx* ctx, const void* Z, const void* W_Q, cons
     XATTN_TRY(xattn::launch_plan(cu_cand, cu_kv, R, 1, 64, total_kv, total_cand, ws + Lw.kplan,
                                  Lw.max_k, nullptr, nullptr, nullptr, nullptr, s),
               "memory plan kernel launch");
+    // per-candidate prefix: absolute end of each candidate's visible memory
+    int* vis = cand_kv_len ? reinterpret_cast<int*>(ws + Lw.vis) : nullptr;
+    if (vis)
+        XATTN_TRY(xattn::launch_prefix_vis(cu_kv, cu_cand, cand_kv_len, R, total_cand, vis, s),
+                  "prefix kernel launch");
     // 3. forward statistics lse and D = <dO, O> per row and head
     float* lse = reinterpret_cast<float*>(ws + Lw.lse);
     float* dsum = reinterpret_cast<float*>(ws + Lw.dsum);
@@ -535,6 +543,7 @@ xattn_status xattn_backward(xattn_ctx* ctx, const void* Z, const void* W_Q, cons
         a.d = d;
         a.heads = heads;
         a.prescaled = 1;
+        a.cand_len = cand_kv_len;
         a.lse = lse;
         a.Dsum = dsum;
         a.dO = dO;
@@ -544,7 +553,7 @@ xattn_status xattn_backward(xattn_ctx* ctx, const void* Z, const void* W_Q, cons
         XATTN_TRY(xattn::launch_attn_f32_stats(reinterpret_cast<const float*>(ws + Lw.qs),
                                                static_cast<const float*>(K),
                                                sep ? static_cast<const float*>(V) : nullptr,
-                                               ws + Lw.plan, Lw.max_q, q, d, heads,
+                                               ws + Lw.plan, cand_kv_len, Lw.max_q, q, d, heads,
                                                static_cast<const float*>(dO), lse, dsum, s),
                   "statistics kernel launch");
     }
@@ -559,6 +568,7 @@ xattn_status xattn_backward(xattn_ctx* ctx, const void* Z, const void* W_Q, cons
     b.Dsum = dsum;
     b.plan = reinterpret_cast<const int*>(ws + Lw.plan);
     b.kplan = reinterpret_cast<const int*>(ws + Lw.kplan);
+    b.vis = vis;
     b.dQ = ws + Lw.dq;
     b.dK = dK;
     b.dV = sep ? dV : nullptr;

@@ -7,6 +7,8 @@
 // work-group of 64 threads per plan work item and head, thread i owning query
 // column c0 + i; memory rows stream through LDS in tiles of 32 and each
 // thread applies the online-softmax update once per tile.
+#include <climits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -195,6 +197,8 @@ __global__ __launch_bounds__(kRows) void bwd_dq_f32_kernel(BwdArgs a) {
         dq[e] = 0.f;
     }
     const float lse = a.lse[row * heads + h], Dr = a.Dsum[row * heads + h];
+    // visible memory rows of this thread's candidate (prefix cutoff)
+    const int Lc = a.vis && valid ? a.vis[c0 + i] - kv0 : L;
     for (int j0 = 0; j0 < L; j0 += kBN) {
         const int nj = min(kBN, L - j0);
         __syncthreads();
@@ -207,6 +211,7 @@ __global__ __launch_bounds__(kRows) void bwd_dq_f32_kernel(BwdArgs a) {
         }
         __syncthreads();
         for (int j = 0; j < nj; ++j) {
+            if (j0 + j >= Lc) break;
             float sc = 0.f, dp = 0.f;
 #pragma unroll
             for (int e = 0; e < DHMAX; ++e) {
@@ -231,6 +236,7 @@ __global__ __launch_bounds__(kRows) void bwd_dkv_f32_kernel(BwdArgs a) {
     __shared__ float qs[kBN][DHMAX];
     __shared__ float ds_[kBN][DHMAX];
     __shared__ float ls[kBN], Ds[kBN];
+    __shared__ int vis_[kBN];
     const int q = a.q, d = a.d, heads = a.heads, dh = d / heads;
     const float scale_log2 = 1.4426950408889634f * a.scale;
     const int tile = blockIdx.x / heads;
@@ -269,9 +275,11 @@ __global__ __launch_bounds__(kRows) void bwd_dkv_f32_kernel(BwdArgs a) {
         if (j < ni) {
             ls[j] = a.lse[(size_t)(row0 + i0 + j) * heads + h];
             Ds[j] = a.Dsum[(size_t)(row0 + i0 + j) * heads + h];
+            vis_[j] = a.vis ? a.vis[(row0 + i0 + j) / q] : INT_MAX;
         }
         __syncthreads();
         for (int i = 0; i < ni; ++i) {
+            if ((int)key >= vis_[i]) continue;   // the row does not see this memory row
             float sc = 0.f, dp = 0.f;
 #pragma unroll
             for (int e = 0; e < DHMAX; ++e) {
@@ -349,11 +357,11 @@ hipError_t launch_attn_f32(const float* Qp, const float* K, const float* V,
 }
 
 hipError_t launch_attn_f32_stats(const float* Qp, const float* K, const float* V, const void* ws,
-                                 int64_t max_tiles, int q, int d, int heads, const float* dO,
-                                 float* lse, float* Dsum, hipStream_t stream) {
+                                 const int* cand_len, int64_t max_tiles, int q, int d, int heads,
+                                 const float* dO, float* lse, float* Dsum, hipStream_t stream) {
     const int dh = d / heads;
 #define XATTN_F32S(N_) \
-    if (dh <= N_) return launch_f32<N_>(Qp, K, V, ws, nullptr, max_tiles, q, d, heads, nullptr, stream, dO, lse, Dsum);
+    if (dh <= N_) return launch_f32<N_>(Qp, K, V, ws, cand_len, max_tiles, q, d, heads, nullptr, stream, dO, lse, Dsum);
     XATTN_F32S(8)
     XATTN_F32S(16)
     XATTN_F32S(32)

@@ -79,7 +79,7 @@ struct DqCfg {
     static constexpr int CPT = kBN * DH / 8 / NT;   // 16-byte chunks per thread and plane
 };
 
-template <int DH, bool SEP>
+template <int DH, bool SEP, bool CUT>
 __global__ __launch_bounds__(128) void bwd_dq_kernel(BwdArgs a) {
     using C = DqCfg<DH, SEP>;
     __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
@@ -119,6 +119,19 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) seed_s[r] = -lse, seed_p[r] = -Dr;
 
+    // Per-candidate prefix (CUT): this lane's query row sees memory rows
+    // [0, cut); the tile loop runs to the largest cut of the work-group's
+    // candidates (computed identically by both waves).
+    int cut = L, L_loop = L;
+    if constexpr (CUT) {
+        cut = qvalid ? a.vis[c0 + qcol] - kv0 : L;
+        int mx = 0;
+        for (int i = lane; i < nc; i += 64) mx = max(mx, a.vis[c0 + i] - kv0);
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) mx = max(mx, __shfl_xor(mx, off, 64));
+        L_loop = __builtin_amdgcn_readfirstlane(mx);
+    }
+
     const bf16* Kh = static_cast<const bf16*>(a.K) + (size_t)kv0 * d + h * DH;
     const bf16* Vh = SEP ? static_cast<const bf16*>(a.V) + (size_t)kv0 * d + h * DH : Kh;
     int goff[C::CPT], loff[C::CPT];
@@ -132,7 +145,7 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(BwdArgs a) {
     uint4 kr[C::CPT], vr[SEP ? C::CPT : 1];
     // tile t of the request's memory; rows past L read as zeros
     auto gload = [&](int t) {
-        const long long left = (long long)(L - t * kBN) * d * 2;
+        const long long left = (long long)(L_loop - t * kBN) * d * 2;
         const __amdgpu_buffer_rsrc_t rk = rsrc(Kh + (size_t)t * kBN * d, left);
 #pragma unroll
         for (int u = 0; u < C::CPT; ++u) kr[u] = bload(rk, goff[u]);
@@ -152,7 +165,7 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(BwdArgs a) {
         }
     };
 
-    const int ntiles = (L + kBN - 1) / kBN;
+    const int ntiles = (L_loop + kBN - 1) / kBN;
     gload(0);
     lstore(0);
     gload(1);
@@ -182,8 +195,9 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(BwdArgs a) {
                 sacc[hh] = mfma32(kf, qb[k], sacc[hh]);
                 pacc[hh] = mfma32(SEP ? ld8(vb + off) : kf, db[k], pacc[hh]);
             }
-        // dS^T = P^T o (dP^T - D), rows past the request's memory masked
-        const int jleft = L - t * kBN;
+        // dS^T = P^T o (dP^T - D), rows past the request's memory (or past
+        // the lane's prefix) masked
+        const int jleft = (CUT ? cut : L) - t * kBN;
         bf16x8 dsb[4];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
@@ -191,7 +205,7 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(BwdArgs a) {
             for (int rr = 0; rr < 16; ++rr) {
                 const int j = hh * 32 + (rr >> 2) * 8 + 4 * g + (rr & 3);
                 float p = __builtin_amdgcn_exp2f(sacc[hh][rr]);
-                if (jleft < kBN && j >= jleft) p = 0.f;
+                if (CUT ? j >= jleft : (jleft < kBN && j >= jleft)) p = 0.f;
                 dsb[hh * 2 + (rr >> 3)][rr & 7] = (bf16)(p * pacc[hh][rr]);
             }
         // dQ^T += K^T dS^T over the four 16-key slabs of the tile
@@ -231,7 +245,7 @@ struct DkvCfg {
     static constexpr int EB = DH / 32, KST = DH / 16;
     static constexpr int LDQ = DH + 8;
     static constexpr int TILE = kBQ * LDQ;                       // elements of one row tile
-    static constexpr int STAGE = 2 * TILE * 2 + 2 * kBQ * 4;     // Qs, dO tiles + lse, D (bytes)
+    static constexpr int STAGE = 2 * TILE * 2 + 3 * kBQ * 4;     // Qs, dO tiles + lse, D, visible end
     static constexpr int STG_BYTES = MS * 2 * STAGE;             // double-buffered per split
     static constexpr int CMB_BYTES = (MS - 1) * WK * 64 * 2 * EB * 16 * 4;
     static constexpr int SMEM = STG_BYTES > CMB_BYTES ? STG_BYTES : CMB_BYTES;
@@ -239,7 +253,7 @@ struct DkvCfg {
     static_assert(CPT >= 1 && kBQ * DH / 8 % (64 * WK) == 0, "row tile must split evenly");
 };
 
-template <int DH, bool SEP>
+template <int DH, bool SEP, bool CUT>
 __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdArgs a) {
     using C = DkvCfg<DH, SEP>;
     __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
@@ -291,7 +305,7 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdArgs a) {
         loff[u] = i * C::LDQ + c8 * 8;
     }
     uint4 qr[C::CPT], dr[C::CPT];
-    float sr = 0.f;   // lse (threads 0..31 of the group) or D (32..63)
+    float sr = 0.f;   // lse (threads 0..31 of the group), D (32..63), visible end (64..95)
     auto gload = [&](int tq) {
         const long long left = (long long)(M - tq * kBQ) * d * 2;
         const __amdgpu_buffer_rsrc_t rq = rsrc(Qh + (size_t)tq * kBQ * d, left);
@@ -301,11 +315,16 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdArgs a) {
             qr[u] = bload(rq, goff[u]);
             dr[u] = bload(rd, goff[u]);
         }
-        if (gt < 2 * kBQ) {
+        if (gt < (CUT ? 3 : 2) * kBQ) {
             const int i = tq * kBQ + (gt & (kBQ - 1));
             const size_t idx = ((size_t)row0 + i) * heads + h;
             // rows past the request: lse = +inf gives zero weight, D = 0
-            sr = gt < kBQ ? (i < M ? a.lse[idx] : INFINITY) : (i < M ? a.Dsum[idx] : 0.f);
+            if (gt < kBQ)
+                sr = i < M ? a.lse[idx] : INFINITY;
+            else if (gt < 2 * kBQ)
+                sr = i < M ? a.Dsum[idx] : 0.f;
+            else   // absolute end of the row's visible memory (an int in a float slot)
+                sr = __builtin_bit_cast(float, i < M ? a.vis[(row0 + i) / q] : 0);
         }
     };
     char* stg = smem + ms * 2 * C::STAGE;
@@ -317,7 +336,7 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdArgs a) {
             *reinterpret_cast<uint4*>(qt + loff[u]) = qr[u];
             *reinterpret_cast<uint4*>(dt + loff[u]) = dr[u];
         }
-        if (gt < 2 * kBQ) reinterpret_cast<float*>(dt + C::TILE)[gt] = sr;
+        if (gt < (CUT ? 3 : 2) * kBQ) reinterpret_cast<float*>(dt + C::TILE)[gt] = sr;
     };
 
     gload(ms);
@@ -353,10 +372,21 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdArgs a) {
                 sacc = mfma32(ld8(qt + off), kb[k], sacc);
                 pacc = mfma32(ld8(dt + off), vb[k], pacc);
             }
+            int vis[16];
+            if constexpr (CUT) {
+                const int* vt = reinterpret_cast<const int*>(Dt + kBQ);
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    const int4 v4 = *reinterpret_cast<const int4*>(vt + 8 * a4 + 4 * g);
+                    vis[4 * a4] = v4.x, vis[4 * a4 + 1] = v4.y;
+                    vis[4 * a4 + 2] = v4.z, vis[4 * a4 + 3] = v4.w;
+                }
+            }
             bf16x8 pb[2], dsb[2];
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
-                const float p = __builtin_amdgcn_exp2f(sacc[rr]);
+                float p = __builtin_amdgcn_exp2f(sacc[rr]);
+                if constexpr (CUT) p = (int)key < vis[rr] ? p : 0.f;   // row sees this memory row?
                 pb[rr >> 3][rr & 7] = (bf16)p;
                 dsb[rr >> 3][rr & 7] = (bf16)(p * pacc[rr]);
             }
@@ -530,28 +560,45 @@ __global__ void bwd_transpose_kernel(const T* __restrict__ wt, int q, int d, T* 
     }
 }
 
+template <int DH, bool SEP, bool CUT>
+hipError_t launch_bwd_variant(const BwdArgs& a, int64_t q_items, int64_t k_items,
+                              hipStream_t stream) {
+    if (q_items > 0)
+        hipLaunchKernelGGL((bwd_dq_kernel<DH, SEP, CUT>), dim3((unsigned)(q_items * a.heads)),
+                           dim3(128), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (k_items > 0)
+        hipLaunchKernelGGL((bwd_dkv_kernel<DH, SEP, CUT>), dim3((unsigned)(k_items * a.heads)),
+                           dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
 template <int DH>
 hipError_t launch_dh_bwd(const BwdArgs& a, bool sep, int64_t q_items, int64_t k_items,
                          hipStream_t stream) {
-    if (q_items > 0) {
-        if (sep)
-            hipLaunchKernelGGL((bwd_dq_kernel<DH, true>), dim3((unsigned)(q_items * a.heads)),
-                               dim3(128), 0, stream, a);
-        else
-            hipLaunchKernelGGL((bwd_dq_kernel<DH, false>), dim3((unsigned)(q_items * a.heads)),
-                               dim3(128), 0, stream, a);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+    const bool cut = a.vis != nullptr;
+    if (sep)
+        return cut ? launch_bwd_variant<DH, true, true>(a, q_items, k_items, stream)
+                   : launch_bwd_variant<DH, true, false>(a, q_items, k_items, stream);
+    return cut ? launch_bwd_variant<DH, false, true>(a, q_items, k_items, stream)
+               : launch_bwd_variant<DH, false, false>(a, q_items, k_items, stream);
+}
+
+// vis[c] = cu_kv[r] + clamp(len[c], 0, L_r) for candidate c of request r
+__global__ void prefix_vis_kernel(const int* __restrict__ cu_kv, const int* __restrict__ cu_cand,
+                                  const int* __restrict__ len, int R, int total_cand,
+                                  int* __restrict__ vis) {
+    const int c = blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= total_cand) return;
+    int lo = 0, hi = R - 1;   // last r with cu_cand[r] <= c
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cu_cand[mid] <= c) lo = mid; else hi = mid - 1;
     }
-    if (k_items > 0) {
-        if (sep)
-            hipLaunchKernelGGL((bwd_dkv_kernel<DH, true>), dim3((unsigned)(k_items * a.heads)),
-                               dim3(256), 0, stream, a);
-        else
-            hipLaunchKernelGGL((bwd_dkv_kernel<DH, false>), dim3((unsigned)(k_items * a.heads)),
-                               dim3(256), 0, stream, a);
-    }
-    return hipGetLastError();
+    const int kv0 = cu_kv[lo], L = cu_kv[lo + 1] - kv0;
+    const int want = len[c];
+    vis[c] = kv0 + (want < 0 ? 0 : (want < L ? want : L));
 }
 
 }  // namespace
@@ -564,6 +611,14 @@ hipError_t launch_bwd_attn_bf16(const BwdArgs& a, bool sep, int64_t q_items, int
         case 128: return launch_dh_bwd<128>(a, sep, q_items, k_items, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_prefix_vis(const int* cu_kv, const int* cu_cand, const int* len, int R,
+                             int total_cand, int* vis, hipStream_t stream) {
+    if (total_cand <= 0) return hipSuccess;
+    hipLaunchKernelGGL(prefix_vis_kernel, dim3((unsigned)((total_cand + 255) / 256)), dim3(256),
+                       0, stream, cu_kv, cu_cand, len, R, total_cand, vis);
+    return hipGetLastError();
 }
 
 int bwd_dw_chunks(int total_cand, int q, int d) {

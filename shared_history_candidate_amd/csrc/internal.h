@@ -78,6 +78,8 @@ struct BwdArgs {
     const float* Dsum;
     const int* plan;
     const int* kplan;
+    // per-candidate end of the visible memory (absolute row), or NULL
+    const int* vis;
     void* dQ;
     void* dK;
     void* dV;
@@ -86,6 +88,9 @@ struct BwdArgs {
 };
 hipError_t launch_bwd_attn_bf16(const BwdArgs& a, bool sep, int64_t q_items, int64_t k_items,
                                 hipStream_t stream);
+// vis[c] = cu_kv[r] + clamp(len[c], 0, L_r) for each candidate c of request r
+hipError_t launch_prefix_vis(const int* cu_kv, const int* cu_cand, const int* len, int R,
+                             int total_cand, int* vis, hipStream_t stream);
 // dW_Q = sum over rows of slot s of dQ^T Z (fp32 [q][d][d], output-major),
 // nch split-K chunks through part ([nch][q][d][d] fp32) reduced in order.
 int bwd_dw_chunks(int total_cand, int q, int d);
@@ -99,8 +104,8 @@ hipError_t launch_bwd_dw_f32(const float* dQ, const float* Z, int total_cand, in
                              float* dW, hipStream_t stream);
 // fp32 forward statistics (lse, Dsum for the backward pass), O may be NULL.
 hipError_t launch_attn_f32_stats(const float* Qp, const float* K, const float* V, const void* ws,
-                                 int64_t max_tiles, int q, int d, int heads, const float* dO,
-                                 float* lse, float* Dsum, hipStream_t stream);
+                                 const int* cand_len, int64_t max_tiles, int q, int d, int heads,
+                                 const float* dO, float* lse, float* Dsum, hipStream_t stream);
 
 // fp32 path (tile_m = 64): attention over projected queries (cand_len: the
 // per-candidate prefix cutoff, or NULL), projection.

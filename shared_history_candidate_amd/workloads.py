@@ -124,11 +124,16 @@ class Workload:
         L = np.repeat(self.lengths, self.cands)
         return np.clip(np.asarray(kv_len, dtype=np.int64), 0, L)
 
-    def flops_backward(self) -> float:
+    def flops_backward(self, kv_len: Optional[np.ndarray] = None) -> float:
         """Algorithmic FLOPs of the backward pass: scores recomputed, dP, dQ,
-        dK and dV (10 * sum_r M_r * L_r * d), dZ and dW_Q (4 * rows * d * d)."""
-        m = self.cands.astype(np.float64) * self.q
-        return 10.0 * float(np.sum(m * self.lengths)) * self.d + 4.0 * self.rows * self.d * self.d
+        dK and dV (10 * sum_r M_r * L_r * d, or 10 * q * d * sum_c n_c with
+        per-candidate prefix lengths), dZ and dW_Q (4 * rows * d * d)."""
+        if kv_len is not None:
+            att = 10.0 * self.q * self.d * float(np.sum(self._visible(kv_len)))
+        else:
+            m = self.cands.astype(np.float64) * self.q
+            att = 10.0 * float(np.sum(m * self.lengths)) * self.d
+        return att + 4.0 * self.rows * self.d * self.d
 
     def bytes_backward(self) -> float:
         """Algorithmic bytes of the backward pass: Z, W_Q, K (and V), dO in;

@@ -76,8 +76,8 @@ def lib():
         L.xattn_attend_q_prefix.restype = ctypes.c_int
         L.xattn_backward_workspace_size.argtypes = [P, I32, I32, I32, I32]
         L.xattn_backward_workspace_size.restype = SZ
-        L.xattn_backward.argtypes = [P, P, P, P, P, P, P, P, I32, I32, I32, I32, P, P, P, P, P,
-                                     SZ, P]
+        L.xattn_backward.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, P, P, P, P,
+                                     P, SZ, P]
         L.xattn_backward.restype = ctypes.c_int
         L.xattn_plan.argtypes = [P, P, P, I32, I32, I32, I32, P, P, P, P,
                                  ctypes.POINTER(I32), P, SZ, P]
@@ -249,11 +249,12 @@ class XAttn:
                                                        total_kv, heads))
 
     def backward(self, Z, W_Q, K, V, dO, cu_seqlens_kv, cu_cand, heads: int, workspace=None,
-                 out=None, stream=None) -> dict:
+                 out=None, stream=None, cand_kv_len=None) -> dict:
         """Gradients of <dO, O> for O = forward(Z, W_Q, K, V, ...) (see
         include/xattn.h, xattn_backward): returns {"dZ", "dW_Q" (fp32), "dK"
         (dH in shared mode), "dV" (None in shared mode)}; `out` may supply
-        those tensors."""
+        those tensors.  cand_kv_len: the per-candidate prefix of
+        forward(..., cand_kv_len=...)."""
         d, q, dt = self.d_model, self.q, self.torch_dtype
         total_cand, total_kv = Z.shape[0], K.shape[0]
         R = cu_seqlens_kv.numel() - 1
@@ -265,6 +266,8 @@ class XAttn:
         self._check_tensor("dO", dO, dt, (total_cand, q, d))
         self._check_tensor("cu_seqlens_kv", cu_seqlens_kv, torch.int32, (R + 1,))
         self._check_tensor("cu_cand", cu_cand, torch.int32, (R + 1,))
+        if cand_kv_len is not None:
+            self._check_tensor("cand_kv_len", cand_kv_len, torch.int32, (total_cand,))
         out = dict(out or {})
         dev = Z.device
         if out.get("dZ") is None:
@@ -286,8 +289,8 @@ class XAttn:
             n = self.backward_workspace_size(R, total_cand, total_kv, heads)
             workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
         _check(lib().xattn_backward(self._h, _ptr(Z), _ptr(W_Q), _ptr(K), _ptr(V), _ptr(dO),
-                                    _ptr(cu_seqlens_kv), _ptr(cu_cand), R, total_cand, total_kv,
-                                    heads, _ptr(out["dZ"]), _ptr(out["dW_Q"]), _ptr(out["dK"]),
+                                    _ptr(cu_seqlens_kv), _ptr(cu_cand), _ptr(cand_kv_len), R,
+                                    total_cand, total_kv, heads, _ptr(out["dZ"]), _ptr(out["dW_Q"]), _ptr(out["dK"]),
                                     _ptr(out["dV"]), _ptr(workspace), workspace.numel(),
                                     _stream(dev, stream)))
         return out

@@ -243,8 +243,8 @@ def test_backward_host_validation(L):
 
     def bwd(h_=h, Z=FAKE, W=FAKE, K=FAKE, V=None, dO=FAKE, R=2, tc=10, tkv=20, heads=4,
             dZ=FAKE, dW=FAKE, dK=FAKE, dV=None, ws=FAKE, wsb=need):
-        return L.xattn_backward(h_, Z, W, K, V, dO, FAKE, FAKE, R, tc, tkv, heads, dZ, dW, dK,
-                                dV, ws, wsb, None)
+        return L.xattn_backward(h_, Z, W, K, V, dO, FAKE, FAKE, None, R, tc, tkv, heads, dZ, dW,
+                                dK, dV, ws, wsb, None)
 
     assert bwd(h_=None) == X.XATTN_EINVAL
     assert bwd(V=FAKE) == X.XATTN_EINVAL           # shared mode: no V
@@ -259,8 +259,8 @@ def test_backward_host_validation(L):
     L.xattn_destroy(h)
     st, h = _create(L, 256, 1, X.XATTN_BF16, X.XATTN_KV_SEPARATE)
     need = L.xattn_backward_workspace_size(h, 2, 10, 20, 4)
-    assert L.xattn_backward(h, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 2, 10, 20, 4, FAKE, FAKE,
-                            FAKE, FAKE, FAKE, need, None) == X.XATTN_EINVAL
-    assert L.xattn_backward(h, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 10, 20, 4, FAKE, FAKE,
-                            FAKE, None, FAKE, need, None) == X.XATTN_EINVAL
+    assert L.xattn_backward(h, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, 2, 10, 20, 4, FAKE,
+                            FAKE, FAKE, FAKE, FAKE, need, None) == X.XATTN_EINVAL
+    assert L.xattn_backward(h, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 2, 10, 20, 4, FAKE,
+                            FAKE, FAKE, None, FAKE, need, None) == X.XATTN_EINVAL
     L.xattn_destroy(h)

@@ -142,3 +142,70 @@ def test_backward_no_candidates():
     assert torch.count_nonzero(g["dK"]).item() == 0
     assert torch.count_nonzero(g["dV"]).item() == 0
     assert torch.count_nonzero(g["dW_Q"]).item() == 0
+
+
+# ---------------------------------------------------------------------------
+# Backward of the per-candidate prefix cutoff (ULT training batches)
+# ---------------------------------------------------------------------------
+def _check_prefix(wl, kv_len, seed=0, what=""):
+    dO = W.output_grad(wl, seed)
+    require_gpu()
+    ctx = ctx_for(wl)
+    t = X.to_device(wl)
+    cl = torch.from_numpy(np.ascontiguousarray(kv_len, dtype=np.int32)).to("cuda")
+    g = ctx.backward(t["Z"], t["W_Q"], t["K"], t["V"], _up(dO, ctx.torch_dtype), t["cu_kv"],
+                     t["cu_cand"], wl.heads, cand_kv_len=cl)
+    torch.cuda.synchronize()
+    ref = oracle.backward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, wl.K, wl.V, dO,
+                          kv_len=kv_len)
+    tol = BWD_BF16_NORM if wl.dtype == "bf16" else BWD_FP32_NORM
+    names = [("dZ", "dZ"), ("dW_Q", "dwt"), ("dK", "dK")] + ([("dV", "dV")] if wl.V is not None
+                                                             else [])
+    for gn, rn in names:
+        got = _np(g[gn], ref[rn].shape)
+        r = ref[rn]
+        err = float(np.max(np.abs(got - r)))
+        scale = float(np.max(np.abs(r)))
+        rel = err / scale if scale > 0 else err
+        print("prefix %s %s: max-abs %.3e normwise %.3e" % (what, gn, err, rel))
+        assert np.all(np.isfinite(got)) and rel <= tol, "%s %s normwise %.3e" % (what, gn, rel)
+
+
+@pytest.mark.parametrize("mode", ["shared", "separate"])
+@pytest.mark.parametrize("dh,heads", [(32, 4), (64, 2), (128, 2)])
+def test_backward_prefix_edge_bf16(mode, dh, heads):
+    wl = W.custom("edge", EDGE_LENGTHS, EDGE_CANDS, q=3, d=dh * heads, heads=heads,
+                  dtype="bf16", kv_mode=mode, seed=dh)
+    _check_prefix(wl, W.prefix_lengths(wl, seed=dh + 1), seed=2,
+                  what="edge dh=%d %s" % (dh, mode))
+
+
+@pytest.mark.parametrize("dh", [16, 64])
+@pytest.mark.parametrize("mode", ["shared", "separate"])
+def test_backward_prefix_fp32(dh, mode):
+    wl = W.custom("f32", [5, 70, 33, 130], [3, 70, 1, 20], q=2, d=dh * 2, heads=2,
+                  dtype="fp32", kv_mode=mode, seed=dh)
+    _check_prefix(wl, W.prefix_lengths(wl, seed=dh), seed=3, what="fp32 dh=%d %s" % (dh, mode))
+
+
+def test_backward_prefix_ragged_training_batch():
+    wl = W.make("ragged", 0)
+    _check_prefix(wl, W.prefix_lengths(wl, seed=4, out_of_range=False), seed=8, what="ragged")
+
+
+@pytest.mark.parametrize("name", ["rest", "ragged"])
+def test_backward_prefix_full_length_matches_plain(name):
+    """Cutoffs at or past L_r give the bits of the backward without cutoffs."""
+    require_gpu()
+    wl = W.make(name, 0)
+    dO = _up(W.output_grad(wl, 3), torch.bfloat16)
+    ctx = ctx_for(wl)
+    t = X.to_device(wl)
+    kv_len = np.repeat(wl.lengths, wl.cands).astype(np.int32)
+    kv_len[::2] += 77
+    a = ctx.backward(t["Z"], t["W_Q"], t["K"], t["V"], dO, t["cu_kv"], t["cu_cand"], wl.heads)
+    b = ctx.backward(t["Z"], t["W_Q"], t["K"], t["V"], dO, t["cu_kv"], t["cu_cand"], wl.heads,
+                     cand_kv_len=torch.from_numpy(kv_len).to("cuda"))
+    torch.cuda.synchronize()
+    for k in ("dZ", "dW_Q", "dK"):
+        assert torch.equal(a[k], b[k]), k
