@@ -263,6 +263,65 @@ xattn_status xattn_backward(xattn_ctx* ctx,
                             void* dZ, float* dW_Q, void* dK, void* dV,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* Coded memory (TransX technical report, s.3).  A published memory keeps,
+ * for every row and head, the length of the head's key (or value) vector and
+ * its direction rotated into the eigenbasis of the directions' covariance and
+ * quantised coordinate by coordinate, with more bits for coordinates of more
+ * energy under a fixed total.  The codebook (fitted offline on a sample of
+ * memory vectors) is device data:
+ *   rotation[h][o][i]  column i = i-th eigenvector of head h (fp32,
+ *                      [heads][d_h][d_h]);
+ *   bits[h][i]         bits of rotated coordinate i (uint8, 0..8), summing to
+ *                      budget_bits for every head;
+ *   center, half_range [heads][d_h] fp32: coordinate i is quantised
+ *                      uniformly on [center - half, center + half] (mid-rise,
+ *                      clamped; a coordinate with 0 bits reads as center).
+ * Codes are packed least-significant bit first, coordinate 0 first, into
+ * budget_bits/32 uint32 words per (row, head); codes [heads][rows][words],
+ * norms [heads][rows] fp32 (head-major, so one head's tile is contiguous).
+ * bf16 contexts only; d_h in {32, 64, 128}. */
+typedef struct {
+    int32_t budget_bits;      /* multiple of 32, at most 8 * d_h              */
+    const uint8_t* bits;      /* [heads][d_h]                                 */
+    const float* center;      /* [heads][d_h]                                 */
+    const float* half_range;  /* [heads][d_h], > 0 where bits > 0             */
+    const float* rotation;    /* [heads][d_h][d_h]                            */
+} xattn_codebook;
+
+/* Encode memory rows X [n_rows][d] (bf16) with codebook cb into codes and
+ * norms (layouts above).  The nearline publishing step. */
+xattn_status xattn_codec_encode(xattn_ctx* ctx, const xattn_codebook* cb, int32_t heads,
+                                const void* X, int32_t n_rows, uint32_t* codes, float* norms,
+                                void* stream);
+
+/* Query weights for a coded memory: W_Q_rot[s] = W_Q[s] with the rows of
+ * head h replaced by rotation_h^T times them (output-major like W_Q, bf16),
+ * so the projection delivers queries in the keys' rotated basis.  Weights
+ * are static: fold once per codebook. */
+xattn_status xattn_codec_fold_query_weights(xattn_ctx* ctx, const xattn_codebook* cb_k,
+                                            int32_t heads, const void* W_Q, void* W_Q_rot,
+                                            void* stream);
+
+/* xattn_forward over a coded memory: O[row, head h] = softmax(q_h k_h^T /
+ * sqrt(d_h)) v_h with every k, v the decoded vector norm * rotation *
+ * reconstruction.  Two launches: the projection GEMM over W_Q_rot (with the
+ * planner), then the attention kernel, which reconstructs each memory tile
+ * while staging it in LDS (HBM carries codes and norms only), accumulates in
+ * the rotated basis and rotates each output row back.  Shared mode: the
+ * memory is both key and value (cb_v, v_codes, v_norms NULL).  Separate mode:
+ * cb_v with the same budget_bits as cb_k.  Offsets, shapes, workspace
+ * (xattn_workspace_size) and errors as for xattn_forward; XATTN_EUNSUPPORTED
+ * in fp32 mode or for a budget that is not a positive multiple of 32 at
+ * most 8 * d_h. */
+xattn_status xattn_forward_codec(xattn_ctx* ctx, const xattn_codebook* cb_k,
+                                 const xattn_codebook* cb_v, const void* Z, const void* W_Q_rot,
+                                 const uint32_t* k_codes, const float* k_norms,
+                                 const uint32_t* v_codes, const float* v_norms,
+                                 const int32_t* cu_seqlens_kv, const int32_t* cu_cand,
+                                 int32_t num_requests, int32_t total_cand, int32_t total_kv,
+                                 int32_t heads, void* O, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
 /* Varlen plan alone (integer outputs, for callers that want the row map and
  * for tests).  Writes, on the device:
  *   cu_q[r]      = q * cu_cand[r]                (R+1 entries)

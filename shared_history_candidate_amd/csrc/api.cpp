@@ -604,6 +604,129 @@ xattn_status xattn_backward(xattn_ctx* ctx, const void* Z, const void* W_Q, cons
     return XATTN_OK;
 }
 
+namespace {
+
+xattn_status codec_book(const xattn_config& c, const xattn_codebook* cb, int heads,
+                        xattn::CodecBook* out) {
+    if (!cb) return fail(XATTN_EINVAL, "NULL codebook");
+    if (!cb->bits || !cb->center || !cb->half_range || !cb->rotation)
+        return fail(XATTN_EINVAL, "NULL codebook array");
+    const int dh = c.d_model / heads;
+    if (cb->budget_bits <= 0 || cb->budget_bits % 32 != 0 || cb->budget_bits > 8 * dh)
+        return fail(XATTN_EUNSUPPORTED, "budget_bits %d: need a positive multiple of 32 <= %d",
+                    cb->budget_bits, 8 * dh);
+    *out = xattn::CodecBook{cb->budget_bits, cb->bits, cb->center, cb->half_range, cb->rotation};
+    return XATTN_OK;
+}
+
+xattn_status codec_shape(const xattn_ctx* ctx, int heads) {
+    if (!ctx) return fail(XATTN_EINVAL, "ctx is NULL");
+    const xattn_config& c = ctx->cfg;
+    if (heads < 1 || c.d_model % heads != 0)
+        return fail(XATTN_EINVAL, "heads=%d does not divide d_model=%d", heads, c.d_model);
+    if (c.dtype != XATTN_BF16) return fail(XATTN_EUNSUPPORTED, "coded memory needs a bf16 context");
+    if (!bf16_dh_supported(c.d_model / heads))
+        return fail(XATTN_EUNSUPPORTED, "head width %d not built", c.d_model / heads);
+    return XATTN_OK;
+}
+
+}  // namespace
+
+xattn_status xattn_codec_encode(xattn_ctx* ctx, const xattn_codebook* cb, int32_t heads,
+                                const void* X, int32_t n_rows, uint32_t* codes, float* norms,
+                                void* stream) {
+    g_last_error.clear();
+    xattn_status st = codec_shape(ctx, heads);
+    if (st != XATTN_OK) return st;
+    xattn::CodecBook b{};
+    if ((st = codec_book(ctx->cfg, cb, heads, &b)) != XATTN_OK) return st;
+    if (n_rows < 0) return fail(XATTN_EINVAL, "negative n_rows");
+    if (n_rows == 0) return XATTN_OK;
+    if (!X || !codes || !norms) return fail(XATTN_EINVAL, "NULL X, codes or norms");
+    DeviceGuard dg(ctx->cfg.device);
+    if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
+    hipError_t e = xattn::launch_codec_encode(b, X, n_rows, ctx->cfg.d_model, heads, codes, norms,
+                                              static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? XATTN_OK : hip_fail(e, "encode kernel launch");
+}
+
+xattn_status xattn_codec_fold_query_weights(xattn_ctx* ctx, const xattn_codebook* cb_k,
+                                            int32_t heads, const void* W_Q, void* W_Q_rot,
+                                            void* stream) {
+    g_last_error.clear();
+    xattn_status st = codec_shape(ctx, heads);
+    if (st != XATTN_OK) return st;
+    xattn::CodecBook b{};
+    if ((st = codec_book(ctx->cfg, cb_k, heads, &b)) != XATTN_OK) return st;
+    if (!W_Q || !W_Q_rot) return fail(XATTN_EINVAL, "NULL W_Q or W_Q_rot");
+    DeviceGuard dg(ctx->cfg.device);
+    if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
+    hipError_t e = xattn::launch_codec_fold(b, W_Q, ctx->cfg.n_slots, ctx->cfg.d_model, heads,
+                                            W_Q_rot, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? XATTN_OK : hip_fail(e, "fold kernel launch");
+}
+
+xattn_status xattn_forward_codec(xattn_ctx* ctx, const xattn_codebook* cb_k,
+                                 const xattn_codebook* cb_v, const void* Z, const void* W_Q_rot,
+                                 const uint32_t* k_codes, const float* k_norms,
+                                 const uint32_t* v_codes, const float* v_norms,
+                                 const int32_t* cu_kv, const int32_t* cu_cand, int32_t R,
+                                 int32_t total_cand, int32_t total_kv, int32_t heads, void* O,
+                                 void* workspace, size_t workspace_bytes_, void* stream) {
+    g_last_error.clear();
+    xattn_status st = check_shape(ctx, R, total_cand, total_kv, heads);
+    if (st != XATTN_OK) return st;
+    if ((st = codec_shape(ctx, heads)) != XATTN_OK) return st;
+    const xattn_config& c = ctx->cfg;
+    const bool sep = c.kv_mode == XATTN_KV_SEPARATE;
+    xattn::CodecArgs a{};
+    if ((st = codec_book(c, cb_k, heads, &a.kb)) != XATTN_OK) return st;
+    if (sep) {
+        if ((st = codec_book(c, cb_v, heads, &a.vb)) != XATTN_OK) return st;
+        if (a.vb.budget != a.kb.budget)
+            return fail(XATTN_EUNSUPPORTED, "key and value budgets differ (%d, %d)", a.kb.budget,
+                        a.vb.budget);
+        if (total_kv > 0 && (!v_codes || !v_norms))
+            return fail(XATTN_EINVAL, "NULL value codes or norms in XATTN_KV_SEPARATE mode");
+    } else if (cb_v || v_codes || v_norms) {
+        return fail(XATTN_EINVAL, "value codebook given in XATTN_KV_SHARED mode");
+    }
+    if (!cu_kv || !cu_cand) return fail(XATTN_EINVAL, "NULL offset array");
+    if (total_cand > 0 && (!Z || !W_Q_rot || !O)) return fail(XATTN_EINVAL, "NULL Z, W_Q_rot or O");
+    if (total_kv > 0 && (!k_codes || !k_norms)) return fail(XATTN_EINVAL, "NULL key codes or norms");
+    const size_t need = workspace_bytes(c, R, total_cand);
+    if (!workspace || workspace_bytes_ < need)
+        return fail(XATTN_EWORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes_);
+    if (R == 0 && (total_cand != 0 || total_kv != 0))
+        return fail(XATTN_EINVAL, "num_requests=0 with total_cand=%d total_kv=%d", total_cand,
+                    total_kv);
+    if (R == 0 || total_cand == 0) return XATTN_OK;
+    const int64_t max_tiles = max_tiles_for(c, R, total_cand, 64);
+    if (max_tiles * heads > INT32_MAX) return fail(XATTN_EUNSUPPORTED, "grid too large");
+    DeviceGuard dg(c.device);
+    if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* qws = static_cast<char*>(workspace) + q_offset(c, R, total_cand);
+    hipError_t e = xattn::launch_project_plan_bf16(Z, W_Q_rot, total_cand, c.n_slots, c.d_model,
+                                                   qws, cu_kv, cu_cand, R, 64, total_kv, workspace,
+                                                   max_tiles, s);
+    if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
+    a.Qr = qws;
+    a.kcodes = k_codes;
+    a.knorms = k_norms;
+    a.vcodes = sep ? v_codes : nullptr;
+    a.vnorms = sep ? v_norms : nullptr;
+    a.plan = static_cast<const int*>(workspace);
+    a.O = O;
+    a.q = c.n_slots;
+    a.d = c.d_model;
+    a.heads = heads;
+    a.total_kv = total_kv;
+    a.scale_log2 = 1.4426950408889634f / sqrtf((float)(c.d_model / heads));
+    e = xattn::launch_codec_attn(a, sep, max_tiles, s);
+    return e == hipSuccess ? XATTN_OK : hip_fail(e, "codec attention kernel launch");
+}
+
 xattn_status xattn_project(xattn_ctx* ctx, const void* Z, const void* W_Q, int32_t total_cand,
                            void* Q, void* stream) {
     g_last_error.clear();

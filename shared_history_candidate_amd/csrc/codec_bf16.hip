@@ -1,0 +1,388 @@
+// TransX memory codec on gfx950 (TransX technical report, s.3: each key or
+// value vector kept as its length plus a direction rotated into the
+// eigenbasis of the directions' covariance and quantised with bits handed
+// out by energy).  Per (memory row, head):
+//   norm  = |x_h|                                   (fp32)
+//   xr    = E_h^T (x_h / norm)                      (rotated direction)
+//   code_i = clamp(floor((xr_i - m_i + a_i) / (2 a_i) * 2^b_i), 0, 2^b_i - 1)
+// packed least-significant bit first into budget/32 words, coordinate 0 first
+// (b_i = 0: no bits, reconstructed as m_i).  Layout, head-major:
+//   codes [heads][rows][budget/32] uint32, norms [heads][rows] fp32.
+//
+// Attention over a coded memory never leaves the rotated basis: the key
+// rotation is folded into the query weights (codec_fold_kernel: W~_Q[s] rows
+// of head h = E_K,h^T W_Q[s] rows of head h), scores are q~ . k^ with
+// k^ = norm * x^ (x^ the reconstructed rotated direction), the output is
+// accumulated as o~ = sum_j p_j v^_j and rotated back once per query row,
+// o = E_V o~ (one d_h x d_h product on the matrix cores in the epilogue).
+// The reconstruction k^ = norm * (lo_i + code_i * step_i) happens while a
+// memory tile is staged in LDS, so HBM carries only the codes and norms.
+#include "common.h"
+#include "internal.h"
+
+namespace xattn {
+
+namespace {
+
+constexpr int kCBN = 64;     // memory rows per tile
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t crsrc(const void* p, long long bytes) {
+    const uint32_t b = bytes <= 0 ? 0u : (bytes > 0xFFFFFFF0ll ? 0xFFFFFFF0u : (uint32_t)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, b, 0x00020000);
+}
+
+// ---------------------------------------------------------------------------
+// encode: one thread per (row, head)
+// ---------------------------------------------------------------------------
+__global__ void codec_encode_kernel(CodecBook cb, const bf16* __restrict__ X, int n, int d,
+                                    int heads, uint32_t* __restrict__ codes,
+                                    float* __restrict__ norms) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (int64_t)n * heads) return;
+    const int h = (int)(idx / n);
+    const int row = (int)(idx - (int64_t)h * n);
+    const int dh = d / heads, W = cb.budget / 32;
+    const bf16* x = X + (size_t)row * d + h * dh;
+    float n2 = 0.f;
+    for (int e = 0; e < dh; ++e) {
+        const float v = (float)x[e];
+        n2 = fmaf(v, v, n2);
+    }
+    const float nrm = sqrtf(n2);
+    norms[(size_t)h * n + row] = nrm;
+    const float inv = nrm > 0.f ? 1.0f / nrm : 0.f;
+    const float* E = cb.rot + (size_t)h * dh * dh;   // E[o][i]: column i = eigenvector i
+    uint32_t* out = codes + ((size_t)h * n + row) * W;
+    uint32_t word = 0;
+    int wi = 0, off = 0;
+    for (int i = 0; i < dh; ++i) {
+        const int b = min((int)cb.bits[h * dh + i], 8);
+        if (b <= 0) continue;
+        float xr = 0.f;
+        for (int o = 0; o < dh; ++o) xr = fmaf((float)x[o] * inv, E[o * dh + i], xr);
+        const float c = cb.center[h * dh + i], a = cb.half[h * dh + i];
+        const float levels = (float)(1u << b);
+        const float t = floorf((xr - c + a) / (2.0f * a) * levels);
+        const uint32_t code = t <= 0.f ? 0u : (t >= levels - 1.f ? (1u << b) - 1u : (uint32_t)t);
+        word |= code << off;
+        if (off + b >= 32) {
+            if (wi < W) out[wi] = word;
+            ++wi;
+            word = off + b > 32 ? code >> (32 - off) : 0u;
+            off = off + b - 32;
+        } else {
+            off += b;
+        }
+    }
+    for (; wi < W; ++wi) {   // a bit table below the budget leaves zero words
+        out[wi] = word;
+        word = 0;
+    }
+}
+
+// W~[s][h*dh + i][c] = sum_o E_h[o][i] W[s][h*dh + o][c]  (fp32 sums, bf16 out)
+__global__ void codec_fold_kernel(CodecBook cb, const bf16* __restrict__ Wq, int q, int d,
+                                  int heads, bf16* __restrict__ Wr) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (int64_t)q * d * d) return;
+    const int c = (int)(idx % d);
+    const int row = (int)((idx / d) % d);
+    const int s = (int)(idx / ((int64_t)d * d));
+    const int dh = d / heads, h = row / dh, i = row - h * dh;
+    const float* E = cb.rot + (size_t)h * dh * dh;
+    const bf16* w = Wq + ((size_t)s * d + h * dh) * d + c;
+    float acc = 0.f;
+    for (int o = 0; o < dh; ++o) acc = fmaf(E[o * dh + i], (float)w[(size_t)o * d], acc);
+    Wr[idx] = (bf16)acc;
+}
+
+// ---------------------------------------------------------------------------
+// attention over the coded memory
+// ---------------------------------------------------------------------------
+template <int DH, bool SEP>
+struct CaCfg {
+    static constexpr int NT = 128;                  // 2 waves x 32 query rows (tile_m = 64)
+    static constexpr int EB = DH / 32, KST = DH / 16;
+    static constexpr int LDK = DH + 8;              // decoded tile pitch (16-byte rows)
+    static constexpr int PLANES = SEP ? 2 : 1;
+    static constexpr int TILE = kCBN * LDK;          // bf16 elements per decoded plane
+    static constexpr int MAXW = DH / 4;              // words per row at 8 bits per coordinate
+    static constexpr int RAWP = MAXW + 1;            // raw row pitch (words), one pad word
+    static constexpr int RAW_WORDS = kCBN * RAWP;    // per plane
+    static constexpr int RCPT = kCBN * MAXW / NT;    // raw words per thread per plane (at most)
+    // LDS: decoded planes, raw codes + norms per plane, decode tables per
+    // plane ({offset, bits, lo, step} per coordinate), output rotation.
+    static constexpr int DEC_BYTES = PLANES * TILE * 2;
+    static constexpr int RAW_BYTES = PLANES * (RAW_WORDS + kCBN) * 4;
+    static constexpr int TAB_BYTES = PLANES * DH * 16;
+    static constexpr int ROT_BYTES = DH * LDK * 2;
+    static constexpr int SMEM = DEC_BYTES + RAW_BYTES + TAB_BYTES + ROT_BYTES;
+};
+
+template <int DH, bool SEP>
+__global__ __launch_bounds__(128) void codec_attn_kernel(CodecArgs a) {
+    using C = CaCfg<DH, SEP>;
+    __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
+    bf16* dec = reinterpret_cast<bf16*>(smem);
+    uint32_t* raw = reinterpret_cast<uint32_t*>(smem + C::DEC_BYTES);
+    int4* tab = reinterpret_cast<int4*>(smem + C::DEC_BYTES + C::RAW_BYTES);
+    bf16* rot = reinterpret_cast<bf16*>(smem + C::DEC_BYTES + C::RAW_BYTES + C::TAB_BYTES);
+
+    const int q = a.q, d = a.d, heads = a.heads;
+    const int* __restrict__ ws = a.plan;
+    const int tile = blockIdx.x / heads;
+    const int h = blockIdx.x - tile * heads;
+    if (tile >= ws[kPlanNTiles] || ws[kPlanTileM] != 64) return;
+    const int4 item = reinterpret_cast<const int4*>(reinterpret_cast<const char*>(ws) +
+                                                    kPlanHeaderBytes)[tile];
+    const int kv0 = __builtin_amdgcn_readfirstlane(item.x);
+    const int L = __builtin_amdgcn_readfirstlane(item.y);
+    const int c0 = __builtin_amdgcn_readfirstlane(item.z);
+    const int iw = __builtin_amdgcn_readfirstlane(item.w);
+    const int nc = iw & kItemNcMask, s = iw >> 16;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 5, l32 = lane & 31;
+    const int qcol = w * 32 + l32;
+    const bool qvalid = qcol < nc;
+    const size_t row = (size_t)(qvalid ? c0 + qcol : c0 + nc - 1) * q + s;
+
+    // decode tables {bit offset, bits, lo, step} and the output rotation E_V
+#pragma unroll
+    for (int p = 0; p < C::PLANES; ++p) {
+        const uint8_t* bits = p == 0 ? a.kb.bits : a.vb.bits;
+        const float* center = p == 0 ? a.kb.center : a.vb.center;
+        const float* half = p == 0 ? a.kb.half : a.vb.half;
+        for (int i = tid; i < DH; i += C::NT) {
+            int off = 0;
+            for (int j = 0; j < i; ++j) off += min((int)bits[h * DH + j], 8);
+            const int b = min((int)bits[h * DH + i], 8);
+            const float m = center[h * DH + i], hr = half[h * DH + i];
+            const float step = b > 0 ? 2.0f * hr / (float)(1u << b) : 0.f;
+            const float lo = b > 0 ? m - hr + 0.5f * step : m;
+            tab[p * DH + i] = make_int4(off, b, __builtin_bit_cast(int, lo),
+                                        __builtin_bit_cast(int, step));
+        }
+    }
+    {
+        const float* rv = SEP ? a.vb.rot : a.kb.rot;
+        for (int idx = tid; idx < DH * DH; idx += C::NT) {
+            const int e = idx / DH, i = idx - e * DH;
+            rot[e * C::LDK + i] = (bf16)rv[((size_t)h * DH + e) * DH + i];
+        }
+    }
+
+    // this lane's rotated query, scaled into exp2 units
+    bf16x8 qb[C::KST];
+    {
+        const bf16* qr = static_cast<const bf16*>(a.Qr) + row * d + h * DH;
+#pragma unroll
+        for (int k = 0; k < C::KST; ++k) {
+            bf16x8 v = *reinterpret_cast<const bf16x8*>(qr + 16 * k + 8 * g);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = (bf16)((float)v[e] * a.scale_log2);
+            qb[k] = v;
+        }
+    }
+
+    const int W = a.kb.budget / 32;
+    const int nrows = a.total_kv;
+    // raw codes of tile t (head h) into registers; rows past L read as zeros
+    uint32_t rr_[C::PLANES][C::RCPT];
+    float rn_[C::PLANES];
+    auto gload = [&](int t) {
+        const int r0 = kv0 + t * kCBN;
+        const int left = L - t * kCBN;
+        for (int p = 0; p < C::PLANES; ++p) {
+            const uint32_t* cp = (p == 0 ? a.kcodes : a.vcodes) + ((size_t)h * nrows + r0) * W;
+            const float* np_ = (p == 0 ? a.knorms : a.vnorms) + (size_t)h * nrows + r0;
+            const __amdgpu_buffer_rsrc_t rc = crsrc(cp, (long long)left * W * 4);
+            const __amdgpu_buffer_rsrc_t rn = crsrc(np_, (long long)left * 4);
+#pragma unroll
+            for (int u = 0; u < C::RCPT; ++u) {
+                const int idx = tid + u * C::NT;
+                rr_[p][u] = idx < kCBN * W ? __builtin_amdgcn_raw_buffer_load_b32(rc, idx * 4, 0, 0)
+                                           : 0u;
+            }
+            rn_[p] = tid < kCBN ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                                rn, tid * 4, 0, 0))
+                                : 0.f;
+        }
+    };
+    auto rstore = [&]() {
+        for (int p = 0; p < C::PLANES; ++p) {
+            uint32_t* rp = raw + p * (C::RAW_WORDS + kCBN);
+#pragma unroll
+            for (int u = 0; u < C::RCPT; ++u) {
+                const int idx = tid + u * C::NT;
+                if (idx < kCBN * W) {
+                    const int r = idx / W, ww = idx - r * W;
+                    rp[r * C::RAWP + ww] = rr_[p][u];
+                }
+            }
+            if (tid < kCBN) {
+                rp[tid * C::RAWP + W] = 0u;   // pad word read by fields that end the row
+                reinterpret_cast<float*>(rp + C::RAW_WORDS)[tid] = rn_[p];
+            }
+        }
+    };
+    // reconstruct the tile: thread (row tid % 64, half tid / 64) decodes half
+    // of the row's coordinates in every plane
+    auto decode = [&]() {
+        const int r = tid & (kCBN - 1), hf = tid >> 6;
+        for (int p = 0; p < C::PLANES; ++p) {
+            const uint32_t* rp = raw + p * (C::RAW_WORDS + kCBN) + r * C::RAWP;
+            const float nrm = reinterpret_cast<const float*>(raw + p * (C::RAW_WORDS + kCBN) +
+                                                             C::RAW_WORDS)[r];
+            bf16* out = dec + p * C::TILE + r * C::LDK;
+#pragma unroll 4
+            for (int i = hf * (DH / 2); i < (hf + 1) * (DH / 2); ++i) {
+                const int4 tb = tab[p * DH + i];
+                const int off = tb.x, b = tb.y;
+                const uint32_t lo = rp[off >> 5], hi = rp[(off >> 5) + 1];
+                const uint32_t v = __builtin_amdgcn_alignbit(hi, lo, off & 31) & ((1u << b) - 1u);
+                out[i] = (bf16)(nrm * fmaf((float)v, __builtin_bit_cast(float, tb.w),
+                                           __builtin_bit_cast(float, tb.z)));
+            }
+        }
+    };
+
+    const int ntiles = (L + kCBN - 1) / kCBN;
+    f32x16 oacc[C::EB];
+#pragma unroll
+    for (int eb = 0; eb < C::EB; ++eb) oacc[eb] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;
+    const int G = lane >> 4, k16 = lane & 15;
+    const int tr_row = 4 * (G >> 1) + (k16 >> 2);
+    const int tr_col = 16 * (G & 1) + 4 * (k16 & 3);
+
+    gload(0);
+    for (int t = 0; t < ntiles; ++t) {
+        rstore();
+        __syncthreads();   // raw tile and (first pass) tables visible
+        gload(t + 1);
+        decode();
+        __syncthreads();   // decoded tile visible
+        const bf16* kb = dec;
+        const bf16* vb = dec + (C::PLANES - 1) * C::TILE;
+        f32x16 sacc[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) sacc[hh] = f32x16{};
+#pragma unroll
+        for (int k = 0; k < C::KST; ++k)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                sacc[hh] = mfma32(*reinterpret_cast<const bf16x8*>(
+                                      kb + (hh * 32 + l32) * C::LDK + 16 * k + 8 * g),
+                                  qb[k], sacc[hh]);
+        const int jleft = L - t * kCBN;
+        float mt = -INFINITY;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int j = hh * 32 + (r >> 2) * 8 + 4 * g + (r & 3);
+                if (j >= jleft) sacc[hh][r] = -INFINITY;
+                mt = fmaxf(mt, sacc[hh][r]);
+            }
+        const float m_new = fmaxf(m_run, fmaxf(mt, xor32(mt)));
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int eb = 0; eb < C::EB; ++eb) oacc[eb] *= alpha;
+        bf16x8 pb[4];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const bf16 p = (bf16)__builtin_amdgcn_exp2f(sacc[hh][r] - m_new);
+                l_run += (float)p;
+                pb[hh * 2 + (r >> 3)][r & 7] = p;
+            }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int eb = 0; eb < C::EB; ++eb) {
+                const bf16* base = vb + (16 * u + tr_row) * C::LDK + eb * 32 + tr_col;
+                oacc[eb] = mfma32(cat(lds_read_tr16(base), lds_read_tr16(base + 8 * C::LDK)),
+                                  pb[u], oacc[eb]);
+            }
+        __syncthreads();   // tile consumed before the next one is written
+    }
+    if (ntiles == 0) __syncthreads();   // the tables and the rotation are staged
+
+    // o = E_V o~ / l, rotated back on the matrix cores
+    l_run += xor32(l_run);
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    bf16x8 ob[C::KST];
+#pragma unroll
+    for (int k = 0; k < C::KST; ++k)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) ob[k][t] = (bf16)(oacc[k >> 1][8 * (k & 1) + t] * inv);
+    bf16* orow = static_cast<bf16*>(a.O) + row * d + h * DH;
+#pragma unroll
+    for (int eo = 0; eo < C::EB; ++eo) {
+        // every lane takes part in the products; only valid rows are stored
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int k = 0; k < C::KST; ++k) {
+            // slot t of slice k is rotated feature 16k + 8(t/4) + 4g + t%4
+            const bf16* rp = rot + (eo * 32 + l32) * C::LDK + 16 * k + 4 * g;
+            acc = mfma32(cat(*reinterpret_cast<const bf16x4*>(rp),
+                             *reinterpret_cast<const bf16x4*>(rp + 8)),
+                         ob[k], acc);
+        }
+        if (qvalid) {
+#pragma unroll
+            for (int b4 = 0; b4 < 4; ++b4) {
+                bf16x4 v;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) v[t] = (bf16)acc[4 * b4 + t];
+                *reinterpret_cast<bf16x4*>(orow + eo * 32 + b4 * 8 + 4 * g) = v;
+            }
+        }
+    }
+}
+
+template <int DH>
+hipError_t launch_codec_dh(const CodecArgs& a, bool sep, int64_t items, hipStream_t stream) {
+    if (items <= 0) return hipSuccess;
+    const dim3 grid((unsigned)(items * a.heads));
+    if (sep)
+        hipLaunchKernelGGL((codec_attn_kernel<DH, true>), grid, dim3(128), 0, stream, a);
+    else
+        hipLaunchKernelGGL((codec_attn_kernel<DH, false>), grid, dim3(128), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_codec_encode(const CodecBook& cb, const void* X, int n, int d, int heads,
+                               uint32_t* codes, float* norms, hipStream_t stream) {
+    const int64_t m = (int64_t)n * heads;
+    if (m <= 0) return hipSuccess;
+    hipLaunchKernelGGL(codec_encode_kernel, dim3((unsigned)((m + 127) / 128)), dim3(128), 0,
+                       stream, cb, static_cast<const bf16*>(X), n, d, heads, codes, norms);
+    return hipGetLastError();
+}
+
+hipError_t launch_codec_fold(const CodecBook& cb, const void* Wq, int q, int d, int heads,
+                             void* Wr, hipStream_t stream) {
+    const int64_t m = (int64_t)q * d * d;
+    if (m <= 0) return hipSuccess;
+    hipLaunchKernelGGL(codec_fold_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, stream,
+                       cb, static_cast<const bf16*>(Wq), q, d, heads, static_cast<bf16*>(Wr));
+    return hipGetLastError();
+}
+
+hipError_t launch_codec_attn(const CodecArgs& a, bool sep, int64_t items, hipStream_t stream) {
+    switch (a.d / a.heads) {
+        case 32: return launch_codec_dh<32>(a, sep, items, stream);
+        case 64: return launch_codec_dh<64>(a, sep, items, stream);
+        case 128: return launch_codec_dh<128>(a, sep, items, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace xattn

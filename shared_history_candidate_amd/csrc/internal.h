@@ -107,6 +107,35 @@ hipError_t launch_attn_f32_stats(const float* Qp, const float* K, const float* V
                                  const int* cand_len, int64_t max_tiles, int q, int d, int heads,
                                  const float* dO, float* lse, float* Dsum, hipStream_t stream);
 
+// Memory codec (codec_bf16.hip).  A codebook per memory role: budget bits
+// per (row, head) vector (a multiple of 32, at most 8 per coordinate), bits
+// [heads][d_h] (0..8), center/half [heads][d_h] of the rotated coordinates'
+// quantiser, rot [heads][d_h][d_h] (rot[h][o][i]: column i = eigenvector i).
+struct CodecBook {
+    int budget;
+    const uint8_t* bits;
+    const float* center;
+    const float* half;
+    const float* rot;
+};
+struct CodecArgs {
+    const void* Qr;              // rotated projected queries [rows][d] (bf16)
+    CodecBook kb, vb;            // vb unused when the memory is both K and V
+    const uint32_t* kcodes;      // [heads][total_kv][budget/32]
+    const float* knorms;         // [heads][total_kv]
+    const uint32_t* vcodes;
+    const float* vnorms;
+    const int* plan;             // query-tile plan, tile_m = 64
+    void* O;
+    int q, d, heads, total_kv;
+    float scale_log2;
+};
+hipError_t launch_codec_encode(const CodecBook& cb, const void* X, int n, int d, int heads,
+                               uint32_t* codes, float* norms, hipStream_t stream);
+hipError_t launch_codec_fold(const CodecBook& cb, const void* Wq, int q, int d, int heads,
+                             void* Wr, hipStream_t stream);
+hipError_t launch_codec_attn(const CodecArgs& a, bool sep, int64_t items, hipStream_t stream);
+
 // fp32 path (tile_m = 64): attention over projected queries (cand_len: the
 // per-candidate prefix cutoff, or NULL), projection.
 hipError_t launch_attn_f32(const float* Qp, const float* K, const float* V, const void* ws,

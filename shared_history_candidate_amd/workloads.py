@@ -33,7 +33,7 @@ from typing import Optional, Sequence
 import numpy as np
 
 __all__ = ["Workload", "CONFIGS", "make", "custom", "round_bf16", "output_weights",
-           "attention_like", "prefix_lengths", "output_grad"]
+           "attention_like", "prefix_lengths", "output_grad", "anisotropic_memory"]
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
@@ -275,6 +275,33 @@ def attention_like(wl: Workload, seed: int = 0, std: float = 0.5) -> np.ndarray:
     rng = np.random.default_rng(seed)
     O = _normal(rng, (wl.total_cand, wl.q, wl.d), std=std)
     return round_bf16(O) if wl.dtype == "bf16" else O
+
+
+def anisotropic_memory(wl: Workload, seed: int = 0, decay: float = 0.85, shift: float = 0.3):
+    """Memory rows whose per-head directions have a decaying spectrum (most
+    energy in a few directions, as the TransX report s.3 observes for its
+    memory), for the coded-memory tests: per head h a random orthogonal basis
+    B_h (QR of a Gaussian matrix), rows (g * decay^i + shift) B_h^T with g
+    N(0, 1), times a norm from U[0.5, 2].  Returns (K, V) [total_kv, d]
+    (V is None in projection-free mode), bf16-rounded in bf16 mode; draws
+    from default_rng(seed): bases, then K, then V."""
+    rng = np.random.default_rng(seed)
+    dh = wl.d // wl.heads
+    bases = [np.linalg.qr(rng.normal(size=(dh, dh)))[0] for _ in range(wl.heads)]
+    scales = decay ** np.arange(dh)
+
+    def draw():
+        X = np.zeros((wl.total_kv, wl.d))
+        for h in range(wl.heads):
+            g = rng.normal(size=(wl.total_kv, dh))
+            X[:, h * dh:(h + 1) * dh] = (g * scales + shift) @ bases[h].T
+        X *= rng.uniform(0.5, 2.0, size=(wl.total_kv, 1))
+        X = X.astype(np.float32)
+        return round_bf16(X) if wl.dtype == "bf16" else X
+
+    K = draw()
+    V = draw() if wl.kv_mode == "separate" else None
+    return K, V
 
 
 def output_grad(wl: Workload, seed: int = 0) -> np.ndarray:

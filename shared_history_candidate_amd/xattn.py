@@ -26,7 +26,37 @@ EXPORTED = ("xattn_create", "xattn_destroy", "xattn_workspace_size", "xattn_forw
             "xattn_attend", "xattn_attend_q", "xattn_plan", "xattn_max_tiles",
             "xattn_forward_launches", "xattn_project", "xattn_output", "xattn_device_error",
             "xattn_last_error", "xattn_forward_prefix", "xattn_attend_q_prefix",
-            "xattn_backward_workspace_size", "xattn_backward")
+            "xattn_backward_workspace_size", "xattn_backward", "xattn_codec_encode",
+            "xattn_codec_fold_query_weights", "xattn_forward_codec")
+
+
+class CodebookStruct(ctypes.Structure):
+    _fields_ = [("budget_bits", ctypes.c_int32), ("bits", ctypes.c_void_p),
+                ("center", ctypes.c_void_p), ("half_range", ctypes.c_void_p),
+                ("rotation", ctypes.c_void_p)]
+
+
+class Codebook:
+    """Device-resident codebook of a coded memory (see include/xattn.h):
+    bits uint8 [heads, d_h], center/half_range/rotation fp32.  The tensors are
+    kept alive by this object."""
+
+    def __init__(self, bits, center, half_range, rotation, budget_bits: int, device="cuda"):
+        t = lambda a, dt: torch.as_tensor(a).to(device=device, dtype=dt).contiguous()
+        self.bits = t(bits, torch.uint8)
+        self.center = t(center, torch.float32)
+        self.half_range = t(half_range, torch.float32)
+        self.rotation = t(rotation, torch.float32)
+        self.budget_bits = int(budget_bits)
+        self.heads, self.d_h = self.bits.shape
+
+    @property
+    def words(self) -> int:
+        return self.budget_bits // 32
+
+    def struct(self) -> CodebookStruct:
+        return CodebookStruct(self.budget_bits, self.bits.data_ptr(), self.center.data_ptr(),
+                              self.half_range.data_ptr(), self.rotation.data_ptr())
 
 
 class Config(ctypes.Structure):
@@ -79,6 +109,14 @@ def lib():
         L.xattn_backward.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, P, P, P, P,
                                      P, SZ, P]
         L.xattn_backward.restype = ctypes.c_int
+        CB = ctypes.POINTER(CodebookStruct)
+        L.xattn_codec_encode.argtypes = [P, CB, I32, P, I32, P, P, P]
+        L.xattn_codec_encode.restype = ctypes.c_int
+        L.xattn_codec_fold_query_weights.argtypes = [P, CB, I32, P, P, P]
+        L.xattn_codec_fold_query_weights.restype = ctypes.c_int
+        L.xattn_forward_codec.argtypes = [P, CB, CB, P, P, P, P, P, P, P, P, I32, I32, I32, I32, P,
+                                          P, SZ, P]
+        L.xattn_forward_codec.restype = ctypes.c_int
         L.xattn_plan.argtypes = [P, P, P, I32, I32, I32, I32, P, P, P, P,
                                  ctypes.POINTER(I32), P, SZ, P]
         L.xattn_plan.restype = ctypes.c_int
@@ -294,6 +332,53 @@ class XAttn:
                                     _ptr(out["dV"]), _ptr(workspace), workspace.numel(),
                                     _stream(dev, stream)))
         return out
+
+    # -- coded memory ----------------------------------------------------------
+    def codec_encode(self, cb: "Codebook", X, stream=None):
+        """Codes [heads, n, words] uint32 and norms [heads, n] fp32 of rows X [n, d]."""
+        n = X.shape[0]
+        self._check_tensor("X", X, self.torch_dtype, (n, self.d_model))
+        codes = torch.empty((cb.heads, n, cb.words), dtype=torch.int32, device=X.device)
+        norms = torch.empty((cb.heads, n), dtype=torch.float32, device=X.device)
+        s = cb.struct()
+        _check(lib().xattn_codec_encode(self._h, ctypes.byref(s), cb.heads, _ptr(X), n,
+                                        _ptr(codes), _ptr(norms), _stream(X.device, stream)))
+        return codes, norms
+
+    def codec_fold(self, cb_k: "Codebook", W_Q, stream=None):
+        """Query weights in the keys' rotated basis (xattn_codec_fold_query_weights)."""
+        self._check_tensor("W_Q", W_Q, self.torch_dtype, (self.q, self.d_model, self.d_model))
+        out = torch.empty_like(W_Q)
+        s = cb_k.struct()
+        _check(lib().xattn_codec_fold_query_weights(self._h, ctypes.byref(s), cb_k.heads,
+                                                    _ptr(W_Q), _ptr(out),
+                                                    _stream(W_Q.device, stream)))
+        return out
+
+    def forward_codec(self, cb_k: "Codebook", cb_v, Z, W_Q_rot, k_codes, k_norms, v_codes,
+                      v_norms, cu_seqlens_kv, cu_cand, heads: int, O=None, workspace=None,
+                      stream=None) -> torch.Tensor:
+        """Cross-attention over a coded memory (xattn_forward_codec)."""
+        d, q, dt = self.d_model, self.q, self.torch_dtype
+        total_cand = Z.shape[0]
+        total_kv = k_norms.shape[1]
+        R = cu_seqlens_kv.numel() - 1
+        self._check_tensor("Z", Z, dt, (total_cand, q, d))
+        self._check_tensor("W_Q_rot", W_Q_rot, dt, (q, d, d))
+        self._check_tensor("k_codes", k_codes, torch.int32, (cb_k.heads, total_kv, cb_k.words))
+        self._check_tensor("k_norms", k_norms, torch.float32, (cb_k.heads, total_kv))
+        if O is None:
+            O = torch.empty((total_cand, q, d), dtype=dt, device=Z.device)
+        if workspace is None:
+            workspace = self.alloc_workspace(R, total_cand, heads)
+        sk = cb_k.struct()
+        sv = cb_v.struct() if cb_v is not None else None
+        _check(lib().xattn_forward_codec(
+            self._h, ctypes.byref(sk), ctypes.byref(sv) if sv is not None else None, _ptr(Z),
+            _ptr(W_Q_rot), _ptr(k_codes), _ptr(k_norms), _ptr(v_codes), _ptr(v_norms),
+            _ptr(cu_seqlens_kv), _ptr(cu_cand), R, total_cand, total_kv, heads, _ptr(O),
+            _ptr(workspace), workspace.numel(), _stream(Z.device, stream)))
+        return O
 
     def plan(self, cu_seqlens_kv, cu_cand, heads: int, total_cand: int, total_kv: int,
              with_row_req: bool = True, workspace=None, stream=None):

@@ -264,3 +264,33 @@ def test_backward_host_validation(L):
     assert L.xattn_backward(h, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 2, 10, 20, 4, FAKE,
                             FAKE, FAKE, None, FAKE, need, None) == X.XATTN_EINVAL
     L.xattn_destroy(h)
+
+
+def test_codec_host_validation(L):
+    CB = X.CodebookStruct
+    st, h = _create(L, 256, 3, X.XATTN_BF16, X.XATTN_KV_SHARED)
+    assert st == 0
+    good = CB(256, FAKE, FAKE, FAKE, FAKE)
+    enc = lambda cb, heads=4, n=10, Xp=FAKE: L.xattn_codec_encode(
+        h, ctypes.byref(cb) if cb is not None else None, heads, Xp, n, FAKE, FAKE, None)
+    assert enc(None) == X.XATTN_EINVAL
+    assert enc(CB(256, None, FAKE, FAKE, FAKE)) == X.XATTN_EINVAL
+    assert enc(CB(250, FAKE, FAKE, FAKE, FAKE)) == X.XATTN_EUNSUPPORTED   # not a multiple of 32
+    assert enc(CB(8 * 64 + 32, FAKE, FAKE, FAKE, FAKE)) == X.XATTN_EUNSUPPORTED   # > 8 bits/coord
+    assert enc(good, heads=3) == X.XATTN_EINVAL
+    assert enc(good, heads=16) == X.XATTN_EUNSUPPORTED
+    assert enc(good, n=-1) == X.XATTN_EINVAL
+    assert enc(good, n=0) == X.XATTN_OK
+    assert enc(good, Xp=None) == X.XATTN_EINVAL
+    ws = L.xattn_workspace_size(h, 2, 10, 4)
+    fwd = lambda cbv=None, vc=None, kc=FAKE: L.xattn_forward_codec(
+        h, ctypes.byref(good), cbv, FAKE, FAKE, kc, FAKE, vc, None, FAKE, FAKE, 2, 10, 20, 4,
+        FAKE, FAKE, ws, None)
+    assert fwd(cbv=ctypes.byref(good)) == X.XATTN_EINVAL    # shared mode takes no value book
+    assert fwd(vc=FAKE) == X.XATTN_EINVAL
+    assert fwd(kc=None) == X.XATTN_EINVAL
+    L.xattn_destroy(h)
+    st, h = _create(L, 256, 3, X.XATTN_FP32, X.XATTN_KV_SHARED)
+    assert L.xattn_codec_encode(h, ctypes.byref(good), 4, FAKE, 10, FAKE, FAKE,
+                                None) == X.XATTN_EUNSUPPORTED
+    L.xattn_destroy(h)
