@@ -52,12 +52,17 @@ def parse():
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--stage", default="attention",
-                   choices=("attention", "output", "prefix", "backward", "backward_prefix"),
+                   choices=("attention", "output", "prefix", "backward", "backward_prefix",
+                            "codec"),
                    help="attention: the hot path (xattn_forward, the default); output: the "
                         "gate and output projection of Eq. (7) alone (xattn_output); prefix: "
                         "the forward with per-candidate prefix lengths (xattn_forward_prefix); "
                         "backward: the gradients of the attention (xattn_backward); "
-                        "backward_prefix: the same with per-candidate prefix lengths")
+                        "backward_prefix: the same with per-candidate prefix lengths; codec: "
+                        "the forward over a coded memory at --codec-bits bits per coordinate "
+                        "(xattn_forward_codec)")
+    p.add_argument("--codec-bits", type=float, default=4.5,
+                   help="average bits per coordinate of the coded memory (stage codec)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="run only a plain device copy of this many MiB (counter calibration)")
     p.add_argument("--ingest-counters", metavar="DIR",
@@ -353,6 +358,20 @@ def main():
         def step():
             ctx.backward(t["Z"], t["W_Q"], t["K"], t["V"], dO_d, t["cu_kv"], t["cu_cand"],
                          wl.heads, workspace=bws, out=grads, stream=stream, cand_kv_len=cl)
+    elif args.stage == "codec":
+        # memory published as codes + norms (encoded once, outside the step)
+        budget = int(round(args.codec_bits * wl.d_h / 32.0)) * 32
+        books = [W.timing_codebook(wl.heads, wl.d_h, budget, args.seed + 5 + i) for i in range(2)]
+        cbs = [X.Codebook(b["bits"], b["center"], b["half"], b["rot"], b["budget"]) for b in books]
+        kc, kn = ctx.codec_encode(cbs[0], t["K"])
+        vc, vn = ctx.codec_encode(cbs[1], t["V"]) if t["V"] is not None else (None, None)
+        cbv = cbs[1] if t["V"] is not None else None
+        Wr = ctx.codec_fold(cbs[0], t["W_Q"])
+        codec_bytes = (kc.numel() + kn.numel()) * 4 * (2 if cbv is not None else 1)
+
+        def step():
+            ctx.forward_codec(cbs[0], cbv, t["Z"], Wr, kc, kn, vc, vn, t["cu_kv"], t["cu_cand"],
+                              wl.heads, O=O, workspace=ws, stream=stream)
     elif args.stage == "prefix":
         # per-candidate prefix lengths: sorted draws from U{0..L_r} per request
         kv_len = W.prefix_lengths(wl, args.seed + 3, out_of_range=False)
@@ -413,6 +432,17 @@ def main():
         print("bench: backward %.4f ms" % bwd_ms, file=sys.stderr, flush=True)
         roof = entry("backward", wl.flops_backward(kv_len), wl.bytes_backward(), bwd_ms)
         roof["other_kernel"] = None
+    elif args.stage == "codec":
+        # projection GEMM over the folded weights, then the codec attention
+        # kernel, timed as one unit; bytes count codes + norms for the memory
+        codec_ms = per_launch_ms(step)
+        print("bench: codec forward %.4f ms (memory %.2f MB coded vs %.2f MB bf16)" %
+              (codec_ms, codec_bytes / 1e6,
+               wl.total_kv * wl.d * 2 * (2 if wl.kv_mode == "separate" else 1) / 1e6),
+              file=sys.stderr, flush=True)
+        b = 2.0 * (2 * wl.rows * wl.d + wl.q * wl.d * wl.d) + codec_bytes
+        roof = entry("codec", wl.flops(), b, codec_ms)
+        roof["other_kernel"] = None
     elif args.stage == "output":
         # gate GEMM (sigmoid and product with O in its epilogue) + W_o GEMM
         out_ms = per_launch_ms(step)
@@ -467,7 +497,9 @@ def main():
                              "backward": "backward pass (gradients of Z, W_Q, K/V for a "
                                          "N(0,1) dO)",
                              "backward_prefix": "backward pass with per-candidate prefix "
-                                                "lengths (sorted U{0..L_r} per request)"}[args.stage]},
+                                                "lengths (sorted U{0..L_r} per request)",
+                             "codec": "forward over a coded memory, %.1f bits per coordinate"
+                                      % args.codec_bits}[args.stage]},
         "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

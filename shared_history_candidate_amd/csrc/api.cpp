@@ -701,15 +701,29 @@ xattn_status xattn_forward_codec(xattn_ctx* ctx, const xattn_codebook* cb_k,
         return fail(XATTN_EINVAL, "num_requests=0 with total_cand=%d total_kv=%d", total_cand,
                     total_kv);
     if (R == 0 || total_cand == 0) return XATTN_OK;
-    const int64_t max_tiles = max_tiles_for(c, R, total_cand, 64);
+    // Query waves sharing each reconstructed memory tile (the reconstruction
+    // is paid once per tile and work-group): as many as the requests' query
+    // rows fill, up to 8 x 32 rows, except that grids of more than 4096
+    // eight-wave work-groups run faster with four (measured: 4 waves on a
+    // batch of 256 requests x 1024 candidates, 8 on 4-8 requests of
+    // 768-1536 rows, 2 on 1..64 candidates per user).  XATTN_CODEC_QW
+    // overrides.
+    const double rows_per_req = (double)total_cand * c.n_slots / R;
+    int qw = rows_per_req >= 512 ? 8 : (rows_per_req >= 128 ? 4 : 2);
+    if (qw == 8 && max_tiles_for(c, R, total_cand, 256) * heads > 4096) qw = 4;
+    if (const char* env = getenv("XATTN_CODEC_QW")) {
+        const int v = atoi(env);
+        if (v == 2 || v == 4 || v == 8) qw = v;
+    }
+    const int64_t max_tiles = max_tiles_for(c, R, total_cand, 32 * qw);
     if (max_tiles * heads > INT32_MAX) return fail(XATTN_EUNSUPPORTED, "grid too large");
     DeviceGuard dg(c.device);
     if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
     hipStream_t s = static_cast<hipStream_t>(stream);
     void* qws = static_cast<char*>(workspace) + q_offset(c, R, total_cand);
     hipError_t e = xattn::launch_project_plan_bf16(Z, W_Q_rot, total_cand, c.n_slots, c.d_model,
-                                                   qws, cu_kv, cu_cand, R, 64, total_kv, workspace,
-                                                   max_tiles, s);
+                                                   qws, cu_kv, cu_cand, R, 32 * qw, total_kv,
+                                                   workspace, max_tiles, s);
     if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
     a.Qr = qws;
     a.kcodes = k_codes;
@@ -723,7 +737,7 @@ xattn_status xattn_forward_codec(xattn_ctx* ctx, const xattn_codebook* cb_k,
     a.heads = heads;
     a.total_kv = total_kv;
     a.scale_log2 = 1.4426950408889634f / sqrtf((float)(c.d_model / heads));
-    e = xattn::launch_codec_attn(a, sep, max_tiles, s);
+    e = xattn::launch_codec_attn(a, sep, qw, max_tiles, s);
     return e == hipSuccess ? XATTN_OK : hip_fail(e, "codec attention kernel launch");
 }
 

@@ -99,9 +99,9 @@ __global__ void codec_fold_kernel(CodecBook cb, const bf16* __restrict__ Wq, int
 // ---------------------------------------------------------------------------
 // attention over the coded memory
 // ---------------------------------------------------------------------------
-template <int DH, bool SEP>
+template <int DH, bool SEP, int QW>
 struct CaCfg {
-    static constexpr int NT = 128;                  // 2 waves x 32 query rows (tile_m = 64)
+    static constexpr int NT = 64 * QW;              // QW waves x 32 query rows (tile_m = 32 QW)
     static constexpr int EB = DH / 32, KST = DH / 16;
     static constexpr int LDK = DH + 8;              // decoded tile pitch (16-byte rows)
     static constexpr int PLANES = SEP ? 2 : 1;
@@ -119,9 +119,9 @@ struct CaCfg {
     static constexpr int SMEM = DEC_BYTES + RAW_BYTES + TAB_BYTES + ROT_BYTES;
 };
 
-template <int DH, bool SEP>
-__global__ __launch_bounds__(128) void codec_attn_kernel(CodecArgs a) {
-    using C = CaCfg<DH, SEP>;
+template <int DH, bool SEP, int QW>
+__global__ __launch_bounds__(64 * QW) void codec_attn_kernel(CodecArgs a) {
+    using C = CaCfg<DH, SEP, QW>;
     __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
     bf16* dec = reinterpret_cast<bf16*>(smem);
     uint32_t* raw = reinterpret_cast<uint32_t*>(smem + C::DEC_BYTES);
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(128) void codec_attn_kernel(CodecArgs a) {
     const int* __restrict__ ws = a.plan;
     const int tile = blockIdx.x / heads;
     const int h = blockIdx.x - tile * heads;
-    if (tile >= ws[kPlanNTiles] || ws[kPlanTileM] != 64) return;
+    if (tile >= ws[kPlanNTiles] || ws[kPlanTileM] != 32 * QW) return;
     const int4 item = reinterpret_cast<const int4*>(reinterpret_cast<const char*>(ws) +
                                                     kPlanHeaderBytes)[tile];
     const int kv0 = __builtin_amdgcn_readfirstlane(item.x);
@@ -226,8 +226,9 @@ __global__ __launch_bounds__(128) void codec_attn_kernel(CodecArgs a) {
             }
         }
     };
-    // reconstruct the tile: thread (row tid % 64, half tid / 64) decodes half
-    // of the row's coordinates in every plane
+    // reconstruct the tile: thread (row tid % 64, part tid / 64) decodes
+    // 1/QW of the row's coordinates in every plane; all QW query waves then
+    // share the reconstructed tile
     auto decode = [&]() {
         const int r = tid & (kCBN - 1), hf = tid >> 6;
         for (int p = 0; p < C::PLANES; ++p) {
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(128) void codec_attn_kernel(CodecArgs a) {
                                                              C::RAW_WORDS)[r];
             bf16* out = dec + p * C::TILE + r * C::LDK;
 #pragma unroll 4
-            for (int i = hf * (DH / 2); i < (hf + 1) * (DH / 2); ++i) {
+            for (int i = hf * (DH / QW); i < (hf + 1) * (DH / QW); ++i) {
                 const int4 tb = tab[p * DH + i];
                 const int off = tb.x, b = tb.y;
                 const uint32_t lo = rp[off >> 5], hi = rp[(off >> 5) + 1];
@@ -345,15 +346,26 @@ __global__ __launch_bounds__(128) void codec_attn_kernel(CodecArgs a) {
     }
 }
 
-template <int DH>
-hipError_t launch_codec_dh(const CodecArgs& a, bool sep, int64_t items, hipStream_t stream) {
-    if (items <= 0) return hipSuccess;
+template <int DH, int QW>
+hipError_t launch_codec_qw(const CodecArgs& a, bool sep, int64_t items, hipStream_t stream) {
     const dim3 grid((unsigned)(items * a.heads));
     if (sep)
-        hipLaunchKernelGGL((codec_attn_kernel<DH, true>), grid, dim3(128), 0, stream, a);
+        hipLaunchKernelGGL((codec_attn_kernel<DH, true, QW>), grid, dim3(64 * QW), 0, stream, a);
     else
-        hipLaunchKernelGGL((codec_attn_kernel<DH, false>), grid, dim3(128), 0, stream, a);
+        hipLaunchKernelGGL((codec_attn_kernel<DH, false, QW>), grid, dim3(64 * QW), 0, stream, a);
     return hipGetLastError();
+}
+
+template <int DH>
+hipError_t launch_codec_dh(const CodecArgs& a, bool sep, int qw, int64_t items,
+                           hipStream_t stream) {
+    if (items <= 0) return hipSuccess;
+    switch (qw) {
+        case 2: return launch_codec_qw<DH, 2>(a, sep, items, stream);
+        case 4: return launch_codec_qw<DH, 4>(a, sep, items, stream);
+        case 8: return launch_codec_qw<DH, 8>(a, sep, items, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -376,11 +388,12 @@ hipError_t launch_codec_fold(const CodecBook& cb, const void* Wq, int q, int d, 
     return hipGetLastError();
 }
 
-hipError_t launch_codec_attn(const CodecArgs& a, bool sep, int64_t items, hipStream_t stream) {
+hipError_t launch_codec_attn(const CodecArgs& a, bool sep, int qw, int64_t items,
+                             hipStream_t stream) {
     switch (a.d / a.heads) {
-        case 32: return launch_codec_dh<32>(a, sep, items, stream);
-        case 64: return launch_codec_dh<64>(a, sep, items, stream);
-        case 128: return launch_codec_dh<128>(a, sep, items, stream);
+        case 32: return launch_codec_dh<32>(a, sep, qw, items, stream);
+        case 64: return launch_codec_dh<64>(a, sep, qw, items, stream);
+        case 128: return launch_codec_dh<128>(a, sep, qw, items, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -134,7 +134,9 @@ hipError_t launch_codec_encode(const CodecBook& cb, const void* X, int n, int d,
                                uint32_t* codes, float* norms, hipStream_t stream);
 hipError_t launch_codec_fold(const CodecBook& cb, const void* Wq, int q, int d, int heads,
                              void* Wr, hipStream_t stream);
-hipError_t launch_codec_attn(const CodecArgs& a, bool sep, int64_t items, hipStream_t stream);
+// qw query waves (2, 4 or 8) share each reconstructed tile: tile_m = 32 qw.
+hipError_t launch_codec_attn(const CodecArgs& a, bool sep, int qw, int64_t items,
+                             hipStream_t stream);
 
 // fp32 path (tile_m = 64): attention over projected queries (cand_len: the
 // per-candidate prefix cutoff, or NULL), projection.

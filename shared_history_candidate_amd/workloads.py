@@ -33,7 +33,8 @@ from typing import Optional, Sequence
 import numpy as np
 
 __all__ = ["Workload", "CONFIGS", "make", "custom", "round_bf16", "output_weights",
-           "attention_like", "prefix_lengths", "output_grad", "anisotropic_memory"]
+           "attention_like", "prefix_lengths", "output_grad", "anisotropic_memory",
+           "timing_codebook"]
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
@@ -302,6 +303,34 @@ def anisotropic_memory(wl: Workload, seed: int = 0, decay: float = 0.85, shift: 
     K = draw()
     V = draw() if wl.kv_mode == "separate" else None
     return K, V
+
+
+def timing_codebook(heads: int, dh: int, budget: int, seed: int = 0) -> dict:
+    """A codebook for timing the coded-memory path (values are irrelevant to
+    its speed): per head a random orthogonal rotation (QR of a Gaussian
+    matrix), centres 0, half-ranges 3 * 0.85^i, and a fixed bit pattern - 8
+    bits for the first quarter of the coordinates, then 4, 2 and whatever
+    is left of the budget spread over the last quarter (at most 8 each) -
+    summing to `budget` (a multiple of 32, at most 8 * dh).  Not a fitted
+    codebook: fitting is offline calibration."""
+    rng = np.random.default_rng(seed)
+    q4 = dh // 4
+    bits = np.zeros(dh, dtype=np.int64)
+    left = budget
+    for k, b in enumerate((8, 4, 2)):
+        take = min(b, left // q4) if q4 else 0
+        bits[k * q4:(k + 1) * q4] = take
+        left -= take * q4
+    for i in range(3 * q4, dh):
+        if left <= 0:
+            break
+        take = min(8, left)
+        bits[i] = take
+        left -= take
+    assert int(bits.sum()) == budget, "budget does not fit the pattern"
+    rot = np.stack([np.linalg.qr(rng.normal(size=(dh, dh)))[0] for _ in range(heads)])
+    return {"rot": rot, "bits": np.tile(bits, (heads, 1)), "center": np.zeros((heads, dh)),
+            "half": np.tile(3.0 * 0.85 ** np.arange(dh), (heads, 1)), "budget": int(budget)}
 
 
 def output_grad(wl: Workload, seed: int = 0) -> np.ndarray:

@@ -159,3 +159,29 @@ def test_codec_attention_transx_slice():
     got = O.float().cpu().numpy().astype(np.float64).reshape(-1, wl.d)
     err, rel = assert_close(got, ref, "bf16", "codec transx")
     print("codec transx: max-abs %.3e normwise %.3e" % (err, rel))
+
+
+@pytest.mark.parametrize("qw", ["2", "4", "8"])
+@pytest.mark.parametrize("dh,heads,mode", [(32, 4, "separate"), (64, 2, "shared"),
+                                           (128, 2, "separate")])
+def test_codec_every_query_wave_count(monkeypatch, qw, dh, heads, mode):
+    """Work-groups of 2, 4 and 8 query waves sharing each reconstructed tile
+    (forced through XATTN_CODEC_QW) give the oracle's result."""
+    require_gpu()
+    monkeypatch.setenv("XATTN_CODEC_QW", qw)
+    wl, K, V, cbk, cbv = _setup([700, 65, 1, 300], [90, 300, 2, 11], dh, heads, mode, 4, seed=3)
+    ctx = ctx_for(wl)
+    t = X.to_device(wl)
+    kc, kn = _gpu_codes(ctx, cbk, K)
+    vc, vn = _gpu_codes(ctx, cbv, V) if V is not None else (None, None)
+    O = ctx.forward_codec(_book(cbk), _book(cbv) if cbv else None, t["Z"],
+                          ctx.codec_fold(_book(cbk), t["W_Q"]), kc, kn, vc, vn, t["cu_kv"],
+                          t["cu_cand"], wl.heads)
+    torch.cuda.synchronize()
+    got = O.float().cpu().numpy().astype(np.float64).reshape(-1, wl.d)
+    Kd = OC.decode(kn.cpu().numpy().T.astype(np.float64), _unpacked(kc, cbk), cbk)
+    Vd = (OC.decode(vn.cpu().numpy().T.astype(np.float64), _unpacked(vc, cbv), cbv)
+          if V is not None else None)
+    ref = oracle.forward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, Kd, Vd)
+    err, rel = assert_close(got, ref, "bf16", "codec qw=%s dh=%d %s" % (qw, dh, mode))
+    print("codec qw=%s dh=%d %s: max-abs %.3e" % (qw, dh, mode, err))
