@@ -502,10 +502,14 @@ xattn_status xattn_backward(xattn_ctx* ctx, const void* Z, const void* W_Q, cons
     // 2. queries (bf16: scaled by log2(e)/sqrt(d_h) exactly as the forward
     //    kernel scales them)
     if (bf) {
+        // one launch: pre-scaled projection, query-tile planner, memory-tile
+        // planner, W_Q transposed
+        const xattn::PrepExtra ex{reinterpret_cast<int*>(ws + Lw.kplan), Lw.max_k, W_Q,
+                                  ws + Lw.wt};
         XATTN_TRY(xattn::launch_project_plan_bf16(Z, W_Q, total_cand, q, d, ws + Lw.qs, cu_kv,
                                                   cu_cand, R, 64, total_kv, ws + Lw.plan, Lw.max_q,
                                                   s, nullptr,
-                                                  1.4426950408889634f / sqrtf((float)dh)),
+                                                  1.4426950408889634f / sqrtf((float)dh), &ex),
                   "projection kernel launch");
     } else {
         XATTN_TRY(xattn::launch_plan(cu_kv, cu_cand, R, q, 64, total_cand, total_kv, ws + Lw.plan,
@@ -516,9 +520,10 @@ xattn_status xattn_backward(xattn_ctx* ctx, const void* Z, const void* W_Q, cons
                                             reinterpret_cast<float*>(ws + Lw.qs), s),
                   "projection kernel launch");
     }
-    XATTN_TRY(xattn::launch_plan(cu_cand, cu_kv, R, 1, 64, total_kv, total_cand, ws + Lw.kplan,
-                                 Lw.max_k, nullptr, nullptr, nullptr, nullptr, s),
-              "memory plan kernel launch");
+    if (!bf)
+        XATTN_TRY(xattn::launch_plan(cu_cand, cu_kv, R, 1, 64, total_kv, total_cand,
+                                     ws + Lw.kplan, Lw.max_k, nullptr, nullptr, nullptr, nullptr, s),
+                  "memory plan kernel launch");
     // per-candidate prefix: absolute end of each candidate's visible memory
     int* vis = cand_kv_len ? reinterpret_cast<int*>(ws + Lw.vis) : nullptr;
     if (vis)
@@ -580,8 +585,9 @@ xattn_status xattn_backward(xattn_ctx* ctx, const void* Z, const void* W_Q, cons
                  : xattn::launch_bwd_attn_f32(b, sep, Lw.max_q, Lw.max_k, s),
               "attention backward launch");
     // 5. dZ = dQ W_Q[slot] through the transposed weights; 6. dW_Q
-    XATTN_TRY(xattn::launch_transpose_weights(W_Q, q, d, !bf, ws + Lw.wt, s),
-              "transpose kernel launch");
+    if (!bf)
+        XATTN_TRY(xattn::launch_transpose_weights(W_Q, q, d, true, ws + Lw.wt, s),
+                  "transpose kernel launch");
     if (bf) {
         XATTN_TRY(xattn::launch_project_plan_bf16(ws + Lw.dq, ws + Lw.wt, total_cand, q, d, dZ,
                                                   nullptr, nullptr, 0, 0, 0, nullptr, 0, s),

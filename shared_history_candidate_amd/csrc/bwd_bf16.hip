@@ -38,8 +38,11 @@
 //
 // bwd_dw_kernel: dW_Q[s] = dQ_s^T Z_s (output-major, fp32) as split-K
 // partial tiles over candidate chunks, summed in chunk order by
-// bwd_dw_reduce.  dZ = dQ W_Q[s] is the projection GEMM over a transposed
-// copy of W_Q (bwd_transpose_kernel).
+// bwd_dw_reduce (many threads: a reduction inside the last work-group of a
+// tile measured 25x slower, its loads mostly missing its XCD's L2).  dZ =
+// dQ W_Q[s] is the projection GEMM over a transposed copy of W_Q, made by
+// side work-groups of the projection launch (bf16) or bwd_transpose_kernel
+// (fp32).
 #include "common.h"
 #include "internal.h"
 

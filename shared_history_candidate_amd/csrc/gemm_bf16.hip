@@ -59,7 +59,40 @@ struct PlanArgs {
     int64_t max_tiles;
     int R, tile_m, total_kv;
     int enabled;
+    PrepExtra ex;   // backward-pass side jobs (memory planner, W transpose)
+    int tr_blocks;  // work-groups of the transpose job
 };
+
+// Side jobs of the backward pass's projection launch: the memory-tile plan
+// (the planner with memory and candidates exchanged, tiles of 64 rows) and
+// W_Q transposed for dZ.
+__device__ void prep_side_jobs(const PlanArgs& pa, int job, int total_cand, int q, int d,
+                               char* smem) {
+    const PrepExtra& ex = pa.ex;
+    if (job == 0) {
+        run_plan<256>(pa.cu_cand, pa.cu_kv, pa.R, 1, 64, pa.total_kv, total_cand, ex.kws,
+                      ex.max_ktiles, nullptr, nullptr, nullptr, nullptr,
+                      *reinterpret_cast<PlanSmem*>(smem));
+        return;
+    }
+    // transpose tile (job - 1): wT[s][i][o] = wt[s][o][i], 32 x 32 per work-group
+    const int t = job - 1, tpd = (d + 31) / 32;
+    const int s = t / (tpd * tpd), rem = t - s * tpd * tpd;
+    const int o0 = (rem / tpd) * 32, i0 = (rem % tpd) * 32;
+    bf16 (*tileb)[33] = reinterpret_cast<bf16 (*)[33]>(smem);
+    const bf16* src = static_cast<const bf16*>(ex.wsrc) + (size_t)s * d * d;
+    bf16* dst = static_cast<bf16*>(ex.wdst) + (size_t)s * d * d;
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 32 x 8
+    for (int y = ty; y < 32; y += 8) {
+        const int o = o0 + y, i = i0 + tx;
+        if (o < d && i < d) tileb[y][tx] = src[(size_t)o * d + i];
+    }
+    __syncthreads();
+    for (int y = ty; y < 32; y += 8) {
+        const int i = i0 + y, o = o0 + tx;
+        if (o < d && i < d) dst[(size_t)i * d + o] = tileb[tx][y];
+    }
+}
 
 __device__ __forceinline__ uint32_t clamp_bytes(size_t b) {
     return b > 0xFFFFFFF0u ? 0xFFFFFFF0u : (uint32_t)b;
@@ -83,6 +116,13 @@ __global__ __launch_bounds__(256) void prep_kernel(const bf16* __restrict__ Z,
             return;
         }
         --bid;
+    }
+    if (pa.ex.kws) {   // side jobs of the backward pass
+        if (bid < 1 + pa.tr_blocks) {
+            prep_side_jobs(pa, bid, total_cand, q, d, smem);
+            return;
+        }
+        bid -= 1 + pa.tr_blocks;
     }
     // Work-groups are dealt to the 8 XCDs (each with its own L2) in turn, so
     // tile number n runs on XCD n % 8.  Remap so that tiles adjacent in
@@ -226,7 +266,8 @@ hipError_t launch_prep(const void* Z, const void* Wq, int total_cand, int q, int
                        const PlanArgs& pa, hipStream_t stream, const void* Og, float oscale) {
     const int tiles_e = (d + TE - 1) / TE;
     const int tiles_c = (total_cand + TC - 1) / TC;
-    const int64_t blocks = (int64_t)q * tiles_e * tiles_c + (pa.enabled ? 1 : 0);
+    const int64_t blocks = (int64_t)q * tiles_e * tiles_c + (pa.enabled ? 1 : 0) +
+                           (pa.ex.kws ? 1 + pa.tr_blocks : 0);
     if (blocks <= 0) return hipSuccess;
     hipLaunchKernelGGL((prep_kernel<TE, TC, KC>), dim3((unsigned)blocks), dim3(256), 0, stream,
                        static_cast<const bf16*>(Z), static_cast<const bf16*>(Wq), total_cand, q, d,
@@ -240,9 +281,14 @@ hipError_t launch_prep(const void* Z, const void* Wq, int total_cand, int q, int
 hipError_t launch_project_plan_bf16(const void* Z, const void* Wq, int total_cand, int q, int d,
                                     void* Q, const int* cu_kv, const int* cu_cand, int R,
                                     int tile_m, int total_kv, void* ws, int64_t max_tiles,
-                                    hipStream_t stream, const void* Og, float oscale) {
+                                    hipStream_t stream, const void* Og, float oscale,
+                                    const PrepExtra* ex) {
     PlanArgs pa{cu_kv, cu_cand, static_cast<int*>(ws), max_tiles, R, tile_m, total_kv,
-                ws != nullptr ? 1 : 0};
+                ws != nullptr ? 1 : 0, ex ? *ex : PrepExtra{}, 0};
+    if (ex) {
+        const int tpd = (d + 31) / 32;
+        pa.tr_blocks = q * tpd * tpd;
+    }
     if (total_cand <= 0 && !pa.enabled) return hipSuccess;
     // XATTN_GEMM="TE,TC,KC" picks a tile shape (tuning).
     if (const char* env = getenv("XATTN_GEMM")) {

@@ -49,13 +49,22 @@ hipError_t launch_attn_bf16(const AttnArgs& a, int rb, int ksplit, hipStream_t s
 
 // bf16 TSP projection Q = Z W_Q[slot] into Qp; when ws is not NULL the same
 // launch also runs the planner into ws (one extra work-group).
+// Backward-pass side jobs run by extra work-groups of the projection launch:
+// the memory-tile plan into kws (max_ktiles items) and wdst = wsrc
+// transposed per slot ([q][d][d] bf16).
+struct PrepExtra {
+    int* kws;
+    int64_t max_ktiles;
+    const void* wsrc;
+    void* wdst;
+};
 // With oscale != 1 the stored value is bf16(float(bf16(acc)) * oscale): the
 // queries pre-scaled exactly as the attention kernel scales them.
 hipError_t launch_project_plan_bf16(const void* Z, const void* Wq, int total_cand, int q, int d,
                                     void* Qp, const int* cu_kv, const int* cu_cand, int R,
                                     int tile_m, int total_kv, void* ws, int64_t max_tiles,
                                     hipStream_t stream, const void* Og = nullptr,
-                                    float oscale = 1.0f);
+                                    float oscale = 1.0f, const PrepExtra* ex = nullptr);
 
 // Output gate and projection of Eq. (7): X = O * sigmoid(Z W_go[slot]) (bf16,
 // [total_cand][q][d]), then Y = X W_o; two launches of the projection kernel.
