@@ -16,9 +16,10 @@
 // softmax normaliser in those units) and D, so a weight is exp2(Qs.k - lse)
 // and both kernels recompute P without any running maximum.
 //
-// bwd_dq_kernel: one work-group (2 waves, 64 query rows) per plan item and
-// head, streaming the request's memory tiles through LDS like the forward
-// kernel.  Per 64-row tile and wave:
+// bwd_dq_kernel: one work-group (2 x KS waves, 64 query rows) per plan item
+// and head, streaming the request's memory tiles through LDS like the
+// forward kernel; KS memory splits (tiles t with t % KS == split), their
+// partial dQ summed on chip in split order.  Per 64-row tile and wave:
 //   S^T - lse  (64 x 32) = K_tile . Qs^T     (accumulator seeded with -lse)
 //   dP^T - D   (64 x 32) = V_tile . dO^T     (seeded with -D)
 //   dQ^T      (d_h x 32) += K_tile^T . dS^T  (K^T from LDS transpose reads)
@@ -43,6 +44,8 @@
 // dQ W_Q[s] is the projection GEMM over a transposed copy of W_Q, made by
 // side work-groups of the projection launch (bf16) or bwd_transpose_kernel
 // (fp32).
+#include <cstdlib>
+
 #include "common.h"
 #include "internal.h"
 
@@ -71,20 +74,23 @@ __device__ __forceinline__ bf16x8 ld8(const bf16* p) {
 // ---------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------
-template <int DH, bool SEP>
+template <int DH, bool SEP, int KS>
 struct DqCfg {
-    static constexpr int NT = 128;
+    static constexpr int NT = 128 * KS;
+    static constexpr int GT = 128;               // threads of one memory split
     static constexpr int EB = DH / 32, KST = DH / 16;
     static constexpr int LDK = DH + 8;           // 16-byte rows
     static constexpr int PLANES = SEP ? 2 : 1;
     static constexpr int TILE = kBN * LDK;
-    static constexpr int SMEM = 2 * PLANES * TILE * 2;
-    static constexpr int CPT = kBN * DH / 8 / NT;   // 16-byte chunks per thread and plane
+    static constexpr int STG = KS * 2 * PLANES * TILE * 2;
+    static constexpr int CMB = (KS - 1) * 2 * EB * 16 * 64 * 4;
+    static constexpr int SMEM = STG > CMB ? STG : CMB;
+    static constexpr int CPT = kBN * DH / 8 / GT;   // 16-byte chunks per thread and plane
 };
 
-template <int DH, bool SEP, bool CUT>
-__global__ __launch_bounds__(128) void bwd_dq_kernel(BwdArgs a) {
-    using C = DqCfg<DH, SEP>;
+template <int DH, bool SEP, bool CUT, int KS>
+__global__ __launch_bounds__(128 * KS) void bwd_dq_kernel(BwdArgs a) {
+    using C = DqCfg<DH, SEP, KS>;
     __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
     const int q = a.q, d = a.d, heads = a.heads;
     const int* __restrict__ ws = a.plan;
@@ -101,8 +107,10 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(BwdArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int qblk = w & 1, ksg = w >> 1;        // query block, memory split
+    const int gt = tid - ksg * C::GT;            // thread index inside the split
     const int g = lane >> 5, l32 = lane & 31;
-    const int qcol = w * 32 + l32;
+    const int qcol = qblk * 32 + l32;
     const bool qvalid = qcol < nc;
     const size_t row = (size_t)(qvalid ? c0 + qcol : c0 + nc - 1) * q + s;
 
@@ -140,7 +148,7 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(BwdArgs a) {
     int goff[C::CPT], loff[C::CPT];
 #pragma unroll
     for (int u = 0; u < C::CPT; ++u) {
-        const int c = tid + u * C::NT;
+        const int c = gt + u * C::GT;
         const int j = c / (DH / 8), c8 = c % (DH / 8);
         goff[u] = (j * d + c8 * 8) * 2;
         loff[u] = j * C::LDK + c8 * 8;
@@ -158,7 +166,7 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(BwdArgs a) {
             for (int u = 0; u < C::CPT; ++u) vr[u] = bload(rv, goff[u]);
         }
     };
-    bf16* lds = reinterpret_cast<bf16*>(smem);
+    bf16* lds = reinterpret_cast<bf16*>(smem) + (size_t)ksg * 2 * C::PLANES * C::TILE;
     auto lstore = [&](int buf) {
         bf16* base = lds + buf * C::PLANES * C::TILE;
 #pragma unroll
@@ -169,9 +177,10 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(BwdArgs a) {
     };
 
     const int ntiles = (L_loop + kBN - 1) / kBN;
-    gload(0);
+    const int n_iter = (ntiles + KS - 1) / KS;   // the same in every split
+    gload(ksg);
     lstore(0);
-    gload(1);
+    gload(ksg + KS);
     __syncthreads();
 
     f32x16 dq[C::EB];
@@ -182,8 +191,10 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(BwdArgs a) {
     const int tr_row = 4 * (G >> 1) + (k16 >> 2);
     const int tr_col = 16 * (G & 1) + 4 * (k16 & 3);
 
-    for (int t = 0; t < ntiles; ++t) {
-        const bf16* kb = lds + (t & 1) * C::PLANES * C::TILE;
+    for (int it = 0; it < n_iter; ++it) {
+      const int t = ksg + it * KS;
+      if (t < ntiles) {
+        const bf16* kb = lds + (it & 1) * C::PLANES * C::TILE;
         const bf16* vb = kb + (C::PLANES - 1) * C::TILE;
         // keys hh*32 + (r/4)*8 + 4g + r%4 of the tile, query row qcol
         f32x16 sacc[2], pacc[2];
@@ -220,9 +231,32 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(BwdArgs a) {
                 dq[eb] = mfma32(cat(lds_read_tr16(base), lds_read_tr16(base + 8 * C::LDK)), dsb[u],
                                 dq[eb]);
             }
-        if (t + 1 < ntiles) lstore((t + 1) & 1);
-        gload(t + 2);
+      }
+        if (it + 1 < n_iter) lstore((it + 1) & 1);
+        gload(t + 2 * KS);
         __syncthreads();
+    }
+    // partial dQ of the memory splits, summed in split order (dQ is linear
+    // in the memory tiles)
+    if constexpr (KS > 1) {
+        float* cmb = reinterpret_cast<float*>(smem);
+        if (ksg > 0) {
+            float* dst = cmb + (size_t)(((ksg - 1) * 2 + qblk) * C::EB * 16) * 64;
+#pragma unroll
+            for (int eb = 0; eb < C::EB; ++eb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dst[(eb * 16 + r) * 64 + lane] = dq[eb][r];
+        }
+        __syncthreads();
+        if (ksg > 0) return;
+#pragma unroll
+        for (int k = 1; k < KS; ++k) {
+            const float* src = cmb + (size_t)(((k - 1) * 2 + qblk) * C::EB * 16) * 64;
+#pragma unroll
+            for (int eb = 0; eb < C::EB; ++eb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dq[eb][r] += src[(eb * 16 + r) * 64 + lane];
+        }
     }
 
     if (qvalid) {
@@ -564,11 +598,33 @@ __global__ void bwd_transpose_kernel(const T* __restrict__ wt, int q, int d, T* 
 }
 
 template <int DH, bool SEP, bool CUT>
+hipError_t launch_dq(const BwdArgs& a, int64_t q_items, hipStream_t stream) {
+    // two memory splits wherever the LDS leaves room for two work-groups per
+    // CU (measured faster than one on every workload, and four no better)
+    const int64_t wgs = q_items * a.heads;
+    int ks = 2;
+    if (const char* env = getenv("XATTN_DQ_KS")) {   // tuning and tests
+        const int v = atoi(env);
+        if (v == 1 || v == 2) ks = v;
+    }
+    const dim3 grid((unsigned)wgs);
+    if constexpr (DqCfg<DH, SEP, 2>::SMEM <= 81920) {
+        if (ks == 2) {
+            hipLaunchKernelGGL((bwd_dq_kernel<DH, SEP, CUT, 2>), grid, dim3(256), 0, stream, a);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((bwd_dq_kernel<DH, SEP, CUT, 1>), grid, dim3(128), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int DH, bool SEP, bool CUT>
 hipError_t launch_bwd_variant(const BwdArgs& a, int64_t q_items, int64_t k_items,
                               hipStream_t stream) {
-    if (q_items > 0)
-        hipLaunchKernelGGL((bwd_dq_kernel<DH, SEP, CUT>), dim3((unsigned)(q_items * a.heads)),
-                           dim3(128), 0, stream, a);
+    if (q_items > 0) {
+        hipError_t e0 = launch_dq<DH, SEP, CUT>(a, q_items, stream);
+        if (e0 != hipSuccess) return e0;
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (k_items > 0)

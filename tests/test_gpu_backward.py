@@ -209,3 +209,18 @@ def test_backward_prefix_full_length_matches_plain(name):
     torch.cuda.synchronize()
     for k in ("dZ", "dW_Q", "dK"):
         assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("ks", ["1", "2"])
+@pytest.mark.parametrize("dh,heads,mode,cut", [(32, 4, "separate", False), (64, 2, "shared", True),
+                                               (128, 2, "shared", False)])
+def test_backward_dq_memory_splits(monkeypatch, ks, dh, heads, mode, cut):
+    """The dQ kernel with 1 and 2 memory splits (forced through XATTN_DQ_KS;
+    two splits are not built where their LDS would not fit twice per CU)."""
+    monkeypatch.setenv("XATTN_DQ_KS", ks)
+    wl = W.custom("ks", [700, 65, 1, 300], [40, 90, 2, 11], q=3, d=dh * heads, heads=heads,
+                  dtype="bf16", kv_mode=mode, seed=int(ks) + dh)
+    if cut:
+        _check_prefix(wl, W.prefix_lengths(wl, seed=3), seed=4, what="ks=%s dh=%d" % (ks, dh))
+    else:
+        _check(wl, seed=4, what="ks=%s dh=%d %s" % (ks, dh, mode))
