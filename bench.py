@@ -38,7 +38,9 @@ KERNEL_SOURCES = {"fused": _ATTN_SRC, "attention": _ATTN_SRC, "prefix": _ATTN_SR
                              "shared_history_candidate_amd/csrc/common.h"],
                   "projection": ["shared_history_candidate_amd/csrc/gemm_bf16.hip",
                                  "shared_history_candidate_amd/csrc/plan_device.h",
-                                 "shared_history_candidate_amd/csrc/common.h"]}
+                                 "shared_history_candidate_amd/csrc/common.h"],
+                  "short": ["shared_history_candidate_amd/csrc/short_bf16.hip",
+                            "shared_history_candidate_amd/csrc/common.h"]}
 
 
 def parse():
@@ -120,9 +122,9 @@ def kernel_sha(kernel):
 
 # Kernel names (regular expressions over the demangled or mangled names) of
 # the kernels a step can run: the single launch of a small batch (attention
-# kernel that projects its own queries: flags PROJ=1, CUT=0), or the
+# kernel that projects its own queries: flags PROJ=1, CUT=0), the
 # projection GEMM and the attention kernel over its output (PROJ=0; CUT=1
-# with per-candidate prefix lengths).
+# with per-candidate prefix lengths), or the short-memory kernel.
 KERNEL_NAMES = {
     "fused": r"attn_bf16_kernel(<\d+, \d+, \d+, \w+, true, false>|"
              r"ILi\d+ELi\d+ELi\d+ELb[01]ELb1ELb0E)",
@@ -130,7 +132,8 @@ KERNEL_NAMES = {
                  r"ILi\d+ELi\d+ELi\d+ELb[01]ELb0ELb0E)",
     "prefix": r"attn_bf16_kernel(<\d+, \d+, \d+, \w+, false, true>|"
               r"ILi\d+ELi\d+ELi\d+ELb[01]ELb0ELb1E)",
-    "projection": r"prep_kernel"}
+    "projection": r"prep_kernel",
+    "short": r"short_bf16_kernel"}
 
 
 def traffic_for(kernel, config):
@@ -417,8 +420,9 @@ def main():
         return a.elapsed_time(b) / args.steps
 
     launches = ctx.forward_launches(wl.R, wl.total_cand, wl.total_kv, wl.heads)
+    path = ctx.forward_path(wl.R, wl.total_cand, wl.total_kv, wl.heads)
     if args.stage != "attention":
-        launches = 0
+        launches = path = 0
 
     def entry(kernel, flops, nbytes, ms):
         return dict(roofline(flops, nbytes, ms, wl.dtype), kernel_ms=round(ms, 5),
@@ -448,6 +452,17 @@ def main():
         out_ms = per_launch_ms(step)
         print("bench: output stage %.4f ms" % out_ms, file=sys.stderr, flush=True)
         roof = entry("output", wl.flops_output(), wl.bytes_output(), out_ms)
+        roof["other_kernel"] = None
+    elif path == X.PATH_SHORT:
+        # The planner, then one kernel that projects and attends: that kernel
+        # alone (xattn_attend over the plan the last step stored) does the
+        # whole path's work.
+        short_ms = per_launch_ms(lambda: ctx.attend(t["Z"], t["W_Q"], t["K"], t["V"], t["cu_kv"],
+                                                    t["cu_cand"], wl.heads, ws, O=O,
+                                                    stream=stream))
+        print("bench: short-memory kernel %.4f ms per launch (step %.4f ms with the planner)" %
+              (short_ms, ms_per_step), file=sys.stderr, flush=True)
+        roof = entry("short", wl.flops(), wl.bytes(), short_ms)
         roof["other_kernel"] = None
     elif launches == 1:
         # The step is one kernel: the attention kernel plans the batch and

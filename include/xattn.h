@@ -126,12 +126,19 @@ size_t xattn_workspace_size(const xattn_ctx* ctx, int32_t num_requests,
 
 /* Shared-history cross-attention forward (Eq. (7) attention with Eq. (8)
  * per-slot W_Q; layouts and precision in the header comment).  Enqueues on
- * `stream` either one kernel - bf16 batches of at most 16 requests on a model
- * of at most 256 features: the attention kernel plans the batch, projects its
- * own queries and writes the plan into the workspace - or the TSP projection
- * (whose launch also runs the varlen planner in one extra work-group) and
- * then the attention kernel, which reads the projected queries and the plan
- * from the workspace (xattn_forward_launches() tells which).
+ * `stream` one of (xattn_forward_path() tells which):
+ *   - one kernel - bf16 batches of at most 16 requests on a model of at most
+ *     256 features: the attention kernel plans the batch, projects its own
+ *     queries and writes the plan into the workspace;
+ *   - the planner, then the short-memory kernel, which projects and attends
+ *     in one launch - bf16 batches on a 256-feature model whose memories are
+ *     short on average (total_kv <= 96 * num_requests with separate K and V,
+ *     192 * num_requests with K = V; the TransX behaviour memory, TransX
+ *     report s.2); any single memory may be longer;
+ *   - the TSP projection (whose launch also runs the varlen planner in one
+ *     extra work-group) and then the attention kernel, which reads the
+ *     projected queries and the plan from the workspace.
+ * The three compute the same roundings (below).
  * `workspace` is device memory of at least xattn_workspace_size() bytes,
  * owned by the caller; its contents on entry are ignored.
  * Errors: XATTN_EINVAL for NULL pointers / negative counts / heads not
@@ -348,13 +355,26 @@ int64_t xattn_max_tiles(const xattn_ctx* ctx, int32_t num_requests,
                         int32_t total_cand, int32_t heads);
 
 /* Number of kernel launches xattn_forward enqueues for this batch shape (for
- * callers that capture or time it): 1 for bf16 batches of at most 16
- * requests on a model of at most 256 features (the attention kernel plans
- * the batch and projects its own queries), 2 for other bf16 batches
- * (projection GEMM with the planner, then attention), 3 in fp32 mode.
+ * callers that capture or time it): 1 on XATTN_PATH_SINGLE, 2 on
+ * XATTN_PATH_GEMM and XATTN_PATH_SHORT, 3 in fp32 mode.
  * Returns 0 for invalid arguments or a batch without query rows. */
 int32_t xattn_forward_launches(const xattn_ctx* ctx, int32_t num_requests,
                                int32_t total_cand, int32_t total_kv, int32_t heads);
+
+/* Kernels xattn_forward (and xattn_attend, minus the planner) runs for this
+ * batch shape. */
+typedef enum {
+    XATTN_PATH_SINGLE = 1,  /* attention kernel plans and projects (<= 16 requests) */
+    XATTN_PATH_GEMM = 2,    /* projection GEMM with the planner, then attention      */
+    XATTN_PATH_FP32 = 3,    /* fp32 planner, projection and attention kernels        */
+    XATTN_PATH_SHORT = 4    /* planner, then the short-memory kernel (projection and
+                               attention in one launch)                              */
+} xattn_path;
+
+/* The xattn_path of this batch shape, or 0 for invalid arguments or a batch
+ * without query rows. */
+int32_t xattn_forward_path(const xattn_ctx* ctx, int32_t num_requests,
+                           int32_t total_cand, int32_t total_kv, int32_t heads);
 
 /* TSP query projection alone (Eq. (8) applied to W_Q of Eq. (7)):
  * Q[row] = Z[row] . W_Q[row % q], Q [total_cand][q][d] in the context's

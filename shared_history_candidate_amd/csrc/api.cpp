@@ -16,6 +16,7 @@
 
 struct xattn_ctx {
     xattn_config cfg;
+    int n_cu = 0;   // compute units of cfg.device, read on first use
 };
 
 namespace {
@@ -53,6 +54,36 @@ struct Variant {
 // (with the planner) and then the attention kernel over its output.
 bool fused_shape(const xattn_config& c, int R) {
     return c.d_model <= xattn::kAttnProjMaxD && R <= xattn::kInPlanMaxRequests;
+}
+
+// Batches of short memories (mean L_r no longer than what LDS holds at once)
+// on a 256-feature bf16 model run the planner and then the short-memory
+// kernel, which projects and attends in one launch (short_bf16.hip); small
+// batches keep the single launch.  XATTN_SHORT=0 / 1 turns the path off / on
+// for every batch it supports (tuning and tests).
+bool short_shape(const xattn_config& c, int R, int total_kv, int heads) {
+    if (c.dtype != XATTN_BF16 || c.d_model != xattn::kShortD || heads < 1 || c.d_model % heads)
+        return false;
+    const int dh = c.d_model / heads;
+    if (dh != 32 && dh != 64 && dh != 128) return false;
+    if (const char* env = getenv("XATTN_SHORT")) return env[0] == '1';
+    if (fused_shape(c, R)) return false;
+    return (int64_t)total_kv <=
+           (int64_t)R * xattn::short_max_rows(c.kv_mode == XATTN_KV_SEPARATE);
+}
+
+// Work-groups of the short-memory kernel: one per compute unit (its LDS
+// footprint admits one), never more than there are work items.
+int short_grid(xattn_ctx* ctx, int64_t max_tiles) {
+    if (ctx->n_cu <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, ctx->cfg.device) !=
+                hipSuccess ||
+            n <= 0)
+            n = 256;
+        ctx->n_cu = n;
+    }
+    return (int)(max_tiles < ctx->n_cu ? max_tiles : ctx->n_cu);
 }
 
 // LDS bytes of a variant as this batch shape launches it.  The choice depends
@@ -191,17 +222,29 @@ int64_t xattn_max_tiles(const xattn_ctx* ctx, int32_t R, int32_t total_cand, int
     return max_tiles_any(ctx->cfg, R, total_cand);
 }
 
-int32_t xattn_forward_launches(const xattn_ctx* ctx, int32_t R, int32_t total_cand,
-                               int32_t total_kv, int32_t heads) {
+int32_t xattn_forward_path(const xattn_ctx* ctx, int32_t R, int32_t total_cand,
+                           int32_t total_kv, int32_t heads) {
     if (!ctx || R <= 0 || total_cand <= 0 || total_kv < 0 || heads < 1 ||
         ctx->cfg.d_model % heads != 0)
         return 0;
     const xattn_config& c = ctx->cfg;
-    if (c.dtype != XATTN_BF16) return 3;
+    if (c.dtype != XATTN_BF16) return XATTN_PATH_FP32;
+    if (short_shape(c, R, total_kv, heads)) return XATTN_PATH_SHORT;
     const Variant var = choose_variant(c, R, total_cand, total_kv, heads);
     return fused_shape(c, R) && xattn::attn_bf16_variant_smem(c.d_model / heads, var.rb, var.ksplit,
                                                               c.kv_mode == XATTN_KV_SEPARATE, true) > 0
-               ? 1 : 2;
+               ? XATTN_PATH_SINGLE : XATTN_PATH_GEMM;
+}
+
+int32_t xattn_forward_launches(const xattn_ctx* ctx, int32_t R, int32_t total_cand,
+                               int32_t total_kv, int32_t heads) {
+    switch (xattn_forward_path(ctx, R, total_cand, total_kv, heads)) {
+        case XATTN_PATH_SINGLE: return 1;
+        case XATTN_PATH_GEMM: return 2;
+        case XATTN_PATH_FP32: return 3;
+        case XATTN_PATH_SHORT: return 2;
+        default: return 0;
+    }
 }
 
 size_t xattn_workspace_size(const xattn_ctx* ctx, int32_t R, int32_t total_cand, int32_t heads) {
@@ -298,6 +341,21 @@ xattn_status run_forward(Mode mode, xattn_ctx* ctx, const void* Z, const void* W
         a.heads = heads;
         a.O = O;
         a.cand_len = cand_len;
+        if (mode != Mode::kAttendQ && !cand_len && short_shape(c, R, total_kv, heads)) {
+            // the planner (forward), then projection and attention in one launch
+            if (mode == Mode::kForward) {
+                e = xattn::launch_plan(cu_kv, cu_cand, R, c.n_slots, tm, total_cand, total_kv,
+                                       workspace, max_tiles, nullptr, nullptr, nullptr, nullptr, s,
+                                       /*rank=*/false);
+                if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
+            }
+            a.Z = Z;
+            a.Wq = W_Q;
+            a.tile_m = tm;
+            e = xattn::launch_short_bf16(a, short_grid(ctx, max_tiles), s);
+            if (e != hipSuccess) return hip_fail(e, "short-memory kernel launch");
+            return XATTN_OK;
+        }
         // the prefix cutoff runs over projected queries in the workspace
         const bool fused_proj =
             !cand_len && fused_shape(c, R) &&

@@ -234,6 +234,7 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(AttnArgs a)
     bf16x8 qb[C::KST];
     uint4 zst[PROJ ? C::ZCPT : 1], wst[PROJ ? C::WCPT : 1];
     const int cpr = d >> 3;   // 16-byte chunks per model row
+    const uint32_t cmg = 0xFFFFFFFFu / (uint32_t)cpr + 1u;
     if constexpr (PROJ) {
         // Operands of the TSP projection (ReST reading note, s.3.3.2 Eq. (8)):
         // this tile's query tokens (candidates c0.., slot s; rows past nc are
@@ -248,7 +249,7 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(AttnArgs a)
             (uint32_t)(DH * d * 2), 0x00020000);
 #pragma unroll
         for (int u = 0; u < C::ZCPT; ++u) {
-            const int idx = tid + u * C::NT, row = idx / cpr, col = idx - row * cpr;
+            const int idx = tid + u * C::NT, row = (int)__umulhi((uint32_t)idx, cmg), col = idx - row * cpr;
             zst[u] = idx < 32 * RB * cpr
                          ? __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                                          rz, (row * q * d + col * 8) * 2, 0, 0))
@@ -256,7 +257,7 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(AttnArgs a)
         }
 #pragma unroll
         for (int u = 0; u < C::WCPT; ++u) {
-            const int idx = tid + u * C::NT, row = idx / cpr, col = idx - row * cpr;
+            const int idx = tid + u * C::NT, row = (int)__umulhi((uint32_t)idx, cmg), col = idx - row * cpr;
             wst[u] = idx < DH * cpr
                          ? __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                                          rw, (row * d + col * 8) * 2, 0, 0))
@@ -277,12 +278,12 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(AttnArgs a)
         bf16* wsh = zs + 32 * RB * C::LDS_K;
 #pragma unroll
         for (int u = 0; u < C::ZCPT; ++u) {
-            const int idx = tid + u * C::NT, row = idx / cpr, col = idx - row * cpr;
+            const int idx = tid + u * C::NT, row = (int)__umulhi((uint32_t)idx, cmg), col = idx - row * cpr;
             if (idx < 32 * RB * cpr) *reinterpret_cast<uint4*>(zs + row * C::LDS_K + col * 8) = zst[u];
         }
 #pragma unroll
         for (int u = 0; u < C::WCPT; ++u) {
-            const int idx = tid + u * C::NT, row = idx / cpr, col = idx - row * cpr;
+            const int idx = tid + u * C::NT, row = (int)__umulhi((uint32_t)idx, cmg), col = idx - row * cpr;
             if (idx < DH * cpr) *reinterpret_cast<uint4*>(wsh + row * C::LDS_K + col * 8) = wst[u];
         }
         __syncthreads();

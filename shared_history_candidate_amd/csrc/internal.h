@@ -8,7 +8,8 @@ namespace xattn {
 
 hipError_t launch_plan(const int* cu_kv, const int* cu_cand, int R, int q, int tile_m,
                        int total_cand, int total_kv, void* ws, int64_t max_tiles, int* cu_q,
-                       int* row_req, int* tiles, int* n_tiles, hipStream_t stream);
+                       int* row_req, int* tiles, int* n_tiles, hipStream_t stream,
+                       bool rank = true);
 
 // bf16 attention (attn_bf16.hip).  A work-group has rb x ksplit waves: rb
 // query blocks of 32 candidates (tile_m = 32 * rb) and ksplit memory splits
@@ -29,6 +30,7 @@ struct AttnArgs {
     const int* cand_len;   // per-candidate prefix cutoff, or NULL (Qp path only)
     int64_t max_tiles;
     int R, total_cand, total_kv, inplan, q, d, heads;
+    int tile_m;         // candidates per plan tile (short-memory kernel's plan check)
     // Qp already holds bf16(Q * log2(e)/sqrt(d_h)) (backward pass)
     int prescaled;
     float scale_log2;   // set by the launcher
@@ -46,6 +48,14 @@ constexpr int kAttnProjMaxD = 256;
 // source, 0 if not built.
 int attn_bf16_variant_smem(int dh, int rb, int ksplit, bool sep, bool proj);
 hipError_t launch_attn_bf16(const AttnArgs& a, int rb, int ksplit, hipStream_t stream);
+
+// Short-memory kernel (short_bf16.hip): projection and attention in one
+// launch over the plan in a.ws, for a model of kShortD features.  Memories of
+// up to short_max_rows() rows stay in LDS whole; longer ones are streamed in
+// chunks of that size.  `grid` work-groups walk the plan's items.
+constexpr int kShortD = 256;
+constexpr int short_max_rows(bool sep) { return sep ? 96 : 192; }
+hipError_t launch_short_bf16(const AttnArgs& a, int grid, hipStream_t stream);
 
 // bf16 TSP projection Q = Z W_Q[slot] into Qp; when ws is not NULL the same
 // launch also runs the planner into ws (one extra work-group).

@@ -1,0 +1,449 @@
+// Short-memory cross-attention with the TSP query projection in the same
+// kernel, bf16 in, fp32 accumulate, bf16 out, for gfx950 matrix cores.
+//
+// It computes what the projection GEMM (gemm_bf16.hip) followed by
+// attn_bf16_kernel computes, with the same roundings:
+//   Q   = Z W_Q[s]                  (ReST reading note s.3.3.2, Eq. (8)),
+//         rounded to bf16, scaled by log2(e)/sqrt(d_h) and rounded again;
+//   O_h = softmax(Q_h K_h^T / sqrt(d_h)) V_h
+//         (ReST reading note s.3.3.1 Eq. (7); separate K and V for the
+//         TransX behaviour memory, TransX report s.2)
+// on a model of d = 256 features.  It is built for memories short enough
+// that every head's keys and values of a request fit in LDS together (the
+// TransX memory of 64 recent rows and 32 chunk summaries): up to 96 rows with
+// separate K and V, 192 rows with K = V.  Longer memories are streamed
+// through LDS in chunks of that many rows (correct, but without overlap).
+//
+// Why one kernel: with one query token per candidate and a memory of ~100
+// rows, the queries are the bulk of the traffic.  A separate projection
+// writes Q to HBM and the attention reads it back (2 x 2 bytes per query
+// feature on top of Z in and O out); here Q lives only in LDS.
+//
+// Work decomposition.  A persistent grid of one 8-wave work-group per compute
+// unit walks the plan's work items in order: work-group i takes items
+// [i T / G, (i + 1) T / G).  The plan keeps the items of a request adjacent,
+// so a request's memory is staged once per work-group that meets it.  Items
+// are processed in chunks of 64 query rows:
+//   1. Projection on the matrix cores.  Wave w holds rows 32w..32w+31 of
+//      W_Q[s] (its 32 output features over all 256 inputs) in registers as A
+//      operands, reloaded only when the slot changes; the chunk's Z rows sit
+//      in LDS and every wave reads them as B operands.  The next chunk's Z
+//      rows are loaded into registers meanwhile and written to LDS at the
+//      end of the chunk.
+//   2. The Q chunk (bf16, rows x features) overwrites the Z chunk in LDS.
+//   3. Attention.  The units (head h, 32-row query block; with 128-wide
+//      heads also one half of the head's output features, so that all eight
+//      waves have work) are dealt to the waves round-robin.  Per 32-row
+//      memory block: scores
+//      S^T = K_h . Q_h^T (lane = query row), the online softmax of
+//      attn_bf16_kernel (exp2 domain, maximum set by the first block and
+//      moved only when a lane's weights of a block sum past 2^12), and
+//      O^T += V_h^T . P^T with V^T from LDS transpose reads.
+#include <type_traits>
+
+#include "common.h"
+#include "internal.h"
+
+namespace xattn {
+
+namespace {
+
+constexpr int D = kShortD;       // model features
+constexpr int NW = 8;            // waves per work-group
+constexpr int NT = 64 * NW;
+constexpr int QR = 64;           // query rows per chunk
+constexpr int LDK = D + 8;       // LDS pitch (elements) of Z, Q, K and V rows: 16-byte rows
+constexpr int MB = 32;           // memory rows per score block
+constexpr float kSumCap = 4096.0f;
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+template <int DH, bool SEP>
+struct SCfg {
+    static constexpr int PLANES = SEP ? 2 : 1;
+    static constexpr int LMAX = short_max_rows(SEP);   // memory rows resident at once
+    static constexpr int EB = DH / 32;                 // 32-wide feature blocks of a head
+    static constexpr int KST = DH / 16;                // k-steps of the score product
+    // A unit is (head, 32-row query block, part of the head's output
+    // features): wide heads split their output features over two waves (both
+    // compute the unit's scores) so that every wave has work.
+    static constexpr int FP = 2 * (D / DH) < NW ? NW / (2 * (D / DH)) : 1;
+    static constexpr int EBW = EB / FP;                // output feature blocks per unit
+    static constexpr int UNITS = 2 * (D / DH) * FP;
+    static constexpr int UPW = UNITS / NW;             // units per wave
+    static_assert(UNITS % NW == 0, "every wave has the same number of units");
+    static constexpr int KV_ELEMS = PLANES * LMAX * LDK;
+    static constexpr int ZQ_OFF = KV_ELEMS * 2;        // byte offset of the Z / Q chunk
+    static constexpr int SMEM = ZQ_OFF + QR * LDK * 2;
+    static constexpr int KV_CPT = LMAX * (D / 8) / NT;  // 16-byte memory chunks per thread per plane
+    static constexpr int Z_CPT = QR * (D / 8) / NT;     // 16-byte Z chunks per thread
+    static_assert(LMAX * (D / 8) % NT == 0 && QR * (D / 8) % NT == 0, "even staging split");
+    static_assert(LMAX % MB == 0, "whole score blocks");
+};
+
+// One query chunk: candidates [cb, cb + nr) of a request, slot s.
+struct Chunk {
+    int kv0, L, c0, nc, s;   // the work item
+    int j;                   // chunk index inside the item
+};
+
+template <int DH, bool SEP>
+__global__ __launch_bounds__(NT) void short_bf16_kernel(AttnArgs a) {
+    using C = SCfg<DH, SEP>;
+    constexpr int LMAX = C::LMAX;
+    __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
+    bf16* kvs = reinterpret_cast<bf16*>(smem);                 // K rows, then V rows (SEP)
+    bf16* zq = reinterpret_cast<bf16*>(smem + C::ZQ_OFF);     // Z, then Q, of one chunk
+    const bf16* vsrc = kvs + (SEP ? LMAX * LDK : 0);
+
+    const int q = a.q;
+    const float scale_log2 = a.scale_log2;
+    const bf16* __restrict__ Z = static_cast<const bf16*>(a.Z);
+    const bf16* __restrict__ Wq = static_cast<const bf16*>(a.Wq);
+    const bf16* __restrict__ K = static_cast<const bf16*>(a.K);
+    const bf16* __restrict__ V = static_cast<const bf16*>(a.V);
+    bf16* __restrict__ O = static_cast<bf16*>(a.O);
+    // The plan is read through the constant address space: it does not
+    // change during the launch, so its uniform reads become scalar loads,
+    // which are not queued behind this kernel's vector loads and stores.
+    typedef const __attribute__((address_space(4))) int cint;
+    cint* ws = (cint*)a.ws;   // address-space conversion: a C-style cast
+    cint* items = (cint*)(static_cast<const char*>(a.ws) + kPlanHeaderBytes);   // int4 each
+
+    // This work-group's items (none if the plan failed validation: T = 0,
+    // or was built for another tile size, i.e. another batch shape).
+    const int T = ws[kPlanTileM] == a.tile_m ? ws[kPlanNTiles] : 0;
+    const int G = gridDim.x;
+    const int i_end = (int)((int64_t)(blockIdx.x + 1) * T / G);
+    int ii = (int)((int64_t)blockIdx.x * T / G);
+    if (ii >= i_end) return;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 5, l32 = lane & 31;
+
+    auto load_item = [&](int i, Chunk& c) {
+        cint* it = items + 4 * (size_t)i;
+        c.kv0 = __builtin_amdgcn_readfirstlane(it[0]);
+        c.L = __builtin_amdgcn_readfirstlane(it[1]);
+        c.c0 = __builtin_amdgcn_readfirstlane(it[2]);
+        const int iw = __builtin_amdgcn_readfirstlane(it[3]);
+        c.nc = iw & kItemNcMask;
+        c.s = iw >> 16;
+        c.j = 0;
+    };
+
+    // Z rows of a chunk -> registers.  Rows past the chunk's candidates lie
+    // outside the descriptor and read as zeros.
+    uint4 zr[C::Z_CPT];
+    auto zload = [&](const Chunk& c) {
+        const int cb = c.c0 + c.j * QR, nr = min(QR, c.nc - c.j * QR);
+        const uint32_t bytes = (uint32_t)(((size_t)(nr - 1) * q + 1) * D * 2);
+        const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(Z + ((size_t)cb * q + c.s) * D), (short)0, bytes, 0x00020000);
+#pragma unroll
+        for (int u = 0; u < C::Z_CPT; ++u) {
+            const int idx = tid + u * NT, row = idx >> 5, col = idx & 31;
+            zr[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rz, (row * q * D + col * 8) * 2, 0, 0));
+        }
+    };
+    auto zstore = [&]() {
+#pragma unroll
+        for (int u = 0; u < C::Z_CPT; ++u) {
+            const int idx = tid + u * NT, row = idx >> 5, col = idx & 31;
+            *reinterpret_cast<uint4*>(zq + row * LDK + col * 8) = zr[u];
+        }
+    };
+
+    // This wave's 32 rows of W_Q[s]: k-step kk holds inputs 16kk + 8g .. +7
+    // of output feature 32w + l32.
+    bf16x8 wa[D / 16];
+    auto wload = [&](int s) {
+        const bf16* wr = Wq + ((size_t)s * D + 32 * w + l32) * D + 8 * g;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) wa[kk] = *reinterpret_cast<const bf16x8*>(wr + 16 * kk);
+    };
+
+    // Memory rows [row0, row0 + nr) of K (and V) for all heads -> LDS rows
+    // 0..LMAX-1; rows past nr read as zeros, so that the V rows behind a
+    // partial score block are finite.
+    int st_row0 = -1, st_rows = -1;
+    auto kv_stage = [&](int row0, int nr) {
+        const uint32_t bytes = (uint32_t)nr * D * 2;
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(K + (size_t)row0 * D), (short)0, bytes, 0x00020000);
+        uint4 kr[C::KV_CPT], vr[SEP ? C::KV_CPT : 1];
+#pragma unroll
+        for (int u = 0; u < C::KV_CPT; ++u) {
+            const int idx = tid + u * NT, row = idx >> 5, col = idx & 31;
+            kr[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rk, (row * D + col * 8) * 2, 0, 0));
+        }
+        if constexpr (SEP) {
+            const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(V + (size_t)row0 * D), (short)0, bytes, 0x00020000);
+#pragma unroll
+            for (int u = 0; u < C::KV_CPT; ++u) {
+                const int idx = tid + u * NT, row = idx >> 5, col = idx & 31;
+                vr[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      rv, (row * D + col * 8) * 2, 0, 0));
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < C::KV_CPT; ++u) {
+            const int idx = tid + u * NT, row = idx >> 5, col = idx & 31;
+            *reinterpret_cast<uint4*>(kvs + row * LDK + col * 8) = kr[u];
+            if constexpr (SEP) *reinterpret_cast<uint4*>(kvs + (LMAX + row) * LDK + col * 8) = vr[u];
+        }
+        st_row0 = row0;
+        st_rows = nr;
+    };
+
+    // transposed V read: lane l receives V[16u + 4g + t][col + l%32], t = 0..3
+    const int G16 = lane >> 4, k16 = lane & 15;
+    const int tr_row = 4 * (G16 >> 1) + (k16 >> 2);
+    const int tr_col = 16 * (G16 & 1) + 4 * (k16 & 3);
+    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+
+    // ---------------- prologue: first chunk's Z in LDS, W_Q rows in registers ----------------
+    Chunk cur;
+    load_item(ii, cur);
+    int wslot = cur.s;
+    wload(wslot);
+    zload(cur);
+    zstore();   // its wait covers the W_Q rows loaded before the Z rows
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(wa[kk]));
+
+    for (;;) {
+        // the chunk after this one (possibly in the next item)
+        Chunk nxt = cur;
+        bool has_next = true;
+        if ((cur.j + 1) * QR < cur.nc) {
+            nxt.j = cur.j + 1;
+        } else if (ii + 1 < i_end) {
+            load_item(ii + 1, nxt);
+        } else {
+            has_next = false;
+        }
+        __syncthreads();   // Z chunk in LDS; every wave is done with the previous chunk's memory
+        if (has_next) zload(nxt);
+        if (cur.s != wslot) {
+            // a new slot (rare): wait for its rows here, so that the
+            // projection below never waits on the vector-memory counter
+            // (which would also hold it for the Z rows loaded above)
+            wslot = cur.s;
+            wload(wslot);
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(wa[kk]));
+        }
+
+        // ---------------- 1. projection: Q^T rows 32w.. = W_Q[s] rows 32w.. . Z^T ----------------
+        f32x16 acc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                const bf16x8 zb =
+                    *reinterpret_cast<const bf16x8*>(zq + (rb * 32 + l32) * LDK + 16 * kk + 8 * g);
+                acc[rb] = mfma32(wa[kk], zb, acc[rb]);
+            }
+        __syncthreads();   // every wave is done reading Z
+
+        // ---------------- 2. Q chunk into LDS, the request's memory if not there ----------------
+        // acc[rb] reg 4*j4 + t: feature 32w + 8*j4 + 4g + t of query row 32rb + l32
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            bf16* qrow = zq + (rb * 32 + l32) * LDK + 32 * w + 4 * g;
+#pragma unroll
+            for (int j4 = 0; j4 < 4; ++j4) {
+                bf16x4 v;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) v[t] = (bf16)((float)(bf16)acc[rb][4 * j4 + t] * scale_log2);
+                *reinterpret_cast<bf16x4*>(qrow + 8 * j4) = v;
+            }
+        }
+        const int rows0 = min(cur.L, LMAX);
+        if (rows0 > 0 && (cur.kv0 != st_row0 || rows0 != st_rows)) kv_stage(cur.kv0, rows0);
+        __syncthreads();   // Q chunk and memory visible
+
+        // ---------------- 3. attention of this wave's units ----------------
+        bf16x8 qb[C::UPW][C::KST];
+#pragma unroll
+        for (int k = 0; k < C::UPW; ++k) {
+            const int v = ((w + NW * k) / C::FP) % (2 * (D / DH));
+            const int h = v >> 1, urb = v & 1;
+#pragma unroll
+            for (int kk = 0; kk < C::KST; ++kk)
+                qb[k][kk] = *reinterpret_cast<const bf16x8*>(zq + (urb * 32 + l32) * LDK + h * DH +
+                                                             16 * kk + 8 * g);
+        }
+        __syncthreads();   // every wave holds its queries: the chunk buffer is free
+
+        f32x16 oacc[C::UPW][C::EBW];
+        float m_run[C::UPW], l_run[C::UPW];
+        bool started[C::UPW];
+#pragma unroll
+        for (int k = 0; k < C::UPW; ++k) {
+#pragma unroll
+            for (int eb = 0; eb < C::EBW; ++eb) oacc[k][eb] = f32x16{};
+            m_run[k] = -INFINITY;
+            l_run[k] = 0.f;
+            started[k] = false;
+        }
+
+        // One 32-row memory block (t) of the staged rows against unit k's queries.
+        auto block = [&](int k, int t, int rows) {
+            const int u = w + NW * k;
+            const int h = (u / C::FP) >> 1, e0 = (u % C::FP) * C::EBW * 32;
+            const bf16* kb = kvs + (t * MB + l32) * LDK + h * DH + 8 * g;
+            bf16x8 kf[C::KST];
+#pragma unroll
+            for (int kk = 0; kk < C::KST; ++kk) kf[kk] = *reinterpret_cast<const bf16x8*>(kb + 16 * kk);
+            // scores come out relative to the running maximum (0 before the first block)
+            f32x16 seed;
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) seed[rr] = started[k] ? -m_run[k] : 0.f;
+            f32x16 sacc = mfma32(kf[0], qb[k][0], seed);
+#pragma unroll
+            for (int kk = 1; kk < C::KST; ++kk) sacc = mfma32(kf[kk], qb[k][kk], sacc);
+            bf16x8 vf[2][C::EBW];
+#pragma unroll
+            for (int u16 = 0; u16 < 2; ++u16)
+#pragma unroll
+                for (int eb = 0; eb < C::EBW; ++eb) {
+                    const bf16* base =
+                        vsrc + (t * MB + 16 * u16 + tr_row) * LDK + h * DH + e0 + eb * 32 + tr_col;
+                    vf[u16][eb] = cat(lds_read_tr16(base), lds_read_tr16(base + 8 * LDK));
+                }
+            // only the last block of the staged rows is partial
+            int jl = rows - t * MB;
+            asm volatile("" : "+s"(jl));
+            if (jl < MB) {
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    const int j = (rr >> 2) * 8 + 4 * g + (rr & 3);
+                    if (j >= jl) sacc[rr] = -INFINITY;
+                }
+            }
+            // P^T k-step u16 slot t <-> score register 8*u16 + t
+            bf16x8 pb[2];
+            auto weights = [&](auto shifted, float shift) {
+                float lt = 0.f;
+#pragma unroll
+                for (int rr = 0; rr < 16; rr += 2) {
+                    float x0 = sacc[rr], x1 = sacc[rr + 1];
+                    if constexpr (decltype(shifted)::value) x0 += shift, x1 += shift;
+                    const float p0 = __builtin_amdgcn_exp2f(x0);
+                    const float p1 = __builtin_amdgcn_exp2f(x1);
+                    const bf16x2 pp = {(bf16)p0, (bf16)p1};
+                    lt = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lt, false);
+                    pb[rr >> 3][rr & 7] = pp[0];
+                    pb[rr >> 3][(rr & 7) + 1] = pp[1];
+                }
+                return lt;
+            };
+            float lt = weights(std::false_type{}, 0.f);
+            if (!started[k] || __any(lt > kSumCap)) {
+                const float m_seed = started[k] ? m_run[k] : 0.f;
+                float mt = fmaxf(sacc[0], sacc[1]);
+#pragma unroll
+                for (int rr = 2; rr < 16; rr += 2) mt = fmaxf(mt, fmaxf(sacc[rr], sacc[rr + 1]));
+                const float m_new = fmaxf(m_run[k], m_seed + fmaxf(mt, xor32(mt)));
+                const float alpha = __builtin_amdgcn_exp2f(m_run[k] - m_new);
+                m_run[k] = m_new;
+                l_run[k] *= alpha;
+#pragma unroll
+                for (int eb = 0; eb < C::EBW; ++eb) oacc[k][eb] *= alpha;
+                lt = weights(std::true_type{}, m_seed - m_new);
+                started[k] = true;
+            }
+            l_run[k] += lt;
+#pragma unroll
+            for (int u16 = 0; u16 < 2; ++u16)
+#pragma unroll
+                for (int eb = 0; eb < C::EBW; ++eb) oacc[k][eb] = mfma32(vf[u16][eb], pb[u16], oacc[k][eb]);
+        };
+
+        // memory chunks of LMAX rows; the first is staged above, later ones
+        // (memories longer than LMAX) between work-group barriers here
+        const int n_mc = (cur.L + LMAX - 1) / LMAX;
+        for (int mc = 0; mc < n_mc; ++mc) {
+            const int row0 = cur.kv0 + mc * LMAX, rows = min(LMAX, cur.L - mc * LMAX);
+            if (mc > 0) {
+                __syncthreads();   // every wave is done with the previous memory chunk
+                kv_stage(row0, rows);
+                __syncthreads();
+            }
+            const int nb = (rows + MB - 1) / MB;
+#pragma unroll
+            for (int k = 0; k < C::UPW; ++k)
+                for (int t = 0; t < nb; ++t) block(k, t, rows);
+        }
+
+        // Normalise and store this chunk's output rows.  Rows past the
+        // chunk's candidates fall outside the descriptor and are dropped, so
+        // every path issues the same stores (and the compiler's wait for the
+        // next chunk's Z rows below never has to cover them).
+        const int cb = cur.c0 + cur.j * QR, nr = min(QR, cur.nc - cur.j * QR);
+        const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(O + ((size_t)cb * q + cur.s) * D), (short)0,
+            (uint32_t)(((size_t)(nr - 1) * q + 1) * D * 2), 0x00020000);
+#pragma unroll
+        for (int k = 0; k < C::UPW; ++k) {
+            const int u = w + NW * k;
+            const int h = (u / C::FP) >> 1, urb = (u / C::FP) & 1, e0 = (u % C::FP) * C::EBW * 32;
+            const float l = l_run[k] + xor32(l_run[k]);
+            const float inv = l > 0.f ? 1.f / l : 0.f;
+            const int off = ((urb * 32 + l32) * q * D + h * DH + e0 + 4 * g) * 2;
+#pragma unroll
+            for (int eb = 0; eb < C::EBW; ++eb)
+#pragma unroll
+                for (int b4 = 0; b4 < 4; ++b4) {
+                    bf16x4 v;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) v[t] = (bf16)(oacc[k][eb][4 * b4 + t] * inv);
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), ro,
+                                                          off + (eb * 32 + b4 * 8) * 2, 0, 0);
+                }
+        }
+        if (!has_next) break;
+        // the next chunk's Z rows, loaded a whole chunk ago, into the free
+        // chunk buffer (the wait covers them and not this chunk's stores)
+        zstore();
+        if (nxt.j == 0) ++ii;
+        cur = nxt;
+    }
+}
+
+template <int DH, bool SEP>
+hipError_t launch_t(const AttnArgs& a, int grid, hipStream_t stream) {
+    AttnArgs k = a;
+    k.scale_log2 = 1.4426950408889634f / sqrtf((float)DH);
+    hipLaunchKernelGGL((short_bf16_kernel<DH, SEP>), dim3((unsigned)grid), dim3(NT), 0, stream, k);
+    return hipGetLastError();
+}
+
+template <int DH>
+hipError_t launch_dh(const AttnArgs& a, int grid, hipStream_t stream) {
+    return a.V ? launch_t<DH, true>(a, grid, stream) : launch_t<DH, false>(a, grid, stream);
+}
+
+}  // namespace
+
+hipError_t launch_short_bf16(const AttnArgs& a, int grid, hipStream_t stream) {
+    if (a.d != kShortD || a.heads < 1 || a.d % a.heads != 0 || !a.Z || !a.Wq || a.cand_len)
+        return hipErrorInvalidValue;
+    if (grid <= 0) return hipSuccess;
+    switch (a.d / a.heads) {
+        case 32: return launch_dh<32>(a, grid, stream);
+        case 64: return launch_dh<64>(a, grid, stream);
+        case 128: return launch_dh<128>(a, grid, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace xattn

@@ -27,7 +27,10 @@ EXPORTED = ("xattn_create", "xattn_destroy", "xattn_workspace_size", "xattn_forw
             "xattn_forward_launches", "xattn_project", "xattn_output", "xattn_device_error",
             "xattn_last_error", "xattn_forward_prefix", "xattn_attend_q_prefix",
             "xattn_backward_workspace_size", "xattn_backward", "xattn_codec_encode",
-            "xattn_codec_fold_query_weights", "xattn_forward_codec")
+            "xattn_codec_fold_query_weights", "xattn_forward_codec", "xattn_forward_path")
+
+# xattn_path values (include/xattn.h)
+PATH_SINGLE, PATH_GEMM, PATH_FP32, PATH_SHORT = 1, 2, 3, 4
 
 
 class CodebookStruct(ctypes.Structure):
@@ -93,6 +96,8 @@ def lib():
         L.xattn_max_tiles.restype = I64
         L.xattn_forward_launches.argtypes = [P, I32, I32, I32, I32]
         L.xattn_forward_launches.restype = I32
+        L.xattn_forward_path.argtypes = [P, I32, I32, I32, I32]
+        L.xattn_forward_path.restype = I32
         L.xattn_forward.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, P, P, SZ, P]
         L.xattn_forward.restype = ctypes.c_int
         L.xattn_forward_prefix.argtypes = [P, P, P, P, P, P, P, P, I32, I32, I32, I32, P, P, SZ,
@@ -188,6 +193,10 @@ class XAttn:
         """Kernel launches xattn_forward enqueues for this batch shape."""
         return int(lib().xattn_forward_launches(self._h, num_requests, total_cand, total_kv,
                                                 heads))
+
+    def forward_path(self, num_requests: int, total_cand: int, total_kv: int, heads: int) -> int:
+        """Which kernels xattn_forward runs for this batch shape (PATH_*)."""
+        return int(lib().xattn_forward_path(self._h, num_requests, total_cand, total_kv, heads))
 
     def alloc_workspace(self, num_requests: int, total_cand: int, heads: int) -> torch.Tensor:
         n = self.workspace_size(num_requests, total_cand, heads)

@@ -111,6 +111,41 @@ def test_forward_launch_count(L):
     L.xattn_destroy(h)
 
 
+def test_forward_path(L, monkeypatch):
+    """Which kernels run: the single launch for small bf16 batches, the
+    short-memory kernel for larger 256-feature batches whose mean memory fits
+    LDS (96 rows with separate K/V, 192 with K = V), the projection GEMM and
+    attention kernel otherwise; XATTN_SHORT forces the short path off / on."""
+    monkeypatch.delenv("XATTN_SHORT", raising=False)
+    L.xattn_forward_path.restype = ctypes.c_int32
+    st, h = _create(L, 256, 3, X.XATTN_BF16, X.XATTN_KV_SHARED)
+    assert st == 0
+    assert L.xattn_forward_path(h, 8, 2048, 5482, 4) == X.PATH_SINGLE
+    assert L.xattn_forward_path(h, 17, 64, 100, 4) == X.PATH_SHORT
+    assert L.xattn_forward_path(h, 64, 2048, 64 * 192, 8) == X.PATH_SHORT
+    assert L.xattn_forward_path(h, 64, 2048, 64 * 192 + 1, 8) == X.PATH_GEMM
+    assert L.xattn_forward_path(h, 64, 0, 100, 4) == 0
+    monkeypatch.setenv("XATTN_SHORT", "0")
+    assert L.xattn_forward_path(h, 17, 64, 100, 4) == X.PATH_GEMM
+    assert L.xattn_forward_launches(h, 17, 64, 100, 4) == 2
+    monkeypatch.setenv("XATTN_SHORT", "1")
+    assert L.xattn_forward_path(h, 8, 2048, 5482, 4) == X.PATH_SHORT
+    assert L.xattn_forward_path(h, 8, 2048, 5482, 2) == X.PATH_SHORT    # d_h = 128
+    assert L.xattn_forward_launches(h, 8, 2048, 5482, 4) == 2
+    monkeypatch.delenv("XATTN_SHORT")
+    L.xattn_destroy(h)
+    st, h = _create(L, 256, 1, X.XATTN_BF16, X.XATTN_KV_SEPARATE)
+    assert L.xattn_forward_path(h, 256, 262144, 256 * 96, 4) == X.PATH_SHORT
+    assert L.xattn_forward_path(h, 256, 262144, 256 * 96 + 1, 4) == X.PATH_GEMM
+    L.xattn_destroy(h)
+    st, h = _create(L, 512, 3, X.XATTN_BF16, X.XATTN_KV_SHARED)     # other widths: never
+    assert L.xattn_forward_path(h, 64, 2048, 64 * 50, 8) == X.PATH_GEMM
+    L.xattn_destroy(h)
+    st, h = _create(L, 256, 3, X.XATTN_FP32, X.XATTN_KV_SHARED)
+    assert L.xattn_forward_path(h, 64, 2048, 64 * 50, 8) == X.PATH_FP32
+    L.xattn_destroy(h)
+
+
 def _fwd(L, h, Z=FAKE, W=FAKE, K=FAKE, V=None, cu_kv=FAKE, cu_c=FAKE, R=2, tc=10, tkv=20,
          heads=4, O=FAKE, ws=FAKE, wsb=1 << 20):
     return L.xattn_forward(h, Z, W, K, V, cu_kv, cu_c, R, tc, tkv, heads, O, ws, wsb, None)
