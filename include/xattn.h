@@ -51,9 +51,10 @@
  *   - Precision: XATTN_BF16 multiplies bf16 operands into fp32 accumulators
  *     on the matrix cores; Q is rounded to bf16 after the projection and once
  *     more after scaling by log2(e)/sqrt(d_h) (the softmax scale folded into
- *     the query operands); the softmax weights are rounded to bf16 for the PV
- *     product; O is rounded to bf16 (nearest-even).  XATTN_FP32 computes in
- *     fp32 throughout.
+ *     the query operands) - except on the short-memory path
+ *     (XATTN_PATH_SHORT), which rounds Q once and scales the fp32 scores; the
+ *     softmax weights are rounded to bf16 for the PV product; O is rounded to
+ *     bf16 (nearest-even).  XATTN_FP32 computes in fp32 throughout.
  *
  * Supported: d_h = d / heads in {32, 64, 128} for bf16 (1..128 for fp32),
  * q in [1, 64], d a multiple of 32 for bf16, R >= 0.
@@ -130,8 +131,9 @@ size_t xattn_workspace_size(const xattn_ctx* ctx, int32_t num_requests,
  *   - one kernel - bf16 batches of at most 16 requests on a model of at most
  *     256 features: the attention kernel plans the batch, projects its own
  *     queries and writes the plan into the workspace;
- *   - the planner, then the short-memory kernel, which projects and attends
- *     in one launch - bf16 batches on a 256-feature model whose memories are
+ *   - one short-memory kernel, which plans the batch (in request order),
+ *     projects and attends in one launch and writes the plan into the
+ *     workspace - bf16 batches on a 256-feature model whose memories are
  *     short on average (total_kv <= 96 * num_requests with separate K and V,
  *     192 * num_requests with K = V; the TransX behaviour memory, TransX
  *     report s.2); any single memory may be longer;
@@ -355,8 +357,8 @@ int64_t xattn_max_tiles(const xattn_ctx* ctx, int32_t num_requests,
                         int32_t total_cand, int32_t heads);
 
 /* Number of kernel launches xattn_forward enqueues for this batch shape (for
- * callers that capture or time it): 1 on XATTN_PATH_SINGLE, 2 on
- * XATTN_PATH_GEMM and XATTN_PATH_SHORT, 3 in fp32 mode.
+ * callers that capture or time it): 1 on XATTN_PATH_SINGLE and
+ * XATTN_PATH_SHORT, 2 on XATTN_PATH_GEMM, 3 in fp32 mode.
  * Returns 0 for invalid arguments or a batch without query rows. */
 int32_t xattn_forward_launches(const xattn_ctx* ctx, int32_t num_requests,
                                int32_t total_cand, int32_t total_kv, int32_t heads);
@@ -367,8 +369,8 @@ typedef enum {
     XATTN_PATH_SINGLE = 1,  /* attention kernel plans and projects (<= 16 requests) */
     XATTN_PATH_GEMM = 2,    /* projection GEMM with the planner, then attention      */
     XATTN_PATH_FP32 = 3,    /* fp32 planner, projection and attention kernels        */
-    XATTN_PATH_SHORT = 4    /* planner, then the short-memory kernel (projection and
-                               attention in one launch)                              */
+    XATTN_PATH_SHORT = 4    /* short-memory kernel: plan, projection and attention in
+                               one launch                                            */
 } xattn_path;
 
 /* The xattn_path of this batch shape, or 0 for invalid arguments or a batch

@@ -242,7 +242,7 @@ int32_t xattn_forward_launches(const xattn_ctx* ctx, int32_t R, int32_t total_ca
         case XATTN_PATH_SINGLE: return 1;
         case XATTN_PATH_GEMM: return 2;
         case XATTN_PATH_FP32: return 3;
-        case XATTN_PATH_SHORT: return 2;
+        case XATTN_PATH_SHORT: return 1;
         default: return 0;
     }
 }
@@ -342,16 +342,13 @@ xattn_status run_forward(Mode mode, xattn_ctx* ctx, const void* Z, const void* W
         a.O = O;
         a.cand_len = cand_len;
         if (mode != Mode::kAttendQ && !cand_len && short_shape(c, R, total_kv, heads)) {
-            // the planner (forward), then projection and attention in one launch
-            if (mode == Mode::kForward) {
-                e = xattn::launch_plan(cu_kv, cu_cand, R, c.n_slots, tm, total_cand, total_kv,
-                                       workspace, max_tiles, nullptr, nullptr, nullptr, nullptr, s,
-                                       /*rank=*/false);
-                if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
-            }
+            // projection and attention in one launch; a forward pass also
+            // plans the batch in that launch (request order) and stores the
+            // plan in the workspace
             a.Z = Z;
             a.Wq = W_Q;
             a.tile_m = tm;
+            a.inplan = mode == Mode::kForward;
             e = xattn::launch_short_bf16(a, short_grid(ctx, max_tiles), s);
             if (e != hipSuccess) return hip_fail(e, "short-memory kernel launch");
             return XATTN_OK;

@@ -2,9 +2,11 @@
 // kernel, bf16 in, fp32 accumulate, bf16 out, for gfx950 matrix cores.
 //
 // It computes what the projection GEMM (gemm_bf16.hip) followed by
-// attn_bf16_kernel computes, with the same roundings:
+// attn_bf16_kernel computes:
 //   Q   = Z W_Q[s]                  (ReST reading note s.3.3.2, Eq. (8)),
-//         rounded to bf16, scaled by log2(e)/sqrt(d_h) and rounded again;
+//         rounded to bf16 once (the softmax scale log2(e)/sqrt(d_h) is
+//         applied to the fp32 scores, in the same FMA that subtracts the
+//         running maximum, instead of to a second bf16 copy of Q);
 //   O_h = softmax(Q_h K_h^T / sqrt(d_h)) V_h
 //         (ReST reading note s.3.3.1 Eq. (7); separate K and V for the
 //         TransX behaviour memory, TransX report s.2)
@@ -39,10 +41,9 @@
 //      attn_bf16_kernel (exp2 domain, maximum set by the first block and
 //      moved only when a lane's weights of a block sum past 2^12), and
 //      O^T += V_h^T . P^T with V^T from LDS transpose reads.
-#include <type_traits>
-
 #include "common.h"
 #include "internal.h"
+#include "plan_device.h"
 
 namespace xattn {
 
@@ -54,6 +55,7 @@ constexpr int NT = 64 * NW;
 constexpr int QR = 64;           // query rows per chunk
 constexpr int LDK = D + 8;       // LDS pitch (elements) of Z, Q, K and V rows: 16-byte rows
 constexpr int MB = 32;           // memory rows per score block
+constexpr int kRing = 256;       // work items held in LDS at a time
 constexpr float kSumCap = 4096.0f;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -75,7 +77,11 @@ struct SCfg {
     static_assert(UNITS % NW == 0, "every wave has the same number of units");
     static constexpr int KV_ELEMS = PLANES * LMAX * LDK;
     static constexpr int ZQ_OFF = KV_ELEMS * 2;        // byte offset of the Z / Q chunk
-    static constexpr int SMEM = ZQ_OFF + QR * LDK * 2;
+    // the plan built in the kernel (exclusive scan of the requests' item
+    // counts) and the ring of this work-group's next work items
+    static constexpr int PLAN_OFF = ZQ_OFF + QR * LDK * 2;
+    static constexpr int RING_OFF = PLAN_OFF + (((kPlanMaxRequests + 1 + 16 + 1) * 4 + 15) & ~15);
+    static constexpr int SMEM = RING_OFF + kRing * 16;
     static constexpr int KV_CPT = LMAX * (D / 8) / NT;  // 16-byte memory chunks per thread per plane
     static constexpr int Z_CPT = QR * (D / 8) / NT;     // 16-byte Z chunks per thread
     static_assert(LMAX * (D / 8) % NT == 0 && QR * (D / 8) % NT == 0, "even staging split");
@@ -104,32 +110,106 @@ __global__ __launch_bounds__(NT) void short_bf16_kernel(AttnArgs a) {
     const bf16* __restrict__ K = static_cast<const bf16*>(a.K);
     const bf16* __restrict__ V = static_cast<const bf16*>(a.V);
     bf16* __restrict__ O = static_cast<bf16*>(a.O);
-    // The plan is read through the constant address space: it does not
-    // change during the launch, so its uniform reads become scalar loads,
-    // which are not queued behind this kernel's vector loads and stores.
-    typedef const __attribute__((address_space(4))) int cint;
-    cint* ws = (cint*)a.ws;   // address-space conversion: a C-style cast
-    cint* items = (cint*)(static_cast<const char*>(a.ws) + kPlanHeaderBytes);   // int4 each
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 5, l32 = lane & 31;
+    const int tile_m = a.tile_m, R = a.R;
+    int* plan_pre = reinterpret_cast<int*>(smem + C::PLAN_OFF);   // [R + 1]
+    int* plan_part = plan_pre + kPlanMaxRequests + 1;              // [16]
+    int* plan_red = plan_part + 16;
+    int4* ring = reinterpret_cast<int4*>(smem + C::RING_OFF);
 
-    // This work-group's items (none if the plan failed validation: T = 0,
-    // or was built for another tile size, i.e. another batch shape).
-    const int T = ws[kPlanTileM] == a.tile_m ? ws[kPlanNTiles] : 0;
+    // ---------------- the work list ----------------
+    // Forward (a.inplan): every work-group plans the batch itself, in request
+    // order (the varlen planner of plan_device.h with rank = false: request r
+    // contributes q * ceil(N_r / tile_m) items {kv0, L, c0, nc | s << 16},
+    // candidate blocks ascending, slots inside a block), after checking the
+    // offsets; work-group 0 writes the plan header and every work-group
+    // publishes its own items, so that later calls can reuse the plan.
+    // Otherwise the plan in the workspace is read (none if it failed
+    // validation, T = 0, or was built for another tile size, i.e. another
+    // batch shape).
+    const int* __restrict__ cu_kv = a.cu_kv;
+    const int* __restrict__ cu_cand = a.cu_cand;
+    int* wsw = static_cast<int*>(a.ws);
+    int4* tiles = reinterpret_cast<int4*>(static_cast<char*>(a.ws) + kPlanHeaderBytes);
+    int T;
+    if (a.inplan) {
+        int err = 0;
+        if (tid == 0) {
+            if (cu_kv[0] != 0 || cu_kv[R] != a.total_kv) err |= kErrCuKv;
+            if (cu_cand[0] != 0 || cu_cand[R] != a.total_cand) err |= kErrCuCand;
+            *plan_red = 0;
+        }
+        for (int r = tid; r < R; r += NT) {
+            if (cu_kv[r + 1] < cu_kv[r]) err |= kErrCuKv;
+            if (cu_cand[r + 1] < cu_cand[r]) err |= kErrCuCand;
+        }
+        __syncthreads();
+        if (err) atomicOr(plan_red, err);
+        __syncthreads();
+        err = *plan_red;
+        T = 0;
+        if (!err) {
+            for (int r = tid; r < R; r += NT) {
+                const int n = cu_cand[r + 1] - cu_cand[r];
+                plan_pre[r] = q * ((n + tile_m - 1) / tile_m);
+            }
+            __syncthreads();
+            T = plan_exclusive_scan<NT>(plan_pre, R, plan_part);
+        }
+        if (blockIdx.x == 0 && tid == 0) {
+            wsw[kPlanNTiles] = T;
+            wsw[kPlanError] = err;
+            wsw[kPlanTileM] = tile_m;
+        }
+    } else {
+        T = wsw[kPlanTileM] == tile_m ? wsw[kPlanNTiles] : 0;
+    }
+    T = __builtin_amdgcn_readfirstlane(T);
     const int G = gridDim.x;
     const int i_end = (int)((int64_t)(blockIdx.x + 1) * T / G);
     int ii = (int)((int64_t)blockIdx.x * T / G);
     if (ii >= i_end) return;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g = lane >> 5, l32 = lane & 31;
+    // items [first, first + kRing) of this work-group's range into the ring
+    int ring_base = ii;
+    auto fill_ring = [&](int first) {
+        __syncthreads();   // no wave reads the ring any more
+        for (int k = tid; k < kRing && first + k < i_end; k += NT) {
+            const int i = first + k;
+            int4 it;
+            if (a.inplan) {
+                int lo = 0, hi = R;   // largest r with pre[r] <= i (skips empty requests)
+                while (hi - lo > 1) {
+                    const int mid = (lo + hi) >> 1;
+                    if (plan_pre[mid] <= i) lo = mid; else hi = mid;
+                }
+                const int local = i - plan_pre[lo], b = local / q, sl = local - b * q;
+                const int c_lo = cu_cand[lo], n = cu_cand[lo + 1] - c_lo;
+                const int kv0 = cu_kv[lo];
+                it = make_int4(kv0, cu_kv[lo + 1] - kv0, c_lo + b * tile_m,
+                               min(tile_m, n - b * tile_m) | (sl << 16));
+                tiles[i] = it;
+            } else {
+                it = tiles[i];
+            }
+            ring[k] = it;
+        }
+        ring_base = first;
+        __syncthreads();
+    };
+    fill_ring(ii);
 
+    // item i (uniform); refills the ring when i has run past it
     auto load_item = [&](int i, Chunk& c) {
-        cint* it = items + 4 * (size_t)i;
-        c.kv0 = __builtin_amdgcn_readfirstlane(it[0]);
-        c.L = __builtin_amdgcn_readfirstlane(it[1]);
-        c.c0 = __builtin_amdgcn_readfirstlane(it[2]);
-        const int iw = __builtin_amdgcn_readfirstlane(it[3]);
+        if (i - ring_base >= kRing) fill_ring(i);
+        const int4 it = ring[i - ring_base];
+        c.kv0 = __builtin_amdgcn_readfirstlane(it.x);
+        c.L = __builtin_amdgcn_readfirstlane(it.y);
+        c.c0 = __builtin_amdgcn_readfirstlane(it.z);
+        const int iw = __builtin_amdgcn_readfirstlane(it.w);
         c.nc = iw & kItemNcMask;
         c.s = iw >> 16;
         c.j = 0;
@@ -262,7 +342,7 @@ __global__ __launch_bounds__(NT) void short_bf16_kernel(AttnArgs a) {
             for (int j4 = 0; j4 < 4; ++j4) {
                 bf16x4 v;
 #pragma unroll
-                for (int t = 0; t < 4; ++t) v[t] = (bf16)((float)(bf16)acc[rb][4 * j4 + t] * scale_log2);
+                for (int t = 0; t < 4; ++t) v[t] = (bf16)acc[rb][4 * j4 + t];
                 *reinterpret_cast<bf16x4*>(qrow + 8 * j4) = v;
             }
         }
@@ -303,11 +383,8 @@ __global__ __launch_bounds__(NT) void short_bf16_kernel(AttnArgs a) {
             bf16x8 kf[C::KST];
 #pragma unroll
             for (int kk = 0; kk < C::KST; ++kk) kf[kk] = *reinterpret_cast<const bf16x8*>(kb + 16 * kk);
-            // scores come out relative to the running maximum (0 before the first block)
-            f32x16 seed;
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr) seed[rr] = started[k] ? -m_run[k] : 0.f;
-            f32x16 sacc = mfma32(kf[0], qb[k][0], seed);
+            // raw scores K_h . Q_h^T (fp32)
+            f32x16 sacc = mfma32(kf[0], qb[k][0], f32x16{});
 #pragma unroll
             for (int kk = 1; kk < C::KST; ++kk) sacc = mfma32(kf[kk], qb[k][kk], sacc);
             bf16x8 vf[2][C::EBW];
@@ -329,16 +406,16 @@ __global__ __launch_bounds__(NT) void short_bf16_kernel(AttnArgs a) {
                     if (j >= jl) sacc[rr] = -INFINITY;
                 }
             }
-            // P^T k-step u16 slot t <-> score register 8*u16 + t
+            // Weights 2^(score * log2(e)/sqrt(d_h) - m) against the running
+            // maximum m (exp2 units).  P^T k-step u16 slot t <-> score
+            // register 8*u16 + t.
             bf16x8 pb[2];
-            auto weights = [&](auto shifted, float shift) {
+            auto weights = [&](float m) {
                 float lt = 0.f;
 #pragma unroll
                 for (int rr = 0; rr < 16; rr += 2) {
-                    float x0 = sacc[rr], x1 = sacc[rr + 1];
-                    if constexpr (decltype(shifted)::value) x0 += shift, x1 += shift;
-                    const float p0 = __builtin_amdgcn_exp2f(x0);
-                    const float p1 = __builtin_amdgcn_exp2f(x1);
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[rr], scale_log2, -m));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[rr + 1], scale_log2, -m));
                     const bf16x2 pp = {(bf16)p0, (bf16)p1};
                     lt = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lt, false);
                     pb[rr >> 3][rr & 7] = pp[0];
@@ -346,20 +423,34 @@ __global__ __launch_bounds__(NT) void short_bf16_kernel(AttnArgs a) {
                 }
                 return lt;
             };
-            float lt = weights(std::false_type{}, 0.f);
-            if (!started[k] || __any(lt > kSumCap)) {
-                const float m_seed = started[k] ? m_run[k] : 0.f;
+            // the block's row maximum in exp2 units (both halves of the wave
+            // agree on it; the scale is positive)
+            auto block_max = [&]() {
                 float mt = fmaxf(sacc[0], sacc[1]);
 #pragma unroll
                 for (int rr = 2; rr < 16; rr += 2) mt = fmaxf(mt, fmaxf(sacc[rr], sacc[rr + 1]));
-                const float m_new = fmaxf(m_run[k], m_seed + fmaxf(mt, xor32(mt)));
-                const float alpha = __builtin_amdgcn_exp2f(m_run[k] - m_new);
-                m_run[k] = m_new;
-                l_run[k] *= alpha;
-#pragma unroll
-                for (int eb = 0; eb < C::EBW; ++eb) oacc[k][eb] *= alpha;
-                lt = weights(std::true_type{}, m_seed - m_new);
+                return fmaxf(mt, xor32(mt)) * scale_log2;
+            };
+            float lt;
+            if (!started[k]) {
+                // a unit's first block sets the running maximum (nothing to
+                // rescale yet)
+                m_run[k] = block_max();
+                lt = weights(m_run[k]);
                 started[k] = true;
+            } else {
+                // the maximum moves only when some weight of the block could
+                // exceed kSumCap
+                lt = weights(m_run[k]);
+                if (__any(lt > kSumCap)) {
+                    const float m_new = fmaxf(m_run[k], block_max());
+                    const float alpha = __builtin_amdgcn_exp2f(m_run[k] - m_new);
+                    m_run[k] = m_new;
+                    l_run[k] *= alpha;
+#pragma unroll
+                    for (int eb = 0; eb < C::EBW; ++eb) oacc[k][eb] *= alpha;
+                    lt = weights(m_new);
+                }
             }
             l_run[k] += lt;
 #pragma unroll

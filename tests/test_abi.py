@@ -91,15 +91,18 @@ def test_workspace_size(L):
     L.xattn_destroy(h)
 
 
-def test_forward_launch_count(L):
-    """One launch for small bf16 batches on narrow models, two otherwise,
-    three in fp32 mode; 0 for invalid shapes or no query rows."""
+def test_forward_launch_count(L, monkeypatch):
+    """One launch for small bf16 batches on narrow models and for batches of
+    short memories, two otherwise, three in fp32 mode; 0 for invalid shapes
+    or no query rows."""
+    monkeypatch.delenv("XATTN_SHORT", raising=False)
     st, h = _create(L, 256, 3, X.XATTN_BF16, X.XATTN_KV_SHARED)
     assert st == 0
     L.xattn_forward_launches.restype = ctypes.c_int32
     assert L.xattn_forward_launches(h, 8, 2048, 5482, 4) == 1
     assert L.xattn_forward_launches(h, 16, 64, 100, 4) == 1
-    assert L.xattn_forward_launches(h, 17, 64, 100, 4) == 2
+    assert L.xattn_forward_launches(h, 17, 64, 100, 4) == 1          # short memories
+    assert L.xattn_forward_launches(h, 17, 64, 17 * 200, 4) == 2
     assert L.xattn_forward_launches(h, 8, 0, 100, 4) == 0
     assert L.xattn_forward_launches(h, 8, 10, 100, 3) == 0
     L.xattn_destroy(h)
@@ -125,13 +128,14 @@ def test_forward_path(L, monkeypatch):
     assert L.xattn_forward_path(h, 64, 2048, 64 * 192, 8) == X.PATH_SHORT
     assert L.xattn_forward_path(h, 64, 2048, 64 * 192 + 1, 8) == X.PATH_GEMM
     assert L.xattn_forward_path(h, 64, 0, 100, 4) == 0
+    assert L.xattn_forward_launches(h, 17, 64, 100, 4) == 1
     monkeypatch.setenv("XATTN_SHORT", "0")
     assert L.xattn_forward_path(h, 17, 64, 100, 4) == X.PATH_GEMM
     assert L.xattn_forward_launches(h, 17, 64, 100, 4) == 2
     monkeypatch.setenv("XATTN_SHORT", "1")
     assert L.xattn_forward_path(h, 8, 2048, 5482, 4) == X.PATH_SHORT
     assert L.xattn_forward_path(h, 8, 2048, 5482, 2) == X.PATH_SHORT    # d_h = 128
-    assert L.xattn_forward_launches(h, 8, 2048, 5482, 4) == 2
+    assert L.xattn_forward_launches(h, 8, 2048, 5482, 4) == 1
     monkeypatch.delenv("XATTN_SHORT")
     L.xattn_destroy(h)
     st, h = _create(L, 256, 1, X.XATTN_BF16, X.XATTN_KV_SEPARATE)
