@@ -104,9 +104,16 @@ Variant choose_variant(const xattn_config& c, int R, int total_cand, int total_k
     }
     const double rows = (double)total_cand * c.n_slots * heads;   // query rows x heads
     const double mean_L = R > 0 ? (double)total_kv / R : 0.0;
+    const double mean_N = R > 0 ? (double)total_cand / R : 0.0;
+    // Measured on MI355X over the benchmark batches and synthetic shapes
+    // (query tiles of 64 x heads from 24 to 16384, mean memory 600 to 16384):
     Variant v{2, 2};
-    if (rows / 128.0 >= 4096.0) v = {4, 1};   // many query tiles already fill the chip
-    else if (rows / 64.0 < 1024.0 && mean_L >= 1024.0) v = {1, 4};   // few tiles, long memory
+    if (rows / 64.0 < 256.0 && mean_L >= 1024.0)
+        v = {1, 4};   // few query tiles, long memories: split the memory
+    else if (rows / 64.0 >= 1024.0 && mean_N >= 128.0)
+        v = {4, 1};   // many full tiles already fill the chip
+    else if (mean_N <= 64.0 && mean_L >= 1024.0 && !fused_shape(c, R))
+        v = {2, 1};   // one 64-candidate tile per request and slot, long memories
     // Take the preferred variant if it leaves room for two work-groups per
     // compute unit, else the first such fallback, else the smallest built one.
     const Variant order[] = {v, {2, 2}, {4, 1}, {1, 4}, {2, 1}};
