@@ -399,7 +399,10 @@ xattn_status xattn_project(xattn_ctx* ctx, const void* Z, const void* W_Q,
  * epilogue; bf16: the gated values are rounded to bf16) writing the last
  * total_cand*q*d elements of `workspace` - the projected-query region of a
  * workspace sized by xattn_workspace_size, so a plan stored there is kept -
- * then the W_o GEMM.  `workspace_bytes` must cover that region.  Errors:
+ * then the W_o GEMM.  In bf16 on a model of d = 256 with at least one unit
+ * of 64 candidates x slot per compute unit it is one launch with the same
+ * arithmetic (bit for bit) that keeps the gated values on chip (the
+ * workspace is then not written).  `workspace_bytes` must cover that region either way.  Errors:
  * XATTN_EINVAL for NULL pointers or a negative count; XATTN_EWORKSPACE for a
  * small workspace; XATTN_EHIP for a launch failure. */
 xattn_status xattn_output(xattn_ctx* ctx, const void* Z, const void* W_go, const void* O,

@@ -852,6 +852,21 @@ xattn_status xattn_output(xattn_ctx* ctx, const void* Z, const void* W_go, const
     DeviceGuard dg(c.device);
     if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
     hipStream_t s = static_cast<hipStream_t>(stream);
+    // bf16 on a 256-feature model with at least one unit of 64 candidates
+    // per compute unit (measured crossover; smaller batches run faster as two
+    // GEMM launches that spread over the chip): one kernel keeps the gated
+    // values on chip.  XATTN_FUSED_OUTPUT=0 / 1 forces either.
+    const int64_t units = (int64_t)c.n_slots * ((total_cand + 63) / 64);
+    const char* fenv = getenv("XATTN_FUSED_OUTPUT");
+    const bool fused = c.dtype == XATTN_BF16 && c.d_model == xattn::kShortD &&
+                       (fenv ? fenv[0] == '1' : units >= short_grid(ctx, INT64_MAX));
+    if (fused) {
+        hipError_t e = xattn::launch_gate_output_fused_bf16(Z, W_go, O, W_o, Y, total_cand,
+                                                            c.n_slots, c.d_model,
+                                                            short_grid(ctx, units), s);
+        if (e != hipSuccess) return hip_fail(e, "output kernel launch");
+        return XATTN_OK;
+    }
     hipError_t e = c.dtype == XATTN_BF16
                        ? xattn::launch_gate_output_bf16(Z, W_go, O, W_o, total_cand, c.n_slots,
                                                         c.d_model, X, Y, s)

@@ -56,6 +56,11 @@ hipError_t launch_attn_bf16(const AttnArgs& a, int rb, int ksplit, hipStream_t s
 constexpr int kShortD = 256;
 constexpr int short_max_rows(bool sep) { return sep ? 96 : 192; }
 hipError_t launch_short_bf16(const AttnArgs& a, int grid, hipStream_t stream);
+// Output gate and W_o in one launch (output_bf16.hip), d = kShortD only;
+// `grid` work-groups (at most one per unit of 64 candidates and slot).
+hipError_t launch_gate_output_fused_bf16(const void* Z, const void* Wgo, const void* O,
+                                         const void* Wo, void* Y, int total_cand, int q, int d,
+                                         int grid, hipStream_t stream);
 
 // bf16 TSP projection Q = Z W_Q[slot] into Qp; when ws is not NULL the same
 // launch also runs the planner into ws (one extra work-group).
