@@ -316,7 +316,12 @@ xattn_status xattn_codec_fold_query_weights(xattn_ctx* ctx, const xattn_codebook
  * reconstruction.  Two launches: the projection GEMM over W_Q_rot (with the
  * planner), then the attention kernel, which reconstructs each memory tile
  * while staging it in LDS (HBM carries codes and norms only), accumulates in
- * the rotated basis and rotates each output row back.  Shared mode: the
+ * the rotated basis and rotates each output row back.  On a 256-feature
+ * model with short memories (the xattn_forward short-path rule, at most 96
+ * rows on average in both modes) they are the planner and the short-memory
+ * kernel, which decodes each request's memory once per work-group (keys in
+ * the rotated basis, values rotated back) and projects and attends as
+ * xattn_forward's short path does.  Shared mode: the
  * memory is both key and value (cb_v, v_codes, v_norms NULL).  Separate mode:
  * cb_v with the same budget_bits as cb_k.  Offsets, shapes, workspace
  * (xattn_workspace_size) and errors as for xattn_forward; XATTN_EUNSUPPORTED

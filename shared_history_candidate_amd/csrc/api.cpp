@@ -769,6 +769,55 @@ xattn_status xattn_forward_codec(xattn_ctx* ctx, const xattn_codebook* cb_k,
         return fail(XATTN_EINVAL, "num_requests=0 with total_cand=%d total_kv=%d", total_cand,
                     total_kv);
     if (R == 0 || total_cand == 0) return XATTN_OK;
+    DeviceGuard dg0(c.device);
+    if (dg0.err != hipSuccess) return hip_fail(dg0.err, "hipSetDevice");
+    // Short memories on a 256-feature model (the TransX memory): the
+    // short-memory kernel decodes each request's memory once per work-group
+    // (keys in the rotated basis, values rotated back) after a planner launch
+    // (request order).  The same rule as the bf16 short path, with at most
+    // 96 rows in both modes (two decoded planes).  XATTN_SHORT overrides.
+    {
+        const int dh = c.d_model / heads;
+        const char* env = getenv("XATTN_SHORT");
+        const bool short_codec =
+            c.d_model == xattn::kShortD && (dh == 32 || dh == 64 || dh == 128) &&
+            (env ? env[0] == '1'
+                 : !fused_shape(c, R) &&
+                       (int64_t)total_kv <= (int64_t)R * xattn::short_max_rows(true));
+        if (short_codec) {
+            const int64_t mt = max_tiles_for(c, R, total_cand, 64);
+            hipStream_t s0 = static_cast<hipStream_t>(stream);
+            hipError_t e0 = xattn::launch_plan(cu_kv, cu_cand, R, c.n_slots, 64, total_cand,
+                                               total_kv, workspace, mt, nullptr, nullptr, nullptr,
+                                               nullptr, s0, /*rank=*/false);
+            if (e0 != hipSuccess) return hip_fail(e0, "plan kernel launch");
+            xattn::AttnArgs aa{};
+            aa.Z = Z;
+            aa.Wq = W_Q_rot;
+            aa.O = O;
+            aa.ws = workspace;
+            aa.cu_kv = cu_kv;
+            aa.cu_cand = cu_cand;
+            aa.max_tiles = mt;
+            aa.R = R;
+            aa.total_cand = total_cand;
+            aa.total_kv = total_kv;
+            aa.q = c.n_slots;
+            aa.d = c.d_model;
+            aa.heads = heads;
+            aa.tile_m = 64;
+            xattn::ShortCodec cd{};
+            cd.kb = a.kb;
+            cd.vb = a.vb;
+            cd.kcodes = k_codes;
+            cd.knorms = k_norms;
+            cd.vcodes = sep ? v_codes : nullptr;
+            cd.vnorms = sep ? v_norms : nullptr;
+            cd.total_kv = total_kv;
+            e0 = xattn::launch_short_codec_bf16(aa, cd, sep, short_grid(ctx, mt), s0);
+            return e0 == hipSuccess ? XATTN_OK : hip_fail(e0, "short-memory codec kernel launch");
+        }
+    }
     // Query waves sharing each reconstructed memory tile (the reconstruction
     // is paid once per tile and work-group): as many as the requests' query
     // rows fill, up to 8 x 32 rows, except that grids of more than 4096

@@ -161,6 +161,20 @@ hipError_t launch_codec_fold(const CodecBook& cb, const void* Wq, int q, int d, 
 // qw query waves (2, 4 or 8) share each reconstructed tile: tile_m = 32 qw.
 hipError_t launch_codec_attn(const CodecArgs& a, bool sep, int qw, int64_t items,
                              hipStream_t stream);
+// Short-memory kernel over a coded memory (short_bf16.hip): memories of up
+// to short_max_rows(true) rows are decoded once per work-group into LDS
+// (keys in the rotated basis, values rotated back); a.Wq is W_Q folded into
+// the keys' basis, the plan comes from the workspace (a.inplan = 0).
+struct ShortCodec {
+    CodecBook kb, vb;            // vb unused when the memory is both K and V
+    const uint32_t* kcodes;      // [heads][total_kv][budget/32]
+    const float* knorms;         // [heads][total_kv]
+    const uint32_t* vcodes;
+    const float* vnorms;
+    int total_kv;
+};
+hipError_t launch_short_codec_bf16(const AttnArgs& a, const ShortCodec& cd, bool sep, int grid,
+                                   hipStream_t stream);
 
 // fp32 path (tile_m = 64): attention over projected queries (cand_len: the
 // per-candidate prefix cutoff, or NULL), projection.

@@ -61,10 +61,13 @@ constexpr float kSumCap = 4096.0f;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-template <int DH, bool SEP>
+template <int DH, bool SEP, bool CODEC>
 struct SCfg {
-    static constexpr int PLANES = SEP ? 2 : 1;
-    static constexpr int LMAX = short_max_rows(SEP);   // memory rows resident at once
+    // a coded memory always stages two planes: keys in the rotated basis,
+    // values rotated back (both decoded from the codes)
+    static constexpr int PLANES = SEP || CODEC ? 2 : 1;
+    static constexpr int LMAX = short_max_rows(SEP || CODEC);   // memory rows resident at once
+    static constexpr int HEADS = D / DH;
     static constexpr int EB = DH / 32;                 // 32-wide feature blocks of a head
     static constexpr int KST = DH / 16;                // k-steps of the score product
     // A unit is (head, 32-row query block, part of the head's output
@@ -78,10 +81,20 @@ struct SCfg {
     static constexpr int KV_ELEMS = PLANES * LMAX * LDK;
     static constexpr int ZQ_OFF = KV_ELEMS * 2;        // byte offset of the Z / Q chunk
     // the plan built in the kernel (exclusive scan of the requests' item
-    // counts) and the ring of this work-group's next work items
+    // counts; not with a coded memory, whose decode tables and code staging
+    // take its place) and the ring of this work-group's next work items
     static constexpr int PLAN_OFF = ZQ_OFF + QR * LDK * 2;
-    static constexpr int RING_OFF = PLAN_OFF + (((kPlanMaxRequests + 1 + 16 + 1) * 4 + 15) & ~15);
-    static constexpr int SMEM = RING_OFF + kRing * 16;
+    static constexpr int PLAN_BYTES = CODEC ? 0 : (((kPlanMaxRequests + 1 + 16 + 1) * 4 + 15) & ~15);
+    static constexpr int RING_OFF = PLAN_OFF + PLAN_BYTES;
+    // coded memory: {bit offset, bits, lo, step} per plane and feature, and
+    // the codes + norm of one 32-row block per (row, head), with a pad word
+    // read by fields that end a row
+    static constexpr int TAB_OFF = RING_OFF + kRing * 16;
+    static constexpr int TAB_BYTES = CODEC ? 2 * D * 16 : 0;
+    static constexpr int RAWP = DH / 4 + 1;            // words per (row, head) at 8 bits per coordinate, + pad
+    static constexpr int RAW_OFF = TAB_OFF + TAB_BYTES;
+    static constexpr int RAW_BYTES = CODEC ? MB * HEADS * (RAWP + 1) * 4 : 0;
+    static constexpr int SMEM = RAW_OFF + RAW_BYTES;
     static constexpr int KV_CPT = LMAX * (D / 8) / NT;  // 16-byte memory chunks per thread per plane
     static constexpr int Z_CPT = QR * (D / 8) / NT;     // 16-byte Z chunks per thread
     static_assert(LMAX * (D / 8) % NT == 0 && QR * (D / 8) % NT == 0, "even staging split");
@@ -94,14 +107,14 @@ struct Chunk {
     int j;                   // chunk index inside the item
 };
 
-template <int DH, bool SEP>
-__global__ __launch_bounds__(NT) void short_bf16_kernel(AttnArgs a) {
-    using C = SCfg<DH, SEP>;
+template <int DH, bool SEP, bool CODEC>
+__global__ __launch_bounds__(NT) void short_bf16_kernel(AttnArgs a, ShortCodec cd) {
+    using C = SCfg<DH, SEP, CODEC>;
     constexpr int LMAX = C::LMAX;
     __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
     bf16* kvs = reinterpret_cast<bf16*>(smem);                 // K rows, then V rows (SEP)
     bf16* zq = reinterpret_cast<bf16*>(smem + C::ZQ_OFF);     // Z, then Q, of one chunk
-    const bf16* vsrc = kvs + (SEP ? LMAX * LDK : 0);
+    const bf16* vsrc = kvs + (SEP || CODEC ? LMAX * LDK : 0);
 
     const int q = a.q;
     const float scale_log2 = a.scale_log2;
@@ -135,7 +148,7 @@ __global__ __launch_bounds__(NT) void short_bf16_kernel(AttnArgs a) {
     int* wsw = static_cast<int*>(a.ws);
     int4* tiles = reinterpret_cast<int4*>(static_cast<char*>(a.ws) + kPlanHeaderBytes);
     int T;
-    if (a.inplan) {
+    if (!CODEC && a.inplan) {
         int err = 0;
         if (tid == 0) {
             if (cu_kv[0] != 0 || cu_kv[R] != a.total_kv) err |= kErrCuKv;
@@ -180,7 +193,7 @@ __global__ __launch_bounds__(NT) void short_bf16_kernel(AttnArgs a) {
         for (int k = tid; k < kRing && first + k < i_end; k += NT) {
             const int i = first + k;
             int4 it;
-            if (a.inplan) {
+            if (!CODEC && a.inplan) {
                 int lo = 0, hi = R;   // largest r with pre[r] <= i (skips empty requests)
                 while (hi - lo > 1) {
                     const int mid = (lo + hi) >> 1;
@@ -247,11 +260,105 @@ __global__ __launch_bounds__(NT) void short_bf16_kernel(AttnArgs a) {
         for (int kk = 0; kk < D / 16; ++kk) wa[kk] = *reinterpret_cast<const bf16x8*>(wr + 16 * kk);
     };
 
+    // Coded memory (TransX report s.3; codec_bf16.hip): per plane (0: keys,
+    // 1: values; with K = V both decode the key codes) and feature h*DH + i,
+    // {bit offset, bits, lo, step} of coordinate i of head h, so that the
+    // rotated coordinate is lo + code * step (the cell centre; lo = centre
+    // and step = 0 for a coordinate without bits).
+    if constexpr (CODEC) {
+        int4* tab = reinterpret_cast<int4*>(smem + C::TAB_OFF);
+        for (int idx = tid; idx < 2 * D; idx += NT) {
+            const int p = idx / D, f = idx - p * D, h = f / DH, i = f - h * DH;
+            const CodecBook& cb = p == 1 && SEP ? cd.vb : cd.kb;
+            int off = 0;
+            for (int j = 0; j < i; ++j) off += min((int)cb.bits[h * DH + j], 8);
+            const int b = min((int)cb.bits[f], 8);
+            const float m = cb.center[f], hr = cb.half[f];
+            const float step = b > 0 ? 2.0f * hr / (float)(1u << b) : 0.f;
+            const float lo = b > 0 ? m - hr + 0.5f * step : m;
+            tab[idx] = make_int4(off, b, __builtin_bit_cast(int, lo), __builtin_bit_cast(int, step));
+        }
+        // visible to the decode behind the first staging barrier
+    }
+
     // Memory rows [row0, row0 + nr) of K (and V) for all heads -> LDS rows
     // 0..LMAX-1; rows past nr read as zeros, so that the V rows behind a
     // partial score block are finite.
     int st_row0 = -1, st_rows = -1;
     auto kv_stage = [&](int row0, int nr) {
+      if constexpr (CODEC) {
+        // Decode 32-row blocks of codes, plane by plane, through LDS: the
+        // key plane keeps the rotated basis (the queries come from W_Q
+        // folded into it); the value plane is rotated back on the matrix
+        // cores, V = norm * E x^, so that the attention needs no output
+        // rotation.  Rows past nr get norm 0, i.e. zero rows.
+        const int W = cd.kb.budget / 32;
+        const int nkv = cd.total_kv;
+        uint32_t* raw = reinterpret_cast<uint32_t*>(smem + C::RAW_OFF);
+        float* rnorm = reinterpret_cast<float*>(raw + MB * C::HEADS * C::RAWP);
+        const int4* tab = reinterpret_cast<const int4*>(smem + C::TAB_OFF);
+        // rotated coordinate f = h*DH + i of row r of the staged block, times its norm
+        auto decode = [&](int pl, int r, int f) {
+            const int h = f / DH;
+            const int4 tb = tab[pl * D + f];
+            const uint32_t* rp = raw + (r * C::HEADS + h) * C::RAWP;
+            const uint32_t v = __builtin_amdgcn_alignbit(rp[(tb.x >> 5) + 1], rp[tb.x >> 5], tb.x & 31) &
+                               ((1u << tb.y) - 1u);
+            return (bf16)(rnorm[r * C::HEADS + h] *
+                          fmaf((float)v, __builtin_bit_cast(float, tb.w), __builtin_bit_cast(float, tb.z)));
+        };
+        for (int pl = 0; pl < 2; ++pl) {
+            const uint32_t* codes = pl == 1 && SEP ? cd.vcodes : cd.kcodes;
+            const float* norms = pl == 1 && SEP ? cd.vnorms : cd.knorms;
+            for (int r0 = 0; r0 < LMAX; r0 += MB) {
+                __syncthreads();   // the previous block's decode is done with the staging area
+                for (int idx = tid; idx < MB * C::HEADS * W; idx += NT) {
+                    const int rh = idx / W, wd = idx - rh * W, r = rh / C::HEADS, h = rh - r * C::HEADS;
+                    raw[rh * C::RAWP + wd] =
+                        r0 + r < nr ? codes[((size_t)h * nkv + row0 + r0 + r) * W + wd] : 0u;
+                }
+                for (int rh = tid; rh < MB * C::HEADS; rh += NT) {
+                    const int r = rh / C::HEADS, h = rh - r * C::HEADS;
+                    raw[rh * C::RAWP + W] = 0u;
+                    rnorm[rh] = r0 + r < nr ? norms[(size_t)h * nkv + row0 + r0 + r] : 0.f;
+                }
+                __syncthreads();
+                if (pl == 0) {
+                    for (int e = tid; e < MB * D; e += NT) {
+                        const int r = e / D, f = e - r * D;
+                        kvs[(r0 + r) * LDK + f] = decode(0, r, f);
+                    }
+                } else {
+                    // wave w: head h, output features 32eb.. of it (heads x DH/32 = 8 pairs):
+                    // C[row][o] = sum_i x^[row][i] E[32eb + o][i] with x^ decoded
+                    // straight into the A operand (rows = lanes' l32)
+                    constexpr int EBH = DH / 32;
+                    const int h = w / EBH, eb = w - h * EBH;
+                    const CodecBook& cb = SEP ? cd.vb : cd.kb;
+                    const float* er = cb.rot + ((size_t)h * DH + 32 * eb + l32) * DH + 8 * g;
+                    f32x16 vacc = f32x16{};
+#pragma unroll
+                    for (int kk = 0; kk < C::KST; ++kk) {
+                        bf16x8 xa, eo;
+#pragma unroll
+                        for (int t = 0; t < 8; ++t) {
+                            xa[t] = decode(1, l32, h * DH + 16 * kk + 8 * g + t);
+                            eo[t] = (bf16)er[16 * kk + t];
+                        }
+                        vacc = mfma32(xa, eo, vacc);
+                    }
+                    // vacc reg rr: row (rr/4)*8 + 4g + rr%4, output feature 32eb + l32
+#pragma unroll
+                    for (int rr = 0; rr < 16; ++rr)
+                        kvs[(LMAX + r0 + (rr >> 2) * 8 + 4 * g + (rr & 3)) * LDK + h * DH + 32 * eb + l32] =
+                            (bf16)vacc[rr];
+                }
+            }
+        }
+        __syncthreads();
+        st_row0 = row0;
+        st_rows = nr;
+      } else {
         const uint32_t bytes = (uint32_t)nr * D * 2;
         const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(K + (size_t)row0 * D), (short)0, bytes, 0x00020000);
@@ -280,6 +387,7 @@ __global__ __launch_bounds__(NT) void short_bf16_kernel(AttnArgs a) {
         }
         st_row0 = row0;
         st_rows = nr;
+      }
     };
 
     // transposed V read: lane l receives V[16u + 4g + t][col + l%32], t = 0..3
@@ -510,17 +618,27 @@ __global__ __launch_bounds__(NT) void short_bf16_kernel(AttnArgs a) {
     }
 }
 
-template <int DH, bool SEP>
-hipError_t launch_t(const AttnArgs& a, int grid, hipStream_t stream) {
+template <int DH, bool SEP, bool CODEC>
+hipError_t launch_t(const AttnArgs& a, const ShortCodec& cd, int grid, hipStream_t stream) {
     AttnArgs k = a;
     k.scale_log2 = 1.4426950408889634f / sqrtf((float)DH);
-    hipLaunchKernelGGL((short_bf16_kernel<DH, SEP>), dim3((unsigned)grid), dim3(NT), 0, stream, k);
+    hipLaunchKernelGGL((short_bf16_kernel<DH, SEP, CODEC>), dim3((unsigned)grid), dim3(NT), 0, stream,
+                       k, cd);
     return hipGetLastError();
 }
 
 template <int DH>
 hipError_t launch_dh(const AttnArgs& a, int grid, hipStream_t stream) {
-    return a.V ? launch_t<DH, true>(a, grid, stream) : launch_t<DH, false>(a, grid, stream);
+    const ShortCodec none{};
+    return a.V ? launch_t<DH, true, false>(a, none, grid, stream)
+               : launch_t<DH, false, false>(a, none, grid, stream);
+}
+
+template <int DH>
+hipError_t launch_dh_codec(const AttnArgs& a, const ShortCodec& cd, bool sep, int grid,
+                           hipStream_t stream) {
+    return sep ? launch_t<DH, true, true>(a, cd, grid, stream)
+               : launch_t<DH, false, true>(a, cd, grid, stream);
 }
 
 }  // namespace
@@ -533,6 +651,20 @@ hipError_t launch_short_bf16(const AttnArgs& a, int grid, hipStream_t stream) {
         case 32: return launch_dh<32>(a, grid, stream);
         case 64: return launch_dh<64>(a, grid, stream);
         case 128: return launch_dh<128>(a, grid, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_short_codec_bf16(const AttnArgs& a, const ShortCodec& cd, bool sep, int grid,
+                                   hipStream_t stream) {
+    if (a.d != kShortD || a.heads < 1 || a.d % a.heads != 0 || !a.Z || !a.Wq || a.inplan ||
+        cd.kb.budget % 32 != 0 || cd.kb.budget <= 0 || (sep && cd.vb.budget != cd.kb.budget))
+        return hipErrorInvalidValue;
+    if (grid <= 0) return hipSuccess;
+    switch (a.d / a.heads) {
+        case 32: return launch_dh_codec<32>(a, cd, sep, grid, stream);
+        case 64: return launch_dh_codec<64>(a, cd, sep, grid, stream);
+        case 128: return launch_dh_codec<128>(a, cd, sep, grid, stream);
         default: return hipErrorInvalidValue;
     }
 }

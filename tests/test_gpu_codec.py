@@ -185,3 +185,61 @@ def test_codec_every_query_wave_count(monkeypatch, qw, dh, heads, mode):
     ref = oracle.forward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, Kd, Vd)
     err, rel = assert_close(got, ref, "bf16", "codec qw=%s dh=%d %s" % (qw, dh, mode))
     print("codec qw=%s dh=%d %s: max-abs %.3e" % (qw, dh, mode, err))
+
+
+SHORT_LENGTHS = [1, 31, 32, 33, 95, 96, 97, 0, 250]
+SHORT_CANDS = [3, 64, 65, 1, 129, 63, 2, 7, 128]
+
+
+def _codec_forward(ctx, wl, t, K, V, cbk, cbv):
+    kc, kn = _gpu_codes(ctx, cbk, K)
+    vc, vn = _gpu_codes(ctx, cbv, V) if V is not None else (None, None)
+    O = ctx.forward_codec(_book(cbk), _book(cbv) if cbv else None, t["Z"],
+                          ctx.codec_fold(_book(cbk), t["W_Q"]), kc, kn, vc, vn, t["cu_kv"],
+                          t["cu_cand"], wl.heads)
+    torch.cuda.synchronize()
+    Kd = OC.decode(kn.cpu().numpy().T.astype(np.float64), _unpacked(kc, cbk), cbk)
+    Vd = (OC.decode(vn.cpu().numpy().T.astype(np.float64), _unpacked(vc, cbv), cbv)
+          if V is not None else None)
+    return O.float().cpu().numpy().astype(np.float64).reshape(-1, wl.d), Kd, Vd
+
+
+@pytest.mark.parametrize("mode", ["shared", "separate"])
+@pytest.mark.parametrize("dh,heads,bpc", [(32, 8, 4), (64, 4, 4.5), (128, 2, 3), (64, 4, 8)])
+def test_codec_short_memory_kernel(monkeypatch, mode, dh, heads, bpc):
+    """The short-memory kernel over a coded memory (d = 256): each request's
+    memory decoded once per work-group, keys in the rotated basis, values
+    rotated back on the matrix cores; memories longer than 96 rows streamed
+    in chunks.  Against the oracle's decode of the GPU's own codes and its
+    forward."""
+    monkeypatch.setenv("XATTN_SHORT", "1")
+    require_gpu()
+    wl, K, V, cbk, cbv = _setup(SHORT_LENGTHS, SHORT_CANDS, dh, heads, mode, bpc, seed=dh + 1)
+    ctx = ctx_for(wl)
+    t = X.to_device(wl)
+    got, Kd, Vd = _codec_forward(ctx, wl, t, K, V, cbk, cbv)
+    ref = oracle.forward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, Kd, Vd)
+    err, rel = assert_close(got, ref, "bf16", "codec short %s dh=%d bpc=%g" % (mode, dh, bpc))
+    print("codec short %s dh=%d bpc=%g: max-abs %.3e normwise %.3e" % (mode, dh, bpc, err, rel))
+    for r in range(wl.R):
+        if wl.lengths[r] == 0:
+            a, b = wl.cu_cand[r] * wl.q, wl.cu_cand[r + 1] * wl.q
+            assert np.all(got[a:b] == 0.0)
+
+
+def test_codec_short_memory_transx_batch():
+    """The whole TransX-like batch at 4.5 bits per coordinate takes the
+    short-memory kernel by default; sampled rows against the oracle."""
+    require_gpu()
+    full = W.make("transx", 0)
+    wl = W.custom("transx_codec", full.lengths, full.cands, q=1, d=full.d, heads=full.heads,
+                  dtype="bf16", kv_mode="separate", seed=5)
+    K, V = W.anisotropic_memory(wl, 6)
+    cbk, cbv = OC.fit(K, wl.heads, 288), OC.fit(V, wl.heads, 288)
+    ctx = ctx_for(wl)
+    t = X.to_device(wl)
+    got, Kd, Vd = _codec_forward(ctx, wl, t, K, V, cbk, cbv)
+    rows = np.sort(np.random.default_rng(2).choice(wl.rows, 1500, replace=False))
+    ref = oracle.forward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, Kd, Vd, rows=rows)
+    err, rel = assert_close(got[rows], ref, "bf16", "codec transx batch")
+    print("codec transx batch: max-abs %.3e normwise %.3e" % (err, rel))
