@@ -27,11 +27,12 @@
 // through double-buffered LDS (one buffer is both K and V in projection-free
 // mode) and V^T operands come from LDS transpose reads.
 //
-// Softmax: exp2 of log2(e)/sqrt(d_h)-scaled scores against a running maximum
-// that is set by the first tile and afterwards moved (with a rescale of the
-// accumulators) only when a lane's weights of a tile sum to more than 2^12.
-// Weights up to that bound are held by fp32 sums and bf16 operands exactly as
-// well as weights <= 1, and no per-tile maximum has to be computed.  Row sums
+// Softmax: exp2 of log2(e)/sqrt(d_h)-scaled scores against a reference that
+// the first tile of each memory split sets (its maximum) and that stays fixed:
+// later weights may exceed 1, which fp32 sums and bf16 operands hold as
+// exactly as weights <= 1, so the memory loop needs neither a per-tile
+// maximum nor a conditional rescale of the accumulators.  A split whose tile
+// weights would pass 2^50 is recomputed with a moving maximum.  Row sums
 // accumulate the bf16-rounded weights that enter the PV product (v_dot2).
 #include <type_traits>
 
@@ -44,7 +45,10 @@ namespace xattn {
 namespace {
 
 constexpr int BN = 64;               // memory rows per tile
-constexpr float kSumCap = 4096.0f;   // largest accepted per-lane weight sum of one tile
+constexpr float kSumCap = 4096.0f;   // largest accepted per-lane weight sum of one tile (moving maximum)
+// Largest per-lane tile weight sum the fixed reference accepts: sums over
+// 2^31 memory rows and their products with values below 2^47 stay finite.
+constexpr float kWeightCap = 1.125899906842624e15f;   // 2^50
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -90,14 +94,23 @@ struct Cfg {
     static constexpr int KV_CHUNKS = BN * DH / 8;                 // 16-byte chunks per plane
     static constexpr int KV_CPT = KV_CHUNKS / (64 * RB);
     static_assert(KV_CHUNKS % (64 * RB) == 0, "memory tile must split evenly over a split group");
-    // Register stages of the memory prefetch: up to 8 x 16 bytes per thread
-    // in flight (32 VGPRs), at most 4 tiles ahead of the LDS stage.
+    // Register stages of the memory prefetch (tiles ahead of the LDS stage).
+    // d_h = 32 tiles are computed quickly, so their loads get the longer
+    // lead: up to 8 x 16 bytes per thread in flight (32 VGPRs), at most 4
+    // tiles ahead.  Wider heads take one stage: a second one costs a wave
+    // per SIMD and measured slower.
     static constexpr int STAGE_REGS = KV_CPT * PLANES;
-    static constexpr int P = STAGE_REGS >= 8 ? 1 : (8 / STAGE_REGS >= 4 ? 4 : 8 / STAGE_REGS);
+    static constexpr int P = DH > 32 || STAGE_REGS >= 8 ? 1 : (8 / STAGE_REGS >= 4 ? 4 : 8 / STAGE_REGS);
+    // Waves per SIMD the register allocation must leave room for: as many as
+    // the LDS footprint admits, up to three (168 VGPRs per wave) with one
+    // register stage, two with deeper ones.
+    static constexpr int LDS_WAVES = (163840 / SMEM) * NW;   // per compute unit
+    static constexpr int WPE = LDS_WAVES >= 12 && P == 1 ? 3 : (LDS_WAVES >= 8 ? 2 : 1);
 };
 
 template <int DH, int RB, int KSPLIT, bool SEP, bool PROJ, bool CUT>
-__global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
+    amdgpu_waves_per_eu(Cfg<DH, RB, KSPLIT, SEP, PROJ, CUT>::WPE))) void attn_bf16_kernel(AttnArgs a) {
     using C = Cfg<DH, RB, KSPLIT, SEP, PROJ, CUT>;
     constexpr int P = C::P;
     __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
@@ -335,16 +348,22 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(AttnArgs a)
     __syncthreads();
 
     // ---------------- 2. stream this split's memory tiles ----------------
+    // Softmax reference.  Every score product is seeded with -m_seed, so the
+    // products deliver s*log2(e)/sqrt(d_h) - m_seed and the weights are a bare
+    // exp2.  The first pass fixes m_seed at the maximum of the split's first
+    // tile and never moves it: later weights may exceed 1, which fp32 sums
+    // and bf16 operands hold exactly as well up to kWeightCap, and the final
+    // normalisation divides the common factor out.  The memory loop then
+    // carries no conditional update of the accumulators.  If some lane's
+    // tile weights summed to more than kWeightCap, the work-group repeats the
+    // split with a moving maximum (second pass, below).
     f32x16 oacc[C::EB];
 #pragma unroll
     for (int eb = 0; eb < C::EB; ++eb) oacc[eb] = f32x16{};
-    float m_run = -INFINITY;   // running max, exp2 domain (identical in both halves)
+    float m_run = -INFINITY;   // what the weights are relative to (-inf: no visible row)
     float l_run = 0.f;         // this half's share of the row sum
-    bool started = false;      // m_run holds a tile maximum (wave-uniform)
-    // Seed of every score accumulator: -m_run once started (0 before), so the
-    // products deliver s*log2(e)/sqrt(d_h) - m_run and the weights are a bare
-    // exp2.  All 16 registers of a lane belong to its query row.
-    f32x16 negm = f32x16{};
+    float m_seed = 0.f;
+    f32x16 negm = f32x16{};    // -m_seed in every register (all 16 belong to the lane's query row)
 
     // transposed V read: lane l receives V[16u + 4g + t][eb*32 + l%32], t = 0..3
     const int G = lane >> 4, k16 = lane & 15;
@@ -352,13 +371,14 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(AttnArgs a)
     const int tr_col = 16 * (G & 1) + 4 * (k16 & 3);
     const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 
-    // One memory tile (t, staged in LDS buffer buf) against this wave's queries.
-    auto tile_step = [&](int t, int buf) {
+    // Scores of the tile in LDS buffer buf against this wave's queries:
+    // sacc[0] keys 0..31, sacc[1] keys 32..63.  All K fragments are read
+    // before the first product so that the LDS latency is paid once per tile.
+    f32x16 sacc[2];
+    bf16x8 vf[4][C::EB];
+    auto scores = [&](int buf) {
         const bf16* kb = kvl + buf * C::PLANES * C::TILE;
         const bf16* vb = kb + (C::PLANES - 1) * C::TILE;
-        // scores: sacc[0] keys 0..31, sacc[1] keys 32..63 of the tile.
-        // All K fragments are read before the first product so that the
-        // LDS latency is paid once per tile.
         bf16x8 kf[2][C::KST];
 #pragma unroll
         for (int k = 0; k < C::KST; ++k) {
@@ -370,7 +390,6 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(AttnArgs a)
                                 *reinterpret_cast<const bf16x4*>(row + 4));
             }
         }
-        f32x16 sacc[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) sacc[hh] = mfma32(kf[hh][0], qb[0], negm);
 #pragma unroll
@@ -382,7 +401,6 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(AttnArgs a)
         __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::KST, 0);
         // V^T fragments for the output product, issued now so that they
         // arrive while the weights are being computed
-        bf16x8 vf[4][C::EB];
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -390,108 +408,191 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) void attn_bf16_kernel(AttnArgs a)
                 const bf16* base = vb + (16 * u + tr_row) * C::LDK + eb * 32 + tr_col;
                 vf[u][eb] = cat(lds_read_tr16(base), lds_read_tr16(base + 8 * C::LDK));
             }
-        // Only the request's last tile is partial (with cutoffs: tiles past
-        // the wave's smallest cutoff).  The opaque copy keeps the compiler
-        // from folding the tile-level test into the per-score tests (which
-        // would then run on every tile).
-        const int jleft = (CUT ? cut : L) - t * BN;   // this lane's visible rows in the tile
+    };
+    // Only the request's last tile is partial (with cutoffs: tiles past the
+    // wave's smallest cutoff).  The opaque copy keeps the compiler from
+    // folding the tile-level test into the per-score tests.
+    auto full_tile = [&](int t) {
         int jl = (CUT ? wmin : L) - t * BN;
         asm volatile("" : "+s"(jl));
-        if (jl < BN) {
+        return jl >= BN;
+    };
+    // Rows past the lane's visible ones take score -inf.  Register rr of
+    // sacc[hh] holds tile row hh*32 + (rr/4)*8 + 4g + rr%4: the test compares
+    // the constant part with the lane's limit (no per-register row index is
+    // kept across tiles).
+    auto mask = [&](int t) {
+        const int lim = (CUT ? cut : L) - t * BN - 4 * g;   // visible rows in the tile, minus 4g
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-                for (int rr = 0; rr < 16; ++rr) {
-                    const int j = hh * 32 + (rr >> 2) * 8 + 4 * g + (rr & 3);
-                    if (j >= jleft) sacc[hh][rr] = -INFINITY;
-                }
-        }
-        // Weights 2^(score - m_run + shift), summed per lane over the bf16
-        // values that enter the PV product.
-        bf16x8 pb[4];
-        auto weights = [&](auto shifted, float shift) {
-            float lt = 0.f;
+            for (int rr = 0; rr < 16; ++rr)
+                if (hh * 32 + (rr >> 2) * 8 + (rr & 3) >= lim) sacc[hh][rr] = -INFINITY;
+    };
+    // Weights 2^(score - m_seed + shift), summed per lane over the bf16
+    // values that enter the PV product (two chains).
+    bf16x8 pb[4];
+    auto weights = [&](auto shifted, float shift) {
+        float lt[2] = {0.f, 0.f};
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-                for (int rr = 0; rr < 16; rr += 2) {
-                    float x0 = sacc[hh][rr], x1 = sacc[hh][rr + 1];
-                    if constexpr (decltype(shifted)::value) x0 += shift, x1 += shift;
-                    const float p0 = __builtin_amdgcn_exp2f(x0);
-                    const float p1 = __builtin_amdgcn_exp2f(x1);
-                    const bf16x2 pp = {(bf16)p0, (bf16)p1};
-                    lt = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lt, false);
-                    pb[hh * 2 + (rr >> 3)][rr & 7] = pp[0];
-                    pb[hh * 2 + (rr >> 3)][(rr & 7) + 1] = pp[1];
-                }
-            return lt;
-        };
-        float lt = weights(std::false_type{}, 0.f);
-        // The running maximum is moved only when it has to be: before the
-        // first tile, or when some weight of this tile could exceed
-        // kSumCap (a lane's sum of its 32 non-negative weights bounds each of
-        // them).  Weights up to kSumCap are as exact in the fp32 sums and as
-        // well represented as bf16 operands as weights <= 1, and the final
-        // normalisation divides the common factor out.
-        // With cutoffs a lane may leave the first tile with maximum -inf
-        // (no visible row); its weights then stay zero: its visible rows
-        // are a prefix of the memory, so a split whose first tile shows it
-        // nothing shows it nothing later either.
-        if (!started || __any(lt > kSumCap)) {
-            // what the scores are relative to (with cutoffs a lane may have
-            // seen no visible row yet: its maximum is still -inf, its seed 0)
-            const float m_seed = CUT ? (m_run == -INFINITY ? 0.f : m_run) : (started ? m_run : 0.f);
-            float mt = fmaxf(sacc[0][0], sacc[0][1]);
-#pragma unroll
-            for (int rr = 2; rr < 16; rr += 2) mt = fmaxf(mt, fmaxf(sacc[0][rr], sacc[0][rr + 1]));
-#pragma unroll
-            for (int rr = 0; rr < 16; rr += 2) mt = fmaxf(mt, fmaxf(sacc[1][rr], sacc[1][rr + 1]));
-            const float m_new = fmaxf(m_run, m_seed + fmaxf(mt, xor32(mt)));
-            // a lane without a visible row so far keeps m = -inf and zero weights
-            const bool none = CUT && m_new == -INFINITY;
-            const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
-            l_run *= alpha;
-#pragma unroll
-            for (int eb = 0; eb < C::EB; ++eb) oacc[eb] *= alpha;
-            lt = weights(std::true_type{}, none ? -INFINITY : m_seed - m_new);
-            started = true;
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr) negm[rr] = none ? 0.f : -m_new;
-        }
-        l_run += lt;
-        // O^T += V^T P^T over the four 16-key slabs of the tile
+            for (int rr = 0; rr < 16; rr += 2) {
+                float x0 = sacc[hh][rr], x1 = sacc[hh][rr + 1];
+                if constexpr (decltype(shifted)::value) x0 += shift, x1 += shift;
+                const float p0 = __builtin_amdgcn_exp2f(x0);
+                const float p1 = __builtin_amdgcn_exp2f(x1);
+                const bf16x2 pp = {(bf16)p0, (bf16)p1};
+                lt[hh] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lt[hh], false);
+                pb[hh * 2 + (rr >> 3)][rr & 7] = pp[0];
+                pb[hh * 2 + (rr >> 3)][(rr & 7) + 1] = pp[1];
+            }
+        return lt[0] + lt[1];
+    };
+    // O^T += V^T P^T over the four 16-key slabs of the tile
+    auto values = [&]() {
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
             for (int eb = 0; eb < C::EB; ++eb) oacc[eb] = mfma32(vf[u][eb], pb[u], oacc[eb]);
     };
+    // lane maximum of the (masked) scores of the tile
+    auto tile_max = [&]() {
+        float mt = fmaxf(sacc[0][0], sacc[0][1]);
+#pragma unroll
+        for (int rr = 2; rr < 16; rr += 2) mt = fmaxf(mt, fmaxf(sacc[0][rr], sacc[0][rr + 1]));
+#pragma unroll
+        for (int rr = 0; rr < 16; rr += 2) mt = fmaxf(mt, fmaxf(sacc[1][rr], sacc[1][rr + 1]));
+        return fmaxf(mt, xor32(mt));   // both halves' keys
+    };
 
     // Iteration it computes this split's tile ksg + it*KSPLIT from LDS buffer
-    // it&1, then moves the next tile from register stage (it+1)%P into the
-    // other buffer and refills that stage with the tile P iterations ahead.
-    // The refill is issued on every path (past the end it moves no bytes), so
-    // the loads in flight are always the same stages in the same order and
-    // the compiler's wait before each LDS store covers only the stage stored.
-    auto step = [&](int it, int j) {
-        const int t = ksg + it * KSPLIT;
-        if (t < ntiles_kv) tile_step(t, it & 1);
+    // it&1, then (advance) moves the next tile from register stage (it+1)%P
+    // into the other buffer and refills that stage with the tile P iterations
+    // ahead.  The refill is issued on every path (past the end it moves no
+    // bytes), so the loads in flight are always the same stages in the same
+    // order and the compiler's wait before each LDS store covers only the
+    // stage stored.
+    auto advance = [&](int it, int j) {
         const int jn = (j + 1) % P;
         if (it + 1 < n_iter) lstore((it + 1) & 1, kreg[jn], vreg[jn]);
         gload(ksg + (it + 1 + P) * KSPLIT, kreg[jn], vreg[jn]);
         if constexpr (!C::PRIVATE) __syncthreads();
     };
-    // Whole groups of P iterations in a loop whose body has no early exit (the
-    // register stage of every step is static), then the remaining < P
-    // iterations once each.
-    int it0 = 0;
-    for (; it0 + P <= n_iter; it0 += P) {
+    // Leading iterations whose tile is full: a loop whose body has no branch.
+    const int n_fast = [&] {
+        const int full = (CUT ? wmin : L) / BN;   // tiles 0 .. full-1 need no mask
+        return full > ksg ? (full - ksg + KSPLIT - 1) / KSPLIT : 0;
+    }();
+
+    // ---- first pass: fixed reference ----
+    float l_peak = 0.f;   // largest tile weight sum of the lane
+    {
+        // iteration 0: the split's first tile sets the reference
+        int it0 = 0;
+        if (n_iter > 0) {
+            scores(0);
+            if (!full_tile(ksg)) mask(ksg);
+            m_run = tile_max();   // -inf for a lane that sees no row of the split
+            m_seed = m_run == -INFINITY ? 0.f : m_run;
 #pragma unroll
-        for (int j = 0; j < P; ++j) step(it0 + j, j);
+            for (int rr = 0; rr < 16; ++rr) negm[rr] = -m_seed;
+            const float lt = weights(std::true_type{}, -m_seed);
+            l_peak = lt;
+            l_run = lt;
+            values();
+            advance(0, 0);
+            it0 = 1;
+        }
+        auto fast = [&](int it) {
+            scores(it & 1);
+            const float lt = weights(std::false_type{}, 0.f);
+            l_peak = fmaxf(l_peak, lt);
+            l_run += lt;
+            values();
+        };
+        auto masked = [&](int it) {
+            const int t = ksg + it * KSPLIT;
+            scores(it & 1);
+            if (!full_tile(t)) mask(t);   // (a split past its last tile: wholly masked)
+            const float lt = weights(std::false_type{}, 0.f);
+            l_peak = fmaxf(l_peak, lt);
+            l_run += lt;
+            values();
+        };
+        // Whole groups of P iterations while they end at or before n_end; the
+        // register stage of every step is static (the groups start at 1, so
+        // group member j is iteration it with it % P = (j + 1) % P).  Then the
+        // remaining < P iterations once each.
+        auto groups = [&](int& i0, int n_end, auto&& body) {
+            for (; i0 + P <= n_end; i0 += P) {
+#pragma unroll
+                for (int j = 0; j < P; ++j) {
+                    body(i0 + j);
+                    advance(i0 + j, (j + 1) % P);
+                }
+            }
+        };
+        groups(it0, n_fast, fast);
+        groups(it0, n_iter, masked);
+#pragma unroll
+        for (int j = 0; j < P - 1; ++j)
+            if (it0 + j < n_iter) {
+                masked(it0 + j);
+                advance(it0 + j, (j + 1) % P);
+            }
     }
+
+    // ---- second pass, only if the first one saw weights past kWeightCap ----
+    // The running maximum then moves with the tiles: it is set by the first
+    // tile and afterwards moved (with a rescale of the accumulators) only
+    // when some weight of a tile could exceed kSumCap (a lane's sum of its 32
+    // non-negative weights bounds each of them).  With cutoffs a lane may
+    // leave the first tile with maximum -inf (no visible row); its weights
+    // then stay zero: its visible rows are a prefix of the memory, so a split
+    // whose first tile shows it nothing shows it nothing later either.
+    if (__syncthreads_or(l_peak > kWeightCap)) {
+        // (rare: a plain loop, one tile at a time through LDS buffer 0)
 #pragma unroll
-    for (int j = 0; j < P - 1; ++j)
-        if (it0 + j < n_iter) step(it0 + j, j);
+        for (int eb = 0; eb < C::EB; ++eb) oacc[eb] = f32x16{};
+        m_run = -INFINITY;
+        l_run = 0.f;
+        negm = f32x16{};
+        bool started = false;   // m_run holds a tile maximum (wave-uniform)
+#pragma unroll 1
+        for (int it = 0; it < n_iter; ++it) {
+            const int t = ksg + it * KSPLIT;
+            gload(t, kreg[0], vreg[0]);
+            lstore(0, kreg[0], vreg[0]);
+            __syncthreads();
+            if (t < ntiles_kv) {
+                scores(0);
+                if (!full_tile(t)) mask(t);
+                float lt = weights(std::false_type{}, 0.f);
+                if (!started || __any(lt > kSumCap)) {
+                    // what the scores are relative to (with cutoffs a lane
+                    // may have seen no visible row yet: its maximum is still
+                    // -inf, its seed 0)
+                    const float m_base = m_run == -INFINITY ? 0.f : m_run;
+                    const float m_new = fmaxf(m_run, m_base + tile_max());
+                    // a lane without a visible row so far keeps m = -inf and zero weights
+                    const bool none = CUT && m_new == -INFINITY;
+                    const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+                    m_run = m_new;
+                    l_run *= alpha;
+#pragma unroll
+                    for (int eb = 0; eb < C::EB; ++eb) oacc[eb] *= alpha;
+                    lt = weights(std::true_type{}, none ? -INFINITY : m_base - m_new);
+                    started = true;
+#pragma unroll
+                    for (int rr = 0; rr < 16; ++rr) negm[rr] = none ? 0.f : -m_new;
+                }
+                l_run += lt;
+                values();
+            }
+            __syncthreads();   // buffer 0 is read by every wave before it is refilled
+        }
+    }
     if constexpr (C::PRIVATE) __syncthreads();   // the merge below reuses the tile buffers
 
     // ---------------- 3. merge the memory splits, normalise, store ----------------

@@ -358,3 +358,43 @@ def test_full_eq7(name):
     ref = oracle.output(wl.Z, wgo, _oracle(wl), wo, wl.q)
     err, rel = assert_close(got, ref, wl.dtype, "eq7 " + name)
     print("full Eq. (7) %s: max-abs %.3e normwise %.3e" % (name, err, rel))
+
+
+# ---------------------------------------------------------------------------
+# Softmax reference: later memory tiles far above a split's first tile
+# ---------------------------------------------------------------------------
+def _rising_memory(mode, seed):
+    """Every query's scores against the memory rows past a request's first tile
+    exceed its scores against the first tile by about 170 in log2 units, so
+    their weights relative to the first tile's maximum overflow fp32: the
+    kernel has to take its moving-maximum pass.  All later rows are the same
+    key (the reference is the mean of their values, well conditioned); every
+    query has a large component along that key's direction."""
+    rng = np.random.default_rng(seed)
+    lengths, cands = [64 * 3 + 17, 64 * 6, 200, 40, 130], [70, 5, 33, 9, 64]
+    wl = W.custom("rising_" + mode, lengths, cands, q=1, d=256, heads=4, dtype="bf16",
+                  kv_mode=mode, seed=seed)
+    dh = wl.d // wl.heads
+    z0 = 3.0 * rng.standard_normal(wl.d)
+    wl.Z = W.round_bf16(z0[None, None, :] + 0.3 * rng.standard_normal(wl.Z.shape))
+    w = z0 @ wl.wt[0].T                       # the common query direction
+    K = np.empty_like(wl.K)
+    for h in range(wl.heads):
+        u = w[h * dh:(h + 1) * dh]
+        K[:, h * dh:(h + 1) * dh] = 20.0 * u / np.linalg.norm(u)
+    for r in range(wl.R):
+        a = int(wl.cu_kv[r])
+        K[a:a + 64] *= -1.0                   # the first tile points the other way
+    wl.K = W.round_bf16(K)
+    return wl
+
+
+@pytest.mark.parametrize("variant", ["default", "2,2", "4,1", "2,1", "1,4"])
+@pytest.mark.parametrize("mode", ["shared", "separate"])
+def test_later_tiles_far_above_the_first(monkeypatch, mode, variant):
+    monkeypatch.setenv("XATTN_SHORT", "0")
+    if variant != "default":
+        monkeypatch.setenv("XATTN_VARIANT", variant)
+    require_gpu()
+    wl = _rising_memory(mode, 31)
+    _check(wl, what="rising memory %s variant %s" % (mode, variant))

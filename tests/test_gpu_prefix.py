@@ -150,3 +150,18 @@ def test_attend_q_prefix_matches_forward_prefix(name):
     b = ctx.attend_q(Q, t["K"], t["V"], t["cu_kv"], t["cu_cand"], wl.heads, ws, cand_kv_len=cl)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("mode", ["shared", "separate"])
+def test_prefix_later_tiles_far_above_the_first(monkeypatch, mode):
+    """Cutoffs on a memory whose later tiles score about 2^170 above the first
+    (the moving-maximum pass, with lanes that see only the first tile, part
+    of it or nothing)."""
+    from test_gpu_parity import _rising_memory
+    monkeypatch.setenv("XATTN_SHORT", "0")
+    wl = _rising_memory(mode, 37)
+    rng = np.random.default_rng(5)
+    kv_len = np.concatenate([rng.integers(-3, int(wl.lengths[r]) + 4, int(wl.cu_cand[r + 1] - wl.cu_cand[r]))
+                             for r in range(wl.R)]).astype(np.int32)
+    kv_len[:4] = [0, 17, 64, 65]
+    _check(wl, kv_len, what="prefix rising memory %s" % mode)
