@@ -311,12 +311,25 @@ xattn_status xattn_codec_fold_query_weights(xattn_ctx* ctx, const xattn_codebook
                                             int32_t heads, const void* W_Q, void* W_Q_rot,
                                             void* stream);
 
+/* Bytes of device workspace xattn_forward_codec needs to decode the memory
+ * once per call: xattn_workspace_size() plus one (shared mode) or two
+ * (separate mode) bf16 planes of total_kv x d (0 on invalid arguments). */
+size_t xattn_codec_workspace_size(const xattn_ctx* ctx, int32_t num_requests,
+                                  int32_t total_cand, int32_t total_kv, int32_t heads);
+
 /* xattn_forward over a coded memory: O[row, head h] = softmax(q_h k_h^T /
  * sqrt(d_h)) v_h with every k, v the decoded vector norm * rotation *
- * reconstruction.  Two launches: the projection GEMM over W_Q_rot (with the
- * planner), then the attention kernel, which reconstructs each memory tile
- * while staging it in LDS (HBM carries codes and norms only), accumulates in
- * the rotated basis and rotates each output row back.  On a 256-feature
+ * reconstruction.  With a workspace of xattn_codec_workspace_size() bytes
+ * (and not the short path below): the memory is decoded once into bf16
+ * planes in the workspace and xattn_forward's kernels run over them with
+ * the queries projected over W_Q_rot.  Separate mode: keys in the rotated
+ * basis, values rotated back.  Shared mode: one plane in the rotated basis
+ * serves as key and value, and a last launch rotates the output rows back
+ * (one more bf16 rounding of O).  With a workspace of only
+ * xattn_workspace_size() bytes: two launches, the projection GEMM over
+ * W_Q_rot (with the planner), then the attention kernel, which reconstructs
+ * each memory tile while staging it in LDS (HBM carries codes and norms
+ * only), accumulates in the rotated basis and rotates each output row back.  On a 256-feature
  * model with short memories (the xattn_forward short-path rule, at most 96
  * rows on average in both modes) they are the planner and the short-memory
  * kernel, which decodes each request's memory once per work-group (keys in

@@ -159,6 +159,22 @@ size_t workspace_bytes(const xattn_config& c, int R, int total_cand) {
     return q_offset(c, R, total_cand) + (size_t)total_cand * c.n_slots * c.d_model * elem_bytes(c);
 }
 
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Coded-memory workspace: the forward's, then (256-byte aligned) the decoded
+// planes, [total_kv][d] bf16 each: one in shared mode, key and value in
+// separate mode.
+size_t codec_plane_offset(const xattn_config& c, int R, int total_cand) {
+    return align256(workspace_bytes(c, R, total_cand));
+}
+size_t codec_plane_bytes(const xattn_config& c, int total_kv) {
+    return align256((size_t)total_kv * c.d_model * 2);
+}
+size_t codec_workspace_bytes(const xattn_config& c, int R, int total_cand, int total_kv) {
+    const int planes = c.kv_mode == XATTN_KV_SEPARATE ? 2 : 1;
+    return codec_plane_offset(c, R, total_cand) + planes * codec_plane_bytes(c, total_kv);
+}
+
 struct DeviceGuard {
     int prev = -1;
     hipError_t err = hipSuccess;
@@ -257,6 +273,12 @@ int32_t xattn_forward_launches(const xattn_ctx* ctx, int32_t R, int32_t total_ca
 size_t xattn_workspace_size(const xattn_ctx* ctx, int32_t R, int32_t total_cand, int32_t heads) {
     if (!ctx || R < 0 || total_cand < 0 || heads < 1) return 0;
     return workspace_bytes(ctx->cfg, R, total_cand);
+}
+
+size_t xattn_codec_workspace_size(const xattn_ctx* ctx, int32_t R, int32_t total_cand,
+                                  int32_t total_kv, int32_t heads) {
+    if (!ctx || R < 0 || total_cand < 0 || total_kv < 0 || heads < 1) return 0;
+    return codec_workspace_bytes(ctx->cfg, R, total_cand, total_kv);
 }
 
 xattn_status xattn_plan(xattn_ctx* ctx, const int32_t* cu_kv, const int32_t* cu_cand, int32_t R,
@@ -816,6 +838,42 @@ xattn_status xattn_forward_codec(xattn_ctx* ctx, const xattn_codebook* cb_k,
             cd.total_kv = total_kv;
             e0 = xattn::launch_short_codec_bf16(aa, cd, sep, short_grid(ctx, mt), s0);
             return e0 == hipSuccess ? XATTN_OK : hip_fail(e0, "short-memory codec kernel launch");
+        }
+    }
+    // Memories that many query tiles read: when the caller's workspace holds
+    // the decoded planes (xattn_codec_workspace_size), the memory is decoded
+    // once per call and the plain forward runs over it, its queries projected
+    // over W_Q_rot.  Separate mode: keys in the rotated basis, values rotated
+    // back.  Shared mode: one plane in the rotated basis serves as key and
+    // value, and the output rows are rotated back afterwards.
+    // XATTN_CODEC_DECODE=0 keeps the per-tile reconstruction below.
+    {
+        const char* env = getenv("XATTN_CODEC_DECODE");
+        const bool decode = (env ? env[0] != '0' : true) &&
+                            workspace_bytes_ >= codec_workspace_bytes(c, R, total_cand, total_kv);
+        if (decode) {
+            char* planes = static_cast<char*>(workspace) + codec_plane_offset(c, R, total_cand);
+            xattn::CodecDecodeArgs da{};
+            da.kb = a.kb;
+            da.vb = a.vb;
+            da.kcodes = k_codes;
+            da.knorms = k_norms;
+            da.vcodes = sep ? v_codes : nullptr;
+            da.vnorms = sep ? v_norms : nullptr;
+            da.Kout = planes;
+            da.Vout = sep ? planes + codec_plane_bytes(c, total_kv) : nullptr;
+            da.d = c.d_model;
+            da.total_kv = total_kv;
+            hipStream_t s0 = static_cast<hipStream_t>(stream);
+            hipError_t e0 = xattn::launch_codec_decode(da, sep, heads, 128, s0);
+            if (e0 != hipSuccess) return hip_fail(e0, "codec decode kernel launch");
+            st = run_forward(Mode::kForward, ctx, Z, W_Q_rot, nullptr, da.Kout, da.Vout, cu_kv,
+                             cu_cand, R, total_cand, total_kv, heads, O, workspace,
+                             workspace_bytes_, stream);
+            if (st != XATTN_OK || sep) return st;
+            e0 = xattn::launch_codec_rotate_out(a.kb, O, total_cand * c.n_slots, c.d_model, heads,
+                                                512, s0);
+            return e0 == hipSuccess ? XATTN_OK : hip_fail(e0, "codec output rotation launch");
         }
     }
     // Query waves sharing each reconstructed memory tile (the reconstruction

@@ -346,6 +346,207 @@ __global__ __launch_bounds__(64 * QW) void codec_attn_kernel(CodecArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// decode a coded memory into bf16 planes (for memories that many query tiles
+// read: decoded once per call instead of once per query tile)
+//   K plane: k^ = norm * x^ in the rotated basis (what the folded queries
+//            score against);
+//   V plane (separate mode): v = E_V (norm * x^), rotated back on the matrix
+//            cores.
+// In shared mode the one plane serves as key and value: attention then
+// leaves its output in the rotated basis and codec_rotate_out_kernel turns
+// it back.  bf16 roundings as in the attention kernels: x^ * norm to bf16,
+// E_V to bf16, fp32 sums.
+// ---------------------------------------------------------------------------
+constexpr int kDR = 64;   // memory rows per decode block
+
+template <int DH, bool SEP>
+struct CdCfg {
+    static constexpr int NT = 256;
+    static constexpr int EB = DH / 32, KST = DH / 16;
+    static constexpr int PLANES = SEP ? 2 : 1;       // coded planes
+    static constexpr int LDK = DH + 8;               // decoded row pitch (16-byte rows)
+    static constexpr int MAXW = DH / 4;              // words per row at 8 bits per coordinate
+    static constexpr int RAWP = MAXW + 1;            // raw row pitch (words), one pad word
+    static constexpr int TAB_BYTES = PLANES * DH * 16;
+    static constexpr int ROT_BYTES = DH * LDK * 2;
+    static constexpr int RAW_BYTES = PLANES * kDR * (RAWP + 1) * 4;
+    static constexpr int ROW_BYTES = kDR * LDK * 2;  // one decoded 64-row plane
+    static constexpr int SMEM = TAB_BYTES + (SEP ? ROT_BYTES : 0) + RAW_BYTES +
+                                (PLANES + (SEP ? 1 : 0)) * ROW_BYTES;
+};
+
+template <int DH, bool SEP>
+__global__ __launch_bounds__(256) void codec_decode_kernel(CodecDecodeArgs a) {
+    using C = CdCfg<DH, SEP>;
+    __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
+    constexpr int ROT = SEP ? C::ROT_BYTES : 0;
+    int4* tab = reinterpret_cast<int4*>(smem);
+    bf16* rot = reinterpret_cast<bf16*>(smem + C::TAB_BYTES);
+    uint32_t* raw = reinterpret_cast<uint32_t*>(smem + C::TAB_BYTES + ROT);
+    bf16* xd = reinterpret_cast<bf16*>(smem + C::TAB_BYTES + ROT + C::RAW_BYTES);
+    bf16* ov = xd + C::PLANES * kDR * C::LDK;
+
+    const int h = blockIdx.y, d = a.d, n = a.total_kv;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 5, l32 = lane & 31;
+    const int W = a.kb.budget / 32;
+
+    // decode tables {bit offset, bits, lo, step} per plane, and E_V (bf16)
+#pragma unroll
+    for (int p = 0; p < C::PLANES; ++p) {
+        const uint8_t* bits = p == 0 ? a.kb.bits : a.vb.bits;
+        const float* center = p == 0 ? a.kb.center : a.vb.center;
+        const float* half = p == 0 ? a.kb.half : a.vb.half;
+        for (int i = tid; i < DH; i += C::NT) {
+            int off = 0;
+            for (int j = 0; j < i; ++j) off += min((int)bits[h * DH + j], 8);
+            const int b = min((int)bits[h * DH + i], 8);
+            const float m = center[h * DH + i], hr = half[h * DH + i];
+            const float step = b > 0 ? 2.0f * hr / (float)(1u << b) : 0.f;
+            const float lo = b > 0 ? m - hr + 0.5f * step : m;
+            tab[p * DH + i] = make_int4(off, b, __builtin_bit_cast(int, lo),
+                                        __builtin_bit_cast(int, step));
+        }
+    }
+    if constexpr (SEP) {
+        for (int idx = tid; idx < DH * DH; idx += C::NT) {
+            const int e = idx / DH, i = idx - e * DH;
+            rot[e * C::LDK + i] = (bf16)a.vb.rot[((size_t)h * DH + e) * DH + i];
+        }
+    }
+
+    const int nblk = (n + kDR - 1) / kDR;
+    for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+        const int r0 = blk * kDR, nr = min(kDR, n - r0);
+        // raw codes and norms of the block (rows past the memory read as zeros)
+#pragma unroll
+        for (int p = 0; p < C::PLANES; ++p) {
+            const uint32_t* cp = (p == 0 ? a.kcodes : a.vcodes) + ((size_t)h * n + r0) * W;
+            const float* np_ = (p == 0 ? a.knorms : a.vnorms) + (size_t)h * n + r0;
+            uint32_t* rp = raw + p * kDR * (C::RAWP + 1);
+            for (int idx = tid; idx < kDR * W; idx += C::NT) {
+                const int r = idx / W, ww = idx - r * W;
+                rp[r * C::RAWP + ww] = r < nr ? cp[idx] : 0u;
+            }
+            if (tid < kDR) {
+                rp[tid * C::RAWP + W] = 0u;   // pad word read by fields that end the row
+                reinterpret_cast<float*>(rp + kDR * C::RAWP)[tid] = tid < nr ? np_[tid] : 0.f;
+            }
+        }
+        __syncthreads();
+        // thread (row tid % 64, quarter tid / 64) decodes a quarter of the
+        // row's coordinates in every plane
+        {
+            const int r = tid & (kDR - 1), part = tid >> 6;
+#pragma unroll
+            for (int p = 0; p < C::PLANES; ++p) {
+                const uint32_t* rp = raw + p * kDR * (C::RAWP + 1) + r * C::RAWP;
+                const float nrm =
+                    reinterpret_cast<const float*>(raw + p * kDR * (C::RAWP + 1) + kDR * C::RAWP)[r];
+                bf16* out = xd + (p * kDR + r) * C::LDK;
+#pragma unroll 4
+                for (int i = part * (DH / 4); i < (part + 1) * (DH / 4); ++i) {
+                    const int4 tb = tab[p * DH + i];
+                    const int off = tb.x, b = tb.y;
+                    const uint32_t lo = rp[off >> 5], hi = rp[(off >> 5) + 1];
+                    const uint32_t v = __builtin_amdgcn_alignbit(hi, lo, off & 31) & ((1u << b) - 1u);
+                    out[i] = (bf16)(nrm * fmaf((float)v, __builtin_bit_cast(float, tb.w),
+                                               __builtin_bit_cast(float, tb.z)));
+                }
+            }
+        }
+        __syncthreads();
+        // K plane rows (rotated basis), 16-byte chunks
+        for (int idx = tid; idx < kDR * (DH / 8); idx += C::NT) {
+            const int r = idx / (DH / 8), c8 = idx - r * (DH / 8);
+            if (r < nr)
+                *reinterpret_cast<uint4*>(static_cast<bf16*>(a.Kout) + (size_t)(r0 + r) * d + h * DH + 8 * c8) =
+                    *reinterpret_cast<const uint4*>(xd + r * C::LDK + 8 * c8);
+        }
+        if constexpr (SEP) {
+        // V plane: rows x^ (32rb..) times E_V^T (features 32eb..) on the
+        // matrix cores; accumulator register t holds row 32rb + (t/4)*8 +
+        // 4g + t%4, feature 32eb + l32
+        const bf16* xv = xd + kDR * C::LDK;
+        for (int blk2 = w; blk2 < 2 * C::EB; blk2 += C::NT / 64) {
+            const int rb = blk2 & 1, eb = blk2 >> 1;
+            f32x16 acc = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < C::KST; ++kk)
+                acc = mfma32(*reinterpret_cast<const bf16x8*>(xv + (32 * rb + l32) * C::LDK + 16 * kk + 8 * g),
+                             *reinterpret_cast<const bf16x8*>(rot + (32 * eb + l32) * C::LDK + 16 * kk + 8 * g),
+                             acc);
+#pragma unroll
+            for (int t = 0; t < 16; ++t)
+                ov[(32 * rb + (t >> 2) * 8 + 4 * g + (t & 3)) * C::LDK + 32 * eb + l32] = (bf16)acc[t];
+        }
+        __syncthreads();
+        for (int idx = tid; idx < kDR * (DH / 8); idx += C::NT) {
+            const int r = idx / (DH / 8), c8 = idx - r * (DH / 8);
+            if (r < nr)
+                *reinterpret_cast<uint4*>(static_cast<bf16*>(a.Vout) + (size_t)(r0 + r) * d + h * DH + 8 * c8) =
+                    *reinterpret_cast<const uint4*>(ov + r * C::LDK + 8 * c8);
+        }
+        }
+        __syncthreads();   // the block's LDS rows are free for the next block
+    }
+}
+
+// Output rows of attention over a shared-mode decoded plane are in the
+// rotated basis: O_h <- E_h O_h per row and head, in place (bf16 in, fp32
+// products on the matrix cores, bf16 out).
+template <int DH>
+__global__ __launch_bounds__(256) void codec_rotate_out_kernel(CodecBook cb, void* Ov, int rows,
+                                                               int d) {
+    constexpr int LDK = DH + 8, EB = DH / 32, KST = DH / 16;
+    __shared__ __attribute__((aligned(16))) bf16 rot[DH * LDK];
+    __shared__ __attribute__((aligned(16))) bf16 xo[2][kDR * LDK];
+    bf16* O = static_cast<bf16*>(Ov);
+    const int h = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 5, l32 = lane & 31;
+    for (int idx = tid; idx < DH * DH; idx += 256) {
+        const int e = idx / DH, i = idx - e * DH;
+        rot[e * LDK + i] = (bf16)cb.rot[((size_t)h * DH + e) * DH + i];
+    }
+    const int nblk = (rows + kDR - 1) / kDR;
+    for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+        const int r0 = blk * kDR, nr = min(kDR, rows - r0);
+        for (int idx = tid; idx < kDR * (DH / 8); idx += 256) {
+            const int r = idx / (DH / 8), c8 = idx - r * (DH / 8);
+            *reinterpret_cast<uint4*>(&xo[0][r * LDK + 8 * c8]) =
+                r < nr ? *reinterpret_cast<const uint4*>(O + (size_t)(r0 + r) * d + h * DH + 8 * c8)
+                       : uint4{};
+        }
+        __syncthreads();
+        // rows (32rb..) times E^T (features 32eb..); register t holds row
+        // 32rb + (t/4)*8 + 4g + t%4, feature 32eb + l32
+        for (int b2 = w; b2 < 2 * EB; b2 += 4) {
+            const int rb = b2 & 1, eb = b2 >> 1;
+            f32x16 acc = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < KST; ++kk)
+                acc = mfma32(*reinterpret_cast<const bf16x8*>(&xo[0][(32 * rb + l32) * LDK + 16 * kk + 8 * g]),
+                             *reinterpret_cast<const bf16x8*>(&rot[(32 * eb + l32) * LDK + 16 * kk + 8 * g]),
+                             acc);
+#pragma unroll
+            for (int t = 0; t < 16; ++t)
+                xo[1][(32 * rb + (t >> 2) * 8 + 4 * g + (t & 3)) * LDK + 32 * eb + l32] = (bf16)acc[t];
+        }
+        __syncthreads();
+        for (int idx = tid; idx < kDR * (DH / 8); idx += 256) {
+            const int r = idx / (DH / 8), c8 = idx - r * (DH / 8);
+            if (r < nr)
+                *reinterpret_cast<uint4*>(O + (size_t)(r0 + r) * d + h * DH + 8 * c8) =
+                    *reinterpret_cast<const uint4*>(&xo[1][r * LDK + 8 * c8]);
+        }
+        __syncthreads();
+    }
+}
+
 template <int DH, int QW>
 hipError_t launch_codec_qw(const CodecArgs& a, bool sep, int64_t items, hipStream_t stream) {
     const dim3 grid((unsigned)(items * a.heads));
@@ -385,6 +586,40 @@ hipError_t launch_codec_fold(const CodecBook& cb, const void* Wq, int q, int d, 
     if (m <= 0) return hipSuccess;
     hipLaunchKernelGGL(codec_fold_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, stream,
                        cb, static_cast<const bf16*>(Wq), q, d, heads, static_cast<bf16*>(Wr));
+    return hipGetLastError();
+}
+
+hipError_t launch_codec_decode(const CodecDecodeArgs& a, bool sep, int heads, int grid_x,
+                               hipStream_t stream) {
+    if (a.total_kv <= 0) return hipSuccess;
+    const int nblk = (a.total_kv + kDR - 1) / kDR;
+    const dim3 grid((unsigned)(grid_x < nblk ? grid_x : nblk), (unsigned)heads);
+#define XATTN_DEC(DH_)                                                                    \
+    if (a.d / heads == DH_) {                                                            \
+        if (sep)                                                                         \
+            hipLaunchKernelGGL((codec_decode_kernel<DH_, true>), grid, dim3(256), 0, stream, a);  \
+        else                                                                             \
+            hipLaunchKernelGGL((codec_decode_kernel<DH_, false>), grid, dim3(256), 0, stream, a); \
+        return hipGetLastError();                                                        \
+    }
+    XATTN_DEC(32)
+    XATTN_DEC(64)
+    XATTN_DEC(128)
+#undef XATTN_DEC
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_codec_rotate_out(const CodecBook& cb, void* O, int rows, int d, int heads,
+                                   int grid_x, hipStream_t stream) {
+    if (rows <= 0) return hipSuccess;
+    const int nblk = (rows + kDR - 1) / kDR;
+    const dim3 grid((unsigned)(grid_x < nblk ? grid_x : nblk), (unsigned)heads);
+    switch (d / heads) {
+        case 32: hipLaunchKernelGGL(codec_rotate_out_kernel<32>, grid, dim3(256), 0, stream, cb, O, rows, d); break;
+        case 64: hipLaunchKernelGGL(codec_rotate_out_kernel<64>, grid, dim3(256), 0, stream, cb, O, rows, d); break;
+        case 128: hipLaunchKernelGGL(codec_rotate_out_kernel<128>, grid, dim3(256), 0, stream, cb, O, rows, d); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

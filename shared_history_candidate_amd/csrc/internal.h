@@ -158,6 +158,23 @@ hipError_t launch_codec_encode(const CodecBook& cb, const void* X, int n, int d,
                                uint32_t* codes, float* norms, hipStream_t stream);
 hipError_t launch_codec_fold(const CodecBook& cb, const void* Wq, int q, int d, int heads,
                              void* Wr, hipStream_t stream);
+// Decoded planes of a coded memory: Kout [total_kv][d] bf16 in the keys'
+// rotated basis; separate mode also Vout [total_kv][d] bf16, rotated back.
+struct CodecDecodeArgs {
+    CodecBook kb, vb;
+    const uint32_t* kcodes;
+    const float* knorms;
+    const uint32_t* vcodes;
+    const float* vnorms;
+    void* Kout;
+    void* Vout;
+    int d, total_kv;
+};
+hipError_t launch_codec_decode(const CodecDecodeArgs& a, bool sep, int heads, int grid_x,
+                               hipStream_t stream);
+// O_h <- E_h O_h in place for rows [rows][d] (shared-mode decoded memory).
+hipError_t launch_codec_rotate_out(const CodecBook& cb, void* O, int rows, int d, int heads,
+                                   int grid_x, hipStream_t stream);
 // qw query waves (2, 4 or 8) share each reconstructed tile: tile_m = 32 qw.
 hipError_t launch_codec_attn(const CodecArgs& a, bool sep, int qw, int64_t items,
                              hipStream_t stream);

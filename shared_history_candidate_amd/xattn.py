@@ -27,7 +27,8 @@ EXPORTED = ("xattn_create", "xattn_destroy", "xattn_workspace_size", "xattn_forw
             "xattn_forward_launches", "xattn_project", "xattn_output", "xattn_device_error",
             "xattn_last_error", "xattn_forward_prefix", "xattn_attend_q_prefix",
             "xattn_backward_workspace_size", "xattn_backward", "xattn_codec_encode",
-            "xattn_codec_fold_query_weights", "xattn_forward_codec", "xattn_forward_path")
+            "xattn_codec_fold_query_weights", "xattn_forward_codec", "xattn_forward_path",
+            "xattn_codec_workspace_size")
 
 # xattn_path values (include/xattn.h)
 PATH_SINGLE, PATH_GEMM, PATH_FP32, PATH_SHORT = 1, 2, 3, 4
@@ -92,6 +93,8 @@ def lib():
         L.xattn_destroy.restype = None
         L.xattn_workspace_size.argtypes = [P, I32, I32, I32]
         L.xattn_workspace_size.restype = SZ
+        L.xattn_codec_workspace_size.argtypes = [P, I32, I32, I32, I32]
+        L.xattn_codec_workspace_size.restype = SZ
         L.xattn_max_tiles.argtypes = [P, I32, I32, I32]
         L.xattn_max_tiles.restype = I64
         L.xattn_forward_launches.argtypes = [P, I32, I32, I32, I32]
@@ -184,6 +187,13 @@ class XAttn:
     # -- sizes ---------------------------------------------------------------
     def workspace_size(self, num_requests: int, total_cand: int, heads: int) -> int:
         return int(lib().xattn_workspace_size(self._h, num_requests, total_cand, heads))
+
+    def codec_workspace_size(self, num_requests: int, total_cand: int, total_kv: int,
+                             heads: int) -> int:
+        """Workspace bytes with room for the decoded memory (xattn_forward_codec
+        decodes the memory once per call)."""
+        return int(lib().xattn_codec_workspace_size(self._h, num_requests, total_cand, total_kv,
+                                                    heads))
 
     def max_tiles(self, num_requests: int, total_cand: int, heads: int) -> int:
         return int(lib().xattn_max_tiles(self._h, num_requests, total_cand, heads))
@@ -366,8 +376,11 @@ class XAttn:
 
     def forward_codec(self, cb_k: "Codebook", cb_v, Z, W_Q_rot, k_codes, k_norms, v_codes,
                       v_norms, cu_seqlens_kv, cu_cand, heads: int, O=None, workspace=None,
-                      stream=None) -> torch.Tensor:
-        """Cross-attention over a coded memory (xattn_forward_codec)."""
+                      stream=None, decode: bool = True) -> torch.Tensor:
+        """Cross-attention over a coded memory (xattn_forward_codec).  Without a
+        workspace one is allocated: with room for the decoded memory when
+        `decode` (the memory decoded once per call), else the plain forward's
+        (each memory tile reconstructed in LDS)."""
         d, q, dt = self.d_model, self.q, self.torch_dtype
         total_cand = Z.shape[0]
         total_kv = k_norms.shape[1]
@@ -379,7 +392,11 @@ class XAttn:
         if O is None:
             O = torch.empty((total_cand, q, d), dtype=dt, device=Z.device)
         if workspace is None:
-            workspace = self.alloc_workspace(R, total_cand, heads)
+            if decode:
+                n = self.codec_workspace_size(R, total_cand, total_kv, heads)
+                workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=Z.device)
+            else:
+                workspace = self.alloc_workspace(R, total_cand, heads)
         sk = cb_k.struct()
         sv = cb_v.struct() if cb_v is not None else None
         _check(lib().xattn_forward_codec(

@@ -23,7 +23,7 @@ from oracle import codec as OC
 from shared_history_candidate_amd import workloads as W
 from shared_history_candidate_amd import xattn as X
 
-from gpu_util import assert_close, ctx_for, require_gpu
+from gpu_util import assert_close, ctx_for, require_gpu, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -108,9 +108,13 @@ EDGE_LENGTHS = [1, 31, 65, 97, 300, 0, 130]
 EDGE_CANDS = [3, 65, 1, 40, 7, 2, 0]
 
 
+@pytest.mark.parametrize("decode", [False, True])
 @pytest.mark.parametrize("mode", ["shared", "separate"])
 @pytest.mark.parametrize("dh,heads,bpc", [(32, 4, 4), (64, 2, 4), (128, 2, 3), (64, 2, 8)])
-def test_codec_attention_matches_oracle(mode, dh, heads, bpc):
+def test_codec_attention_matches_oracle(mode, dh, heads, bpc, decode):
+    """Both paths over a coded memory: each tile reconstructed in LDS (plain
+    workspace) and the memory decoded once into bf16 planes (codec
+    workspace)."""
     require_gpu()
     wl, K, V, cbk, cbv = _setup(EDGE_LENGTHS, EDGE_CANDS, dh, heads, mode, bpc, seed=dh)
     ctx = ctx_for(wl)
@@ -119,7 +123,7 @@ def test_codec_attention_matches_oracle(mode, dh, heads, bpc):
     vc, vn = _gpu_codes(ctx, cbv, V) if V is not None else (None, None)
     Wr = ctx.codec_fold(_book(cbk), t["W_Q"])
     O = ctx.forward_codec(_book(cbk), _book(cbv) if cbv else None, t["Z"], Wr, kc, kn, vc, vn,
-                          t["cu_kv"], t["cu_cand"], wl.heads)
+                          t["cu_kv"], t["cu_cand"], wl.heads, decode=decode)
     torch.cuda.synchronize()
     got = O.float().cpu().numpy().astype(np.float64).reshape(-1, wl.d)
     # the GPU's own codes, decoded by the oracle
@@ -176,7 +180,7 @@ def test_codec_every_query_wave_count(monkeypatch, qw, dh, heads, mode):
     vc, vn = _gpu_codes(ctx, cbv, V) if V is not None else (None, None)
     O = ctx.forward_codec(_book(cbk), _book(cbv) if cbv else None, t["Z"],
                           ctx.codec_fold(_book(cbk), t["W_Q"]), kc, kn, vc, vn, t["cu_kv"],
-                          t["cu_cand"], wl.heads)
+                          t["cu_cand"], wl.heads, decode=False)
     torch.cuda.synchronize()
     got = O.float().cpu().numpy().astype(np.float64).reshape(-1, wl.d)
     Kd = OC.decode(kn.cpu().numpy().T.astype(np.float64), _unpacked(kc, cbk), cbk)
@@ -243,3 +247,34 @@ def test_codec_short_memory_transx_batch():
     ref = oracle.forward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, Kd, Vd, rows=rows)
     err, rel = assert_close(got[rows], ref, "bf16", "codec transx batch")
     print("codec transx batch: max-abs %.3e normwise %.3e" % (err, rel))
+
+
+@pytest.mark.parametrize("mode", ["shared", "separate"])
+@pytest.mark.parametrize("dh,heads", [(64, 4), (128, 2)])
+def test_codec_decoded_planes_long_memory(mode, dh, heads):
+    """The decode path on memories of more decode blocks than the decode grid
+    (9001 rows: work-groups loop over 64-row blocks, the last one partial),
+    against the oracle on sampled rows; the same inputs through the per-tile
+    reconstruction agree with it within the same bound."""
+    require_gpu()
+    wl, K, V, cbk, cbv = _setup([5000, 4001], [40, 3], dh, heads, mode, 4.5, seed=11)
+    ctx = ctx_for(wl)
+    t = X.to_device(wl)
+    kc, kn = _gpu_codes(ctx, cbk, K)
+    vc, vn = _gpu_codes(ctx, cbv, V) if V is not None else (None, None)
+    Wr = ctx.codec_fold(_book(cbk), t["W_Q"])
+    outs = {}
+    for decode in (True, False):
+        O = ctx.forward_codec(_book(cbk), _book(cbv) if cbv else None, t["Z"], Wr, kc, kn, vc,
+                              vn, t["cu_kv"], t["cu_cand"], wl.heads, decode=decode)
+        torch.cuda.synchronize()
+        outs[decode] = O.float().cpu().numpy().astype(np.float64).reshape(-1, wl.d)
+    Kd = OC.decode(kn.cpu().numpy().T.astype(np.float64), _unpacked(kc, cbk), cbk)
+    Vd = (OC.decode(vn.cpu().numpy().T.astype(np.float64), _unpacked(vc, cbv), cbv)
+          if V is not None else None)
+    rows = sample_rows(wl, 60)
+    ref = oracle.forward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, Kd, Vd, rows=rows)
+    for decode in (True, False):
+        err, rel = assert_close(outs[decode][rows], ref, "bf16",
+                                "codec long %s dh=%d decode=%s" % (mode, dh, decode))
+        print("codec long %s dh=%d decode=%s: max-abs %.3e" % (mode, dh, decode, err))
