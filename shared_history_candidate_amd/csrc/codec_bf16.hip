@@ -80,6 +80,102 @@ __global__ void codec_encode_kernel(CodecBook cb, const bf16* __restrict__ X, in
     }
 }
 
+// encode, block form: a work-group per head and 64-row block (grid-stride),
+// the block's rows (fp32, padded pitch) and E_h staged in LDS.  The same
+// fp32 operations in the same order as codec_encode_kernel: the norm as a
+// running fmaf over the row, each rotated coordinate as a running fmaf over
+// o of (x_o * inv) * E[o][i], then the quantiser and the packing.  Thread
+// (row, quarter) forms a quarter of the row's coordinates (o outer, its
+// coordinates inner, E rows read as broadcasts); one thread per row packs.
+template <int DH>
+__global__ __launch_bounds__(256) void codec_encode_block_kernel(CodecBook cb, const bf16* __restrict__ X,
+                                                                 int n, int d,
+                                                                 uint32_t* __restrict__ codes,
+                                                                 float* __restrict__ norms) {
+    constexpr int XP = DH + 1;   // row pitch (floats): a lane per row, no bank conflicts
+    constexpr int NQ = DH / 4;   // coordinates per thread
+    __shared__ float E[DH * DH];
+    __shared__ float xs[64 * XP];
+    __shared__ float invs[64];
+    __shared__ int nbits[DH];
+    __shared__ uint8_t cs[64 * DH];
+    const int h = blockIdx.y, tid = threadIdx.x;
+    const int W = cb.budget / 32;
+    for (int idx = tid; idx < DH * DH; idx += 256) E[idx] = cb.rot[(size_t)h * DH * DH + idx];
+    for (int i = tid; i < DH; i += 256) nbits[i] = min((int)cb.bits[h * DH + i], 8);
+    const int nblk = (n + 63) / 64;
+    for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+        const int r0 = blk * 64, nr = min(64, n - r0);
+        for (int idx = tid; idx < 64 * DH; idx += 256) {
+            const int r = idx / DH, o = idx - r * DH;
+            xs[r * XP + o] = r < nr ? (float)X[(size_t)(r0 + r) * d + h * DH + o] : 0.f;
+        }
+        __syncthreads();
+        if (tid < 64) {
+            float n2 = 0.f;
+            for (int o = 0; o < DH; ++o) {
+                const float v = xs[tid * XP + o];
+                n2 = fmaf(v, v, n2);
+            }
+            const float nrm = sqrtf(n2);
+            if (tid < nr) norms[(size_t)h * n + r0 + tid] = nrm;
+            invs[tid] = nrm > 0.f ? 1.0f / nrm : 0.f;
+        }
+        __syncthreads();
+        {
+            const int r = tid & 63, i0 = (tid >> 6) * NQ;
+            const float inv = invs[r];
+            float xr[NQ];
+#pragma unroll
+            for (int k = 0; k < NQ; ++k) xr[k] = 0.f;
+#pragma unroll 2
+            for (int o = 0; o < DH; ++o) {
+                const float xo = xs[r * XP + o] * inv;
+                const float* eo = E + o * DH + i0;
+#pragma unroll
+                for (int k = 0; k < NQ; ++k) xr[k] = fmaf(xo, eo[k], xr[k]);
+            }
+#pragma unroll
+            for (int k = 0; k < NQ; ++k) {
+                const int i = i0 + k, b = nbits[i];
+                uint32_t code = 0;
+                if (b > 0) {
+                    const float c = cb.center[h * DH + i], a = cb.half[h * DH + i];
+                    const float levels = (float)(1u << b);
+                    const float t = floorf((xr[k] - c + a) / (2.0f * a) * levels);
+                    code = t <= 0.f ? 0u : (t >= levels - 1.f ? (1u << b) - 1u : (uint32_t)t);
+                }
+                cs[r * DH + i] = (uint8_t)code;
+            }
+        }
+        __syncthreads();
+        if (tid < nr) {
+            uint32_t* out = codes + ((size_t)h * n + r0 + tid) * W;
+            uint32_t word = 0;
+            int wi = 0, off = 0;
+            for (int i = 0; i < DH; ++i) {
+                const int b = nbits[i];
+                if (b <= 0) continue;
+                const uint32_t code = cs[tid * DH + i];
+                word |= code << off;
+                if (off + b >= 32) {
+                    if (wi < W) out[wi] = word;
+                    ++wi;
+                    word = off + b > 32 ? code >> (32 - off) : 0u;
+                    off = off + b - 32;
+                } else {
+                    off += b;
+                }
+            }
+            for (; wi < W; ++wi) {   // a bit table below the budget leaves zero words
+                out[wi] = word;
+                word = 0;
+            }
+        }
+        __syncthreads();   // the block's LDS rows are free for the next block
+    }
+}
+
 // W~[s][h*dh + i][c] = sum_o E_h[o][i] W[s][h*dh + o][c]  (fp32 sums, bf16 out)
 __global__ void codec_fold_kernel(CodecBook cb, const bf16* __restrict__ Wq, int q, int d,
                                   int heads, bf16* __restrict__ Wr) {
@@ -575,8 +671,18 @@ hipError_t launch_codec_encode(const CodecBook& cb, const void* X, int n, int d,
                                uint32_t* codes, float* norms, hipStream_t stream) {
     const int64_t m = (int64_t)n * heads;
     if (m <= 0) return hipSuccess;
-    hipLaunchKernelGGL(codec_encode_kernel, dim3((unsigned)((m + 127) / 128)), dim3(128), 0,
-                       stream, cb, static_cast<const bf16*>(X), n, d, heads, codes, norms);
+    const int dh = d / heads;
+    const int nblk = (n + 63) / 64;
+    const dim3 grid((unsigned)(nblk < 512 ? nblk : 512), (unsigned)heads);
+    const bf16* x = static_cast<const bf16*>(X);
+    switch (dh) {
+        case 32: hipLaunchKernelGGL(codec_encode_block_kernel<32>, grid, dim3(256), 0, stream, cb, x, n, d, codes, norms); break;
+        case 64: hipLaunchKernelGGL(codec_encode_block_kernel<64>, grid, dim3(256), 0, stream, cb, x, n, d, codes, norms); break;
+        case 128: hipLaunchKernelGGL(codec_encode_block_kernel<128>, grid, dim3(256), 0, stream, cb, x, n, d, codes, norms); break;
+        default:   // other head widths: one thread per (row, head)
+            hipLaunchKernelGGL(codec_encode_kernel, dim3((unsigned)((m + 127) / 128)), dim3(128), 0,
+                               stream, cb, x, n, d, heads, codes, norms);
+    }
     return hipGetLastError();
 }
 
