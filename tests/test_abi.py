@@ -305,6 +305,23 @@ def test_backward_host_validation(L):
     L.xattn_destroy(h)
 
 
+def test_codec_workspace_size(L):
+    """The forward's workspace, then one bf16 plane of total_kv x d per coded
+    plane (one in shared mode, two in separate mode), 256-byte aligned."""
+    for mode, planes in ((X.XATTN_KV_SHARED, 1), (X.XATTN_KV_SEPARATE, 2)):
+        st, h = _create(L, 256, 3, X.XATTN_BF16, mode)
+        assert st == 0
+        base = L.xattn_workspace_size(h, 2, 10, 4)
+        plane = (1000 * 256 * 2 + 255) // 256 * 256
+        assert L.xattn_codec_workspace_size(h, 2, 10, 1000, 4) == (base + 255) // 256 * 256 + planes * plane
+        assert L.xattn_codec_workspace_size(h, 2, 10, 0, 4) == (base + 255) // 256 * 256
+        assert L.xattn_codec_workspace_size(h, 2, 10, -1, 4) == 0
+        assert L.xattn_codec_workspace_size(h, -1, 10, 5, 4) == 0
+        assert L.xattn_codec_workspace_size(h, 2, 10, 5, 0) == 0
+        assert L.xattn_codec_workspace_size(None, 2, 10, 5, 4) == 0
+        L.xattn_destroy(h)
+
+
 def test_codec_host_validation(L):
     CB = X.CodebookStruct
     st, h = _create(L, 256, 3, X.XATTN_BF16, X.XATTN_KV_SHARED)
