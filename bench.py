@@ -361,6 +361,24 @@ def main():
         def step():
             ctx.backward(t["Z"], t["W_Q"], t["K"], t["V"], dO_d, t["cu_kv"], t["cu_cand"],
                          wl.heads, workspace=bws, out=grads, stream=stream, cand_kv_len=cl)
+
+        # the training pair: a forward that keeps the normalisers, and the
+        # backward that reuses them (bf16 only)
+        train_pair = wl.dtype == "bf16"
+        if train_pair:
+            O_tr, lse_tr = ctx.forward_train(t["Z"], t["W_Q"], t["K"], t["V"], t["cu_kv"],
+                                             t["cu_cand"], wl.heads, workspace=ws,
+                                             cand_kv_len=cl)
+
+            def step_train_fwd():
+                ctx.forward_train(t["Z"], t["W_Q"], t["K"], t["V"], t["cu_kv"], t["cu_cand"],
+                                  wl.heads, O=O_tr, lse=lse_tr, workspace=ws, stream=stream,
+                                  cand_kv_len=cl)
+
+            def step_saved():
+                ctx.backward(t["Z"], t["W_Q"], t["K"], t["V"], dO_d, t["cu_kv"], t["cu_cand"],
+                             wl.heads, workspace=bws, out=grads, stream=stream, cand_kv_len=cl,
+                             O=O_tr, lse=lse_tr)
     elif args.stage == "codec":
         # memory published as codes + norms (encoded once, outside the step)
         budget = int(round(args.codec_bits * wl.d_h / 32.0)) * 32
@@ -445,6 +463,12 @@ def main():
         print("bench: backward %.4f ms" % bwd_ms, file=sys.stderr, flush=True)
         roof = entry("backward", wl.flops_backward(kv_len), wl.bytes_backward(), bwd_ms)
         roof["other_kernel"] = None
+        if train_pair:
+            tf_ms, sv_ms = per_launch_ms(step_train_fwd), per_launch_ms(step_saved)
+            print("bench: training forward (keeps lse) %.4f ms; backward from the stored "
+                  "statistics %.4f ms" % (tf_ms, sv_ms), file=sys.stderr, flush=True)
+            roof["training_forward_ms"] = round(tf_ms, 5)
+            roof["saved_statistics_backward_ms"] = round(sv_ms, 5)
     elif args.stage == "codec":
         # the coded forward timed as one unit; bytes count codes + norms for
         # the memory.  For reference, the same call with the plain workspace

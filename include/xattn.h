@@ -179,6 +179,30 @@ xattn_status xattn_forward_prefix(xattn_ctx* ctx,
                                   void* O, void* workspace, size_t workspace_bytes,
                                   void* stream);
 
+/* Training forward: xattn_forward (cand_kv_len NULL) or xattn_forward_prefix
+ * (cand_kv_len not NULL) that also stores, for xattn_backward_saved, the
+ * softmax normaliser of every query row and head (ReST reading note s.3.3.1,
+ * Eq. (7): the denominator of the row's softmax over its request's memory).
+ *   - lse [total_cand][q][heads] fp32, device, written: the base-2 logarithm
+ *     of sum_j exp(q_h . k_{h,j} / sqrt(d_h)) over the rows j the row sees,
+ *     with q_h the bf16 projected query (as the products use it: scaled by
+ *     log2(e)/sqrt(d_h) and rounded to bf16); -inf for a row that sees no
+ *     memory.
+ * O, the workspace and the other arguments as for xattn_forward.  Batches
+ * that xattn_forward would send to the short-memory kernel take the
+ * projection GEMM and attention kernel here (that kernel keeps no
+ * statistics).  bf16 contexts only (XATTN_EUNSUPPORTED otherwise); a NULL
+ * lse with total_cand > 0 is XATTN_EINVAL. */
+xattn_status xattn_forward_train(xattn_ctx* ctx,
+                                 const void* Z, const void* W_Q,
+                                 const void* K, const void* V,
+                                 const int32_t* cu_seqlens_kv, const int32_t* cu_cand,
+                                 const int32_t* cand_kv_len,
+                                 int32_t num_requests, int32_t total_cand,
+                                 int32_t total_kv, int32_t heads,
+                                 void* O, float* lse, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
 /* Projection and attention without re-planning (one kernel where
  * xattn_forward would run one): like xattn_forward, but the plan is read
  * from `workspace`, where a previous xattn_plan or xattn_forward call left it
@@ -271,6 +295,28 @@ xattn_status xattn_backward(xattn_ctx* ctx,
                             int32_t total_kv, int32_t heads,
                             void* dZ, float* dW_Q, void* dK, void* dV,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* xattn_backward from the statistics of xattn_forward_train: O
+ * [total_cand][q][d] bf16 (16-byte aligned, as dO) and lse
+ * [total_cand][q][heads] fp32 are that call's outputs for the same inputs
+ * (and the same cand_kv_len).  The statistics pass (a repeat of the forward)
+ * is replaced by one pass over dO and O for D = <dO_row, O_row> per head; D
+ * is taken from the bf16 O rather than the forward's fp32 accumulators, so
+ * the gradients differ from xattn_backward's by rounding.  Same workspace
+ * size, outputs and errors as xattn_backward; bf16 contexts only
+ * (XATTN_EUNSUPPORTED otherwise); NULL O or lse with total_cand > 0, or a
+ * misaligned O or dO, is XATTN_EINVAL.  Stored statistics of other inputs
+ * give undefined gradients. */
+xattn_status xattn_backward_saved(xattn_ctx* ctx,
+                                  const void* Z, const void* W_Q,
+                                  const void* K, const void* V, const void* dO,
+                                  const void* O, const float* lse,
+                                  const int32_t* cu_seqlens_kv, const int32_t* cu_cand,
+                                  const int32_t* cand_kv_len,
+                                  int32_t num_requests, int32_t total_cand,
+                                  int32_t total_kv, int32_t heads,
+                                  void* dZ, float* dW_Q, void* dK, void* dV,
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* Coded memory (TransX technical report, s.3).  A published memory keeps,
  * for every row and head, the length of the head's key (or value) vector and

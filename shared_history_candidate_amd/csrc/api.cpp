@@ -313,12 +313,13 @@ enum class Mode { kForward, kAttend, kAttendQ };
 // (projection + attention over the plan in the workspace), xattn_attend_q
 // (attention over caller-projected queries and the plan in the workspace) and
 // xattn_forward_prefix (xattn_forward with a per-candidate memory prefix,
-// cand_len not NULL).
+// cand_len not NULL) and xattn_forward_train (lse not NULL: the attention
+// kernel also stores each row's log2 softmax normaliser per head).
 xattn_status run_forward(Mode mode, xattn_ctx* ctx, const void* Z, const void* W_Q, const void* Qin,
                          const void* K, const void* V, const int32_t* cu_kv,
                          const int32_t* cu_cand, int32_t R, int32_t total_cand, int32_t total_kv,
                          int32_t heads, void* O, void* workspace, size_t workspace_bytes_,
-                         void* stream, const int32_t* cand_len = nullptr) {
+                         void* stream, const int32_t* cand_len = nullptr, float* lse = nullptr) {
     g_last_error.clear();
     xattn_status st = check_shape(ctx, R, total_cand, total_kv, heads);
     if (st != XATTN_OK) return st;
@@ -327,6 +328,8 @@ xattn_status run_forward(Mode mode, xattn_ctx* ctx, const void* Z, const void* W
         return fail(XATTN_EINVAL, "V must be NULL in XATTN_KV_SHARED mode (V = K = H)");
     if (!cu_kv || !cu_cand) return fail(XATTN_EINVAL, "NULL offset array");
     if (total_cand > 0 && !O) return fail(XATTN_EINVAL, "NULL O");
+    if (lse && c.dtype != XATTN_BF16)
+        return fail(XATTN_EUNSUPPORTED, "stored statistics need a bf16 context");
     if (total_cand > 0 && mode != Mode::kAttendQ && (!Z || !W_Q))
         return fail(XATTN_EINVAL, "NULL Z or W_Q");
     if (total_cand > 0 && mode == Mode::kAttendQ && !Qin) return fail(XATTN_EINVAL, "NULL Q");
@@ -370,7 +373,8 @@ xattn_status run_forward(Mode mode, xattn_ctx* ctx, const void* Z, const void* W
         a.heads = heads;
         a.O = O;
         a.cand_len = cand_len;
-        if (mode != Mode::kAttendQ && !cand_len && short_shape(c, R, total_kv, heads)) {
+        a.lse = lse;   // the short-memory kernel keeps no statistics
+        if (mode != Mode::kAttendQ && !cand_len && !lse && short_shape(c, R, total_kv, heads)) {
             // projection and attention in one launch; a forward pass also
             // plans the batch in that launch (request order) and stores the
             // plan in the workspace
@@ -449,6 +453,18 @@ xattn_status xattn_forward_prefix(xattn_ctx* ctx, const void* Z, const void* W_Q
     }
     return run_forward(Mode::kForward, ctx, Z, W_Q, nullptr, K, V, cu_kv, cu_cand, R, total_cand,
                        total_kv, heads, O, workspace, workspace_bytes_, stream, cand_kv_len);
+}
+
+xattn_status xattn_forward_train(xattn_ctx* ctx, const void* Z, const void* W_Q, const void* K,
+                                 const void* V, const int32_t* cu_kv, const int32_t* cu_cand,
+                                 const int32_t* cand_kv_len, int32_t R, int32_t total_cand,
+                                 int32_t total_kv, int32_t heads, void* O, float* lse,
+                                 void* workspace, size_t workspace_bytes_, void* stream) {
+    g_last_error.clear();
+    if (ctx && total_cand > 0 && !lse) return fail(XATTN_EINVAL, "NULL lse");
+    return run_forward(Mode::kForward, ctx, Z, W_Q, nullptr, K, V, cu_kv, cu_cand, R, total_cand,
+                       total_kv, heads, O, workspace, workspace_bytes_, stream, cand_kv_len,
+                       total_cand > 0 ? lse : nullptr);
 }
 
 xattn_status xattn_attend(xattn_ctx* ctx, const void* Z, const void* W_Q, const void* K,
@@ -534,17 +550,30 @@ size_t xattn_backward_workspace_size(const xattn_ctx* ctx, int32_t R, int32_t to
     return bwd_layout(ctx->cfg, R, total_cand, total_kv, heads).total;
 }
 
-xattn_status xattn_backward(xattn_ctx* ctx, const void* Z, const void* W_Q, const void* K,
-                            const void* V, const void* dO, const int32_t* cu_kv,
-                            const int32_t* cu_cand, const int32_t* cand_kv_len, int32_t R,
-                            int32_t total_cand,
-                            int32_t total_kv, int32_t heads, void* dZ, float* dW_Q, void* dK,
-                            void* dV, void* workspace, size_t workspace_bytes_, void* stream) {
+namespace {
+
+// Body of xattn_backward (O_saved and lse_saved NULL: the forward statistics
+// are recomputed) and xattn_backward_saved (the forward's output and
+// normalisers are given; only D = <dO, O> is computed).
+xattn_status run_backward(xattn_ctx* ctx, const void* Z, const void* W_Q, const void* K,
+                          const void* V, const void* dO, const void* O_saved,
+                          const float* lse_saved, const int32_t* cu_kv, const int32_t* cu_cand,
+                          const int32_t* cand_kv_len, int32_t R, int32_t total_cand,
+                          int32_t total_kv, int32_t heads, void* dZ, float* dW_Q, void* dK,
+                          void* dV, void* workspace, size_t workspace_bytes_, void* stream) {
     g_last_error.clear();
     xattn_status st = check_shape(ctx, R, total_cand, total_kv, heads);
     if (st != XATTN_OK) return st;
     const xattn_config& c = ctx->cfg;
     const bool sep = c.kv_mode == XATTN_KV_SEPARATE;
+    const bool saved = O_saved || lse_saved;
+    if (saved && c.dtype != XATTN_BF16)
+        return fail(XATTN_EUNSUPPORTED, "stored statistics need a bf16 context");
+    if (saved && total_cand > 0 && (!O_saved || !lse_saved))
+        return fail(XATTN_EINVAL, "NULL O or lse");
+    if (saved && total_cand > 0 &&
+        ((reinterpret_cast<uintptr_t>(O_saved) | reinterpret_cast<uintptr_t>(dO)) & 15) != 0)
+        return fail(XATTN_EINVAL, "O and dO must be 16-byte aligned");
     if (!sep && (V || dV))
         return fail(XATTN_EINVAL, "V and dV must be NULL in XATTN_KV_SHARED mode (dK is dH)");
     if (!cu_kv || !cu_cand) return fail(XATTN_EINVAL, "NULL offset array");
@@ -616,7 +645,11 @@ xattn_status xattn_backward(xattn_ctx* ctx, const void* Z, const void* W_Q, cons
     // 3. forward statistics lse and D = <dO, O> per row and head
     float* lse = reinterpret_cast<float*>(ws + Lw.lse);
     float* dsum = reinterpret_cast<float*>(ws + Lw.dsum);
-    if (bf) {
+    if (saved) {
+        XATTN_TRY(xattn::launch_bwd_dsum_bf16(dO, O_saved, (int64_t)total_cand * q, d, heads, dsum,
+                                              s),
+                  "statistics kernel launch");
+    } else if (bf) {
         xattn::AttnArgs a{};
         a.Qp = ws + Lw.qs;
         a.K = K;
@@ -653,7 +686,7 @@ xattn_status xattn_backward(xattn_ctx* ctx, const void* Z, const void* W_Q, cons
     b.K = K;
     b.V = sep ? V : nullptr;
     b.dO = dO;
-    b.lse = lse;
+    b.lse = saved ? lse_saved : lse;
     b.Dsum = dsum;
     b.plan = reinterpret_cast<const int*>(ws + Lw.plan);
     b.kplan = reinterpret_cast<const int*>(ws + Lw.kplan);
@@ -692,6 +725,38 @@ xattn_status xattn_backward(xattn_ctx* ctx, const void* Z, const void* W_Q, cons
     }
 #undef XATTN_TRY
     return XATTN_OK;
+}
+
+}  // namespace
+
+xattn_status xattn_backward(xattn_ctx* ctx, const void* Z, const void* W_Q, const void* K,
+                            const void* V, const void* dO, const int32_t* cu_kv,
+                            const int32_t* cu_cand, const int32_t* cand_kv_len, int32_t R,
+                            int32_t total_cand, int32_t total_kv, int32_t heads, void* dZ,
+                            float* dW_Q, void* dK, void* dV, void* workspace,
+                            size_t workspace_bytes_, void* stream) {
+    return run_backward(ctx, Z, W_Q, K, V, dO, nullptr, nullptr, cu_kv, cu_cand, cand_kv_len, R,
+                        total_cand, total_kv, heads, dZ, dW_Q, dK, dV, workspace, workspace_bytes_,
+                        stream);
+}
+
+xattn_status xattn_backward_saved(xattn_ctx* ctx, const void* Z, const void* W_Q, const void* K,
+                                  const void* V, const void* dO, const void* O, const float* lse,
+                                  const int32_t* cu_kv, const int32_t* cu_cand,
+                                  const int32_t* cand_kv_len, int32_t R, int32_t total_cand,
+                                  int32_t total_kv, int32_t heads, void* dZ, float* dW_Q,
+                                  void* dK, void* dV, void* workspace, size_t workspace_bytes_,
+                                  void* stream) {
+    if (ctx && total_cand > 0 && (!O || !lse)) {
+        g_last_error.clear();
+        return fail(XATTN_EINVAL, "NULL O or lse");
+    }
+    // with no query rows there is nothing to reuse: the plain pass zeroes dW_Q and the memory
+    // gradients
+    return run_backward(ctx, Z, W_Q, K, V, dO, total_cand > 0 ? O : nullptr,
+                        total_cand > 0 ? lse : nullptr, cu_kv, cu_cand, cand_kv_len, R,
+                        total_cand, total_kv, heads, dZ, dW_Q, dK, dV, workspace,
+                        workspace_bytes_, stream);
 }
 
 namespace {

@@ -660,7 +660,47 @@ __global__ void prefix_vis_kernel(const int* __restrict__ cu_kv, const int* __re
     vis[c] = kv0 + (want < 0 ? 0 : (want < L ? want : L));
 }
 
+// D[row][h] = <dO_row, O_row> over head h's features from the forward's stored
+// output (the second per-row statistic of dS = P o (dP - D)), for a backward
+// pass that reuses the forward's normalisers.  One thread per 8 features
+// (16-byte loads of both operands); the d_h/8 threads of a head sum their
+// partials in a fixed xor-tree order.  The loop bound is uniform per block, so
+// every lane reaches the shuffles.
+__global__ __launch_bounds__(256) void bwd_dsum_kernel(const uint4* __restrict__ dO,
+                                                       const uint4* __restrict__ O, int64_t n,
+                                                       int g, float* __restrict__ dsum) {
+    for (int64_t i0 = (int64_t)blockIdx.x * 256; i0 < n; i0 += (int64_t)gridDim.x * 256) {
+        const int64_t i = i0 + threadIdx.x;
+        float acc = 0.f;
+        if (i < n) {
+            const uint4 a = dO[i], b = O[i];
+            const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                acc = fmaf(__uint_as_float(aw[k] << 16), __uint_as_float(bw[k] << 16), acc);
+                acc = fmaf(__uint_as_float(aw[k] & 0xFFFF0000u), __uint_as_float(bw[k] & 0xFFFF0000u),
+                           acc);
+            }
+        }
+        for (int off = g >> 1; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+        if (i < n && (i & (g - 1)) == 0) dsum[i / g] = acc;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_bwd_dsum_bf16(const void* dO, const void* O, int64_t rows, int d, int heads,
+                                float* dsum, hipStream_t stream) {
+    const int g = d / heads / 8;   // 16-byte chunks per head: 4, 8 or 16
+    if (g < 1 || (g & (g - 1)) != 0 || 64 % g != 0 || rows < 0) return hipErrorInvalidValue;
+    const int64_t n = rows * (d / 8);
+    if (n == 0) return hipSuccess;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(bwd_dsum_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const uint4*>(dO), static_cast<const uint4*>(O), n, g, dsum);
+    return hipGetLastError();
+}
 
 hipError_t launch_bwd_attn_bf16(const BwdArgs& a, bool sep, int64_t q_items, int64_t k_items,
                                 hipStream_t stream) {

@@ -112,6 +112,10 @@ struct BwdArgs {
 };
 hipError_t launch_bwd_attn_bf16(const BwdArgs& a, bool sep, int64_t q_items, int64_t k_items,
                                 hipStream_t stream);
+// dsum[row][h] = <dO_row, O_row> over head h's features (bf16 [rows][d], rows
+// 16-byte aligned, d/heads in {32, 64, 128}; fp32 sums in a fixed order)
+hipError_t launch_bwd_dsum_bf16(const void* dO, const void* O, int64_t rows, int d, int heads,
+                                float* dsum, hipStream_t stream);
 // vis[c] = cu_kv[r] + clamp(len[c], 0, L_r) for each candidate c of request r
 hipError_t launch_prefix_vis(const int* cu_kv, const int* cu_cand, const int* len, int R,
                              int total_cand, int* vis, hipStream_t stream);

@@ -28,7 +28,7 @@ EXPORTED = ("xattn_create", "xattn_destroy", "xattn_workspace_size", "xattn_forw
             "xattn_last_error", "xattn_forward_prefix", "xattn_attend_q_prefix",
             "xattn_backward_workspace_size", "xattn_backward", "xattn_codec_encode",
             "xattn_codec_fold_query_weights", "xattn_forward_codec", "xattn_forward_path",
-            "xattn_codec_workspace_size")
+            "xattn_codec_workspace_size", "xattn_forward_train", "xattn_backward_saved")
 
 # xattn_path values (include/xattn.h)
 PATH_SINGLE, PATH_GEMM, PATH_FP32, PATH_SHORT = 1, 2, 3, 4
@@ -117,6 +117,12 @@ def lib():
         L.xattn_backward.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, P, P, P, P,
                                      P, SZ, P]
         L.xattn_backward.restype = ctypes.c_int
+        L.xattn_forward_train.argtypes = [P, P, P, P, P, P, P, P, I32, I32, I32, I32, P, P, P, SZ,
+                                          P]
+        L.xattn_forward_train.restype = ctypes.c_int
+        L.xattn_backward_saved.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, P,
+                                           P, P, P, P, SZ, P]
+        L.xattn_backward_saved.restype = ctypes.c_int
         CB = ctypes.POINTER(CodebookStruct)
         L.xattn_codec_encode.argtypes = [P, CB, I32, P, I32, P, P, P]
         L.xattn_codec_encode.restype = ctypes.c_int
@@ -263,6 +269,37 @@ class XAttn:
                   workspace.numel(), _stream(Z.device, stream)))
         return O
 
+    def forward_train(self, Z, W_Q, K, V, cu_seqlens_kv, cu_cand, heads: int, O=None,
+                      lse=None, workspace=None, stream=None, cand_kv_len=None):
+        """(O, lse): forward() that also keeps each row's base-2 log softmax
+        normaliser per head, lse [total_cand, q, heads] fp32, for
+        backward(..., O=O, lse=lse) (include/xattn.h, xattn_forward_train)."""
+        d, q, dt = self.d_model, self.q, self.torch_dtype
+        total_cand, total_kv = Z.shape[0], K.shape[0]
+        R = cu_seqlens_kv.numel() - 1
+        self._check_tensor("Z", Z, dt, (total_cand, q, d))
+        self._check_tensor("W_Q", W_Q, dt, (q, d, d))
+        self._check_tensor("K", K, dt, (total_kv, d))
+        if V is not None:
+            self._check_tensor("V", V, dt, (total_kv, d))
+        self._check_tensor("cu_seqlens_kv", cu_seqlens_kv, torch.int32, (R + 1,))
+        self._check_tensor("cu_cand", cu_cand, torch.int32, (R + 1,))
+        if cand_kv_len is not None:
+            self._check_tensor("cand_kv_len", cand_kv_len, torch.int32, (total_cand,))
+        if O is None:
+            O = torch.empty((total_cand, q, d), dtype=dt, device=Z.device)
+        if lse is None:
+            lse = torch.empty((total_cand, q, heads), dtype=torch.float32, device=Z.device)
+        self._check_tensor("O", O, dt, (total_cand, q, d))
+        self._check_tensor("lse", lse, torch.float32, (total_cand, q, heads))
+        if workspace is None:
+            workspace = self.alloc_workspace(R, total_cand, heads)
+        _check(lib().xattn_forward_train(
+            self._h, _ptr(Z), _ptr(W_Q), _ptr(K), _ptr(V), _ptr(cu_seqlens_kv), _ptr(cu_cand),
+            _ptr(cand_kv_len), R, total_cand, total_kv, heads, _ptr(O), _ptr(lse),
+            _ptr(workspace), workspace.numel(), _stream(Z.device, stream)))
+        return O, lse
+
     def attend(self, Z, W_Q, K, V, cu_seqlens_kv, cu_cand, heads: int, workspace, O=None,
                stream=None) -> torch.Tensor:
         """Projection + attention, reusing the plan a previous forward()/plan() of
@@ -306,12 +343,14 @@ class XAttn:
                                                        total_kv, heads))
 
     def backward(self, Z, W_Q, K, V, dO, cu_seqlens_kv, cu_cand, heads: int, workspace=None,
-                 out=None, stream=None, cand_kv_len=None) -> dict:
+                 out=None, stream=None, cand_kv_len=None, O=None, lse=None) -> dict:
         """Gradients of <dO, O> for O = forward(Z, W_Q, K, V, ...) (see
         include/xattn.h, xattn_backward): returns {"dZ", "dW_Q" (fp32), "dK"
         (dH in shared mode), "dV" (None in shared mode)}; `out` may supply
         those tensors.  cand_kv_len: the per-candidate prefix of
-        forward(..., cand_kv_len=...)."""
+        forward(..., cand_kv_len=...).  O and lse: the outputs of
+        forward_train() on the same inputs, which replace the recomputed
+        forward statistics (xattn_backward_saved)."""
         d, q, dt = self.d_model, self.q, self.torch_dtype
         total_cand, total_kv = Z.shape[0], K.shape[0]
         R = cu_seqlens_kv.numel() - 1
@@ -345,6 +384,17 @@ class XAttn:
         if workspace is None:
             n = self.backward_workspace_size(R, total_cand, total_kv, heads)
             workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+        if O is not None or lse is not None:
+            if O is None or lse is None:
+                raise ValueError("the stored statistics need both O and lse")
+            self._check_tensor("O", O, dt, (total_cand, q, d))
+            self._check_tensor("lse", lse, torch.float32, (total_cand, q, heads))
+            _check(lib().xattn_backward_saved(
+                self._h, _ptr(Z), _ptr(W_Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(O), _ptr(lse),
+                _ptr(cu_seqlens_kv), _ptr(cu_cand), _ptr(cand_kv_len), R, total_cand, total_kv,
+                heads, _ptr(out["dZ"]), _ptr(out["dW_Q"]), _ptr(out["dK"]), _ptr(out["dV"]),
+                _ptr(workspace), workspace.numel(), _stream(dev, stream)))
+            return out
         _check(lib().xattn_backward(self._h, _ptr(Z), _ptr(W_Q), _ptr(K), _ptr(V), _ptr(dO),
                                     _ptr(cu_seqlens_kv), _ptr(cu_cand), _ptr(cand_kv_len), R,
                                     total_cand, total_kv, heads, _ptr(out["dZ"]), _ptr(out["dW_Q"]), _ptr(out["dK"]),
