@@ -188,11 +188,10 @@ xattn_status xattn_forward_prefix(xattn_ctx* ctx,
  *     with q_h the bf16 projected query (as the products use it: scaled by
  *     log2(e)/sqrt(d_h) and rounded to bf16); -inf for a row that sees no
  *     memory.
- * O, the workspace and the other arguments as for xattn_forward.  Batches
- * that xattn_forward would send to the short-memory kernel take the
- * projection GEMM and attention kernel here (that kernel keeps no
- * statistics).  bf16 contexts only (XATTN_EUNSUPPORTED otherwise); a NULL
- * lse with total_cand > 0 is XATTN_EINVAL. */
+ * O, the workspace, the launches and the other arguments as for
+ * xattn_forward (or xattn_forward_prefix).  bf16 contexts only
+ * (XATTN_EUNSUPPORTED otherwise); a NULL lse with total_cand > 0 is
+ * XATTN_EINVAL. */
 xattn_status xattn_forward_train(xattn_ctx* ctx,
                                  const void* Z, const void* W_Q,
                                  const void* K, const void* V,

@@ -373,8 +373,8 @@ xattn_status run_forward(Mode mode, xattn_ctx* ctx, const void* Z, const void* W
         a.heads = heads;
         a.O = O;
         a.cand_len = cand_len;
-        a.lse = lse;   // the short-memory kernel keeps no statistics
-        if (mode != Mode::kAttendQ && !cand_len && !lse && short_shape(c, R, total_kv, heads)) {
+        a.lse = lse;
+        if (mode != Mode::kAttendQ && !cand_len && short_shape(c, R, total_kv, heads)) {
             // projection and attention in one launch; a forward pass also
             // plans the batch in that launch (request order) and stores the
             // plan in the workspace

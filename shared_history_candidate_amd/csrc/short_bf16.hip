@@ -597,6 +597,11 @@ __global__ __launch_bounds__(NT) void short_bf16_kernel(AttnArgs a, ShortCodec c
             const int h = (u / C::FP) >> 1, urb = (u / C::FP) & 1, e0 = (u % C::FP) * C::EBW * 32;
             const float l = l_run[k] + xor32(l_run[k]);
             const float inv = l > 0.f ? 1.f / l : 0.f;
+            // the row's log2 softmax normaliser (exp2 units of the scaled
+            // scores), kept for a backward pass, from one lane per row
+            if (a.lse && u % C::FP == 0 && g == 0 && urb * 32 + l32 < nr)
+                a.lse[((size_t)(cb + urb * 32 + l32) * q + cur.s) * a.heads + h] =
+                    l > 0.f ? m_run[k] + __builtin_amdgcn_logf(l) : -INFINITY;   // v_log_f32 is log2
             const int off = ((urb * 32 + l32) * q * D + h * DH + e0 + 4 * g) * 2;
 #pragma unroll
             for (int eb = 0; eb < C::EBW; ++eb)

@@ -98,8 +98,7 @@ def test_forward_train_output_and_lse(name):
 @pytest.mark.parametrize("mode", ["shared", "separate"])
 @pytest.mark.parametrize("dh,heads", [(32, 4), (64, 2), (128, 2)])
 def test_forward_train_edge_shapes(mode, dh, heads):
-    """Ragged tails, a request without memory rows (lse = -inf, O = 0) and the
-    short-memory shape, which the training forward sends to the other path."""
+    """Ragged tails and a request without memory rows (lse = -inf, O = 0)."""
     wl = W.custom("edge", [1, 0, 31, 65, 1023, 300], [1, 4, 65, 3, 129, 40], q=3,
                   d=dh * heads, heads=heads, dtype="bf16", kv_mode=mode, seed=dh)
     _, _, _, O, lse = _train(wl)
@@ -110,6 +109,9 @@ def test_forward_train_edge_shapes(mode, dh, heads):
 
 
 def test_forward_train_short_memory_shape():
+    """The short-memory kernel's lse (its scale is applied in fp32 to the
+    unscaled scores, so it meets the backward's pre-scaled scores only to
+    within the same bound)."""
     full = W.make("transx", 0)
     wl = W.custom("transx_part", full.lengths[:32], full.cands[:32], q=1, d=full.d,
                   heads=full.heads, dtype="bf16", kv_mode="separate", seed=4)
@@ -171,8 +173,9 @@ def test_backward_saved_prefix_ragged():
 
 
 def test_backward_saved_transx_part():
+    """32 TransX requests: the short-memory kernel stores the statistics."""
     full = W.make("transx", 0)
-    wl = W.custom("transx_part", full.lengths[:16], full.cands[:16], q=1, d=full.d,
+    wl = W.custom("transx_part", full.lengths[:32], full.cands[:32], q=1, d=full.d,
                   heads=full.heads, dtype="bf16", kv_mode="separate", seed=3)
     _check_saved(wl, seed=6, what="transx part")
 
