@@ -350,3 +350,41 @@ def test_codec_host_validation(L):
     assert L.xattn_codec_encode(h, ctypes.byref(good), 4, FAKE, 10, FAKE, FAKE,
                                 None) == X.XATTN_EUNSUPPORTED
     L.xattn_destroy(h)
+
+
+def test_training_pair_host_validation(L):
+    """xattn_forward_train / xattn_backward_saved reject missing or misaligned
+    statistics and fp32 contexts before anything is enqueued."""
+    st, h = _create(L, 256, 3, X.XATTN_BF16, X.XATTN_KV_SHARED)
+    assert st == 0
+    ws = L.xattn_workspace_size(h, 2, 10, 4)
+
+    def fwd(h_=h, lse=FAKE, O=FAKE):
+        return L.xattn_forward_train(h_, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, 2, 10, 20, 4,
+                                     O, lse, FAKE, ws, None)
+
+    assert fwd(h_=None) == X.XATTN_EINVAL
+    assert fwd(lse=None) == X.XATTN_EINVAL
+    assert fwd(O=None) == X.XATTN_EINVAL
+    need = L.xattn_backward_workspace_size(h, 2, 10, 20, 4)
+
+    def bwd(h_=h, O=FAKE, lse=FAKE, dO=FAKE):
+        return L.xattn_backward_saved(h_, FAKE, FAKE, FAKE, None, dO, O, lse, FAKE, FAKE, None,
+                                      2, 10, 20, 4, FAKE, FAKE, FAKE, None, FAKE, need, None)
+
+    assert bwd(h_=None) == X.XATTN_EINVAL
+    assert bwd(O=None) == X.XATTN_EINVAL
+    assert bwd(lse=None) == X.XATTN_EINVAL
+    assert bwd(O=ctypes.c_void_p(0x10008)) == X.XATTN_EINVAL     # O not 16-byte aligned
+    assert bwd(dO=ctypes.c_void_p(0x10004)) == X.XATTN_EINVAL    # dO not 16-byte aligned
+    L.xattn_destroy(h)
+    st, h = _create(L, 64, 2, X.XATTN_FP32, X.XATTN_KV_SHARED)
+    assert st == 0
+    ws = L.xattn_workspace_size(h, 2, 10, 2)
+    assert L.xattn_forward_train(h, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, 2, 10, 20, 2, FAKE,
+                                 FAKE, FAKE, ws, None) == X.XATTN_EUNSUPPORTED
+    need = L.xattn_backward_workspace_size(h, 2, 10, 20, 2)
+    assert L.xattn_backward_saved(h, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                  2, 10, 20, 2, FAKE, FAKE, FAKE, None, FAKE, need,
+                                  None) == X.XATTN_EUNSUPPORTED
+    L.xattn_destroy(h)
