@@ -4,15 +4,23 @@
 One step = one xattn_forward call over one batch of synthetic inputs resident
 in HBM.  For small batches (at most 16 requests, model width at most 256)
 that is a single kernel that plans the batch, projects its queries and runs
-the attention; otherwise it is the projection GEMM (which also runs the
-planner) followed by the attention kernel.  Default workload: the ReST-like
-serving batch (8 requests, history length U{512..1024}, d = 256 as 4 heads x
-64, 256 candidates x 3 query tokens, bf16).
+the attention; for batches of short memories on a 256-wide model it is the
+short-memory kernel; otherwise it is the projection GEMM (which also runs the
+planner) followed by the attention kernel.  Default workload: the long
+history (4 requests of 16384 memory rows, d = 512 as 8 heads x 64, 512
+candidates x 3 query tokens, K = V = H, bf16), the largest single-GPU batch
+by work: the ReST length and width scaling point (ReST reading note, s.5.3).
 
 Prints one JSON line with the whole-step throughput (candidate-queries/s),
 the dominant kernel's roofline fraction (its average launch duration measured
-with HIP events on the launch stream), and the fp64 CPU oracle timed on a
-bounded sample of the same workload on this host's cores.
+with HIP events on the launch stream), the fp64 CPU oracle timed on a bounded
+sample of the same workload on this host's cores, and the same forward
+measurement for the other benchmark batches (field "other_workloads").
+
+Timing.  Every timed loop makes C-ABI calls whose arguments were marshalled
+once (BoundCall), so host-side checks add nothing between kernels.  Before
+the W warm-up steps the step runs untimed for --settle-ms so that the clocks
+have left their idle state; the K timed steps follow the W warm-up steps.
 """
 import argparse
 import hashlib
@@ -48,7 +56,11 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=500)
     p.add_argument("--warmup", type=int, default=200)
-    p.add_argument("--config", default="rest", choices=CONFIGS)
+    p.add_argument("--config", default="long", choices=CONFIGS)
+    p.add_argument("--settle-ms", type=float, default=300.0,
+                   help="untimed run of the step before the warm-up steps (clock ramp)")
+    p.add_argument("--only", action="store_true",
+                   help="measure --config alone (no other_workloads field)")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle baseline sample")
@@ -307,6 +319,127 @@ def calib_copy(mib):
                       "copy_gbs": round(2.0 * n / (ms * 1e-3) / 1e9, 1)}))
 
 
+def settle(step, stream, ms):
+    """Run step untimed for about ms milliseconds of device time (clocks
+    leave their idle state; the timed loops then see a steady clock)."""
+    import torch
+    if ms <= 0:
+        return
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    done, n = 0.0, 4
+    while done < ms:
+        a.record(stream)
+        for _ in range(n):
+            step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        dt = a.elapsed_time(b)
+        done += dt
+        n = min(4096, n * 2)
+
+
+def timed_loop(fn, stream, n):
+    """Device time of n back-to-back calls of fn between one HIP event pair on
+    the launch stream, per call (an event pair per call would add its own
+    ~1-2 us to every call)."""
+    import torch
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(n):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def forward_setup(ctx, wl, t, ws, O, stream, cut=None):
+    """Bound calls of the forward step and of its kernels alone for one batch:
+    (step, kernels) with kernels = {name: (bound call, flops, bytes)} for the
+    kernels a step launches, and the path taken."""
+    import torch
+    from shared_history_candidate_amd import xattn as X
+    path = ctx.forward_path(wl.R, wl.total_cand, wl.total_kv, wl.heads)
+    launches = ctx.forward_launches(wl.R, wl.total_cand, wl.total_kv, wl.heads)
+    step = ctx.forward(t["Z"], t["W_Q"], t["K"], t["V"], t["cu_kv"], t["cu_cand"], wl.heads,
+                       O=O, workspace=ws, stream=stream, cand_kv_len=cut, bind=True)
+    step()   # the plan the kernels alone read below
+    if cut is None and path == X.PATH_SHORT:
+        # one kernel plans the batch, projects and attends: the path's work
+        kernels = {"short": (step, wl.flops(), wl.bytes())}
+    elif cut is None and launches == 1:
+        # the attention kernel plans the batch and projects its own queries
+        kernels = {"fused": (step, wl.flops(), wl.bytes())}
+    else:
+        Qbuf = torch.empty_like(O)
+        proj = ctx.project(t["Z"], t["W_Q"], Q=Qbuf, stream=stream, bind=True)
+        proj()
+        attn = ctx.attend_q(Qbuf, t["K"], t["V"], t["cu_kv"], t["cu_cand"], wl.heads, ws, O=O,
+                            stream=stream, cand_kv_len=cut, bind=True)
+        attn.keep = Qbuf   # the bound call reads this buffer
+        kv_arg = cut.cpu().numpy() if cut is not None else None
+        kernels = {("prefix" if cut is not None else "attention"):
+                       (attn, wl.flops_attention(kv_arg), wl.bytes_attention(kv_arg)),
+                   "projection": (proj, wl.flops_projection(), wl.bytes_projection())}
+    return step, kernels, path
+
+
+def measure_forward(ctx, wl, t, ws, O, stream, steps, warmup, settle_ms, config_name, cut=None):
+    """ms per forward step and the roofline entry of its dominant kernel
+    (the other kernel, if any, in other_kernel)."""
+    step, kernels, path = forward_setup(ctx, wl, t, ws, O, stream, cut)
+    settle(step, stream, settle_ms)
+    for _ in range(warmup):
+        step()
+    ms_per_step = timed_loop(step, stream, steps)
+    entries = {}
+    for name, (fn, flops, nbytes) in kernels.items():
+        kms = ms_per_step if fn is step else timed_loop(fn, stream, steps)
+        entries[name] = dict(roofline(flops, nbytes, kms, wl.dtype), kernel_ms=round(kms, 5),
+                             algorithmic_flops=flops, algorithmic_bytes=nbytes,
+                             traffic=traffic_for(name, config_name), kernel=name)
+    dominant = max(entries, key=lambda k: entries[k]["kernel_ms"])
+    roof = dict(entries[dominant])
+    others = [v for k, v in entries.items() if k != dominant]
+    roof["other_kernel"] = others[0] if others else None
+    if roof["kernel_ms"] > ms_per_step * 1.001:
+        raise RuntimeError("kernel time %.5f ms exceeds the step time %.5f ms: the timing is "
+                           "not trustworthy" % (roof["kernel_ms"], ms_per_step))
+    return ms_per_step, roof, path
+
+
+def other_workloads(args, X, W, torch):
+    """The forward measurement of every other benchmark batch (shorter loops,
+    no CPU baseline): one small dict per workload."""
+    out = []
+    stream = torch.cuda.current_stream()
+    for name in CONFIGS:
+        if name in (args.config, "tiny"):
+            continue
+        wl = W.make(name, args.seed)
+        ctx = X.XAttn(wl.d, wl.q, wl.dtype, wl.kv_mode)
+        t = X.to_device(wl)
+        ws = ctx.alloc_workspace(wl.R, wl.total_cand, wl.heads)
+        O = torch.empty((wl.total_cand, wl.q, wl.d), dtype=ctx.torch_dtype, device="cuda")
+        n = max(20, min(args.steps, 200))
+        ms, roof, path = measure_forward(ctx, wl, t, ws, O, stream, n, max(args.warmup, 5),
+                                         args.settle_ms / 3, name)
+        out.append({"workload": wl.name, "steps": n, "ms_per_step": round(ms, 5),
+                    "value": round(wl.rows / (ms * 1e-3), 1), "unit": "candidate-queries/s",
+                    "kernel": roof["kernel"], "kernel_ms": roof["kernel_ms"],
+                    "bound": roof["bound"], "achieved": roof["achieved"],
+                    "unit_roofline": roof["unit"], "frac": roof["frac"],
+                    "traffic": roof["traffic"]})
+        print("bench: %s %.4f ms/step, %s %.4f ms (%.1f %% of %s peak)" %
+              (wl.name, ms, roof["kernel"], roof["kernel_ms"], 100 * roof["frac"], roof["bound"]),
+              file=sys.stderr, flush=True)
+        del ctx, t, ws, O
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -324,7 +457,7 @@ def main():
         micro()
         return
 
-    import numpy as np
+    import numpy as np  # noqa: F401
     import torch
     from shared_history_candidate_amd import workloads as W
     from shared_history_candidate_amd import xattn as X
@@ -337,196 +470,139 @@ def main():
     ws = ctx.alloc_workspace(wl.R, wl.total_cand, wl.heads)
     O = torch.empty((wl.total_cand, wl.q, wl.d), dtype=ctx.torch_dtype, device="cuda")
     stream = torch.cuda.current_stream()
+    kv_len = None
+    others = None
 
-    if args.stage == "output":
-        wgo, wo = W.output_weights(wl, args.seed + 1)
-        dt = ctx.torch_dtype
-        up = lambda a: torch.from_numpy(a).to("cuda").to(dt).contiguous()
-        Wgo_d, Wo_d, O_in = up(wgo), up(wo), up(W.attention_like(wl, args.seed + 2))
+    if args.stage in ("attention", "prefix"):
+        cl = None
+        if args.stage == "prefix":
+            # per-candidate prefix lengths: sorted draws from U{0..L_r} per request
+            kv_len = W.prefix_lengths(wl, args.seed + 3, out_of_range=False)
+            cl = torch.from_numpy(kv_len).to("cuda")
+        ms_per_step, roof, path = measure_forward(ctx, wl, t, ws, O, stream, args.steps,
+                                                  args.warmup, args.settle_ms, args.config, cl)
+        print("bench: %d steps, %.4f ms/step; %s %.4f ms per launch" %
+              (args.steps, ms_per_step, roof["kernel"], roof["kernel_ms"]),
+              file=sys.stderr, flush=True)
+        if roof["other_kernel"]:
+            print("bench: %s %.4f ms per launch" % (roof["other_kernel"]["kernel"],
+                                                   roof["other_kernel"]["kernel_ms"]),
+                  file=sys.stderr, flush=True)
+        if path == X.PATH_SHORT and args.stage == "attention":
+            # the same kernel over the stored plan (no planning), for reference
+            att = ctx.forward(t["Z"], t["W_Q"], t["K"], t["V"], t["cu_kv"], t["cu_cand"],
+                              wl.heads, O=O, workspace=ws, stream=stream, plan=False, bind=True)
+            print("bench: short-memory kernel over a stored plan %.4f ms" %
+                  timed_loop(att, stream, args.steps), file=sys.stderr, flush=True)
+        if args.stage == "attention" and not args.only:
+            others = other_workloads(args, X, W, torch)
+    else:
+        if args.stage == "output":
+            wgo, wo = W.output_weights(wl, args.seed + 1)
+            dt = ctx.torch_dtype
+            up = lambda a: torch.from_numpy(a).to("cuda").to(dt).contiguous()
+            Wgo_d, Wo_d, O_in = up(wgo), up(wo), up(W.attention_like(wl, args.seed + 2))
 
-        def step():
-            ctx.output(t["Z"], Wgo_d, O_in, Wo_d, ws, Y=O, stream=stream)
-    elif args.stage in ("backward", "backward_prefix"):
-        dO_d = torch.from_numpy(W.output_grad(wl, args.seed + 4)).to("cuda").to(
-            ctx.torch_dtype).contiguous()
-        kv_len = (W.prefix_lengths(wl, args.seed + 3, out_of_range=False)
-                  if args.stage == "backward_prefix" else None)
-        cl = torch.from_numpy(kv_len).to("cuda") if kv_len is not None else None
-        grads = ctx.backward(t["Z"], t["W_Q"], t["K"], t["V"], dO_d, t["cu_kv"], t["cu_cand"],
-                             wl.heads, cand_kv_len=cl)
-        bws = torch.empty(max(ctx.backward_workspace_size(wl.R, wl.total_cand, wl.total_kv,
-                                                          wl.heads), 256),
-                          dtype=torch.uint8, device="cuda")
+            def step():
+                ctx.output(t["Z"], Wgo_d, O_in, Wo_d, ws, Y=O, stream=stream)
+        elif args.stage in ("backward", "backward_prefix"):
+            dO_d = torch.from_numpy(W.output_grad(wl, args.seed + 4)).to("cuda").to(
+                ctx.torch_dtype).contiguous()
+            kv_len = (W.prefix_lengths(wl, args.seed + 3, out_of_range=False)
+                      if args.stage == "backward_prefix" else None)
+            cl = torch.from_numpy(kv_len).to("cuda") if kv_len is not None else None
+            grads = ctx.backward(t["Z"], t["W_Q"], t["K"], t["V"], dO_d, t["cu_kv"],
+                                 t["cu_cand"], wl.heads, cand_kv_len=cl)
+            bws = torch.empty(max(ctx.backward_workspace_size(wl.R, wl.total_cand, wl.total_kv,
+                                                              wl.heads), 256),
+                              dtype=torch.uint8, device="cuda")
 
-        def step():
-            ctx.backward(t["Z"], t["W_Q"], t["K"], t["V"], dO_d, t["cu_kv"], t["cu_cand"],
-                         wl.heads, workspace=bws, out=grads, stream=stream, cand_kv_len=cl)
-
-        # the training pair: a forward that keeps the normalisers, and the
-        # backward that reuses them (bf16 only)
-        train_pair = wl.dtype == "bf16"
-        if train_pair:
-            O_tr, lse_tr = ctx.forward_train(t["Z"], t["W_Q"], t["K"], t["V"], t["cu_kv"],
-                                             t["cu_cand"], wl.heads, workspace=ws,
-                                             cand_kv_len=cl)
-
-            def step_train_fwd():
-                ctx.forward_train(t["Z"], t["W_Q"], t["K"], t["V"], t["cu_kv"], t["cu_cand"],
-                                  wl.heads, O=O_tr, lse=lse_tr, workspace=ws, stream=stream,
-                                  cand_kv_len=cl)
-
-            def step_saved():
+            def step():
                 ctx.backward(t["Z"], t["W_Q"], t["K"], t["V"], dO_d, t["cu_kv"], t["cu_cand"],
-                             wl.heads, workspace=bws, out=grads, stream=stream, cand_kv_len=cl,
-                             O=O_tr, lse=lse_tr)
-    elif args.stage == "codec":
-        # memory published as codes + norms (encoded once, outside the step)
-        budget = int(round(args.codec_bits * wl.d_h / 32.0)) * 32
-        books = [W.timing_codebook(wl.heads, wl.d_h, budget, args.seed + 5 + i) for i in range(2)]
-        cbs = [X.Codebook(b["bits"], b["center"], b["half"], b["rot"], b["budget"]) for b in books]
-        kc, kn = ctx.codec_encode(cbs[0], t["K"])
-        vc, vn = ctx.codec_encode(cbs[1], t["V"]) if t["V"] is not None else (None, None)
-        cbv = cbs[1] if t["V"] is not None else None
-        Wr = ctx.codec_fold(cbs[0], t["W_Q"])
-        codec_bytes = (kc.numel() + kn.numel()) * 4 * (2 if cbv is not None else 1)
-        # a workspace with room for the decoded memory: the memory is decoded
-        # once per call where the short-memory kernel does not take the batch
-        cws = torch.empty(max(ctx.codec_workspace_size(wl.R, wl.total_cand, wl.total_kv,
-                                                       wl.heads), 256),
-                          dtype=torch.uint8, device="cuda")
+                             wl.heads, workspace=bws, out=grads, stream=stream, cand_kv_len=cl)
 
-        def step():
-            ctx.forward_codec(cbs[0], cbv, t["Z"], Wr, kc, kn, vc, vn, t["cu_kv"], t["cu_cand"],
-                              wl.heads, O=O, workspace=cws, stream=stream)
+            # the training pair: a forward that keeps the normalisers, and the
+            # backward that reuses them (bf16 only)
+            train_pair = wl.dtype == "bf16"
+            if train_pair:
+                O_tr, lse_tr = ctx.forward_train(t["Z"], t["W_Q"], t["K"], t["V"], t["cu_kv"],
+                                                 t["cu_cand"], wl.heads, workspace=ws,
+                                                 cand_kv_len=cl)
 
-        def step_lds():
-            ctx.forward_codec(cbs[0], cbv, t["Z"], Wr, kc, kn, vc, vn, t["cu_kv"], t["cu_cand"],
-                              wl.heads, O=O, workspace=ws, stream=stream)
-    elif args.stage == "prefix":
-        # per-candidate prefix lengths: sorted draws from U{0..L_r} per request
-        kv_len = W.prefix_lengths(wl, args.seed + 3, out_of_range=False)
-        cl = torch.from_numpy(kv_len).to("cuda")
+                def step_train_fwd():
+                    ctx.forward_train(t["Z"], t["W_Q"], t["K"], t["V"], t["cu_kv"],
+                                      t["cu_cand"], wl.heads, O=O_tr, lse=lse_tr, workspace=ws,
+                                      stream=stream, cand_kv_len=cl)
 
-        def step():
-            ctx.forward(t["Z"], t["W_Q"], t["K"], t["V"], t["cu_kv"], t["cu_cand"], wl.heads,
-                        O=O, workspace=ws, stream=stream, cand_kv_len=cl)
-    else:
-        def step():
-            ctx.forward(t["Z"], t["W_Q"], t["K"], t["V"], t["cu_kv"], t["cu_cand"], wl.heads,
-                        O=O, workspace=ws, stream=stream)
+                def step_saved():
+                    ctx.backward(t["Z"], t["W_Q"], t["K"], t["V"], dO_d, t["cu_kv"],
+                                 t["cu_cand"], wl.heads, workspace=bws, out=grads,
+                                 stream=stream, cand_kv_len=cl, O=O_tr, lse=lse_tr)
+        elif args.stage == "codec":
+            # memory published as codes + norms (encoded once, outside the step)
+            budget = int(round(args.codec_bits * wl.d_h / 32.0)) * 32
+            books = [W.timing_codebook(wl.heads, wl.d_h, budget, args.seed + 5 + i)
+                     for i in range(2)]
+            cbs = [X.Codebook(b["bits"], b["center"], b["half"], b["rot"], b["budget"])
+                   for b in books]
+            kc, kn = ctx.codec_encode(cbs[0], t["K"])
+            vc, vn = ctx.codec_encode(cbs[1], t["V"]) if t["V"] is not None else (None, None)
+            cbv = cbs[1] if t["V"] is not None else None
+            Wr = ctx.codec_fold(cbs[0], t["W_Q"])
+            codec_bytes = (kc.numel() + kn.numel()) * 4 * (2 if cbv is not None else 1)
+            # a workspace with room for the decoded memory: the memory is decoded
+            # once per call where the short-memory kernel does not take the batch
+            cws = torch.empty(max(ctx.codec_workspace_size(wl.R, wl.total_cand, wl.total_kv,
+                                                           wl.heads), 256),
+                              dtype=torch.uint8, device="cuda")
 
-    for _ in range(args.warmup):
+            def step():
+                ctx.forward_codec(cbs[0], cbv, t["Z"], Wr, kc, kn, vc, vn, t["cu_kv"],
+                                  t["cu_cand"], wl.heads, O=O, workspace=cws, stream=stream)
+
+            def step_lds():
+                ctx.forward_codec(cbs[0], cbv, t["Z"], Wr, kc, kn, vc, vn, t["cu_kv"],
+                                  t["cu_cand"], wl.heads, O=O, workspace=ws, stream=stream)
+
+        # these stages are timed as one unit per call (several launches; the
+        # per-kernel split is in the kernel traces)
         step()
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for _ in range(args.steps):
-        step()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / args.steps
-    print("bench: %d steps, %.4f ms/step" % (args.steps, ms_per_step), file=sys.stderr, flush=True)
+        settle(step, stream, args.settle_ms)
+        for _ in range(args.warmup):
+            step()
+        ms_per_step = timed_loop(step, stream, args.steps)
+        print("bench: %d steps, %.4f ms/step" % (args.steps, ms_per_step), file=sys.stderr,
+              flush=True)
 
-    # Each kernel alone: K back-to-back launches between one HIP event pair on
-    # the launch stream, averaged (an event pair per launch would add its own
-    # ~1-2 us to every launch).  The projection writes a query buffer and the
-    # attention kernel reads it with the plan the last step left in the
-    # workspace.
-    Qbuf = torch.empty_like(O)
+        def entry(kernel, flops, nbytes, ms):
+            return dict(roofline(flops, nbytes, ms, wl.dtype), kernel_ms=round(ms, 5),
+                        algorithmic_flops=flops, algorithmic_bytes=nbytes,
+                        traffic=traffic_for(kernel, args.config), kernel=kernel,
+                        other_kernel=None)
 
-    def per_launch_ms(fn):
-        fn()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(args.steps):
-            fn()
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / args.steps
-
-    launches = ctx.forward_launches(wl.R, wl.total_cand, wl.total_kv, wl.heads)
-    path = ctx.forward_path(wl.R, wl.total_cand, wl.total_kv, wl.heads)
-    if args.stage != "attention":
-        launches = path = 0
-
-    def entry(kernel, flops, nbytes, ms):
-        return dict(roofline(flops, nbytes, ms, wl.dtype), kernel_ms=round(ms, 5),
-                    algorithmic_flops=flops, algorithmic_bytes=nbytes,
-                    traffic=traffic_for(kernel, args.config), kernel=kernel)
-
-    if args.stage in ("backward", "backward_prefix"):
-        # eight launches (plans, projection, statistics, dQ, dK/dV, transpose,
-        # dZ, dW_Q) timed as one unit; the per-kernel split is in the trace
-        bwd_ms = per_launch_ms(step)
-        print("bench: backward %.4f ms" % bwd_ms, file=sys.stderr, flush=True)
-        roof = entry("backward", wl.flops_backward(kv_len), wl.bytes_backward(), bwd_ms)
-        roof["other_kernel"] = None
-        if train_pair:
-            tf_ms, sv_ms = per_launch_ms(step_train_fwd), per_launch_ms(step_saved)
-            print("bench: training forward (keeps lse) %.4f ms; backward from the stored "
-                  "statistics %.4f ms" % (tf_ms, sv_ms), file=sys.stderr, flush=True)
-            roof["training_forward_ms"] = round(tf_ms, 5)
-            roof["saved_statistics_backward_ms"] = round(sv_ms, 5)
-    elif args.stage == "codec":
-        # the coded forward timed as one unit; bytes count codes + norms for
-        # the memory.  For reference, the same call with the plain workspace
-        # (each memory tile reconstructed in LDS by every query tile).
-        codec_ms = per_launch_ms(step)
-        lds_ms = per_launch_ms(step_lds)
-        print("bench: codec forward %.4f ms (memory %.2f MB coded vs %.2f MB bf16); "
-              "with the plain workspace %.4f ms" %
-              (codec_ms, codec_bytes / 1e6,
-               wl.total_kv * wl.d * 2 * (2 if wl.kv_mode == "separate" else 1) / 1e6, lds_ms),
-              file=sys.stderr, flush=True)
-        b = 2.0 * (2 * wl.rows * wl.d + wl.q * wl.d * wl.d) + codec_bytes
-        roof = entry("codec", wl.flops(), b, codec_ms)
-        roof["other_kernel"] = None
-    elif args.stage == "output":
-        # gate GEMM (sigmoid and product with O in its epilogue) + W_o GEMM
-        out_ms = per_launch_ms(step)
-        print("bench: output stage %.4f ms" % out_ms, file=sys.stderr, flush=True)
-        roof = entry("output", wl.flops_output(), wl.bytes_output(), out_ms)
-        roof["other_kernel"] = None
-    elif path == X.PATH_SHORT:
-        # One kernel plans the batch, projects and attends: its work is the
-        # whole path's (xattn_attend over the stored plan runs it without the
-        # planning, shown for reference).
-        short_ms = per_launch_ms(step)
-        attend_ms = per_launch_ms(lambda: ctx.attend(t["Z"], t["W_Q"], t["K"], t["V"],
-                                                     t["cu_kv"], t["cu_cand"], wl.heads, ws,
-                                                     O=O, stream=stream))
-        print("bench: short-memory kernel %.4f ms per launch (%.4f ms over a stored plan)" %
-              (short_ms, attend_ms), file=sys.stderr, flush=True)
-        roof = entry("short", wl.flops(), wl.bytes(), short_ms)
-        roof["other_kernel"] = None
-    elif launches == 1:
-        # The step is one kernel: the attention kernel plans the batch and
-        # projects its own queries.  Its work is the whole path's.
-        fused_ms = per_launch_ms(step)
-        print("bench: single launch %.4f ms" % fused_ms, file=sys.stderr, flush=True)
-        roof = entry("fused", wl.flops(), wl.bytes(), fused_ms)
-        roof["other_kernel"] = None
-    else:
-        cut = cl if args.stage == "prefix" else None
-        kv_arg = kv_len if args.stage == "prefix" else None
-        attn_name = "prefix" if args.stage == "prefix" else "attention"
-        proj_ms = per_launch_ms(lambda: ctx.project(t["Z"], t["W_Q"], Q=Qbuf, stream=stream))
-        attn_ms = per_launch_ms(lambda: ctx.attend_q(Qbuf, t["K"], t["V"], t["cu_kv"],
-                                                     t["cu_cand"], wl.heads, ws, O=O,
-                                                     stream=stream, cand_kv_len=cut))
-        print("bench: projection %.4f ms, attention %.4f ms per launch" % (proj_ms, attn_ms),
-              file=sys.stderr, flush=True)
-        kernels = {
-            "attention": entry(attn_name, wl.flops_attention(kv_arg), wl.bytes_attention(kv_arg),
-                               attn_ms),
-            "projection": entry("projection", wl.flops_projection(), wl.bytes_projection(),
-                                proj_ms),
-        }
-        dominant = max(kernels, key=lambda k: kernels[k]["kernel_ms"])
-        roof = dict(kernels[dominant])
-        roof["other_kernel"] = kernels["projection" if dominant == "attention" else "attention"]
+        if args.stage in ("backward", "backward_prefix"):
+            roof = entry("backward", wl.flops_backward(kv_len), wl.bytes_backward(), ms_per_step)
+            if train_pair:
+                tf_ms = timed_loop(step_train_fwd, stream, args.steps)
+                sv_ms = timed_loop(step_saved, stream, args.steps)
+                print("bench: training forward (keeps lse) %.4f ms; backward from the stored "
+                      "statistics %.4f ms" % (tf_ms, sv_ms), file=sys.stderr, flush=True)
+                roof["training_forward_ms"] = round(tf_ms, 5)
+                roof["saved_statistics_backward_ms"] = round(sv_ms, 5)
+        elif args.stage == "codec":
+            # bytes count codes + norms for the memory.  For reference, the same
+            # call with the plain workspace (each memory tile reconstructed in
+            # LDS by every query tile).
+            lds_ms = timed_loop(step_lds, stream, args.steps)
+            print("bench: codec forward %.4f ms (memory %.2f MB coded vs %.2f MB bf16); "
+                  "with the plain workspace %.4f ms" %
+                  (ms_per_step, codec_bytes / 1e6,
+                   wl.total_kv * wl.d * 2 * (2 if wl.kv_mode == "separate" else 1) / 1e6,
+                   lds_ms), file=sys.stderr, flush=True)
+            b = 2.0 * (2 * wl.rows * wl.d + wl.q * wl.d * wl.d) + codec_bytes
+            roof = entry("codec", wl.flops(), b, ms_per_step)
+        else:
+            roof = entry("output", wl.flops_output(), wl.bytes_output(), ms_per_step)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -552,8 +628,13 @@ def main():
                                                 "lengths (sorted U{0..L_r} per request)",
                              "codec": "forward over a coded memory, %.1f bits per coordinate"
                                       % args.codec_bits}[args.stage]},
+        "timing": "HIP events on the launch stream around K back-to-back C-ABI calls with "
+                  "pre-marshalled arguments (steps, then each kernel of a step alone); "
+                  "%.0f ms untimed settle run before the W warm-up steps" % args.settle_ms,
         "roofline": roof, "cpu_baseline": cpu,
     }
+    if others is not None:
+        line["other_workloads"] = others
     print(json.dumps(line), flush=True)
 
 

@@ -151,6 +151,31 @@ def _check(status: int) -> None:
         raise XAttnError(status, lib().xattn_last_error().decode())
 
 
+class BoundCall:
+    """One C-ABI call with its arguments marshalled once (tensors by data
+    pointer, scalars as ctypes values).  Calling it makes the same call again
+    and raises on a non-OK status.  For tight timing loops, where the per-call
+    argument checks of the methods below would leave host gaps between short
+    kernels; the caller keeps the tensors alive."""
+
+    def __init__(self, fn, args):
+        self._fn = fn
+        self._args = tuple(args)
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st != XATTN_OK:
+            _check(st)
+
+
+def _call(fn, args, bind: bool):
+    """Call fn(*args), or return it as a BoundCall when bind is set."""
+    if bind:
+        return BoundCall(fn, args)
+    _check(fn(*args))
+    return None
+
+
 def _ptr(t: Optional[torch.Tensor]):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
@@ -231,12 +256,14 @@ class XAttn:
     # -- entry points ----------------------------------------------------------
     def forward(self, Z, W_Q, K, V, cu_seqlens_kv, cu_cand, heads: int, O=None,
                 workspace=None, stream=None, plan: bool = True,
-                cand_kv_len=None) -> torch.Tensor:
+                cand_kv_len=None, bind: bool = False) -> torch.Tensor:
         """O = cross-attention of Z's query tokens against their requests' memory
         (see include/xattn.h).  Z [total_cand, q, d], W_Q [q, d, d] output-major,
         K [total_kv, d] (= H), V [total_kv, d] or None, cu_* int32 [R+1].
         cand_kv_len (int32 [total_cand], optional): candidate c sees only the
-        first cand_kv_len[c] memory rows of its request (xattn_forward_prefix)."""
+        first cand_kv_len[c] memory rows of its request (xattn_forward_prefix).
+        With bind=True nothing runs: the checked call comes back as a
+        BoundCall (O and workspace must then be given)."""
         d, q, dt = self.d_model, self.q, self.torch_dtype
         total_cand, total_kv = Z.shape[0], K.shape[0]
         R = cu_seqlens_kv.numel() - 1
@@ -247,6 +274,8 @@ class XAttn:
             self._check_tensor("V", V, dt, (total_kv, d))
         self._check_tensor("cu_seqlens_kv", cu_seqlens_kv, torch.int32, (R + 1,))
         self._check_tensor("cu_cand", cu_cand, torch.int32, (R + 1,))
+        if bind and (O is None or workspace is None):
+            raise ValueError("a bound call needs O and the workspace")
         if O is None:
             O = torch.empty((total_cand, q, d), dtype=dt, device=Z.device)
         self._check_tensor("O", O, dt, (total_cand, q, d))
@@ -258,16 +287,17 @@ class XAttn:
             if not plan:
                 raise ValueError("a per-candidate prefix is only available with planning")
             self._check_tensor("cand_kv_len", cand_kv_len, torch.int32, (total_cand,))
-            _check(lib().xattn_forward_prefix(
-                self._h, _ptr(Z), _ptr(W_Q), _ptr(K), _ptr(V), _ptr(cu_seqlens_kv),
-                _ptr(cu_cand), _ptr(cand_kv_len), R, total_cand, total_kv, heads, _ptr(O),
-                _ptr(workspace), workspace.numel(), _stream(Z.device, stream)))
-            return O
+            b = _call(lib().xattn_forward_prefix,
+                      (self._h, _ptr(Z), _ptr(W_Q), _ptr(K), _ptr(V), _ptr(cu_seqlens_kv),
+                       _ptr(cu_cand), _ptr(cand_kv_len), R, total_cand, total_kv, heads,
+                       _ptr(O), _ptr(workspace), workspace.numel(), _stream(Z.device, stream)),
+                      bind)
+            return b if bind else O
         fn = lib().xattn_forward if plan else lib().xattn_attend
-        _check(fn(self._h, _ptr(Z), _ptr(W_Q), _ptr(K), _ptr(V), _ptr(cu_seqlens_kv),
-                  _ptr(cu_cand), R, total_cand, total_kv, heads, _ptr(O), _ptr(workspace),
-                  workspace.numel(), _stream(Z.device, stream)))
-        return O
+        b = _call(fn, (self._h, _ptr(Z), _ptr(W_Q), _ptr(K), _ptr(V), _ptr(cu_seqlens_kv),
+                       _ptr(cu_cand), R, total_cand, total_kv, heads, _ptr(O), _ptr(workspace),
+                       workspace.numel(), _stream(Z.device, stream)), bind)
+        return b if bind else O
 
     def forward_train(self, Z, W_Q, K, V, cu_seqlens_kv, cu_cand, heads: int, O=None,
                       lse=None, workspace=None, stream=None, cand_kv_len=None):
@@ -308,10 +338,11 @@ class XAttn:
                             workspace=workspace, stream=stream, plan=False)
 
     def attend_q(self, Q, K, V, cu_seqlens_kv, cu_cand, heads: int, workspace, O=None,
-                 stream=None, cand_kv_len=None) -> torch.Tensor:
+                 stream=None, cand_kv_len=None, bind: bool = False) -> torch.Tensor:
         """Attention kernel alone over already-projected queries Q [total_cand, q, d],
         reusing the plan in `workspace`; cand_kv_len as for forward()
-        (xattn_attend_q_prefix)."""
+        (xattn_attend_q_prefix).  bind=True returns the checked call as a
+        BoundCall instead of running it."""
         d, q, dt = self.d_model, self.q, self.torch_dtype
         total_cand, total_kv = Q.shape[0], K.shape[0]
         R = cu_seqlens_kv.numel() - 1
@@ -326,16 +357,16 @@ class XAttn:
         self._check_tensor("O", O, dt, (total_cand, q, d))
         if cand_kv_len is not None:
             self._check_tensor("cand_kv_len", cand_kv_len, torch.int32, (total_cand,))
-            _check(lib().xattn_attend_q_prefix(
-                self._h, _ptr(Q), _ptr(K), _ptr(V), _ptr(cu_seqlens_kv), _ptr(cu_cand),
-                _ptr(cand_kv_len), R, total_cand, total_kv, heads, _ptr(O), _ptr(workspace),
-                workspace.numel(), _stream(Q.device, stream)))
-            return O
-        _check(lib().xattn_attend_q(self._h, _ptr(Q), _ptr(K), _ptr(V), _ptr(cu_seqlens_kv),
-                                    _ptr(cu_cand), R, total_cand, total_kv, heads, _ptr(O),
-                                    _ptr(workspace), workspace.numel(),
-                                    _stream(Q.device, stream)))
-        return O
+            b = _call(lib().xattn_attend_q_prefix,
+                      (self._h, _ptr(Q), _ptr(K), _ptr(V), _ptr(cu_seqlens_kv), _ptr(cu_cand),
+                       _ptr(cand_kv_len), R, total_cand, total_kv, heads, _ptr(O),
+                       _ptr(workspace), workspace.numel(), _stream(Q.device, stream)), bind)
+            return b if bind else O
+        b = _call(lib().xattn_attend_q,
+                  (self._h, _ptr(Q), _ptr(K), _ptr(V), _ptr(cu_seqlens_kv), _ptr(cu_cand), R,
+                   total_cand, total_kv, heads, _ptr(O), _ptr(workspace), workspace.numel(),
+                   _stream(Q.device, stream)), bind)
+        return b if bind else O
 
     def backward_workspace_size(self, num_requests: int, total_cand: int, total_kv: int,
                                 heads: int) -> int:
@@ -479,18 +510,22 @@ class XAttn:
         rr = row_req[: total_cand * self.q] if row_req is not None else None
         return cu_q, rr, tiles[:n], tm.value
 
-    def project(self, Z, W_Q, Q=None, stream=None) -> torch.Tensor:
-        """TSP projection alone: Q[row] = Z[row] . W_Q[row % q] (output-major W_Q)."""
+    def project(self, Z, W_Q, Q=None, stream=None, bind: bool = False) -> torch.Tensor:
+        """TSP projection alone: Q[row] = Z[row] . W_Q[row % q] (output-major W_Q).
+        bind=True returns the checked call as a BoundCall (Q must be given)."""
         d, q, dt = self.d_model, self.q, self.torch_dtype
         total_cand = Z.shape[0]
         self._check_tensor("Z", Z, dt, (total_cand, q, d))
         self._check_tensor("W_Q", W_Q, dt, (q, d, d))
+        if bind and Q is None:
+            raise ValueError("a bound call needs Q")
         if Q is None:
             Q = torch.empty((total_cand, q, d), dtype=dt, device=Z.device)
         self._check_tensor("Q", Q, dt, (total_cand, q, d))
-        _check(lib().xattn_project(self._h, _ptr(Z), _ptr(W_Q), total_cand, _ptr(Q),
-                                   _stream(Z.device, stream)))
-        return Q
+        b = _call(lib().xattn_project,
+                  (self._h, _ptr(Z), _ptr(W_Q), total_cand, _ptr(Q), _stream(Z.device, stream)),
+                  bind)
+        return b if bind else Q
 
     def output(self, Z, W_go, O, W_o, workspace, Y=None, stream=None) -> torch.Tensor:
         """Output gate and projection of Eq. (7):
