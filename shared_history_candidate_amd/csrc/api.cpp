@@ -16,7 +16,8 @@
 
 struct xattn_ctx {
     xattn_config cfg;
-    int n_cu = 0;   // compute units of cfg.device, read on first use
+    xattn::Tuning tune;   // overrides from the environment, read at creation
+    int n_cu = 0;         // compute units of cfg.device, read on first use
 };
 
 namespace {
@@ -39,11 +40,37 @@ xattn_status hip_fail(hipError_t e, const char* what) {
 
 bool bf16_dh_supported(int dh) { return dh == 32 || dh == 64 || dh == 128; }
 
+// The XATTN_* tuning overrides (internal.h), read once per context.
+xattn::Tuning read_tuning() {
+    xattn::Tuning t;
+    if (const char* env = getenv("XATTN_VARIANT")) {
+        int rb = 0, ks = 0;
+        if (sscanf(env, "%d,%d", &rb, &ks) == 2) t.variant_rb = rb, t.variant_ks = ks;
+    }
+    if (const char* env = getenv("XATTN_SHORT")) t.short_path = env[0] == '1' ? 1 : 0;
+    if (const char* env = getenv("XATTN_CODEC_DECODE")) t.codec_decode = env[0] == '0' ? 0 : 1;
+    if (const char* env = getenv("XATTN_CODEC_QW")) {
+        const int v = atoi(env);
+        if (v == 2 || v == 4 || v == 8) t.codec_qw = v;
+    }
+    if (const char* env = getenv("XATTN_FUSED_OUTPUT")) t.fused_output = env[0] == '1' ? 1 : 0;
+    if (const char* env = getenv("XATTN_GEMM")) {
+        int te = 0, tc = 0, kc = 0;
+        if (sscanf(env, "%d,%d,%d", &te, &tc, &kc) == 3) t.gemm_te = te, t.gemm_tc = tc, t.gemm_kc = kc;
+    }
+    if (const char* env = getenv("XATTN_DQ_KS")) {
+        const int v = atoi(env);
+        if (v == 1 || v == 2) t.dq_ks = v;
+    }
+    return t;
+}
+
 // Work-group shape of the bf16 kernel: rb query blocks of 32 candidates and
 // ksplit memory splits (rb * ksplit waves).  Long memories favour splitting
 // the memory so that every SIMD holds several waves; batches with many query
 // tiles favour wide query blocks that share each staged memory tile.
-// XATTN_VARIANT="rb,ksplit" overrides the choice (tuning and tests).
+// The context's XATTN_VARIANT="rb,ksplit" overrides the choice (tuning and
+// tests).
 struct Variant {
     int rb, ksplit;
 };
@@ -59,14 +86,15 @@ bool fused_shape(const xattn_config& c, int R) {
 // Batches of short memories (mean L_r no longer than what LDS holds at once)
 // on a 256-feature bf16 model run the planner and then the short-memory
 // kernel, which projects and attends in one launch (short_bf16.hip); small
-// batches keep the single launch.  XATTN_SHORT=0 / 1 turns the path off / on
-// for every batch it supports (tuning and tests).
-bool short_shape(const xattn_config& c, int R, int total_kv, int heads) {
+// batches keep the single launch.  The context's XATTN_SHORT=0 / 1 turns the
+// path off / on for every batch it supports (tuning and tests).
+bool short_shape(const xattn_ctx* ctx, int R, int total_kv, int heads) {
+    const xattn_config& c = ctx->cfg;
     if (c.dtype != XATTN_BF16 || c.d_model != xattn::kShortD || heads < 1 || c.d_model % heads)
         return false;
     const int dh = c.d_model / heads;
     if (dh != 32 && dh != 64 && dh != 128) return false;
-    if (const char* env = getenv("XATTN_SHORT")) return env[0] == '1';
+    if (ctx->tune.short_path >= 0) return ctx->tune.short_path == 1;
     if (fused_shape(c, R)) return false;
     return (int64_t)total_kv <=
            (int64_t)R * xattn::short_max_rows(c.kv_mode == XATTN_KV_SEPARATE);
@@ -95,12 +123,12 @@ int variant_smem(const xattn_config& c, int R, int dh, int rb, int ks) {
     return proj > 0 ? proj : xattn::attn_bf16_variant_smem(dh, rb, ks, sep, false);
 }
 
-Variant choose_variant(const xattn_config& c, int R, int total_cand, int total_kv, int heads) {
+Variant choose_variant(const xattn_ctx* ctx, int R, int total_cand, int total_kv, int heads) {
+    const xattn_config& c = ctx->cfg;
     const int dh = c.d_model / heads;
-    if (const char* env = getenv("XATTN_VARIANT")) {
-        int rb = 0, ks = 0;
-        if (sscanf(env, "%d,%d", &rb, &ks) == 2 && variant_smem(c, R, dh, rb, ks) > 0)
-            return {rb, ks};
+    {
+        const int rb = ctx->tune.variant_rb, ks = ctx->tune.variant_ks;
+        if (rb > 0 && variant_smem(c, R, dh, rb, ks) > 0) return {rb, ks};
     }
     const double rows = (double)total_cand * c.n_slots * heads;   // query rows x heads
     const double mean_L = R > 0 ? (double)total_kv / R : 0.0;
@@ -130,9 +158,9 @@ Variant choose_variant(const xattn_config& c, int R, int total_cand, int total_k
     return best;
 }
 
-int tile_m_for(const xattn_config& c, int R, int total_cand, int total_kv, int heads) {
-    if (c.dtype != XATTN_BF16) return 64;
-    return 32 * choose_variant(c, R, total_cand, total_kv, heads).rb;
+int tile_m_for(const xattn_ctx* ctx, int R, int total_cand, int total_kv, int heads) {
+    if (ctx->cfg.dtype != XATTN_BF16) return 64;
+    return 32 * choose_variant(ctx, R, total_cand, total_kv, heads).rb;
 }
 
 int64_t max_tiles_for(const xattn_config& c, int R, int total_cand, int tile_m) {
@@ -234,6 +262,7 @@ xattn_status xattn_create(const xattn_config* cfg, xattn_ctx** out) {
     xattn_ctx* ctx = new (std::nothrow) xattn_ctx;
     if (!ctx) return fail(XATTN_EINVAL, "out of host memory");
     ctx->cfg = *cfg;
+    ctx->tune = read_tuning();
     *out = ctx;
     return XATTN_OK;
 }
@@ -252,8 +281,8 @@ int32_t xattn_forward_path(const xattn_ctx* ctx, int32_t R, int32_t total_cand,
         return 0;
     const xattn_config& c = ctx->cfg;
     if (c.dtype != XATTN_BF16) return XATTN_PATH_FP32;
-    if (short_shape(c, R, total_kv, heads)) return XATTN_PATH_SHORT;
-    const Variant var = choose_variant(c, R, total_cand, total_kv, heads);
+    if (short_shape(ctx, R, total_kv, heads)) return XATTN_PATH_SHORT;
+    const Variant var = choose_variant(ctx, R, total_cand, total_kv, heads);
     return fused_shape(c, R) && xattn::attn_bf16_variant_smem(c.d_model / heads, var.rb, var.ksplit,
                                                               c.kv_mode == XATTN_KV_SEPARATE, true) > 0
                ? XATTN_PATH_SINGLE : XATTN_PATH_GEMM;
@@ -293,7 +322,7 @@ xattn_status xattn_plan(xattn_ctx* ctx, const int32_t* cu_kv, const int32_t* cu_
     if (!workspace || workspace_bytes < xattn_workspace_size(ctx, R, total_cand, heads))
         return fail(XATTN_EWORKSPACE, "workspace needs %zu bytes, got %zu",
                     xattn_workspace_size(ctx, R, total_cand, heads), workspace_bytes);
-    const int tm = tile_m_for(ctx->cfg, R, total_cand, total_kv, heads);
+    const int tm = tile_m_for(ctx, R, total_cand, total_kv, heads);
     if (tile_m) *tile_m = tm;
     DeviceGuard dg(ctx->cfg.device);
     if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
@@ -336,27 +365,28 @@ xattn_status run_forward(Mode mode, xattn_ctx* ctx, const void* Z, const void* W
     if (total_kv > 0 && !K) return fail(XATTN_EINVAL, "NULL K");
     if (total_kv > 0 && c.kv_mode == XATTN_KV_SEPARATE && !V)
         return fail(XATTN_EINVAL, "V is NULL in XATTN_KV_SEPARATE mode");
-    const size_t need = workspace_bytes(c, R, total_cand);
-    if (!workspace || workspace_bytes_ < need)
-        return fail(XATTN_EWORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes_);
     if (R == 0 && (total_cand != 0 || total_kv != 0))
         return fail(XATTN_EINVAL, "num_requests=0 with total_cand=%d total_kv=%d", total_cand,
                     total_kv);
+    const size_t need = workspace_bytes(c, R, total_cand);
+    if (!workspace || workspace_bytes_ < need)
+        return fail(XATTN_EWORKSPACE, "workspace needs %zu bytes, got %zu", need,
+                    workspace_bytes_);
     if (R == 0 || total_cand == 0) return XATTN_OK;  // no query rows: nothing to compute
 
-    const Variant var = c.dtype == XATTN_BF16 ? choose_variant(c, R, total_cand, total_kv, heads)
+    const Variant var = c.dtype == XATTN_BF16 ? choose_variant(ctx, R, total_cand, total_kv, heads)
                                               : Variant{2, 1};
-    const int tm = tile_m_for(c, R, total_cand, total_kv, heads);
+    const int tm = tile_m_for(ctx, R, total_cand, total_kv, heads);
     const int64_t max_tiles = max_tiles_for(c, R, total_cand, tm);
     if (max_tiles * heads > INT32_MAX)
         return fail(XATTN_EUNSUPPORTED, "grid of %lld work-groups is too large",
                     (long long)(max_tiles * heads));
-    void* qws = static_cast<char*>(workspace) + q_offset(c, R, total_cand);
-    const void* Qp = mode == Mode::kAttendQ ? Qin : qws;
     hipStream_t s = static_cast<hipStream_t>(stream);
     DeviceGuard dg(c.device);
     if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
     hipError_t e = hipSuccess;
+    void* qws = static_cast<char*>(workspace) + q_offset(c, R, total_cand);
+    const void* Qp = mode == Mode::kAttendQ ? Qin : qws;
     if (c.dtype == XATTN_BF16) {
         xattn::AttnArgs a{};
         a.K = K;
@@ -374,7 +404,7 @@ xattn_status run_forward(Mode mode, xattn_ctx* ctx, const void* Z, const void* W
         a.O = O;
         a.cand_len = cand_len;
         a.lse = lse;
-        if (mode != Mode::kAttendQ && !cand_len && short_shape(c, R, total_kv, heads)) {
+        if (mode != Mode::kAttendQ && !cand_len && short_shape(ctx, R, total_kv, heads)) {
             // projection and attention in one launch; a forward pass also
             // plans the batch in that launch (request order) and stores the
             // plan in the workspace
@@ -405,7 +435,7 @@ xattn_status run_forward(Mode mode, xattn_ctx* ctx, const void* Z, const void* W
             e = xattn::launch_project_plan_bf16(Z, W_Q, total_cand, c.n_slots, c.d_model, qws, cu_kv,
                                                 cu_cand, R, tm, total_kv,
                                                 mode == Mode::kForward ? workspace : nullptr,
-                                                max_tiles, s);
+                                                max_tiles, s, nullptr, 1.0f, nullptr, &ctx->tune);
             if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
             a.Qp = qws;
         }
@@ -622,7 +652,8 @@ xattn_status run_backward(xattn_ctx* ctx, const void* Z, const void* W_Q, const 
         XATTN_TRY(xattn::launch_project_plan_bf16(Z, W_Q, total_cand, q, d, ws + Lw.qs, cu_kv,
                                                   cu_cand, R, 64, total_kv, ws + Lw.plan, Lw.max_q,
                                                   s, nullptr,
-                                                  1.4426950408889634f / sqrtf((float)dh), &ex),
+                                                  1.4426950408889634f / sqrtf((float)dh), &ex,
+                                                  &ctx->tune),
                   "projection kernel launch");
     } else {
         XATTN_TRY(xattn::launch_plan(cu_kv, cu_cand, R, q, 64, total_cand, total_kv, ws + Lw.plan,
@@ -698,7 +729,7 @@ xattn_status run_backward(xattn_ctx* ctx, const void* Z, const void* W_Q, const 
     b.d = d;
     b.heads = heads;
     b.scale = 1.0f / sqrtf((float)dh);
-    XATTN_TRY(bf ? xattn::launch_bwd_attn_bf16(b, sep, Lw.max_q, Lw.max_k, s)
+    XATTN_TRY(bf ? xattn::launch_bwd_attn_bf16(b, sep, Lw.max_q, Lw.max_k, s, ctx->tune.dq_ks)
                  : xattn::launch_bwd_attn_f32(b, sep, Lw.max_q, Lw.max_k, s),
               "attention backward launch");
     // 5. dZ = dQ W_Q[slot] through the transposed weights; 6. dW_Q
@@ -707,7 +738,8 @@ xattn_status run_backward(xattn_ctx* ctx, const void* Z, const void* W_Q, const 
                   "transpose kernel launch");
     if (bf) {
         XATTN_TRY(xattn::launch_project_plan_bf16(ws + Lw.dq, ws + Lw.wt, total_cand, q, d, dZ,
-                                                  nullptr, nullptr, 0, 0, 0, nullptr, 0, s),
+                                                  nullptr, nullptr, 0, 0, 0, nullptr, 0, s,
+                                                  nullptr, 1.0f, nullptr, &ctx->tune),
                   "input-gradient launch");
         XATTN_TRY(xattn::launch_bwd_dw_bf16(ws + Lw.dq, Z, total_cand, q, d,
                                             reinterpret_cast<float*>(ws + Lw.part), Lw.nch, dW_Q,
@@ -862,15 +894,16 @@ xattn_status xattn_forward_codec(xattn_ctx* ctx, const xattn_codebook* cb_k,
     // short-memory kernel decodes each request's memory once per work-group
     // (keys in the rotated basis, values rotated back) after a planner launch
     // (request order).  The same rule as the bf16 short path, with at most
-    // 96 rows in both modes (two decoded planes).  XATTN_SHORT overrides.
+    // 96 rows in both modes (two decoded planes).  The context's XATTN_SHORT
+    // overrides.
     {
         const int dh = c.d_model / heads;
-        const char* env = getenv("XATTN_SHORT");
+        const int forced = ctx->tune.short_path;
         const bool short_codec =
             c.d_model == xattn::kShortD && (dh == 32 || dh == 64 || dh == 128) &&
-            (env ? env[0] == '1'
-                 : !fused_shape(c, R) &&
-                       (int64_t)total_kv <= (int64_t)R * xattn::short_max_rows(true));
+            (forced >= 0 ? forced == 1
+                         : !fused_shape(c, R) &&
+                               (int64_t)total_kv <= (int64_t)R * xattn::short_max_rows(true));
         if (short_codec) {
             const int64_t mt = max_tiles_for(c, R, total_cand, 64);
             hipStream_t s0 = static_cast<hipStream_t>(stream);
@@ -911,10 +944,10 @@ xattn_status xattn_forward_codec(xattn_ctx* ctx, const xattn_codebook* cb_k,
     // over W_Q_rot.  Separate mode: keys in the rotated basis, values rotated
     // back.  Shared mode: one plane in the rotated basis serves as key and
     // value, and the output rows are rotated back afterwards.
-    // XATTN_CODEC_DECODE=0 keeps the per-tile reconstruction below.
+    // The context's XATTN_CODEC_DECODE=0 keeps the per-tile reconstruction
+    // below.
     {
-        const char* env = getenv("XATTN_CODEC_DECODE");
-        const bool decode = (env ? env[0] != '0' : true) &&
+        const bool decode = ctx->tune.codec_decode != 0 &&
                             workspace_bytes_ >= codec_workspace_bytes(c, R, total_cand, total_kv);
         if (decode) {
             char* planes = static_cast<char*>(workspace) + codec_plane_offset(c, R, total_cand);
@@ -951,10 +984,7 @@ xattn_status xattn_forward_codec(xattn_ctx* ctx, const xattn_codebook* cb_k,
     const double rows_per_req = (double)total_cand * c.n_slots / R;
     int qw = rows_per_req >= 512 ? 8 : (rows_per_req >= 128 ? 4 : 2);
     if (qw == 8 && max_tiles_for(c, R, total_cand, 256) * heads > 4096) qw = 4;
-    if (const char* env = getenv("XATTN_CODEC_QW")) {
-        const int v = atoi(env);
-        if (v == 2 || v == 4 || v == 8) qw = v;
-    }
+    if (ctx->tune.codec_qw) qw = ctx->tune.codec_qw;
     const int64_t max_tiles = max_tiles_for(c, R, total_cand, 32 * qw);
     if (max_tiles * heads > INT32_MAX) return fail(XATTN_EUNSUPPORTED, "grid too large");
     DeviceGuard dg(c.device);
@@ -963,7 +993,8 @@ xattn_status xattn_forward_codec(xattn_ctx* ctx, const xattn_codebook* cb_k,
     void* qws = static_cast<char*>(workspace) + q_offset(c, R, total_cand);
     hipError_t e = xattn::launch_project_plan_bf16(Z, W_Q_rot, total_cand, c.n_slots, c.d_model,
                                                    qws, cu_kv, cu_cand, R, 32 * qw, total_kv,
-                                                   workspace, max_tiles, s);
+                                                   workspace, max_tiles, s, nullptr, 1.0f,
+                                                   nullptr, &ctx->tune);
     if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
     a.Qr = qws;
     a.kcodes = k_codes;
@@ -995,7 +1026,7 @@ xattn_status xattn_project(xattn_ctx* ctx, const void* Z, const void* W_Q, int32
     hipError_t e = c.dtype == XATTN_BF16
                        ? xattn::launch_project_plan_bf16(Z, W_Q, total_cand, c.n_slots, c.d_model,
                                                          Q, nullptr, nullptr, 0, 0, 0, nullptr, 0,
-                                                         s)
+                                                         s, nullptr, 1.0f, nullptr, &ctx->tune)
                        : xattn::launch_project_f32(static_cast<const float*>(Z),
                                                    static_cast<const float*>(W_Q), total_cand,
                                                    c.n_slots, c.d_model, static_cast<float*>(Q), s);
@@ -1027,11 +1058,11 @@ xattn_status xattn_output(xattn_ctx* ctx, const void* Z, const void* W_go, const
     // bf16 on a 256-feature model with at least one unit of 64 candidates
     // per compute unit (measured crossover; smaller batches run faster as two
     // GEMM launches that spread over the chip): one kernel keeps the gated
-    // values on chip.  XATTN_FUSED_OUTPUT=0 / 1 forces either.
+    // values on chip.  The context's XATTN_FUSED_OUTPUT=0 / 1 forces either.
     const int64_t units = (int64_t)c.n_slots * ((total_cand + 63) / 64);
-    const char* fenv = getenv("XATTN_FUSED_OUTPUT");
+    const int forced = ctx->tune.fused_output;
     const bool fused = c.dtype == XATTN_BF16 && c.d_model == xattn::kShortD &&
-                       (fenv ? fenv[0] == '1' : units >= short_grid(ctx, INT64_MAX));
+                       (forced >= 0 ? forced == 1 : units >= short_grid(ctx, INT64_MAX));
     if (fused) {
         hipError_t e = xattn::launch_gate_output_fused_bf16(Z, W_go, O, W_o, Y, total_cand,
                                                             c.n_slots, c.d_model,
@@ -1041,7 +1072,7 @@ xattn_status xattn_output(xattn_ctx* ctx, const void* Z, const void* W_go, const
     }
     hipError_t e = c.dtype == XATTN_BF16
                        ? xattn::launch_gate_output_bf16(Z, W_go, O, W_o, total_cand, c.n_slots,
-                                                        c.d_model, X, Y, s)
+                                                        c.d_model, X, Y, s, &ctx->tune)
                        : xattn::launch_gate_output_f32(
                              static_cast<const float*>(Z), static_cast<const float*>(W_go),
                              static_cast<const float*>(O), static_cast<const float*>(W_o),

@@ -598,15 +598,12 @@ __global__ void bwd_transpose_kernel(const T* __restrict__ wt, int q, int d, T* 
 }
 
 template <int DH, bool SEP, bool CUT>
-hipError_t launch_dq(const BwdArgs& a, int64_t q_items, hipStream_t stream) {
+hipError_t launch_dq(const BwdArgs& a, int64_t q_items, hipStream_t stream, int dq_ks) {
     // two memory splits wherever the LDS leaves room for two work-groups per
-    // CU (measured faster than one on every workload, and four no better)
+    // CU (measured faster than one on every workload, and four no better);
+    // dq_ks = 1 or 2 forces either (tuning and tests)
     const int64_t wgs = q_items * a.heads;
-    int ks = 2;
-    if (const char* env = getenv("XATTN_DQ_KS")) {   // tuning and tests
-        const int v = atoi(env);
-        if (v == 1 || v == 2) ks = v;
-    }
+    const int ks = dq_ks == 1 || dq_ks == 2 ? dq_ks : 2;
     const dim3 grid((unsigned)wgs);
     if constexpr (DqCfg<DH, SEP, 2>::SMEM <= 81920) {
         if (ks == 2) {
@@ -620,9 +617,9 @@ hipError_t launch_dq(const BwdArgs& a, int64_t q_items, hipStream_t stream) {
 
 template <int DH, bool SEP, bool CUT>
 hipError_t launch_bwd_variant(const BwdArgs& a, int64_t q_items, int64_t k_items,
-                              hipStream_t stream) {
+                              hipStream_t stream, int dq_ks) {
     if (q_items > 0) {
-        hipError_t e0 = launch_dq<DH, SEP, CUT>(a, q_items, stream);
+        hipError_t e0 = launch_dq<DH, SEP, CUT>(a, q_items, stream, dq_ks);
         if (e0 != hipSuccess) return e0;
     }
     hipError_t e = hipGetLastError();
@@ -635,13 +632,13 @@ hipError_t launch_bwd_variant(const BwdArgs& a, int64_t q_items, int64_t k_items
 
 template <int DH>
 hipError_t launch_dh_bwd(const BwdArgs& a, bool sep, int64_t q_items, int64_t k_items,
-                         hipStream_t stream) {
+                         hipStream_t stream, int dq_ks) {
     const bool cut = a.vis != nullptr;
     if (sep)
-        return cut ? launch_bwd_variant<DH, true, true>(a, q_items, k_items, stream)
-                   : launch_bwd_variant<DH, true, false>(a, q_items, k_items, stream);
-    return cut ? launch_bwd_variant<DH, false, true>(a, q_items, k_items, stream)
-               : launch_bwd_variant<DH, false, false>(a, q_items, k_items, stream);
+        return cut ? launch_bwd_variant<DH, true, true>(a, q_items, k_items, stream, dq_ks)
+                   : launch_bwd_variant<DH, true, false>(a, q_items, k_items, stream, dq_ks);
+    return cut ? launch_bwd_variant<DH, false, true>(a, q_items, k_items, stream, dq_ks)
+               : launch_bwd_variant<DH, false, false>(a, q_items, k_items, stream, dq_ks);
 }
 
 // vis[c] = cu_kv[r] + clamp(len[c], 0, L_r) for candidate c of request r
@@ -703,11 +700,11 @@ hipError_t launch_bwd_dsum_bf16(const void* dO, const void* O, int64_t rows, int
 }
 
 hipError_t launch_bwd_attn_bf16(const BwdArgs& a, bool sep, int64_t q_items, int64_t k_items,
-                                hipStream_t stream) {
+                                hipStream_t stream, int dq_ks) {
     switch (a.d / a.heads) {
-        case 32: return launch_dh_bwd<32>(a, sep, q_items, k_items, stream);
-        case 64: return launch_dh_bwd<64>(a, sep, q_items, k_items, stream);
-        case 128: return launch_dh_bwd<128>(a, sep, q_items, k_items, stream);
+        case 32: return launch_dh_bwd<32>(a, sep, q_items, k_items, stream, dq_ks);
+        case 64: return launch_dh_bwd<64>(a, sep, q_items, k_items, stream, dq_ks);
+        case 128: return launch_dh_bwd<128>(a, sep, q_items, k_items, stream, dq_ks);
         default: return hipErrorInvalidValue;
     }
 }

@@ -282,7 +282,7 @@ hipError_t launch_project_plan_bf16(const void* Z, const void* Wq, int total_can
                                     void* Q, const int* cu_kv, const int* cu_cand, int R,
                                     int tile_m, int total_kv, void* ws, int64_t max_tiles,
                                     hipStream_t stream, const void* Og, float oscale,
-                                    const PrepExtra* ex) {
+                                    const PrepExtra* ex, const Tuning* tune) {
     PlanArgs pa{cu_kv, cu_cand, static_cast<int*>(ws), max_tiles, R, tile_m, total_kv,
                 ws != nullptr ? 1 : 0, ex ? *ex : PrepExtra{}, 0};
     if (ex) {
@@ -290,10 +290,10 @@ hipError_t launch_project_plan_bf16(const void* Z, const void* Wq, int total_can
         pa.tr_blocks = q * tpd * tpd;
     }
     if (total_cand <= 0 && !pa.enabled) return hipSuccess;
-    // XATTN_GEMM="TE,TC,KC" picks a tile shape (tuning).
-    if (const char* env = getenv("XATTN_GEMM")) {
-        int te = 0, tc = 0, kc = 0;
-        if (sscanf(env, "%d,%d,%d", &te, &tc, &kc) == 3) {
+    // the context's tile-shape override (tuning), if it names a built shape
+    if (tune && tune->gemm_te > 0) {
+        const int te = tune->gemm_te, tc = tune->gemm_tc, kc = tune->gemm_kc;
+        {
 #define XATTN_GEMM_CASE(A_, B_, C_) \
     if (te == A_ && tc == B_ && kc == C_) return launch_prep<A_, B_, C_>(Z, Wq, total_cand, q, d, Q, pa, stream, Og, oscale);
             XATTN_GEMM_CASE(128, 128, 64)
@@ -314,12 +314,12 @@ hipError_t launch_project_plan_bf16(const void* Z, const void* Wq, int total_can
 
 hipError_t launch_gate_output_bf16(const void* Z, const void* Wgo, const void* O, const void* Wo,
                                    int total_cand, int q, int d, void* X, void* Y,
-                                   hipStream_t stream) {
+                                   hipStream_t stream, const Tuning* tune) {
     hipError_t e = launch_project_plan_bf16(Z, Wgo, total_cand, q, d, X, nullptr, nullptr, 0, 0, 0,
-                                            nullptr, 0, stream, O);
+                                            nullptr, 0, stream, O, 1.0f, nullptr, tune);
     if (e != hipSuccess) return e;
     return launch_project_plan_bf16(X, Wo, total_cand * q, 1, d, Y, nullptr, nullptr, 0, 0, 0,
-                                    nullptr, 0, stream, nullptr);
+                                    nullptr, 0, stream, nullptr, 1.0f, nullptr, tune);
 }
 
 }  // namespace xattn

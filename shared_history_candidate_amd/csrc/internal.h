@@ -6,6 +6,26 @@
 
 namespace xattn {
 
+// Tuning overrides, read from the environment once when a context is
+// created (tests and tuning runs force kernel choices this way); 0 / -1 keep
+// the library's own choice.
+//   XATTN_VARIANT="rb,ks"   attention work-group shape
+//   XATTN_SHORT=0|1         short-memory path off / on where it applies
+//   XATTN_CODEC_DECODE=0    coded memory: per-tile reconstruction, never decode once
+//   XATTN_CODEC_QW=2|4|8    coded memory: query waves per work-group
+//   XATTN_FUSED_OUTPUT=0|1  output stage as two GEMM launches / one launch
+//   XATTN_GEMM="te,tc,kc"   projection GEMM tile shape
+//   XATTN_DQ_KS=1|2         backward dQ kernel: memory splits per work-group
+struct Tuning {
+    int variant_rb = 0, variant_ks = 0;
+    int short_path = -1;
+    int codec_decode = -1;
+    int codec_qw = 0;
+    int fused_output = -1;
+    int gemm_te = 0, gemm_tc = 0, gemm_kc = 0;
+    int dq_ks = 0;
+};
+
 hipError_t launch_plan(const int* cu_kv, const int* cu_cand, int R, int q, int tile_m,
                        int total_cand, int total_kv, void* ws, int64_t max_tiles, int* cu_q,
                        int* row_req, int* tiles, int* n_tiles, hipStream_t stream,
@@ -75,17 +95,19 @@ struct PrepExtra {
 };
 // With oscale != 1 the stored value is bf16(float(bf16(acc)) * oscale): the
 // queries pre-scaled exactly as the attention kernel scales them.
+// tune (may be NULL): the context's tile-shape override.
 hipError_t launch_project_plan_bf16(const void* Z, const void* Wq, int total_cand, int q, int d,
                                     void* Qp, const int* cu_kv, const int* cu_cand, int R,
                                     int tile_m, int total_kv, void* ws, int64_t max_tiles,
                                     hipStream_t stream, const void* Og = nullptr,
-                                    float oscale = 1.0f, const PrepExtra* ex = nullptr);
+                                    float oscale = 1.0f, const PrepExtra* ex = nullptr,
+                                    const Tuning* tune = nullptr);
 
 // Output gate and projection of Eq. (7): X = O * sigmoid(Z W_go[slot]) (bf16,
 // [total_cand][q][d]), then Y = X W_o; two launches of the projection kernel.
 hipError_t launch_gate_output_bf16(const void* Z, const void* Wgo, const void* O, const void* Wo,
                                    int total_cand, int q, int d, void* X, void* Y,
-                                   hipStream_t stream);
+                                   hipStream_t stream, const Tuning* tune = nullptr);
 
 // Backward pass (bwd_bf16.hip, bwd in attn_f32.hip).  plan: query tiles of
 // 64 candidates (the forward's plan layout); kplan: memory tiles of 64 rows,
@@ -110,8 +132,9 @@ struct BwdArgs {
     int q, d, heads;
     float scale;   // 1/sqrt(d_h)
 };
+// dq_ks: memory splits of the dQ kernel (0: the library's choice, 1 or 2).
 hipError_t launch_bwd_attn_bf16(const BwdArgs& a, bool sep, int64_t q_items, int64_t k_items,
-                                hipStream_t stream);
+                                hipStream_t stream, int dq_ks = 0);
 // dsum[row][h] = <dO_row, O_row> over head h's features (bf16 [rows][d], rows
 // 16-byte aligned, d/heads in {32, 64, 128}; fp32 sums in a fixed order)
 hipError_t launch_bwd_dsum_bf16(const void* dO, const void* O, int64_t rows, int d, int heads,

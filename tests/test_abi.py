@@ -129,10 +129,17 @@ def test_forward_path(L, monkeypatch):
     assert L.xattn_forward_path(h, 64, 2048, 64 * 192 + 1, 8) == X.PATH_GEMM
     assert L.xattn_forward_path(h, 64, 0, 100, 4) == 0
     assert L.xattn_forward_launches(h, 17, 64, 100, 4) == 1
+    # the tuning variable is read when a context is created: a context made
+    # before it was set keeps the library's choice
     monkeypatch.setenv("XATTN_SHORT", "0")
+    assert L.xattn_forward_path(h, 17, 64, 100, 4) == X.PATH_SHORT
+    L.xattn_destroy(h)
+    st, h = _create(L, 256, 3, X.XATTN_BF16, X.XATTN_KV_SHARED)
     assert L.xattn_forward_path(h, 17, 64, 100, 4) == X.PATH_GEMM
     assert L.xattn_forward_launches(h, 17, 64, 100, 4) == 2
+    L.xattn_destroy(h)
     monkeypatch.setenv("XATTN_SHORT", "1")
+    st, h = _create(L, 256, 3, X.XATTN_BF16, X.XATTN_KV_SHARED)
     assert L.xattn_forward_path(h, 8, 2048, 5482, 4) == X.PATH_SHORT
     assert L.xattn_forward_path(h, 8, 2048, 5482, 2) == X.PATH_SHORT    # d_h = 128
     assert L.xattn_forward_launches(h, 8, 2048, 5482, 4) == 1
