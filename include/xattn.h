@@ -156,6 +156,46 @@ xattn_status xattn_forward(xattn_ctx* ctx,
                            void* O, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* Bytes of the device scratch array that xattn_forward_noalloc uses in place
+ * of a workspace (32 MiB).  Every GPU the library runs on holds one such
+ * array from the first xattn_forward_noalloc call on it until the process
+ * ends. */
+#define XATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* xattn_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same computation, kernels, launches and results as xattn_forward; the
+ * workspace is replaced by a library-owned device array of
+ * XATTN_NOALLOC_SCRATCH_BYTES per GPU.  No HIP allocation, free or memset is
+ * made: the call validates, makes ctx's device current, looks up (first call
+ * on that device: resolves) the array's device address, and enqueues the
+ * kernels on `stream`.
+ *   - Scratch use: the plan (a 256-byte header and 16 bytes per query tile,
+ *     at most q * ceil-sum of N_r / 32 tiles) on the single-launch and
+ *     short-memory paths; on the other paths (projection GEMM + attention,
+ *     fp32) also the projected queries, total_cand * q * d elements of the
+ *     context's type, after the plan (256-byte aligned).  A batch whose path
+ *     needs more than XATTN_NOALLOC_SCRATCH_BYTES is rejected with
+ *     XATTN_EUNSUPPORTED before anything is enqueued (use xattn_forward).
+ *   - Nothing in the array needs to start at zero: every call rewrites the
+ *     plan header before any kernel reads it.
+ *   - All calls on one GPU share that GPU's array and it keeps the last
+ *     call's contents: calls that may overlap on one GPU (other streams,
+ *     other threads, other contexts) race on it and must be serialised by
+ *     the caller.
+ *   - The device-side check of the offset arrays still runs (on a mismatch
+ *     no output is computed), but its flag stays in the library's array;
+ *     callers that need to read it use xattn_forward and xattn_device_error.
+ * Other arguments and errors as for xattn_forward; a HIP failure while
+ * resolving the array's address is XATTN_EHIP. */
+xattn_status xattn_forward_noalloc(xattn_ctx* ctx,
+                                   const void* Z, const void* W_Q,
+                                   const void* K, const void* V,
+                                   const int32_t* cu_seqlens_kv, const int32_t* cu_cand,
+                                   int32_t num_requests, int32_t total_cand,
+                                   int32_t total_kv, int32_t heads,
+                                   void* O, void* stream);
+
 /* xattn_forward with a per-candidate memory prefix (ReST reading note, s.3.5:
  * under the unified-long-term reading every training sample of a user sees
  * only the part of that user's sequence that precedes it, so the candidates

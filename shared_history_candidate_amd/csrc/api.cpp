@@ -338,6 +338,17 @@ namespace {
 
 enum class Mode { kForward, kAttend, kAttendQ };
 
+// Workspace bytes a forward pass (plan + projection + attention, no prefix
+// cutoff) really touches on the path this batch takes: the plan alone on the
+// single-launch and short-memory paths (their queries never leave the chip),
+// the plan and the projected queries on the others.
+size_t forward_path_ws_bytes(const xattn_ctx* ctx, int R, int total_cand, int total_kv,
+                             int heads) {
+    const int path = xattn_forward_path(ctx, R, total_cand, total_kv, heads);
+    if (path == XATTN_PATH_SHORT || path == XATTN_PATH_SINGLE) return q_offset(ctx->cfg, R, total_cand);
+    return workspace_bytes(ctx->cfg, R, total_cand);
+}
+
 // Shared body of xattn_forward (plan + projection + attention), xattn_attend
 // (projection + attention over the plan in the workspace), xattn_attend_q
 // (attention over caller-projected queries and the plan in the workspace) and
@@ -348,7 +359,8 @@ xattn_status run_forward(Mode mode, xattn_ctx* ctx, const void* Z, const void* W
                          const void* K, const void* V, const int32_t* cu_kv,
                          const int32_t* cu_cand, int32_t R, int32_t total_cand, int32_t total_kv,
                          int32_t heads, void* O, void* workspace, size_t workspace_bytes_,
-                         void* stream, const int32_t* cand_len = nullptr, float* lse = nullptr) {
+                         void* stream, const int32_t* cand_len = nullptr, float* lse = nullptr,
+                         bool use_scratch = false) {
     g_last_error.clear();
     xattn_status st = check_shape(ctx, R, total_cand, total_kv, heads);
     if (st != XATTN_OK) return st;
@@ -368,10 +380,21 @@ xattn_status run_forward(Mode mode, xattn_ctx* ctx, const void* Z, const void* W
     if (R == 0 && (total_cand != 0 || total_kv != 0))
         return fail(XATTN_EINVAL, "num_requests=0 with total_cand=%d total_kv=%d", total_cand,
                     total_kv);
-    const size_t need = workspace_bytes(c, R, total_cand);
-    if (!workspace || workspace_bytes_ < need)
-        return fail(XATTN_EWORKSPACE, "workspace needs %zu bytes, got %zu", need,
-                    workspace_bytes_);
+    if (use_scratch) {
+        // the library's own array stands in for the workspace: the batch must
+        // fit what its path touches
+        const size_t need = forward_path_ws_bytes(ctx, R, total_cand, total_kv, heads);
+        if (need > xattn::scratch_capacity())
+            return fail(XATTN_EUNSUPPORTED,
+                        "batch needs %zu bytes of scratch, more than the %zu the no-alloc "
+                        "forward holds (use xattn_forward with a workspace)",
+                        need, xattn::scratch_capacity());
+    } else {
+        const size_t need = workspace_bytes(c, R, total_cand);
+        if (!workspace || workspace_bytes_ < need)
+            return fail(XATTN_EWORKSPACE, "workspace needs %zu bytes, got %zu", need,
+                        workspace_bytes_);
+    }
     if (R == 0 || total_cand == 0) return XATTN_OK;  // no query rows: nothing to compute
 
     const Variant var = c.dtype == XATTN_BF16 ? choose_variant(ctx, R, total_cand, total_kv, heads)
@@ -385,6 +408,13 @@ xattn_status run_forward(Mode mode, xattn_ctx* ctx, const void* Z, const void* W
     DeviceGuard dg(c.device);
     if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
     hipError_t e = hipSuccess;
+    if (use_scratch) {
+        // the array's device address on this (now current) device; the
+        // host-side name of the array is never passed to a kernel
+        e = xattn::scratch_on_device(c.device, &workspace);
+        if (e != hipSuccess) return hip_fail(e, "no-alloc scratch address (hipGetSymbolAddress)");
+        workspace_bytes_ = xattn::scratch_capacity();
+    }
     void* qws = static_cast<char*>(workspace) + q_offset(c, R, total_cand);
     const void* Qp = mode == Mode::kAttendQ ? Qin : qws;
     if (c.dtype == XATTN_BF16) {
@@ -470,6 +500,15 @@ xattn_status xattn_forward(xattn_ctx* ctx, const void* Z, const void* W_Q, const
                            void* O, void* workspace, size_t workspace_bytes_, void* stream) {
     return run_forward(Mode::kForward, ctx, Z, W_Q, nullptr, K, V, cu_kv, cu_cand, R, total_cand,
                        total_kv, heads, O, workspace, workspace_bytes_, stream);
+}
+
+xattn_status xattn_forward_noalloc(xattn_ctx* ctx, const void* Z, const void* W_Q, const void* K,
+                                   const void* V, const int32_t* cu_kv, const int32_t* cu_cand,
+                                   int32_t R, int32_t total_cand, int32_t total_kv, int32_t heads,
+                                   void* O, void* stream) {
+    return run_forward(Mode::kForward, ctx, Z, W_Q, nullptr, K, V, cu_kv, cu_cand, R, total_cand,
+                       total_kv, heads, O, nullptr, 0, stream, nullptr, nullptr,
+                       /*use_scratch=*/true);
 }
 
 xattn_status xattn_forward_prefix(xattn_ctx* ctx, const void* Z, const void* W_Q, const void* K,

@@ -26,6 +26,13 @@ struct Tuning {
     int dq_ks = 0;
 };
 
+// Library-owned scratch of xattn_forward_noalloc (scratch.hip): its size,
+// and its device address on `device`, which must be the current device
+// (resolved with hipGetSymbolAddress on the first call per device, then
+// cached).
+size_t scratch_capacity();
+hipError_t scratch_on_device(int device, void** out);
+
 hipError_t launch_plan(const int* cu_kv, const int* cu_cand, int R, int q, int tile_m,
                        int total_cand, int total_kv, void* ws, int64_t max_tiles, int* cu_q,
                        int* row_req, int* tiles, int* n_tiles, hipStream_t stream,

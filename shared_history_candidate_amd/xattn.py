@@ -28,7 +28,11 @@ EXPORTED = ("xattn_create", "xattn_destroy", "xattn_workspace_size", "xattn_forw
             "xattn_last_error", "xattn_forward_prefix", "xattn_attend_q_prefix",
             "xattn_backward_workspace_size", "xattn_backward", "xattn_codec_encode",
             "xattn_codec_fold_query_weights", "xattn_forward_codec", "xattn_forward_path",
-            "xattn_codec_workspace_size", "xattn_forward_train", "xattn_backward_saved")
+            "xattn_codec_workspace_size", "xattn_forward_train", "xattn_backward_saved",
+            "xattn_forward_noalloc")
+
+# include/xattn.h: bytes of the library-owned scratch of xattn_forward_noalloc
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 # xattn_path values (include/xattn.h)
 PATH_SINGLE, PATH_GEMM, PATH_FP32, PATH_SHORT = 1, 2, 3, 4
@@ -103,6 +107,8 @@ def lib():
         L.xattn_forward_path.restype = I32
         L.xattn_forward.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, P, P, SZ, P]
         L.xattn_forward.restype = ctypes.c_int
+        L.xattn_forward_noalloc.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, P, P]
+        L.xattn_forward_noalloc.restype = ctypes.c_int
         L.xattn_forward_prefix.argtypes = [P, P, P, P, P, P, P, P, I32, I32, I32, I32, P, P, SZ,
                                            P]
         L.xattn_forward_prefix.restype = ctypes.c_int
@@ -298,6 +304,30 @@ class XAttn:
                        _ptr(cu_cand), R, total_cand, total_kv, heads, _ptr(O), _ptr(workspace),
                        workspace.numel(), _stream(Z.device, stream)), bind)
         return b if bind else O
+
+    def forward_noalloc(self, Z, W_Q, K, V, cu_seqlens_kv, cu_cand, heads: int, O=None,
+                        stream=None) -> torch.Tensor:
+        """forward() without a workspace (xattn_forward_noalloc): the library's
+        own device scratch stands in for it, so the call allocates nothing but
+        O (when O is not given).  Calls that may overlap on one GPU race on
+        that scratch."""
+        d, q, dt = self.d_model, self.q, self.torch_dtype
+        total_cand, total_kv = Z.shape[0], K.shape[0]
+        R = cu_seqlens_kv.numel() - 1
+        self._check_tensor("Z", Z, dt, (total_cand, q, d))
+        self._check_tensor("W_Q", W_Q, dt, (q, d, d))
+        self._check_tensor("K", K, dt, (total_kv, d))
+        if V is not None:
+            self._check_tensor("V", V, dt, (total_kv, d))
+        self._check_tensor("cu_seqlens_kv", cu_seqlens_kv, torch.int32, (R + 1,))
+        self._check_tensor("cu_cand", cu_cand, torch.int32, (R + 1,))
+        if O is None:
+            O = torch.empty((total_cand, q, d), dtype=dt, device=Z.device)
+        self._check_tensor("O", O, dt, (total_cand, q, d))
+        _check(lib().xattn_forward_noalloc(self._h, _ptr(Z), _ptr(W_Q), _ptr(K), _ptr(V),
+                                           _ptr(cu_seqlens_kv), _ptr(cu_cand), R, total_cand,
+                                           total_kv, heads, _ptr(O), _stream(Z.device, stream)))
+        return O
 
     def forward_train(self, Z, W_Q, K, V, cu_seqlens_kv, cu_cand, heads: int, O=None,
                       lse=None, workspace=None, stream=None, cand_kv_len=None):

@@ -395,3 +395,38 @@ def test_training_pair_host_validation(L):
                                   2, 10, 20, 2, FAKE, FAKE, FAKE, None, FAKE, need,
                                   None) == X.XATTN_EUNSUPPORTED
     L.xattn_destroy(h)
+
+
+def test_forward_noalloc_host_validation(L):
+    """xattn_forward_noalloc validates like xattn_forward, and rejects a batch
+    whose path needs more than the library's scratch before touching a
+    device (fake pointers: nothing is dereferenced or launched)."""
+    L.xattn_forward_noalloc.restype = ctypes.c_int
+
+    def fwd(h, Z=FAKE, K=FAKE, V=None, O=FAKE, R=2, tc=10, tkv=20, heads=4):
+        return L.xattn_forward_noalloc(h, Z, FAKE, K, V, FAKE, FAKE, R, tc, tkv, heads, O, None)
+
+    st, h = _create(L, 512, 3, X.XATTN_BF16, X.XATTN_KV_SHARED)
+    assert st == 0
+    assert fwd(None) == X.XATTN_EINVAL
+    assert fwd(h, heads=5) == X.XATTN_EINVAL
+    assert fwd(h, Z=None) == X.XATTN_EINVAL
+    assert fwd(h, O=None) == X.XATTN_EINVAL
+    assert fwd(h, V=FAKE) == X.XATTN_EINVAL
+    assert fwd(h, R=-1) == X.XATTN_EINVAL
+    # projection GEMM path: 12000 candidates x 3 slots x 512 bf16 features of
+    # projected queries (36.9 MB) exceed the 32 MiB scratch
+    assert X.NOALLOC_SCRATCH_BYTES == 32 << 20
+    assert fwd(h, R=2, tc=12000, tkv=40000, heads=8) == X.XATTN_EUNSUPPORTED
+    assert "scratch" in L.xattn_last_error().decode()
+    # empty batch: valid, nothing launched and no device touched
+    assert fwd(h, R=0, tc=0, tkv=0, heads=8) == X.XATTN_OK
+    L.xattn_destroy(h)
+    # short-memory path (d = 256, separate K/V): only the plan is staged, so a
+    # batch whose projected queries alone would exceed the scratch passes the
+    # size check (this one: 262144 rows x 256 features = 134 MB of queries);
+    # xattn_forward_path confirms the path without launching anything
+    st, h = _create(L, 256, 1, X.XATTN_BF16, X.XATTN_KV_SEPARATE)
+    L.xattn_forward_path.restype = ctypes.c_int32
+    assert L.xattn_forward_path(h, 256, 262144, 256 * 96, 4) == X.PATH_SHORT
+    L.xattn_destroy(h)
