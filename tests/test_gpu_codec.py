@@ -9,9 +9,11 @@ oracle (oracle/codec.py) and the fp64 attention oracle.
     its code must lie in [floor(t - dt), floor(t + dt)] (clamped), and must
     equal the oracle's wherever that set is a single code;
   * fold: the rotated query weights against E^T W_Q in fp64 (bf16 rounding);
-  * attention over the coded memory: the GPU's own codes decoded by the
-    oracle (fp64) and run through the oracle's forward, against the GPU's
-    output, element-wise max-abs <= 2e-2 (bf16).
+  * attention over the coded memory: the oracle encodes and packs the memory
+    (codes, and norms rounded to the fp32 the library takes), the library
+    attends over exactly those codes, and the oracle decodes the same codes
+    and norms (fp64) and runs its forward; element-wise max-abs <= 2e-2
+    (bf16).  No input of these checks comes from the GPU.
 The codebooks are fitted by the oracle on a sample of the memory rows with a
 decaying spectrum, so bit tables are uneven and contain 0-bit coordinates."""
 import numpy as np
@@ -48,6 +50,19 @@ def _gpu_codes(ctx, cb, Xrows):
     codes, norms = ctx.codec_encode(_book(cb), t)
     torch.cuda.synchronize()
     return codes, norms
+
+
+def _oracle_codes(cb, Xrows):
+    """The oracle's codes of the rows Xrows as the library takes them (packed
+    words [heads, n, words] int32 and fp32 norms [heads, n], on the device),
+    and the oracle's fp64 decode of exactly those codes and norms."""
+    n64, c = OC.encode(Xrows, cb)
+    n32 = n64.astype(np.float32)
+    words = OC.pack(c, cb["bits"])                           # [n, heads, words]
+    codes_t = torch.from_numpy(
+        np.ascontiguousarray(np.transpose(words, (1, 0, 2))).view(np.int32)).to("cuda")
+    norms_t = torch.from_numpy(np.ascontiguousarray(n32.T)).to("cuda")
+    return codes_t, norms_t, OC.decode(n32.astype(np.float64), c, cb)
 
 
 def _unpacked(codes_t, cb):
@@ -119,17 +134,13 @@ def test_codec_attention_matches_oracle(mode, dh, heads, bpc, decode):
     wl, K, V, cbk, cbv = _setup(EDGE_LENGTHS, EDGE_CANDS, dh, heads, mode, bpc, seed=dh)
     ctx = ctx_for(wl)
     t = X.to_device(wl)
-    kc, kn = _gpu_codes(ctx, cbk, K)
-    vc, vn = _gpu_codes(ctx, cbv, V) if V is not None else (None, None)
+    kc, kn, Kd = _oracle_codes(cbk, K)
+    vc, vn, Vd = _oracle_codes(cbv, V) if V is not None else (None, None, None)
     Wr = ctx.codec_fold(_book(cbk), t["W_Q"])
     O = ctx.forward_codec(_book(cbk), _book(cbv) if cbv else None, t["Z"], Wr, kc, kn, vc, vn,
                           t["cu_kv"], t["cu_cand"], wl.heads, decode=decode)
     torch.cuda.synchronize()
     got = O.float().cpu().numpy().astype(np.float64).reshape(-1, wl.d)
-    # the GPU's own codes, decoded by the oracle
-    Kd = OC.decode(kn.cpu().numpy().T.astype(np.float64), _unpacked(kc, cbk), cbk)
-    Vd = (OC.decode(vn.cpu().numpy().T.astype(np.float64), _unpacked(vc, cbv), cbv)
-          if V is not None else None)
     ref = oracle.forward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, Kd, Vd)
     err, rel = assert_close(got, ref, "bf16", "codec %s dh=%d bpc=%d" % (mode, dh, bpc))
     print("codec %s dh=%d bpc=%d: max-abs %.3e normwise %.3e" % (mode, dh, bpc, err, rel))
@@ -152,13 +163,11 @@ def test_codec_attention_transx_slice():
     cbk, cbv = OC.fit(K, wl.heads, budget), OC.fit(V, wl.heads, budget)
     ctx = ctx_for(wl)
     t = X.to_device(wl)
-    kc, kn = _gpu_codes(ctx, cbk, K)
-    vc, vn = _gpu_codes(ctx, cbv, V)
+    kc, kn, Kd = _oracle_codes(cbk, K)
+    vc, vn, Vd = _oracle_codes(cbv, V)
     O = ctx.forward_codec(_book(cbk), _book(cbv), t["Z"], ctx.codec_fold(_book(cbk), t["W_Q"]),
                           kc, kn, vc, vn, t["cu_kv"], t["cu_cand"], wl.heads)
     torch.cuda.synchronize()
-    Kd = OC.decode(kn.cpu().numpy().T.astype(np.float64), _unpacked(kc, cbk), cbk)
-    Vd = OC.decode(vn.cpu().numpy().T.astype(np.float64), _unpacked(vc, cbv), cbv)
     ref = oracle.forward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, Kd, Vd)
     got = O.float().cpu().numpy().astype(np.float64).reshape(-1, wl.d)
     err, rel = assert_close(got, ref, "bf16", "codec transx")
@@ -176,16 +185,13 @@ def test_codec_every_query_wave_count(monkeypatch, qw, dh, heads, mode):
     wl, K, V, cbk, cbv = _setup([700, 65, 1, 300], [90, 300, 2, 11], dh, heads, mode, 4, seed=3)
     ctx = ctx_for(wl)
     t = X.to_device(wl)
-    kc, kn = _gpu_codes(ctx, cbk, K)
-    vc, vn = _gpu_codes(ctx, cbv, V) if V is not None else (None, None)
+    kc, kn, Kd = _oracle_codes(cbk, K)
+    vc, vn, Vd = _oracle_codes(cbv, V) if V is not None else (None, None, None)
     O = ctx.forward_codec(_book(cbk), _book(cbv) if cbv else None, t["Z"],
                           ctx.codec_fold(_book(cbk), t["W_Q"]), kc, kn, vc, vn, t["cu_kv"],
                           t["cu_cand"], wl.heads, decode=False)
     torch.cuda.synchronize()
     got = O.float().cpu().numpy().astype(np.float64).reshape(-1, wl.d)
-    Kd = OC.decode(kn.cpu().numpy().T.astype(np.float64), _unpacked(kc, cbk), cbk)
-    Vd = (OC.decode(vn.cpu().numpy().T.astype(np.float64), _unpacked(vc, cbv), cbv)
-          if V is not None else None)
     ref = oracle.forward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, Kd, Vd)
     err, rel = assert_close(got, ref, "bf16", "codec qw=%s dh=%d %s" % (qw, dh, mode))
     print("codec qw=%s dh=%d %s: max-abs %.3e" % (qw, dh, mode, err))
@@ -196,15 +202,14 @@ SHORT_CANDS = [3, 64, 65, 1, 129, 63, 2, 7, 128]
 
 
 def _codec_forward(ctx, wl, t, K, V, cbk, cbv):
-    kc, kn = _gpu_codes(ctx, cbk, K)
-    vc, vn = _gpu_codes(ctx, cbv, V) if V is not None else (None, None)
+    """The library's coded forward over the oracle's codes of K (and V), and
+    the oracle's decode of those codes."""
+    kc, kn, Kd = _oracle_codes(cbk, K)
+    vc, vn, Vd = _oracle_codes(cbv, V) if V is not None else (None, None, None)
     O = ctx.forward_codec(_book(cbk), _book(cbv) if cbv else None, t["Z"],
                           ctx.codec_fold(_book(cbk), t["W_Q"]), kc, kn, vc, vn, t["cu_kv"],
                           t["cu_cand"], wl.heads)
     torch.cuda.synchronize()
-    Kd = OC.decode(kn.cpu().numpy().T.astype(np.float64), _unpacked(kc, cbk), cbk)
-    Vd = (OC.decode(vn.cpu().numpy().T.astype(np.float64), _unpacked(vc, cbv), cbv)
-          if V is not None else None)
     return O.float().cpu().numpy().astype(np.float64).reshape(-1, wl.d), Kd, Vd
 
 
@@ -214,8 +219,8 @@ def test_codec_short_memory_kernel(monkeypatch, mode, dh, heads, bpc):
     """The short-memory kernel over a coded memory (d = 256): each request's
     memory decoded once per work-group, keys in the rotated basis, values
     rotated back on the matrix cores; memories longer than 96 rows streamed
-    in chunks.  Against the oracle's decode of the GPU's own codes and its
-    forward."""
+    in chunks.  Against the oracle's decode of its own codes (the ones the
+    library attends over) and its forward."""
     monkeypatch.setenv("XATTN_SHORT", "1")
     require_gpu()
     wl, K, V, cbk, cbv = _setup(SHORT_LENGTHS, SHORT_CANDS, dh, heads, mode, bpc, seed=dh + 1)
@@ -260,8 +265,8 @@ def test_codec_decoded_planes_long_memory(mode, dh, heads):
     wl, K, V, cbk, cbv = _setup([5000, 4001], [40, 3], dh, heads, mode, 4.5, seed=11)
     ctx = ctx_for(wl)
     t = X.to_device(wl)
-    kc, kn = _gpu_codes(ctx, cbk, K)
-    vc, vn = _gpu_codes(ctx, cbv, V) if V is not None else (None, None)
+    kc, kn, Kd = _oracle_codes(cbk, K)
+    vc, vn, Vd = _oracle_codes(cbv, V) if V is not None else (None, None, None)
     Wr = ctx.codec_fold(_book(cbk), t["W_Q"])
     outs = {}
     for decode in (True, False):
@@ -269,9 +274,6 @@ def test_codec_decoded_planes_long_memory(mode, dh, heads):
                               vn, t["cu_kv"], t["cu_cand"], wl.heads, decode=decode)
         torch.cuda.synchronize()
         outs[decode] = O.float().cpu().numpy().astype(np.float64).reshape(-1, wl.d)
-    Kd = OC.decode(kn.cpu().numpy().T.astype(np.float64), _unpacked(kc, cbk), cbk)
-    Vd = (OC.decode(vn.cpu().numpy().T.astype(np.float64), _unpacked(vc, cbv), cbv)
-          if V is not None else None)
     rows = sample_rows(wl, 60)
     ref = oracle.forward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, Kd, Vd, rows=rows)
     for decode in (True, False):

@@ -1,8 +1,9 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
 same seeded inputs.  bf16: element-wise max-abs <= 2e-2; fp32: normwise
-relative <= 1e-4; integer plan outputs bit-exact.  Full-size workloads are
-checked on every row where the oracle is fast enough and on sampled rows
-(plus every request's first and last row) where it is not."""
+relative <= 1e-4; integer plan outputs bit-exact.  The benchmark workloads
+run at full size with seeds 0-4: every row where the host oracle is fast
+enough (tiny, rest, ragged, transx), and on the long history the rows of
+every (request, slot, 32-candidate block) work item."""
 import numpy as np
 import pytest
 import torch
@@ -31,30 +32,56 @@ def _check(wl, rows=None, what=""):
 
 
 # ---------------------------------------------------------------------------
-# The five benchmark workloads
+# The five benchmark workloads, seeds 0-4
 # ---------------------------------------------------------------------------
-def test_config_tiny_fp32():
-    _check(W.make("tiny", 0))
+SEEDS = range(5)
 
 
-@pytest.mark.parametrize("seed", [0, 1])
+def block_rows(wl, block=32, seed=0):
+    """Rows of every (request, slot, block of `block` candidates) work item of
+    the attention kernels: the block's first and last candidate and one drawn
+    inside it, for every slot (every head is compared on each row)."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for r in range(wl.R):
+        c0, c1 = int(wl.cu_cand[r]), int(wl.cu_cand[r + 1])
+        for b0 in range(c0, c1, block):
+            b1 = min(b0 + block, c1)
+            for c in {b0, b1 - 1, int(rng.integers(b0, b1))}:
+                rows.update(c * wl.q + s for s in range(wl.q))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_config_tiny_fp32(seed):
+    _check(W.make("tiny", seed), what="tiny seed %d" % seed)
+
+
+@pytest.mark.parametrize("seed", SEEDS)
 def test_config_rest_bf16(seed):
-    _check(W.make("rest", seed))
+    _check(W.make("rest", seed), what="rest seed %d" % seed)
 
 
-def test_config_ragged_bf16():
-    wl = W.make("ragged", 0)
-    _check(wl, rows=sample_rows(wl, 2000))
+@pytest.mark.parametrize("seed", SEEDS)
+def test_config_ragged_bf16(seed):
+    """Every row."""
+    _check(W.make("ragged", seed), what="ragged seed %d" % seed)
 
 
-def test_config_transx_bf16():
-    wl = W.make("transx", 0)
-    _check(wl, rows=sample_rows(wl, 2048))
+@pytest.mark.parametrize("seed", SEEDS)
+def test_config_transx_bf16(seed):
+    """Every row (262144 query rows)."""
+    _check(W.make("transx", seed), what="transx seed %d" % seed)
 
 
-def test_config_long_bf16():
-    wl = W.make("long", 0)
-    _check(wl, rows=sample_rows(wl, 48))
+@pytest.mark.parametrize("seed", SEEDS)
+def test_config_long_bf16(seed):
+    """Rows of every (request, slot, 32-candidate block) work item: 4 x 3 x
+    16 blocks, each checked at its first, last and one inner candidate."""
+    wl = W.make("long", seed)
+    rows = block_rows(wl, 32, seed)
+    assert len(rows) >= wl.R * wl.q * (512 // 32) * 2
+    _check(wl, rows=rows, what="long seed %d" % seed)
 
 
 # ---------------------------------------------------------------------------

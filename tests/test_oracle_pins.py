@@ -301,6 +301,41 @@ def test_request_independence_and_order(oracle_mod):
     assert np.array_equal(O2, O[rows])
 
 
+def _check_probs(orc, seed, kv_mode):
+    """oracle.probs, which projects the query itself, against (i) torch's
+    float64 softmax of the row's scores computed here from the definition
+    (Q = Z . W_Q[slot] with output-major weights, scores over the head's
+    slice scaled by 1/sqrt(d_h)), and (ii) the forward: probs . V must give
+    the oracle's output row for that head.  Largest deviation over every row
+    and head."""
+    rng = np.random.default_rng(seed)
+    wl = _rand_case(rng, R=3, q=3, d=8, heads=2, kv_mode=kv_mode)
+    O = _oracle_out(orc, wl)
+    f64 = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))
+    Z = f64(wl.Z.reshape(-1, wl.d))
+    wt = f64(wl.wt)
+    K = f64(wl.K)
+    V = K if wl.V is None else f64(wl.V)
+    dh = wl.d // wl.heads
+    err = 0.0
+    for row in range(wl.rows):
+        r = int(np.searchsorted(wl.cu_cand * wl.q, row, side="right") - 1)
+        a, b = int(wl.cu_kv[r]), int(wl.cu_kv[r + 1])
+        qv = wt[row % wl.q] @ Z[row]
+        for h in range(wl.heads):
+            sl = slice(h * dh, (h + 1) * dh)
+            ref = torch.softmax(K[a:b, sl] @ qv[sl] / np.sqrt(dh), dim=0).numpy()
+            p = orc.probs(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, wl.K, row, h)
+            err = max(err, float(np.max(np.abs(p - ref))))
+            err = max(err, float(np.max(np.abs(p @ V[a:b, sl].numpy() - O[row, sl]))))
+    return err
+
+
+@pytest.mark.parametrize("kv_mode", ["shared", "separate"])
+def test_probs_match_torch_softmax_and_forward(oracle_mod, kv_mode):
+    assert _check_probs(oracle_mod, 13, kv_mode) < 1e-12
+
+
 def test_softmax_rows_sum_to_one(oracle_mod):
     rng = np.random.default_rng(12)
     wl = _rand_case(rng, R=2, q=2, d=8, heads=2, kv_mode="shared")
@@ -820,6 +855,14 @@ MUTANTS = {
                          "for (long row = 0; row < total_rows; row += 1) {"),
     "bwd_dq_reads_values": ("dqi[e] += c * ds * kj[e];",
                             "dqi[e] += c * ds * Vm[(size_t)(kv0 + j) * d + h * d_h + e];"),
+    # oracle_probs projects the query with a copy of the loop of the forward:
+    # mistakes planted in that copy alone
+    "probs_slot_ignored": ("return ORACLE_EINVAL;\n    const double *w = wt + (size_t)(row % q) * d * d;",
+                           "return ORACLE_EINVAL;\n    const double *w = wt + (size_t)0 * d * d;"),
+    "probs_weight_transposed": ("acc += Z[(size_t)row * d + i] * w[(size_t)o * d + i];\n        qrow[o] = acc;\n    }\n    if (L > 0)",
+                                "acc += Z[(size_t)row * d + i] * w[(size_t)i * d + o];\n        qrow[o] = acc;\n    }\n    if (L > 0)"),
+    "probs_head_offset": ("softmax_weights(qrow, K, d, d_h, head, kv0, L, p);",
+                          "softmax_weights(qrow, K, d, d_h, 0, kv0, L, p);"),
     "bwd_cutoff_ignored": ("Lc = want < 0 ? 0 : (want < L ? want : L);\n                    }\n                    if (Lc == 0)\n                        continue;",
                            "Lc = L;\n                    }\n                    if (Lc == 0)\n                        continue;"),
 }
@@ -840,6 +883,8 @@ def _all_pins(orc):
         "translation": lambda: _check_translation(orc, 7) < 1e-12,
         "permutation": lambda: _check_permutation(orc, 9) < 1e-13,
         "shared_prefix": lambda: _check_shared_prefix(orc, 10) == 0.0,
+        "probs_shared": lambda: _check_probs(orc, 13, "shared") < 1e-12,
+        "probs_separate": lambda: _check_probs(orc, 13, "separate") < 1e-12,
         "gate_half_saturated": lambda: _check_gate_half_and_saturated(orc, 0) == 0.0,
         "gate_symmetry": lambda: _check_gate_symmetry(orc, 1) < 1e-12,
         "prefix_sdpa": lambda: all(_check_prefix_sdpa(orc, s_) < 1e-12 for s_ in range(2)),
