@@ -55,16 +55,42 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // Widest model the fused projection stages in LDS.
 constexpr int kProjMaxD = kAttnProjMaxD;
 
+// One direct global-to-LDS load: every lane's 16 bytes at byte offset voff of
+// the buffer land in LDS at lds_addr + 16 * lane.  Written out (M0 set in the
+// same block) because the compiler, seeing an LDS-writing load, would make the
+// next LDS read of any buffer wait for it; the kernel instead waits for these
+// loads explicitly (s_waitcnt vmcnt) before the barrier that publishes a
+// tile, and before the tile buffers are reused for anything else.  The load
+// writes no register.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_addr, int voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 ::"s"(lds_addr), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
 template <int DH, int RB, int KSPLIT, bool SEP, bool PROJ, bool CUT = false>
 struct Cfg {
     static constexpr int NW = RB * KSPLIT;
     static constexpr int NT = 64 * NW;
     static constexpr int EB = DH / 32;        // 32-wide feature blocks
     static constexpr int KST = DH / 16;       // k-steps of the score product
-    // Row padding of the memory tile (elements).  16-byte rows (8) let the
-    // score operands come in single 16-byte LDS reads; the separate-K/V tiles
-    // measured faster with 8-byte rows (4).
-    static constexpr int PAD = SEP ? 4 : 8;
+    // Memory tiles over caller-projected queries at head width 64 with K = V
+    // are staged by direct global-to-LDS loads (no registers, no LDS store
+    // instructions), NBUF buffers deep per split: the tile NBUF - 1 ahead is
+    // in flight while one is computed.  Their rows are unpadded, with the
+    // 16-byte chunks of row r permuted by chunk ^ ((r >> 1) & 7), which keeps
+    // the score-operand and transposed value reads as free of bank conflicts
+    // as the padded rows of the register-staged tiles.
+    static constexpr bool DMA = !PROJ && !SEP && DH == 64;
+    static constexpr int NBUF = DMA ? (KSPLIT <= 2 ? 3 : 2) : 2;
+    // Row padding of the register-staged memory tile (elements).  16-byte
+    // rows (8) let the score operands come in single 16-byte LDS reads; the
+    // separate-K/V tiles measured faster with 8-byte rows (4).
+    static constexpr int PAD = DMA ? 0 : (SEP ? 4 : 8);
     static constexpr int LDK = DH + PAD;      // memory tile pitch (elements)
     // one wave per split: a wave reads only the tiles it stored itself, so the
     // memory loop needs no work-group barrier (a wave's LDS operations retire
@@ -72,7 +98,9 @@ struct Cfg {
     static constexpr bool PRIVATE = RB == 1;
     static constexpr int PLANES = SEP ? 2 : 1;
     static constexpr int TILE = BN * LDK;     // elements per plane per buffer
-    static constexpr int KV_BYTES = KSPLIT * 2 * PLANES * TILE * 2;
+    static constexpr int KV_BYTES = KSPLIT * NBUF * PLANES * TILE * 2;
+    // direct loads per wave and tile: a load fills 1 KB (8 rows of 128 bytes)
+    static constexpr int DPW = DMA ? BN * DH * 2 / 1024 / RB : 0;
     static constexpr int CMB_BYTES = KSPLIT > 1 ? RB * (KSPLIT - 1) * 64 * (EB * 16 + 2) * 4 : 0;
     // Fused projection (PROJ): the tile's query tokens (32*RB rows) and head
     // h's rows of W_Q[s] (DH rows) are staged in LDS (up to kProjMaxD wide,
@@ -221,7 +249,7 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
                 vr[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, goff[u], 0, 0));
         }
     };
-    bf16* kvl = reinterpret_cast<bf16*>(smem) + (size_t)ksg * 2 * C::PLANES * C::TILE;
+    bf16* kvl = reinterpret_cast<bf16*>(smem) + (size_t)ksg * C::NBUF * C::PLANES * C::TILE;
     auto lstore = [&](int buf, const uint4 (&kr)[C::KV_CPT], const uint4 (&vr)[SEP ? C::KV_CPT : 1]) {
         bf16* base = kvl + buf * C::PLANES * C::TILE;
 #pragma unroll
@@ -240,6 +268,50 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
                 }
             }
         }
+    };
+
+    // Direct global-to-LDS staging (C::DMA): load j of this wave fills the
+    // 1 KB of tile rows 8b .. 8b+7, b = rb * DPW + j, of a buffer; lane l
+    // writes row 8b + l/8 at chunk position l % 8, so it loads that row's
+    // global chunk (l % 8) ^ ((row >> 1) & 7).  Rows past the request's last
+    // memory row (and whole tiles past it) read as zeros.
+    int dgoff[C::DMA ? C::DPW : 1];
+    if constexpr (C::DMA) {
+#pragma unroll
+        for (int j = 0; j < C::DPW; ++j) {
+            const int r = 8 * (rb * C::DPW + j) + (lane >> 3);
+            const int c = (lane & 7) ^ ((r >> 1) & 7);
+            dgoff[j] = (r * d + c * 8) * 2;
+        }
+    }
+    auto dma = [&](int t, int buf) {
+        const int row0 = t * BN;
+        const int left = L_loop - row0;
+        const size_t nb = left > 0 ? (size_t)left * d * 2 : 0;
+        const uint32_t bytes = nb > 0xFFFFFFF0u ? 0xFFFFFFF0u : (uint32_t)nb;
+        const size_t roff = left > 0 ? (size_t)row0 * d : 0;
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(Kh + roff), (short)0, bytes, 0x00020000);
+        const uint32_t base =
+            __builtin_amdgcn_readfirstlane(lds_addr_of(kvl + buf * C::PLANES * C::TILE + rb * C::DPW * 512));
+#pragma unroll
+        for (int j = 0; j < C::DPW; ++j) lds_dma16(rk, base + j * 1024, dgoff[j]);
+    };
+    // Element offsets inside a tile buffer of the fragments a lane reads: the
+    // score operand of rows hh*32 + l32, k-step k (features 16k + 8g ..), and
+    // the transposed value read of rows 16u + tr_row (+8) at column col.
+    auto kofs = [&](int hh, int k) {
+        const int r = hh * 32 + (lane & 31);
+        if constexpr (C::DMA)
+            return r * C::LDK + (((2 * k + (lane >> 5)) ^ ((r >> 1) & 7)) << 3);
+        else
+            return r * C::LDK + 16 * k + 8 * (lane >> 5);
+    };
+    auto vofs = [&](int row, int col) {
+        if constexpr (C::DMA)
+            return row * C::LDK + ((((col >> 3) ^ ((row >> 1) & 7))) << 3) + (col & 7);
+        else
+            return row * C::LDK + col;
     };
 
     // k-step k, half g: features 16k + 8g .. 16k + 8g + 7 of the lane's query
@@ -283,9 +355,15 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
         for (int k = 0; k < C::KST; ++k)
             qb[k] = *reinterpret_cast<const bf16x8*>(qrow + 16 * k + 8 * g);
     }
-    // The first P tiles of this split are requested right behind.
+    // The first tiles of this split are requested right behind: P register
+    // stages, or (direct staging) the NBUF - 1 buffers ahead of the computed one.
+    if constexpr (C::DMA) {
 #pragma unroll
-    for (int j = 0; j < P; ++j) gload(ksg + j * KSPLIT, kreg[j], vreg[j]);
+        for (int j = 0; j < C::NBUF - 1; ++j) dma(ksg + j * KSPLIT, j);
+    } else {
+#pragma unroll
+        for (int j = 0; j < P; ++j) gload(ksg + j * KSPLIT, kreg[j], vreg[j]);
+    }
     if constexpr (PROJ) {
         bf16* zs = reinterpret_cast<bf16*>(smem);
         bf16* wsh = zs + 32 * RB * C::LDS_K;
@@ -343,9 +421,11 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
 #pragma unroll
         for (int e = 0; e < 8; ++e) qb[k][e] = (bf16)((float)qb[k][e] * scale_log2);
 
-    lstore(0, kreg[0], vreg[0]);
-    gload(ksg + P * KSPLIT, kreg[0], vreg[0]);
-    __syncthreads();
+    if constexpr (!C::DMA) {
+        lstore(0, kreg[0], vreg[0]);
+        gload(ksg + P * KSPLIT, kreg[0], vreg[0]);
+        __syncthreads();
+    }
 
     // ---------------- 2. stream this split's memory tiles ----------------
     // Softmax reference.  Every score product is seeded with -m_seed, so the
@@ -382,10 +462,9 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
         bf16x8 kf[2][C::KST];
 #pragma unroll
         for (int k = 0; k < C::KST; ++k) {
-            const int e0 = 16 * k + 8 * g;
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
-                const bf16* row = kb + (hh * 32 + l32) * C::LDK + e0;
+                const bf16* row = kb + kofs(hh, k);
                 kf[hh][k] = cat(*reinterpret_cast<const bf16x4*>(row),
                                 *reinterpret_cast<const bf16x4*>(row + 4));
             }
@@ -405,8 +484,8 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
         for (int u = 0; u < 4; ++u)
 #pragma unroll
             for (int eb = 0; eb < C::EB; ++eb) {
-                const bf16* base = vb + (16 * u + tr_row) * C::LDK + eb * 32 + tr_col;
-                vf[u][eb] = cat(lds_read_tr16(base), lds_read_tr16(base + 8 * C::LDK));
+                const int row = 16 * u + tr_row, col = eb * 32 + tr_col;
+                vf[u][eb] = cat(lds_read_tr16(vb + vofs(row, col)), lds_read_tr16(vb + vofs(row + 8, col)));
             }
     };
     // Only the request's last tile is partial (with cutoffs: tiles past the
@@ -487,7 +566,65 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
 
     // ---- first pass: fixed reference ----
     float l_peak = 0.f;   // largest tile weight sum of the lane
-    {
+    if constexpr (C::DMA) {
+        // Direct staging: iteration it computes the tile in buffer bc (it %
+        // NBUF) while the tiles up to it + PD are in flight.
+        constexpr int PD = C::NBUF - 1;
+        int bc = 0;
+        auto begin = [&](int it) {
+            // this wave's loads of tile it have landed (the PD - 1 tiles behind
+            // it may still be in flight) and its LDS reads of tile it - 1 are
+            // done; past the barrier every wave's loads have landed and the
+            // buffer of tile it - 1 takes tile it + PD
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((PD - 1) * C::DPW) : "memory");
+            if constexpr (!C::PRIVATE) __builtin_amdgcn_s_barrier();
+            const int b = bc + PD < C::NBUF ? bc + PD : bc + PD - C::NBUF;
+            dma(ksg + (it + PD) * KSPLIT, b);
+        };
+        auto end = [&]() { bc = bc + 1 < C::NBUF ? bc + 1 : 0; };
+        int it0 = 0;
+        if (n_iter > 0) {
+            // iteration 0: the split's first tile sets the reference
+            begin(0);
+            scores(bc);
+            if (!full_tile(ksg)) mask(ksg);
+            m_run = tile_max();   // -inf for a lane that sees no row of the split
+            m_seed = m_run == -INFINITY ? 0.f : m_run;
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) negm[rr] = -m_seed;
+            const float lt = weights(std::true_type{}, -m_seed);
+            l_peak = lt;
+            l_run = lt;
+            values();
+            end();
+            it0 = 1;
+        }
+#pragma unroll 1
+        for (int it = it0; it < n_fast; ++it) {   // full tiles: no mask
+            begin(it);
+            scores(bc);
+            const float lt = weights(std::false_type{}, 0.f);
+            l_peak = fmaxf(l_peak, lt);
+            l_run += lt;
+            values();
+            end();
+        }
+#pragma unroll 1
+        for (int it = it0 > n_fast ? it0 : n_fast; it < n_iter; ++it) {
+            const int t = ksg + it * KSPLIT;
+            begin(it);
+            scores(bc);
+            if (!full_tile(t)) mask(t);   // (a split past its last tile: wholly masked)
+            const float lt = weights(std::false_type{}, 0.f);
+            l_peak = fmaxf(l_peak, lt);
+            l_run += lt;
+            values();
+            end();
+        }
+        // the loads issued past the split's last tile (zeros) land before the
+        // buffers are reused
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
         // iteration 0: the split's first tile sets the reference
         int it0 = 0;
         if (n_iter > 0) {
@@ -562,8 +699,13 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
 #pragma unroll 1
         for (int it = 0; it < n_iter; ++it) {
             const int t = ksg + it * KSPLIT;
-            gload(t, kreg[0], vreg[0]);
-            lstore(0, kreg[0], vreg[0]);
+            if constexpr (C::DMA) {
+                dma(t, 0);
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            } else {
+                gload(t, kreg[0], vreg[0]);
+                lstore(0, kreg[0], vreg[0]);
+            }
             __syncthreads();
             if (t < ntiles_kv) {
                 scores(0);
