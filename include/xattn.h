@@ -91,7 +91,10 @@ typedef enum {
     XATTN_EINVAL = -1,        /* invalid argument; nothing enqueued            */
     XATTN_EUNSUPPORTED = -2,  /* valid but not supported (e.g. d_h = 48, bf16) */
     XATTN_EHIP = -3,          /* HIP runtime error                             */
-    XATTN_EWORKSPACE = -4     /* workspace NULL or smaller than required       */
+    XATTN_EWORKSPACE = -4,    /* workspace NULL or smaller than required       */
+    XATTN_EDEVICE_VALIDATION = -5  /* xattn_device_error: the device found the
+                                      offset arrays inconsistent with the host
+                                      totals (nothing was computed)          */
 } xattn_status;
 
 typedef enum { XATTN_BF16 = 0, XATTN_FP32 = 1 } xattn_dtype;
@@ -225,9 +228,13 @@ xattn_status xattn_forward_prefix(xattn_ctx* ctx,
  * Eq. (7): the denominator of the row's softmax over its request's memory).
  *   - lse [total_cand][q][heads] fp32, device, written: the base-2 logarithm
  *     of sum_j exp(q_h . k_{h,j} / sqrt(d_h)) over the rows j the row sees,
- *     with q_h the bf16 projected query (as the products use it: scaled by
- *     log2(e)/sqrt(d_h) and rounded to bf16); -inf for a row that sees no
- *     memory.
+ *     with q_h the bf16 projected query as the products use it: scaled by
+ *     log2(e)/sqrt(d_h) and rounded to bf16 once more - except on the
+ *     short-memory path (XATTN_PATH_SHORT), whose products use the query
+ *     rounded once and scale the fp32 scores, so its lse belongs to those
+ *     scores (xattn_backward_saved recomputes with the pre-scaled query, so
+ *     there the weights it forms sum to 1 only up to that rounding); -inf for
+ *     a row that sees no memory.
  * O, the workspace, the launches and the other arguments as for
  * xattn_forward (or xattn_forward_prefix).  bf16 contexts only
  * (XATTN_EUNSUPPORTED otherwise); a NULL lse with total_cand > 0 is
@@ -335,6 +342,10 @@ xattn_status xattn_backward(xattn_ctx* ctx,
                             void* dZ, float* dW_Q, void* dK, void* dV,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* (dO, and O where given, are read in 16-byte pieces: rows of d bf16
+ * elements, so the base pointers must be 16-byte aligned - XATTN_EINVAL
+ * otherwise, for both backward entry points.) */
+
 /* xattn_backward from the statistics of xattn_forward_train: O
  * [total_cand][q][d] bf16 (16-byte aligned, as dO) and lse
  * [total_cand][q][heads] fp32 are that call's outputs for the same inputs
@@ -435,7 +446,11 @@ xattn_status xattn_forward_codec(xattn_ctx* ctx, const xattn_codebook* cb_k,
                                  void* stream);
 
 /* Varlen plan alone (integer outputs, for callers that want the row map and
- * for tests).  Writes, on the device:
+ * for tests).  The pages pack ragged requests without padding (ReST reading
+ * note s.5.5: padding removal; HELIX card, "Sequence Modeling": padding-free
+ * variable-length execution; TransX report s.2: each request's memory goes to
+ * that request's candidates); this is the work list of that packing.
+ * Writes, on the device:
  *   cu_q[r]      = q * cu_cand[r]                (R+1 entries)
  *   row_req[row] = r for cu_q[r] <= row < cu_q[r+1]   (total_cand*q entries;
  *                  may be NULL)
@@ -515,7 +530,9 @@ xattn_status xattn_output(xattn_ctx* ctx, const void* Z, const void* W_go, const
 /* Synchronise `stream` and read the device-side validation flag a previous
  * xattn_forward / xattn_plan left in `workspace`: *flag = 0 when the offset
  * arrays were consistent, otherwise a bitmask (1: cu_seqlens_kv, 2: cu_cand).
- * Clears nothing. */
+ * Returns XATTN_OK when the flag is 0 and XATTN_EDEVICE_VALIDATION when it is
+ * not (that call then computed nothing); XATTN_EINVAL / XATTN_EHIP when the
+ * flag could not be read.  Clears nothing. */
 xattn_status xattn_device_error(xattn_ctx* ctx, const void* workspace,
                                 int32_t* flag, void* stream);
 

@@ -640,9 +640,12 @@ xattn_status run_backward(xattn_ctx* ctx, const void* Z, const void* W_Q, const 
         return fail(XATTN_EUNSUPPORTED, "stored statistics need a bf16 context");
     if (saved && total_cand > 0 && (!O_saved || !lse_saved))
         return fail(XATTN_EINVAL, "NULL O or lse");
-    if (saved && total_cand > 0 &&
-        ((reinterpret_cast<uintptr_t>(O_saved) | reinterpret_cast<uintptr_t>(dO)) & 15) != 0)
-        return fail(XATTN_EINVAL, "O and dO must be 16-byte aligned");
+    // dO (and the stored O) are read in 16-byte pieces by both paths
+    if (total_cand > 0 &&
+        ((reinterpret_cast<uintptr_t>(saved ? O_saved : nullptr) |
+          reinterpret_cast<uintptr_t>(dO)) & 15) != 0)
+        return fail(XATTN_EINVAL, saved ? "O and dO must be 16-byte aligned"
+                                        : "dO must be 16-byte aligned");
     if (!sep && (V || dV))
         return fail(XATTN_EINVAL, "V and dV must be NULL in XATTN_KV_SHARED mode (dK is dH)");
     if (!cu_kv || !cu_cand) return fail(XATTN_EINVAL, "NULL offset array");
@@ -1135,6 +1138,11 @@ xattn_status xattn_device_error(xattn_ctx* ctx, const void* workspace, int32_t* 
                   sizeof v, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(e, "hipMemcpy");
     *flag = v;
+    if (v != 0)
+        return fail(XATTN_EDEVICE_VALIDATION,
+                    "the device found the offset arrays inconsistent (flag %d: %s%s)", v,
+                    (v & xattn::kErrCuKv) ? "cu_seqlens_kv " : "",
+                    (v & xattn::kErrCuCand) ? "cu_cand" : "");
     return XATTN_OK;
 }
 

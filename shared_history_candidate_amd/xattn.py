@@ -19,6 +19,7 @@ _LIB_PATH = os.environ.get("XATTN_LIB") or os.path.join(
 _lib = None
 
 XATTN_OK, XATTN_EINVAL, XATTN_EUNSUPPORTED, XATTN_EHIP, XATTN_EWORKSPACE = 0, -1, -2, -3, -4
+XATTN_EDEVICE_VALIDATION = -5
 XATTN_BF16, XATTN_FP32 = 0, 1
 XATTN_KV_SHARED, XATTN_KV_SEPARATE = 0, 1
 
@@ -576,10 +577,15 @@ class XAttn:
         return Y
 
     def device_error(self, workspace, stream=None) -> int:
-        """Synchronise and read the device-side offset-validation flag."""
+        """Synchronise and read the device-side offset-validation flag (0: the
+        offsets were consistent; else 1 = cu_seqlens_kv, 2 = cu_cand).  The C
+        call reports a set flag as XATTN_EDEVICE_VALIDATION; here the flag is
+        returned either way."""
         flag = ctypes.c_int32(0)
-        _check(lib().xattn_device_error(self._h, _ptr(workspace), ctypes.byref(flag),
-                                        _stream(workspace.device, stream)))
+        st = lib().xattn_device_error(self._h, _ptr(workspace), ctypes.byref(flag),
+                                      _stream(workspace.device, stream))
+        if st not in (XATTN_OK, XATTN_EDEVICE_VALIDATION):
+            _check(st)
         return flag.value
 
 

@@ -302,6 +302,9 @@ def test_backward_host_validation(L):
     assert bwd(ws=None) == X.XATTN_EWORKSPACE
     assert bwd(wsb=need - 1) == X.XATTN_EWORKSPACE
     assert bwd(R=0, tc=5, tkv=0) == X.XATTN_EINVAL
+    # dO is read in 16-byte pieces by the plain backward as by the saved one
+    assert bwd(dO=ctypes.c_void_p(0x10008)) == X.XATTN_EINVAL
+    assert "16-byte" in L.xattn_last_error().decode()
     L.xattn_destroy(h)
     st, h = _create(L, 256, 1, X.XATTN_BF16, X.XATTN_KV_SEPARATE)
     need = L.xattn_backward_workspace_size(h, 2, 10, 20, 4)
@@ -429,4 +432,42 @@ def test_forward_noalloc_host_validation(L):
     st, h = _create(L, 256, 1, X.XATTN_BF16, X.XATTN_KV_SEPARATE)
     L.xattn_forward_path.restype = ctypes.c_int32
     assert L.xattn_forward_path(h, 256, 262144, 256 * 96, 4) == X.PATH_SHORT
+    L.xattn_destroy(h)
+
+
+def _enum_values(src, name):
+    """name = value pairs of the C enum typedef'd as `name` in a header."""
+    body = re.search(r"typedef enum \{([^{}]*)\}\s*%s;" % name, src).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    return {k: int(v) for k, v in re.findall(r"(XATTN_\w+)\s*=\s*(-?\d+)", body)}
+
+
+def test_header_contract_matches_binding():
+    """The status, dtype, memory-mode and path enums of include/xattn.h (the
+    documented contract, status XATTN_EDEVICE_VALIDATION included) are the
+    values the binding uses; the no-alloc scratch size is the header's."""
+    src = open(os.path.join(ROOT, "include", "xattn.h")).read()
+    assert _enum_values(src, "xattn_status") == {
+        "XATTN_OK": X.XATTN_OK, "XATTN_EINVAL": X.XATTN_EINVAL,
+        "XATTN_EUNSUPPORTED": X.XATTN_EUNSUPPORTED, "XATTN_EHIP": X.XATTN_EHIP,
+        "XATTN_EWORKSPACE": X.XATTN_EWORKSPACE,
+        "XATTN_EDEVICE_VALIDATION": X.XATTN_EDEVICE_VALIDATION}
+    assert _enum_values(src, "xattn_dtype") == {"XATTN_BF16": X.XATTN_BF16,
+                                                 "XATTN_FP32": X.XATTN_FP32}
+    assert _enum_values(src, "xattn_kv_mode") == {"XATTN_KV_SHARED": X.XATTN_KV_SHARED,
+                                                   "XATTN_KV_SEPARATE": X.XATTN_KV_SEPARATE}
+    assert _enum_values(src, "xattn_path") == {"XATTN_PATH_SINGLE": X.PATH_SINGLE,
+                                                "XATTN_PATH_GEMM": X.PATH_GEMM,
+                                                "XATTN_PATH_FP32": X.PATH_FP32,
+                                                "XATTN_PATH_SHORT": X.PATH_SHORT}
+    m = re.search(r"#define XATTN_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == X.NOALLOC_SCRATCH_BYTES
+    # documented layouts the kernels rely on: output-major W_Q, slot-minor rows
+    assert "W_Q   [q][d][d]            output-major" in src
+    assert "row c*q+s is slot s of cand c" in src
+
+
+def test_device_error_null_flag(L):
+    st, h = _create(L, 256, 3, X.XATTN_BF16, X.XATTN_KV_SHARED)
+    assert L.xattn_device_error(h, FAKE, None, None) == X.XATTN_EINVAL
     L.xattn_destroy(h)

@@ -4,6 +4,8 @@ relative <= 1e-4; integer plan outputs bit-exact.  The benchmark workloads
 run at full size with seeds 0-4: every row where the host oracle is fast
 enough (tiny, rest, ragged, transx), and on the long history the rows of
 every (request, slot, 32-candidate block) work item."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -265,6 +267,10 @@ def test_device_validation_flags_bad_offsets():
     O = torch.full((wl.total_cand, wl.q, wl.d), 7.0, dtype=torch.bfloat16, device="cuda")
     bad_kv = torch.tensor([0, 25, 20], dtype=torch.int32, device="cuda")  # decreasing
     ctx.forward(t["Z"], t["W_Q"], t["K"], None, bad_kv, t["cu_cand"], wl.heads, O=O, workspace=ws)
+    flag = ctypes.c_int32(0)
+    st = X.lib().xattn_device_error(ctx._h, ctypes.c_void_p(ws.data_ptr()), ctypes.byref(flag),
+                                    None)
+    assert st == X.XATTN_EDEVICE_VALIDATION and flag.value == 1
     assert ctx.device_error(ws) == 1
     assert torch.all(O == 7.0)
     bad_c = torch.tensor([0, 4, 9], dtype=torch.int32, device="cuda")  # cu[R] != total_cand
