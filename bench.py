@@ -457,7 +457,7 @@ def main():
         micro()
         return
 
-    import numpy as np  # noqa: F401
+    import numpy as np
     import torch
     from shared_history_candidate_amd import workloads as W
     from shared_history_candidate_amd import xattn as X
@@ -540,9 +540,14 @@ def main():
                                  stream=stream, cand_kv_len=cl, O=O_tr, lse=lse_tr)
         elif args.stage == "codec":
             # memory published as codes + norms (encoded once, outside the step)
+            # codebooks fitted by the library on a sample of the memory rows
+            # (offline calibration, not part of a step)
             budget = int(round(args.codec_bits * wl.d_h / 32.0)) * 32
-            books = [W.timing_codebook(wl.heads, wl.d_h, budget, args.seed + 5 + i)
-                     for i in range(2)]
+            rng = np.random.default_rng(args.seed + 5)
+            pick = np.sort(rng.choice(wl.total_kv, min(wl.total_kv, 4096), replace=False))
+            mem = [wl.K] + ([wl.V] if wl.V is not None else [])
+            books = [X.codec_fit(m[pick], wl.heads, budget) for m in mem]
+            books += books[:1] * (2 - len(books))
             cbs = [X.Codebook(b["bits"], b["center"], b["half"], b["rot"], b["budget"])
                    for b in books]
             kc, kn = ctx.codec_encode(cbs[0], t["K"])

@@ -393,6 +393,28 @@ typedef struct {
     const float* rotation;    /* [heads][d_h][d_h]                            */
 } xattn_codebook;
 
+/* Fit a codebook on the host from a calibration sample of memory rows
+ * (TransX report s.3: the directions' covariance is estimated on a sample,
+ * the rotation is its full eigenvector matrix, bits go by energy under a
+ * fixed total).  Offline calibration, fp64 inside, all pointers host memory:
+ *   - X [n_rows][d_model] fp32: the sample (key rows for a key codebook,
+ *     value rows for a value codebook);
+ *   - per head h, over the directions u = x_h / |x_h| of the rows with
+ *     |x_h| > 0: mean mu and centred covariance C = E diag(lam) E^T, lam
+ *     descending (ties keep their order), each column of E signed so that
+ *     its largest-magnitude entry is positive;
+ *   - outputs, layouts of xattn_codebook: rotation[h] = E (row-major,
+ *     column i = eigenvector i), center[h] = E^T mu, half_range[h] =
+ *     3 sqrt(max(lam, 0)), bits[h] = integers in [0, 8] summing to
+ *     budget_bits, handed out one at a time to the largest lam_i 4^-b_i
+ *     (lower index on ties).
+ * Errors: XATTN_EINVAL for NULL pointers, n_rows < 1, heads not dividing
+ * d_model, or a head whose sample slices are all zero; XATTN_EUNSUPPORTED
+ * for budget_bits outside [0, 8 d_h].  Enqueues nothing. */
+xattn_status xattn_codec_fit(int32_t d_model, int32_t heads, const float* X, int64_t n_rows,
+                             int32_t budget_bits, uint8_t* bits, float* center,
+                             float* half_range, float* rotation);
+
 /* Encode memory rows X [n_rows][d] (bf16) with codebook cb into codes and
  * norms (layouts above).  The nearline publishing step. */
 xattn_status xattn_codec_encode(xattn_ctx* ctx, const xattn_codebook* cb, int32_t heads,

@@ -30,7 +30,7 @@ EXPORTED = ("xattn_create", "xattn_destroy", "xattn_workspace_size", "xattn_forw
             "xattn_backward_workspace_size", "xattn_backward", "xattn_codec_encode",
             "xattn_codec_fold_query_weights", "xattn_forward_codec", "xattn_forward_path",
             "xattn_codec_workspace_size", "xattn_forward_train", "xattn_backward_saved",
-            "xattn_forward_noalloc")
+            "xattn_forward_noalloc", "xattn_codec_fit")
 
 # include/xattn.h: bytes of the library-owned scratch of xattn_forward_noalloc
 NOALLOC_SCRATCH_BYTES = 32 << 20
@@ -66,6 +66,27 @@ class Codebook:
     def struct(self) -> CodebookStruct:
         return CodebookStruct(self.budget_bits, self.bits.data_ptr(), self.center.data_ptr(),
                               self.half_range.data_ptr(), self.rotation.data_ptr())
+
+
+def codec_fit(X, heads: int, budget_bits: int) -> dict:
+    """Codebook fitted by the library on the host (xattn_codec_fit) from a
+    calibration sample X [n, d] (array-like, read as fp32): dict of bits
+    uint8 [heads, d_h], center, half and rot fp32, budget (what Codebook
+    takes)."""
+    import numpy as np
+    Xh = np.ascontiguousarray(np.asarray(X, dtype=np.float32))
+    n, d = Xh.shape
+    dh = d // heads
+    bits = np.zeros((heads, dh), dtype=np.uint8)
+    center = np.zeros((heads, dh), dtype=np.float32)
+    half = np.zeros((heads, dh), dtype=np.float32)
+    rot = np.zeros((heads, dh, dh), dtype=np.float32)
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    st = lib().xattn_codec_fit(d, heads, p(Xh), n, int(budget_bits), p(bits), p(center), p(half),
+                               p(rot))
+    if st != XATTN_OK:
+        raise XAttnError(st, "xattn_codec_fit rejected its arguments")
+    return {"bits": bits, "center": center, "half": half, "rot": rot, "budget": int(budget_bits)}
 
 
 class Config(ctypes.Structure):
@@ -131,6 +152,8 @@ def lib():
                                            P, P, P, P, SZ, P]
         L.xattn_backward_saved.restype = ctypes.c_int
         CB = ctypes.POINTER(CodebookStruct)
+        L.xattn_codec_fit.argtypes = [I32, I32, P, I64, I32, P, P, P, P]
+        L.xattn_codec_fit.restype = ctypes.c_int
         L.xattn_codec_encode.argtypes = [P, CB, I32, P, I32, P, P, P]
         L.xattn_codec_encode.restype = ctypes.c_int
         L.xattn_codec_fold_query_weights.argtypes = [P, CB, I32, P, P, P]
