@@ -42,12 +42,22 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found: the ROCm toolchain is required to build libxattn")
 
 
-def _compile(src: str, obj: str, verbose: bool) -> None:
+# Host-side AddressSanitizer build (build(asan=True)): the host code of every
+# source is instrumented, the device code is not (-Xarch_host keeps the flag
+# off the gfx950 pass).  For host checks of the C ABI on a machine without a
+# GPU; the product library is the plain build.
+ASAN_HOST_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer",
+                   "-shared-libasan"]
+
+
+def _compile(src: str, obj: str, verbose: bool, asan: bool = False) -> None:
     extra = os.environ.get("XATTN_EXTRA_HIPCC_FLAGS", "").split()   # tuning experiments
+    if asan:
+        extra = extra + ASAN_HOST_FLAGS
     cmd = [_hipcc()] + HIPCC_FLAGS + extra + ["-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd = [_hipcc(), "-O3", "-std=c++17", "-fPIC", "-Wall", "-I" + INCLUDE, "-I" + CSRC,
-               "-c", src, "-o", obj]
+               "-c", src, "-o", obj] + (ASAN_HOST_FLAGS if asan else [])
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -58,15 +68,20 @@ def _compile(src: str, obj: str, verbose: bool) -> None:
         print(errs)
 
 
-def build(verbose: bool = False, jobs: int = 8, out: str = LIB) -> str:
-    """Compile every HIP/C++ source under csrc/ and link libxattn.so (or `out`)."""
-    os.makedirs(OBJDIR, exist_ok=True)
+def build(verbose: bool = False, jobs: int = 8, out: str = LIB, asan: bool = False) -> str:
+    """Compile every HIP/C++ source under csrc/ and link libxattn.so (or `out`);
+    asan=True instruments the host code with AddressSanitizer (objects kept
+    apart from the plain build's)."""
+    objdir = OBJDIR + ("_asan" if asan else "")
+    os.makedirs(objdir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
-    objs = [os.path.join(OBJDIR, os.path.basename(s) + ".o") for s in srcs]
+    objs = [os.path.join(objdir, os.path.basename(s) + ".o") for s in srcs]
     with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
-        list(ex.map(lambda so: _compile(so[0], so[1], verbose), zip(srcs, objs)))
+        list(ex.map(lambda so: _compile(so[0], so[1], verbose, asan), zip(srcs, objs)))
     tmp = out + ".tmp%d" % os.getpid()
     cmd = [_hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
+    if asan:
+        cmd += ["-fsanitize=address", "-shared-libasan"]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -78,4 +93,8 @@ def build(verbose: bool = False, jobs: int = 8, out: str = LIB) -> str:
 
 if __name__ == "__main__":
     import sys
-    print(build(verbose="-v" in sys.argv))
+    if "--asan" in sys.argv:
+        # python -m shared_history_candidate_amd.build --asan OUT.so
+        print(build(verbose="-v" in sys.argv, asan=True, out=sys.argv[sys.argv.index("--asan") + 1]))
+    else:
+        print(build(verbose="-v" in sys.argv))
