@@ -38,6 +38,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 CONFIGS = ("rest", "long", "transx", "ragged", "tiny")
 _ATTN_SRC = ["shared_history_candidate_amd/csrc/attn_bf16.hip",
+             "shared_history_candidate_amd/csrc/lds_dma.h",
              "shared_history_candidate_amd/csrc/plan_wave.h",
              "shared_history_candidate_amd/csrc/common.h"]
 KERNEL_SOURCES = {"fused": _ATTN_SRC, "attention": _ATTN_SRC, "prefix": _ATTN_SRC,

@@ -38,6 +38,7 @@
 
 #include "common.h"
 #include "internal.h"
+#include "lds_dma.h"
 #include "plan_wave.h"
 
 namespace xattn {
@@ -54,23 +55,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Widest model the fused projection stages in LDS.
 constexpr int kProjMaxD = kAttnProjMaxD;
-
-// One direct global-to-LDS load: every lane's 16 bytes at byte offset voff of
-// the buffer land in LDS at lds_addr + 16 * lane.  Written out (M0 set in the
-// same block) because the compiler, seeing an LDS-writing load, would make the
-// next LDS read of any buffer wait for it; the kernel instead waits for these
-// loads explicitly (s_waitcnt vmcnt) before the barrier that publishes a
-// tile, and before the tile buffers are reused for anything else.  The load
-// writes no register.
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_addr, int voff) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 ::"s"(lds_addr), "v"(voff), "s"(rsrc)
-                 : "memory", "m0");
-}
-
-__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-}
 
 template <int DH, int RB, int KSPLIT, bool SEP, bool PROJ, bool CUT = false>
 struct Cfg {
