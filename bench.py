@@ -314,10 +314,18 @@ def calib_copy(mib):
     b = torch.empty_like(a)
     st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     ms = L.xattn_micro_copy(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(b.data_ptr()), n, 5, st)
+    L.xattn_micro_half_line_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                             ctypes.c_void_p, ctypes.c_void_p]
+    L.xattn_micro_half_line_read.restype = ctypes.c_float
+    out = torch.empty(256 * 8 * 256, dtype=torch.float32, device="cuda")
+    ms_half = L.xattn_micro_half_line_read(ctypes.c_void_p(a.data_ptr()), n, 5,
+                                           ctypes.c_void_p(out.data_ptr()), st)
     torch.cuda.synchronize()
     print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n,
                       "launches": 6, "ms_per_copy": round(ms, 4),
-                      "copy_gbs": round(2.0 * n / (ms * 1e-3) / 1e9, 1)}))
+                      "copy_gbs": round(2.0 * n / (ms * 1e-3) / 1e9, 1),
+                      "half_line_read_bytes": n // 2, "half_line_launches": 6,
+                      "ms_per_half_line_read": round(ms_half, 4)}))
 
 
 def settle(step, stream, ms):

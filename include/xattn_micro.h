@@ -22,8 +22,16 @@ extern "C" {
 float xattn_micro_run(int kind, int blocks, int iters, int reps, float* out, void* stream);
 
 /* Device-to-device copy of `bytes` (a multiple of 16) from a to b, timed over
- * `reps` launches; returns average milliseconds per launch. */
+ * `reps` launches; returns average milliseconds per launch.  Each lane keeps
+ * four 16-byte loads in flight before storing them (kernel copy_kernel). */
 float xattn_micro_copy(const void* a, void* b, int64_t bytes, int reps, void* stream);
+
+/* Reads the first 64 bytes of every 128-byte line of the `bytes` (a multiple
+ * of 128, else -1) at device address a, timed over `reps` launches; `out` is
+ * device memory of 524288 floats (written).  The known-size reference of the
+ * read counters for 64-byte slices of 128-byte rows (kernel
+ * half_line_read_kernel): bytes / 2 useful bytes per launch. */
+float xattn_micro_half_line_read(const void* a, int64_t bytes, int reps, float* out, void* stream);
 
 #ifdef __cplusplus
 }

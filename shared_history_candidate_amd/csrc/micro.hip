@@ -96,10 +96,32 @@ __global__ __launch_bounds__(256) void lds_loop(int iters, float* out) {
     out[blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
+// Grid-stride copy, U 16-byte loads in flight per lane before their stores.
+template <int U>
 __global__ void copy_kernel(const uint4* __restrict__ a, uint4* __restrict__ b, int64_t n) {
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-         i += (int64_t)gridDim.x * blockDim.x)
-        b[i] = a[i];
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + (U - 1) * stride < n; i += U * stride) {
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = a[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < U; ++u) b[i + u * stride] = v[u];
+    }
+    for (; i < n; i += stride) b[i] = a[i];
+}
+
+// Reads the first 64 bytes of every 128-byte line (four lanes per line, 16
+// bytes each): the access of a 64-byte head slice of 128-byte memory rows.
+// One value per thread is written so that the loads are kept.
+__global__ void half_line_read_kernel(const uint4* __restrict__ a, int64_t lines, float* out) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    uint32_t acc = 0;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < lines * 4; i += stride) {
+        const uint4 v = a[(i >> 2) * 8 + (i & 3)];
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = (float)acc;
 }
 
 template <typename F>
@@ -150,8 +172,21 @@ float xattn_micro_copy(const void* a, void* b, int64_t bytes, int reps, void* st
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t n = bytes / 16;
     return time_ms([&] {
-        hipLaunchKernelGGL(copy_kernel, dim3(256 * 16), dim3(256), 0, s,
+        hipLaunchKernelGGL(copy_kernel<4>, dim3(256 * 8), dim3(256), 0, s,
                            static_cast<const uint4*>(a), static_cast<uint4*>(b), n);
+    }, reps, s);
+}
+
+// Reads the first 64 bytes of each 128-byte line of `bytes` (a multiple of
+// 128) at a; `out` is device scratch of 256 * 8 * 256 floats.  Returns
+// average milliseconds per launch (negative on error).
+float xattn_micro_half_line_read(const void* a, int64_t bytes, int reps, float* out, void* stream) {
+    using namespace xattn;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (bytes % 128 != 0 || bytes <= 0) return -1.f;
+    return time_ms([&] {
+        hipLaunchKernelGGL(half_line_read_kernel, dim3(256 * 8), dim3(256), 0, s,
+                           static_cast<const uint4*>(a), bytes / 128, out);
     }, reps, s);
 }
 
