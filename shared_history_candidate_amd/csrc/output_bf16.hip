@@ -15,11 +15,12 @@
 // registers as A operands (reloaded only when the slot changes).  Per unit:
 //   1. the unit's Z rows (staged in LDS, loaded into registers one unit
 //      ahead) give G^T rows 32w.. = W_go[s] rows 32w.. . Z^T on the matrix
-//      cores; the unit's O values are loaded straight into the accumulator's
-//      layout;
+//      cores; the unit's O values are loaded 16 bytes per lane and moved
+//      into the accumulator's layout by an exchange between the lane halves;
 //   2. gated = O * sigmoid(G), rounded to bf16, replaces the Z rows in LDS;
 //   3. Y^T rows 32w.. = W_o rows 32w.. . gated^T, rounded to bf16 and stored
-//      through a descriptor that covers the unit's rows only.
+//      16 bytes per lane (the same exchange) through a descriptor that covers
+//      the unit's rows only.
 #include "common.h"
 #include "internal.h"
 
@@ -36,6 +37,7 @@ constexpr int Z_CPT = UR * (D / 8) / NT;   // 16-byte Z chunks per thread
 static_assert(UR * (D / 8) % NT == 0, "even staging split");
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 struct OutArgs {
     const bf16* Z;
@@ -117,19 +119,19 @@ __global__ __launch_bounds__(NT) void gate_output_kernel(OutArgs a) {
         int s2 = s, cb2 = cb, nr2 = nr;
         if (has_next) unit(u + 1, s2, cb2, nr2);
         __syncthreads();   // the unit's Z rows are in LDS
-        // O values in the accumulator's layout (rows 32rb + l32, features
-        // 32w + 8j4 + 4g .. +3), requested before the next unit's Z rows:
-        // the vector-memory counter completes in order, so waiting for them
-        // in the gate epilogue does not wait for the Z rows
+        // O rows 32rb + l32, features 32w + 16jp + 8g .. +7 (16 bytes per
+        // lane), requested before the next unit's Z rows: the vector-memory
+        // counter completes in order, so waiting for them in the gate
+        // epilogue does not wait for the Z rows
         const __amdgpu_buffer_rsrc_t ro = rows_rsrc(a.O, s, cb, nr);
-        u32x2 ov[2][4];
+        u32x4 ol[2][2];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-            for (int j4 = 0; j4 < 4; ++j4)
-                ov[rb][j4] = __builtin_bit_cast(
-                    u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                               ro, ((rb * 32 + l32) * q * D + 32 * w + 8 * j4 + 4 * g) * 2, 0, 0));
+            for (int jp = 0; jp < 2; ++jp)
+                ol[rb][jp] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                               ro, ((rb * 32 + l32) * q * D + 32 * w + 16 * jp + 8 * g) * 2, 0, 0));
         if (has_next) zload(s2, cb2, nr2);
         if (s != wslot) {
             // a new slot (rare): wait for its rows here
@@ -151,7 +153,22 @@ __global__ __launch_bounds__(NT) void gate_output_kernel(OutArgs a) {
         __syncthreads();   // every wave is done reading Z
 
         // 2. gated = O * sigmoid(G), bf16, into LDS (acc reg 4*j4 + t:
-        //    feature 32w + 8j4 + 4g + t of row 32rb + l32)
+        //    feature 32w + 8j4 + 4g + t of row 32rb + l32).  A lane holds
+        //    features 16jp + 8g .. +7 of O; one v_permlane32_swap per dword
+        //    (upper lanes of the first operand <-> lower lanes of the second)
+        //    leaves runs j4 = 2jp and 2jp + 1 of the accumulator layout.
+        u32x2 ov[2][4];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int jp = 0; jp < 2; ++jp)
+#pragma unroll
+                for (int dw = 0; dw < 2; ++dw) {
+                    const auto sw = __builtin_amdgcn_permlane32_swap(ol[rb][jp][dw], ol[rb][jp][2 + dw],
+                                                                     false, false);
+                    ov[rb][2 * jp][dw] = sw[0];
+                    ov[rb][2 * jp + 1][dw] = sw[1];
+                }
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -177,17 +194,25 @@ __global__ __launch_bounds__(NT) void gate_output_kernel(OutArgs a) {
                 acc[rb] = mfma32(wo[kk], *reinterpret_cast<const bf16x8*>(
                                              buf + (rb * 32 + l32) * LDK + 16 * kk + 8 * g),
                                  acc[rb]);
+        // Y rows, 16 bytes per lane: the lane-half exchange joins runs
+        // j4 = 2jp (lower half) and 2jp + 1 (upper half) into whole 8-feature runs
         const __amdgpu_buffer_rsrc_t ry = rows_rsrc(a.Y, s, cb, nr);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-            for (int j4 = 0; j4 < 4; ++j4) {
-                bf16x4 v;
+            for (int jp = 0; jp < 2; ++jp) {
+                bf16x4 ve, vo;
 #pragma unroll
-                for (int t = 0; t < 4; ++t) v[t] = (bf16)acc[rb][4 * j4 + t];
-                __builtin_amdgcn_raw_buffer_store_b64(
-                    __builtin_bit_cast(u32x2, v), ry,
-                    ((rb * 32 + l32) * q * D + 32 * w + 8 * j4 + 4 * g) * 2, 0, 0);
+                for (int t = 0; t < 4; ++t) {
+                    ve[t] = (bf16)acc[rb][8 * jp + t];
+                    vo[t] = (bf16)acc[rb][8 * jp + 4 + t];
+                }
+                const u32x2 pe = __builtin_bit_cast(u32x2, ve), po = __builtin_bit_cast(u32x2, vo);
+                const auto s0 = __builtin_amdgcn_permlane32_swap(pe[0], po[0], false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(pe[1], po[1], false, false);
+                const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    v, ry, ((rb * 32 + l32) * q * D + 32 * w + 16 * jp + 8 * g) * 2, 0, 0);
             }
         if (!has_next) break;
         __syncthreads();   // every wave is done reading the gated rows
