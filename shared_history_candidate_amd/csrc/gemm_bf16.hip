@@ -225,7 +225,11 @@ __global__ __launch_bounds__(256) void prep_kernel(const bf16* __restrict__ Z,
     }
 
     // accumulator (i, j) reg 4*b4 + t holds o = e0 + wr*TE/2 + 32i + 8*b4 + 4g + t
-    // for candidate c0 + wc*TC/2 + 32j + l32
+    // for candidate c0 + wc*TC/2 + 32j + l32.  Runs b4 = 2bp and 2bp + 1 are
+    // exchanged between the lane halves (join_runs / split_runs, common.h),
+    // so that each lane stores (and, gated, loads) 16 bytes: features
+    // 16bp + 8g .. +7 of the 32-wide block.  Both halves of a pair hold the
+    // same candidate, so they skip (c past the batch) together.
 #pragma unroll
     for (int j = 0; j < C::BC; ++j) {
         const int c = c0 + wc * (TC / 2) + j * 32 + l32;
@@ -234,29 +238,41 @@ __global__ __launch_bounds__(256) void prep_kernel(const bf16* __restrict__ Z,
 #pragma unroll
         for (int i = 0; i < C::BE; ++i)
 #pragma unroll
-            for (int b4 = 0; b4 < 4; ++b4) {
-                const int o = e0 + wr * (TE / 2) + i * 32 + b4 * 8 + 4 * g;
-                if (o < d) {
-                    bf16x4 v;
-                    if (Og) {
-                        const bf16x4 ov =
-                            *reinterpret_cast<const bf16x4*>(Og + ((size_t)c * q + s) * d + o);
+            for (int bp = 0; bp < 2; ++bp) {
+                const int o0 = e0 + wr * (TE / 2) + i * 32 + 16 * bp;   // the pair's first feature
+                const int o = o0 + 8 * g;                                 // this lane's run
+                bf16x4 v[2];
+                if (Og) {
+                    u32x2 og[2] = {u32x2{0u, 0u}, u32x2{0u, 0u}};
+                    if (o0 < d) {
+                        const u32x4 ol = o < d ? *reinterpret_cast<const u32x4*>(Og + ((size_t)c * q + s) * d + o)
+                                               : u32x4{0u, 0u, 0u, 0u};
+                        split_runs(ol, og[0], og[1]);
+                    }
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const bf16x4 ov = __builtin_bit_cast(bf16x4, og[h2]);
 #pragma unroll
                         for (int t = 0; t < 4; ++t) {
-                            const float e = __builtin_amdgcn_exp2f(-acc[i][j][4 * b4 + t] *
+                            const float e = __builtin_amdgcn_exp2f(-acc[i][j][8 * bp + 4 * h2 + t] *
                                                                    1.4426950408889634f);
-                            v[t] = (bf16)((float)ov[t] / (1.0f + e));
+                            v[h2][t] = (bf16)((float)ov[t] / (1.0f + e));
                         }
-                    } else if (oscale == 1.0f) {
+                    }
+                } else if (oscale == 1.0f) {
 #pragma unroll
-                        for (int t = 0; t < 4; ++t) v[t] = (bf16)acc[i][j][4 * b4 + t];
-                    } else {
+                    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) v[h2][t] = (bf16)acc[i][j][8 * bp + 4 * h2 + t];
+                } else {
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
                         for (int t = 0; t < 4; ++t)
-                            v[t] = (bf16)((float)(bf16)acc[i][j][4 * b4 + t] * oscale);
-                    }
-                    *reinterpret_cast<bf16x4*>(qrow + o) = v;
+                            v[h2][t] = (bf16)((float)(bf16)acc[i][j][8 * bp + 4 * h2 + t] * oscale);
                 }
+                const u32x4 out = join_runs(v[0], v[1]);
+                if (o < d) *reinterpret_cast<u32x4*>(qrow + o) = out;
             }
     }
 }

@@ -36,8 +36,6 @@ constexpr int LDK = D + 8;   // LDS pitch (elements): 16-byte rows
 constexpr int Z_CPT = UR * (D / 8) / NT;   // 16-byte Z chunks per thread
 static_assert(UR * (D / 8) % NT == 0, "even staging split");
 
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 struct OutArgs {
     const bf16* Z;
@@ -154,21 +152,13 @@ __global__ __launch_bounds__(NT) void gate_output_kernel(OutArgs a) {
 
         // 2. gated = O * sigmoid(G), bf16, into LDS (acc reg 4*j4 + t:
         //    feature 32w + 8j4 + 4g + t of row 32rb + l32).  A lane holds
-        //    features 16jp + 8g .. +7 of O; one v_permlane32_swap per dword
-        //    (upper lanes of the first operand <-> lower lanes of the second)
-        //    leaves runs j4 = 2jp and 2jp + 1 of the accumulator layout.
+        //    features 16jp + 8g .. +7 of O; split_runs leaves runs j4 = 2jp
+        //    and 2jp + 1 of the accumulator layout.
         u32x2 ov[2][4];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-            for (int jp = 0; jp < 2; ++jp)
-#pragma unroll
-                for (int dw = 0; dw < 2; ++dw) {
-                    const auto sw = __builtin_amdgcn_permlane32_swap(ol[rb][jp][dw], ol[rb][jp][2 + dw],
-                                                                     false, false);
-                    ov[rb][2 * jp][dw] = sw[0];
-                    ov[rb][2 * jp + 1][dw] = sw[1];
-                }
+            for (int jp = 0; jp < 2; ++jp) split_runs(ol[rb][jp], ov[rb][2 * jp], ov[rb][2 * jp + 1]);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -194,8 +184,7 @@ __global__ __launch_bounds__(NT) void gate_output_kernel(OutArgs a) {
                 acc[rb] = mfma32(wo[kk], *reinterpret_cast<const bf16x8*>(
                                              buf + (rb * 32 + l32) * LDK + 16 * kk + 8 * g),
                                  acc[rb]);
-        // Y rows, 16 bytes per lane: the lane-half exchange joins runs
-        // j4 = 2jp (lower half) and 2jp + 1 (upper half) into whole 8-feature runs
+        // Y rows, 16 bytes per lane (join_runs)
         const __amdgpu_buffer_rsrc_t ry = rows_rsrc(a.Y, s, cb, nr);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
@@ -207,12 +196,8 @@ __global__ __launch_bounds__(NT) void gate_output_kernel(OutArgs a) {
                     ve[t] = (bf16)acc[rb][8 * jp + t];
                     vo[t] = (bf16)acc[rb][8 * jp + 4 + t];
                 }
-                const u32x2 pe = __builtin_bit_cast(u32x2, ve), po = __builtin_bit_cast(u32x2, vo);
-                const auto s0 = __builtin_amdgcn_permlane32_swap(pe[0], po[0], false, false);
-                const auto s1 = __builtin_amdgcn_permlane32_swap(pe[1], po[1], false, false);
-                const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
                 __builtin_amdgcn_raw_buffer_store_b128(
-                    v, ry, ((rb * 32 + l32) * q * D + 32 * w + 16 * jp + 8 * g) * 2, 0, 0);
+                    join_runs(ve, vo), ry, ((rb * 32 + l32) * q * D + 32 * w + 16 * jp + 8 * g) * 2, 0, 0);
             }
         if (!has_next) break;
         __syncthreads();   // every wave is done reading the gated rows

@@ -59,8 +59,6 @@ constexpr int kRing = 256;       // work items held in LDS at a time
 constexpr float kSumCap = 4096.0f;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 template <int DH, bool SEP, bool CODEC>
 struct SCfg {
@@ -603,12 +601,9 @@ __global__ __launch_bounds__(NT) void short_bf16_kernel(AttnArgs a, ShortCodec c
             if (a.lse && u % C::FP == 0 && g == 0 && urb * 32 + l32 < nr)
                 a.lse[((size_t)(cb + urb * 32 + l32) * q + cur.s) * a.heads + h] =
                     l > 0.f ? m_run[k] + __builtin_amdgcn_logf(l) : -INFINITY;   // v_log_f32 is log2
-            // Register 4*b4 + t of oacc holds feature 32eb + 8b4 + 4g + t: the
-            // two lane halves hold the two 8-byte halves of each 16-byte run.
-            // One v_permlane32_swap per dword (upper lanes of the first operand
-            // <-> lower lanes of the second) gives the lower half the whole run
-            // b4 = 2bp and the upper half the run b4 = 2bp + 1, stored as one
-            // 16-byte store per (eb, bp) instead of two 8-byte stores.
+            // Register 4*b4 + t of oacc holds feature 32eb + 8b4 + 4g + t;
+            // join_runs makes one 16-byte store per (eb, bp) instead of two
+            // 8-byte stores.
             const int off = ((urb * 32 + l32) * q * D + h * DH + e0 + 8 * g) * 2;
 #pragma unroll
             for (int eb = 0; eb < C::EBW; ++eb)
@@ -620,11 +615,8 @@ __global__ __launch_bounds__(NT) void short_bf16_kernel(AttnArgs a, ShortCodec c
                         ve[t] = (bf16)(oacc[k][eb][8 * bp + t] * inv);
                         vo[t] = (bf16)(oacc[k][eb][8 * bp + 4 + t] * inv);
                     }
-                    const u32x2 pe = __builtin_bit_cast(u32x2, ve), po = __builtin_bit_cast(u32x2, vo);
-                    const auto s0 = __builtin_amdgcn_permlane32_swap(pe[0], po[0], false, false);
-                    const auto s1 = __builtin_amdgcn_permlane32_swap(pe[1], po[1], false, false);
-                    const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
-                    __builtin_amdgcn_raw_buffer_store_b128(v, ro, off + (eb * 32 + 16 * bp) * 2, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(join_runs(ve, vo), ro, off + (eb * 32 + 16 * bp) * 2,
+                                                           0, 0);
                 }
         }
         if (!has_next) break;
