@@ -779,21 +779,18 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
         }
     }
     if (qvalid && O) {
-        // Register 4*b4 + t of oacc[eb] holds feature 32eb + 8b4 + 4g + t;
-        // join_runs (both lane halves hold the same query row, so both are
-        // active or neither) makes one 16-byte store per (eb, bp).
+        // (8-byte stores: the 16-byte form of join_runs costs this kernel's
+        // epilogue spill slots, and its output rows are a small share of its
+        // traffic)
         bf16* orow = O + ((size_t)cand * q + s) * d + h * DH;
 #pragma unroll
         for (int eb = 0; eb < C::EB; ++eb) {
 #pragma unroll
-            for (int bp = 0; bp < 2; ++bp) {
-                bf16x4 ve, vo;
+            for (int b4 = 0; b4 < 4; ++b4) {
+                bf16x4 v;
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    ve[t] = (bf16)(oacc[eb][8 * bp + t] * inv);
-                    vo[t] = (bf16)(oacc[eb][8 * bp + 4 + t] * inv);
-                }
-                *reinterpret_cast<u32x4*>(orow + eb * 32 + 16 * bp + 8 * g) = join_runs(ve, vo);
+                for (int t = 0; t < 4; ++t) v[t] = (bf16)(oacc[eb][4 * b4 + t] * inv);
+                *reinterpret_cast<bf16x4*>(orow + eb * 32 + b4 * 8 + 4 * g) = v;
             }
         }
     }
