@@ -22,8 +22,9 @@ extern "C" {
 float xattn_micro_run(int kind, int blocks, int iters, int reps, float* out, void* stream);
 
 /* Device-to-device copy of `bytes` (a multiple of 16) from a to b, timed over
- * `reps` launches; returns average milliseconds per launch.  Each lane keeps
- * four 16-byte loads in flight before storing them (kernel copy_kernel). */
+ * `reps` launches; returns average milliseconds per launch.  256 work-groups,
+ * each lane keeping four 16-byte nontemporal loads in flight before storing
+ * them (kernel copy_kernel). */
 float xattn_micro_copy(const void* a, void* b, int64_t bytes, int reps, void* stream);
 
 /* Reads the first 64 bytes of every 128-byte line of the `bytes` (a multiple
