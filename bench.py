@@ -137,13 +137,14 @@ def kernel_sha(kernel):
 # the kernels a step can run: the single launch of a small batch (attention
 # kernel that projects its own queries: flags PROJ=1, CUT=0), the
 # projection GEMM and the attention kernel over its output (PROJ=0; CUT=1
-# with per-candidate prefix lengths), or the short-memory kernel.
+# with per-candidate prefix lengths; a last flag set for the head-pair form
+# of 32-wide heads), or the short-memory kernel.
 KERNEL_NAMES = {
-    "fused": r"attn_bf16_kernel(<\d+, \d+, \d+, \w+, true, false>|"
+    "fused": r"attn_bf16_kernel(<\d+, \d+, \d+, \w+, true, false(, \w+)?>|"
              r"ILi\d+ELi\d+ELi\d+ELb[01]ELb1ELb0E)",
-    "attention": r"attn_bf16_kernel(<\d+, \d+, \d+, \w+, false, false>|"
+    "attention": r"attn_bf16_kernel(<\d+, \d+, \d+, \w+, false, false(, \w+)?>|"
                  r"ILi\d+ELi\d+ELi\d+ELb[01]ELb0ELb0E)",
-    "prefix": r"attn_bf16_kernel(<\d+, \d+, \d+, \w+, false, true>|"
+    "prefix": r"attn_bf16_kernel(<\d+, \d+, \d+, \w+, false, true(, \w+)?>|"
               r"ILi\d+ELi\d+ELi\d+ELb[01]ELb0ELb1E)",
     "projection": r"prep_kernel",
     "short": r"short_bf16_kernel"}

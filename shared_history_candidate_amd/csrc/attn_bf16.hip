@@ -15,6 +15,11 @@
 // and memory split ks = w / RB (memory tiles t with t % KSPLIT == ks).  The
 // waves of one split share the staged memory tiles; the KSPLIT partial
 // softmax states of a query block are merged through LDS at the end.
+// Head pairs (HS, 32-wide heads, K = V): HBM is read in 128-byte lines and a
+// 32-wide head is half a line of each memory row, so a work-group takes the
+// two heads of a line instead: its two wave groups (ks = 0, 1) attend heads
+// 2p and 2p + 1 over the same staged tiles of both heads' 64 features, with
+// no memory split and no merge.
 //
 // Products are computed transposed so that each lane holds one query row and
 // the softmax reductions along the key axis stay inside the lane (plus one
@@ -56,10 +61,15 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // Widest model the fused projection stages in LDS.
 constexpr int kProjMaxD = kAttnProjMaxD;
 
-template <int DH, int RB, int KSPLIT, bool SEP, bool PROJ, bool CUT = false>
+template <int DH, int RB, int KSPLIT, bool SEP, bool PROJ, bool CUT = false, bool HS = false>
 struct Cfg {
     static constexpr int NW = RB * KSPLIT;
     static constexpr int NT = 64 * NW;
+    // head pairs: the KSPLIT = 2 wave groups are the pair's heads, not memory splits
+    static_assert(!HS || (DH == 32 && KSPLIT == 2 && !SEP && !PROJ && !CUT), "head pairs");
+    static constexpr int MS = HS ? 1 : KSPLIT;       // memory splits
+    static constexpr int DS = HS ? 2 * DH : DH;      // staged features per memory row
+    static constexpr int SG = HS ? NW : RB;          // waves staging one tile
     static constexpr int EB = DH / 32;        // 32-wide feature blocks
     static constexpr int KST = DH / 16;       // k-steps of the score product
     // Memory tiles over caller-projected queries at head width 64 with K = V
@@ -75,17 +85,17 @@ struct Cfg {
     // rows (8) let the score operands come in single 16-byte LDS reads; the
     // separate-K/V tiles measured faster with 8-byte rows (4).
     static constexpr int PAD = DMA ? 0 : (SEP ? 4 : 8);
-    static constexpr int LDK = DH + PAD;      // memory tile pitch (elements)
+    static constexpr int LDK = DS + PAD;      // memory tile pitch (elements)
     // one wave per split: a wave reads only the tiles it stored itself, so the
     // memory loop needs no work-group barrier (a wave's LDS operations retire
     // in program order)
-    static constexpr bool PRIVATE = RB == 1;
+    static constexpr bool PRIVATE = RB == 1 && !HS;
     static constexpr int PLANES = SEP ? 2 : 1;
     static constexpr int TILE = BN * LDK;     // elements per plane per buffer
-    static constexpr int KV_BYTES = KSPLIT * NBUF * PLANES * TILE * 2;
+    static constexpr int KV_BYTES = MS * NBUF * PLANES * TILE * 2;
     // direct loads per wave and tile: a load fills 1 KB (8 rows of 128 bytes)
     static constexpr int DPW = DMA ? BN * DH * 2 / 1024 / RB : 0;
-    static constexpr int CMB_BYTES = KSPLIT > 1 ? RB * (KSPLIT - 1) * 64 * (EB * 16 + 2) * 4 : 0;
+    static constexpr int CMB_BYTES = MS > 1 ? RB * (MS - 1) * 64 * (EB * 16 + 2) * 4 : 0;
     // Fused projection (PROJ): the tile's query tokens (32*RB rows) and head
     // h's rows of W_Q[s] (DH rows) are staged in LDS (up to kProjMaxD wide,
     // aliasing the memory buffers, which are filled only afterwards); the
@@ -103,9 +113,9 @@ struct Cfg {
     static constexpr int SMEM = SMEM_MAIN > CMB_BYTES ? SMEM_MAIN : CMB_BYTES;
     // the staging registers must leave room for the rest of the prologue
     static constexpr bool BUILT = !PROJ || ZCPT + WCPT <= 24;
-    static constexpr int KV_CHUNKS = BN * DH / 8;                 // 16-byte chunks per plane
-    static constexpr int KV_CPT = KV_CHUNKS / (64 * RB);
-    static_assert(KV_CHUNKS % (64 * RB) == 0, "memory tile must split evenly over a split group");
+    static constexpr int KV_CHUNKS = BN * DS / 8;                 // 16-byte chunks per plane
+    static constexpr int KV_CPT = KV_CHUNKS / (64 * SG);
+    static_assert(KV_CHUNKS % (64 * SG) == 0, "memory tile must split evenly over a staging group");
     // Register stages of the memory prefetch (tiles ahead of the LDS stage).
     // d_h = 32 tiles are computed quickly, so their loads get the longer
     // lead: up to 8 x 16 bytes per thread in flight (32 VGPRs), at most 4
@@ -120,10 +130,10 @@ struct Cfg {
     static constexpr int WPE = LDS_WAVES >= 12 && P == 1 ? 3 : (LDS_WAVES >= 8 ? 2 : 1);
 };
 
-template <int DH, int RB, int KSPLIT, bool SEP, bool PROJ, bool CUT>
+template <int DH, int RB, int KSPLIT, bool SEP, bool PROJ, bool CUT, bool HS = false>
 __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
-    amdgpu_waves_per_eu(Cfg<DH, RB, KSPLIT, SEP, PROJ, CUT>::WPE))) void attn_bf16_kernel(AttnArgs a) {
-    using C = Cfg<DH, RB, KSPLIT, SEP, PROJ, CUT>;
+    amdgpu_waves_per_eu(Cfg<DH, RB, KSPLIT, SEP, PROJ, CUT, HS>::WPE))) void attn_bf16_kernel(AttnArgs a) {
+    using C = Cfg<DH, RB, KSPLIT, SEP, PROJ, CUT, HS>;
     constexpr int P = C::P;
     __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
     const int q = a.q, d = a.d, heads = a.heads;
@@ -133,8 +143,9 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
     bf16* __restrict__ O = static_cast<bf16*>(a.O);
     int* __restrict__ ws = static_cast<int*>(a.ws);
 
-    const int tile = blockIdx.x / heads;
-    const int h = blockIdx.x - tile * heads;
+    const int hgroups = HS ? heads / 2 : heads;   // work-groups per work item
+    const int tile = blockIdx.x / hgroups;
+    const int hw = blockIdx.x - tile * hgroups;   // head (HS: head pair)
     int4 item;
     if (a.inplan) {
         // Small batch: every wave plans it (one lane per request) and takes
@@ -165,12 +176,15 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
     // the wave index is uniform across the wave: keep it (and every tile
     // address derived from it) in scalar registers
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int rb = w % RB, ksg = w / RB;     // query block, memory split
+    const int rb = w % RB, ksg = w / RB;     // query block, memory split (HS: head of the pair)
+    const int ms = HS ? 0 : ksg;             // memory split
+    const int hsel = HS ? ksg : 0;           // head within the staged features
+    const int h = HS ? 2 * hw + ksg : hw;    // this wave's head
     const int g = lane >> 5, l32 = lane & 31;
     const int qcol = rb * 32 + l32;
     const bool qvalid = qcol < nc;
     const int cand = c0 + qcol;
-    const int gt = tid - ksg * 64 * RB;       // thread index inside the split group
+    const int gt = HS ? tid : tid - ksg * 64 * RB;   // thread index inside the staging group
 
     // Per-candidate prefix cutoff (CUT; ReST reading note s.3.5, ULT): the
     // lane's query row sees memory rows [0, cut) of its request.  The tile
@@ -197,8 +211,8 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
 
     // ---------------- 1. memory prefetch and this wave's Q_h^T operands ----------------
     const int ntiles_kv = (L_loop + BN - 1) / BN;
-    const int n_iter = (ntiles_kv + KSPLIT - 1) / KSPLIT;
-    const bf16* Kh = K + (size_t)kv0 * d + h * DH;
+    const int n_iter = (ntiles_kv + C::MS - 1) / C::MS;
+    const bf16* Kh = K + (size_t)kv0 * d + (HS ? 2 * hw : h) * DH;
     const bf16* Vh = SEP ? V + (size_t)kv0 * d + h * DH : nullptr;
     // Chunk u of this thread: tile row j_u, 16-byte column chunk c8_u.  Its
     // global byte offset inside a tile and its LDS element offset are fixed;
@@ -208,8 +222,8 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
     int goff[C::KV_CPT], loff[C::KV_CPT];
 #pragma unroll
     for (int u = 0; u < C::KV_CPT; ++u) {
-        const int c = gt + u * 64 * RB;
-        const int j = c / (DH / 8), c8 = c % (DH / 8);
+        const int c = gt + u * 64 * C::SG;
+        const int j = c / (C::DS / 8), c8 = c % (C::DS / 8);
         goff[u] = (j * d + c8 * 8) * 2;
         loff[u] = j * C::LDK + c8 * 8;
     }
@@ -233,7 +247,7 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
                 vr[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, goff[u], 0, 0));
         }
     };
-    bf16* kvl = reinterpret_cast<bf16*>(smem) + (size_t)ksg * C::NBUF * C::PLANES * C::TILE;
+    bf16* kvl = reinterpret_cast<bf16*>(smem) + (size_t)ms * C::NBUF * C::PLANES * C::TILE;
     auto lstore = [&](int buf, const uint4 (&kr)[C::KV_CPT], const uint4 (&vr)[SEP ? C::KV_CPT : 1]) {
         bf16* base = kvl + buf * C::PLANES * C::TILE;
 #pragma unroll
@@ -289,13 +303,13 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
         if constexpr (C::DMA)
             return r * C::LDK + (((2 * k + (lane >> 5)) ^ ((r >> 1) & 7)) << 3);
         else
-            return r * C::LDK + 16 * k + 8 * (lane >> 5);
+            return r * C::LDK + hsel * DH + 16 * k + 8 * (lane >> 5);
     };
     auto vofs = [&](int row, int col) {
         if constexpr (C::DMA)
             return row * C::LDK + ((((col >> 3) ^ ((row >> 1) & 7))) << 3) + (col & 7);
         else
-            return row * C::LDK + col;
+            return row * C::LDK + hsel * DH + col;
     };
 
     // k-step k, half g: features 16k + 8g .. 16k + 8g + 7 of the lane's query
@@ -343,10 +357,10 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
     // stages, or (direct staging) the NBUF - 1 buffers ahead of the computed one.
     if constexpr (C::DMA) {
 #pragma unroll
-        for (int j = 0; j < C::NBUF - 1; ++j) dma(ksg + j * KSPLIT, j);
+        for (int j = 0; j < C::NBUF - 1; ++j) dma(ms + j * C::MS, j);
     } else {
 #pragma unroll
-        for (int j = 0; j < P; ++j) gload(ksg + j * KSPLIT, kreg[j], vreg[j]);
+        for (int j = 0; j < P; ++j) gload(ms + j * C::MS, kreg[j], vreg[j]);
     }
     if constexpr (PROJ) {
         bf16* zs = reinterpret_cast<bf16*>(smem);
@@ -407,7 +421,7 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
 
     if constexpr (!C::DMA) {
         lstore(0, kreg[0], vreg[0]);
-        gload(ksg + P * KSPLIT, kreg[0], vreg[0]);
+        gload(ms + P * C::MS, kreg[0], vreg[0]);
         __syncthreads();
     }
 
@@ -529,7 +543,7 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
         return fmaxf(mt, xor32(mt));   // both halves' keys
     };
 
-    // Iteration it computes this split's tile ksg + it*KSPLIT from LDS buffer
+    // Iteration it computes this split's tile ms + it*MS from LDS buffer
     // it&1, then (advance) moves the next tile from register stage (it+1)%P
     // into the other buffer and refills that stage with the tile P iterations
     // ahead.  The refill is issued on every path (past the end it moves no
@@ -539,13 +553,13 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
     auto advance = [&](int it, int j) {
         const int jn = (j + 1) % P;
         if (it + 1 < n_iter) lstore((it + 1) & 1, kreg[jn], vreg[jn]);
-        gload(ksg + (it + 1 + P) * KSPLIT, kreg[jn], vreg[jn]);
+        gload(ms + (it + 1 + P) * C::MS, kreg[jn], vreg[jn]);
         if constexpr (!C::PRIVATE) __syncthreads();
     };
     // Leading iterations whose tile is full: a loop whose body has no branch.
     const int n_fast = [&] {
         const int full = (CUT ? wmin : L) / BN;   // tiles 0 .. full-1 need no mask
-        return full > ksg ? (full - ksg + KSPLIT - 1) / KSPLIT : 0;
+        return full > ms ? (full - ms + C::MS - 1) / C::MS : 0;
     }();
 
     // ---- first pass: fixed reference ----
@@ -563,7 +577,7 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
             asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((PD - 1) * C::DPW) : "memory");
             if constexpr (!C::PRIVATE) __builtin_amdgcn_s_barrier();
             const int b = bc + PD < C::NBUF ? bc + PD : bc + PD - C::NBUF;
-            dma(ksg + (it + PD) * KSPLIT, b);
+            dma(ms + (it + PD) * C::MS, b);
         };
         auto end = [&]() { bc = bc + 1 < C::NBUF ? bc + 1 : 0; };
         int it0 = 0;
@@ -571,7 +585,7 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
             // iteration 0: the split's first tile sets the reference
             begin(0);
             scores(bc);
-            if (!full_tile(ksg)) mask(ksg);
+            if (!full_tile(ms)) mask(ms);
             m_run = tile_max();   // -inf for a lane that sees no row of the split
             m_seed = m_run == -INFINITY ? 0.f : m_run;
 #pragma unroll
@@ -595,7 +609,7 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
         }
 #pragma unroll 1
         for (int it = it0 > n_fast ? it0 : n_fast; it < n_iter; ++it) {
-            const int t = ksg + it * KSPLIT;
+            const int t = ms + it * C::MS;
             begin(it);
             scores(bc);
             if (!full_tile(t)) mask(t);   // (a split past its last tile: wholly masked)
@@ -613,7 +627,7 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
         int it0 = 0;
         if (n_iter > 0) {
             scores(0);
-            if (!full_tile(ksg)) mask(ksg);
+            if (!full_tile(ms)) mask(ms);
             m_run = tile_max();   // -inf for a lane that sees no row of the split
             m_seed = m_run == -INFINITY ? 0.f : m_run;
 #pragma unroll
@@ -633,7 +647,7 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
             values();
         };
         auto masked = [&](int it) {
-            const int t = ksg + it * KSPLIT;
+            const int t = ms + it * C::MS;
             scores(it & 1);
             if (!full_tile(t)) mask(t);   // (a split past its last tile: wholly masked)
             const float lt = weights(std::false_type{}, 0.f);
@@ -682,7 +696,7 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
         bool started = false;   // m_run holds a tile maximum (wave-uniform)
 #pragma unroll 1
         for (int it = 0; it < n_iter; ++it) {
-            const int t = ksg + it * KSPLIT;
+            const int t = ms + it * C::MS;
             if constexpr (C::DMA) {
                 dma(t, 0);
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -723,7 +737,7 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
 
     // ---------------- 3. merge the memory splits, normalise, store ----------------
     l_run += xor32(l_run);   // both halves' keys
-    if constexpr (KSPLIT > 1) {
+    if constexpr (C::MS > 1) {
         float* cmb = reinterpret_cast<float*>(smem);
         constexpr int PER = C::EB * 16 + 2;
         if (ksg > 0) {
@@ -824,6 +838,16 @@ hipError_t launch_one(const AttnArgs& a, hipStream_t stream) {
                 return hipErrorInvalidValue;
             } else {
                 hipLaunchKernelGGL((attn_bf16_kernel<DH, RB, KSPLIT, SEP, false, true>),
+                                   dim3((unsigned)blocks), dim3(64 * RB * KSPLIT), 0, stream, k);
+            }
+        } else if constexpr (DH == 32 && KSPLIT == 1 && !SEP && !PROJ) {
+            // 32-wide heads over one K = V memory: head pairs share each
+            // staged 128-byte line (two wave groups, one per head)
+            if (a.heads % 2 == 0) {
+                hipLaunchKernelGGL((attn_bf16_kernel<DH, RB, 2, false, false, false, true>),
+                                   dim3((unsigned)(blocks / 2)), dim3(64 * RB * 2), 0, stream, k);
+            } else {
+                hipLaunchKernelGGL((attn_bf16_kernel<DH, RB, KSPLIT, SEP, PROJ, false>),
                                    dim3((unsigned)blocks), dim3(64 * RB * KSPLIT), 0, stream, k);
             }
         } else {

@@ -304,6 +304,8 @@ def test_attend_and_attend_q_match_forward(name):
 @pytest.mark.parametrize("R,dh,heads,q,mode", [
     (1, 64, 4, 3, "shared"), (5, 32, 8, 2, "separate"), (16, 64, 2, 1, "shared"),
     (16, 128, 2, 3, "separate"), (17, 64, 4, 3, "shared"), (3, 64, 8, 2, "shared"),
+    # 32-wide heads over one memory: head pairs (an even count) and single heads
+    (7, 32, 8, 2, "shared"), (4, 32, 3, 1, "shared"), (9, 32, 2, 3, "shared"),
 ])
 def test_single_launch_and_split_paths_agree(R, dh, heads, q, mode):
     """Small batches on models up to 256 wide run as one launch (the attention
@@ -396,7 +398,7 @@ def test_full_eq7(name):
 # ---------------------------------------------------------------------------
 # Softmax reference: later memory tiles far above a split's first tile
 # ---------------------------------------------------------------------------
-def _rising_memory(mode, seed):
+def _rising_memory(mode, seed, heads=4):
     """Every query's scores against the memory rows past a request's first tile
     exceed its scores against the first tile by about 170 in log2 units, so
     their weights relative to the first tile's maximum overflow fp32: the
@@ -405,7 +407,7 @@ def _rising_memory(mode, seed):
     query has a large component along that key's direction."""
     rng = np.random.default_rng(seed)
     lengths, cands = [64 * 3 + 17, 64 * 6, 200, 40, 130], [70, 5, 33, 9, 64]
-    wl = W.custom("rising_" + mode, lengths, cands, q=1, d=256, heads=4, dtype="bf16",
+    wl = W.custom("rising_" + mode, lengths, cands, q=1, d=256, heads=heads, dtype="bf16",
                   kv_mode=mode, seed=seed)
     dh = wl.d // wl.heads
     z0 = 3.0 * rng.standard_normal(wl.d)
@@ -431,3 +433,28 @@ def test_later_tiles_far_above_the_first(monkeypatch, mode, variant):
     require_gpu()
     wl = _rising_memory(mode, 31)
     _check(wl, what="rising memory %s variant %s" % (mode, variant))
+
+
+@pytest.mark.parametrize("variant", ["default", "2,1", "4,1"])
+def test_later_tiles_far_above_the_first_head_pairs(monkeypatch, variant):
+    """The same memory at 32-wide heads over one K = V memory, attended over
+    projected queries (attend_q), where a work-group takes two heads over
+    shared tiles: the moving-maximum pass runs for the pair."""
+    monkeypatch.setenv("XATTN_SHORT", "0")
+    if variant != "default":
+        monkeypatch.setenv("XATTN_VARIANT", variant)
+    require_gpu()
+    wl = _rising_memory("shared", 37, heads=8)
+    ctx = ctx_for(wl)
+    t = X.to_device(wl)
+    ws = ctx.alloc_workspace(wl.R, wl.total_cand, wl.heads)
+    # the forward leaves the batch's plan in the workspace for attend_q
+    a = ctx.forward(t["Z"], t["W_Q"], t["K"], t["V"], t["cu_kv"], t["cu_cand"], wl.heads,
+                    workspace=ws).clone()
+    Q = ctx.project(t["Z"], t["W_Q"])
+    O = ctx.attend_q(Q, t["K"], t["V"], t["cu_kv"], t["cu_cand"], wl.heads, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, O)
+    got = O.float().cpu().numpy().astype(np.float64).reshape(wl.rows, wl.d)
+    err, rel = assert_close(got, _oracle(wl), "bf16", "rising memory head pairs %s" % variant)
+    print("rising memory head pairs %s: max-abs %.3e normwise %.3e" % (variant, err, rel))
