@@ -562,6 +562,23 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
         return full > ms ? (full - ms + C::MS - 1) / C::MS : 0;
     }();
 
+    // Pacing (direct staging: the long history, three work-groups per
+    // compute unit over equal memories).  A SIMD's instruction arbiter
+    // favours its oldest wave, so those work-groups ran at unequal speeds
+    // and finished one after another (per-work-group time stamps: 138, 168
+    // and 198 us), the last one alone on the SIMDs.  Each wave starts at the
+    // highest priority and steps down as it passes each quarter of its
+    // tiles, so that a wave that is behind goes first (174, 186, 196 us).
+    const int q1 = n_iter >> 2, q2 = n_iter >> 1, q3 = q1 + q2;
+    auto pace = [&](int it) {
+        if constexpr (C::DMA) {
+            if (it == q1) __builtin_amdgcn_s_setprio(2);
+            if (it == q2) __builtin_amdgcn_s_setprio(1);
+            if (it == q3) __builtin_amdgcn_s_setprio(0);
+        }
+    };
+    if constexpr (C::DMA) __builtin_amdgcn_s_setprio(3);
+
     // ---- first pass: fixed reference ----
     float l_peak = 0.f;   // largest tile weight sum of the lane
     if constexpr (C::DMA) {
@@ -570,6 +587,7 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
         constexpr int PD = C::NBUF - 1;
         int bc = 0;
         auto begin = [&](int it) {
+            pace(it);
             // this wave's loads of tile it have landed (the PD - 1 tiles behind
             // it may still be in flight) and its LDS reads of tile it - 1 are
             // done; past the barrier every wave's loads have landed and the
