@@ -117,17 +117,21 @@ struct Cfg {
     static constexpr int KV_CPT = KV_CHUNKS / (64 * SG);
     static_assert(KV_CHUNKS % (64 * SG) == 0, "memory tile must split evenly over a staging group");
     // Register stages of the memory prefetch (tiles ahead of the LDS stage).
-    // d_h = 32 tiles are computed quickly, so their loads get the longer
-    // lead: up to 8 x 16 bytes per thread in flight (32 VGPRs), at most 4
-    // tiles ahead.  Wider heads take one stage: a second one costs a wave
-    // per SIMD and measured slower.
+    // Per-head d_h = 32 tiles are computed quickly, so their loads get the
+    // longer lead: up to 8 x 16 bytes per thread in flight (32 VGPRs), at
+    // most 4 tiles ahead.  Wider heads take one stage: a second one costs a
+    // wave per SIMD and measured slower.  Head pairs take one stage too:
+    // their four waves share each tile's loads, and one stage leaves the
+    // registers for four waves per SIMD (ragged 46.4 -> 43.2 us against
+    // four stages at two waves).
     static constexpr int STAGE_REGS = KV_CPT * PLANES;
-    static constexpr int P = DH > 32 || STAGE_REGS >= 8 ? 1 : (8 / STAGE_REGS >= 4 ? 4 : 8 / STAGE_REGS);
+    static constexpr int P = HS || DH > 32 || STAGE_REGS >= 8 ? 1 : (8 / STAGE_REGS >= 4 ? 4 : 8 / STAGE_REGS);
     // Waves per SIMD the register allocation must leave room for: as many as
     // the LDS footprint admits, up to three (168 VGPRs per wave) with one
-    // register stage, two with deeper ones.
+    // register stage, two with deeper ones; head pairs four (128 VGPRs).
     static constexpr int LDS_WAVES = (163840 / SMEM) * NW;   // per compute unit
-    static constexpr int WPE = LDS_WAVES >= 12 && P == 1 ? 3 : (LDS_WAVES >= 8 ? 2 : 1);
+    static constexpr int WPE = HS && LDS_WAVES >= 16 ? 4
+                             : (LDS_WAVES >= 12 && P == 1 ? 3 : (LDS_WAVES >= 8 ? 2 : 1));
 };
 
 template <int DH, int RB, int KSPLIT, bool SEP, bool PROJ, bool CUT, bool HS = false>
