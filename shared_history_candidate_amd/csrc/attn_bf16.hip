@@ -61,6 +61,19 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // Widest model the fused projection stages in LDS.
 constexpr int kProjMaxD = kAttnProjMaxD;
 
+// Work-group order of the head-pair form.  Work-groups go to the eight XCDs
+// (each with its own L2) in turn, work-group b to XCD b % 8.  The plan lists
+// the items of one request (its slots and candidate blocks, which all read
+// the request's memory rows) one after another, so chunks of kXcdChunk
+// consecutive items go to one XCD with the same head pair: XCD x takes head
+// pair x % pairs and every (8 / pairs)-th chunk, in plan order, and a memory
+// line read by one item of the chunk is in that XCD's L2 for the others.
+// (The plain order puts consecutive items of one head pair on alternate
+// XCDs, and each line is fetched twice.)  Head counts whose pairs do not
+// divide 8 keep the plain order.
+constexpr int kXcds = 8, kXcdChunk = 8;
+__host__ __device__ inline bool xcd_chunked(int pairs) { return pairs <= kXcds && kXcds % pairs == 0; }
+
 template <int DH, int RB, int KSPLIT, bool SEP, bool PROJ, bool CUT = false, bool HS = false>
 struct Cfg {
     static constexpr int NW = RB * KSPLIT;
@@ -148,8 +161,15 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
     int* __restrict__ ws = static_cast<int*>(a.ws);
 
     const int hgroups = HS ? heads / 2 : heads;   // work-groups per work item
-    const int tile = blockIdx.x / hgroups;
-    const int hw = blockIdx.x - tile * hgroups;   // head (HS: head pair)
+    int tile = blockIdx.x / hgroups;
+    int hw = blockIdx.x - tile * hgroups;         // head (HS: head pair)
+    if constexpr (HS) {
+        if (xcd_chunked(hgroups)) {
+            const int x = blockIdx.x % kXcds, k = blockIdx.x / kXcds;
+            hw = x % hgroups;
+            tile = ((k / kXcdChunk) * (kXcds / hgroups) + x / hgroups) * kXcdChunk + k % kXcdChunk;
+        }
+    }
     int4 item;
     if (a.inplan) {
         // Small batch: every wave plans it (one lane per request) and takes
@@ -163,10 +183,11 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
         item = wave_plan_item(wp, tile, q, 32 * RB);
     } else {
         const int n_tiles = ws[kPlanNTiles];
+        // A plan built for another tile size (another batch shape) is not
+        // ours; work-groups past the plan's tiles have nothing to do.
+        if (tile >= n_tiles || ws[kPlanTileM] != 32 * RB) return;
         item = reinterpret_cast<const int4*>(reinterpret_cast<const char*>(ws) +
                                              kPlanHeaderBytes)[tile];
-        // A plan built for another tile size (another batch shape) is not ours.
-        if (tile >= n_tiles || ws[kPlanTileM] != 32 * RB) return;
     }
     // the item is the same in every lane: keep it in scalar registers
     const int kv0 = __builtin_amdgcn_readfirstlane(item.x);
@@ -866,8 +887,17 @@ hipError_t launch_one(const AttnArgs& a, hipStream_t stream) {
             // 32-wide heads over one K = V memory: head pairs share each
             // staged 128-byte line (two wave groups, one per head)
             if (a.heads % 2 == 0) {
+                const int pairs = a.heads / 2;
+                int64_t grid = blocks / 2;
+                if (xcd_chunked(pairs)) {
+                    // chunks of items dealt to the 8 / pairs XCDs of each
+                    // head pair; work-groups past the last item exit
+                    const int64_t chunks = (a.max_tiles + kXcdChunk - 1) / kXcdChunk;
+                    const int64_t per = kXcds / pairs;
+                    grid = (chunks + per - 1) / per * kXcdChunk * kXcds;
+                }
                 hipLaunchKernelGGL((attn_bf16_kernel<DH, RB, 2, false, false, false, true>),
-                                   dim3((unsigned)(blocks / 2)), dim3(64 * RB * 2), 0, stream, k);
+                                   dim3((unsigned)grid), dim3(64 * RB * 2), 0, stream, k);
             } else {
                 hipLaunchKernelGGL((attn_bf16_kernel<DH, RB, KSPLIT, SEP, PROJ, false>),
                                    dim3((unsigned)blocks), dim3(64 * RB * KSPLIT), 0, stream, k);
