@@ -79,7 +79,7 @@ struct Cfg {
     static constexpr int NW = RB * KSPLIT;
     static constexpr int NT = 64 * NW;
     // head pairs: the KSPLIT = 2 wave groups are the pair's heads, not memory splits
-    static_assert(!HS || (DH == 32 && KSPLIT == 2 && !SEP && !PROJ && !CUT), "head pairs");
+    static_assert(!HS || (DH == 32 && KSPLIT == 2 && !SEP && !PROJ), "head pairs");
     static constexpr int MS = HS ? 1 : KSPLIT;       // memory splits
     static constexpr int DS = HS ? 2 * DH : DH;      // staged features per memory row
     static constexpr int SG = HS ? NW : RB;          // waves staging one tile
@@ -877,17 +877,10 @@ hipError_t launch_one(const AttnArgs& a, hipStream_t stream) {
         k.scale_log2 = a.prescaled ? 1.0f : 1.4426950408889634f / sqrtf((float)DH);
         const int64_t blocks = a.max_tiles * a.heads;
         if (blocks <= 0) return hipSuccess;
-        if (a.cand_len) {
-            // cutoffs run over caller-projected queries only
-            if constexpr (PROJ) {
-                return hipErrorInvalidValue;
-            } else {
-                hipLaunchKernelGGL((attn_bf16_kernel<DH, RB, KSPLIT, SEP, false, true>),
-                                   dim3((unsigned)blocks), dim3(64 * RB * KSPLIT), 0, stream, k);
-            }
-        } else if constexpr (DH == 32 && KSPLIT == 1 && !SEP && !PROJ) {
-            // 32-wide heads over one K = V memory: head pairs share each
-            // staged 128-byte line (two wave groups, one per head)
+        // 32-wide heads over one K = V memory (caller-projected queries, an
+        // even head count, with or without cutoffs): head pairs, two wave
+        // groups over each staged 128-byte line, in XCD-chunked order
+        if constexpr (DH == 32 && KSPLIT == 1 && !SEP && !PROJ) {
             if (a.heads % 2 == 0) {
                 const int pairs = a.heads / 2;
                 int64_t grid = blocks / 2;
@@ -898,10 +891,21 @@ hipError_t launch_one(const AttnArgs& a, hipStream_t stream) {
                     const int64_t per = kXcds / pairs;
                     grid = (chunks + per - 1) / per * kXcdChunk * kXcds;
                 }
-                hipLaunchKernelGGL((attn_bf16_kernel<DH, RB, 2, false, false, false, true>),
-                                   dim3((unsigned)grid), dim3(64 * RB * 2), 0, stream, k);
+                if (a.cand_len)
+                    hipLaunchKernelGGL((attn_bf16_kernel<DH, RB, 2, false, false, true, true>),
+                                       dim3((unsigned)grid), dim3(64 * RB * 2), 0, stream, k);
+                else
+                    hipLaunchKernelGGL((attn_bf16_kernel<DH, RB, 2, false, false, false, true>),
+                                       dim3((unsigned)grid), dim3(64 * RB * 2), 0, stream, k);
+                return hipGetLastError();
+            }
+        }
+        if (a.cand_len) {
+            // cutoffs run over caller-projected queries only
+            if constexpr (PROJ) {
+                return hipErrorInvalidValue;
             } else {
-                hipLaunchKernelGGL((attn_bf16_kernel<DH, RB, KSPLIT, SEP, PROJ, false>),
+                hipLaunchKernelGGL((attn_bf16_kernel<DH, RB, KSPLIT, SEP, false, true>),
                                    dim3((unsigned)blocks), dim3(64 * RB * KSPLIT), 0, stream, k);
             }
         } else {
