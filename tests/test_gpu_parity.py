@@ -458,3 +458,34 @@ def test_later_tiles_far_above_the_first_head_pairs(monkeypatch, variant):
     got = O.float().cpu().numpy().astype(np.float64).reshape(wl.rows, wl.d)
     err, rel = assert_close(got, _oracle(wl), "bf16", "rising memory head pairs %s" % variant)
     print("rising memory head pairs %s: max-abs %.3e normwise %.3e" % (variant, err, rel))
+
+
+@pytest.mark.parametrize("cut", [False, True])
+@pytest.mark.parametrize("heads", [2, 6, 16, 32])
+def test_head_pairs_every_pair_count(heads, cut):
+    """32-wide heads over one K = V memory run as head pairs; the work-group
+    order is XCD-chunked when the pair count divides 8 (1, 8 pairs here) and
+    plain otherwise (3, 16 pairs).  Every row of a 24-request batch (more
+    than the single launch takes, so the projection GEMM and the attention
+    kernel run) against the oracle, with and without per-candidate prefix
+    cutoffs."""
+    require_gpu()
+    rng = np.random.default_rng(heads * 10 + cut)
+    R = 24
+    lengths = rng.integers(1, 700, R)
+    cands = rng.integers(0, 80, R)
+    wl = W.custom("pairs%d" % heads, lengths, cands, q=2, d=32 * heads, heads=heads,
+                  dtype="bf16", kv_mode="shared", seed=heads + 100 * cut)
+    if wl.total_cand == 0:
+        pytest.skip("no candidates drawn")
+    ctx = ctx_for(wl)
+    t = X.to_device(wl)
+    kv_len = W.prefix_lengths(wl, seed=heads) if cut else None
+    cl = torch.from_numpy(kv_len).to("cuda") if cut else None
+    O = ctx.forward(t["Z"], t["W_Q"], t["K"], t["V"], t["cu_kv"], t["cu_cand"], wl.heads,
+                    cand_kv_len=cl)
+    torch.cuda.synchronize()
+    got = O.float().cpu().numpy().astype(np.float64).reshape(wl.rows, wl.d)
+    ref = oracle.forward(wl.cu_kv, wl.cu_cand, wl.q, wl.heads, wl.Z, wl.wt, wl.K, wl.V, kv_len=kv_len)
+    err, rel = assert_close(got, ref, "bf16", "head pairs heads=%d cut=%d" % (heads, cut))
+    print("head pairs heads=%d cut=%d: rows=%d max-abs %.3e normwise %.3e" % (heads, cut, wl.rows, err, rel))
