@@ -742,7 +742,10 @@ xattn_status run_backward(xattn_ctx* ctx, const void* Z, const void* W_Q, const 
         a.lse = lse;
         a.Dsum = dsum;
         a.dO = dO;
-        const int ks = xattn::attn_bf16_variant_smem(dh, 2, 2, sep, false) > 0 ? 2 : 1;
+        // 64-candidate tiles (the plan above); 32-wide heads over one K = V
+        // memory take the (2, 1) shape, which runs as head pairs
+        const bool pairs = dh == 32 && !sep && heads % 2 == 0;
+        const int ks = !pairs && xattn::attn_bf16_variant_smem(dh, 2, 2, sep, false) > 0 ? 2 : 1;
         XATTN_TRY(xattn::launch_attn_bf16(a, 2, ks, s), "statistics kernel launch");
     } else {
         XATTN_TRY(xattn::launch_attn_f32_stats(reinterpret_cast<const float*>(ws + Lw.qs),
