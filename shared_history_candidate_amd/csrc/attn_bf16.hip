@@ -605,6 +605,14 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
         }
     };
     if constexpr (C::DMA) __builtin_amdgcn_s_setprio(3);
+    // The epilogue's pointers, in scalar registers before the memory loop: a
+    // scalar load still in flight there (the compiler issues them early)
+    // would turn each wait for this tile's LDS reads into a wait for all of
+    // them.
+    float* const lse_out = a.lse;
+    float* const dsum_out = a.Dsum;
+    const bf16* const dO_in = static_cast<const bf16*>(a.dO);
+    asm volatile("" ::"s"(O), "s"(lse_out), "s"(dsum_out), "s"(dO_in));
 
     // ---- first pass: fixed reference ----
     float l_peak = 0.f;   // largest tile weight sum of the lane
@@ -815,12 +823,12 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
         }
     }
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    if (a.lse) {
+    if (lse_out) {
         // statistics for the backward pass: the row's log2 normaliser and
         // D = <dO_row, O_row> over this head's features (fp32 O)
         float dpart = 0.f;
-        if (a.dO && qvalid) {
-            const bf16* drow = static_cast<const bf16*>(a.dO) + ((size_t)cand * q + s) * d + h * DH;
+        if (dO_in && qvalid) {
+            const bf16* drow = dO_in + ((size_t)cand * q + s) * d + h * DH;
 #pragma unroll
             for (int eb = 0; eb < C::EB; ++eb)
 #pragma unroll
@@ -833,8 +841,8 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
         dpart += xor32(dpart);
         if (qvalid && g == 0) {
             const size_t idx = ((size_t)cand * q + s) * heads + h;
-            a.lse[idx] = l_run > 0.f ? m_run + __builtin_amdgcn_logf(l_run) : -INFINITY;   // v_log_f32 is log2
-            if (a.Dsum) a.Dsum[idx] = dpart;
+            lse_out[idx] = l_run > 0.f ? m_run + __builtin_amdgcn_logf(l_run) : -INFINITY;   // v_log_f32 is log2
+            if (dsum_out) dsum_out[idx] = dpart;
         }
     }
     if (qvalid && O) {
