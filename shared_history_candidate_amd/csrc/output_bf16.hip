@@ -61,6 +61,16 @@ __global__ __launch_bounds__(NT) void gate_output_kernel(OutArgs a) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, l32 = lane & 31;
 
+    // Every pointer the unit loop uses, in scalar registers before it: a
+    // scalar load still in flight in the loop would make each wait for an
+    // LDS read there a wait for all of them (no LDS read ahead of the
+    // products).
+    const bf16* const Zp = a.Z;
+    const bf16* const Op = a.O;
+    const bf16* const Wgop = a.Wgo;
+    bf16* const Yp = a.Y;
+    asm volatile("" ::"s"(Zp), "s"(Op), "s"(Wgop), "s"(Yp));
+
     // unit u: slot s = u / n_chunks, candidates [cb, cb + nr)
     auto unit = [&](int uu, int& s, int& cb, int& nr) {
         s = uu / n_chunks;
@@ -78,7 +88,7 @@ __global__ __launch_bounds__(NT) void gate_output_kernel(OutArgs a) {
 
     uint4 zr[Z_CPT];
     auto zload = [&](int s, int cb, int nr) {
-        const __amdgpu_buffer_rsrc_t rz = rows_rsrc(a.Z, s, cb, nr);
+        const __amdgpu_buffer_rsrc_t rz = rows_rsrc(Zp, s, cb, nr);
 #pragma unroll
         for (int i = 0; i < Z_CPT; ++i) {
             const int idx = tid + i * NT, row = idx >> 5, col = idx & 31;
@@ -102,11 +112,31 @@ __global__ __launch_bounds__(NT) void gate_output_kernel(OutArgs a) {
         for (int kk = 0; kk < D / 16; ++kk) wr[kk] = *reinterpret_cast<const bf16x8*>(rowp + 16 * kk);
     };
 
+    // acc[rb] = wr . (rows 32rb.. of the LDS tile)^T over the D inputs, with
+    // each k-step's B fragments read one k-step ahead of its products
+    auto gemm = [&](const bf16x8 (&wr)[D / 16], f32x16 (&acc)[2]) {
+        auto frag = [&](int kk, int rb) {
+            return *reinterpret_cast<const bf16x8*>(buf + (rb * 32 + l32) * LDK + 16 * kk + 8 * g);
+        };
+        bf16x8 b[2][2];
+        b[0][0] = frag(0, 0);
+        b[0][1] = frag(0, 1);
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            if (kk + 1 < D / 16) {
+                b[(kk + 1) & 1][0] = frag(kk + 1, 0);
+                b[(kk + 1) & 1][1] = frag(kk + 1, 1);
+            }
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) acc[rb] = mfma32(wr[kk], b[kk & 1][rb], acc[rb]);
+        }
+    };
+
     int s, cb, nr;
     unit(u, s, cb, nr);
     int wslot = s;
     wload(wo, a.Wo + (size_t)(32 * w + l32) * D + 8 * g);
-    wload(wg, a.Wgo + ((size_t)s * D + 32 * w + l32) * D + 8 * g);
+    wload(wg, Wgop + ((size_t)s * D + 32 * w + l32) * D + 8 * g);
     zload(s, cb, nr);
     zstore();   // its wait covers the weight rows loaded before the Z rows
 #pragma unroll
@@ -121,7 +151,7 @@ __global__ __launch_bounds__(NT) void gate_output_kernel(OutArgs a) {
         // lane), requested before the next unit's Z rows: the vector-memory
         // counter completes in order, so waiting for them in the gate
         // epilogue does not wait for the Z rows
-        const __amdgpu_buffer_rsrc_t ro = rows_rsrc(a.O, s, cb, nr);
+        const __amdgpu_buffer_rsrc_t ro = rows_rsrc(Op, s, cb, nr);
         u32x4 ol[2][2];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
@@ -134,20 +164,14 @@ __global__ __launch_bounds__(NT) void gate_output_kernel(OutArgs a) {
         if (s != wslot) {
             // a new slot (rare): wait for its rows here
             wslot = s;
-            wload(wg, a.Wgo + ((size_t)s * D + 32 * w + l32) * D + 8 * g);
+            wload(wg, Wgop + ((size_t)s * D + 32 * w + l32) * D + 8 * g);
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(wg[kk]));
         }
 
         // 1. gate: G^T rows 32w.. = W_go[s] rows 32w.. . Z^T
         f32x16 acc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-                acc[rb] = mfma32(wg[kk], *reinterpret_cast<const bf16x8*>(
-                                             buf + (rb * 32 + l32) * LDK + 16 * kk + 8 * g),
-                                 acc[rb]);
+        gemm(wg, acc);
         __syncthreads();   // every wave is done reading Z
 
         // 2. gated = O * sigmoid(G), bf16, into LDS (acc reg 4*j4 + t:
@@ -177,15 +201,9 @@ __global__ __launch_bounds__(NT) void gate_output_kernel(OutArgs a) {
         // 3. Y^T rows 32w.. = W_o rows 32w.. . gated^T
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) acc[rb] = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-                acc[rb] = mfma32(wo[kk], *reinterpret_cast<const bf16x8*>(
-                                             buf + (rb * 32 + l32) * LDK + 16 * kk + 8 * g),
-                                 acc[rb]);
+        gemm(wo, acc);
         // Y rows, 16 bytes per lane (join_runs)
-        const __amdgpu_buffer_rsrc_t ry = rows_rsrc(a.Y, s, cb, nr);
+        const __amdgpu_buffer_rsrc_t ry = rows_rsrc(Yp, s, cb, nr);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
