@@ -40,10 +40,12 @@ CONFIGS = ("rest", "long", "transx", "ragged", "tiny")
 _ATTN_SRC = ["shared_history_candidate_amd/csrc/attn_bf16.hip",
              "shared_history_candidate_amd/csrc/lds_dma.h",
              "shared_history_candidate_amd/csrc/plan_wave.h",
+             "shared_history_candidate_amd/csrc/xcd_order.h",
              "shared_history_candidate_amd/csrc/common.h"]
 KERNEL_SOURCES = {"fused": _ATTN_SRC, "attention": _ATTN_SRC, "prefix": _ATTN_SRC,
                   "backward": ["shared_history_candidate_amd/csrc/bwd_bf16.hip"] + _ATTN_SRC,
                   "output": ["shared_history_candidate_amd/csrc/gemm_bf16.hip",
+                             "shared_history_candidate_amd/csrc/output_bf16.hip",
                              "shared_history_candidate_amd/csrc/common.h"],
                   "projection": ["shared_history_candidate_amd/csrc/gemm_bf16.hip",
                                  "shared_history_candidate_amd/csrc/plan_device.h",

@@ -45,6 +45,7 @@
 #include "internal.h"
 #include "lds_dma.h"
 #include "plan_wave.h"
+#include "xcd_order.h"
 
 namespace xattn {
 
@@ -61,18 +62,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // Widest model the fused projection stages in LDS.
 constexpr int kProjMaxD = kAttnProjMaxD;
 
-// Work-group order of the head-pair form.  Work-groups go to the eight XCDs
-// (each with its own L2) in turn, work-group b to XCD b % 8.  The plan lists
-// the items of one request (its slots and candidate blocks, which all read
-// the request's memory rows) one after another, so chunks of kXcdChunk
-// consecutive items go to one XCD with the same head pair: XCD x takes head
-// pair x % pairs and every (8 / pairs)-th chunk, in plan order, and a memory
-// line read by one item of the chunk is in that XCD's L2 for the others.
-// (The plain order puts consecutive items of one head pair on alternate
-// XCDs, and each line is fetched twice.)  Head counts whose pairs do not
-// divide 8 keep the plain order.
-constexpr int kXcds = 8, kXcdChunk = 8;
-__host__ __device__ inline bool xcd_chunked(int pairs) { return pairs <= kXcds && kXcds % pairs == 0; }
 
 template <int DH, int RB, int KSPLIT, bool SEP, bool PROJ, bool CUT = false, bool HS = false>
 struct Cfg {
@@ -163,13 +152,7 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
     const int hgroups = HS ? heads / 2 : heads;   // work-groups per work item
     int tile = blockIdx.x / hgroups;
     int hw = blockIdx.x - tile * hgroups;         // head (HS: head pair)
-    if constexpr (HS) {
-        if (xcd_chunked(hgroups)) {
-            const int x = blockIdx.x % kXcds, k = blockIdx.x / kXcds;
-            hw = x % hgroups;
-            tile = ((k / kXcdChunk) * (kXcds / hgroups) + x / hgroups) * kXcdChunk + k % kXcdChunk;
-        }
-    }
+    if constexpr (HS) xcd_pair_item(blockIdx.x, hgroups, tile, hw);   // XCD-chunked order
     int4 item;
     if (a.inplan) {
         // Small batch: every wave plans it (one lane per request) and takes
@@ -890,15 +873,8 @@ hipError_t launch_one(const AttnArgs& a, hipStream_t stream) {
         // groups over each staged 128-byte line, in XCD-chunked order
         if constexpr (DH == 32 && KSPLIT == 1 && !SEP && !PROJ) {
             if (a.heads % 2 == 0) {
-                const int pairs = a.heads / 2;
-                int64_t grid = blocks / 2;
-                if (xcd_chunked(pairs)) {
-                    // chunks of items dealt to the 8 / pairs XCDs of each
-                    // head pair; work-groups past the last item exit
-                    const int64_t chunks = (a.max_tiles + kXcdChunk - 1) / kXcdChunk;
-                    const int64_t per = kXcds / pairs;
-                    grid = (chunks + per - 1) / per * kXcdChunk * kXcds;
-                }
+                // (work-groups past the last item exit)
+                const int64_t grid = xcd_pair_grid(a.max_tiles, a.heads / 2);
                 if (a.cand_len)
                     hipLaunchKernelGGL((attn_bf16_kernel<DH, RB, 2, false, false, true, true>),
                                        dim3((unsigned)grid), dim3(64 * RB * 2), 0, stream, k);
