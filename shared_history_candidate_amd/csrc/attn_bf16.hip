@@ -19,7 +19,8 @@
 // 32-wide head is half a line of each memory row, so a work-group takes the
 // two heads of a line instead: its two wave groups (ks = 0, 1) attend heads
 // 2p and 2p + 1 over the same staged tiles of both heads' 64 features, with
-// no memory split and no merge.
+// no memory split and no merge, one register stage (four waves per SIMD),
+// launched in XCD-chunked order (xcd_order.h).
 //
 // Products are computed transposed so that each lane holds one query row and
 // the softmax reductions along the key axis stay inside the lane (plus one
