@@ -98,6 +98,10 @@ struct SCfg {
     static constexpr int Z_CPT = QR * (D / 8) / NT;     // 16-byte Z chunks per thread
     static_assert(LMAX * (D / 8) % NT == 0 && QR * (D / 8) % NT == 0, "even staging split");
     static_assert(LMAX % MB == 0, "whole score blocks");
+    // memory blocks attended in one pass (unit_exact): up to three, for
+    // 64-wide heads (with 32- and 128-wide heads the kernel's registers do
+    // not hold their scores: the compiler spills)
+    static constexpr int NBX = CODEC || DH != 64 ? 0 : (LMAX / MB < 3 ? LMAX / MB : 3);
 };
 
 // One query chunk: candidates [cb, cb + nr) of a request, slot s.
@@ -566,9 +570,89 @@ __global__ __launch_bounds__(NT) void short_bf16_kernel(AttnArgs a, ShortCodec c
                 for (int eb = 0; eb < C::EBW; ++eb) oacc[k][eb] = mfma32(vf[u16][eb], pb[u16], oacc[k][eb]);
         };
 
+        // A memory of at most NBX blocks (the TransX memory: 96 rows) is
+        // attended in one pass: the scores of all its blocks first (NBX
+        // independent product chains that the matrix cores run back to
+        // back), then their exact row maximum, the weights, and the PV
+        // products.  No running maximum, no rescale.  Blocks past the
+        // memory's rows read the zero rows staged behind them and are masked.
+        auto unit_exact = [&](int k, int rows) {
+            const int u = w + NW * k;
+            const int h = (u / C::FP) >> 1, e0 = (u % C::FP) * C::EBW * 32;
+            constexpr int NB = C::NBX > 0 ? C::NBX : 1;
+            f32x16 sc[NB];
+#pragma unroll
+            for (int t = 0; t < NB; ++t) {
+                const bf16* kb = kvs + (t * MB + l32) * LDK + h * DH + 8 * g;
+                bf16x8 kf[C::KST];
+#pragma unroll
+                for (int kk = 0; kk < C::KST; ++kk) kf[kk] = *reinterpret_cast<const bf16x8*>(kb + 16 * kk);
+                sc[t] = mfma32(kf[0], qb[k][0], f32x16{});
+#pragma unroll
+                for (int kk = 1; kk < C::KST; ++kk) sc[t] = mfma32(kf[kk], qb[k][kk], sc[t]);
+            }
+            // register rr of block t holds memory row t*MB + (rr/4)*8 + 4g + rr%4
+#pragma unroll
+            for (int t = 0; t < NB; ++t) {
+                int jl = rows - t * MB;
+                asm volatile("" : "+s"(jl));
+                if (jl < MB) {
+#pragma unroll
+                    for (int rr = 0; rr < 16; ++rr)
+                        if ((rr >> 2) * 8 + 4 * g + (rr & 3) >= jl) sc[t][rr] = -INFINITY;
+                }
+            }
+            float mt = fmaxf(sc[0][0], sc[0][1]);
+#pragma unroll
+            for (int t = 0; t < NB; ++t)
+#pragma unroll
+                for (int rr = (t == 0 ? 2 : 0); rr < 16; rr += 2) mt = fmaxf(mt, fmaxf(sc[t][rr], sc[t][rr + 1]));
+            const float m = fmaxf(mt, xor32(mt)) * scale_log2;   // row 0 is always visible: finite
+            float lt[NB];
+#pragma unroll
+            for (int t = 0; t < NB; ++t) {
+                bf16x8 pb[2];
+                lt[t] = 0.f;
+#pragma unroll
+                for (int rr = 0; rr < 16; rr += 2) {
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[t][rr], scale_log2, -m));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[t][rr + 1], scale_log2, -m));
+                    const bf16x2 pp = {(bf16)p0, (bf16)p1};
+                    lt[t] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lt[t], false);
+                    pb[rr >> 3][rr & 7] = pp[0];
+                    pb[rr >> 3][(rr & 7) + 1] = pp[1];
+                }
+                bf16x8 vf[2][C::EBW];
+#pragma unroll
+                for (int u16 = 0; u16 < 2; ++u16)
+#pragma unroll
+                    for (int eb = 0; eb < C::EBW; ++eb) {
+                        const bf16* base =
+                            vsrc + (t * MB + 16 * u16 + tr_row) * LDK + h * DH + e0 + eb * 32 + tr_col;
+                        vf[u16][eb] = cat(lds_read_tr16(base), lds_read_tr16(base + 8 * LDK));
+                    }
+#pragma unroll
+                for (int u16 = 0; u16 < 2; ++u16)
+#pragma unroll
+                    for (int eb = 0; eb < C::EBW; ++eb)
+                        oacc[k][eb] = mfma32(vf[u16][eb], pb[u16], oacc[k][eb]);
+            }
+            float l = lt[0];
+#pragma unroll
+            for (int t = 1; t < NB; ++t) l += lt[t];
+            m_run[k] = m;
+            l_run[k] = l;
+        };
+
         // memory chunks of LMAX rows; the first is staged above, later ones
         // (memories longer than LMAX) between work-group barriers here
         const int n_mc = (cur.L + LMAX - 1) / LMAX;
+        if (C::NBX > 0 && cur.L > 0 && cur.L <= C::NBX * MB) {
+            if constexpr (C::NBX > 0) {
+#pragma unroll
+                for (int k = 0; k < C::UPW; ++k) unit_exact(k, cur.L);
+            }
+        } else
         for (int mc = 0; mc < n_mc; ++mc) {
             const int row0 = cur.kv0 + mc * LMAX, rows = min(LMAX, cur.L - mc * LMAX);
             if (mc > 0) {
