@@ -291,16 +291,19 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
             dgoff[j] = (r * d + c * 8) * 2;
         }
     }
+    // A tile reads at most BN rows, so its descriptor covers at most BN rows
+    // (32-bit arithmetic, all scalar); the LDS address of this wave's part
+    // of buffer 0 is taken once.
+    const uint32_t dma_lds0 = __builtin_amdgcn_readfirstlane(lds_addr_of(kvl + rb * C::DPW * 512));
     auto dma = [&](int t, int buf) {
         const int row0 = t * BN;
         const int left = L_loop - row0;
-        const size_t nb = left > 0 ? (size_t)left * d * 2 : 0;
-        const uint32_t bytes = nb > 0xFFFFFFF0u ? 0xFFFFFFF0u : (uint32_t)nb;
-        const size_t roff = left > 0 ? (size_t)row0 * d : 0;
+        const int rows = __builtin_amdgcn_readfirstlane(left <= 0 ? 0 : (left < BN ? left : BN));
+        const uint32_t bytes = (uint32_t)rows * (uint32_t)d * 2u;
+        const size_t roff = rows > 0 ? (size_t)row0 * d : 0;
         const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(Kh + roff), (short)0, bytes, 0x00020000);
-        const uint32_t base =
-            __builtin_amdgcn_readfirstlane(lds_addr_of(kvl + buf * C::PLANES * C::TILE + rb * C::DPW * 512));
+        const uint32_t base = dma_lds0 + (uint32_t)(buf * C::PLANES * C::TILE * 2);
 #pragma unroll
         for (int j = 0; j < C::DPW; ++j) lds_dma16(rk, base + j * 1024, dgoff[j]);
     };
