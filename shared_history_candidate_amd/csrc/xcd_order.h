@@ -11,6 +11,15 @@
 // consecutive items of one head pair on alternate XCDs, and each line is
 // fetched twice.)  Head counts whose pairs do not divide 8 keep the plain
 // order.
+//
+// The plan is sorted longest memory first, and each XCD deals its
+// work-groups to its compute units in turn, so without more care the first
+// compute unit of an XCD would get the longest item of every round and the
+// last one the shortest.  Every other round of kXcdRound work-groups per XCD
+// (one per compute unit) therefore runs in reverse order: compute unit j
+// takes positions j, 2 kXcdRound - 1 - j, 2 kXcdRound + j, ..., whose memory
+// lengths sum to about the same for every j.  The grid covers whole rounds,
+// so the reversal stays inside it.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -19,6 +28,8 @@
 namespace xattn {
 
 constexpr int kXcds = 8, kXcdChunk = 8;
+constexpr int kXcdRound = 32;   // compute units per XCD (MI355X: 256 in 8 XCDs)
+static_assert(kXcdRound % kXcdChunk == 0, "a round holds whole chunks");
 
 __host__ __device__ inline bool xcd_chunked(int pairs) {
     return pairs <= kXcds && kXcds % pairs == 0;
@@ -28,7 +39,10 @@ __host__ __device__ inline bool xcd_chunked(int pairs) {
 // get an item index the caller rejects against the plan's item count.
 __device__ inline void xcd_pair_item(int b, int pairs, int& item, int& pair) {
     if (xcd_chunked(pairs)) {
-        const int x = b % kXcds, k = b / kXcds;
+        const int x = b % kXcds;
+        int k = b / kXcds;
+        const int r = k / kXcdRound;
+        if (r & 1) k = r * kXcdRound + (kXcdRound - 1) - (k - r * kXcdRound);
         pair = x % pairs;
         item = ((k / kXcdChunk) * (kXcds / pairs) + x / pairs) * kXcdChunk + k % kXcdChunk;
     } else {
@@ -42,7 +56,8 @@ inline int64_t xcd_pair_grid(int64_t max_items, int pairs) {
     if (!xcd_chunked(pairs)) return max_items * pairs;
     const int64_t chunks = (max_items + kXcdChunk - 1) / kXcdChunk;
     const int64_t per = kXcds / pairs;
-    return (chunks + per - 1) / per * kXcdChunk * kXcds;
+    const int64_t per_xcd = (chunks + per - 1) / per * kXcdChunk;   // work-groups per XCD
+    return (per_xcd + kXcdRound - 1) / kXcdRound * kXcdRound * kXcds;
 }
 
 }  // namespace xattn
