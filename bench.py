@@ -43,6 +43,7 @@ _ATTN_SRC = ["shared_history_candidate_amd/csrc/attn_bf16.hip",
              "shared_history_candidate_amd/csrc/xcd_order.h",
              "shared_history_candidate_amd/csrc/common.h"]
 KERNEL_SOURCES = {"fused": _ATTN_SRC, "attention": _ATTN_SRC, "prefix": _ATTN_SRC,
+                  "fused_prefix": _ATTN_SRC,
                   "backward": ["shared_history_candidate_amd/csrc/bwd_bf16.hip"] + _ATTN_SRC,
                   "output": ["shared_history_candidate_amd/csrc/gemm_bf16.hip",
                              "shared_history_candidate_amd/csrc/output_bf16.hip",
@@ -137,13 +138,15 @@ def kernel_sha(kernel):
 
 # Kernel names (regular expressions over the demangled or mangled names) of
 # the kernels a step can run: the single launch of a small batch (attention
-# kernel that projects its own queries: flags PROJ=1, CUT=0), the
-# projection GEMM and the attention kernel over its output (PROJ=0; CUT=1
-# with per-candidate prefix lengths; a last flag set for the head-pair form
-# of 32-wide heads), or the short-memory kernel.
+# kernel that projects its own queries: flags PROJ=1, CUT=0, or CUT=1 with
+# per-candidate prefix lengths), the projection GEMM and the attention kernel
+# over its output (PROJ=0; CUT=1 with prefix lengths; a last flag set for the
+# head-pair form of 32-wide heads), or the short-memory kernel.
 KERNEL_NAMES = {
     "fused": r"attn_bf16_kernel(<\d+, \d+, \d+, \w+, true, false(, \w+)?>|"
              r"ILi\d+ELi\d+ELi\d+ELb[01]ELb1ELb0E)",
+    "fused_prefix": r"attn_bf16_kernel(<\d+, \d+, \d+, \w+, true, true(, \w+)?>|"
+                    r"ILi\d+ELi\d+ELi\d+ELb[01]ELb1ELb1E)",
     "attention": r"attn_bf16_kernel(<\d+, \d+, \d+, \w+, false, false(, \w+)?>|"
                  r"ILi\d+ELi\d+ELi\d+ELb[01]ELb0ELb0E)",
     "prefix": r"attn_bf16_kernel(<\d+, \d+, \d+, \w+, false, true(, \w+)?>|"
@@ -384,6 +387,14 @@ def forward_setup(ctx, wl, t, ws, O, stream, cut=None):
     elif cut is None and launches == 1:
         # the attention kernel plans the batch and projects its own queries
         kernels = {"fused": (step, wl.flops(), wl.bytes())}
+    elif launches == 1:
+        # the same single launch with per-candidate prefix lengths: the
+        # projection's work and the visible rows' attention, with Z and W_Q
+        # read in place of Q
+        kv_arg = cut.cpu().numpy()
+        b = 2 if wl.dtype == "bf16" else 4
+        kernels = {"fused_prefix": (step, wl.flops_projection() + wl.flops_attention(kv_arg),
+                                    wl.bytes_attention(kv_arg) + b * wl.q * wl.d * wl.d)}
     else:
         Qbuf = torch.empty_like(O)
         proj = ctx.project(t["Z"], t["W_Q"], Q=Qbuf, stream=stream, bind=True)

@@ -207,8 +207,12 @@ xattn_status xattn_forward_noalloc(xattn_ctx* ctx,
  *     attends to memory rows [cu_seqlens_kv[r], cu_seqlens_kv[r] + n) with
  *     n = cand_kv_len[c] clamped to [0, L_r]; every slot of the candidate
  *     uses the same n.  A candidate with n = 0 gets all-zero output rows.
- * Always two launches in bf16 (projection GEMM with the planner, then the
- * attention kernel with the per-row mask), three in fp32.  Other arguments,
+ * In bf16, one launch for a batch of at most 16 requests on a model of at
+ * most 256 features (the attention kernel plans the batch, projects its own
+ * queries and applies the per-row mask, as xattn_forward's single launch
+ * does), otherwise two (projection GEMM with the planner, then the attention
+ * kernel with the per-row mask); the short-memory kernel is never used here.
+ * Three launches in fp32.  Other arguments,
  * workspace and errors as for xattn_forward; a NULL cand_kv_len with
  * total_cand > 0 is XATTN_EINVAL.  With every cand_kv_len[c] >= L_r the
  * result equals xattn_forward's. */

@@ -446,9 +446,9 @@ xattn_status run_forward(Mode mode, xattn_ctx* ctx, const void* Z, const void* W
             if (e != hipSuccess) return hip_fail(e, "short-memory kernel launch");
             return XATTN_OK;
         }
-        // the prefix cutoff runs over projected queries in the workspace
+        // small batches, with or without prefix cutoffs: one launch
         const bool fused_proj =
-            !cand_len && fused_shape(c, R) &&
+            fused_shape(c, R) &&
             xattn::attn_bf16_variant_smem(c.d_model / heads, var.rb, var.ksplit,
                                           c.kv_mode == XATTN_KV_SEPARATE, true) > 0;
         if (mode == Mode::kAttendQ) {

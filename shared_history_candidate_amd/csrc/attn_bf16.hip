@@ -889,13 +889,8 @@ hipError_t launch_one(const AttnArgs& a, hipStream_t stream) {
             }
         }
         if (a.cand_len) {
-            // cutoffs run over caller-projected queries only
-            if constexpr (PROJ) {
-                return hipErrorInvalidValue;
-            } else {
-                hipLaunchKernelGGL((attn_bf16_kernel<DH, RB, KSPLIT, SEP, false, true>),
-                                   dim3((unsigned)blocks), dim3(64 * RB * KSPLIT), 0, stream, k);
-            }
+            hipLaunchKernelGGL((attn_bf16_kernel<DH, RB, KSPLIT, SEP, PROJ, true>),
+                               dim3((unsigned)blocks), dim3(64 * RB * KSPLIT), 0, stream, k);
         } else {
             hipLaunchKernelGGL((attn_bf16_kernel<DH, RB, KSPLIT, SEP, PROJ, false>),
                                dim3((unsigned)blocks), dim3(64 * RB * KSPLIT), 0, stream, k);
