@@ -100,9 +100,8 @@ bool short_shape(const xattn_ctx* ctx, int R, int total_kv, int heads) {
            (int64_t)R * xattn::short_max_rows(c.kv_mode == XATTN_KV_SEPARATE);
 }
 
-// Work-groups of the short-memory kernel: one per compute unit (its LDS
-// footprint admits one), never more than there are work items.
-int short_grid(xattn_ctx* ctx, int64_t max_tiles) {
+// Compute units of the context's device (read once).
+int cu_count(xattn_ctx* ctx) {
     if (ctx->n_cu <= 0) {
         int n = 0;
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, ctx->cfg.device) !=
@@ -111,7 +110,14 @@ int short_grid(xattn_ctx* ctx, int64_t max_tiles) {
             n = 256;
         ctx->n_cu = n;
     }
-    return (int)(max_tiles < ctx->n_cu ? max_tiles : ctx->n_cu);
+    return ctx->n_cu;
+}
+
+// Work-groups of the short-memory kernel: one per compute unit (its LDS
+// footprint admits one), never more than there are work items.
+int short_grid(xattn_ctx* ctx, int64_t max_tiles) {
+    const int n = cu_count(ctx);
+    return (int)(max_tiles < n ? max_tiles : n);
 }
 
 // LDS bytes of a variant as this batch shape launches it.  The choice depends
@@ -434,6 +440,7 @@ xattn_status run_forward(Mode mode, xattn_ctx* ctx, const void* Z, const void* W
         a.O = O;
         a.cand_len = cand_len;
         a.lse = lse;
+        a.ncu = cu_count(ctx);
         if (mode != Mode::kAttendQ && !cand_len && short_shape(ctx, R, total_kv, heads)) {
             // projection and attention in one launch; a forward pass also
             // plans the batch in that launch (request order) and stores the

@@ -68,6 +68,9 @@ struct AttnArgs {
     float* lse;
     float* Dsum;
     const void* dO;
+    // compute units of the device (0: unknown); the attention kernel's
+    // pacing reads a work-group's dispatch round from it
+    int ncu;
 };
 // Widest model (d) whose queries the attention kernel projects itself.
 constexpr int kAttnProjMaxD = 256;
