@@ -643,8 +643,42 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
             end();
             it0 = 1;
         }
+        // Full tiles: no mask.  With three buffers the loop runs in groups
+        // of three iterations whose buffers are constants (iteration it uses
+        // buffer it % 3, and the loop starts at it0 = 1), so that every LDS
+        // address is a loop-invariant register plus an immediate offset; a
+        // scheduling barrier ends each iteration, so that the compiler keeps
+        // each tile's work in its own iteration.
+        int itf = it0;
+        if constexpr (C::NBUF == 3) {
+            auto body = [&](int it, auto bufc) {
+                constexpr int B = decltype(bufc)::value;
+                pace(it);
+                asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((PD - 1) * C::DPW) : "memory");
+                if constexpr (!C::PRIVATE) __builtin_amdgcn_s_barrier();
+                dma(ms + (it + PD) * C::MS, (B + PD) % C::NBUF);
+                scores(B);
+                const float lt = weights(std::false_type{}, 0.f);
+                l_peak = fmaxf(l_peak, lt);
+                l_run += lt;
+                values();
+                // the row sums are materialised here (left alone, the
+                // compiler sinks all three tiles' v_dot2 sums into the last
+                // iteration of the group)
+                asm volatile("" : "+v"(l_run), "+v"(l_peak));
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            if (itf == 1) {
 #pragma unroll 1
-        for (int it = it0; it < n_fast; ++it) {   // full tiles: no mask
+                for (; itf + 3 <= n_fast; itf += 3) {
+                    body(itf, std::integral_constant<int, 1>{});
+                    body(itf + 1, std::integral_constant<int, 2>{});
+                    body(itf + 2, std::integral_constant<int, 0>{});
+                }
+            }
+        }
+#pragma unroll 1
+        for (int it = itf; it < n_fast; ++it) {
             begin(it);
             scores(bc);
             const float lt = weights(std::false_type{}, 0.f);
