@@ -298,7 +298,11 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
     auto dma = [&](int t, int buf) {
         const int row0 = t * BN;
         const int left = L_loop - row0;
-        const int rows = __builtin_amdgcn_readfirstlane(left <= 0 ? 0 : (left < BN ? left : BN));
+        // two scalar operations (written as a clamp, the compiler takes a
+        // VALU med3 and reads its result back)
+        int rows = left < BN ? left : BN;
+        asm volatile("" : "+s"(rows));
+        rows = rows > 0 ? rows : 0;
         const uint32_t bytes = (uint32_t)rows * (uint32_t)d * 2u;
         const size_t roff = rows > 0 ? (size_t)row0 * d : 0;
         const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
@@ -466,7 +470,9 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
     // before the first product so that the LDS latency is paid once per tile.
     f32x16 sacc[2];
     bf16x8 vf[4][C::EB];
-    auto scores = [&](int buf) {
+    // (mid: issued between the K-fragment reads and the first product, in
+    // the reads' latency)
+    auto scores = [&](int buf, auto&& mid) {
         const bf16* kb = kvl + buf * C::PLANES * C::TILE;
         const bf16* vb = kb + (C::PLANES - 1) * C::TILE;
         bf16x8 kf[2][C::KST];
@@ -479,6 +485,7 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
                                 *reinterpret_cast<const bf16x4*>(row + 4));
             }
         }
+        mid();
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) sacc[hh] = mfma32(kf[hh][0], qb[0], negm);
 #pragma unroll
@@ -630,7 +637,7 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
         if (n_iter > 0) {
             // iteration 0: the split's first tile sets the reference
             begin(0);
-            scores(bc);
+            scores(bc, [] {});
             if (!full_tile(ms)) mask(ms);
             m_run = tile_max();   // -inf for a lane that sees no row of the split
             m_seed = m_run == -INFINITY ? 0.f : m_run;
@@ -656,8 +663,7 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
                 pace(it);
                 asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((PD - 1) * C::DPW) : "memory");
                 if constexpr (!C::PRIVATE) __builtin_amdgcn_s_barrier();
-                dma(ms + (it + PD) * C::MS, (B + PD) % C::NBUF);
-                scores(B);
+                scores(B, [&] { dma(ms + (it + PD) * C::MS, (B + PD) % C::NBUF); });
                 const float lt = weights(std::false_type{}, 0.f);
                 l_peak = fmaxf(l_peak, lt);
                 l_run += lt;
@@ -680,7 +686,7 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
 #pragma unroll 1
         for (int it = itf; it < n_fast; ++it) {
             begin(it);
-            scores(bc);
+            scores(bc, [] {});
             const float lt = weights(std::false_type{}, 0.f);
             l_peak = fmaxf(l_peak, lt);
             l_run += lt;
@@ -691,7 +697,7 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
         for (int it = it0 > n_fast ? it0 : n_fast; it < n_iter; ++it) {
             const int t = ms + it * C::MS;
             begin(it);
-            scores(bc);
+            scores(bc, [] {});
             if (!full_tile(t)) mask(t);   // (a split past its last tile: wholly masked)
             const float lt = weights(std::false_type{}, 0.f);
             l_peak = fmaxf(l_peak, lt);
@@ -706,7 +712,7 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
         // iteration 0: the split's first tile sets the reference
         int it0 = 0;
         if (n_iter > 0) {
-            scores(0);
+            scores(0, [] {});
             if (!full_tile(ms)) mask(ms);
             m_run = tile_max();   // -inf for a lane that sees no row of the split
             m_seed = m_run == -INFINITY ? 0.f : m_run;
@@ -720,7 +726,7 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
             it0 = 1;
         }
         auto fast = [&](int it) {
-            scores(it & 1);
+            scores(it & 1, [] {});
             const float lt = weights(std::false_type{}, 0.f);
             l_peak = fmaxf(l_peak, lt);
             l_run += lt;
@@ -728,7 +734,7 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
         };
         auto masked = [&](int it) {
             const int t = ms + it * C::MS;
-            scores(it & 1);
+            scores(it & 1, [] {});
             if (!full_tile(t)) mask(t);   // (a split past its last tile: wholly masked)
             const float lt = weights(std::false_type{}, 0.f);
             l_peak = fmaxf(l_peak, lt);
@@ -786,7 +792,7 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
             }
             __syncthreads();
             if (t < ntiles_kv) {
-                scores(0);
+                scores(0, [] {});
                 if (!full_tile(t)) mask(t);
                 float lt = weights(std::false_type{}, 0.f);
                 if (!started || __any(lt > kSumCap)) {
