@@ -172,10 +172,13 @@ def test_plan_bit_exact_ragged_edges():
         assert np.array_equal(tiles.cpu().numpy(), o[2])
 
 
-@pytest.mark.parametrize("R,spread", [(1025, 3), (2049, 10**6), (4096, 40), (4096, 10**6)])
+@pytest.mark.parametrize("R,spread", [(512, 10**6), (513, 40), (1025, 3), (2049, 10**6),
+                                      (4096, 40), (4096, 10**6)])
 def test_plan_bit_exact_many_requests(R, spread):
     """More requests than the planner has threads: the ranking sorts in LDS
-    (few distinct lengths: long runs of ties broken by request index)."""
+    (few distinct lengths: long runs of ties broken by request index); 512
+    and 513 requests sit on either side of the batches whose offsets the
+    planner holds in LDS."""
     require_gpu()
     rng = np.random.default_rng(R + spread)
     wl = W.custom("p_many", rng.integers(0, spread, R) % 200, rng.integers(0, 5, R), q=2, d=64,
@@ -190,7 +193,7 @@ def test_plan_bit_exact_many_requests(R, spread):
     assert np.array_equal(tiles.cpu().numpy(), o[2])
 
 
-@pytest.mark.parametrize("R", [300, 4096])
+@pytest.mark.parametrize("R", [256, 300, 4096])
 def test_forward_many_requests_projection_path(monkeypatch, R):
     """The planner inside the projection launch (256 threads) with more
     requests than threads; every row against the oracle."""
