@@ -54,8 +54,8 @@ namespace {
 
 constexpr int BN = 64;               // memory rows per tile
 constexpr float kSumCap = 4096.0f;   // largest accepted per-lane weight sum of one tile (moving maximum)
-// Largest per-lane tile weight sum the fixed reference accepts: sums over
-// 2^31 memory rows and their products with values below 2^47 stay finite.
+// Largest per-lane weight sum the fixed reference accepts: the weights and
+// their products with values below 2^47 stay finite.
 constexpr float kWeightCap = 1.125899906842624e15f;   // 2^50
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -449,7 +449,7 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
     // and bf16 operands hold exactly as well up to kWeightCap, and the final
     // normalisation divides the common factor out.  The memory loop then
     // carries no conditional update of the accumulators.  If some lane's
-    // tile weights summed to more than kWeightCap, the work-group repeats the
+    // weights summed to more than kWeightCap, the work-group repeats the
     // split with a moving maximum (second pass, below).
     f32x16 oacc[C::EB];
 #pragma unroll
@@ -539,7 +539,7 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
                 const float p0 = __builtin_amdgcn_exp2f(x0);
                 const float p1 = __builtin_amdgcn_exp2f(x1);
                 const bf16x2 pp = {(bf16)p0, (bf16)p1};
-                lt[hh] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lt[hh], false);
+                lt[hh] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, rr == 0 ? 0.f : lt[hh], false);
                 pb[hh * 2 + (rr >> 3)][rr & 7] = pp[0];
                 pb[hh * 2 + (rr >> 3)][(rr & 7) + 1] = pp[1];
             }
@@ -615,7 +615,6 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
     asm volatile("" ::"s"(O), "s"(lse_out), "s"(dsum_out), "s"(dO_in));
 
     // ---- first pass: fixed reference ----
-    float l_peak = 0.f;   // largest tile weight sum of the lane
     if constexpr (C::DMA) {
         // Direct staging: iteration it computes the tile in buffer bc (it %
         // NBUF) while the tiles up to it + PD are in flight.
@@ -644,7 +643,6 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) negm[rr] = -m_seed;
             const float lt = weights(std::true_type{}, -m_seed);
-            l_peak = lt;
             l_run = lt;
             values();
             end();
@@ -665,13 +663,12 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
                 if constexpr (!C::PRIVATE) __builtin_amdgcn_s_barrier();
                 scores(B, [&] { dma(ms + (it + PD) * C::MS, (B + PD) % C::NBUF); });
                 const float lt = weights(std::false_type{}, 0.f);
-                l_peak = fmaxf(l_peak, lt);
                 l_run += lt;
                 values();
                 // the row sums are materialised here (left alone, the
                 // compiler sinks all three tiles' v_dot2 sums into the last
                 // iteration of the group)
-                asm volatile("" : "+v"(l_run), "+v"(l_peak));
+                asm volatile("" : "+v"(l_run));
                 __builtin_amdgcn_sched_barrier(0);
             };
             if (itf == 1) {
@@ -688,7 +685,6 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
             begin(it);
             scores(bc, [] {});
             const float lt = weights(std::false_type{}, 0.f);
-            l_peak = fmaxf(l_peak, lt);
             l_run += lt;
             values();
             end();
@@ -700,7 +696,6 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
             scores(bc, [] {});
             if (!full_tile(t)) mask(t);   // (a split past its last tile: wholly masked)
             const float lt = weights(std::false_type{}, 0.f);
-            l_peak = fmaxf(l_peak, lt);
             l_run += lt;
             values();
             end();
@@ -719,7 +714,6 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) negm[rr] = -m_seed;
             const float lt = weights(std::true_type{}, -m_seed);
-            l_peak = lt;
             l_run = lt;
             values();
             advance(0, 0);
@@ -728,7 +722,6 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
         auto fast = [&](int it) {
             scores(it & 1, [] {});
             const float lt = weights(std::false_type{}, 0.f);
-            l_peak = fmaxf(l_peak, lt);
             l_run += lt;
             values();
         };
@@ -737,7 +730,6 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
             scores(it & 1, [] {});
             if (!full_tile(t)) mask(t);   // (a split past its last tile: wholly masked)
             const float lt = weights(std::false_type{}, 0.f);
-            l_peak = fmaxf(l_peak, lt);
             l_run += lt;
             values();
         };
@@ -772,7 +764,9 @@ __global__ __launch_bounds__(64 * RB * KSPLIT) __attribute__((
     // leave the first tile with maximum -inf (no visible row); its weights
     // then stay zero: its visible rows are a prefix of the memory, so a split
     // whose first tile shows it nothing shows it nothing later either.
-    if (__syncthreads_or(l_peak > kWeightCap)) {
+    // (the lane's running sum bounds every tile's sum: testing it is the
+    // stricter condition, and needs no per-tile maximum in the loop)
+    if (__syncthreads_or(l_run > kWeightCap)) {
         // (rare: a plain loop, one tile at a time through LDS buffer 0)
 #pragma unroll
         for (int eb = 0; eb < C::EB; ++eb) oacc[eb] = f32x16{};
