@@ -211,15 +211,29 @@ __global__ __launch_bounds__(128 * KS) void bwd_dq_kernel(BwdArgs a) {
             }
         // dS^T = P^T o (dP^T - D), rows past the request's memory (or past
         // the lane's prefix) masked
+        // Only a request's last tile is partial (with cutoffs: any tile):
+        // there the scores of masked rows become -inf, so that their weights
+        // are 0 (and dP - D is finite: rows past the memory read as zeros);
+        // the other tiles skip the per-score test.  The opaque copy keeps
+        // the compiler from folding the tile test into per-score tests.
         const int jleft = (CUT ? cut : L) - t * kBN;
+        int jl = L - t * kBN;
+        asm volatile("" : "+s"(jl));
+        if (CUT || jl < kBN) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    const int j = hh * 32 + (rr >> 2) * 8 + 4 * g + (rr & 3);
+                    if (j >= jleft) sacc[hh][rr] = -INFINITY;
+                }
+        }
         bf16x8 dsb[4];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
-                const int j = hh * 32 + (rr >> 2) * 8 + 4 * g + (rr & 3);
-                float p = __builtin_amdgcn_exp2f(sacc[hh][rr]);
-                if (CUT ? j >= jleft : (jleft < kBN && j >= jleft)) p = 0.f;
+                const float p = __builtin_amdgcn_exp2f(sacc[hh][rr]);
                 dsb[hh * 2 + (rr >> 3)][rr & 7] = (bf16)(p * pacc[hh][rr]);
             }
         // dQ^T += K^T dS^T over the four 16-key slabs of the tile
