@@ -305,7 +305,8 @@ struct DkvCfg {
 };
 
 template <int DH, bool SEP, bool CUT>
-__global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DH == 64 && !SEP ? 3 : 1)))
+void bwd_dkv_kernel(BwdArgs a) {
     using C = DkvCfg<DH, SEP>;
     __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
     const int q = a.q, d = a.d, heads = a.heads;
