@@ -256,7 +256,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const bf16* __restrict__ Z,
                         for (int t = 0; t < 4; ++t) {
                             const float e = __builtin_amdgcn_exp2f(-acc[i][j][8 * bp + 4 * h2 + t] *
                                                                    1.4426950408889634f);
-                            v[h2][t] = (bf16)((float)ov[t] / (1.0f + e));
+                            v[h2][t] = (bf16)((float)ov[t] * __builtin_amdgcn_rcpf(1.0f + e));
                         }
                     }
                 } else if (oscale == 1.0f) {

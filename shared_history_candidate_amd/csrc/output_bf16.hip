@@ -5,9 +5,10 @@
 //
 // (ReST reading note s.3.3.1 Eq. (7); the gate projection token-specific as
 // in s.3.3.2 Eq. (8), W_o shared by all slots).  Same arithmetic as the two
-// GEMM launches of gemm_bf16.hip (fp32 gate, sigmoid via exp2, the gated
-// values rounded to bf16 before the W_o product), without the gated values'
-// round trip through HBM: they stay in LDS.
+// GEMM launches of gemm_bf16.hip (fp32 gate, sigmoid via exp2 and the
+// hardware reciprocal, the gated values rounded to bf16 before the W_o
+// product), without the gated values' round trip through HBM: they stay in
+// LDS.
 //
 // Work decomposition.  A persistent grid of one 8-wave work-group per compute
 // unit walks the units (slot s, 64 candidates), slot-major, in equal
@@ -192,7 +193,7 @@ __global__ __launch_bounds__(NT) void gate_output_kernel(OutArgs a) {
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     const float e = __builtin_amdgcn_exp2f(-acc[rb][4 * j4 + t] * 1.4426950408889634f);
-                    v[t] = (bf16)((float)o[t] / (1.0f + e));
+                    v[t] = (bf16)((float)o[t] * __builtin_amdgcn_rcpf(1.0f + e));
                 }
                 *reinterpret_cast<bf16x4*>(buf + (rb * 32 + l32) * LDK + 32 * w + 8 * j4 + 4 * g) = v;
             }
