@@ -525,6 +525,18 @@ __global__ __launch_bounds__(256) void bwd_dw_kernel(const bf16* __restrict__ dQ
     __shared__ __attribute__((aligned(16))) bf16 sb[2][kWC * kWLD];
     const int tpd = (d + kWT - 1) / kWT;
     int bid = blockIdx.x;
+    {
+        // The tpd x tpd output tiles of one (chunk, slot) read the same
+        // candidate rows of dQ and Z: all of them on one XCD (work-group b
+        // runs on XCD b % 8), so that those rows come from HBM once and from
+        // that XCD's L2 for the other tiles.  Rounds of 8 (chunk, slot)
+        // units; a last partial round keeps the plain order.
+        const int G = tpd * tpd, per = 8 * G;
+        if (bid < (int)gridDim.x / per * per) {
+            const int x = bid % 8, k = bid / 8;
+            bid = ((k / G) * 8 + x) * G + k % G;
+        }
+    }
     const int it = bid % tpd;
     bid /= tpd;
     const int ot = bid % tpd;
